@@ -1,0 +1,277 @@
+"""Float64 CPU oracle for block-sparse GQA decode attention.
+
+TEST INFRASTRUCTURE ONLY.  Only the tests, the package smoke check and the
+benchmark's CPU-baseline leg may import or call this module.  The product path
+(the HIP library and its binding) never routes through it, and it shares no
+code, table or helper with that path.
+
+What it computes, written out from the pages' definitions with no blocking,
+fusion or reordering:
+
+* ``sparse_decode`` -- each decode query token attends, per kv head, only the
+  keys of its selected 128-token pages that are causally visible at its
+  position (vLLM API page ``vllm.models.minimax_m3.common.sparse_attention``:
+  ``MiniMaxM3SparseImpl`` docstring and ``MiniMaxM3SparseTritonImpl.forward``;
+  vLLM test file ``test_minimax_m3_msa_cutlass_sparse_decode.py``:
+  ``_make_topk``).  Steps: dequant -> gather the selected live pages -> causal
+  mask -> softmax -> PV.
+* ``block_max_scores`` -- the indexer's per-block causal max of q.k over the
+  group's q heads and visible keys (TensorRT-LLM PR #17171 "Custom decode
+  kernels for MinimaxM3", indexer-scorer commit message).
+* ``select_topk`` -- top-k blocks per (token, kv head) by score, ties to the
+  lower block index, padded with -1 (same PR, selector; tie rule from the
+  full-decode-step workload statement).
+
+Readings taken where the pages leave a step open (each is also listed in the
+design notes):
+
+1. Top-k entries are *logical* block ids into the request's block-table row
+   (``_make_topk`` writes ``arange(visible_pages)`` over a shuffled pool).
+2. Token ``t = r*dql + l`` sits at ``pos = seq_len[r] - dql + l`` and sees keys
+   ``0..pos`` (``_make_topk``: ``visible_tokens = seq_len - query_len +
+   local_query + 1``).
+3. A negative index, or a block that starts after ``pos``, contributes nothing
+   and its block-table entry is not read.
+4. A row with no visible key (all -1, or a padding row ``t >= batch*dql``)
+   outputs exact zeros (PR #17171, flash-decoding commit: zeroed, not NaN,
+   output for padding rows).
+5. q head ``j`` reads kv head ``j // G`` with ``G = Hq / Hkv``.
+6. KV bytes are OCP fp8 e4m3fn (``torch.float8_e4m3fn`` in the test file) or
+   bf16; K is the first 128 entries of the packed last dim, V the last 128
+   (``msa_cutlass_sparse_decode``: ``kv_cache.split(_HEAD_DIM, dim=-1)``).
+   ``k_scale``/``v_scale`` multiply the decoded values.
+7. The scorer uses the attention q and the K half of the same cache, raw dot
+   product (no softmax scale), ``-inf`` for blocks that start after ``pos``.
+8. The selector ranks blocks with score ``> -inf`` by (score desc, block asc).
+
+Pins: every function here is checked in ``tests/test_oracle_pins.py`` against
+something other than itself (torch's fp8/bf16 casts, dense causal attention
+through ``torch.nn.functional.scaled_dot_product_attention``, closed forms,
+invariances, brute-force loops).
+"""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+
+PAGE = 128
+HEAD_DIM = 128
+
+
+# ---------------------------------------------------------------------------
+# number formats
+# ---------------------------------------------------------------------------
+
+def decode_e4m3fn(codes) -> np.ndarray:
+    """OCP fp8 e4m3fn code -> float64 value.
+
+    Bit fields: sign s (bit 7), exponent E (bits 6..3, bias 7), mantissa M
+    (bits 2..0).  E == 15 and M == 7 is NaN (no infinities); E == 0 is
+    subnormal ``M/8 * 2^-6``; otherwise ``(1 + M/8) * 2^(E-7)``.  Largest
+    finite magnitude 448.
+    """
+    c = np.asarray(codes).astype(np.int64)
+    s = (c >> 7) & 1
+    e = (c >> 3) & 0xF
+    m = c & 0x7
+    sign = np.where(s == 1, -1.0, 1.0)
+    sub = sign * (m / 8.0) * 2.0 ** -6
+    nor = sign * (1.0 + m / 8.0) * np.exp2(e.astype(np.float64) - 7.0)
+    v = np.where(e == 0, sub, nor)
+    v = np.where((e == 15) & (m == 7), np.nan, v)
+    return v.astype(np.float64)
+
+
+_E4M3_TABLE = decode_e4m3fn(np.arange(256))
+
+
+def decode_bf16(bits) -> np.ndarray:
+    """bf16 bit pattern (uint16) -> float64 (exact: bf16 is the top half of an
+    fp32)."""
+    b = np.asarray(bits).astype(np.uint32) << np.uint32(16)
+    with np.errstate(invalid="ignore"):
+        return b.view(np.float32).astype(np.float64)
+
+
+def dequant(raw: np.ndarray, kv_dtype: str, scale: float) -> np.ndarray:
+    """Stored KV entries -> float64 values times the per-tensor scale."""
+    if kv_dtype == "fp8_e4m3":
+        return _E4M3_TABLE[np.asarray(raw, dtype=np.uint8)] * float(scale)
+    if kv_dtype == "bf16":
+        return decode_bf16(raw) * float(scale)
+    raise ValueError(f"unknown kv dtype {kv_dtype!r}")
+
+
+# ---------------------------------------------------------------------------
+# indexing helpers (small on purpose: the pin tests plant mistakes in them)
+# ---------------------------------------------------------------------------
+
+def token_position(seq_len: int, dql: int, local: int) -> int:
+    """Absolute 0-based position of local decode token ``local``."""
+    return int(seq_len) - int(dql) + int(local)
+
+
+def visible_rows(pos: int, block: int) -> int:
+    """Number of keys of logical block ``block`` visible at ``pos``
+    (0 when the block starts after ``pos``)."""
+    if block < 0 or block * PAGE > pos:
+        return 0
+    return min(PAGE, pos - block * PAGE + 1)
+
+
+def kv_head_of(q_head: int, group: int) -> int:
+    return q_head // group
+
+
+def split_kv(raw_rows: np.ndarray):
+    """Packed rows [n, 2*D] -> (K rows, V rows)."""
+    return raw_rows[:, :HEAD_DIM], raw_rows[:, HEAD_DIM:]
+
+
+def softmax_attend(qv: np.ndarray, k: np.ndarray, v: np.ndarray,
+                   sm_scale: float) -> np.ndarray:
+    """softmax(sm_scale * q k^T) v for one query vector, float64."""
+    z = sm_scale * (k @ qv)
+    z = z - z.max()
+    w = np.exp(z)
+    return (w @ v) / w.sum()
+
+
+# ---------------------------------------------------------------------------
+# the attend
+# ---------------------------------------------------------------------------
+
+def gather_live(kv, kv_dtype, k_scale, v_scale, block_table_row, pos, head,
+                indices, check_distinct=True):
+    """Dequantized K and V rows of the selected blocks visible at ``pos``."""
+    ks, vs, seen = [], [], set()
+    for b in indices:
+        b = int(b)
+        n = visible_rows(pos, b)
+        if n <= 0:
+            continue
+        if check_distinct:
+            assert b not in seen, f"duplicate block index {b}"
+            seen.add(b)
+        p = int(block_table_row[b])
+        kraw, vraw = split_kv(kv[p, head, :n, :])
+        ks.append(dequant(kraw, kv_dtype, k_scale))
+        vs.append(dequant(vraw, kv_dtype, v_scale))
+    if not ks:
+        return None, None
+    return np.concatenate(ks, axis=0), np.concatenate(vs, axis=0)
+
+
+def sparse_decode(q_bits, kv, kv_dtype, k_scale, v_scale, block_table, seq_lens,
+                  topk, decode_query_len, num_kv_heads, sm_scale, rows=None):
+    """Block-sparse GQA decode, float64.
+
+    q_bits   uint16 bf16 bits [num_token_rows, Hq, 128]
+    kv       uint8 (fp8 codes) or uint16 (bf16 bits) [num_blocks, Hkv, 128, 256]
+    topk     int32 [num_token_rows, Hkv, k] logical block ids (-1 = none)
+    rows     optional iterable of token rows to evaluate (default: all)
+
+    Returns float64 [len(rows), Hq, 128].  Rows at or past
+    ``batch*decode_query_len`` are padding rows and come back as zeros.
+    """
+    q_bits = np.asarray(q_bits)
+    num_rows, hq, d = q_bits.shape
+    assert d == HEAD_DIM and hq % num_kv_heads == 0
+    group = hq // num_kv_heads
+    dql = int(decode_query_len)
+    real = len(seq_lens) * dql
+    row_list = range(num_rows) if rows is None else list(rows)
+    out = np.zeros((len(row_list), hq, HEAD_DIM), dtype=np.float64)
+    for i, t in enumerate(row_list):
+        if t >= real:
+            continue
+        r, loc = divmod(int(t), dql)
+        pos = token_position(seq_lens[r], dql, loc)
+        gathered = {}
+        for j in range(hq):
+            h = kv_head_of(j, group)
+            if h not in gathered:
+                gathered[h] = gather_live(kv, kv_dtype, k_scale, v_scale,
+                                          block_table[r], pos, h, topk[t, h, :])
+            k, v = gathered[h]
+            if k is None:
+                continue
+            out[i, j] = softmax_attend(decode_bf16(q_bits[t, j]), k, v, sm_scale)
+    return out
+
+
+# ---------------------------------------------------------------------------
+# the indexer block-max scorer and the top-k selector
+# ---------------------------------------------------------------------------
+
+def block_max_scores(q_bits, kv, kv_dtype, k_scale, block_table, seq_lens,
+                     decode_query_len, num_kv_heads, max_blocks, rows=None):
+    """score[h, b, t] = max over the group's q heads g and the visible keys j
+    of block b of q[t, h*G+g] . K[page(b), h, j]; -inf where block b starts
+    after token t's position.  Raw dot product (no softmax scale).
+
+    Returns float64 [Hkv, max_blocks, len(rows)].
+    """
+    q_bits = np.asarray(q_bits)
+    num_rows, hq, _ = q_bits.shape
+    group = hq // num_kv_heads
+    dql = int(decode_query_len)
+    real = len(seq_lens) * dql
+    row_list = range(min(num_rows, real)) if rows is None else list(rows)
+    score = np.full((num_kv_heads, max_blocks, len(row_list)), -np.inf)
+    for i, t in enumerate(row_list):
+        if t >= real:
+            continue
+        r, loc = divmod(int(t), dql)
+        pos = token_position(seq_lens[r], dql, loc)
+        for h in range(num_kv_heads):
+            qs = decode_bf16(q_bits[t, h * group:(h + 1) * group])   # [G, D]
+            for b in range(max_blocks):
+                n = visible_rows(pos, b)
+                if n <= 0:
+                    continue
+                p = int(block_table[r, b])
+                kraw, _ = split_kv(kv[p, h, :n, :])
+                k = dequant(kraw, kv_dtype, k_scale)                 # [n, D]
+                score[h, b, i] = np.max(qs @ k.T)
+    return score
+
+
+def select_topk(score, k: int) -> np.ndarray:
+    """score [Hkv, NB, T] -> int32 [T, Hkv, k]: blocks with score > -inf ranked
+    by (score descending, block id ascending), first k, padded with -1."""
+    score = np.asarray(score, dtype=np.float64)
+    hkv, nb, nt = score.shape
+    out = np.full((nt, hkv, k), -1, dtype=np.int32)
+    for h in range(hkv):
+        for t in range(nt):
+            s = score[h, :, t]
+            cand = [b for b in range(nb) if s[b] > -math.inf]
+            cand.sort(key=lambda b: (-s[b], b))
+            sel = cand[:k]
+            out[t, h, :len(sel)] = sel
+    return out
+
+
+# ---------------------------------------------------------------------------
+# byte accounting (the quantities the throughput figures are built from)
+# ---------------------------------------------------------------------------
+
+def live_rows_per_unit(block_table, seq_lens, topk, decode_query_len):
+    """For every real (token, kv head) unit: list of (block, visible rows)."""
+    dql = int(decode_query_len)
+    real = len(seq_lens) * dql
+    hkv = topk.shape[1]
+    res = {}
+    for t in range(real):
+        r, loc = divmod(t, dql)
+        pos = token_position(seq_lens[r], dql, loc)
+        for h in range(hkv):
+            lst = []
+            for b in topk[t, h, :]:
+                n = visible_rows(pos, int(b))
+                if n > 0:
+                    lst.append((int(b), n))
+            res[(t, h)] = lst
+    return res

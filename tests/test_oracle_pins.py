@@ -1,0 +1,558 @@
+"""Pins for the float64 oracle (CPU only).
+
+Each check ties the oracle to something other than itself: torch's own fp8 /
+bf16 casts, dense causal attention computed by
+``torch.nn.functional.scaled_dot_product_attention`` on the un-paged sequence,
+closed forms, invariances, brute-force loops and hand-worked values from the
+pages (``tests/golden/page_facts.json``).  The last group plants plausible
+mistakes in the oracle's helpers and checks that a pin catches each one.
+"""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle.msa_oracle as om
+from workloads import gen
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "page_facts.json")
+
+
+def golden():
+    with open(GOLDEN) as f:
+        return json.load(f)
+
+
+# ---------------------------------------------------------------------------
+# independent reference helpers (torch casts, SDPA)
+# ---------------------------------------------------------------------------
+
+def torch_values(kv: np.ndarray, kv_dtype: str) -> torch.Tensor:
+    """Decode the stored entries with torch's own dtype casts (float64)."""
+    if kv_dtype == gen.KV_FP8:
+        return torch.from_numpy(np.ascontiguousarray(kv)).view(torch.float8_e4m3fn).to(
+            torch.float64)
+    return torch.from_numpy(np.ascontiguousarray(kv).view(np.int16)).view(
+        torch.bfloat16).to(torch.float64)
+
+
+def torch_q(q_bits: np.ndarray) -> torch.Tensor:
+    return torch.from_numpy(np.ascontiguousarray(q_bits).view(np.int16)).view(
+        torch.bfloat16).to(torch.float64)
+
+
+def dense_reference(case: gen.DecodeCase) -> np.ndarray:
+    """Textbook causal GQA attention over each request's whole (un-paged)
+    sequence, via SDPA in float64.  Equals the sparse attend when the index
+    lists cover every visible block."""
+    hq, hkv = case.num_q_heads, case.num_kv_heads
+    g = hq // hkv
+    vals = torch_values(case.kv, case.kv_dtype)
+    q = torch_q(case.q)
+    out = torch.zeros(case.num_token_rows, hq, 128, dtype=torch.float64)
+    for r in range(case.batch):
+        s = int(case.seq_lens[r])
+        n = gen.pages_for(s)
+        pages = torch.from_numpy(case.block_table[r, :n].astype(np.int64))
+        seqkv = vals[pages].permute(1, 0, 2, 3).reshape(hkv, n * 128, 256)[:, :s]
+        k = (seqkv[..., :128] * case.k_scale).repeat_interleave(g, dim=0)
+        v = (seqkv[..., 128:] * case.v_scale).repeat_interleave(g, dim=0)
+        t0 = r * case.dql
+        qh = q[t0:t0 + case.dql].permute(1, 0, 2)
+        pos = s - case.dql + torch.arange(case.dql)
+        mask = torch.arange(s)[None, :] <= pos[:, None]
+        o = torch.nn.functional.scaled_dot_product_attention(
+            qh, k, v, attn_mask=mask, scale=case.sm_scale)
+        out[t0:t0 + case.dql] = o.permute(1, 0, 2)
+    return out.numpy()
+
+
+def run_oracle(case: gen.DecodeCase, topk=None, **over) -> np.ndarray:
+    kw = dict(q_bits=case.q, kv=case.kv, kv_dtype=case.kv_dtype, k_scale=case.k_scale,
+              v_scale=case.v_scale, block_table=case.block_table, seq_lens=case.seq_lens,
+              topk=case.topk if topk is None else topk, decode_query_len=case.dql,
+              num_kv_heads=case.num_kv_heads, sm_scale=case.sm_scale)
+    kw.update(over)
+    return om.sparse_decode(**kw)
+
+
+def dense_pin_error(case: gen.DecodeCase) -> float:
+    got = run_oracle(case)
+    ref = dense_reference(case)
+    return float(np.max(np.abs(got - ref)))
+
+
+def small_dense_case(hq=16, hkv=1, dql=4, kv_dtype=gen.KV_FP8, pattern=(257, 513),
+                     pairs=1, seed=0, k_scale=1.0, v_scale=1.0):
+    case = gen.make_p3_case(hq, hkv, pairs, dql, seq_pattern=pattern, seed=seed,
+                            kv_dtype=kv_dtype, topk_k=8)
+    case.k_scale, case.v_scale = k_scale, v_scale
+    return case
+
+
+# ---------------------------------------------------------------------------
+# number formats
+# ---------------------------------------------------------------------------
+
+def test_e4m3fn_decode_exhaustive_vs_torch():
+    codes = np.arange(256, dtype=np.uint8)
+    mine = om.decode_e4m3fn(codes)
+    ref = torch.from_numpy(codes).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    both_nan = np.isnan(mine) & np.isnan(ref)
+    assert np.array_equal(np.isnan(mine), np.isnan(ref))
+    assert np.all(both_nan | (mine == ref))
+    # sign of zero too
+    assert np.array_equal(np.signbit(mine[~both_nan]), np.signbit(ref[~both_nan]))
+
+
+def test_e4m3fn_golden_codes():
+    g = golden()["e4m3fn"]
+    for code, val in g["codes"].items():
+        assert om.decode_e4m3fn(np.array([int(code, 16)]))[0] == val, code
+    nan = {int(c, 16) for c in g["nan_codes"]}
+    vals = om.decode_e4m3fn(np.arange(256))
+    assert set(np.nonzero(np.isnan(vals))[0].tolist()) == nan
+    assert np.nanmax(vals) == 448.0 and np.nanmin(vals) == -448.0
+
+
+def test_bf16_decode_exhaustive_vs_torch():
+    bits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    mine = om.decode_bf16(bits)
+    ref = torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).to(
+        torch.float64).numpy()
+    assert np.array_equal(np.isnan(mine), np.isnan(ref))
+    ok = ~np.isnan(ref)
+    assert np.array_equal(mine[ok], ref[ok])
+
+
+def test_dequant_applies_scale():
+    codes = np.arange(0, 0x7E, dtype=np.uint8)
+    assert np.array_equal(om.dequant(codes, "fp8_e4m3", 0.5), om.decode_e4m3fn(codes) * 0.5)
+
+
+# ---------------------------------------------------------------------------
+# page-fixed facts
+# ---------------------------------------------------------------------------
+
+def test_visible_pages_match_test_page_formula():
+    for c in golden()["visible_pages"]["cases"]:
+        s, ql = c["seq_len"], c["query_len"]
+        got = []
+        for loc in range(ql):
+            pos = om.token_position(s, ql, loc)
+            got.append(sum(1 for b in range(64) if om.visible_rows(pos, b) > 0))
+        assert got == c["pages"], c
+
+
+def test_generator_stride_and_scale_facts():
+    g = golden()
+    case = gen.make_p3_case(64, 4, 1, 1, seed=0, poison=False)
+    strides = [s // case.kv.itemsize for s in case.kv.strides]
+    assert strides == g["kv_cache_strides_hnd"]["num_kv_heads_4"]
+    assert case.sm_scale == g["sm_scale"]["value"]
+    case1 = gen.make_p3_case(16, 1, 1, 1, seed=0, poison=False)
+    assert [s // case1.kv.itemsize for s in case1.kv.strides] == \
+        g["kv_cache_strides_hnd"]["num_kv_heads_1"]
+
+
+# ---------------------------------------------------------------------------
+# attend == dense causal attention when every visible block is selected
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("dql", [1, 2, 3, 4, 8])
+@pytest.mark.parametrize("heads", [(16, 1), (8, 2)])
+@pytest.mark.parametrize("kv_dtype", [gen.KV_FP8, gen.KV_BF16])
+def test_dense_equivalence(dql, heads, kv_dtype):
+    case = small_dense_case(heads[0], heads[1], dql, kv_dtype)
+    assert dense_pin_error(case) < 1e-12
+
+
+@pytest.mark.parametrize("pattern", [(129, 385), (1, 128), (127, 130)])
+def test_dense_equivalence_boundaries(pattern):
+    case = small_dense_case(8, 2, 2 if min(pattern) > 1 else 1, pattern=pattern)
+    assert dense_pin_error(case) < 1e-12
+
+
+def test_dense_equivalence_with_scales():
+    case = small_dense_case(8, 2, 3, k_scale=0.5, v_scale=2.0)
+    assert dense_pin_error(case) < 1e-12
+
+
+# ---------------------------------------------------------------------------
+# closed forms
+# ---------------------------------------------------------------------------
+
+def _const_v_case(code):
+    case = small_dense_case(8, 2, 4)
+    kv = case.kv.copy()
+    kv[..., 128:] = code
+    case.kv = kv
+    return case
+
+
+def test_constant_v_gives_that_value():
+    code = 0x3C  # 1.5
+    case = _const_v_case(code)
+    case.v_scale = 2.0
+    # the tails past seq_len were overwritten too, but they must stay invisible:
+    out = run_oracle(case)
+    assert np.allclose(out, 3.0, rtol=0, atol=1e-12)
+
+
+def test_single_visible_key():
+    # dql = 1, seq = b*128 + 1: token position b*128 sees exactly one key of
+    # block b; selecting only block b gives that key's V.
+    case = gen.make_p3_case(16, 1, 1, 1, seq_pattern=(3 * 128 + 1,), seed=3)
+    topk = np.full_like(case.topk, -1)
+    topk[0, 0, 0] = 3
+    out = run_oracle(case, topk=topk)
+    p = case.block_table[0, 3]
+    v = torch_values(case.kv[p, 0, 0, 128:], case.kv_dtype).numpy() * case.v_scale
+    assert np.allclose(out[0], v[None, :], rtol=0, atol=1e-15)
+
+
+def test_seq_len_one():
+    case = gen.make_p3_case(16, 1, 1, 1, seq_pattern=(1,), seed=4)
+    out = run_oracle(case)
+    p = case.block_table[0, 0]
+    v = torch_values(case.kv[p, 0, 0, 128:], case.kv_dtype).numpy()
+    assert np.allclose(out[0], v[None, :], rtol=0, atol=1e-15)
+
+
+def _visible_v_mean(case, t, h, topk_row):
+    r, loc = divmod(t, case.dql)
+    pos = int(case.seq_lens[r]) - case.dql + loc
+    rows = []
+    for b in topk_row:
+        if b < 0 or b * 128 > pos:
+            continue
+        n = min(128, pos - b * 128 + 1)
+        p = case.block_table[r, b]
+        rows.append(torch_values(case.kv[p, h, :n, 128:], case.kv_dtype).numpy())
+    return np.concatenate(rows).mean(axis=0)
+
+
+def test_identical_keys_give_mean_of_v():
+    case = small_dense_case(8, 2, 3)
+    kv = case.kv.copy()
+    kv[..., :128] = 0x30  # every key row identical (0.5 in every entry)
+    case.kv = kv
+    out = run_oracle(case)
+    g = case.num_q_heads // case.num_kv_heads
+    for t in range(case.real_rows):
+        for j in range(case.num_q_heads):
+            ref = _visible_v_mean(case, t, j // g, case.topk[t, j // g])
+            assert np.allclose(out[t, j], ref, rtol=0, atol=1e-12)
+
+
+def test_zero_scale_gives_mean_of_v():
+    case = small_dense_case(16, 1, 2)
+    out = run_oracle(case, sm_scale=0.0)
+    for t in range(case.real_rows):
+        ref = _visible_v_mean(case, t, 0, case.topk[t, 0])
+        assert np.allclose(out[t], ref[None, :], rtol=0, atol=1e-12)
+
+
+def test_large_scale_picks_argmax_key():
+    case = small_dense_case(8, 2, 1, pattern=(200, 300))
+    scale = 1e4
+    out = run_oracle(case, sm_scale=scale)
+    vals = torch_values(case.kv, case.kv_dtype).numpy()
+    q = torch_q(case.q).numpy()
+    g = case.num_q_heads // case.num_kv_heads
+    checked = 0
+    for t in range(case.real_rows):
+        r = t // case.dql
+        s = int(case.seq_lens[r])
+        pages = case.block_table[r, :gen.pages_for(s)]
+        for j in range(case.num_q_heads):
+            h = j // g
+            seqkv = vals[pages, h].reshape(-1, 256)[:s]
+            logits = seqkv[:, :128] @ q[t, j]
+            order = np.argsort(-logits)
+            if (logits[order[0]] - logits[order[1]]) * scale < 60:
+                continue
+            assert np.allclose(out[t, j], seqkv[order[0], 128:], rtol=0, atol=1e-12)
+            checked += 1
+    assert checked > case.real_rows * case.num_q_heads // 2
+
+
+# ---------------------------------------------------------------------------
+# invariances and -1 handling
+# ---------------------------------------------------------------------------
+
+def _rand_case(**kw):
+    base = dict(seed=11, batch=3, dql=3, num_q_heads=8, num_kv_heads=2, topk_k=6,
+                seq_lo=300, seq_hi=1400)
+    base.update(kw)
+    return gen.make_random_case(**base)
+
+
+def test_topk_row_order_invariance():
+    case = _rand_case()
+    a = run_oracle(case)
+    rng = np.random.default_rng(0)
+    perm = case.topk.copy()
+    for t in range(perm.shape[0]):
+        for h in range(perm.shape[1]):
+            perm[t, h] = rng.permutation(perm[t, h])
+    b = run_oracle(case, topk=perm)
+    assert np.allclose(a, b, rtol=0, atol=1e-13)
+
+
+def test_inserting_minus_one_changes_nothing():
+    case = _rand_case()
+    a = run_oracle(case)
+    k = case.topk.shape[2]
+    wide = np.full((case.topk.shape[0], case.topk.shape[1], 2 * k), -1, np.int32)
+    rng = np.random.default_rng(1)
+    for t in range(wide.shape[0]):
+        for h in range(wide.shape[1]):
+            slots = np.sort(rng.choice(2 * k, size=k, replace=False))
+            wide[t, h, slots] = case.topk[t, h]
+    b = run_oracle(case, topk=wide)
+    assert np.array_equal(a, b)
+
+
+def test_physical_page_relabelling_invariance():
+    case = _rand_case()
+    a = run_oracle(case)
+    rng = np.random.default_rng(2)
+    perm = rng.permutation(case.num_blocks)
+    kv2 = np.empty_like(case.kv)
+    kv2[perm] = case.kv
+    bt2 = perm[case.block_table].astype(np.int32)
+    b = run_oracle(case, kv=kv2, block_table=bt2)
+    assert np.array_equal(a, b)
+
+
+def test_poison_outside_visible_rows_changes_nothing():
+    case = _rand_case()
+    clean = gen.make_random_case(seed=11, batch=3, dql=3, num_q_heads=8, num_kv_heads=2,
+                                 topk_k=6, seq_lo=300, seq_hi=1400, poison=False)
+    a = run_oracle(clean)
+    b = run_oracle(case)   # same draws, with NaN in tails and in the spare page
+    assert not np.isnan(b).any()
+    assert np.array_equal(a, b)
+
+
+def test_invisible_indices_change_nothing():
+    case = _rand_case(dql=4)
+    a = run_oracle(case)
+    k = case.topk.shape[2]
+    extra = np.concatenate([case.topk, np.full(case.topk.shape[:2] + (2,), -1, np.int32)],
+                           axis=2)
+    for t in range(case.real_rows):
+        r, loc = divmod(t, case.dql)
+        pos = int(case.seq_lens[r]) - case.dql + loc
+        extra[t, :, k] = pos // 128 + 1          # starts after pos
+        extra[t, :, k + 1] = pos // 128 + 40     # far beyond the table row
+    b = run_oracle(case, topk=extra)
+    assert np.array_equal(a, b)
+
+
+def test_all_minus_one_and_padding_rows_are_zero():
+    case = _rand_case(pad_rows=3)
+    topk = case.topk.copy()
+    topk[1] = -1
+    out = run_oracle(case, topk=topk)
+    assert np.all(out[1] == 0.0)
+    assert np.all(out[case.real_rows:] == 0.0)
+    assert np.all(np.abs(out[0]) > 0)
+
+
+def test_row_subset_matches_full():
+    case = _rand_case()
+    full = run_oracle(case)
+    sub = run_oracle(case, rows=[5, 2])
+    assert np.array_equal(sub, full[[5, 2]])
+
+
+# ---------------------------------------------------------------------------
+# scorer
+# ---------------------------------------------------------------------------
+
+def brute_scores(case, max_blocks):
+    """Triple loop over (h, b, t) and every (g, j) pair, torch-decoded K."""
+    vals = torch_values(case.kv, case.kv_dtype).numpy()
+    q = torch_q(case.q).numpy()
+    g = case.num_q_heads // case.num_kv_heads
+    out = np.full((case.num_kv_heads, max_blocks, case.real_rows), -np.inf)
+    for t in range(case.real_rows):
+        r, loc = divmod(t, case.dql)
+        pos = int(case.seq_lens[r]) - case.dql + loc
+        for h in range(case.num_kv_heads):
+            for b in range(max_blocks):
+                best = -np.inf
+                for key in range(b * 128, min(b * 128 + 128, pos + 1)):
+                    p = case.block_table[r, key // 128]
+                    krow = vals[p, h, key % 128, :128] * case.k_scale
+                    for gg in range(g):
+                        best = max(best, float(np.dot(q[t, h * g + gg], krow)))
+                out[h, b, t] = best
+    return out
+
+
+def run_scores(case, max_blocks=None, **over):
+    kw = dict(q_bits=case.q, kv=case.kv, kv_dtype=case.kv_dtype, k_scale=case.k_scale,
+              block_table=case.block_table, seq_lens=case.seq_lens,
+              decode_query_len=case.dql, num_kv_heads=case.num_kv_heads,
+              max_blocks=max_blocks or case.max_blocks)
+    kw.update(over)
+    return om.block_max_scores(**kw)
+
+
+@pytest.mark.parametrize("kv_dtype", [gen.KV_FP8, gen.KV_BF16])
+def test_scorer_brute_force(kv_dtype):
+    case = gen.make_random_case(seed=21, batch=2, dql=2, num_q_heads=4, num_kv_heads=2,
+                                topk_k=4, seq_lo=129, seq_hi=400, kv_dtype=kv_dtype)
+    case.k_scale = 0.5
+    mb = case.max_blocks + 1
+    a = run_scores(case, mb)
+    b = brute_scores(case, mb)
+    assert np.array_equal(np.isinf(a), np.isinf(b))
+    fin = np.isfinite(b)
+    assert np.allclose(a[fin], b[fin], rtol=1e-12, atol=1e-12)
+
+
+def test_scorer_one_hot_query():
+    case = gen.make_random_case(seed=22, batch=2, dql=1, num_q_heads=4, num_kv_heads=1,
+                                topk_k=4, seq_lo=200, seq_hi=600)
+    d = 37
+    q = np.zeros_like(case.q)
+    q[..., d] = gen.encode_bf16(np.array([1.0]))[0]
+    case.q = q
+    sc = run_scores(case)
+    vals = torch_values(case.kv, case.kv_dtype).numpy()
+    for t in range(case.real_rows):
+        pos = int(case.seq_lens[t]) - 1
+        for b in range(case.max_blocks):
+            if b * 128 > pos:
+                assert sc[0, b, t] == -np.inf
+                continue
+            n = min(128, pos - b * 128 + 1)
+            p = case.block_table[t, b]
+            assert sc[0, b, t] == vals[p, 0, :n, d].max()
+
+
+def test_scorer_zero_keys():
+    case = gen.make_random_case(seed=23, batch=2, dql=2, num_q_heads=4, num_kv_heads=2,
+                                topk_k=4, seq_lo=200, seq_hi=600, poison=False)
+    kv = case.kv.copy()
+    kv[..., :128] = 0
+    case.kv = kv
+    sc = run_scores(case)
+    for t in range(case.real_rows):
+        r, loc = divmod(t, case.dql)
+        pos = int(case.seq_lens[r]) - case.dql + loc
+        nvis = pos // 128 + 1
+        assert np.all(sc[:, :nvis, t] == 0.0)
+        assert np.all(sc[:, nvis:, t] == -np.inf)
+
+
+# ---------------------------------------------------------------------------
+# selector
+# ---------------------------------------------------------------------------
+
+def brute_topk(scores_1d, k):
+    remaining = [b for b in range(len(scores_1d)) if scores_1d[b] > -math.inf]
+    out = []
+    while remaining and len(out) < k:
+        best = remaining[0]
+        for b in remaining[1:]:
+            if scores_1d[b] > scores_1d[best]:
+                best = b   # strict: the earlier (lower) index wins ties
+        out.append(best)
+        remaining.remove(best)
+    return out + [-1] * (k - len(out))
+
+
+def test_select_topk_golden_example():
+    g = golden()["select_topk_example"]
+    s = np.array([float(x) for x in g["scores"]])[None, :, None]
+    got = om.select_topk(s, g["k"])
+    assert got[0, 0].tolist() == g["expected"]
+
+
+@pytest.mark.parametrize("tie_frac", [0.0, 0.3])
+def test_select_topk_brute_force(tie_frac):
+    seq = np.array([129, 700, 2000], dtype=np.int32)
+    sc = gen.make_scores(31, 2, 16, 6, seq, 2, tie_frac=tie_frac)
+    got = om.select_topk(sc, 5)
+    for h in range(2):
+        for t in range(6):
+            assert got[t, h].tolist() == brute_topk(sc[h, :, t].astype(np.float64), 5)
+
+
+def test_select_topk_pads_when_few_visible():
+    s = np.full((1, 8, 1), -np.inf)
+    s[0, 2, 0] = 1.0
+    s[0, 5, 0] = 1.0
+    assert om.select_topk(s, 4)[0, 0].tolist() == [2, 5, -1, -1]
+
+
+# ---------------------------------------------------------------------------
+# planted mistakes: each must trip at least one pin
+# ---------------------------------------------------------------------------
+
+MUTANTS = {
+    "visible_rows_off_by_one": ("visible_rows",
+                                lambda pos, b: 0 if b < 0 or b * 128 > pos
+                                else min(128, pos - b * 128)),
+    "causal_start_strict": ("visible_rows",
+                            lambda pos, b: 0 if b < 0 or b * 128 >= pos
+                            else min(128, pos - b * 128 + 1)),
+    "position_plus_one": ("token_position", lambda s, dql, loc: int(s) - int(dql) + int(loc) + 1),
+    "kv_head_modulo": ("kv_head_of", lambda j, g: j % 2),
+    "kv_swapped": ("split_kv", lambda raw: (raw[:, 128:], raw[:, :128])),
+    "no_sm_scale": ("softmax_attend",
+                    lambda qv, k, v, sc: (lambda z: (np.exp(z - z.max()) @ v)
+                                          / np.exp(z - z.max()).sum())(k @ qv)),
+    "scale_ignored": ("dequant", lambda raw, dt, scale: (
+        om._E4M3_TABLE[np.asarray(raw, dtype=np.uint8)] if dt == "fp8_e4m3"
+        else om.decode_bf16(raw))),
+}
+
+
+def _pins_pass():
+    cases = [small_dense_case(8, 2, 4), small_dense_case(8, 2, 1),
+             small_dense_case(8, 2, 3, k_scale=0.5, v_scale=2.0)]
+    return all(dense_pin_error(c) < 1e-12 for c in cases)
+
+
+def test_pins_pass_on_clean_oracle():
+    assert _pins_pass()
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_planted_mistake_is_caught(name, monkeypatch):
+    attr, fn = MUTANTS[name]
+    monkeypatch.setattr(om, attr, fn)
+    try:
+        ok = _pins_pass()
+    except (AssertionError, IndexError, ValueError):
+        ok = False
+    assert not ok, f"planted mistake {name} was not caught"
+
+
+def test_planted_scorer_mistakes_are_caught(monkeypatch):
+    case = gen.make_random_case(seed=24, batch=2, dql=2, num_q_heads=4, num_kv_heads=2,
+                                topk_k=4, seq_lo=129, seq_hi=400)
+    ref = brute_scores(case, case.max_blocks)
+    monkeypatch.setattr(om, "visible_rows",
+                        lambda pos, b: 0 if b < 0 or b * 128 > pos else 128)
+    with np.errstate(invalid="ignore"):
+        bad = run_scores(case)
+    assert not np.array_equal(np.nan_to_num(bad), np.nan_to_num(ref))
+
+
+def test_planted_selector_mistake_is_caught():
+    g = golden()["select_topk_example"]
+    s = np.array([float(x) for x in g["scores"]])
+    # reversed tie rule: higher block id first among equal scores
+    cand = [b for b in range(len(s)) if s[b] > -math.inf]
+    cand.sort(key=lambda b: (-s[b], -b))
+    assert cand[: g["k"]] != g["expected"]

@@ -1,0 +1,468 @@
+"""Seeded synthetic inputs for block-sparse GQA decode.
+
+This module is shared by the float64 oracle tests and by the HIP path tests and
+bench.  It holds none of the method's arithmetic: only random draws (NumPy
+PCG64), page-table construction, index-list construction and the encoding of
+drawn values into bf16 / OCP fp8 e4m3fn bit patterns (done by torch's CPU
+casts, round-to-nearest-even).
+
+Shapes and structure follow the workloads the pages describe:
+
+* KV cache: vLLM API page ``vllm.models.minimax_m3.common.sparse_attention``,
+  ``MiniMaxM3SparseBackend.get_kv_cache_shape`` -- logical
+  ``(num_blocks, num_kv_heads, block_size=128, 2*head_size)`` with K in the
+  first 128 entries of the last dim and V in the last 128, HND stride order.
+* Paged layout over a shuffled physical pool and the "every visible page"
+  index pattern: vLLM test file
+  ``test_minimax_m3_msa_cutlass_sparse_decode.py``, helpers
+  ``_make_paged_layout`` and ``_make_topk``.
+* Token row ``t = request * dql + local`` at position
+  ``seq_len - dql + local`` (same test file, ``_make_topk``).
+
+Every array is plain NumPy: fp8 codes as ``uint8``, bf16 as ``uint16`` bit
+patterns, indices as ``int32``.
+"""
+from __future__ import annotations
+
+import math
+from dataclasses import dataclass, field
+
+import numpy as np
+
+PAGE = 128
+HEAD_DIM = 128
+FP8_MAX = 448.0
+BF16_NAN_BITS = 0x7FC0
+FP8_NAN_CODE = 0x7F
+
+KV_FP8 = "fp8_e4m3"
+KV_BF16 = "bf16"
+
+
+# ---------------------------------------------------------------------------
+# encoders (torch CPU casts; no attention arithmetic)
+# ---------------------------------------------------------------------------
+
+def encode_bf16(x: np.ndarray) -> np.ndarray:
+    """float array -> bf16 bit patterns (uint16), round-to-nearest-even."""
+    import torch
+
+    t = torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32))
+    return t.to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16).copy()
+
+
+def encode_e4m3fn(x: np.ndarray) -> np.ndarray:
+    """float array -> OCP fp8 e4m3fn codes (uint8), clipped to +-448 first."""
+    import torch
+
+    t = torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32))
+    t = t.clamp(-FP8_MAX, FP8_MAX)
+    return t.to(torch.float8_e4m3fn).view(torch.uint8).numpy().copy()
+
+
+def _normal_f32(rng: np.random.Generator, shape, std: float) -> np.ndarray:
+    x = rng.standard_normal(size=shape, dtype=np.float32)
+    if std != 1.0:
+        x *= np.float32(std)
+    return x
+
+
+def _encode(x: np.ndarray, kv_dtype: str) -> np.ndarray:
+    return encode_e4m3fn(x) if kv_dtype == KV_FP8 else encode_bf16(x)
+
+
+# ---------------------------------------------------------------------------
+# case container
+# ---------------------------------------------------------------------------
+
+@dataclass
+class DecodeCase:
+    """One decode step's inputs (optionally with extra (q, topk) replicas)."""
+
+    name: str
+    seed: int
+    batch: int
+    dql: int
+    num_token_rows: int
+    num_q_heads: int
+    num_kv_heads: int
+    topk_k: int
+    kv_dtype: str
+    seq_lens: np.ndarray           # int32 [batch]
+    block_table: np.ndarray        # int32 [batch, stride]
+    kv: np.ndarray                 # uint8 / uint16 [num_blocks, Hkv, 128, 256]
+    q: np.ndarray                  # uint16 bf16 bits [rows, Hq, 128]
+    topk: np.ndarray | None        # int32 [rows, Hkv, k] logical block ids, -1 pad
+    sm_scale: float = HEAD_DIM ** -0.5
+    k_scale: float = 1.0
+    v_scale: float = 1.0
+    max_blocks: int = 0            # ceil(max seq / 128)
+    replicas: list = field(default_factory=list)   # [(q, topk)] extra sets
+    notes: str = ""
+
+    @property
+    def num_blocks(self) -> int:
+        return int(self.kv.shape[0])
+
+    @property
+    def real_rows(self) -> int:
+        return self.batch * self.dql
+
+    def positions(self) -> np.ndarray:
+        """pos[t] for the real token rows (0-based absolute position)."""
+        r = np.arange(self.real_rows) // self.dql
+        loc = np.arange(self.real_rows) % self.dql
+        return self.seq_lens[r].astype(np.int64) - self.dql + loc
+
+
+# ---------------------------------------------------------------------------
+# page tables and index lists
+# ---------------------------------------------------------------------------
+
+def pages_for(seq_len: int) -> int:
+    return (int(seq_len) + PAGE - 1) // PAGE
+
+
+def paged_layout(rng: np.random.Generator, seq_lens, spare_pages: int = 0,
+                 fill_page: int | None = None):
+    """Block table over a shuffled physical pool (like ``_make_paged_layout``).
+
+    Returns (block_table int32 [B, max_pages], num_pages, spare_ids).  Spare
+    pages are extra physical pages no request owns; unused table entries point
+    at ``fill_page`` (default: the first spare page if any, else 0).
+    """
+    per = [pages_for(s) for s in seq_lens]
+    used = int(sum(per))
+    total = used + spare_pages
+    perm = rng.permutation(total).astype(np.int32)
+    owned, spare = perm[:used], perm[used:]
+    if fill_page is None:
+        fill_page = int(spare[0]) if spare_pages else 0
+    bt = np.full((len(seq_lens), max(per)), fill_page, dtype=np.int32)
+    off = 0
+    for r, n in enumerate(per):
+        bt[r, :n] = owned[off:off + n]
+        off += n
+    return bt, total, spare
+
+
+def last_visible_block(pos: int) -> int:
+    return int(pos) // PAGE
+
+
+def pick_uniform(rng: np.random.Generator, last: int, k: int) -> np.ndarray:
+    """k distinct blocks from [0, last], always including ``last``, shuffled."""
+    n = last + 1
+    if n <= k:
+        sel = np.arange(n, dtype=np.int64)
+    else:
+        others = rng.choice(last, size=k - 1, replace=False)
+        sel = np.concatenate([others, [last]])
+    return rng.permutation(sel).astype(np.int32)
+
+
+def pick_zipf_recent(rng: np.random.Generator, last: int, k: int) -> np.ndarray:
+    """``last`` plus k-1 distinct earlier blocks with weight 1/(last-b)."""
+    if last + 1 <= k:
+        return rng.permutation(np.arange(last + 1)).astype(np.int32)
+    d = np.arange(last, 0, -1, dtype=np.float64)   # distance of block b=0..last-1
+    w = 1.0 / d
+    w /= w.sum()
+    others = rng.choice(last, size=k - 1, replace=False, p=w)
+    sel = np.concatenate([others, [last]])
+    return rng.permutation(sel).astype(np.int32)
+
+
+def pad_row(sel: np.ndarray, k: int) -> np.ndarray:
+    out = np.full(k, -1, dtype=np.int32)
+    out[: len(sel)] = sel[:k]
+    return out
+
+
+def every_visible_topk(seq_lens, num_kv_heads: int, dql: int, k: int) -> np.ndarray:
+    """The ``_make_topk`` pattern: ascending 0..visible_pages-1, then -1."""
+    rows = len(seq_lens) * dql
+    topk = np.full((rows, num_kv_heads, k), -1, dtype=np.int32)
+    for r, s in enumerate(seq_lens):
+        for loc in range(dql):
+            t = r * dql + loc
+            visible_tokens = int(s) - dql + loc + 1
+            vp = math.ceil(visible_tokens / PAGE)
+            vp = max(0, min(vp, k))
+            topk[t, :, :vp] = np.arange(vp, dtype=np.int32)
+    return topk
+
+
+def poison_tail_slots(kv: np.ndarray, block_table, seq_lens, kv_dtype: str) -> None:
+    """Write NaN patterns into the slots past seq_len of every last page."""
+    bad = FP8_NAN_CODE if kv_dtype == KV_FP8 else BF16_NAN_BITS
+    for r, s in enumerate(seq_lens):
+        n = pages_for(s)
+        used = int(s) - (n - 1) * PAGE
+        if used < PAGE:
+            kv[block_table[r, n - 1], :, used:, :] = bad
+
+
+def fill_pages(kv: np.ndarray, pages, kv_dtype: str) -> None:
+    bad = FP8_NAN_CODE if kv_dtype == KV_FP8 else BF16_NAN_BITS
+    for p in pages:
+        kv[int(p)] = bad
+
+
+def make_pool(rng: np.random.Generator, num_pages: int, num_kv_heads: int,
+              kv_dtype: str, std: float, chunk_pages: int = 512) -> np.ndarray:
+    """Packed K|V pool ``(num_pages, Hkv, 128, 256)``; values N(0, std) encoded."""
+    dt = np.uint8 if kv_dtype == KV_FP8 else np.uint16
+    kv = np.empty((num_pages, num_kv_heads, PAGE, 2 * HEAD_DIM), dtype=dt)
+    for p0 in range(0, num_pages, chunk_pages):
+        p1 = min(num_pages, p0 + chunk_pages)
+        x = _normal_f32(rng, (p1 - p0, num_kv_heads, PAGE, 2 * HEAD_DIM), std)
+        kv[p0:p1] = _encode(x, kv_dtype)
+    return kv
+
+
+def make_q(rng: np.random.Generator, rows: int, num_q_heads: int, std: float = 1.0):
+    return encode_bf16(_normal_f32(rng, (rows, num_q_heads, HEAD_DIM), std))
+
+
+# ---------------------------------------------------------------------------
+# the named workloads
+# ---------------------------------------------------------------------------
+
+CONFIG_NAMES = ("c1_tiny_bf16", "c2_tp4_fp8", "c3_tp1_fp8", "c4_spec_ragged",
+                "c5_full_step")
+
+
+def _topk_rows(rng, seq_lens, dql, hkv, k, rule, per_head, pad_rows=0):
+    rows = len(seq_lens) * dql
+    topk = np.full((rows + pad_rows, hkv, k), -1, dtype=np.int32)
+    for r, s in enumerate(seq_lens):
+        for loc in range(dql):
+            t = r * dql + loc
+            pos = int(s) - dql + loc
+            last = last_visible_block(pos)
+            if per_head:
+                for h in range(hkv):
+                    topk[t, h] = pad_row(rule(r, last), k)
+            else:
+                topk[t, :] = pad_row(rule(r, last), k)
+    return topk
+
+
+def make_config(name: str, replicas: int = 0, poison: bool = True) -> DecodeCase:
+    """Build one of the five named workloads (seeded 1..5)."""
+    if name == "c1_tiny_bf16":
+        return _make_c1(replicas, poison)
+    if name == "c2_tp4_fp8":
+        return _make_c2(replicas, poison)
+    if name == "c3_tp1_fp8":
+        return _make_c3(replicas, poison)
+    if name == "c4_spec_ragged":
+        return _make_c4(replicas, poison)
+    if name == "c5_full_step":
+        return _make_c5(replicas, poison)
+    raise KeyError(name)
+
+
+def _make_c1(replicas: int, poison: bool) -> DecodeCase:
+    rng = np.random.default_rng(1)
+    seq = np.array([512, 1000], dtype=np.int32)
+    bt, total, spare = paged_layout(rng, seq, spare_pages=4)
+    assert total == 16
+    kv = make_pool(rng, total, 1, KV_BF16, 1.0)
+    if poison:
+        fill_pages(kv, spare, KV_BF16)
+        poison_tail_slots(kv, bt, seq, KV_BF16)
+
+    def one(rng_):
+        q = make_q(rng_, 2, 16)
+        topk = _topk_rows(rng_, seq, 1, 1, 4,
+                          lambda r, last: pick_uniform(rng_, last, 4), False)
+        return q, topk
+
+    q, topk = one(rng)
+    reps = [one(rng) for _ in range(replicas)]
+    return DecodeCase("c1_tiny_bf16", 1, 2, 1, 2, 16, 1, 4, KV_BF16, seq, bt, kv,
+                      q, topk, max_blocks=int(bt.shape[1]), replicas=reps)
+
+
+def _make_c2(replicas: int, poison: bool) -> DecodeCase:
+    rng = np.random.default_rng(2)
+    B, dql, hq, hkv, k = 32, 4, 16, 1, 16
+    seq = rng.integers(16384, 65536, size=B, endpoint=True).astype(np.int32)
+    bt, total, spare = paged_layout(rng, seq, spare_pages=1)
+    kv = make_pool(rng, total, hkv, KV_FP8, 0.5)
+    if poison:
+        fill_pages(kv, spare, KV_FP8)
+        poison_tail_slots(kv, bt, seq, KV_FP8)
+
+    def one(rng_):
+        q = make_q(rng_, B * dql, hq)
+        topk = _topk_rows(rng_, seq, dql, hkv, k,
+                          lambda r, last: pick_uniform(rng_, last, k), False)
+        return q, topk
+
+    q, topk = one(rng)
+    reps = [one(rng) for _ in range(replicas)]
+    return DecodeCase("c2_tp4_fp8", 2, B, dql, B * dql, hq, hkv, k, KV_FP8, seq, bt,
+                      kv, q, topk, max_blocks=int(bt.shape[1]), replicas=reps)
+
+
+def _make_c3(replicas: int, poison: bool) -> DecodeCase:
+    rng = np.random.default_rng(3)
+    B, dql, hq, hkv, k = 16, 4, 64, 4, 16
+    seq = rng.integers(32768, 131072, size=B, endpoint=True).astype(np.int32)
+    bt, total, spare = paged_layout(rng, seq, spare_pages=1)
+    kv = make_pool(rng, total, hkv, KV_FP8, 0.5)
+    if poison:
+        fill_pages(kv, spare, KV_FP8)
+        poison_tail_slots(kv, bt, seq, KV_FP8)
+
+    def one(rng_):
+        q = make_q(rng_, B * dql, hq)
+        topk = _topk_rows(rng_, seq, dql, hkv, k,
+                          lambda r, last: pick_zipf_recent(rng_, last, k), True)
+        return q, topk
+
+    q, topk = one(rng)
+    reps = [one(rng) for _ in range(replicas)]
+    return DecodeCase("c3_tp1_fp8", 3, B, dql, B * dql, hq, hkv, k, KV_FP8, seq, bt,
+                      kv, q, topk, max_blocks=int(bt.shape[1]), replicas=reps)
+
+
+def _make_c4(replicas: int, poison: bool) -> DecodeCase:
+    rng = np.random.default_rng(4)
+    B, dql, hq, hkv, k, pad = 16, 32, 64, 4, 16, 4
+    long_ids = np.sort(rng.permutation(B)[: B // 2])
+    seq = np.empty(B, dtype=np.int32)
+    for r in range(B):
+        seq[r] = 131072 if r in long_ids else int(rng.integers(200, 1900, endpoint=True))
+    bt, total, spare = paged_layout(rng, seq, spare_pages=1)
+    kv = make_pool(rng, total, hkv, KV_FP8, 0.5)
+    if poison:
+        fill_pages(kv, spare, KV_FP8)
+        poison_tail_slots(kv, bt, seq, KV_FP8)
+    is_long = np.isin(np.arange(B), long_ids)
+
+    def rule(rng_):
+        def f(r, last):
+            if is_long[r]:
+                return pick_zipf_recent(rng_, last, k)
+            return rng_.permutation(np.arange(last + 1)).astype(np.int32)
+        return f
+
+    def one(rng_):
+        q = make_q(rng_, B * dql + pad, hq)
+        topk = _topk_rows(rng_, seq, dql, hkv, k, rule(rng_), True, pad_rows=pad)
+        return q, topk
+
+    q, topk = one(rng)
+    reps = [one(rng) for _ in range(replicas)]
+    return DecodeCase("c4_spec_ragged", 4, B, dql, B * dql + pad, hq, hkv, k, KV_FP8,
+                      seq, bt, kv, q, topk, max_blocks=int(bt.shape[1]), replicas=reps,
+                      notes="rows 512..515 are padding rows")
+
+
+def c5_seq_lens(rng: np.random.Generator, B: int = 64) -> np.ndarray:
+    mu = math.log(math.sqrt(8192.0 * 262144.0))
+    sigma = math.log(32.0) / 4.0
+    s = np.exp(rng.normal(mu, sigma, size=B))
+    return np.clip(np.rint(s), 8192, 262144).astype(np.int32)
+
+
+def _make_c5(replicas: int, poison: bool) -> DecodeCase:
+    rng = np.random.default_rng(5)
+    B, dql, hq, hkv, k = 64, 1, 64, 4, 16
+    seq = c5_seq_lens(rng, B)
+    bt, total, spare = paged_layout(rng, seq, spare_pages=1)
+    kv = make_pool(rng, total, hkv, KV_FP8, 0.5)
+    if poison:
+        fill_pages(kv, spare, KV_FP8)
+        poison_tail_slots(kv, bt, seq, KV_FP8)
+    q = make_q(rng, B, hq)
+    reps = [(make_q(rng, B, hq), None) for _ in range(replicas)]
+    return DecodeCase("c5_full_step", 5, B, dql, B, hq, hkv, k, KV_FP8, seq, bt, kv, q,
+                      None, max_blocks=int(bt.shape[1]), replicas=reps,
+                      notes="top-k comes from the block-max scorer and selector")
+
+
+# ---------------------------------------------------------------------------
+# small cases for parity and oracle pins
+# ---------------------------------------------------------------------------
+
+def make_p3_case(num_q_heads: int, num_kv_heads: int, pairs: int, dql: int,
+                 seq_pattern=(257, 513), seed: int = 0, kv_dtype: str = KV_FP8,
+                 std: float = 0.25, topk_k: int = 16, poison: bool = True) -> DecodeCase:
+    """The test page's parity shape: seq_lens = pattern * pairs, every visible
+    page selected (``_make_topk``), K and V ~ N(0, std) encoded, Q ~ N(0,1)."""
+    rng = np.random.default_rng(1000 + seed)
+    seq = np.array(list(seq_pattern) * pairs, dtype=np.int32)
+    bt, total, spare = paged_layout(rng, seq, spare_pages=1)
+    kv = make_pool(rng, total, num_kv_heads, kv_dtype, std)
+    if poison:
+        fill_pages(kv, spare, kv_dtype)
+        poison_tail_slots(kv, bt, seq, kv_dtype)
+    rows = len(seq) * dql
+    q = make_q(rng, rows, num_q_heads)
+    topk = every_visible_topk(seq, num_kv_heads, dql, topk_k)
+    return DecodeCase(f"p3_h{num_q_heads}_{num_kv_heads}_pairs{pairs}_dql{dql}", seed,
+                      len(seq), dql, rows, num_q_heads, num_kv_heads, topk_k, kv_dtype,
+                      seq, bt, kv, q, topk, max_blocks=int(bt.shape[1]))
+
+
+def make_random_case(seed: int, batch: int, dql: int, num_q_heads: int,
+                     num_kv_heads: int, topk_k: int, seq_lo: int, seq_hi: int,
+                     kv_dtype: str = KV_FP8, std: float = 0.5, pad_rows: int = 0,
+                     per_head: bool = True, rule: str = "uniform",
+                     neg_frac: float = 0.0, poison: bool = True,
+                     stride_extra: int = 0) -> DecodeCase:
+    """A generic seeded case: uniform seq lens, random distinct blocks that
+    include each token's causal last block, optional extra -1 entries."""
+    rng = np.random.default_rng(seed)
+    seq = rng.integers(seq_lo, seq_hi, size=batch, endpoint=True).astype(np.int32)
+    bt, total, spare = paged_layout(rng, seq, spare_pages=1)
+    if stride_extra:
+        bt = np.concatenate(
+            [bt, np.full((batch, stride_extra), bt[0, 0], dtype=np.int32)], axis=1)
+    kv = make_pool(rng, total, num_kv_heads, kv_dtype, std)
+    if poison:
+        fill_pages(kv, spare, kv_dtype)
+        poison_tail_slots(kv, bt, seq, kv_dtype)
+    rows = batch * dql
+    q = make_q(rng, rows + pad_rows, num_q_heads)
+    pick = pick_uniform if rule == "uniform" else pick_zipf_recent
+    topk = _topk_rows(rng, seq, dql, num_kv_heads, topk_k,
+                      lambda r, last: pick(rng, last, topk_k), per_head,
+                      pad_rows=pad_rows)
+    if neg_frac > 0:
+        mask = rng.random(topk.shape) < neg_frac
+        topk[mask] = -1
+    return DecodeCase(f"rand_s{seed}", seed, batch, dql, rows + pad_rows, num_q_heads,
+                      num_kv_heads, topk_k, kv_dtype, seq, bt, kv, q, topk,
+                      max_blocks=int(bt.shape[1]))
+
+
+def make_scores(seed: int, num_kv_heads: int, max_blocks: int, rows: int, seq_lens,
+                dql: int, tie_frac: float = 0.0) -> np.ndarray:
+    """fp32 score buffer [Hkv, max_blocks, rows] for selector tests: N(0,1)
+    values for causally visible blocks, -inf elsewhere; optionally with
+    planted exact ties (copied values)."""
+    rng = np.random.default_rng(seed)
+    s = rng.standard_normal((num_kv_heads, max_blocks, rows)).astype(np.float32)
+    for r, sl in enumerate(seq_lens):
+        for loc in range(dql):
+            t = r * dql + loc
+            pos = int(sl) - dql + loc
+            nvis = pos // PAGE + 1 if pos >= 0 else 0
+            s[:, nvis:, t] = -np.inf
+    if tie_frac > 0:
+        for h in range(num_kv_heads):
+            for t in range(rows):
+                fin = np.nonzero(np.isfinite(s[h, :, t]))[0]
+                if len(fin) < 2:
+                    continue
+                n = max(1, int(tie_frac * len(fin)))
+                src = rng.choice(fin, size=n)
+                dst = rng.choice(fin, size=n)
+                s[h, dst, t] = s[h, src, t]
+    return s
