@@ -1,0 +1,343 @@
+"""Block-sparse GQA decode attention for MI355X (gfx950).
+
+Python binding over ``libmsa_decode.so`` (C ABI: ``include/msa_sparse_decode.h``).
+This module only marshals arguments: every step of the decode path runs in the
+library's HIP kernels, and there is no fallback.  If the library is not built,
+every call raises.
+
+Entry points carry the C names:
+
+* ``msa_sparse_decode_plan``  -- validate a static shape, build a plan (with its
+  persistent split-K arena); ``PlanCache`` keys plans like the plan cache of the
+  vLLM API page ``vllm.models.minimax_m3.nvidia.msa_cutlass_sparse_decode``
+  (``MSACutlassDecodePlanCache.prepare``).
+* ``msa_sparse_decode_run``   -- one sparse decode step (the attend).
+* ``msa_block_score_topk``    -- indexer block-max scores, then the top-k.
+* ``msa_topk_select``         -- the top-k selector alone.
+* ``msa_fp8_e4m3_to_bf16``    -- the in-register fp8 conversion, as a check.
+
+Tensor checks follow ``MSACutlassDecodePlanCache.prepare`` (contiguous int32
+block table with one row per request, contiguous int32 sequence lengths on the
+same device) and the backend contract of the vLLM API page
+``vllm.models.minimax_m3.common.sparse_attention`` (head size 128, page size
+128, bf16 or fp8 e4m3 KV in a packed ``(num_blocks, Hkv, 128, 256)`` cache).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import torch
+
+__all__ = [
+    "MsaError", "MsaInvalidArgument", "MsaUnsupported", "DecodePlan", "PlanCache",
+    "msa_sparse_decode_plan", "msa_sparse_decode_run", "msa_block_score_topk",
+    "msa_topk_select", "msa_fp8_e4m3_to_bf16", "library_path", "load_library",
+    "KV_BF16", "KV_FP8_E4M3", "PAGE_SIZE", "HEAD_DIM",
+]
+
+PAGE_SIZE = 128
+HEAD_DIM = 128
+KV_BF16 = 0
+KV_FP8_E4M3 = 1
+
+MSA_OK = 0
+MSA_ERR_INVALID_ARG = -1
+MSA_ERR_UNSUPPORTED = -2
+MSA_ERR_DEVICE = -3
+MSA_ERR_OUT_OF_MEMORY = -4
+
+_PKG_DIR = os.path.dirname(os.path.abspath(__file__))
+_LIB_NAME = "libmsa_decode.so"
+
+
+class MsaError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"[msa status {status}] {message}")
+        self.status = status
+
+
+class MsaInvalidArgument(MsaError, ValueError):
+    pass
+
+
+class MsaUnsupported(MsaError, NotImplementedError):
+    pass
+
+
+class _Shape(ctypes.Structure):
+    _fields_ = [(name, ctypes.c_int32) for name in (
+        "batch", "decode_query_len", "num_token_rows", "page_table_stride",
+        "num_q_heads", "num_kv_heads", "page_size", "head_dim", "topk_blocks",
+        "kv_dtype", "num_splits")]
+
+
+_I64x4 = ctypes.c_int64 * 4
+_I64x3 = ctypes.c_int64 * 3
+_LIB = None
+
+
+def library_path() -> str:
+    return os.path.join(_PKG_DIR, _LIB_NAME)
+
+
+def load_library():
+    """Load the built HIP library (raises if it is missing)."""
+    global _LIB
+    if _LIB is not None:
+        return _LIB
+    path = library_path()
+    if not os.path.exists(path):
+        raise RuntimeError(
+            f"{path} is not built: run `python -c 'import __graft_entry__ as g; g.build()'` "
+            "or `python -m block_sparse_gqa_decode_amd.build_lib`")
+    lib = ctypes.CDLL(path)
+    vp, i32, i64, f32 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_float
+    pi64 = ctypes.POINTER(ctypes.c_int64)
+    sig = {
+        "msa_sparse_decode_plan": (i32, [ctypes.POINTER(_Shape), ctypes.c_int,
+                                         ctypes.POINTER(vp)]),
+        "msa_sparse_decode_plan_destroy": (i32, [vp]),
+        "msa_sparse_decode_plan_info": (i32, [vp, ctypes.POINTER(i32), ctypes.POINTER(i64),
+                                              ctypes.POINTER(_Shape)]),
+        "msa_sparse_decode_run": (i32, [vp, vp, vp, pi64, i64, f32, f32, vp, vp, vp,
+                                        pi64, vp, f32, vp]),
+        "msa_block_score_topk": (i32, [ctypes.POINTER(_Shape), vp, vp, pi64, i64, f32,
+                                       vp, vp, i32, vp, pi64, vp, i32, vp]),
+        "msa_topk_select": (i32, [vp, pi64, i32, i32, i32, vp, i32, vp]),
+        "msa_fp8_e4m3_to_bf16": (i32, [vp, vp, i64, vp]),
+        "msa_last_error": (ctypes.c_char_p, []),
+        "msa_abi_version": (i32, []),
+    }
+    for name, (res, args) in sig.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    _LIB = lib
+    return lib
+
+
+def _check(status: int):
+    if status == MSA_OK:
+        return
+    msg = load_library().msa_last_error().decode(errors="replace")
+    if status == MSA_ERR_INVALID_ARG:
+        raise MsaInvalidArgument(status, msg)
+    if status == MSA_ERR_UNSUPPORTED:
+        raise MsaUnsupported(status, msg)
+    raise MsaError(status, msg)
+
+
+def _stream_handle(stream, device) -> Optional[int]:
+    if stream is None:
+        return torch.cuda.current_stream(device).cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def _kv_dtype_of(kv: torch.Tensor) -> int:
+    if kv.dtype in (torch.uint8, torch.float8_e4m3fn):
+        return KV_FP8_E4M3
+    if kv.dtype == torch.bfloat16:
+        return KV_BF16
+    raise ValueError(f"unsupported kv cache dtype {kv.dtype}: expected uint8/float8_e4m3fn "
+                     "(fp8 e4m3) or bfloat16")
+
+
+def _check_kv(kv: torch.Tensor, num_kv_heads: int):
+    if kv.device.type != "cuda":
+        raise ValueError("kv_cache must be a device tensor")
+    if kv.dim() != 4 or kv.shape[1] != num_kv_heads or kv.shape[2] != PAGE_SIZE \
+            or kv.shape[3] != 2 * HEAD_DIM:
+        raise ValueError(f"kv_cache must be logically (num_blocks, {num_kv_heads}, 128, 256), "
+                         f"got {tuple(kv.shape)}")
+    if kv.stride(3) != 1:
+        raise ValueError("kv_cache last dimension must be contiguous")
+
+
+def _check_tables(block_table: torch.Tensor, seq_lens: torch.Tensor, batch: int):
+    if (block_table.device.type != "cuda" or block_table.dtype != torch.int32
+            or not block_table.is_contiguous() or block_table.dim() != 2
+            or block_table.shape[0] != batch):
+        raise ValueError("MSA sparse decode requires a contiguous device int32 block "
+                         "table with one row per request")
+    if (seq_lens.dtype != torch.int32 or not seq_lens.is_contiguous()
+            or seq_lens.device != block_table.device or seq_lens.shape != (batch,)):
+        raise ValueError("MSA sparse decode requires contiguous device int32 sequence "
+                         "lengths on the block table device")
+
+
+def _check_q(q: torch.Tensor, name: str, rows: int, hq: int):
+    if q.device.type != "cuda" or q.dtype != torch.bfloat16 or not q.is_contiguous():
+        raise ValueError(f"{name} must be a contiguous device bfloat16 tensor")
+    if tuple(q.shape) != (rows, hq, HEAD_DIM):
+        raise ValueError(f"{name} must have shape ({rows}, {hq}, {HEAD_DIM}), "
+                         f"got {tuple(q.shape)}")
+
+
+class DecodePlan:
+    """A validated static shape plus the library plan (owns the split-K arena)."""
+
+    def __init__(self, handle: int, device: int):
+        self._handle = ctypes.c_void_p(handle)
+        self.device = device
+        splits = ctypes.c_int32()
+        arena = ctypes.c_int64()
+        shape = _Shape()
+        _check(load_library().msa_sparse_decode_plan_info(
+            self._handle, ctypes.byref(splits), ctypes.byref(arena), ctypes.byref(shape)))
+        self.batch = shape.batch
+        self.decode_query_len = shape.decode_query_len
+        self.num_token_rows = shape.num_token_rows
+        self.page_table_stride = shape.page_table_stride
+        self.num_q_heads = shape.num_q_heads
+        self.num_kv_heads = shape.num_kv_heads
+        self.topk_blocks = shape.topk_blocks
+        self.kv_dtype = shape.kv_dtype
+        self.num_splits = splits.value
+        self.arena_bytes = arena.value
+
+    @property
+    def handle(self):
+        return self._handle
+
+    def close(self):
+        if self._handle is not None and self._handle.value:
+            _check(load_library().msa_sparse_decode_plan_destroy(self._handle))
+        self._handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+def msa_sparse_decode_plan(batch: int, decode_query_len: int, *, num_q_heads: int,
+                           num_kv_heads: int, page_table_stride: int, topk_blocks: int,
+                           kv_dtype: int, num_token_rows: int = 0, num_splits: int = 0,
+                           page_size: int = PAGE_SIZE, head_dim: int = HEAD_DIM,
+                           device=None) -> DecodePlan:
+    lib = load_library()
+    shape = _Shape(batch, decode_query_len, num_token_rows, page_table_stride, num_q_heads,
+                   num_kv_heads, page_size, head_dim, topk_blocks, kv_dtype, num_splits)
+    if device is None:
+        dev = torch.cuda.current_device() if torch.cuda.is_available() else 0
+    elif isinstance(device, int):
+        dev = device
+    else:
+        dev = torch.device(device).index
+        if dev is None:
+            dev = torch.cuda.current_device()
+    handle = ctypes.c_void_p()
+    _check(lib.msa_sparse_decode_plan(ctypes.byref(shape), int(dev), ctypes.byref(handle)))
+    return DecodePlan(handle.value, int(dev))
+
+
+def msa_sparse_decode_run(plan: DecodePlan, q: torch.Tensor, kv_cache: torch.Tensor,
+                          block_table: torch.Tensor, seq_lens: torch.Tensor,
+                          topk: torch.Tensor, out: torch.Tensor, *, sm_scale: float,
+                          k_scale: float = 1.0, v_scale: float = 1.0, stream=None) -> None:
+    """out[t, j] = sparse causal attention of q[t, j] over the selected pages."""
+    rows = plan.num_token_rows
+    _check_q(q, "q", rows, plan.num_q_heads)
+    _check_q(out, "out", rows, plan.num_q_heads)
+    _check_kv(kv_cache, plan.num_kv_heads)
+    if _kv_dtype_of(kv_cache) != plan.kv_dtype:
+        raise ValueError("kv_cache dtype does not match the plan's kv_dtype")
+    _check_tables(block_table, seq_lens, plan.batch)
+    if block_table.stride(0) != plan.page_table_stride:
+        raise ValueError("block_table row stride does not match the plan")
+    if (topk.dtype != torch.int32 or topk.dim() != 3
+            or tuple(topk.shape) != (rows, plan.num_kv_heads, plan.topk_blocks)):
+        raise ValueError(f"topk must be int32 [{rows}, {plan.num_kv_heads}, "
+                         f"{plan.topk_blocks}], got {topk.dtype} {tuple(topk.shape)}")
+    for name, t in (("kv_cache", kv_cache), ("block_table", block_table), ("topk", topk),
+                    ("q", q), ("out", out)):
+        if t.device != seq_lens.device:
+            raise ValueError(f"{name} is not on the sequence-length device")
+    kvs = _I64x4(*kv_cache.stride())
+    tks = _I64x3(*topk.stride())
+    _check(load_library().msa_sparse_decode_run(
+        plan.handle, q.data_ptr(), kv_cache.data_ptr(), kvs, kv_cache.shape[0],
+        float(k_scale), float(v_scale), block_table.data_ptr(), seq_lens.data_ptr(),
+        topk.data_ptr(), tks, out.data_ptr(), float(sm_scale),
+        _stream_handle(stream, q.device)))
+
+
+def msa_block_score_topk(q: torch.Tensor, kv_cache: torch.Tensor, block_table: torch.Tensor,
+                         seq_lens: torch.Tensor, *, decode_query_len: int, num_kv_heads: int,
+                         max_blocks: int, score: torch.Tensor, topk_out: torch.Tensor,
+                         k_scale: float = 1.0, num_token_rows: int = 0, stream=None) -> None:
+    """score[h, b, t] (logical; any strides) and topk_out[t, h, :] for every row."""
+    batch = int(seq_lens.shape[0])
+    rows = num_token_rows or batch * decode_query_len
+    _check_q(q, "q", rows, q.shape[1] if q.dim() == 3 else -1)
+    _check_kv(kv_cache, num_kv_heads)
+    _check_tables(block_table, seq_lens, batch)
+    if score.dtype != torch.float32 or score.dim() != 3 or \
+            tuple(score.shape) != (num_kv_heads, max_blocks, rows):
+        raise ValueError(f"score must be float32 [{num_kv_heads}, {max_blocks}, {rows}]")
+    if topk_out.dtype != torch.int32 or not topk_out.is_contiguous() or topk_out.dim() != 3 \
+            or topk_out.shape[0] != rows or topk_out.shape[1] != num_kv_heads:
+        raise ValueError(f"topk_out must be contiguous int32 [{rows}, {num_kv_heads}, k]")
+    shape = _Shape(batch, decode_query_len, rows, block_table.stride(0), q.shape[1],
+                   num_kv_heads, PAGE_SIZE, HEAD_DIM, topk_out.shape[2],
+                   _kv_dtype_of(kv_cache), 0)
+    _check(load_library().msa_block_score_topk(
+        ctypes.byref(shape), q.data_ptr(), kv_cache.data_ptr(), _I64x4(*kv_cache.stride()),
+        kv_cache.shape[0], float(k_scale), block_table.data_ptr(), seq_lens.data_ptr(),
+        int(max_blocks), score.data_ptr(), _I64x3(*score.stride()), topk_out.data_ptr(),
+        int(topk_out.shape[2]), _stream_handle(stream, q.device)))
+
+
+def msa_topk_select(score: torch.Tensor, topk_out: torch.Tensor, stream=None) -> None:
+    """topk_out[t, h, :] from a float32 logical [Hkv, max_blocks, rows] score."""
+    if score.dtype != torch.float32 or score.dim() != 3 or score.device.type != "cuda":
+        raise ValueError("score must be a 3-D float32 device tensor [Hkv, blocks, rows]")
+    hkv, nb, rows = score.shape
+    if topk_out.dtype != torch.int32 or not topk_out.is_contiguous() or \
+            tuple(topk_out.shape[:2]) != (rows, hkv):
+        raise ValueError(f"topk_out must be contiguous int32 [{rows}, {hkv}, k]")
+    _check(load_library().msa_topk_select(
+        score.data_ptr(), _I64x3(*score.stride()), hkv, nb, rows, topk_out.data_ptr(),
+        int(topk_out.shape[2]), _stream_handle(stream, score.device)))
+
+
+def msa_fp8_e4m3_to_bf16(inp: torch.Tensor, out: torch.Tensor, stream=None) -> None:
+    if inp.dtype not in (torch.uint8, torch.float8_e4m3fn) or not inp.is_contiguous():
+        raise ValueError("inp must be contiguous uint8 / float8_e4m3fn")
+    if out.dtype != torch.bfloat16 or not out.is_contiguous() or out.numel() != inp.numel():
+        raise ValueError("out must be contiguous bfloat16 with inp's element count")
+    _check(load_library().msa_fp8_e4m3_to_bf16(inp.data_ptr(), out.data_ptr(), inp.numel(),
+                                               _stream_handle(stream, inp.device)))
+
+
+class PlanCache:
+    """Plans keyed by (batch, decode_query_len, page_table_stride, num_q_heads,
+    num_kv_heads, page_size, topk_blocks) plus kv dtype, padding rows and split
+    count -- the key of ``MSACutlassDecodePlanCache.prepare``."""
+
+    def __init__(self):
+        self.plans = {}
+
+    def prepare(self, block_table: torch.Tensor, seq_lens: torch.Tensor,
+                decode_query_len: int, *, num_q_heads: int, num_kv_heads: int,
+                topk_blocks: int, kv_dtype: int, page_size: int = PAGE_SIZE,
+                num_token_rows: int = 0, num_splits: int = 0) -> DecodePlan:
+        batch = int(seq_lens.shape[0])
+        _check_tables(block_table, seq_lens, batch)
+        stride = int(block_table.stride(0))
+        key = (batch, decode_query_len, stride, num_q_heads, num_kv_heads, page_size,
+               topk_blocks, kv_dtype, num_token_rows, num_splits)
+        plan = self.plans.get(key)
+        if plan is None:
+            plan = msa_sparse_decode_plan(
+                batch, decode_query_len, num_q_heads=num_q_heads, num_kv_heads=num_kv_heads,
+                page_table_stride=stride, topk_blocks=topk_blocks, kv_dtype=kv_dtype,
+                num_token_rows=num_token_rows, num_splits=num_splits, page_size=page_size,
+                device=block_table.device)
+            self.plans[key] = plan
+        return plan

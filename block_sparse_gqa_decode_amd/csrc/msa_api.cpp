@@ -1,0 +1,407 @@
+// C ABI of the block-sparse GQA decode library (declared in
+// include/msa_sparse_decode.h).  Argument checks are plain host code and run
+// before any HIP call, so misuse is reported the same way with or without a
+// GPU.  The plan mirrors the plan cache of the vLLM API page
+// "vllm.models.minimax_m3.nvidia.msa_cutlass_sparse_decode"
+// (MSACutlassDecodePlanCache: one plan per static shape whose device state
+// keeps stable addresses across CUDA/HIP graph replays); its only device state
+// is the fp32 split-K partial arena (TensorRT-LLM PR #17171, flash-decoding
+// commit: partials from a persistent buffer arena).
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <new>
+#include <string>
+
+#include "msa_internal.h"
+#include "msa_sparse_decode.h"
+
+struct msa_plan_s {
+  msa_decode_shape shape;
+  int device;
+  int32_t splits;
+  int32_t real_rows;
+  int32_t num_rows;
+  int64_t arena_bytes;
+  void* arena;
+  float* part_o;
+  float* part_ml;
+};
+
+namespace {
+
+thread_local std::string g_last_error;
+
+msa_status fail(msa_status s, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return s;
+}
+
+msa_status ok() {
+  g_last_error.clear();
+  return MSA_OK;
+}
+
+msa_status device_fail(hipError_t e, const char* what) {
+  return fail(MSA_ERR_DEVICE, "%s failed: %s", what, hipGetErrorString(e));
+}
+
+int64_t elem_bytes(int32_t kv_dtype) { return kv_dtype == MSA_KV_BF16 ? 2 : 1; }
+
+bool aligned16(const void* ptr) { return (reinterpret_cast<uintptr_t>(ptr) & 15u) == 0; }
+
+// Checks shared by the plan and the indexer entry point.
+msa_status check_common_shape(const msa_decode_shape* s) {
+  if (s == nullptr) return fail(MSA_ERR_INVALID_ARG, "shape is NULL");
+  if (s->batch < 1) return fail(MSA_ERR_INVALID_ARG, "batch must be >= 1 (got %d)", s->batch);
+  if (s->decode_query_len < 1 || s->decode_query_len > 32)
+    return fail(MSA_ERR_INVALID_ARG, "decode_query_len must be in 1..32 (got %d)",
+                s->decode_query_len);
+  const int64_t real = (int64_t)s->batch * s->decode_query_len;
+  if (real > (1 << 24))
+    return fail(MSA_ERR_UNSUPPORTED, "batch*decode_query_len = %lld exceeds 2^24",
+                (long long)real);
+  if (s->num_token_rows != 0 && s->num_token_rows < real)
+    return fail(MSA_ERR_INVALID_ARG,
+                "num_token_rows (%d) must be 0 or >= batch*decode_query_len (%lld)",
+                s->num_token_rows, (long long)real);
+  if (s->num_token_rows > (1 << 24))
+    return fail(MSA_ERR_UNSUPPORTED, "num_token_rows exceeds 2^24");
+  if (s->page_table_stride < 1)
+    return fail(MSA_ERR_INVALID_ARG, "page_table_stride must be >= 1 (got %d)",
+                s->page_table_stride);
+  if (s->num_q_heads < 1 || s->num_kv_heads < 1)
+    return fail(MSA_ERR_INVALID_ARG, "head counts must be >= 1 (got %d q, %d kv)",
+                s->num_q_heads, s->num_kv_heads);
+  if (s->num_q_heads % s->num_kv_heads != 0)
+    return fail(MSA_ERR_INVALID_ARG, "num_q_heads (%d) must be a multiple of num_kv_heads (%d)",
+                s->num_q_heads, s->num_kv_heads);
+  if (s->num_q_heads / s->num_kv_heads > msa::kMaxGroup)
+    return fail(MSA_ERR_UNSUPPORTED, "GQA group %d exceeds %d q heads per kv head",
+                s->num_q_heads / s->num_kv_heads, msa::kMaxGroup);
+  if (s->num_q_heads > 1024)
+    return fail(MSA_ERR_UNSUPPORTED, "num_q_heads exceeds 1024");
+  if (s->page_size != msa::kPage)
+    return fail(MSA_ERR_UNSUPPORTED, "page_size must be 128 (got %d)", s->page_size);
+  if (s->head_dim != msa::kHeadDim)
+    return fail(MSA_ERR_UNSUPPORTED, "head_dim must be 128 (got %d)", s->head_dim);
+  if (s->kv_dtype != MSA_KV_BF16 && s->kv_dtype != MSA_KV_FP8_E4M3)
+    return fail(MSA_ERR_INVALID_ARG, "unknown kv_dtype %d", s->kv_dtype);
+  return MSA_OK;
+}
+
+msa_status check_kv(const void* kv_cache, const int64_t kv_strides[4], int64_t num_kv_blocks,
+                    int32_t kv_dtype) {
+  if (kv_cache == nullptr) return fail(MSA_ERR_INVALID_ARG, "kv_cache is NULL");
+  if (kv_strides == nullptr) return fail(MSA_ERR_INVALID_ARG, "kv_strides is NULL");
+  if (num_kv_blocks < 1) return fail(MSA_ERR_INVALID_ARG, "num_kv_blocks must be >= 1");
+  if (num_kv_blocks > INT32_MAX) return fail(MSA_ERR_UNSUPPORTED, "num_kv_blocks exceeds 2^31-1");
+  if (kv_strides[3] != 1)
+    return fail(MSA_ERR_INVALID_ARG, "kv_cache last-dim stride must be 1 (got %lld)",
+                (long long)kv_strides[3]);
+  const int64_t eb = elem_bytes(kv_dtype);
+  for (int d = 0; d < 3; ++d) {
+    if (kv_strides[d] < 1)
+      return fail(MSA_ERR_INVALID_ARG, "kv_cache stride %d must be positive", d);
+    if ((kv_strides[d] * eb) % 16 != 0)
+      return fail(MSA_ERR_INVALID_ARG, "kv_cache stride %d (%lld elements) is not a multiple "
+                  "of 16 bytes", d, (long long)kv_strides[d]);
+  }
+  if (kv_strides[2] < 2 * msa::kHeadDim)
+    return fail(MSA_ERR_INVALID_ARG, "kv_cache row stride %lld is shorter than a packed K|V "
+                "row (256 elements)", (long long)kv_strides[2]);
+  if (!aligned16(kv_cache)) return fail(MSA_ERR_INVALID_ARG, "kv_cache is not 16-byte aligned");
+  return MSA_OK;
+}
+
+int32_t choose_splits(const msa_decode_shape* s, int32_t real_rows) {
+  if (s->num_splits > 0) return s->num_splits;
+  const int64_t units = (int64_t)real_rows * s->num_kv_heads;
+  int32_t splits = 1;
+  const int32_t cap = s->topk_blocks < 8 ? s->topk_blocks : 8;
+  while (units * splits < 512 && splits * 2 <= cap) splits *= 2;
+  return splits;
+}
+
+struct DeviceGuard {
+  int prev = -1;
+  bool changed = false;
+  hipError_t enter(int dev) {
+    hipError_t e = hipGetDevice(&prev);
+    if (e != hipSuccess) return e;
+    if (prev != dev) {
+      e = hipSetDevice(dev);
+      if (e != hipSuccess) return e;
+      changed = true;
+    }
+    return hipSuccess;
+  }
+  ~DeviceGuard() {
+    if (changed) (void)hipSetDevice(prev);
+  }
+};
+
+}  // namespace
+
+extern "C" {
+
+int32_t msa_abi_version(void) { return MSA_ABI_VERSION; }
+
+const char* msa_last_error(void) { return g_last_error.c_str(); }
+
+msa_status msa_sparse_decode_plan(const msa_decode_shape* shape, int device, msa_plan* plan_out) {
+  if (plan_out == nullptr) return fail(MSA_ERR_INVALID_ARG, "plan_out is NULL");
+  *plan_out = nullptr;
+  msa_status st = check_common_shape(shape);
+  if (st != MSA_OK) return st;
+  if (shape->topk_blocks < 1)
+    return fail(MSA_ERR_INVALID_ARG, "topk_blocks must be >= 1 (got %d)", shape->topk_blocks);
+  if (shape->topk_blocks > msa::kMaxTopk)
+    return fail(MSA_ERR_UNSUPPORTED, "topk_blocks %d exceeds %d", shape->topk_blocks,
+                msa::kMaxTopk);
+  if (shape->num_splits < 0 || shape->num_splits > msa::kMaxSplits)
+    return fail(MSA_ERR_INVALID_ARG, "num_splits must be 0 (auto) or 1..%d (got %d)",
+                msa::kMaxSplits, shape->num_splits);
+  if (device < 0) return fail(MSA_ERR_INVALID_ARG, "device must be >= 0 (got %d)", device);
+
+  const int32_t real_rows = shape->batch * shape->decode_query_len;
+  const int32_t num_rows = shape->num_token_rows ? shape->num_token_rows : real_rows;
+  const int32_t splits = choose_splits(shape, real_rows);
+  const int64_t grid = (int64_t)num_rows * shape->num_kv_heads * splits;
+  if (grid > INT32_MAX) return fail(MSA_ERR_UNSUPPORTED, "launch grid too large");
+  const int64_t per_row = (int64_t)shape->num_q_heads * splits;
+  const int64_t o_bytes = splits > 1 ? (int64_t)num_rows * per_row * msa::kHeadDim * 4 : 0;
+  const int64_t ml_bytes = splits > 1 ? (int64_t)num_rows * per_row * 2 * 4 : 0;
+
+  msa_plan plan = new (std::nothrow) msa_plan_s();
+  if (plan == nullptr) return fail(MSA_ERR_OUT_OF_MEMORY, "host allocation failed");
+  plan->shape = *shape;
+  plan->shape.num_token_rows = num_rows;
+  plan->shape.num_splits = splits;
+  plan->device = device;
+  plan->splits = splits;
+  plan->real_rows = real_rows;
+  plan->num_rows = num_rows;
+  plan->arena_bytes = o_bytes + ml_bytes;
+  plan->arena = nullptr;
+  plan->part_o = nullptr;
+  plan->part_ml = nullptr;
+  if (plan->arena_bytes > 0) {
+    // The arena is the plan's only device state; a plan without one makes no
+    // HIP call here.
+    DeviceGuard guard;
+    hipError_t e = guard.enter(device);
+    if (e != hipSuccess) {
+      delete plan;
+      return device_fail(e, "hipSetDevice");
+    }
+    e = hipMalloc(&plan->arena, (size_t)plan->arena_bytes);
+    if (e != hipSuccess) {
+      delete plan;
+      if (e == hipErrorOutOfMemory || e == hipErrorMemoryAllocation)
+        return fail(MSA_ERR_OUT_OF_MEMORY, "partial arena of %lld bytes: %s",
+                    (long long)(o_bytes + ml_bytes), hipGetErrorString(e));
+      return device_fail(e, "hipMalloc");
+    }
+    plan->part_o = static_cast<float*>(plan->arena);
+    plan->part_ml = reinterpret_cast<float*>(static_cast<char*>(plan->arena) + o_bytes);
+  }
+  *plan_out = plan;
+  return ok();
+}
+
+msa_status msa_sparse_decode_plan_destroy(msa_plan plan) {
+  if (plan == nullptr) return ok();
+  msa_status st = MSA_OK;
+  if (plan->arena != nullptr) {
+    DeviceGuard guard;
+    hipError_t e = guard.enter(plan->device);
+    if (e == hipSuccess) e = hipFree(plan->arena);
+    if (e != hipSuccess) st = device_fail(e, "hipFree");
+  }
+  delete plan;
+  return st == MSA_OK ? ok() : st;
+}
+
+msa_status msa_sparse_decode_plan_info(msa_plan plan, int32_t* num_splits, int64_t* arena_bytes,
+                                       msa_decode_shape* shape_out) {
+  if (plan == nullptr) return fail(MSA_ERR_INVALID_ARG, "plan is NULL");
+  if (num_splits) *num_splits = plan->splits;
+  if (arena_bytes) *arena_bytes = plan->arena_bytes;
+  if (shape_out) *shape_out = plan->shape;
+  return ok();
+}
+
+msa_status msa_sparse_decode_run(msa_plan plan, const void* q, const void* kv_cache,
+                                 const int64_t kv_strides[4], int64_t num_kv_blocks,
+                                 float k_scale, float v_scale, const int32_t* block_table,
+                                 const int32_t* seq_lens, const int32_t* topk,
+                                 const int64_t topk_strides[3], void* out, float sm_scale,
+                                 void* stream) {
+  if (plan == nullptr) return fail(MSA_ERR_INVALID_ARG, "plan is NULL");
+  const msa_decode_shape& s = plan->shape;
+  if (q == nullptr || out == nullptr) return fail(MSA_ERR_INVALID_ARG, "q and out must be non-NULL");
+  if (!aligned16(q) || !aligned16(out))
+    return fail(MSA_ERR_INVALID_ARG, "q and out must be 16-byte aligned");
+  if (block_table == nullptr || seq_lens == nullptr || topk == nullptr)
+    return fail(MSA_ERR_INVALID_ARG, "block_table, seq_lens and topk must be non-NULL");
+  if (topk_strides == nullptr) return fail(MSA_ERR_INVALID_ARG, "topk_strides is NULL");
+  for (int d = 0; d < 3; ++d)
+    if (topk_strides[d] < 0) return fail(MSA_ERR_INVALID_ARG, "topk strides must be >= 0");
+  msa_status st = check_kv(kv_cache, kv_strides, num_kv_blocks, s.kv_dtype);
+  if (st != MSA_OK) return st;
+  if (!std::isfinite(k_scale) || !std::isfinite(v_scale) || !std::isfinite(sm_scale))
+    return fail(MSA_ERR_INVALID_ARG, "scales must be finite");
+
+  const int64_t eb = elem_bytes(s.kv_dtype);
+  msa::AttendParams p{};
+  p.q = static_cast<const uint16_t*>(q);
+  p.kv = static_cast<const uint8_t*>(kv_cache);
+  p.kv_s0 = kv_strides[0] * eb;
+  p.kv_s1 = kv_strides[1] * eb;
+  p.kv_s2 = kv_strides[2] * eb;
+  p.num_kv_blocks = num_kv_blocks;
+  p.block_table = block_table;
+  p.bt_stride = s.page_table_stride;
+  p.seq_lens = seq_lens;
+  p.topk = topk;
+  p.tk_s0 = topk_strides[0];
+  p.tk_s1 = topk_strides[1];
+  p.tk_s2 = topk_strides[2];
+  p.out = static_cast<uint16_t*>(out);
+  p.part_o = plan->part_o;
+  p.part_ml = plan->part_ml;
+  p.scale_log2 = (float)((double)sm_scale * (double)k_scale * 1.4426950408889634);
+  p.v_scale = v_scale;
+  p.dql = s.decode_query_len;
+  p.real_rows = plan->real_rows;
+  p.num_rows = plan->num_rows;
+  p.hq = s.num_q_heads;
+  p.hkv = s.num_kv_heads;
+  p.group = s.num_q_heads / s.num_kv_heads;
+  p.topk_k = s.topk_blocks;
+  p.splits = plan->splits;
+
+  DeviceGuard guard;
+  hipError_t e = guard.enter(plan->device);
+  if (e != hipSuccess) return device_fail(e, "hipSetDevice");
+  hipStream_t st_ = static_cast<hipStream_t>(stream);
+  e = msa::launch_attend(p, s.kv_dtype == MSA_KV_FP8_E4M3, st_);
+  if (e != hipSuccess) return device_fail(e, "attend launch");
+  if (plan->splits > 1) {
+    e = msa::launch_combine(p, st_);
+    if (e != hipSuccess) return device_fail(e, "combine launch");
+  }
+  return ok();
+}
+
+msa_status msa_topk_select(const float* score, const int64_t score_strides[3],
+                           int32_t num_kv_heads, int32_t max_blocks, int32_t num_rows,
+                           int32_t* topk_out, int32_t topk_k, void* stream) {
+  if (score == nullptr || topk_out == nullptr)
+    return fail(MSA_ERR_INVALID_ARG, "score and topk_out must be non-NULL");
+  if (score_strides == nullptr) return fail(MSA_ERR_INVALID_ARG, "score_strides is NULL");
+  for (int d = 0; d < 3; ++d)
+    if (score_strides[d] < 0) return fail(MSA_ERR_INVALID_ARG, "score strides must be >= 0");
+  if (num_kv_heads < 1 || num_rows < 1)
+    return fail(MSA_ERR_INVALID_ARG, "num_kv_heads and num_rows must be >= 1");
+  if (max_blocks < 1 || max_blocks > msa::kMaxScoreBlocks)
+    return fail(MSA_ERR_INVALID_ARG, "max_blocks must be in 1..%d (got %d)",
+                msa::kMaxScoreBlocks, max_blocks);
+  if (topk_k < 1 || topk_k > msa::kMaxTopk)
+    return fail(MSA_ERR_INVALID_ARG, "topk_k must be in 1..%d (got %d)", msa::kMaxTopk, topk_k);
+  if ((int64_t)num_rows * num_kv_heads > INT32_MAX)
+    return fail(MSA_ERR_UNSUPPORTED, "launch grid too large");
+  msa::SelectParams p{};
+  p.score = score;
+  p.sc_s0 = score_strides[0];
+  p.sc_s1 = score_strides[1];
+  p.sc_s2 = score_strides[2];
+  p.topk_out = topk_out;
+  p.hkv = num_kv_heads;
+  p.max_blocks = max_blocks;
+  p.num_rows = num_rows;
+  p.k = topk_k;
+  hipError_t e = msa::launch_select(p, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return device_fail(e, "select launch");
+  return ok();
+}
+
+msa_status msa_block_score_topk(const msa_decode_shape* shape, const void* q,
+                                const void* kv_cache, const int64_t kv_strides[4],
+                                int64_t num_kv_blocks, float k_scale,
+                                const int32_t* block_table, const int32_t* seq_lens,
+                                int32_t max_blocks, float* score,
+                                const int64_t score_strides[3], int32_t* topk_out,
+                                int32_t topk_k, void* stream) {
+  msa_status st = check_common_shape(shape);
+  if (st != MSA_OK) return st;
+  if (q == nullptr || !aligned16(q)) return fail(MSA_ERR_INVALID_ARG, "q must be non-NULL and 16-byte aligned");
+  if (block_table == nullptr || seq_lens == nullptr)
+    return fail(MSA_ERR_INVALID_ARG, "block_table and seq_lens must be non-NULL");
+  if (score == nullptr || topk_out == nullptr)
+    return fail(MSA_ERR_INVALID_ARG, "score and topk_out must be non-NULL");
+  if (score_strides == nullptr) return fail(MSA_ERR_INVALID_ARG, "score_strides is NULL");
+  for (int d = 0; d < 3; ++d)
+    if (score_strides[d] < 0) return fail(MSA_ERR_INVALID_ARG, "score strides must be >= 0");
+  st = check_kv(kv_cache, kv_strides, num_kv_blocks, shape->kv_dtype);
+  if (st != MSA_OK) return st;
+  if (max_blocks < 1 || max_blocks > msa::kMaxScoreBlocks)
+    return fail(MSA_ERR_INVALID_ARG, "max_blocks must be in 1..%d (got %d)",
+                msa::kMaxScoreBlocks, max_blocks);
+  if (topk_k < 1 || topk_k > msa::kMaxTopk)
+    return fail(MSA_ERR_INVALID_ARG, "topk_k must be in 1..%d (got %d)", msa::kMaxTopk, topk_k);
+  if (!std::isfinite(k_scale)) return fail(MSA_ERR_INVALID_ARG, "k_scale must be finite");
+  if (shape->batch >= 65535)
+    return fail(MSA_ERR_UNSUPPORTED, "the scorer supports batch < 65535 (got %d)", shape->batch);
+
+  const int32_t real_rows = shape->batch * shape->decode_query_len;
+  const int32_t num_rows = shape->num_token_rows ? shape->num_token_rows : real_rows;
+  const int64_t eb = elem_bytes(shape->kv_dtype);
+  msa::ScoreParams p{};
+  p.q = static_cast<const uint16_t*>(q);
+  p.kv = static_cast<const uint8_t*>(kv_cache);
+  p.kv_s0 = kv_strides[0] * eb;
+  p.kv_s1 = kv_strides[1] * eb;
+  p.kv_s2 = kv_strides[2] * eb;
+  p.num_kv_blocks = num_kv_blocks;
+  p.block_table = block_table;
+  p.bt_stride = shape->page_table_stride;
+  p.seq_lens = seq_lens;
+  p.score = score;
+  p.sc_s0 = score_strides[0];
+  p.sc_s1 = score_strides[1];
+  p.sc_s2 = score_strides[2];
+  p.k_scale = k_scale;
+  p.batch = shape->batch;
+  p.dql = shape->decode_query_len;
+  p.real_rows = real_rows;
+  p.num_rows = num_rows;
+  p.hq = shape->num_q_heads;
+  p.hkv = shape->num_kv_heads;
+  p.group = shape->num_q_heads / shape->num_kv_heads;
+  p.max_blocks = max_blocks;
+  hipStream_t hs = static_cast<hipStream_t>(stream);
+  hipError_t e = msa::launch_score(p, shape->kv_dtype == MSA_KV_FP8_E4M3, hs);
+  if (e != hipSuccess) return device_fail(e, "score launch");
+  return msa_topk_select(score, score_strides, shape->num_kv_heads, max_blocks, num_rows,
+                         topk_out, topk_k, stream);
+}
+
+msa_status msa_fp8_e4m3_to_bf16(const void* in, void* out, int64_t n, void* stream) {
+  if (in == nullptr || out == nullptr) return fail(MSA_ERR_INVALID_ARG, "in and out must be non-NULL");
+  if (n < 1 || n > ((int64_t)1 << 40)) return fail(MSA_ERR_INVALID_ARG, "n out of range");
+  hipError_t e = msa::launch_fp8_to_bf16(static_cast<const uint8_t*>(in),
+                                         static_cast<uint16_t*>(out), n,
+                                         static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return device_fail(e, "fp8 conversion launch");
+  return ok();
+}
+
+}  // extern "C"

@@ -1,0 +1,440 @@
+// Block-sparse GQA decode attend for gfx950.
+//
+// What is computed: each decode token attends, per kv head, only the keys of
+// its indexer-selected 128-token pages that are causally visible at its
+// position (vLLM API page "vllm.models.minimax_m3.common.sparse_attention",
+// MiniMaxM3SparseImpl; vLLM test file test_minimax_m3_msa_cutlass_sparse_decode.py,
+// _make_topk), with split-K over the selected blocks, fp32 partials and zeroed
+// padding rows (TensorRT-LLM PR #17171, flash-decoding commit).
+//
+// Work decomposition.  A unit is one (token row t, kv head h); its G q heads
+// are the 16 rows of one MFMA tile.  A workgroup of 4 wavefronts handles one
+// unit's share (split) of its live pages; wavefront w owns keys
+// [32w, 32w+32) of every page, so the workgroup reads each page once and the
+// four wavefronts keep separate online-softmax states that are merged through
+// LDS at the end.
+//
+// Register layouts (16x16x32 bf16 MFMA, lane l, n = l % 16, g = l / 16):
+//  * S^T = K Q^T: A = K rows (key n of a 16-key tile), B = Q^T (q row n).  The
+//    contraction slot (g, c, j) of chunk c maps to head dim
+//    d = 64*(c/2) + 16*g + 8*(c%2) + j, so a lane reads two contiguous 16-dim
+//    runs of its key row.  The accumulator gives lane l the scores of keys
+//    4g..4g+3 of the tile for q row n.
+//  * O^T += V^T P^T: B = P^T comes straight from the two S^T accumulators of
+//    the wavefront's 32 keys (contraction slot j of group g = key
+//    4g+j for j<4, 16+4g+(j-4) for j>=4).  A = V^T uses the same key slots;
+//    its row m of d-tile t8 is head dim 8m+t8, so lane l loads the 8
+//    contiguous head dims 8n..8n+7 of each of its 8 keys and a byte permute
+//    transposes them into the 8 d-tiles.  The accumulator then holds
+//    O[q row n][32g + 8i + t8] for i < 4, t8 < 8: 32 contiguous outputs.
+//
+// NaN safety: rows past a page's visible count are never loaded (row index
+// clamped to the last visible row) and their scores are set to -inf, so stale
+// cache bytes cannot reach the MFMAs.
+#include "msa_device.h"
+#include "msa_internal.h"
+
+namespace msa {
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kWaves = 4;
+constexpr int kKeysPerWave = 32;
+constexpr int kOPad = 4;
+
+template <bool kFp8>
+struct PageRegs;
+
+template <>
+struct PageRegs<true> {
+  u32x4_t k[2][2];  // [key tile][run]: 16 fp8 each (head dims 16g.., 64+16g..)
+  u32x2_t v[8];     // 8 fp8 (head dims 8n..8n+7) of key slot j
+};
+
+template <>
+struct PageRegs<false> {
+  u32x4_t k[2][4];  // [key tile][chunk]: 8 bf16 each
+  u32x4_t v[8];     // 8 bf16 of key slot j
+};
+
+__device__ __forceinline__ int key_of_slot(int g, int j) {
+  return j < 4 ? 4 * g + j : 16 + 4 * g + (j - 4);
+}
+
+template <bool kFp8>
+__device__ __forceinline__ void load_page(PageRegs<kFp8>& r, const uint8_t* page_head,
+                                          int64_t row_stride, int kbase, int nvis,
+                                          int n, int g) {
+#pragma unroll
+  for (int tau = 0; tau < 2; ++tau) {
+    const int kr = min(kbase + 16 * tau + n, nvis - 1);
+    const uint8_t* row = page_head + kr * row_stride;
+    if constexpr (kFp8) {
+      r.k[tau][0] = *reinterpret_cast<const u32x4_t*>(row + 16 * g);
+      r.k[tau][1] = *reinterpret_cast<const u32x4_t*>(row + 64 + 16 * g);
+    } else {
+      r.k[tau][0] = *reinterpret_cast<const u32x4_t*>(row + 2 * (16 * g));
+      r.k[tau][1] = *reinterpret_cast<const u32x4_t*>(row + 2 * (16 * g + 8));
+      r.k[tau][2] = *reinterpret_cast<const u32x4_t*>(row + 2 * (64 + 16 * g));
+      r.k[tau][3] = *reinterpret_cast<const u32x4_t*>(row + 2 * (64 + 16 * g + 8));
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const int kr = min(kbase + key_of_slot(g, j), nvis - 1);
+    const uint8_t* row = page_head + kr * row_stride;
+    if constexpr (kFp8) {
+      r.v[j] = *reinterpret_cast<const u32x2_t*>(row + kHeadDim + 8 * n);
+    } else {
+      r.v[j] = *reinterpret_cast<const u32x4_t*>(row + 2 * kHeadDim + 16 * n);
+    }
+  }
+}
+
+template <bool kFp8>
+__device__ __forceinline__ void attend_page(const PageRegs<kFp8>& r,
+                                            const bf16x8_t (&qf)[4], int kbase,
+                                            int nvis, int g, float scale_log2,
+                                            float& m_run, float& l_part,
+                                            f32x4_t (&o)[8]) {
+  // S^T for the wavefront's two 16-key tiles.
+  f32x4_t s[2];
+#pragma unroll
+  for (int tau = 0; tau < 2; ++tau) {
+    bf16x8_t kf[4];
+    if constexpr (kFp8) {
+      kf[0] = as_bf16x8(fp8x8_to_bf16x8(r.k[tau][0].x, r.k[tau][0].y));
+      kf[1] = as_bf16x8(fp8x8_to_bf16x8(r.k[tau][0].z, r.k[tau][0].w));
+      kf[2] = as_bf16x8(fp8x8_to_bf16x8(r.k[tau][1].x, r.k[tau][1].y));
+      kf[3] = as_bf16x8(fp8x8_to_bf16x8(r.k[tau][1].z, r.k[tau][1].w));
+    } else {
+#pragma unroll
+      for (int c = 0; c < 4; ++c) kf[c] = as_bf16x8(r.k[tau][c]);
+    }
+    s[tau] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int c = 0; c < 4; ++c) s[tau] = mfma_bf16_16x16x32(kf[c], qf[c], s[tau]);
+  }
+
+  // Scale into log2 units, mask keys past the visible count.
+  float z[8];
+#pragma unroll
+  for (int tau = 0; tau < 2; ++tau) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int kp = kbase + 16 * tau + 4 * g + i;
+      z[4 * tau + i] = kp < nvis ? s[tau][i] * scale_log2 : -INFINITY;
+    }
+  }
+  float mx = z[0];
+#pragma unroll
+  for (int e = 1; e < 8; ++e) mx = fmaxf(mx, z[e]);
+  mx = wave_max_xor_16_32(mx);
+  const float m_new = fmaxf(m_run, mx);
+  const float m_use = m_new == -INFINITY ? 0.f : m_new;
+  const float alpha = fast_exp2(m_run - m_use);
+  float pz[8];
+  float sum = 0.f;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    pz[e] = fast_exp2(z[e] - m_use);
+    sum += pz[e];
+  }
+  l_part = l_part * alpha + sum;
+  m_run = m_new;
+#pragma unroll
+  for (int t8 = 0; t8 < 8; ++t8) o[t8] *= alpha;
+
+  u32x4_t pw;
+  pw.x = pack_bf16x2(pz[0], pz[1]);
+  pw.y = pack_bf16x2(pz[2], pz[3]);
+  pw.z = pack_bf16x2(pz[4], pz[5]);
+  pw.w = pack_bf16x2(pz[6], pz[7]);
+  const bf16x8_t pb = as_bf16x8(pw);
+
+  // V rows as bf16 pairs along the head dim: vd[j][w] = dims (8n+2w, 8n+2w+1).
+  u32x4_t vd[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    if constexpr (kFp8) {
+      vd[j] = fp8x8_to_bf16x8(r.v[j].x, r.v[j].y);
+    } else {
+      vd[j] = r.v[j];
+    }
+  }
+#pragma unroll
+  for (int t8 = 0; t8 < 8; ++t8) {
+    const uint32_t sel = (t8 & 1) ? 0x07060302u : 0x05040100u;
+    const int w = t8 >> 1;
+    u32x4_t a;
+    a.x = byte_perm(vd[1][w], vd[0][w], sel);
+    a.y = byte_perm(vd[3][w], vd[2][w], sel);
+    a.z = byte_perm(vd[5][w], vd[4][w], sel);
+    a.w = byte_perm(vd[7][w], vd[6][w], sel);
+    o[t8] = mfma_bf16_16x16x32(as_bf16x8(a), pb, o[t8]);
+  }
+}
+
+template <bool kFp8>
+__global__ __launch_bounds__(kThreads) void attend_kernel(AttendParams p) {
+  __shared__ int32_t s_page[kMaxTopk];
+  __shared__ int32_t s_nvis[kMaxTopk];
+  __shared__ int32_t s_nlive;
+  __shared__ float s_m[kWaves][16];
+  __shared__ float s_l[kWaves][16];
+  __shared__ float s_o[kWaves][16][kHeadDim + kOPad];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int n = lane & 15;
+  const int g = lane >> 4;
+  const int split = blockIdx.x % p.splits;
+  const int unit = blockIdx.x / p.splits;
+  const int t = unit / p.hkv;
+  const int h = unit - t * p.hkv;
+
+  if (t >= p.real_rows) {
+    // Padding row: zeros (written here when there is no combine pass).
+    if (p.splits == 1) {
+      const int qr = tid >> 4;
+      const int d0 = (tid & 15) * 8;
+      if (qr < p.group) {
+        uint16_t* dst = p.out + ((int64_t)t * p.hq + h * p.group + qr) * kHeadDim + d0;
+        *reinterpret_cast<u32x4_t*>(dst) = u32x4_t{0u, 0u, 0u, 0u};
+      }
+    }
+    return;
+  }
+
+  const int r = t / p.dql;
+  const int loc = t - r * p.dql;
+  const int pos = p.seq_lens[r] - p.dql + loc;
+
+  // Resolve the top-k row into the ordered list of live pages.
+  if (wave == 0) {
+    bool live = false;
+    int page = 0, nvis = 0;
+    if (lane < p.topk_k) {
+      const int b = p.topk[t * p.tk_s0 + h * p.tk_s1 + lane * p.tk_s2];
+      if (b >= 0 && b < p.bt_stride && (int64_t)b * kPage <= pos) {
+        const int pg = p.block_table[(int64_t)r * p.bt_stride + b];
+        if (pg >= 0 && pg < p.num_kv_blocks) {
+          live = true;
+          page = pg;
+          nvis = min(kPage, pos - b * kPage + 1);
+        }
+      }
+    }
+    const uint64_t mask = __ballot(live);
+    if (live) {
+      const int idx = __popcll(mask & ((1ull << lane) - 1ull));
+      s_page[idx] = page;
+      s_nvis[idx] = nvis;
+    }
+    if (lane == 0) s_nlive = __popcll(mask);
+  }
+
+  // Q^T operand: q row n, head dims 16g.. and 64+16g.. (see header comment).
+  bf16x8_t qf[4];
+  if (n < p.group) {
+    const uint16_t* qp = p.q + ((int64_t)t * p.hq + h * p.group + n) * kHeadDim;
+    qf[0] = as_bf16x8(*reinterpret_cast<const u32x4_t*>(qp + 16 * g));
+    qf[1] = as_bf16x8(*reinterpret_cast<const u32x4_t*>(qp + 16 * g + 8));
+    qf[2] = as_bf16x8(*reinterpret_cast<const u32x4_t*>(qp + 64 + 16 * g));
+    qf[3] = as_bf16x8(*reinterpret_cast<const u32x4_t*>(qp + 64 + 16 * g + 8));
+  } else {
+#pragma unroll
+    for (int c = 0; c < 4; ++c) qf[c] = as_bf16x8(u32x4_t{0u, 0u, 0u, 0u});
+  }
+  __syncthreads();
+
+  const int nlive = s_nlive;
+  const int per = (nlive + p.splits - 1) / p.splits;
+  const int lo = min(nlive, split * per);
+  const int hi = min(nlive, lo + per);
+  const int kbase = wave * kKeysPerWave;
+  const uint8_t* head_base = p.kv + h * p.kv_s1;
+
+  float m_run = -INFINITY;
+  float l_part = 0.f;
+  f32x4_t o[8];
+#pragma unroll
+  for (int t8 = 0; t8 < 8; ++t8) o[t8] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+  // Two-deep software pipeline over the live pages: the next page's loads are
+  // in flight while the current one is computed.
+  PageRegs<kFp8> cur{}, nxt{};
+  bool act_cur = false;
+  int nv_cur = 0;
+  if (lo < hi) {
+    nv_cur = s_nvis[lo];
+    act_cur = kbase < nv_cur;
+    if (act_cur) load_page<kFp8>(cur, head_base + s_page[lo] * p.kv_s0, p.kv_s2, kbase,
+                                 nv_cur, n, g);
+  }
+  for (int i = lo; i < hi; ++i) {
+    bool act_nxt = false;
+    int nv_nxt = 0;
+    if (i + 1 < hi) {
+      nv_nxt = s_nvis[i + 1];
+      act_nxt = kbase < nv_nxt;
+      if (act_nxt) load_page<kFp8>(nxt, head_base + s_page[i + 1] * p.kv_s0, p.kv_s2,
+                                   kbase, nv_nxt, n, g);
+    }
+    if (act_cur) attend_page<kFp8>(cur, qf, kbase, nv_cur, g, p.scale_log2, m_run, l_part, o);
+    cur = nxt;
+    act_cur = act_nxt;
+    nv_cur = nv_nxt;
+  }
+
+  // Merge the four wavefronts' states through LDS.
+  const float l_run = wave_sum_xor_16_32(l_part);
+  if (g == 0) {
+    s_m[wave][n] = m_run;
+    s_l[wave][n] = l_run;
+  }
+#pragma unroll
+  for (int t8 = 0; t8 < 8; ++t8) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) s_o[wave][n][32 * g + 8 * i + t8] = o[t8][i];
+  }
+  __syncthreads();
+
+  const int qr = tid >> 4;
+  const int d0 = (tid & 15) * 8;
+  if (qr >= p.group) return;
+  float mw[kWaves];
+  float M = -INFINITY;
+#pragma unroll
+  for (int w = 0; w < kWaves; ++w) {
+    mw[w] = s_m[w][qr];
+    M = fmaxf(M, mw[w]);
+  }
+  float L = 0.f;
+  float acc[8];
+#pragma unroll
+  for (int k = 0; k < 8; ++k) acc[k] = 0.f;
+#pragma unroll
+  for (int w = 0; w < kWaves; ++w) {
+    if (mw[w] == -INFINITY) continue;
+    const float e = fast_exp2(mw[w] - M);
+    L += e * s_l[w][qr];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) acc[k] += e * s_o[w][qr][d0 + k];
+  }
+
+  const int64_t row = (int64_t)t * p.hq + h * p.group + qr;
+  if (p.splits == 1) {
+    u32x4_t ov = u32x4_t{0u, 0u, 0u, 0u};
+    if (L > 0.f) {
+      const float inv = p.v_scale / L;
+      ov.x = pack_bf16x2(acc[0] * inv, acc[1] * inv);
+      ov.y = pack_bf16x2(acc[2] * inv, acc[3] * inv);
+      ov.z = pack_bf16x2(acc[4] * inv, acc[5] * inv);
+      ov.w = pack_bf16x2(acc[6] * inv, acc[7] * inv);
+    }
+    *reinterpret_cast<u32x4_t*>(p.out + row * kHeadDim + d0) = ov;
+  } else {
+    float* po = p.part_o + (row * p.splits + split) * kHeadDim + d0;
+    *reinterpret_cast<f32x4_t*>(po) = f32x4_t{acc[0], acc[1], acc[2], acc[3]};
+    *reinterpret_cast<f32x4_t*>(po + 4) = f32x4_t{acc[4], acc[5], acc[6], acc[7]};
+    if (d0 == 0) {
+      float* pml = p.part_ml + (row * p.splits + split) * 2;
+      pml[0] = M;
+      pml[1] = L;
+    }
+  }
+}
+
+// Log-sum-exp merge of the split partials of every (token row, q head) and
+// the bf16 store; rows with no live key and padding rows get exact zeros.
+__global__ __launch_bounds__(256) void combine_kernel(AttendParams p) {
+  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t total = (int64_t)p.num_rows * p.hq * 16;
+  if (idx >= total) return;
+  const int64_t row = idx >> 4;
+  const int d0 = (int)(idx & 15) * 8;
+  const int64_t t = row / p.hq;
+  u32x4_t ov = u32x4_t{0u, 0u, 0u, 0u};
+  if (t < p.real_rows) {
+    const float* ml = p.part_ml + row * p.splits * 2;
+    float M = -INFINITY;
+    for (int s = 0; s < p.splits; ++s) M = fmaxf(M, ml[2 * s]);
+    if (M != -INFINITY) {
+      float L = 0.f;
+      float acc[8];
+#pragma unroll
+      for (int k = 0; k < 8; ++k) acc[k] = 0.f;
+      for (int s = 0; s < p.splits; ++s) {
+        const float ms = ml[2 * s];
+        if (ms == -INFINITY) continue;
+        const float e = fast_exp2(ms - M);
+        L += e * ml[2 * s + 1];
+        const float* po = p.part_o + (row * p.splits + s) * kHeadDim + d0;
+        const f32x4_t a = *reinterpret_cast<const f32x4_t*>(po);
+        const f32x4_t b = *reinterpret_cast<const f32x4_t*>(po + 4);
+        acc[0] += e * a.x; acc[1] += e * a.y; acc[2] += e * a.z; acc[3] += e * a.w;
+        acc[4] += e * b.x; acc[5] += e * b.y; acc[6] += e * b.z; acc[7] += e * b.w;
+      }
+      if (L > 0.f) {
+        const float inv = p.v_scale / L;
+        ov.x = pack_bf16x2(acc[0] * inv, acc[1] * inv);
+        ov.y = pack_bf16x2(acc[2] * inv, acc[3] * inv);
+        ov.z = pack_bf16x2(acc[4] * inv, acc[5] * inv);
+        ov.w = pack_bf16x2(acc[6] * inv, acc[7] * inv);
+      }
+    }
+  }
+  *reinterpret_cast<u32x4_t*>(p.out + row * kHeadDim + d0) = ov;
+}
+
+// fp8 -> bf16 through the same conversion helper the attend uses.
+__global__ __launch_bounds__(256) void fp8_to_bf16_kernel(const uint8_t* in, uint16_t* out,
+                                                          int64_t n) {
+  const int64_t base = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;
+  if (base >= n) return;
+  uint32_t w = 0;
+#pragma unroll
+  for (int b = 0; b < 4; ++b)
+    if (base + b < n) w |= (uint32_t)in[base + b] << (8 * b);
+  const u32x4_t v = fp8x8_to_bf16x8(w, 0u);
+  const uint16_t vals[4] = {(uint16_t)(v.x & 0xffffu), (uint16_t)(v.x >> 16),
+                            (uint16_t)(v.y & 0xffffu), (uint16_t)(v.y >> 16)};
+#pragma unroll
+  for (int b = 0; b < 4; ++b)
+    if (base + b < n) out[base + b] = vals[b];
+}
+
+}  // namespace
+
+hipError_t launch_attend(const AttendParams& p, bool fp8, hipStream_t stream) {
+  const int64_t grid = (int64_t)p.num_rows * p.hkv * p.splits;
+  if (grid <= 0) return hipSuccess;
+  if (fp8) {
+    hipLaunchKernelGGL(attend_kernel<true>, dim3((uint32_t)grid), dim3(kThreads), 0,
+                       stream, p);
+  } else {
+    hipLaunchKernelGGL(attend_kernel<false>, dim3((uint32_t)grid), dim3(kThreads), 0,
+                       stream, p);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_combine(const AttendParams& p, hipStream_t stream) {
+  const int64_t total = (int64_t)p.num_rows * p.hq * 16;
+  const int64_t grid = (total + 255) / 256;
+  if (grid <= 0) return hipSuccess;
+  hipLaunchKernelGGL(combine_kernel, dim3((uint32_t)grid), dim3(256), 0, stream, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_fp8_to_bf16(const uint8_t* in, uint16_t* out, int64_t n,
+                              hipStream_t stream) {
+  const int64_t grid = (n + 1023) / 1024;
+  hipLaunchKernelGGL(fp8_to_bf16_kernel, dim3((uint32_t)grid), dim3(256), 0, stream, in,
+                     out, n);
+  return hipGetLastError();
+}
+
+}  // namespace msa

@@ -1,0 +1,64 @@
+// Launch parameters and launcher declarations shared by the C-ABI layer
+// (msa_api.cpp) and the kernel translation units.  Host-visible only: no
+// device code here.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace msa {
+
+constexpr int kPage = 128;      // tokens per KV page (= sparse block)
+constexpr int kHeadDim = 128;   // head dimension
+constexpr int kMaxGroup = 16;   // q heads per kv head handled by one MFMA tile
+constexpr int kMaxTopk = 64;    // entries per top-k row
+constexpr int kMaxSplits = 16;
+constexpr int kMaxScoreBlocks = 16384;
+
+struct AttendParams {
+  const uint16_t* q;        // bf16 [rows, hq, 128]
+  const uint8_t* kv;        // packed K|V base (bytes)
+  int64_t kv_s0, kv_s1, kv_s2;  // strides in bytes (page, head, row)
+  int64_t num_kv_blocks;
+  const int32_t* block_table;
+  int32_t bt_stride;
+  const int32_t* seq_lens;
+  const int32_t* topk;
+  int64_t tk_s0, tk_s1, tk_s2;  // strides in elements
+  uint16_t* out;            // bf16 [rows, hq, 128]
+  float* part_o;            // fp32 [rows, hq, splits, 128]
+  float* part_ml;           // fp32 [rows, hq, splits, 2] = (max, sum) in log2 units
+  float scale_log2;         // sm_scale * k_scale * log2(e)
+  float v_scale;
+  int32_t dql, real_rows, num_rows, hq, hkv, group, topk_k, splits;
+};
+
+struct ScoreParams {
+  const uint16_t* q;        // bf16 [rows, hq, 128]
+  const uint8_t* kv;
+  int64_t kv_s0, kv_s1, kv_s2;  // bytes
+  int64_t num_kv_blocks;
+  const int32_t* block_table;
+  int32_t bt_stride;
+  const int32_t* seq_lens;
+  float* score;             // fp32 logical [hkv, max_blocks, rows]
+  int64_t sc_s0, sc_s1, sc_s2;  // elements
+  float k_scale;
+  int32_t batch, dql, real_rows, num_rows, hq, hkv, group, max_blocks;
+};
+
+struct SelectParams {
+  const float* score;
+  int64_t sc_s0, sc_s1, sc_s2;
+  int32_t* topk_out;        // int32 [rows, hkv, k]
+  int32_t hkv, max_blocks, num_rows, k;
+};
+
+hipError_t launch_attend(const AttendParams& p, bool fp8, hipStream_t stream);
+hipError_t launch_combine(const AttendParams& p, hipStream_t stream);
+hipError_t launch_score(const ScoreParams& p, bool fp8, hipStream_t stream);
+hipError_t launch_select(const SelectParams& p, hipStream_t stream);
+hipError_t launch_fp8_to_bf16(const uint8_t* in, uint16_t* out, int64_t n,
+                              hipStream_t stream);
+
+}  // namespace msa

@@ -1,0 +1,184 @@
+/*
+ * msa_sparse_decode.h -- C ABI of the MI355X (gfx950) block-sparse GQA decode
+ * library: MiniMax-M3-style sparse attention decode over indexer-selected
+ * 128-token KV pages, plus the indexer block-max scorer and top-k selector.
+ *
+ * Sources of the operation (the pages this library implements):
+ *  - vLLM API page "vllm.models.minimax_m3.nvidia.msa_cutlass_sparse_decode":
+ *    MSACutlassDecodePlanCache.prepare / _build_plan (plan keyed by the static
+ *    shape, graph-stable mutable state, argument checks), msa_cutlass_sparse_decode
+ *    (packed cache split into K = first 128, V = last 128 of the last dim;
+ *    sm_scale, k/v scales), prepare_decode_metadata.
+ *  - vLLM API page "vllm.models.minimax_m3.common.sparse_attention":
+ *    MiniMaxM3SparseBackend (head size 128, block size 128, bf16 / fp8 KV,
+ *    cache shape (num_blocks, num_kv_heads, 128, 2*128) in HND order),
+ *    MiniMaxM3SparseImpl (each query attends only the indexer-selected
+ *    blocks), MiniMaxM3SparseTritonImpl.forward (decode call arguments).
+ *  - vLLM test file test_minimax_m3_msa_cutlass_sparse_decode.py: _make_topk
+ *    (logical block ids per (token, kv head), -1 padding, token position
+ *    seq_len - query_len + local), _make_paged_layout (one block-table row
+ *    per request over a shuffled pool), static-dispatch cases (decode query
+ *    length 1..32).
+ *  - TensorRT-LLM PR #17171 "Custom decode kernels for MinimaxM3": split-K
+ *    flash decoding with fp32 partials in a persistent arena, zeroed (not
+ *    NaN) output for padding rows; per-block causal max score of q.k and a
+ *    strided top-k selector.
+ *
+ * Conventions for every entry point:
+ *  - All tensor arguments are DEVICE pointers on the plan's (or the current)
+ *    HIP device, owned by the caller.  The library never frees them.
+ *  - Strides are in ELEMENTS of the tensor's element type.
+ *  - `stream` is a hipStream_t passed as void* (NULL = the null stream).
+ *    Launches are asynchronous; no entry point synchronises the host with the
+ *    device or allocates device memory except msa_sparse_decode_plan.
+ *  - A negative status is returned for misuse that the host can detect; the
+ *    message is then available from msa_last_error() (thread-local).  No
+ *    exception crosses the ABI.  Argument checks run before any HIP call.
+ *  - Data-dependent inputs are not errors: a negative top-k entry, a block
+ *    that starts after the token's position, a block id at or beyond
+ *    page_table_stride, or a block-table entry outside [0, num_kv_blocks)
+ *    contributes nothing.  Duplicate block ids in one row are a precondition
+ *    violation (result unspecified, memory-safe).
+ */
+#ifndef MSA_SPARSE_DECODE_H_
+#define MSA_SPARSE_DECODE_H_
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MSA_ABI_VERSION 1
+
+typedef enum msa_status {
+  MSA_OK = 0,
+  MSA_ERR_INVALID_ARG = -1,   /* bad pointer, size, stride or alignment       */
+  MSA_ERR_UNSUPPORTED = -2,   /* valid but outside what the kernels implement */
+  MSA_ERR_DEVICE = -3,        /* a HIP runtime call failed (no GPU, bad device) */
+  MSA_ERR_OUT_OF_MEMORY = -4  /* plan arena allocation failed                  */
+} msa_status;
+
+typedef enum msa_kv_dtype {
+  MSA_KV_BF16 = 0,            /* bf16 K|V entries                              */
+  MSA_KV_FP8_E4M3 = 1         /* OCP fp8 e4m3fn K|V entries, per-tensor scale  */
+} msa_kv_dtype;
+
+/* Static shape of one decode step: the plan key (batch, decode query length,
+ * page-table stride, q heads, kv heads, page size, top-k) of the plan cache in
+ * MSACutlassDecodePlanCache.prepare, plus KV dtype, padding rows and split
+ * count. */
+typedef struct msa_decode_shape {
+  int32_t batch;              /* requests, >= 1                                  */
+  int32_t decode_query_len;   /* query tokens per request, 1..32                 */
+  int32_t num_token_rows;     /* rows of q/topk/out; >= batch*decode_query_len.
+                                 Rows past batch*decode_query_len are padding
+                                 rows and produce exact zeros. 0 = no padding.   */
+  int32_t page_table_stride;  /* elements between block-table rows, >= 1         */
+  int32_t num_q_heads;        /* Hq, multiple of num_kv_heads                    */
+  int32_t num_kv_heads;       /* Hkv; Hq/Hkv (the GQA group) must be 1..16       */
+  int32_t page_size;          /* must be 128 (one sparse block per KV page)      */
+  int32_t head_dim;           /* must be 128                                     */
+  int32_t topk_blocks;        /* entries per top-k row, 1..64                    */
+  int32_t kv_dtype;           /* msa_kv_dtype                                    */
+  int32_t num_splits;         /* split-K factor over a row's live blocks; 0 lets
+                                 the plan choose, else 1..16                     */
+} msa_decode_shape;
+
+typedef struct msa_plan_s* msa_plan;
+
+/* Validate `shape`, choose the launch configuration and allocate the plan's
+ * persistent fp32 split-K partial arena on HIP device `device` (the only
+ * allocation the library makes).  On success *plan_out owns that arena until
+ * msa_sparse_decode_plan_destroy.  A plan must not be run concurrently on two
+ * streams (the arena is shared).  Shape errors return MSA_ERR_INVALID_ARG or
+ * MSA_ERR_UNSUPPORTED before any HIP call. */
+msa_status msa_sparse_decode_plan(const msa_decode_shape* shape, int device,
+                                  msa_plan* plan_out);
+
+/* Free the plan and its arena (no-op on NULL).  The caller must make sure no
+ * launched run that uses the plan is still executing. */
+msa_status msa_sparse_decode_plan_destroy(msa_plan plan);
+
+/* Report the plan's split factor, partial-arena size in bytes and the
+ * shape it was built for (any output pointer may be NULL). */
+msa_status msa_sparse_decode_plan_info(msa_plan plan, int32_t* num_splits,
+                                       int64_t* arena_bytes,
+                                       msa_decode_shape* shape_out);
+
+/* One sparse decode step (the attend).  For token row t = r*dql + l (request r,
+ * local token l) at position pos = seq_lens[r] - dql + l, kv head h and each q
+ * head j = h*G + g (G = Hq/Hkv):
+ *   out[t, j, :] = softmax_k( sm_scale * q[t,j,:] . K[k,:] ) V[k,:]
+ * over the keys k = b*128 + i of every selected logical block b =
+ * topk[t, h, s] with b >= 0 and b*128 <= pos, i < min(128, pos - b*128 + 1),
+ * read from physical page block_table[r, b].  K and V are the decoded cache
+ * entries times k_scale / v_scale.  Rows with no visible key, and padding
+ * rows, are written as exact zeros.
+ *
+ *   q            bf16 [num_token_rows, Hq, 128], contiguous.
+ *   kv_cache     packed K|V entries, logical [num_kv_blocks, Hkv, 128, 256]
+ *                with strides kv_strides (elements); kv_strides[3] must be 1
+ *                and the other strides must be positive multiples of 16 bytes.
+ *                HND (vLLM's default) is {Hkv*128*256, 128*256, 256, 1}.
+ *   block_table  int32 [batch, page_table_stride] physical page ids.
+ *   seq_lens     int32 [batch] device copy, including the new tokens; read on
+ *                the device, so runs are graph-capturable and may change
+ *                between replays.
+ *   topk         int32 logical [num_token_rows, Hkv, topk_blocks] with
+ *                topk_strides (elements), -1 = no block.
+ *   out          bf16 [num_token_rows, Hq, 128], contiguous.
+ */
+msa_status msa_sparse_decode_run(msa_plan plan, const void* q, const void* kv_cache,
+                                 const int64_t kv_strides[4], int64_t num_kv_blocks,
+                                 float k_scale, float v_scale,
+                                 const int32_t* block_table, const int32_t* seq_lens,
+                                 const int32_t* topk, const int64_t topk_strides[3],
+                                 void* out, float sm_scale, void* stream);
+
+/* Indexer step of a full decode: per-block causal max score, then top-k.
+ *   score[h, b, t] = max over g < G and visible keys i of block b of
+ *                    q[t, h*G+g, :] . K[block_table[r,b], h, i, :]
+ * (raw dot product with K = decoded entries * k_scale, no softmax scale),
+ * -inf for blocks b < max_blocks that start after the token's position; then
+ * topk_out[t, h, :] = the topk_k blocks with the largest score > -inf, in
+ * descending score order with ties to the lower block id, padded with -1.
+ *   shape        batch, decode_query_len, num_token_rows (padding rows get
+ *                -inf scores and all -1 selections), heads, page_table_stride,
+ *                page_size, head_dim, kv_dtype are used; topk_blocks and
+ *                num_splits are ignored.
+ *   score        float32 logical [Hkv, max_blocks, num_token_rows] with
+ *                score_strides (elements); caller-owned scratch, required.
+ *   max_blocks   1..16384, at least ceil(max seq_len / 128).
+ *   topk_out     int32 [num_token_rows, Hkv, topk_k], contiguous; topk_k 1..64.
+ */
+msa_status msa_block_score_topk(const msa_decode_shape* shape, const void* q,
+                                const void* kv_cache, const int64_t kv_strides[4],
+                                int64_t num_kv_blocks, float k_scale,
+                                const int32_t* block_table, const int32_t* seq_lens,
+                                int32_t max_blocks, float* score,
+                                const int64_t score_strides[3], int32_t* topk_out,
+                                int32_t topk_k, void* stream);
+
+/* The selector alone: topk_out[t, h, :] from score (same layout and rule as
+ * msa_block_score_topk) for num_rows rows and num_kv_heads heads. */
+msa_status msa_topk_select(const float* score, const int64_t score_strides[3],
+                           int32_t num_kv_heads, int32_t max_blocks, int32_t num_rows,
+                           int32_t* topk_out, int32_t topk_k, void* stream);
+
+/* Decode n OCP fp8 e4m3fn codes to bf16 with the same in-register conversion
+ * the attend uses (a self-check of the conversion path).  in: uint8[n],
+ * out: bf16 bits uint16[n], device pointers, n >= 1. */
+msa_status msa_fp8_e4m3_to_bf16(const void* in, void* out, int64_t n, void* stream);
+
+/* Message for the last non-OK status returned on this thread ("" if none). */
+const char* msa_last_error(void);
+
+/* MSA_ABI_VERSION of the built library. */
+int32_t msa_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MSA_SPARSE_DECODE_H_ */

@@ -1,0 +1,82 @@
+"""Helpers shared by the GPU parity tests: move a seeded case to the device,
+run the HIP path through the C ABI, and compare with the float64 oracle."""
+import numpy as np
+import torch
+
+import block_sparse_gqa_decode_amd as msa
+from oracle import msa_oracle as om
+from workloads import gen
+
+ATOL = 1e-2
+RTOL = 1e-2
+
+
+class DevCase:
+    def __init__(self, case: gen.DecodeCase, dev="cuda:0", layout="hnd"):
+        self.case = case
+        self.dev = torch.device(dev)
+        if case.kv_dtype == gen.KV_FP8:
+            kv = torch.from_numpy(case.kv)
+        else:
+            kv = torch.from_numpy(case.kv.view(np.int16)).view(torch.bfloat16)
+        if layout == "nhd":
+            # physical (num_blocks, 128, Hkv, 256), viewed logically as HND
+            kv = kv.permute(0, 2, 1, 3).contiguous().to(self.dev).permute(0, 2, 1, 3)
+        else:
+            kv = kv.to(self.dev)
+        self.kv = kv
+        self.q = torch.from_numpy(case.q.view(np.int16)).view(torch.bfloat16).to(self.dev)
+        self.block_table = torch.from_numpy(case.block_table).to(self.dev)
+        self.seq_lens = torch.from_numpy(case.seq_lens).to(self.dev)
+        self.topk = (torch.from_numpy(case.topk).to(self.dev)
+                     if case.topk is not None else None)
+        self.out = torch.full_like(self.q, float("nan"))
+
+    @property
+    def kv_dtype(self):
+        return msa.KV_FP8_E4M3 if self.case.kv_dtype == gen.KV_FP8 else msa.KV_BF16
+
+    def plan(self, num_splits=0):
+        c = self.case
+        return msa.msa_sparse_decode_plan(
+            c.batch, c.dql, num_q_heads=c.num_q_heads, num_kv_heads=c.num_kv_heads,
+            page_table_stride=self.block_table.stride(0), topk_blocks=c.topk_k,
+            kv_dtype=self.kv_dtype, num_token_rows=c.num_token_rows, num_splits=num_splits,
+            device=self.dev)
+
+    def run(self, plan, topk=None, out=None, stream=None):
+        c = self.case
+        out = self.out if out is None else out
+        msa.msa_sparse_decode_run(plan, self.q, self.kv, self.block_table, self.seq_lens,
+                                  self.topk if topk is None else topk, out,
+                                  sm_scale=c.sm_scale, k_scale=c.k_scale, v_scale=c.v_scale,
+                                  stream=stream)
+        return out
+
+
+def oracle_attend(case: gen.DecodeCase, rows=None, topk=None):
+    return om.sparse_decode(case.q, case.kv, case.kv_dtype, case.k_scale, case.v_scale,
+                            case.block_table, case.seq_lens,
+                            case.topk if topk is None else topk, case.dql,
+                            case.num_kv_heads, case.sm_scale, rows=rows)
+
+
+def to_f64(x: torch.Tensor) -> np.ndarray:
+    return x.float().cpu().numpy().astype(np.float64)
+
+
+def assert_parity(got: np.ndarray, ref: np.ndarray, atol=ATOL, rtol=RTOL, what=""):
+    """max |got-ref| <= atol, ||got-ref|| <= rtol*||ref||, and elementwise
+    |got-ref| <= atol + rtol*|ref|."""
+    assert got.shape == ref.shape, (got.shape, ref.shape)
+    assert np.isfinite(got).all(), f"{what}: non-finite output"
+    diff = np.abs(got - ref)
+    max_abs = float(diff.max()) if diff.size else 0.0
+    nref = float(np.linalg.norm(ref))
+    rel = float(np.linalg.norm(got - ref) / nref) if nref > 0 else 0.0
+    print(f"[parity] {what}: max_abs={max_abs:.3e} rel_l2={rel:.3e} n={diff.size}",
+          flush=True)
+    assert max_abs <= atol, f"{what}: max abs err {max_abs}"
+    assert rel <= rtol, f"{what}: relative L2 err {rel}"
+    assert np.all(diff <= atol + rtol * np.abs(ref)), f"{what}: elementwise tolerance"
+    return max_abs, rel

@@ -1,0 +1,262 @@
+"""Host-side checks of the C-ABI library (no GPU needed, no kernel launched).
+
+* the built library loads and exports every function the header declares;
+* argument validation runs before any HIP call and reports misuse with a
+  status and a message -- the analogue of the static-dispatch and ValueError
+  cases of the vLLM test file test_minimax_m3_msa_cutlass_sparse_decode.py
+  (decode query length 1..32, page size 128, head size 128) and of
+  MSACutlassDecodePlanCache.prepare's tensor checks.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+import block_sparse_gqa_decode_amd as msa
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "msa_sparse_decode.h")
+
+
+def header_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = re.findall(r"^\s*(?:msa_status|const char\*|int32_t)\s+(msa_\w+)\s*\(", text,
+                       flags=re.M)
+    return sorted(set(names))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return msa.load_library()
+
+
+def shape(**kw):
+    base = dict(batch=32, decode_query_len=4, num_token_rows=0, page_table_stride=512,
+                num_q_heads=16, num_kv_heads=1, page_size=128, head_dim=128, topk_blocks=16,
+                kv_dtype=msa.KV_FP8_E4M3, num_splits=1)
+    base.update(kw)
+    return msa._Shape(*[base[f] for f, _ in msa._Shape._fields_])
+
+
+def plan_status(lib, s, device=0):
+    h = ctypes.c_void_p()
+    st = lib.msa_sparse_decode_plan(ctypes.byref(s), device, ctypes.byref(h))
+    if st == 0:
+        lib.msa_sparse_decode_plan_destroy(h)
+    return st, lib.msa_last_error().decode()
+
+
+def test_header_declares_the_boundary():
+    names = header_functions()
+    for required in ("msa_sparse_decode_plan", "msa_sparse_decode_run",
+                     "msa_block_score_topk"):
+        assert required in names
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for name in header_functions():
+        assert hasattr(lib, name), f"{name} declared in the header but not exported"
+
+
+def test_abi_version_matches_header(lib):
+    m = re.search(r"#define MSA_ABI_VERSION (\d+)", open(HEADER).read())
+    assert lib.msa_abi_version() == int(m.group(1))
+
+
+def test_shape_struct_matches_header():
+    text = open(HEADER).read()
+    body = re.search(r"typedef struct msa_decode_shape \{(.*?)\} msa_decode_shape;", text,
+                     flags=re.S).group(1)
+    body = re.sub(r"/\*.*?\*/", "", body, flags=re.S)
+    fields = re.findall(r"int32_t\s+([\w\s,]+);", body)
+    names = [n.strip() for grp in fields for n in grp.split(",")]
+    assert names == [f for f, _ in msa._Shape._fields_]
+
+
+# The static-dispatch cases of the test page, as argument validation: query
+# length 0 and 33 are rejected, 1..32 accepted.  Accepted shapes with one
+# split make no HIP call, so they succeed here without a GPU.
+@pytest.mark.parametrize("batch,dql,hq,hkv,ok", [
+    (16, 4, 64, 4, True), (16, 4, 16, 1, True), (24, 4, 16, 1, True), (32, 4, 16, 1, True),
+    (16, 1, 64, 4, True), (16, 1, 16, 1, True), (16, 2, 64, 4, True), (16, 2, 16, 1, True),
+    (16, 32, 64, 4, True), (16, 0, 64, 4, False), (16, 33, 64, 4, False),
+    (8, 4, 64, 4, True),   # no minimum batch here: that was a tile heuristic
+])
+def test_decode_query_len_bounds(lib, batch, dql, hq, hkv, ok):
+    st, msg = plan_status(lib, shape(batch=batch, decode_query_len=dql, num_q_heads=hq,
+                                     num_kv_heads=hkv))
+    if ok:
+        assert st == 0, msg
+    else:
+        assert st == msa.MSA_ERR_INVALID_ARG and "decode_query_len" in msg
+
+
+@pytest.mark.parametrize("field,value,status,fragment", [
+    ("page_size", 64, msa.MSA_ERR_UNSUPPORTED, "page_size"),
+    ("head_dim", 64, msa.MSA_ERR_UNSUPPORTED, "head_dim"),
+    ("num_kv_heads", 3, msa.MSA_ERR_INVALID_ARG, "multiple"),
+    ("num_kv_heads", 0, msa.MSA_ERR_INVALID_ARG, "head counts"),
+    ("num_q_heads", 64, msa.MSA_ERR_UNSUPPORTED, "GQA group"),
+    ("topk_blocks", 0, msa.MSA_ERR_INVALID_ARG, "topk_blocks"),
+    ("topk_blocks", 65, msa.MSA_ERR_UNSUPPORTED, "topk_blocks"),
+    ("batch", 0, msa.MSA_ERR_INVALID_ARG, "batch"),
+    ("page_table_stride", 0, msa.MSA_ERR_INVALID_ARG, "page_table_stride"),
+    ("num_token_rows", 5, msa.MSA_ERR_INVALID_ARG, "num_token_rows"),
+    ("kv_dtype", 7, msa.MSA_ERR_INVALID_ARG, "kv_dtype"),
+    ("num_splits", 17, msa.MSA_ERR_INVALID_ARG, "num_splits"),
+    ("num_splits", -1, msa.MSA_ERR_INVALID_ARG, "num_splits"),
+])
+def test_plan_rejects_bad_shapes(lib, field, value, status, fragment):
+    st, msg = plan_status(lib, shape(**{field: value}))
+    assert st == status and fragment in msg, (st, msg)
+
+
+def test_plan_null_arguments(lib):
+    h = ctypes.c_void_p()
+    assert lib.msa_sparse_decode_plan(None, 0, ctypes.byref(h)) == msa.MSA_ERR_INVALID_ARG
+    s = shape()
+    assert lib.msa_sparse_decode_plan(ctypes.byref(s), 0, None) == msa.MSA_ERR_INVALID_ARG
+    assert lib.msa_sparse_decode_plan(ctypes.byref(s), -1, ctypes.byref(h)) == \
+        msa.MSA_ERR_INVALID_ARG
+
+
+def test_binding_raises_value_error_subclass():
+    with pytest.raises(msa.MsaInvalidArgument, match="decode_query_len"):
+        msa.msa_sparse_decode_plan(16, 33, num_q_heads=64, num_kv_heads=4,
+                                   page_table_stride=8, topk_blocks=16,
+                                   kv_dtype=msa.KV_FP8_E4M3, num_splits=1, device=0)
+    with pytest.raises(msa.MsaUnsupported, match="page_size"):
+        msa.msa_sparse_decode_plan(16, 4, num_q_heads=64, num_kv_heads=4,
+                                   page_table_stride=8, topk_blocks=16,
+                                   kv_dtype=msa.KV_FP8_E4M3, num_splits=1, page_size=64,
+                                   device=0)
+
+
+def test_plan_info_reports_normalised_shape():
+    plan = msa.msa_sparse_decode_plan(4, 3, num_q_heads=16, num_kv_heads=1,
+                                      page_table_stride=10, topk_blocks=8,
+                                      kv_dtype=msa.KV_BF16, num_splits=1, device=0)
+    assert plan.num_token_rows == 12 and plan.num_splits == 1 and plan.arena_bytes == 0
+    plan.close()
+
+
+# ---------------------------------------------------------------------------
+# run / score / select argument checks (all fail before any HIP call)
+# ---------------------------------------------------------------------------
+
+FAKE = 0x10000  # a 16-byte-aligned non-NULL address; never dereferenced here
+
+
+def _plan(lib, **kw):
+    h = ctypes.c_void_p()
+    s = shape(**kw)
+    assert lib.msa_sparse_decode_plan(ctypes.byref(s), 0, ctypes.byref(h)) == 0
+    return h
+
+
+def _run(lib, h, **over):
+    args = dict(q=FAKE, kv=FAKE, kvs=(256 * 128, 256 * 128, 256, 1), nb=10, ks=1.0,
+                vs=1.0, bt=FAKE, sl=FAKE, tk=FAKE, tks=(16, 16, 1), out=FAKE, sm=0.088,
+                stream=None)
+    args.update(over)
+    kvs = msa._I64x4(*args["kvs"]) if args["kvs"] is not None else None
+    tks = msa._I64x3(*args["tks"]) if args["tks"] is not None else None
+    st = lib.msa_sparse_decode_run(h, args["q"], args["kv"], kvs, args["nb"], args["ks"],
+                                   args["vs"], args["bt"], args["sl"], args["tk"], tks,
+                                   args["out"], args["sm"], args["stream"])
+    return st, lib.msa_last_error().decode()
+
+
+@pytest.mark.parametrize("over,fragment", [
+    (dict(q=None), "q and out"),
+    (dict(out=None), "q and out"),
+    (dict(q=FAKE + 4), "aligned"),
+    (dict(bt=None), "block_table"),
+    (dict(tk=None), "block_table"),
+    (dict(kv=None), "kv_cache is NULL"),
+    (dict(kv=FAKE + 8), "kv_cache is not 16-byte aligned"),
+    (dict(kvs=None), "kv_strides"),
+    (dict(tks=None), "topk_strides"),
+    (dict(tks=(16, 16, -1)), "topk strides"),
+    (dict(kvs=(256 * 128, 256 * 128, 256, 2)), "last-dim stride"),
+    (dict(kvs=(256 * 128, 256 * 128, 264, 1)), "16 bytes"),
+    (dict(kvs=(256 * 128, 256 * 128, 128, 1)), "shorter"),
+    (dict(kvs=(0, 256 * 128, 256, 1)), "positive"),
+    (dict(nb=0), "num_kv_blocks"),
+    (dict(sm=float("nan")), "finite"),
+    (dict(ks=float("inf")), "finite"),
+])
+def test_run_rejects_bad_arguments(lib, over, fragment):
+    h = _plan(lib)
+    try:
+        st, msg = _run(lib, h, **over)
+        assert st == msa.MSA_ERR_INVALID_ARG and fragment in msg, (st, msg)
+    finally:
+        lib.msa_sparse_decode_plan_destroy(h)
+
+
+def test_run_null_plan(lib):
+    st, msg = _run(lib, None)
+    assert st == msa.MSA_ERR_INVALID_ARG and "plan" in msg
+
+
+def test_bf16_strides_are_checked_in_bytes(lib):
+    h = _plan(lib, kv_dtype=msa.KV_BF16)
+    try:
+        # 260 bf16 elements = 520 bytes: not a multiple of 16 bytes
+        st, msg = _run(lib, h, kvs=(260 * 128, 260 * 128, 260, 1))
+        assert st == msa.MSA_ERR_INVALID_ARG and "16 bytes" in msg
+    finally:
+        lib.msa_sparse_decode_plan_destroy(h)
+
+
+def _score(lib, s, **over):
+    args = dict(q=FAKE, kv=FAKE, kvs=(256 * 128, 256 * 128, 256, 1), nb=10, ks=1.0, bt=FAKE,
+                sl=FAKE, mb=64, sc=FAKE, scs=(64 * 8, 8, 1), to=FAKE, k=16)
+    args.update(over)
+    st = lib.msa_block_score_topk(ctypes.byref(s), args["q"], args["kv"],
+                                  msa._I64x4(*args["kvs"]), args["nb"], args["ks"], args["bt"],
+                                  args["sl"], args["mb"], args["sc"], msa._I64x3(*args["scs"]),
+                                  args["to"], args["k"], None)
+    return st, lib.msa_last_error().decode()
+
+
+@pytest.mark.parametrize("over,fragment", [
+    (dict(sc=None), "score and topk_out"),
+    (dict(to=None), "score and topk_out"),
+    (dict(mb=0), "max_blocks"),
+    (dict(mb=16385), "max_blocks"),
+    (dict(k=0), "topk_k"),
+    (dict(k=65), "topk_k"),
+    (dict(scs=(1, -1, 1)), "score strides"),
+    (dict(ks=float("nan")), "k_scale"),
+    (dict(q=FAKE + 2), "q must be"),
+])
+def test_score_topk_rejects_bad_arguments(lib, over, fragment):
+    st, msg = _score(lib, shape(batch=2, decode_query_len=4), **over)
+    assert st == msa.MSA_ERR_INVALID_ARG and fragment in msg, (st, msg)
+
+
+def test_score_topk_validates_shape(lib):
+    st, msg = _score(lib, shape(decode_query_len=40))
+    assert st == msa.MSA_ERR_INVALID_ARG and "decode_query_len" in msg
+
+
+def test_topk_select_rejects_bad_arguments(lib):
+    scs = msa._I64x3(1, 1, 1)
+    assert lib.msa_topk_select(None, scs, 1, 8, 1, FAKE, 4, None) == msa.MSA_ERR_INVALID_ARG
+    assert lib.msa_topk_select(FAKE, scs, 1, 0, 1, FAKE, 4, None) == msa.MSA_ERR_INVALID_ARG
+    assert lib.msa_topk_select(FAKE, scs, 1, 8, 1, FAKE, 0, None) == msa.MSA_ERR_INVALID_ARG
+    assert lib.msa_topk_select(FAKE, scs, 0, 8, 1, FAKE, 4, None) == msa.MSA_ERR_INVALID_ARG
+
+
+def test_fp8_conversion_rejects_bad_arguments(lib):
+    assert lib.msa_fp8_e4m3_to_bf16(None, FAKE, 4, None) == msa.MSA_ERR_INVALID_ARG
+    assert lib.msa_fp8_e4m3_to_bf16(FAKE, FAKE, 0, None) == msa.MSA_ERR_INVALID_ARG
+
+
+def test_destroy_null_is_ok(lib):
+    assert lib.msa_sparse_decode_plan_destroy(None) == 0
+    assert lib.msa_last_error().decode() == ""

@@ -1,0 +1,342 @@
+"""GPU parity of the HIP decode path against the float64 oracle.
+
+Every case is seeded and synthetic (workloads/gen.py).  Shapes follow the
+pages: the test page's parity shapes (seq_lens 257/513 then 129/385 with the
+same plan, then a graph replay; heads (64,4) and (16,1); query lengths
+1,2,3,4,8), the five named workloads at full size on sampled rows, and
+randomized edge cases (-1 padding, padding rows, G < 16, NHD strides,
+transposed top-k views, non-unit scales, every split count).
+Tolerance: max abs <= 1e-2, relative L2 <= 1e-2, elementwise
+|a-o| <= 1e-2 + 1e-2|o| on the bf16 outputs.
+"""
+import numpy as np
+import pytest
+import torch
+
+import block_sparse_gqa_decode_amd as msa
+from oracle import msa_oracle as om
+from workloads import gen
+
+from gpu_helpers import DevCase, assert_parity, oracle_attend, to_f64
+
+pytestmark = pytest.mark.gpu
+
+
+def _banner(msg):
+    print(f"[case] {msg}", flush=True)
+
+
+# ---------------------------------------------------------------------------
+# the fp8 conversion the attend uses
+# ---------------------------------------------------------------------------
+
+def test_fp8_conversion_exhaustive():
+    _banner("fp8 e4m3fn -> bf16, all 256 codes")
+    codes = torch.arange(256, dtype=torch.int32).to(torch.uint8).repeat(5).cuda()
+    out = torch.empty(codes.numel(), dtype=torch.bfloat16, device="cuda")
+    msa.msa_fp8_e4m3_to_bf16(codes, out)
+    torch.cuda.synchronize()
+    got = to_f64(out)
+    ref = np.tile(om.decode_e4m3fn(np.arange(256)), 5)
+    assert np.array_equal(np.isnan(got), np.isnan(ref))
+    ok = ~np.isnan(ref)
+    assert np.array_equal(got[ok], ref[ok])
+
+
+# ---------------------------------------------------------------------------
+# the test page's shapes
+# ---------------------------------------------------------------------------
+
+P3_CASES = [
+    (64, 4, 8, 1, True), (64, 4, 8, 2, False), (64, 4, 8, 3, False), (64, 4, 8, 4, True),
+    (64, 4, 8, 8, False), (16, 1, 8, 1, True), (16, 1, 16, 4, True),
+]
+
+
+@pytest.mark.parametrize("hq,hkv,pairs,dql,capture", P3_CASES)
+def test_p3_shapes_with_replanned_lengths_and_graph(hq, hkv, pairs, dql, capture):
+    _banner(f"p3 heads=({hq},{hkv}) pairs={pairs} dql={dql} capture={capture}")
+    case = gen.make_p3_case(hq, hkv, pairs, dql, seq_pattern=(257, 513), seed=0)
+    d = DevCase(case)
+    plan = d.plan()
+    d.run(plan)
+    torch.cuda.synchronize()
+    assert_parity(to_f64(d.out), oracle_attend(case), what="seq 257/513")
+
+    # Same plan, ragged lengths changed in place (129/385).
+    case2 = gen.make_p3_case(hq, hkv, pairs, dql, seq_pattern=(257, 513), seed=0)
+    case2.seq_lens = np.array([129, 385] * pairs, dtype=np.int32)
+    case2.topk = gen.every_visible_topk(case2.seq_lens, hkv, dql, 16)
+    d.seq_lens.copy_(torch.from_numpy(case2.seq_lens))
+    d.topk.copy_(torch.from_numpy(case2.topk))
+    d.run(plan)
+    torch.cuda.synchronize()
+    assert_parity(to_f64(d.out), oracle_attend(case2), what="seq 129/385, same plan")
+
+    if capture:
+        g = torch.cuda.CUDAGraph()
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s):
+            d.run(plan)
+        torch.cuda.current_stream().wait_stream(s)
+        torch.cuda.synchronize()
+        with torch.cuda.graph(g):
+            d.run(plan)
+        for it, (pattern, c) in enumerate([((257, 513), case), ((129, 385), case2),
+                                           ((257, 513), case)]):
+            d.seq_lens.copy_(torch.from_numpy(c.seq_lens))
+            d.topk.copy_(torch.from_numpy(c.topk))
+            d.out.fill_(float("nan"))
+            torch.cuda.synchronize()
+            g.replay()
+            torch.cuda.synchronize()
+            assert_parity(to_f64(d.out), oracle_attend(c), what=f"graph replay {it} {pattern}")
+
+
+# ---------------------------------------------------------------------------
+# the tiny bf16 workload and randomized edge cases
+# ---------------------------------------------------------------------------
+
+def test_c1_tiny_bf16_all_rows():
+    _banner("c1 tiny bf16")
+    case = gen.make_config("c1_tiny_bf16")
+    d = DevCase(case)
+    for splits in (0, 1, 2, 4):
+        d.out.fill_(float("nan"))
+        d.run(d.plan(splits))
+        torch.cuda.synchronize()
+        assert_parity(to_f64(d.out), oracle_attend(case), what=f"c1 splits={splits}")
+
+
+RANDOM_CASES = [
+    # seed, batch, dql, hq, hkv, k, seq_lo, seq_hi, kv_dtype, pad, neg_frac, splits, layout
+    (101, 3, 1, 16, 1, 16, 1, 3000, gen.KV_FP8, 0, 0.0, 0, "hnd"),
+    (102, 4, 4, 64, 4, 16, 300, 5000, gen.KV_FP8, 2, 0.2, 0, "hnd"),
+    (103, 2, 8, 32, 4, 8, 129, 1200, gen.KV_BF16, 1, 0.1, 3, "hnd"),
+    (104, 5, 2, 16, 4, 12, 1, 2500, gen.KV_FP8, 3, 0.3, 16, "hnd"),
+    (105, 3, 3, 8, 8, 5, 100, 700, gen.KV_FP8, 0, 0.0, 1, "nhd"),
+    (106, 2, 32, 64, 4, 16, 200, 1900, gen.KV_FP8, 4, 0.0, 0, "hnd"),
+    (107, 6, 1, 12, 3, 64, 5000, 9000, gen.KV_FP8, 0, 0.5, 2, "nhd"),
+    (108, 2, 5, 16, 1, 16, 1, 40, gen.KV_BF16, 2, 0.0, 8, "hnd"),
+]
+
+
+@pytest.mark.parametrize("seed,batch,dql,hq,hkv,k,lo,hi,kvd,pad,neg,splits,layout",
+                         RANDOM_CASES)
+def test_random_cases(seed, batch, dql, hq, hkv, k, lo, hi, kvd, pad, neg, splits, layout):
+    _banner(f"random seed={seed} B={batch} dql={dql} heads=({hq},{hkv}) k={k} "
+            f"kv={kvd} pad={pad} splits={splits} layout={layout}")
+    case = gen.make_random_case(seed, batch, dql, hq, hkv, k, lo, hi, kv_dtype=kvd,
+                                pad_rows=pad, neg_frac=neg)
+    d = DevCase(case, layout=layout)
+    d.run(d.plan(splits))
+    torch.cuda.synchronize()
+    got = to_f64(d.out)
+    ref = oracle_attend(case)
+    assert_parity(got, ref, what=f"random {seed}")
+    assert np.all(got[case.real_rows:] == 0.0)
+
+
+def test_scales_and_transposed_topk_view():
+    _banner("k/v scales + head-major top-k view")
+    case = gen.make_random_case(111, 4, 4, 64, 4, 16, 400, 4000)
+    case.k_scale, case.v_scale = 0.5, 1.75
+    d = DevCase(case)
+    # Head-major physical buffer [Hkv, rows, k] viewed as [rows, Hkv, k].
+    tk_hm = torch.from_numpy(np.ascontiguousarray(case.topk.transpose(1, 0, 2))).cuda()
+    d.run(d.plan(), topk=tk_hm.transpose(0, 1))
+    torch.cuda.synchronize()
+    assert_parity(to_f64(d.out), oracle_attend(case), what="scales + strided topk")
+
+
+def test_all_minus_one_and_padding_rows_are_exact_zeros():
+    _banner("zero rows")
+    case = gen.make_random_case(112, 4, 2, 16, 1, 16, 500, 3000, pad_rows=3)
+    topk = case.topk.copy()
+    topk[1] = -1
+    topk[4, 0, :] = -1
+    case.topk = topk
+    d = DevCase(case)
+    for splits in (1, 4):
+        d.out.fill_(float("nan"))
+        d.run(d.plan(splits))
+        torch.cuda.synchronize()
+        got = to_f64(d.out)
+        for t in (1, 4, 8, 9, 10):
+            assert np.all(got[t] == 0.0) and not np.signbit(got[t]).any(), (t, splits)
+        assert_parity(got, oracle_attend(case), what=f"zero rows splits={splits}")
+
+
+def test_invisible_indices_and_out_of_range_blocks_are_skipped():
+    _banner("invisible / beyond-table indices")
+    case = gen.make_random_case(113, 3, 4, 16, 1, 16, 600, 2000, stride_extra=0)
+    topk = case.topk.copy()
+    rng = np.random.default_rng(0)
+    for t in range(case.real_rows):
+        r, loc = divmod(t, case.dql)
+        pos = int(case.seq_lens[r]) - case.dql + loc
+        slots = rng.choice(16, size=2, replace=False)
+        topk[t, 0, slots[0]] = pos // 128 + 1             # starts after the position
+        topk[t, 0, slots[1]] = case.block_table.shape[1] + 7  # beyond the table row
+    case_ref = gen.make_random_case(113, 3, 4, 16, 1, 16, 600, 2000)
+    case_ref.topk = topk
+    d = DevCase(case)
+    d.run(d.plan(), topk=torch.from_numpy(topk).cuda())
+    torch.cuda.synchronize()
+    assert_parity(to_f64(d.out), oracle_attend(case_ref), what="skipped indices")
+
+
+def test_deterministic_bitwise():
+    _banner("determinism")
+    case = gen.make_random_case(114, 8, 4, 16, 1, 16, 2000, 20000)
+    d = DevCase(case)
+    plan = d.plan()
+    a = d.run(plan, out=torch.empty_like(d.q)).clone()
+    b = d.run(plan, out=torch.empty_like(d.q)).clone()
+    torch.cuda.synchronize()
+    assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+
+
+# ---------------------------------------------------------------------------
+# the named workloads at full size, in the launch configuration the bench
+# uses, checked on sampled rows the oracle evaluates one by one
+# ---------------------------------------------------------------------------
+
+def _sample_rows(case, n, seed):
+    rng = np.random.default_rng(seed)
+    rows = rng.choice(case.real_rows, size=min(n, case.real_rows), replace=False)
+    extra = list(range(case.real_rows, case.num_token_rows))
+    return sorted(set(rows.tolist())) + extra
+
+
+@pytest.mark.parametrize("name,nrows", [("c2_tp4_fp8", 40), ("c3_tp1_fp8", 24),
+                                        ("c4_spec_ragged", 48)])
+def test_named_workload_full_size(name, nrows):
+    _banner(f"{name} full size")
+    case = gen.make_config(name)
+    d = DevCase(case)
+    d.run(d.plan())
+    torch.cuda.synchronize()
+    rows = _sample_rows(case, nrows, 7)
+    if name == "c4_spec_ragged":
+        # make sure both long and short requests are covered
+        long_rows = [t for t in range(case.real_rows)
+                     if case.seq_lens[t // case.dql] == 131072][:8]
+        short_rows = [t for t in range(case.real_rows)
+                      if case.seq_lens[t // case.dql] < 2000][:8]
+        rows = sorted(set(rows) | set(long_rows) | set(short_rows))
+    got = to_f64(d.out)[rows]
+    ref = oracle_attend(case, rows=rows)
+    assert_parity(got, ref, what=f"{name} {len(rows)} sampled rows")
+    if case.num_token_rows > case.real_rows:
+        assert np.all(to_f64(d.out)[case.real_rows:] == 0.0)
+
+
+# ---------------------------------------------------------------------------
+# indexer scorer and top-k selector
+# ---------------------------------------------------------------------------
+
+def _run_scorer(d: DevCase, max_blocks, k, transposed=False):
+    c = d.case
+    rows = c.num_token_rows
+    if transposed:
+        # physical [Hkv, rows, blocks], logical [Hkv, blocks, rows]
+        phys = torch.full((c.num_kv_heads, rows, max_blocks), float("nan"), device="cuda")
+        score = phys.transpose(1, 2)
+    else:
+        score = torch.full((c.num_kv_heads, max_blocks, rows), float("nan"), device="cuda")
+    topk_out = torch.full((rows, c.num_kv_heads, k), -7, dtype=torch.int32, device="cuda")
+    msa.msa_block_score_topk(d.q, d.kv, d.block_table, d.seq_lens, decode_query_len=c.dql,
+                             num_kv_heads=c.num_kv_heads, max_blocks=max_blocks, score=score,
+                             topk_out=topk_out, k_scale=c.k_scale, num_token_rows=rows)
+    torch.cuda.synchronize()
+    return score.cpu().numpy().astype(np.float64), topk_out.cpu().numpy()
+
+
+def _scores_close(got, ref):
+    assert np.array_equal(np.isneginf(got), np.isneginf(ref))
+    fin = np.isfinite(ref)
+    assert np.isfinite(got[fin]).all()
+    tol = 2e-5 * np.max(np.abs(ref[fin])) + 1e-5
+    err = float(np.max(np.abs(got[fin] - ref[fin]))) if fin.any() else 0.0
+    print(f"[parity] scores: max_abs={err:.3e} tol={tol:.3e}", flush=True)
+    assert err <= tol
+    return tol
+
+
+@pytest.mark.parametrize("kvd,dql,hq,hkv,transposed", [
+    (gen.KV_FP8, 1, 64, 4, False), (gen.KV_FP8, 4, 16, 1, True), (gen.KV_BF16, 2, 32, 4, False),
+    (gen.KV_FP8, 3, 8, 2, True)])
+def test_scorer_matches_oracle(kvd, dql, hq, hkv, transposed):
+    _banner(f"scorer kv={kvd} dql={dql} heads=({hq},{hkv}) transposed={transposed}")
+    case = gen.make_random_case(121, 3, dql, hq, hkv, 16, 100, 3000, kv_dtype=kvd, pad_rows=2)
+    case.k_scale = 0.75
+    d = DevCase(case)
+    mb = case.max_blocks + 2
+    score, _ = _run_scorer(d, mb, 16, transposed)
+    ref = om.block_max_scores(case.q, case.kv, case.kv_dtype, case.k_scale, case.block_table,
+                              case.seq_lens, case.dql, case.num_kv_heads, mb)
+    _scores_close(score[:, :, :case.real_rows], ref)
+    assert np.all(np.isneginf(score[:, :, case.real_rows:]))
+
+
+@pytest.mark.parametrize("tie_frac,transposed,k", [(0.0, False, 16), (0.4, False, 16),
+                                                   (0.4, True, 5), (0.0, True, 64)])
+def test_selector_bit_exact_on_given_scores(tie_frac, transposed, k):
+    _banner(f"selector ties={tie_frac} transposed={transposed} k={k}")
+    seq = np.array([129, 700, 5000, 20000], dtype=np.int32)
+    nb = 160
+    sc = gen.make_scores(131, 3, nb, 8, seq, 2, tie_frac=tie_frac)
+    if transposed:
+        dev = torch.from_numpy(np.ascontiguousarray(sc.transpose(0, 2, 1))).cuda().transpose(1, 2)
+    else:
+        dev = torch.from_numpy(sc).cuda()
+    out = torch.full((8, 3, k), -7, dtype=torch.int32, device="cuda")
+    msa.msa_topk_select(dev, out)
+    torch.cuda.synchronize()
+    ref = om.select_topk(sc.astype(np.float64), k)
+    assert np.array_equal(out.cpu().numpy(), ref)
+
+
+def _gap_ok_rows(ref_scores, k, eps):
+    """(t, h) pairs whose oracle k-th and (k+1)-th scores differ by > eps."""
+    hkv, nb, nt = ref_scores.shape
+    ok = np.zeros((nt, hkv), dtype=bool)
+    for h in range(hkv):
+        for t in range(nt):
+            s = np.sort(ref_scores[h, :, t][np.isfinite(ref_scores[h, :, t])])[::-1]
+            if len(s) <= k:
+                ok[t, h] = True
+            else:
+                ok[t, h] = (s[k - 1] - s[k]) > eps and np.all(np.diff(s[:k + 1]) != 0)
+    return ok
+
+
+def test_full_step_score_select_attend():
+    _banner("full step: score -> top-16 -> attend")
+    case = gen.make_random_case(141, 6, 1, 64, 4, 16, 3000, 30000)
+    d = DevCase(case)
+    mb = case.max_blocks
+    score, sel = _run_scorer(d, mb, 16)
+    ref_scores = om.block_max_scores(case.q, case.kv, case.kv_dtype, case.k_scale,
+                                     case.block_table, case.seq_lens, case.dql,
+                                     case.num_kv_heads, mb)
+    tol = _scores_close(score[:, :, :case.real_rows], ref_scores)
+    ref_sel = om.select_topk(ref_scores, 16)
+    ok = _gap_ok_rows(ref_scores, 16, 4 * tol)
+    assert ok.mean() > 0.8
+    assert np.array_equal(sel[ok], ref_sel[ok])
+    # Rows without a clear gap: every GPU pick scores within tolerance of the
+    # oracle's k-th best.
+    for t, h in zip(*np.nonzero(~ok)):
+        kth = np.sort(ref_scores[h, :, t][np.isfinite(ref_scores[h, :, t])])[::-1][15]
+        for b in sel[t, h]:
+            assert b >= 0 and ref_scores[h, b, t] >= kth - 4 * tol
+    # Attend over the GPU's own selection, compared where it equals the oracle's.
+    case.topk = ref_sel
+    out = torch.full_like(d.q, float("nan"))
+    d.run(d.plan(), topk=torch.from_numpy(sel).cuda(), out=out)
+    torch.cuda.synchronize()
+    rows = [t for t in range(case.real_rows) if ok[t].all()]
+    assert_parity(to_f64(out)[rows], oracle_attend(case, rows=rows), what="full step")

@@ -25,6 +25,8 @@ patterns, indices as ``int32``.
 from __future__ import annotations
 
 import math
+import os
+from concurrent.futures import ThreadPoolExecutor
 from dataclasses import dataclass, field
 
 import numpy as np
@@ -210,14 +212,32 @@ def fill_pages(kv: np.ndarray, pages, kv_dtype: str) -> None:
 
 
 def make_pool(rng: np.random.Generator, num_pages: int, num_kv_heads: int,
-              kv_dtype: str, std: float, chunk_pages: int = 512) -> np.ndarray:
-    """Packed K|V pool ``(num_pages, Hkv, 128, 256)``; values N(0, std) encoded."""
+              kv_dtype: str, std: float, chunk_pages: int = 256) -> np.ndarray:
+    """Packed K|V pool ``(num_pages, Hkv, 128, 256)``; values N(0, std) encoded.
+
+    One 63-bit pool seed is drawn from ``rng``; page chunk ``i`` is then drawn
+    from ``default_rng([pool_seed, i])``, so chunks are independent,
+    reproducible one at a time, and generated on several threads.
+    """
     dt = np.uint8 if kv_dtype == KV_FP8 else np.uint16
     kv = np.empty((num_pages, num_kv_heads, PAGE, 2 * HEAD_DIM), dtype=dt)
-    for p0 in range(0, num_pages, chunk_pages):
+    pool_seed = int(rng.integers(0, 2 ** 63 - 1))
+
+    def fill(i):
+        p0 = i * chunk_pages
         p1 = min(num_pages, p0 + chunk_pages)
-        x = _normal_f32(rng, (p1 - p0, num_kv_heads, PAGE, 2 * HEAD_DIM), std)
+        crng = np.random.default_rng([pool_seed, i])
+        x = _normal_f32(crng, (p1 - p0, num_kv_heads, PAGE, 2 * HEAD_DIM), std)
         kv[p0:p1] = _encode(x, kv_dtype)
+
+    n_chunks = (num_pages + chunk_pages - 1) // chunk_pages
+    workers = max(1, min(8, os.cpu_count() or 1, n_chunks))
+    if workers == 1:
+        for i in range(n_chunks):
+            fill(i)
+    else:
+        with ThreadPoolExecutor(max_workers=workers) as ex:
+            list(ex.map(fill, range(n_chunks)))
     return kv
 
 
