@@ -1,0 +1,463 @@
+#!/usr/bin/env python3
+"""Benchmark of the block-sparse GQA decode attend on one MI355X.
+
+Metric: decode tokens/s and effective KV GB/s (% of HBM peak) of the sparse
+GQA attend.  Default workload: the TP4-shaped fp8 decode (batch 32, decode
+query length 4, 16 q heads / 1 kv head, head dim 128, page 128, top-16,
+fp8 e4m3 packed K|V cache, seq_lens uniform in [16384, 65536]).
+
+A step is one call of ``msa_sparse_decode_run`` (page gather, fp8 dequant,
+MFMA QK^T / PV, online softmax, split-K with the fused log-sum-exp merge and
+zeroed padding rows: one kernel launch) over one batch.  Timing:
+
+* R independent (q, top-k) replicas, each over its own device copy of the KV
+  pool, so a cycle of R steps touches more bytes than the 256 MiB MALL holds
+  and pages are read from HBM;
+* all R steps are captured in one HIP graph; W warm-up steps, then exactly K
+  timed steps between two synchronisations, timed with HIP events recorded on
+  the stream the kernels run on (and with the host clock as a cross-check);
+* algorithmic bytes per step = every live (token, kv head, selected page)'s
+  visible K|V rows + q + out + indices + block-table entries (the bytes the
+  attend must move as defined per token), and the unique-page lower bound.
+
+With --profile-mode the script instead launches eagerly (no graph) a few
+steps for rocprofv3 kernel traces and counters; --copy-calibration runs a
+plain device copy of known size for the counter scale factor.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "decode tokens/s and effective KV GB/s (% HBM peak), sparse GQA attend, 1 GPU"
+HBM_PEAK_GBS = 8000.0
+DEFAULT_CONFIG = "c2_tp4_fp8"
+OTHER_CONFIGS = ("c3_tp1_fp8", "c4_spec_ragged")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attend_traffic.json")
+KERNEL_SOURCES = ("block_sparse_gqa_decode_amd/csrc/msa_attend.hip",
+                  "block_sparse_gqa_decode_amd/csrc/msa_device.h",
+                  "block_sparse_gqa_decode_amd/csrc/msa_internal.h")
+
+CONFIG_TEXT = {
+    "c1_tiny_bf16": "tiny bf16 decode: B=2, dql=1, 16/1 heads, top-4, seq {512,1000}",
+    "c2_tp4_fp8": "TP4-shaped fp8 decode: B=32, dql=4, 16/1 heads, top-16, "
+                  "seq U[16384,65536]",
+    "c3_tp1_fp8": "TP1-shaped fp8 decode: B=16, dql=4, 64/4 heads, top-16, "
+                  "seq U[32768,131072], Zipf-recent indices",
+    "c4_spec_ragged": "speculative/ragged fp8 decode: B=16, dql=32, 64/4 heads, top-16, "
+                      "8 requests at 131072 + 8 in [200,1900], 4 padding rows",
+}
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+# ---------------------------------------------------------------------------
+# byte accounting
+# ---------------------------------------------------------------------------
+
+def step_bytes(case, q, topk):
+    """Algorithmic bytes of one attend step (see module docstring)."""
+    import numpy as np
+
+    e = 1 if case.kv_dtype == "fp8_e4m3" else 2
+    row_bytes = 2 * 128 * e
+    real = case.real_rows
+    t = np.arange(real)
+    r = t // case.dql
+    pos = case.seq_lens[r].astype(np.int64) - case.dql + (t % case.dql)
+    b = topk[:real].astype(np.int64)                       # [T, Hkv, k]
+    start = b * 128
+    live = (b >= 0) & (start <= pos[:, None, None]) & (b < case.block_table.shape[1])
+    nvis = np.where(live, np.minimum(128, pos[:, None, None] - start + 1), 0)
+    eff_kv = int(nvis.sum()) * row_bytes
+    # unique (request, head, block) pages, at their largest visible count
+    hh = np.broadcast_to(np.arange(case.num_kv_heads)[None, :, None], b.shape)
+    rr = np.broadcast_to(r[:, None, None], b.shape)
+    key = (rr[live].astype(np.int64) * case.num_kv_heads + hh[live]) * (1 << 22) + b[live]
+    order = np.lexsort((-nvis[live], key))
+    ks, nv = key[order], nvis[live][order]
+    first = np.ones(len(ks), dtype=bool)
+    first[1:] = ks[1:] != ks[:-1]
+    uniq_kv = int(nv[first].sum()) * row_bytes
+    n_live = int(live.sum())
+    q_bytes = real * case.num_q_heads * 128 * 2
+    out_bytes = case.num_token_rows * case.num_q_heads * 128 * 2
+    idx_bytes = real * case.num_kv_heads * case.topk_k * 4
+    meta = idx_bytes + n_live * 4 + case.batch * 4
+    return {
+        "effective_kv": eff_kv,
+        "unique_kv": uniq_kv,
+        "q_out_meta": q_bytes + out_bytes + meta,
+        "algorithmic": eff_kv + q_bytes + out_bytes + meta,
+        "live_pages": n_live,
+    }
+
+
+# ---------------------------------------------------------------------------
+# device setup
+# ---------------------------------------------------------------------------
+
+class DeviceSet:
+    """R replicas of one step's inputs, each over its own copy of the pool."""
+
+    def __init__(self, case, replicas: int, splits: int, dev):
+        import numpy as np
+        import torch
+
+        import block_sparse_gqa_decode_amd as msa
+
+        self.case = case
+        fp8 = case.kv_dtype == "fp8_e4m3"
+        host = torch.from_numpy(case.kv) if fp8 else \
+            torch.from_numpy(case.kv.view(np.int16)).view(torch.bfloat16)
+        nb = case.num_blocks
+        self.kv = torch.empty((replicas * nb,) + tuple(host.shape[1:]), dtype=host.dtype,
+                              device=dev)
+        self.kv[:nb].copy_(host)
+        for i in range(1, replicas):
+            self.kv[i * nb:(i + 1) * nb].copy_(self.kv[:nb])
+        self.seq_lens = torch.from_numpy(case.seq_lens).to(dev)
+        sets = [(case.q, case.topk)] + list(case.replicas)
+        assert len(sets) >= replicas, "not enough replicas generated"
+        self.steps = []
+        self.bytes = []
+        for i in range(replicas):
+            qh, tk = sets[i]
+            bt = torch.from_numpy((case.block_table.astype(np.int64) + i * nb).astype(
+                np.int32)).to(dev)
+            q = torch.from_numpy(qh.view(np.int16)).view(torch.bfloat16).to(dev)
+            topk = torch.from_numpy(tk).to(dev)
+            out = torch.empty_like(q)
+            self.steps.append((q, bt, topk, out))
+            self.bytes.append(step_bytes(case, qh, tk))
+        self.plan = msa.msa_sparse_decode_plan(
+            case.batch, case.dql, num_q_heads=case.num_q_heads,
+            num_kv_heads=case.num_kv_heads, page_table_stride=case.block_table.shape[1],
+            topk_blocks=case.topk_k,
+            kv_dtype=msa.KV_FP8_E4M3 if fp8 else msa.KV_BF16,
+            num_token_rows=case.num_token_rows, num_splits=splits, device=dev)
+        self.msa = msa
+
+    def run_step(self, i):
+        q, bt, topk, out = self.steps[i]
+        c = self.case
+        self.msa.msa_sparse_decode_run(self.plan, q, self.kv, bt, self.seq_lens, topk, out,
+                                       sm_scale=c.sm_scale, k_scale=c.k_scale,
+                                       v_scale=c.v_scale)
+
+    def run_attend(self, i):
+        q, bt, topk, out = self.steps[i]
+        c = self.case
+        self.msa.msa_sparse_decode_attend(self.plan, q, self.kv, bt, self.seq_lens, topk, out,
+                                          sm_scale=c.sm_scale, k_scale=c.k_scale,
+                                          v_scale=c.v_scale)
+
+    def mean_bytes(self, key):
+        return sum(b[key] for b in self.bytes) / len(self.bytes)
+
+
+def time_config(name, steps, warmup, replicas, splits, dev, verbose=True):
+    import torch
+
+    from workloads import gen
+
+    t0 = time.time()
+    case = gen.make_config(name, replicas=replicas - 1)
+    ds = DeviceSet(case, replicas, splits, dev)
+    if verbose:
+        print(f"[bench] {name}: generated + uploaded in {time.time() - t0:.1f}s "
+              f"(pool {case.kv.nbytes / 2**20:.0f} MiB x {replicas}, splits "
+              f"{ds.plan.num_splits})", file=sys.stderr, flush=True)
+
+    # Warm the plan on a side stream, then capture the R steps in one graph,
+    # and the R attend launches alone in a second graph.
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        for i in range(replicas):
+            ds.run_step(i)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        for i in range(replicas):
+            ds.run_step(i)
+    attend_graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(attend_graph):
+        for i in range(replicas):
+            ds.run_attend(i)
+    torch.cuda.synchronize()
+
+    def timed(g, n_replays):
+        ev0 = torch.cuda.Event(enable_timing=True)
+        ev1 = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        h0 = time.perf_counter()
+        ev0.record()
+        for _ in range(n_replays):
+            g.replay()
+        ev1.record()
+        torch.cuda.synchronize()
+        return ev0.elapsed_time(ev1), time.perf_counter() - h0
+
+    warm_replays = max(1, (warmup + replicas - 1) // replicas)
+    replays = max(1, (steps + replicas - 1) // replicas)
+    n_steps = replays * replicas
+    for _ in range(warm_replays):
+        graph.replay()
+    gpu_ms, host_s = timed(graph, replays)
+    ms_step = gpu_ms / n_steps
+    # The attend kernel alone: same launches, without the merge pass.
+    for _ in range(warm_replays):
+        attend_graph.replay()
+    attend_ms, _ = timed(attend_graph, replays)
+    attend_ms /= n_steps
+    eff = ds.mean_bytes("effective_kv")
+    uniq = ds.mean_bytes("unique_kv")
+    alg = ds.mean_bytes("algorithmic")
+    s = ms_step / 1e3
+    res = {
+        "config": name,
+        "steps": n_steps,
+        "ms_per_step": ms_step,
+        "host_ms_per_step": host_s * 1e3 / n_steps,
+        "tokens_per_s": case.real_rows / s,
+        "effective_kv_gbs": eff / s / 1e9,
+        "unique_kv_gbs": uniq / s / 1e9,
+        "algorithmic_gbs": alg / s / 1e9,
+        "effective_kv_bytes": eff,
+        "unique_kv_bytes": uniq,
+        "algorithmic_bytes": alg,
+        "splits": ds.plan.num_splits,
+        "launches_per_step": 1 if ds.plan.num_splits == 1 else 2,
+        "attend_ms": attend_ms,
+        "real_rows": case.real_rows,
+    }
+    res["effective_pct_peak"] = 100.0 * res["effective_kv_gbs"] / HBM_PEAK_GBS
+    res["unique_pct_peak"] = 100.0 * res["unique_kv_gbs"] / HBM_PEAK_GBS
+    del graph, attend_graph
+    return res, case
+
+
+def cpu_baseline(case, seconds: float):
+    """The float64 oracle, single-threaded, on a bounded sample of the same
+    workload's token rows; scaled to tokens/s."""
+    import numpy as np
+
+    try:
+        from threadpoolctl import threadpool_limits
+    except ImportError:  # pragma: no cover
+        threadpool_limits = None
+    from oracle import msa_oracle as om
+
+    rows_done = 0
+    t0 = time.perf_counter()
+    ctx = threadpool_limits(limits=1) if threadpool_limits else None
+    if ctx is not None:
+        ctx.__enter__()
+    try:
+        order = np.random.default_rng(0).permutation(case.real_rows)
+        done = False
+        while not done:
+            for t in order:
+                om.sparse_decode(case.q, case.kv, case.kv_dtype, case.k_scale,
+                                 case.v_scale, case.block_table, case.seq_lens, case.topk,
+                                 case.dql, case.num_kv_heads, case.sm_scale, rows=[int(t)])
+                rows_done += 1
+                if time.perf_counter() - t0 >= seconds:
+                    done = True
+                    break
+    finally:
+        if ctx is not None:
+            ctx.__exit__(None, None, None)
+    el = time.perf_counter() - t0
+    b = step_bytes(case, case.q, case.topk)
+    per_row_bytes = b["effective_kv"] / case.real_rows
+    return {
+        "value": rows_done / el,
+        "unit": "tokens/s",
+        "cores": 1,
+        "kind": "oracle",
+        "sample": f"{rows_done} token rows (passes over the {case.real_rows} rows of "
+                  f"replica 0 in a seeded order; {rows_done * case.num_kv_heads} "
+                  f"(token, kv head) units), {el:.1f} s, one thread (BLAS limited to 1)",
+        "effective_kv_gbs": rows_done * per_row_bytes / el / 1e9,
+        "host_cpus": len(os.sched_getaffinity(0)),
+    }
+
+
+def load_traffic(src_hash):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, if it
+    was taken on the current kernel source; else None."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if rec.get("kernel_source_sha") != src_hash:
+        return None
+    return rec
+
+
+def profile_mode(name, launches, splits, dev):
+    """Eager launches of whole steps for rocprofv3 (kernel trace / counters)."""
+    import torch
+
+    from workloads import gen
+
+    case = gen.make_config(name, replicas=1)
+    ds = DeviceSet(case, 2, splits, dev)
+    for i in range(launches):
+        ds.run_step(i % 2)
+    torch.cuda.synchronize()
+    b = ds.mean_bytes("algorithmic")
+    print(json.dumps({"profile_mode": name, "launches": launches,
+                      "algorithmic_bytes_per_launch": b,
+                      "effective_kv_bytes_per_launch": ds.mean_bytes("effective_kv"),
+                      "unique_kv_bytes_per_launch": ds.mean_bytes("unique_kv"),
+                      "kernel_source_sha": kernel_source_hash()}), flush=True)
+
+
+def copy_calibration(dev, mib=1024, launches=4):
+    """A plain device copy of known size: the FETCH_SIZE / WRITE_SIZE scale."""
+    import torch
+
+    n = mib * 2**20
+    a = torch.empty(n, dtype=torch.uint8, device=dev)
+    a.fill_(1)
+    b = torch.empty_like(a)
+    torch.cuda.synchronize()
+    for _ in range(launches):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes": n, "launches": launches}), flush=True)
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=400)
+    ap.add_argument("--warmup", type=int, default=40)
+    ap.add_argument("--config", default=DEFAULT_CONFIG, choices=sorted(CONFIG_TEXT))
+    ap.add_argument("--replicas", type=int, default=8)
+    ap.add_argument("--splits", type=int, default=0, help="0 = the plan's choice")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-other-configs", action="store_true")
+    ap.add_argument("--profile-mode", action="store_true")
+    ap.add_argument("--profile-launches", type=int, default=20)
+    ap.add_argument("--copy-calibration", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only: this build has no multi-GPU path "
+              f"(--gpus {args.gpus} requested). The decode step shards by kv head or by "
+              f"request with no exchange, so each GPU would run this same kernel on its "
+              f"share.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    dev = torch.device("cuda:0")
+    import block_sparse_gqa_decode_amd as msa
+
+    msa.load_library()  # fail loudly if the HIP library is missing
+
+    if args.copy_calibration:
+        copy_calibration(dev)
+        return
+    if args.profile_mode:
+        profile_mode(args.config, args.profile_launches, args.splits, dev)
+        return
+
+    res, case = time_config(args.config, args.steps, args.warmup, args.replicas,
+                            args.splits, dev)
+    others = {}
+    if not args.no_other_configs:
+        for name in OTHER_CONFIGS:
+            if name == args.config:
+                continue
+            r2, _ = time_config(name, max(64, args.steps // 4), args.warmup,
+                                args.replicas, args.splits, dev)
+            others[name] = {k: (round(v, 4) if isinstance(v, float) else v)
+                            for k, v in r2.items()}
+    src_hash = kernel_source_hash()
+    traffic = load_traffic(src_hash)
+    kernel_s = res["attend_ms"] / 1e3
+    achieved = res["algorithmic_bytes"] / kernel_s / 1e9
+    roofline = {
+        "bound": "hbm",
+        "achieved": round(achieved, 1),
+        "peak": HBM_PEAK_GBS,
+        "unit": "GB/s",
+        "frac": round(achieved / HBM_PEAK_GBS, 4),
+        "traffic": None if traffic is None else traffic.get("hbm_bytes_per_launch"),
+        "kernel": "attend_kernel<fp8>" if case.kv_dtype == "fp8_e4m3" else
+                  "attend_kernel<bf16>",
+        "algorithmic_bytes_per_launch": int(res["algorithmic_bytes"]),
+        "avg_launch_us": round(kernel_s * 1e6, 3),
+        "timing": "HIP events around graph replays of the attend launches alone, on "
+                  "the stream they run on",
+    }
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(case, args.cpu_seconds)
+    line = {
+        "metric": METRIC,
+        "value": round(res["tokens_per_s"], 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": res["steps"],
+        "warmup": args.warmup,
+        "ms_per_step": round(res["ms_per_step"], 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": f"{args.config}: {CONFIG_TEXT[args.config]}",
+            "kv_cache": case.kv_dtype,
+            "global_batch": case.batch,
+            "decode_query_len": case.dql,
+            "num_q_heads": case.num_q_heads,
+            "num_kv_heads": case.num_kv_heads,
+            "topk_blocks": case.topk_k,
+            "page_size": 128,
+            "head_dim": 128,
+            "replicas": args.replicas,
+            "splits": res["splits"],
+            "parallelism": "single GPU",
+        },
+        "effective_kv_gbs": round(res["effective_kv_gbs"], 1),
+        "effective_pct_hbm_peak": round(res["effective_pct_peak"], 2),
+        "unique_kv_gbs": round(res["unique_kv_gbs"], 1),
+        "unique_pct_hbm_peak": round(res["unique_pct_peak"], 2),
+        "host_ms_per_step": round(res["host_ms_per_step"], 5),
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "other_configs": others,
+        "kernel_source_sha": src_hash,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

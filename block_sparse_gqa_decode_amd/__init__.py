@@ -32,7 +32,8 @@ import torch
 
 __all__ = [
     "MsaError", "MsaInvalidArgument", "MsaUnsupported", "DecodePlan", "PlanCache",
-    "msa_sparse_decode_plan", "msa_sparse_decode_run", "msa_block_score_topk",
+    "msa_sparse_decode_plan", "msa_sparse_decode_run", "msa_sparse_decode_attend",
+    "msa_sparse_decode_merge", "msa_block_score_topk",
     "msa_topk_select", "msa_fp8_e4m3_to_bf16", "library_path", "load_library",
     "KV_BF16", "KV_FP8_E4M3", "PAGE_SIZE", "HEAD_DIM",
 ]
@@ -103,6 +104,9 @@ def load_library():
                                               ctypes.POINTER(_Shape)]),
         "msa_sparse_decode_run": (i32, [vp, vp, vp, pi64, i64, f32, f32, vp, vp, vp,
                                         pi64, vp, f32, vp]),
+        "msa_sparse_decode_attend": (i32, [vp, vp, vp, pi64, i64, f32, f32, vp, vp, vp,
+                                           pi64, vp, f32, vp]),
+        "msa_sparse_decode_merge": (i32, [vp, vp, f32, vp]),
         "msa_block_score_topk": (i32, [ctypes.POINTER(_Shape), vp, vp, pi64, i64, f32,
                                        vp, vp, i32, vp, pi64, vp, i32, vp]),
         "msa_topk_select": (i32, [vp, pi64, i32, i32, i32, vp, i32, vp]),
@@ -236,11 +240,7 @@ def msa_sparse_decode_plan(batch: int, decode_query_len: int, *, num_q_heads: in
     return DecodePlan(handle.value, int(dev))
 
 
-def msa_sparse_decode_run(plan: DecodePlan, q: torch.Tensor, kv_cache: torch.Tensor,
-                          block_table: torch.Tensor, seq_lens: torch.Tensor,
-                          topk: torch.Tensor, out: torch.Tensor, *, sm_scale: float,
-                          k_scale: float = 1.0, v_scale: float = 1.0, stream=None) -> None:
-    """out[t, j] = sparse causal attention of q[t, j] over the selected pages."""
+def _run_args(plan, q, kv_cache, block_table, seq_lens, topk, out):
     rows = plan.num_token_rows
     _check_q(q, "q", rows, plan.num_q_heads)
     _check_q(out, "out", rows, plan.num_q_heads)
@@ -258,13 +258,40 @@ def msa_sparse_decode_run(plan: DecodePlan, q: torch.Tensor, kv_cache: torch.Ten
                     ("q", q), ("out", out)):
         if t.device != seq_lens.device:
             raise ValueError(f"{name} is not on the sequence-length device")
-    kvs = _I64x4(*kv_cache.stride())
-    tks = _I64x3(*topk.stride())
+    return (plan.handle, q.data_ptr(), kv_cache.data_ptr(), _I64x4(*kv_cache.stride()),
+            kv_cache.shape[0])
+
+
+def msa_sparse_decode_run(plan: DecodePlan, q: torch.Tensor, kv_cache: torch.Tensor,
+                          block_table: torch.Tensor, seq_lens: torch.Tensor,
+                          topk: torch.Tensor, out: torch.Tensor, *, sm_scale: float,
+                          k_scale: float = 1.0, v_scale: float = 1.0, stream=None) -> None:
+    """out[t, j] = sparse causal attention of q[t, j] over the selected pages."""
+    head = _run_args(plan, q, kv_cache, block_table, seq_lens, topk, out)
     _check(load_library().msa_sparse_decode_run(
-        plan.handle, q.data_ptr(), kv_cache.data_ptr(), kvs, kv_cache.shape[0],
-        float(k_scale), float(v_scale), block_table.data_ptr(), seq_lens.data_ptr(),
-        topk.data_ptr(), tks, out.data_ptr(), float(sm_scale),
+        *head, float(k_scale), float(v_scale), block_table.data_ptr(), seq_lens.data_ptr(),
+        topk.data_ptr(), _I64x3(*topk.stride()), out.data_ptr(), float(sm_scale),
         _stream_handle(stream, q.device)))
+
+
+def msa_sparse_decode_attend(plan: DecodePlan, q: torch.Tensor, kv_cache: torch.Tensor,
+                             block_table: torch.Tensor, seq_lens: torch.Tensor,
+                             topk: torch.Tensor, out: torch.Tensor, *, sm_scale: float,
+                             k_scale: float = 1.0, v_scale: float = 1.0, stream=None) -> None:
+    """First launch of a step (see ``msa_sparse_decode_run``)."""
+    head = _run_args(plan, q, kv_cache, block_table, seq_lens, topk, out)
+    _check(load_library().msa_sparse_decode_attend(
+        *head, float(k_scale), float(v_scale), block_table.data_ptr(), seq_lens.data_ptr(),
+        topk.data_ptr(), _I64x3(*topk.stride()), out.data_ptr(), float(sm_scale),
+        _stream_handle(stream, q.device)))
+
+
+def msa_sparse_decode_merge(plan: DecodePlan, out: torch.Tensor, *, v_scale: float = 1.0,
+                            stream=None) -> None:
+    """Second launch of a step: merge the split partials into ``out``."""
+    _check_q(out, "out", plan.num_token_rows, plan.num_q_heads)
+    _check(load_library().msa_sparse_decode_merge(plan.handle, out.data_ptr(), float(v_scale),
+                                                  _stream_handle(stream, out.device)))
 
 
 def msa_block_score_topk(q: torch.Tensor, kv_cache: torch.Tensor, block_table: torch.Tensor,

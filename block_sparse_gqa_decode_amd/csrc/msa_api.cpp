@@ -113,6 +113,8 @@ msa_status check_kv(const void* kv_cache, const int64_t kv_strides[4], int64_t n
       return fail(MSA_ERR_INVALID_ARG, "kv_cache stride %d (%lld elements) is not a multiple "
                   "of 16 bytes", d, (long long)kv_strides[d]);
   }
+  if (kv_strides[2] * eb > (1 << 24))
+    return fail(MSA_ERR_UNSUPPORTED, "kv_cache row stride above 16 MiB");
   if (kv_strides[2] < 2 * msa::kHeadDim)
     return fail(MSA_ERR_INVALID_ARG, "kv_cache row stride %lld is shorter than a packed K|V "
                 "row (256 elements)", (long long)kv_strides[2]);
@@ -120,12 +122,16 @@ msa_status check_kv(const void* kv_cache, const int64_t kv_strides[4], int64_t n
   return MSA_OK;
 }
 
+// Split-K only when there are too few (token, kv head) units to give every CU
+// a workgroup: each split costs a partial write plus a merge launch, which
+// pays off only below one unit per CU.
 int32_t choose_splits(const msa_decode_shape* s, int32_t real_rows) {
   if (s->num_splits > 0) return s->num_splits;
   const int64_t units = (int64_t)real_rows * s->num_kv_heads;
+  constexpr int64_t kTargetWorkgroups = 256;
   int32_t splits = 1;
   const int32_t cap = s->topk_blocks < 8 ? s->topk_blocks : 8;
-  while (units * splits < 512 && splits * 2 <= cap) splits *= 2;
+  while (units * splits < kTargetWorkgroups && splits * 2 <= cap) splits *= 2;
   return splits;
 }
 
@@ -173,7 +179,9 @@ msa_status msa_sparse_decode_plan(const msa_decode_shape* shape, int device, msa
   const int32_t real_rows = shape->batch * shape->decode_query_len;
   const int32_t num_rows = shape->num_token_rows ? shape->num_token_rows : real_rows;
   const int32_t splits = choose_splits(shape, real_rows);
-  const int64_t grid = (int64_t)num_rows * shape->num_kv_heads * splits;
+  const int64_t units = (int64_t)num_rows * shape->num_kv_heads;
+  const int64_t grid =
+      (units + msa::kXcdSlots - 1) / msa::kXcdSlots * msa::kXcdSlots * splits;
   if (grid > INT32_MAX) return fail(MSA_ERR_UNSUPPORTED, "launch grid too large");
   const int64_t per_row = (int64_t)shape->num_q_heads * splits;
   const int64_t o_bytes = splits > 1 ? (int64_t)num_rows * per_row * msa::kHeadDim * 4 : 0;
@@ -206,11 +214,12 @@ msa_status msa_sparse_decode_plan(const msa_decode_shape* shape, int device, msa
       delete plan;
       if (e == hipErrorOutOfMemory || e == hipErrorMemoryAllocation)
         return fail(MSA_ERR_OUT_OF_MEMORY, "partial arena of %lld bytes: %s",
-                    (long long)(o_bytes + ml_bytes), hipGetErrorString(e));
+                    (long long)plan->arena_bytes, hipGetErrorString(e));
       return device_fail(e, "hipMalloc");
     }
-    plan->part_o = static_cast<float*>(plan->arena);
-    plan->part_ml = reinterpret_cast<float*>(static_cast<char*>(plan->arena) + o_bytes);
+    char* base = static_cast<char*>(plan->arena);
+    plan->part_o = reinterpret_cast<float*>(base);
+    plan->part_ml = reinterpret_cast<float*>(base + o_bytes);
   }
   *plan_out = plan;
   return ok();
@@ -238,12 +247,12 @@ msa_status msa_sparse_decode_plan_info(msa_plan plan, int32_t* num_splits, int64
   return ok();
 }
 
-msa_status msa_sparse_decode_run(msa_plan plan, const void* q, const void* kv_cache,
-                                 const int64_t kv_strides[4], int64_t num_kv_blocks,
-                                 float k_scale, float v_scale, const int32_t* block_table,
-                                 const int32_t* seq_lens, const int32_t* topk,
-                                 const int64_t topk_strides[3], void* out, float sm_scale,
-                                 void* stream) {
+static msa_status run_phases(msa_plan plan, const void* q, const void* kv_cache,
+                             const int64_t kv_strides[4], int64_t num_kv_blocks, float k_scale,
+                             float v_scale, const int32_t* block_table,
+                             const int32_t* seq_lens, const int32_t* topk,
+                             const int64_t topk_strides[3], void* out, float sm_scale,
+                             void* stream, bool merge) {
   if (plan == nullptr) return fail(MSA_ERR_INVALID_ARG, "plan is NULL");
   const msa_decode_shape& s = plan->shape;
   if (q == nullptr || out == nullptr) return fail(MSA_ERR_INVALID_ARG, "q and out must be non-NULL");
@@ -258,6 +267,8 @@ msa_status msa_sparse_decode_run(msa_plan plan, const void* q, const void* kv_ca
   if (st != MSA_OK) return st;
   if (!std::isfinite(k_scale) || !std::isfinite(v_scale) || !std::isfinite(sm_scale))
     return fail(MSA_ERR_INVALID_ARG, "scales must be finite");
+  if (!(sm_scale > 0.f) || !(k_scale > 0.f))
+    return fail(MSA_ERR_INVALID_ARG, "sm_scale and k_scale must be positive");
 
   const int64_t eb = elem_bytes(s.kv_dtype);
   msa::AttendParams p{};
@@ -287,6 +298,7 @@ msa_status msa_sparse_decode_run(msa_plan plan, const void* q, const void* kv_ca
   p.group = s.num_q_heads / s.num_kv_heads;
   p.topk_k = s.topk_blocks;
   p.splits = plan->splits;
+  p.num_units = plan->num_rows * s.num_kv_heads;
 
   DeviceGuard guard;
   hipError_t e = guard.enter(plan->device);
@@ -294,10 +306,59 @@ msa_status msa_sparse_decode_run(msa_plan plan, const void* q, const void* kv_ca
   hipStream_t st_ = static_cast<hipStream_t>(stream);
   e = msa::launch_attend(p, s.kv_dtype == MSA_KV_FP8_E4M3, st_);
   if (e != hipSuccess) return device_fail(e, "attend launch");
-  if (plan->splits > 1) {
-    e = msa::launch_combine(p, st_);
-    if (e != hipSuccess) return device_fail(e, "combine launch");
+  if (merge && plan->splits > 1) {
+    e = msa::launch_merge(p, st_);
+    if (e != hipSuccess) return device_fail(e, "merge launch");
   }
+  return ok();
+}
+
+msa_status msa_sparse_decode_run(msa_plan plan, const void* q, const void* kv_cache,
+                                 const int64_t kv_strides[4], int64_t num_kv_blocks,
+                                 float k_scale, float v_scale, const int32_t* block_table,
+                                 const int32_t* seq_lens, const int32_t* topk,
+                                 const int64_t topk_strides[3], void* out, float sm_scale,
+                                 void* stream) {
+  return run_phases(plan, q, kv_cache, kv_strides, num_kv_blocks, k_scale, v_scale,
+                    block_table, seq_lens, topk, topk_strides, out, sm_scale, stream, true);
+}
+
+msa_status msa_sparse_decode_attend(msa_plan plan, const void* q, const void* kv_cache,
+                                    const int64_t kv_strides[4], int64_t num_kv_blocks,
+                                    float k_scale, float v_scale, const int32_t* block_table,
+                                    const int32_t* seq_lens, const int32_t* topk,
+                                    const int64_t topk_strides[3], void* out, float sm_scale,
+                                    void* stream) {
+  return run_phases(plan, q, kv_cache, kv_strides, num_kv_blocks, k_scale, v_scale,
+                    block_table, seq_lens, topk, topk_strides, out, sm_scale, stream, false);
+}
+
+msa_status msa_sparse_decode_merge(msa_plan plan, void* out, float v_scale, void* stream) {
+  if (plan == nullptr) return fail(MSA_ERR_INVALID_ARG, "plan is NULL");
+  if (out == nullptr || !aligned16(out))
+    return fail(MSA_ERR_INVALID_ARG, "out must be non-NULL and 16-byte aligned");
+  if (!std::isfinite(v_scale)) return fail(MSA_ERR_INVALID_ARG, "scales must be finite");
+  if (plan->splits == 1) return ok();
+  const msa_decode_shape& s = plan->shape;
+  msa::AttendParams p{};
+  p.out = static_cast<uint16_t*>(out);
+  p.part_o = plan->part_o;
+  p.part_ml = plan->part_ml;
+  p.v_scale = v_scale;
+  p.dql = s.decode_query_len;
+  p.real_rows = plan->real_rows;
+  p.num_rows = plan->num_rows;
+  p.hq = s.num_q_heads;
+  p.hkv = s.num_kv_heads;
+  p.group = s.num_q_heads / s.num_kv_heads;
+  p.topk_k = s.topk_blocks;
+  p.splits = plan->splits;
+  p.num_units = plan->num_rows * s.num_kv_heads;
+  DeviceGuard guard;
+  hipError_t e = guard.enter(plan->device);
+  if (e != hipSuccess) return device_fail(e, "hipSetDevice");
+  e = msa::launch_merge(p, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return device_fail(e, "merge launch");
   return ok();
 }
 

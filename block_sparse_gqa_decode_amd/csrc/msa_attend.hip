@@ -28,6 +28,22 @@
 //    transposes them into the 8 d-tiles.  The accumulator then holds
 //    O[q row n][32g + 8i + t8] for i < 4, t8 < 8: 32 contiguous outputs.
 //
+// Split-K: with S > 1 splits every workgroup writes its fp32 partial
+// (unnormalised O, running max and sum in log2 units) to the plan's arena and a
+// second, small kernel merges the S partials of each row by log-sum-exp.  (A
+// merge by the last-arriving workgroup needs a device-scope release, which on
+// this part is a walk of the whole L2 per workgroup: slower than a second
+// launch even without the acquire-side invalidate.)  Workgroup ids are laid
+// out so all splits of a unit get the same XCD slot (the dispatcher deals
+// consecutive workgroups to the 8 XCDs in turn), so they share its L2.
+//
+// Pipeline: each wavefront keeps two pages in registers, one in flight while
+// it computes the other, as a ring unrolled twice so every buffer index is
+// static and each wait covers only the page computed.  (Deeper rings, eight
+// wavefronts per workgroup over alternate pages, or two workgroups per unit
+// over half the q heads each measured no faster: with one workgroup per CU
+// the step is bound by HBM latency and bandwidth, not by issue.)
+//
 // NaN safety: rows past a page's visible count are never loaded (row index
 // clamped to the last visible row) and their scores are set to -inf, so stale
 // cache bytes cannot reach the MFMAs.
@@ -37,10 +53,12 @@
 namespace msa {
 namespace {
 
-constexpr int kThreads = 256;
-constexpr int kWaves = 4;
+constexpr int kWaves = 4;      // wavefronts sharing one page (32 keys each)
+constexpr int kThreads = 64 * kWaves;
+constexpr int kDepth = 2;      // pages per wavefront in the register ring
 constexpr int kKeysPerWave = 32;
 constexpr int kOPad = 4;
+constexpr float kRescaleSlack = 8.0f;
 
 template <bool kFp8>
 struct PageRegs;
@@ -61,32 +79,53 @@ __device__ __forceinline__ int key_of_slot(int g, int j) {
   return j < 4 ? 4 * g + j : 16 + 4 * g + (j - 4);
 }
 
+// Per-lane constants of the page loads: the page rows a lane reads for the two
+// S^T tiles and the eight P^T / V^T slots, and its byte columns.
+struct LaneRows {
+  int rk[2];
+  int rv[8];
+  uint32_t ck;  // first K byte of the lane's runs
+  uint32_t cv;  // first V byte of the lane's run
+};
+
 template <bool kFp8>
-__device__ __forceinline__ void load_page(PageRegs<kFp8>& r, const uint8_t* page_head,
-                                          int64_t row_stride, int kbase, int nvis,
-                                          int n, int g) {
+__device__ __forceinline__ LaneRows lane_rows(int kbase, int n, int g) {
+  LaneRows lr;
+#pragma unroll
+  for (int tau = 0; tau < 2; ++tau) lr.rk[tau] = kbase + 16 * tau + n;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) lr.rv[j] = kbase + key_of_slot(g, j);
+  lr.ck = kFp8 ? 16u * g : 32u * g;
+  lr.cv = kFp8 ? kHeadDim + 8u * n : 2 * kHeadDim + 16u * n;
+  return lr;
+}
+
+// Loads of one page into registers.  `page` is wave-uniform (SGPRs); rows are
+// clamped to the last visible row `lim`, so rows past it are never read; the
+// per-lane part of every address is a 32-bit offset.
+template <bool kFp8>
+__device__ __forceinline__ void load_page(PageRegs<kFp8>& r, const uint8_t* page,
+                                          uint32_t row_stride, int lim, const LaneRows& lr) {
 #pragma unroll
   for (int tau = 0; tau < 2; ++tau) {
-    const int kr = min(kbase + 16 * tau + n, nvis - 1);
-    const uint8_t* row = page_head + kr * row_stride;
+    const uint32_t off = (uint32_t)min(lr.rk[tau], lim) * row_stride + lr.ck;
     if constexpr (kFp8) {
-      r.k[tau][0] = *reinterpret_cast<const u32x4_t*>(row + 16 * g);
-      r.k[tau][1] = *reinterpret_cast<const u32x4_t*>(row + 64 + 16 * g);
+      r.k[tau][0] = *reinterpret_cast<const u32x4_t*>(page + off);
+      r.k[tau][1] = *reinterpret_cast<const u32x4_t*>(page + off + 64);
     } else {
-      r.k[tau][0] = *reinterpret_cast<const u32x4_t*>(row + 2 * (16 * g));
-      r.k[tau][1] = *reinterpret_cast<const u32x4_t*>(row + 2 * (16 * g + 8));
-      r.k[tau][2] = *reinterpret_cast<const u32x4_t*>(row + 2 * (64 + 16 * g));
-      r.k[tau][3] = *reinterpret_cast<const u32x4_t*>(row + 2 * (64 + 16 * g + 8));
+      r.k[tau][0] = *reinterpret_cast<const u32x4_t*>(page + off);
+      r.k[tau][1] = *reinterpret_cast<const u32x4_t*>(page + off + 16);
+      r.k[tau][2] = *reinterpret_cast<const u32x4_t*>(page + off + 128);
+      r.k[tau][3] = *reinterpret_cast<const u32x4_t*>(page + off + 144);
     }
   }
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
-    const int kr = min(kbase + key_of_slot(g, j), nvis - 1);
-    const uint8_t* row = page_head + kr * row_stride;
+    const uint32_t off = (uint32_t)min(lr.rv[j], lim) * row_stride + lr.cv;
     if constexpr (kFp8) {
-      r.v[j] = *reinterpret_cast<const u32x2_t*>(row + kHeadDim + 8 * n);
+      r.v[j] = *reinterpret_cast<const u32x2_t*>(page + off);
     } else {
-      r.v[j] = *reinterpret_cast<const u32x4_t*>(row + 2 * kHeadDim + 16 * n);
+      r.v[j] = *reinterpret_cast<const u32x4_t*>(page + off);
     }
   }
 }
@@ -116,34 +155,44 @@ __device__ __forceinline__ void attend_page(const PageRegs<kFp8>& r,
     for (int c = 0; c < 4; ++c) s[tau] = mfma_bf16_16x16x32(kf[c], qf[c], s[tau]);
   }
 
-  // Scale into log2 units, mask keys past the visible count.
+  // Raw scores; keys past the visible count (only on a token's last page)
+  // become -inf.  The positive scale is applied after the max.
   float z[8];
 #pragma unroll
   for (int tau = 0; tau < 2; ++tau) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int kp = kbase + 16 * tau + 4 * g + i;
-      z[4 * tau + i] = kp < nvis ? s[tau][i] * scale_log2 : -INFINITY;
+    for (int i = 0; i < 4; ++i) z[4 * tau + i] = s[tau][i];
+  }
+  if (kbase + kKeysPerWave > nvis) {
+#pragma unroll
+    for (int tau = 0; tau < 2; ++tau) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        if (kbase + 16 * tau + 4 * g + i >= nvis) z[4 * tau + i] = -INFINITY;
+      }
     }
   }
-  float mx = z[0];
+  // Lazy rescaling: the reference point m_run of a row only moves when one of
+  // its scores exceeds it by more than kRescaleSlack (log2 units); then
+  // probabilities stay <= 2^kRescaleSlack, far inside fp32 / bf16 range.  The
+  // test uses each lane's own maximum and one wave vote, so the cross-lane row
+  // maximum is only formed on the (rare) pages that move a reference point;
+  // m_run = -inf (no key yet) always moves.
+  const float mx = fmaxf(fmaxf(fmaxf(z[0], z[1]), fmaxf(z[2], z[3])),
+                         fmaxf(fmaxf(z[4], z[5]), fmaxf(z[6], z[7]))) * scale_log2;
+  if (__any(mx > m_run + kRescaleSlack)) {
+    const float mrow = wave_max_xor_16_32(mx);
+    const float m_new = mrow > m_run + kRescaleSlack ? mrow : m_run;
+    const float alpha = fast_exp2(m_run - m_new);
+    l_part *= alpha;
 #pragma unroll
-  for (int e = 1; e < 8; ++e) mx = fmaxf(mx, z[e]);
-  mx = wave_max_xor_16_32(mx);
-  const float m_new = fmaxf(m_run, mx);
-  const float m_use = m_new == -INFINITY ? 0.f : m_new;
-  const float alpha = fast_exp2(m_run - m_use);
-  float pz[8];
-  float sum = 0.f;
-#pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    pz[e] = fast_exp2(z[e] - m_use);
-    sum += pz[e];
+    for (int t8 = 0; t8 < 8; ++t8) o[t8] *= alpha;
+    m_run = m_new;
   }
-  l_part = l_part * alpha + sum;
-  m_run = m_new;
+  float pz[8];
 #pragma unroll
-  for (int t8 = 0; t8 < 8; ++t8) o[t8] *= alpha;
+  for (int e = 0; e < 8; ++e) pz[e] = fast_exp2(fmaf(z[e], scale_log2, -m_run));
+  l_part += ((pz[0] + pz[1]) + (pz[2] + pz[3])) + ((pz[4] + pz[5]) + (pz[6] + pz[7]));
 
   u32x4_t pw;
   pw.x = pack_bf16x2(pz[0], pz[1]);
@@ -175,6 +224,47 @@ __device__ __forceinline__ void attend_page(const PageRegs<kFp8>& r,
   }
 }
 
+// bf16 store of one output row chunk: acc / L * v_scale, or exact zeros when
+// the row saw no key (L == 0).
+__device__ __forceinline__ void store_row(uint16_t* dst, const float (&acc)[8], float L,
+                                          float v_scale) {
+  u32x4_t ov = u32x4_t{0u, 0u, 0u, 0u};
+  if (L > 0.f) {
+    const float inv = v_scale / L;
+    ov.x = pack_bf16x2(acc[0] * inv, acc[1] * inv);
+    ov.y = pack_bf16x2(acc[2] * inv, acc[3] * inv);
+    ov.z = pack_bf16x2(acc[4] * inv, acc[5] * inv);
+    ov.w = pack_bf16x2(acc[6] * inv, acc[7] * inv);
+  }
+  *reinterpret_cast<u32x4_t*>(dst) = ov;
+}
+
+// Log-sum-exp merge of the split partials of one (token row, q head) and the
+// bf16 store of head dims d0..d0+7.
+__device__ __forceinline__ void merge_splits(const AttendParams& p, int64_t row, int d0) {
+  const float* ml = p.part_ml + row * p.splits * 2;
+  float M = -INFINITY;
+  for (int s = 0; s < p.splits; ++s) M = fmaxf(M, ml[2 * s]);
+  float L = 0.f;
+  float acc[8];
+#pragma unroll
+  for (int k = 0; k < 8; ++k) acc[k] = 0.f;
+  if (M != -INFINITY) {
+    for (int s = 0; s < p.splits; ++s) {
+      const float ms = ml[2 * s];
+      if (ms == -INFINITY) continue;
+      const float e = fast_exp2(ms - M);
+      L += e * ml[2 * s + 1];
+      const float* po = p.part_o + (row * p.splits + s) * kHeadDim + d0;
+      const f32x4_t a = *reinterpret_cast<const f32x4_t*>(po);
+      const f32x4_t b = *reinterpret_cast<const f32x4_t*>(po + 4);
+      acc[0] += e * a.x; acc[1] += e * a.y; acc[2] += e * a.z; acc[3] += e * a.w;
+      acc[4] += e * b.x; acc[5] += e * b.y; acc[6] += e * b.z; acc[7] += e * b.w;
+    }
+  }
+  store_row(p.out + row * kHeadDim + d0, acc, L, p.v_scale);
+}
+
 template <bool kFp8>
 __global__ __launch_bounds__(kThreads) void attend_kernel(AttendParams p) {
   __shared__ int32_t s_page[kMaxTopk];
@@ -189,14 +279,19 @@ __global__ __launch_bounds__(kThreads) void attend_kernel(AttendParams p) {
   const int wave = tid >> 6;
   const int n = lane & 15;
   const int g = lane >> 4;
-  const int split = blockIdx.x % p.splits;
-  const int unit = blockIdx.x / p.splits;
+  const int xslot = blockIdx.x % kXcdSlots;
+  const int q8 = blockIdx.x / kXcdSlots;
+  const int split = q8 % p.splits;
+  const int unit = (q8 / p.splits) * kXcdSlots + xslot;
+  if (unit >= p.num_units) return;
   const int t = unit / p.hkv;
   const int h = unit - t * p.hkv;
+  const int rows = p.group;  // q heads of the unit = MFMA rows in use
+  const int head0 = h * p.group;
 
   if (t >= p.real_rows) {
-    // Padding row: zeros (written here when there is no combine pass).
-    if (p.splits == 1) {
+    // Padding row: exact zeros, written once.
+    if (split == 0) {
       const int qr = tid >> 4;
       const int d0 = (tid & 15) * 8;
       if (qr < p.group) {
@@ -237,8 +332,8 @@ __global__ __launch_bounds__(kThreads) void attend_kernel(AttendParams p) {
 
   // Q^T operand: q row n, head dims 16g.. and 64+16g.. (see header comment).
   bf16x8_t qf[4];
-  if (n < p.group) {
-    const uint16_t* qp = p.q + ((int64_t)t * p.hq + h * p.group + n) * kHeadDim;
+  if (n < rows) {
+    const uint16_t* qp = p.q + ((int64_t)t * p.hq + head0 + n) * kHeadDim;
     qf[0] = as_bf16x8(*reinterpret_cast<const u32x4_t*>(qp + 16 * g));
     qf[1] = as_bf16x8(*reinterpret_cast<const u32x4_t*>(qp + 16 * g + 8));
     qf[2] = as_bf16x8(*reinterpret_cast<const u32x4_t*>(qp + 64 + 16 * g));
@@ -255,6 +350,8 @@ __global__ __launch_bounds__(kThreads) void attend_kernel(AttendParams p) {
   const int hi = min(nlive, lo + per);
   const int kbase = wave * kKeysPerWave;
   const uint8_t* head_base = p.kv + h * p.kv_s1;
+  const uint32_t row_stride = (uint32_t)p.kv_s2;
+  const LaneRows lr = lane_rows<kFp8>(kbase, n, g);
 
   float m_run = -INFINITY;
   float l_part = 0.f;
@@ -262,33 +359,39 @@ __global__ __launch_bounds__(kThreads) void attend_kernel(AttendParams p) {
 #pragma unroll
   for (int t8 = 0; t8 < 8; ++t8) o[t8] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-  // Two-deep software pipeline over the live pages: the next page's loads are
-  // in flight while the current one is computed.
-  PageRegs<kFp8> cur{}, nxt{};
-  bool act_cur = false;
-  int nv_cur = 0;
+  // kDepth-deep ring over the live pages (see the header comment).  Loads are
+  // issued unconditionally: a page past the split's end re-reads the split's
+  // last page (an L2 hit) and an inactive wavefront's rows all clamp to one
+  // visible row, so no load sits on a conditional path before a wait.  Page
+  // ids and visible counts are wave-uniform and live in scalar registers.
   if (lo < hi) {
-    nv_cur = s_nvis[lo];
-    act_cur = kbase < nv_cur;
-    if (act_cur) load_page<kFp8>(cur, head_base + s_page[lo] * p.kv_s0, p.kv_s2, kbase,
-                                 nv_cur, n, g);
-  }
-  for (int i = lo; i < hi; ++i) {
-    bool act_nxt = false;
-    int nv_nxt = 0;
-    if (i + 1 < hi) {
-      nv_nxt = s_nvis[i + 1];
-      act_nxt = kbase < nv_nxt;
-      if (act_nxt) load_page<kFp8>(nxt, head_base + s_page[i + 1] * p.kv_s0, p.kv_s2,
-                                   kbase, nv_nxt, n, g);
+    PageRegs<kFp8> buf[kDepth];
+#pragma unroll
+    for (int j = 0; j < kDepth - 1; ++j) {
+      const int pi = min(lo + j, hi - 1);
+      const int pg = __builtin_amdgcn_readfirstlane(s_page[pi]);
+      const int nv = __builtin_amdgcn_readfirstlane(s_nvis[pi]);
+      load_page<kFp8>(buf[j], head_base + (int64_t)pg * p.kv_s0, row_stride, nv - 1, lr);
     }
-    if (act_cur) attend_page<kFp8>(cur, qf, kbase, nv_cur, g, p.scale_log2, m_run, l_part, o);
-    cur = nxt;
-    act_cur = act_nxt;
-    nv_cur = nv_nxt;
+    for (int i = lo;; i += kDepth) {
+#pragma unroll
+      for (int j = 0; j < kDepth; ++j) {
+        const int cur = i + j;
+        if (cur >= hi) goto pages_done;
+        const int pn = min(cur + kDepth - 1, hi - 1);
+        const int pg = __builtin_amdgcn_readfirstlane(s_page[pn]);
+        const int nvn = __builtin_amdgcn_readfirstlane(s_nvis[pn]);
+        load_page<kFp8>(buf[(j + kDepth - 1) % kDepth], head_base + (int64_t)pg * p.kv_s0,
+                        row_stride, nvn - 1, lr);
+        const int nv = __builtin_amdgcn_readfirstlane(s_nvis[cur]);
+        if (kbase < nv)
+          attend_page<kFp8>(buf[j], qf, kbase, nv, g, p.scale_log2, m_run, l_part, o);
+      }
+    }
   }
+pages_done:
 
-  // Merge the four wavefronts' states through LDS.
+  // Merge the wavefronts' states through LDS.
   const float l_run = wave_sum_xor_16_32(l_part);
   if (g == 0) {
     s_m[wave][n] = m_run;
@@ -303,39 +406,36 @@ __global__ __launch_bounds__(kThreads) void attend_kernel(AttendParams p) {
 
   const int qr = tid >> 4;
   const int d0 = (tid & 15) * 8;
-  if (qr >= p.group) return;
-  float mw[kWaves];
+  const bool owner = qr < rows;
   float M = -INFINITY;
-#pragma unroll
-  for (int w = 0; w < kWaves; ++w) {
-    mw[w] = s_m[w][qr];
-    M = fmaxf(M, mw[w]);
-  }
   float L = 0.f;
   float acc[8];
 #pragma unroll
   for (int k = 0; k < 8; ++k) acc[k] = 0.f;
+  if (owner) {
+    float mw[kWaves];
 #pragma unroll
-  for (int w = 0; w < kWaves; ++w) {
-    if (mw[w] == -INFINITY) continue;
-    const float e = fast_exp2(mw[w] - M);
-    L += e * s_l[w][qr];
+    for (int w = 0; w < kWaves; ++w) {
+      mw[w] = s_m[w][qr];
+      M = fmaxf(M, mw[w]);
+    }
 #pragma unroll
-    for (int k = 0; k < 8; ++k) acc[k] += e * s_o[w][qr][d0 + k];
+    for (int w = 0; w < kWaves; ++w) {
+      if (mw[w] == -INFINITY) continue;
+      const float e = fast_exp2(mw[w] - M);
+      L += e * s_l[w][qr];
+#pragma unroll
+      for (int k = 0; k < 8; ++k) acc[k] += e * s_o[w][qr][d0 + k];
+    }
   }
 
-  const int64_t row = (int64_t)t * p.hq + h * p.group + qr;
+  const int64_t row = (int64_t)t * p.hq + head0 + qr;
   if (p.splits == 1) {
-    u32x4_t ov = u32x4_t{0u, 0u, 0u, 0u};
-    if (L > 0.f) {
-      const float inv = p.v_scale / L;
-      ov.x = pack_bf16x2(acc[0] * inv, acc[1] * inv);
-      ov.y = pack_bf16x2(acc[2] * inv, acc[3] * inv);
-      ov.z = pack_bf16x2(acc[4] * inv, acc[5] * inv);
-      ov.w = pack_bf16x2(acc[6] * inv, acc[7] * inv);
-    }
-    *reinterpret_cast<u32x4_t*>(p.out + row * kHeadDim + d0) = ov;
-  } else {
+    if (owner) store_row(p.out + row * kHeadDim + d0, acc, L, p.v_scale);
+    return;
+  }
+
+  if (owner) {
     float* po = p.part_o + (row * p.splits + split) * kHeadDim + d0;
     *reinterpret_cast<f32x4_t*>(po) = f32x4_t{acc[0], acc[1], acc[2], acc[3]};
     *reinterpret_cast<f32x4_t*>(po + 4) = f32x4_t{acc[4], acc[5], acc[6], acc[7]};
@@ -347,46 +447,57 @@ __global__ __launch_bounds__(kThreads) void attend_kernel(AttendParams p) {
   }
 }
 
-// Log-sum-exp merge of the split partials of every (token row, q head) and
-// the bf16 store; rows with no live key and padding rows get exact zeros.
-__global__ __launch_bounds__(256) void combine_kernel(AttendParams p) {
-  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  const int64_t total = (int64_t)p.num_rows * p.hq * 16;
-  if (idx >= total) return;
-  const int64_t row = idx >> 4;
-  const int d0 = (int)(idx & 15) * 8;
-  const int64_t t = row / p.hq;
-  u32x4_t ov = u32x4_t{0u, 0u, 0u, 0u};
-  if (t < p.real_rows) {
-    const float* ml = p.part_ml + row * p.splits * 2;
-    float M = -INFINITY;
-    for (int s = 0; s < p.splits; ++s) M = fmaxf(M, ml[2 * s]);
-    if (M != -INFINITY) {
-      float L = 0.f;
-      float acc[8];
+// Merge pass: one workgroup per (token row, kv head) unit, placed on the same
+// XCD slot as that unit's attend workgroups so the partials come from the
+// L2 they were written through; thread (q row, 8 head dims).  All of a row's
+// partial loads are issued before any is used.
+template <int kS>
+__device__ __forceinline__ void merge_fixed(const AttendParams& p, int64_t row, int d0) {
+  const float* ml = p.part_ml + row * kS * 2;
+  const float* po = p.part_o + row * kS * kHeadDim + d0;
+  f32x2_t m_l[kS];
+  f32x4_t a[kS], b[kS];
 #pragma unroll
-      for (int k = 0; k < 8; ++k) acc[k] = 0.f;
-      for (int s = 0; s < p.splits; ++s) {
-        const float ms = ml[2 * s];
-        if (ms == -INFINITY) continue;
-        const float e = fast_exp2(ms - M);
-        L += e * ml[2 * s + 1];
-        const float* po = p.part_o + (row * p.splits + s) * kHeadDim + d0;
-        const f32x4_t a = *reinterpret_cast<const f32x4_t*>(po);
-        const f32x4_t b = *reinterpret_cast<const f32x4_t*>(po + 4);
-        acc[0] += e * a.x; acc[1] += e * a.y; acc[2] += e * a.z; acc[3] += e * a.w;
-        acc[4] += e * b.x; acc[5] += e * b.y; acc[6] += e * b.z; acc[7] += e * b.w;
-      }
-      if (L > 0.f) {
-        const float inv = p.v_scale / L;
-        ov.x = pack_bf16x2(acc[0] * inv, acc[1] * inv);
-        ov.y = pack_bf16x2(acc[2] * inv, acc[3] * inv);
-        ov.z = pack_bf16x2(acc[4] * inv, acc[5] * inv);
-        ov.w = pack_bf16x2(acc[6] * inv, acc[7] * inv);
-      }
+  for (int s = 0; s < kS; ++s) {
+    m_l[s] = *reinterpret_cast<const f32x2_t*>(ml + 2 * s);
+    a[s] = *reinterpret_cast<const f32x4_t*>(po + s * kHeadDim);
+    b[s] = *reinterpret_cast<const f32x4_t*>(po + s * kHeadDim + 4);
+  }
+  float M = -INFINITY;
+#pragma unroll
+  for (int s = 0; s < kS; ++s) M = fmaxf(M, m_l[s].x);
+  float L = 0.f;
+  float acc[8];
+#pragma unroll
+  for (int k = 0; k < 8; ++k) acc[k] = 0.f;
+  if (M != -INFINITY) {
+#pragma unroll
+    for (int s = 0; s < kS; ++s) {
+      // A split with no key has max -inf, sum 0 and zero O: weight 0.
+      const float e = m_l[s].x == -INFINITY ? 0.f : fast_exp2(m_l[s].x - M);
+      L += e * m_l[s].y;
+      acc[0] += e * a[s].x; acc[1] += e * a[s].y; acc[2] += e * a[s].z; acc[3] += e * a[s].w;
+      acc[4] += e * b[s].x; acc[5] += e * b[s].y; acc[6] += e * b[s].z; acc[7] += e * b[s].w;
     }
   }
-  *reinterpret_cast<u32x4_t*>(p.out + row * kHeadDim + d0) = ov;
+  store_row(p.out + row * kHeadDim + d0, acc, L, p.v_scale);
+}
+
+__global__ __launch_bounds__(256) void merge_kernel(AttendParams p) {
+  const int unit = blockIdx.x;
+  const int t = unit / p.hkv;
+  const int h = unit - t * p.hkv;
+  const int qr = threadIdx.x >> 4;
+  if (t >= p.real_rows || qr >= p.group) return;
+  const int64_t row = (int64_t)t * p.hq + h * p.group + qr;
+  const int d0 = (threadIdx.x & 15) * 8;
+  switch (p.splits) {
+    case 2: merge_fixed<2>(p, row, d0); break;
+    case 3: merge_fixed<3>(p, row, d0); break;
+    case 4: merge_fixed<4>(p, row, d0); break;
+    case 8: merge_fixed<8>(p, row, d0); break;
+    default: merge_splits(p, row, d0); break;
+  }
 }
 
 // fp8 -> bf16 through the same conversion helper the attend uses.
@@ -409,23 +520,25 @@ __global__ __launch_bounds__(256) void fp8_to_bf16_kernel(const uint8_t* in, uin
 }  // namespace
 
 hipError_t launch_attend(const AttendParams& p, bool fp8, hipStream_t stream) {
-  const int64_t grid = (int64_t)p.num_rows * p.hkv * p.splits;
+  const int64_t groups = ((int64_t)p.num_units + kXcdSlots - 1) / kXcdSlots;
+  const int64_t grid = groups * kXcdSlots * p.splits;
   if (grid <= 0) return hipSuccess;
   if (fp8) {
-    hipLaunchKernelGGL(attend_kernel<true>, dim3((uint32_t)grid), dim3(kThreads), 0,
-                       stream, p);
+    hipLaunchKernelGGL(attend_kernel<true>, dim3((uint32_t)grid), dim3(kThreads), 0, stream,
+                       p);
   } else {
-    hipLaunchKernelGGL(attend_kernel<false>, dim3((uint32_t)grid), dim3(kThreads), 0,
-                       stream, p);
+    hipLaunchKernelGGL(attend_kernel<false>, dim3((uint32_t)grid), dim3(kThreads), 0, stream,
+                       p);
   }
   return hipGetLastError();
 }
 
-hipError_t launch_combine(const AttendParams& p, hipStream_t stream) {
-  const int64_t total = (int64_t)p.num_rows * p.hq * 16;
-  const int64_t grid = (total + 255) / 256;
+hipError_t launch_merge(const AttendParams& p, hipStream_t stream) {
+  // Unit u's attend workgroups sit on XCD slot u % 8; merge workgroup u is
+  // dealt to the same slot.
+  const int64_t grid = (int64_t)p.real_rows * p.hkv;
   if (grid <= 0) return hipSuccess;
-  hipLaunchKernelGGL(combine_kernel, dim3((uint32_t)grid), dim3(256), 0, stream, p);
+  hipLaunchKernelGGL(merge_kernel, dim3((uint32_t)grid), dim3(256), 0, stream, p);
   return hipGetLastError();
 }
 

@@ -10,6 +10,7 @@ namespace msa {
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 
@@ -67,6 +68,10 @@ __device__ __forceinline__ float fast_exp2(float x) {
   return __builtin_amdgcn_exp2f(x);
 }
 
+// Reductions across the four 16-lane rows of a wavefront (lanes l, l^16,
+// l^32, l^48).  (The gfx950 row-swap permutes would avoid the LDS crossbar,
+// but this compiler folds max(swap.a, swap.b) to swap.a when both inputs are
+// one value, so the plain lane shuffles stay.)
 __device__ __forceinline__ float wave_max_xor_16_32(float v) {
   v = fmaxf(v, __shfl_xor(v, 16));
   v = fmaxf(v, __shfl_xor(v, 32));

@@ -14,6 +14,7 @@ constexpr int kMaxGroup = 16;   // q heads per kv head handled by one MFMA tile
 constexpr int kMaxTopk = 64;    // entries per top-k row
 constexpr int kMaxSplits = 16;
 constexpr int kMaxScoreBlocks = 16384;
+constexpr int kXcdSlots = 8;   // XCDs a launch is dealt across, round robin
 
 struct AttendParams {
   const uint16_t* q;        // bf16 [rows, hq, 128]
@@ -30,7 +31,7 @@ struct AttendParams {
   float* part_ml;           // fp32 [rows, hq, splits, 2] = (max, sum) in log2 units
   float scale_log2;         // sm_scale * k_scale * log2(e)
   float v_scale;
-  int32_t dql, real_rows, num_rows, hq, hkv, group, topk_k, splits;
+  int32_t dql, real_rows, num_rows, hq, hkv, group, topk_k, splits, num_units;
 };
 
 struct ScoreParams {
@@ -55,7 +56,7 @@ struct SelectParams {
 };
 
 hipError_t launch_attend(const AttendParams& p, bool fp8, hipStream_t stream);
-hipError_t launch_combine(const AttendParams& p, hipStream_t stream);
+hipError_t launch_merge(const AttendParams& p, hipStream_t stream);
 hipError_t launch_score(const ScoreParams& p, bool fp8, hipStream_t stream);
 hipError_t launch_select(const SelectParams& p, hipStream_t stream);
 hipError_t launch_fp8_to_bf16(const uint8_t* in, uint16_t* out, int64_t n,

@@ -128,6 +128,8 @@ msa_status msa_sparse_decode_plan_info(msa_plan plan, int32_t* num_splits,
  *   topk         int32 logical [num_token_rows, Hkv, topk_blocks] with
  *                topk_strides (elements), -1 = no block.
  *   out          bf16 [num_token_rows, Hq, 128], contiguous.
+ *   sm_scale, k_scale must be finite and > 0 (the kernel takes each row's
+ *   maximum before applying them); v_scale must be finite.
  */
 msa_status msa_sparse_decode_run(msa_plan plan, const void* q, const void* kv_cache,
                                  const int64_t kv_strides[4], int64_t num_kv_blocks,
@@ -135,6 +137,24 @@ msa_status msa_sparse_decode_run(msa_plan plan, const void* q, const void* kv_ca
                                  const int32_t* block_table, const int32_t* seq_lens,
                                  const int32_t* topk, const int64_t topk_strides[3],
                                  void* out, float sm_scale, void* stream);
+
+/* The two launches of msa_sparse_decode_run, for callers that schedule or
+ * time them apart.  msa_sparse_decode_run(...) is exactly
+ * msa_sparse_decode_attend(...) followed by msa_sparse_decode_merge(...) on the
+ * same stream.  With one split (msa_sparse_decode_plan_info) the attend writes
+ * `out` itself and the merge launches nothing; with more, the attend leaves
+ * fp32 split partials in the plan's arena and the merge combines them by
+ * log-sum-exp into `out` (TensorRT-LLM PR #17171, flash-decoding commit:
+ * split-K with fp32 partials, zeroed padding rows).  The merge must use the
+ * same `out`, `v_scale` and stream as the attend before it, and no other run
+ * of the plan may come between them. */
+msa_status msa_sparse_decode_attend(msa_plan plan, const void* q, const void* kv_cache,
+                                    const int64_t kv_strides[4], int64_t num_kv_blocks,
+                                    float k_scale, float v_scale,
+                                    const int32_t* block_table, const int32_t* seq_lens,
+                                    const int32_t* topk, const int64_t topk_strides[3],
+                                    void* out, float sm_scale, void* stream);
+msa_status msa_sparse_decode_merge(msa_plan plan, void* out, float v_scale, void* stream);
 
 /* Indexer step of a full decode: per-block causal max score, then top-k.
  *   score[h, b, t] = max over g < G and visible keys i of block b of

@@ -260,3 +260,32 @@ def test_fp8_conversion_rejects_bad_arguments(lib):
 def test_destroy_null_is_ok(lib):
     assert lib.msa_sparse_decode_plan_destroy(None) == 0
     assert lib.msa_last_error().decode() == ""
+
+
+def test_merge_rejects_bad_arguments(lib):
+    assert lib.msa_sparse_decode_merge(None, FAKE, 1.0, None) == msa.MSA_ERR_INVALID_ARG
+    h = _plan(lib)
+    try:
+        assert lib.msa_sparse_decode_merge(h, None, 1.0, None) == msa.MSA_ERR_INVALID_ARG
+        assert lib.msa_sparse_decode_merge(h, FAKE + 4, 1.0, None) == msa.MSA_ERR_INVALID_ARG
+        assert lib.msa_sparse_decode_merge(h, FAKE, float("nan"), None) == \
+            msa.MSA_ERR_INVALID_ARG
+        # one split: the merge has nothing to do and launches nothing
+        assert lib.msa_sparse_decode_merge(h, FAKE, 1.0, None) == 0
+    finally:
+        lib.msa_sparse_decode_plan_destroy(h)
+
+
+def test_attend_rejects_bad_arguments(lib):
+    h = _plan(lib)
+    try:
+        kvs = msa._I64x4(256 * 128, 256 * 128, 256, 1)
+        tks = msa._I64x3(16, 16, 1)
+        st = lib.msa_sparse_decode_attend(h, FAKE, FAKE, kvs, 10, 1.0, 1.0, FAKE, FAKE, FAKE,
+                                          tks, None, 0.08, None)
+        assert st == msa.MSA_ERR_INVALID_ARG
+        st = lib.msa_sparse_decode_attend(h, FAKE, FAKE, kvs, 10, -1.0, 1.0, FAKE, FAKE, FAKE,
+                                          tks, FAKE, 0.08, None)
+        assert st == msa.MSA_ERR_INVALID_ARG and "positive" in lib.msa_last_error().decode()
+    finally:
+        lib.msa_sparse_decode_plan_destroy(h)

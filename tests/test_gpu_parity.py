@@ -340,3 +340,20 @@ def test_full_step_score_select_attend():
     torch.cuda.synchronize()
     rows = [t for t in range(case.real_rows) if ok[t].all()]
     assert_parity(to_f64(out)[rows], oracle_attend(case, rows=rows), what="full step")
+
+
+def test_attend_then_merge_equals_run():
+    _banner("attend + merge == run")
+    case = gen.make_random_case(115, 4, 4, 16, 1, 16, 2000, 20000, pad_rows=2)
+    d = DevCase(case)
+    for splits in (1, 2, 4):
+        plan = d.plan(splits)
+        a = torch.full_like(d.q, float("nan"))
+        b = torch.full_like(d.q, float("nan"))
+        d.run(plan, out=a)
+        msa.msa_sparse_decode_attend(plan, d.q, d.kv, d.block_table, d.seq_lens, d.topk, b,
+                                     sm_scale=case.sm_scale, k_scale=case.k_scale,
+                                     v_scale=case.v_scale)
+        msa.msa_sparse_decode_merge(plan, b, v_scale=case.v_scale)
+        torch.cuda.synchronize()
+        assert torch.equal(a.view(torch.int16), b.view(torch.int16)), splits
