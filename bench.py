@@ -41,6 +41,7 @@ METRIC = "decode tokens/s and effective KV GB/s (% HBM peak), sparse GQA attend,
 HBM_PEAK_GBS = 8000.0
 DEFAULT_CONFIG = "c2_tp4_fp8"
 OTHER_CONFIGS = ("c3_tp1_fp8", "c4_spec_ragged")
+FULL_STEP_CONFIG = "c5_full_step"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attend_traffic.json")
 KERNEL_SOURCES = ("block_sparse_gqa_decode_amd/csrc/msa_attend.hip",
                   "block_sparse_gqa_decode_amd/csrc/msa_device.h",
@@ -54,6 +55,8 @@ CONFIG_TEXT = {
                   "seq U[32768,131072], Zipf-recent indices",
     "c4_spec_ragged": "speculative/ragged fp8 decode: B=16, dql=32, 64/4 heads, top-16, "
                       "8 requests at 131072 + 8 in [200,1900], 4 padding rows",
+    "c5_full_step": "full decode step with indexer: B=64, dql=1, 64/4 heads, fp8, seq "
+                    "log-normal in [8192,262144]; block-max scores -> top-16 -> attend",
 }
 
 
@@ -253,6 +256,159 @@ def time_config(name, steps, warmup, replicas, splits, dev, verbose=True):
     return res, case
 
 
+def scorer_bytes(case):
+    """Algorithmic bytes of the indexer step: the K half of every visible page
+    of every (request, kv head), q, the score write and its read by the
+    selector, and the top-k write."""
+    import numpy as np
+
+    e = 1 if case.kv_dtype == "fp8_e4m3" else 2
+    kv_rows = 0
+    for r in range(case.batch):
+        pos_last = int(case.seq_lens[r]) - 1
+        nb = pos_last // 128 + 1
+        kv_rows += (nb - 1) * 128 + (pos_last - (nb - 1) * 128 + 1)
+    k_bytes = kv_rows * case.num_kv_heads * 128 * e
+    q_bytes = case.real_rows * case.num_q_heads * 128 * 2
+    score_bytes = case.num_kv_heads * case.max_blocks * case.num_token_rows * 4
+    topk_bytes = case.num_token_rows * case.num_kv_heads * case.topk_k * 4
+    table_bytes = int(np.sum((case.seq_lens.astype(np.int64) + 127) // 128)) * 4 * \
+        case.num_kv_heads
+    return {"k_half": k_bytes, "algorithmic": k_bytes + q_bytes + 2 * score_bytes +
+            topk_bytes + table_bytes}
+
+
+class FullStepSet:
+    """R replicas of the full decode step with the indexer: block-max scores ->
+    top-k -> attend, each replica over its own copy of the pool."""
+
+    def __init__(self, case, replicas: int, dev):
+        import numpy as np
+        import torch
+
+        import block_sparse_gqa_decode_amd as msa
+
+        self.case, self.msa = case, msa
+        host = torch.from_numpy(case.kv)
+        nb = case.num_blocks
+        self.kv = torch.empty((replicas * nb,) + tuple(host.shape[1:]), dtype=host.dtype,
+                              device=dev)
+        self.kv[:nb].copy_(host)
+        for i in range(1, replicas):
+            self.kv[i * nb:(i + 1) * nb].copy_(self.kv[:nb])
+        self.seq_lens = torch.from_numpy(case.seq_lens).to(dev)
+        qs = [case.q] + [qh for qh, _ in case.replicas]
+        rows = case.num_token_rows
+        self.sets = []
+        for i in range(replicas):
+            bt = torch.from_numpy((case.block_table.astype(np.int64) + i * nb).astype(
+                np.int32)).to(dev)
+            q = torch.from_numpy(qs[i].view(np.int16)).view(torch.bfloat16).to(dev)
+            # physical [Hkv, rows, blocks] so that the selector's row reads are
+            # contiguous; passed as the logical [Hkv, blocks, rows] view
+            score = torch.empty((case.num_kv_heads, rows, case.max_blocks), dtype=torch.float32,
+                                device=dev).transpose(1, 2)
+            sel = torch.empty((rows, case.num_kv_heads, case.topk_k), dtype=torch.int32,
+                              device=dev)
+            self.sets.append((q, bt, score, sel, torch.empty_like(q)))
+        self.plan = msa.msa_sparse_decode_plan(
+            case.batch, case.dql, num_q_heads=case.num_q_heads,
+            num_kv_heads=case.num_kv_heads, page_table_stride=case.block_table.shape[1],
+            topk_blocks=case.topk_k, kv_dtype=msa.KV_FP8_E4M3, device=dev)
+
+    def run_score(self, i):
+        q, bt, score, sel, _ = self.sets[i]
+        c = self.case
+        self.msa.msa_block_score_topk(q, self.kv, bt, self.seq_lens, decode_query_len=c.dql,
+                                      num_kv_heads=c.num_kv_heads, max_blocks=c.max_blocks,
+                                      score=score, topk_out=sel, k_scale=c.k_scale)
+
+    def run_attend(self, i):
+        q, bt, _, sel, out = self.sets[i]
+        c = self.case
+        self.msa.msa_sparse_decode_run(self.plan, q, self.kv, bt, self.seq_lens, sel, out,
+                                       sm_scale=c.sm_scale, k_scale=c.k_scale,
+                                       v_scale=c.v_scale)
+
+    def run_step(self, i):
+        self.run_score(i)
+        self.run_attend(i)
+
+
+def _graph_time(fns, replicas, steps, warmup):
+    """HIP-event time per step of graph replays of fns over the R replicas."""
+    import torch
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        for i in range(replicas):
+            fns(i)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for i in range(replicas):
+            fns(i)
+    torch.cuda.synchronize()
+    replays = max(1, (steps + replicas - 1) // replicas)
+    for _ in range(max(1, (warmup + replicas - 1) // replicas)):
+        g.replay()
+    torch.cuda.synchronize()
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    ev0.record()
+    for _ in range(replays):
+        g.replay()
+    ev1.record()
+    torch.cuda.synchronize()
+    ms = ev0.elapsed_time(ev1) / (replays * replicas)
+    del g
+    return ms, replays * replicas
+
+
+def time_full_step(name, steps, warmup, replicas, dev, verbose=True):
+    """The full decode step with the indexer (score -> top-k -> attend)."""
+    import torch
+
+    from workloads import gen
+
+    t0 = time.time()
+    case = gen.make_config(name, replicas=replicas - 1)
+    fs = FullStepSet(case, replicas, dev)
+    if verbose:
+        print(f"[bench] {name}: generated + uploaded in {time.time() - t0:.1f}s "
+              f"(pool {case.kv.nbytes / 2**20:.0f} MiB x {replicas}, max_blocks "
+              f"{case.max_blocks})", file=sys.stderr, flush=True)
+    step_ms, n = _graph_time(fs.run_step, replicas, steps, warmup)
+    score_ms, _ = _graph_time(fs.run_score, replicas, steps, warmup)
+    attend_ms, _ = _graph_time(fs.run_attend, replicas, steps, warmup)
+    torch.cuda.synchronize()
+    sb = scorer_bytes(case)
+    ab = []
+    for i in range(replicas):
+        sel = fs.sets[i][3].cpu().numpy()
+        qh = case.q if i == 0 else case.replicas[i - 1][0]
+        ab.append(step_bytes(case, qh, sel))
+    att = sum(b["algorithmic"] for b in ab) / len(ab)
+    eff = sum(b["effective_kv"] for b in ab) / len(ab)
+    res = {
+        "config": name, "steps": n, "ms_per_step": step_ms,
+        "tokens_per_s": case.real_rows / (step_ms / 1e3),
+        "score_topk_ms": score_ms, "attend_ms": attend_ms,
+        "score_k_half_bytes": sb["k_half"], "score_algorithmic_bytes": sb["algorithmic"],
+        "score_algorithmic_gbs": sb["algorithmic"] / (score_ms / 1e3) / 1e9,
+        "score_pct_hbm_peak": 100 * sb["algorithmic"] / (score_ms / 1e3) / 1e9 / HBM_PEAK_GBS,
+        "attend_algorithmic_bytes": att, "attend_effective_kv_bytes": eff,
+        "attend_algorithmic_gbs": att / (attend_ms / 1e3) / 1e9,
+        "step_algorithmic_gbs": (att + sb["algorithmic"]) / (step_ms / 1e3) / 1e9,
+        "splits": fs.plan.num_splits, "real_rows": case.real_rows,
+    }
+    del fs
+    torch.cuda.empty_cache()
+    return res
+
+
 def cpu_baseline(case, seconds: float):
     """The float64 oracle, single-threaded, on a bounded sample of the same
     workload's token rows; scaled to tokens/s."""
@@ -352,7 +508,10 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=400)
     ap.add_argument("--warmup", type=int, default=40)
-    ap.add_argument("--config", default=DEFAULT_CONFIG, choices=sorted(CONFIG_TEXT))
+    ap.add_argument("--config", default=DEFAULT_CONFIG,
+                    choices=sorted(k for k in CONFIG_TEXT if k != FULL_STEP_CONFIG))
+    ap.add_argument("--full-step-only", action="store_true",
+                    help="time only the full step with the indexer and print its record")
     ap.add_argument("--replicas", type=int, default=8)
     ap.add_argument("--splits", type=int, default=0, help="0 = the plan's choice")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
@@ -387,6 +546,11 @@ def main():
         profile_mode(args.config, args.profile_launches, args.splits, dev)
         return
 
+    if args.full_step_only:
+        r5 = time_full_step(FULL_STEP_CONFIG, max(32, args.steps // 8), args.warmup,
+                            args.replicas, dev)
+        print(json.dumps(r5), flush=True)
+        return
     res, case = time_config(args.config, args.steps, args.warmup, args.replicas,
                             args.splits, dev)
     others = {}
@@ -398,6 +562,10 @@ def main():
                                 args.replicas, args.splits, dev)
             others[name] = {k: (round(v, 4) if isinstance(v, float) else v)
                             for k, v in r2.items()}
+        r5 = time_full_step(FULL_STEP_CONFIG, max(32, args.steps // 8), args.warmup,
+                            args.replicas, dev)
+        others[FULL_STEP_CONFIG] = {k: (round(v, 4) if isinstance(v, float) else v)
+                                    for k, v in r5.items()}
     src_hash = kernel_source_hash()
     traffic = load_traffic(src_hash)
     kernel_s = res["attend_ms"] / 1e3

@@ -419,8 +419,9 @@ msa_status msa_block_score_topk(const msa_decode_shape* shape, const void* q,
   if (topk_k < 1 || topk_k > msa::kMaxTopk)
     return fail(MSA_ERR_INVALID_ARG, "topk_k must be in 1..%d (got %d)", msa::kMaxTopk, topk_k);
   if (!std::isfinite(k_scale)) return fail(MSA_ERR_INVALID_ARG, "k_scale must be finite");
-  if (shape->batch >= 65535)
-    return fail(MSA_ERR_UNSUPPORTED, "the scorer supports batch < 65535 (got %d)", shape->batch);
+  if (shape->batch > msa::kMaxScoreBatch)
+    return fail(MSA_ERR_UNSUPPORTED, "the scorer supports batch <= %d (got %d)",
+                msa::kMaxScoreBatch, shape->batch);
 
   const int32_t real_rows = shape->batch * shape->decode_query_len;
   const int32_t num_rows = shape->num_token_rows ? shape->num_token_rows : real_rows;

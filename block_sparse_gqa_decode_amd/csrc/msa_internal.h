@@ -14,6 +14,8 @@ constexpr int kMaxGroup = 16;   // q heads per kv head handled by one MFMA tile
 constexpr int kMaxTopk = 64;    // entries per top-k row
 constexpr int kMaxSplits = 16;
 constexpr int kMaxScoreBlocks = 16384;
+constexpr int kMaxScoreBatch = 4096;   // requests per scorer launch (LDS prefix sum)
+constexpr int kMaxScoreDql = 32;
 constexpr int kXcdSlots = 8;   // XCDs a launch is dealt across, round robin
 
 struct AttendParams {

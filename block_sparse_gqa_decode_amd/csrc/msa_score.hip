@@ -4,16 +4,25 @@
 // block b visible at token t's position of q[t, h*G+g] . K[page(b), h, i],
 // -inf for blocks that start after the position (TensorRT-LLM PR #17171
 // "Custom decode kernels for MinimaxM3", indexer commit: per-block causal max
-// of Q.K with a grid sized to the batch).  One wavefront owns one (request,
-// kv head, block): it loads the block's K half once and evaluates every
-// decode token of the request against it with the same S^T = K Q^T MFMA
-// layout as the attend (16x16x32 bf16, q heads as the 16 columns).
+// of Q.K, here with the q heads as the 16 columns of the same S^T = K Q^T MFMA
+// tile the attend uses).
+//
+// Work decomposition.  The visible (kv head, request, block) items -- every
+// block a request's last token can see -- are counted on the device from
+// seq_lens (a prefix sum over the batch in LDS), and each workgroup of a
+// persistent grid takes an equal contiguous slice of them.  A slice is walked
+// as segments of consecutive blocks of one (request, kv head): per segment the
+// q operand is loaded once and the blocks' K halves stream through a
+// kScoreDepth-deep register ring, each of the 4 wavefronts reading 32 keys of
+// every block (4 KiB), so loads stay deep without many registers.  Per-block
+// wavefront maxima meet in LDS and are written every kFlush items.  Cells of
+// blocks past a request's last block, and padding rows, get -inf in a separate
+// strided pass of the same grid.
 //
 // Selector: per (token, kv head), the k blocks with score > -inf in
-// (score descending, block ascending) order, padded with -1 (same PR, strided
-// selector; ties to the lower block index).  One wavefront per row runs k
-// rounds; round i finds the best block strictly after winner i-1 in that
-// order, so no per-element state is kept and any score stride works.
+// (score descending, block ascending) order, padded with -1 (same PR, top-k
+// selector; ties to the lower block index), by an exact radix select over
+// order-preserving integer images of the scores.
 #include <climits>
 
 #include "msa_device.h"
@@ -23,174 +32,475 @@ namespace msa {
 namespace {
 
 constexpr int kScoreWaves = 4;
+constexpr int kScoreThreads = 64 * kScoreWaves;
+constexpr int kScoreKeys = 32;     // keys of a block per wavefront
+constexpr int kScoreDepth = 4;     // blocks in flight per wavefront
+constexpr int kFlush = 32;         // items between LDS flushes of the maxima
 
 template <bool kFp8>
-struct BlockK;
+struct KHalf;
 
 template <>
-struct BlockK<true> {
-  u32x4_t k[8][2];  // [key tile][run of 16 fp8]
+struct KHalf<true> {
+  u32x4_t k[2][2];  // [key tile][run of 16 fp8]
 };
 
 template <>
-struct BlockK<false> {
-  u32x4_t k[8][4];  // [key tile][chunk of 8 bf16]
+struct KHalf<false> {
+  u32x4_t k[2][4];  // [key tile][chunk of 8 bf16]
 };
 
 template <bool kFp8>
-__device__ __forceinline__ void k_operands(const BlockK<kFp8>& kb, int tile,
-                                           bf16x8_t (&kf)[4]) {
-  if constexpr (kFp8) {
-    kf[0] = as_bf16x8(fp8x8_to_bf16x8(kb.k[tile][0].x, kb.k[tile][0].y));
-    kf[1] = as_bf16x8(fp8x8_to_bf16x8(kb.k[tile][0].z, kb.k[tile][0].w));
-    kf[2] = as_bf16x8(fp8x8_to_bf16x8(kb.k[tile][1].x, kb.k[tile][1].y));
-    kf[3] = as_bf16x8(fp8x8_to_bf16x8(kb.k[tile][1].z, kb.k[tile][1].w));
+__device__ __forceinline__ void load_khalf(KHalf<kFp8>& r, const uint8_t* page,
+                                           uint32_t row_stride, int lim, int kbase, int n,
+                                           int g) {
+#pragma unroll
+  for (int tau = 0; tau < 2; ++tau) {
+    const uint32_t off = (uint32_t)min(kbase + 16 * tau + n, lim) * row_stride +
+                         (kFp8 ? 16u * g : 32u * g);
+    if constexpr (kFp8) {
+      r.k[tau][0] = *reinterpret_cast<const u32x4_t*>(page + off);
+      r.k[tau][1] = *reinterpret_cast<const u32x4_t*>(page + off + 64);
+    } else {
+      r.k[tau][0] = *reinterpret_cast<const u32x4_t*>(page + off);
+      r.k[tau][1] = *reinterpret_cast<const u32x4_t*>(page + off + 16);
+      r.k[tau][2] = *reinterpret_cast<const u32x4_t*>(page + off + 128);
+      r.k[tau][3] = *reinterpret_cast<const u32x4_t*>(page + off + 144);
+    }
+  }
+}
+
+__device__ __forceinline__ void load_q(bf16x8_t (&qf)[4], const ScoreParams& p, int t, int h,
+                                       int n, int g) {
+  if (n < p.group) {
+    const uint16_t* qp = p.q + ((int64_t)t * p.hq + h * p.group + n) * kHeadDim;
+    qf[0] = as_bf16x8(*reinterpret_cast<const u32x4_t*>(qp + 16 * g));
+    qf[1] = as_bf16x8(*reinterpret_cast<const u32x4_t*>(qp + 16 * g + 8));
+    qf[2] = as_bf16x8(*reinterpret_cast<const u32x4_t*>(qp + 64 + 16 * g));
+    qf[3] = as_bf16x8(*reinterpret_cast<const u32x4_t*>(qp + 64 + 16 * g + 8));
   } else {
 #pragma unroll
-    for (int c = 0; c < 4; ++c) kf[c] = as_bf16x8(kb.k[tile][c]);
+    for (int c = 0; c < 4; ++c) qf[c] = as_bf16x8(u32x4_t{0u, 0u, 0u, 0u});
   }
 }
 
+// The wavefront's max over its 32 keys (those < nvis) and the group's rows of
+// k_scale * q.k for one block and one token.
 template <bool kFp8>
-__global__ __launch_bounds__(64 * kScoreWaves) void score_kernel(ScoreParams p) {
-  const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+__device__ __forceinline__ float block_max(const KHalf<kFp8>& r, const bf16x8_t (&qf)[4],
+                                           int kbase, int nvis, int n, int g, int group,
+                                           float k_scale) {
+  float best = -INFINITY;
+#pragma unroll
+  for (int tau = 0; tau < 2; ++tau) {
+    bf16x8_t kf[4];
+    if constexpr (kFp8) {
+      kf[0] = as_bf16x8(fp8x8_to_bf16x8(r.k[tau][0].x, r.k[tau][0].y));
+      kf[1] = as_bf16x8(fp8x8_to_bf16x8(r.k[tau][0].z, r.k[tau][0].w));
+      kf[2] = as_bf16x8(fp8x8_to_bf16x8(r.k[tau][1].x, r.k[tau][1].y));
+      kf[3] = as_bf16x8(fp8x8_to_bf16x8(r.k[tau][1].z, r.k[tau][1].w));
+    } else {
+#pragma unroll
+      for (int c = 0; c < 4; ++c) kf[c] = as_bf16x8(r.k[tau][c]);
+    }
+    f32x4_t s = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int c = 0; c < 4; ++c) s = mfma_bf16_16x16x32(kf[c], qf[c], s);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int key = kbase + 16 * tau + 4 * g + i;
+      if (key < nvis && n < group) best = fmaxf(best, s[i] * k_scale);
+    }
+  }
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) best = fmaxf(best, __shfl_xor(best, off));
+  return best;
+}
+
+typedef __attribute__((address_space(4))) const int32_t const_i32;
+
+template <bool kFp8, bool kOneToken>
+__global__ __launch_bounds__(kScoreThreads) void score_kernel(ScoreParams p) {
+  __shared__ int32_t s_pref[kMaxScoreBatch + 1];       // blocks before request r
+  __shared__ int32_t s_scan[kScoreThreads];
+  __shared__ float s_part[kScoreWaves][kFlush * kMaxScoreDql];
+  __shared__ int32_t s_item_r[kFlush], s_item_h[kFlush], s_item_b[kFlush];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
   const int n = lane & 15;
   const int g = lane >> 4;
-  const int b = blockIdx.x * kScoreWaves + wave;
-  const int h = blockIdx.y;
-  const int r = blockIdx.z;
-  if (b >= p.max_blocks) return;
-  float* sc = p.score + h * p.sc_s0 + (int64_t)b * p.sc_s1;
 
-  if (r >= p.batch) {
-    // Padding token rows: nothing is visible.
-    for (int t = p.real_rows + lane; t < p.num_rows; t += 64) sc[t * p.sc_s2] = -INFINITY;
-    return;
+  // Prefix sum of visible blocks per request (a request's last token sees
+  // blocks 0 .. (seq_len-1)/128, within the score buffer and the table row).
+  if (tid == 0) s_pref[0] = 0;
+  int carry = 0;
+  for (int base = 0; base < p.batch; base += kScoreThreads) {
+    const int r = base + tid;
+    int nb = 0;
+    if (r < p.batch) {
+      const int s = p.seq_lens[r];
+      nb = s > 0 ? min((s - 1) / kPage + 1, min(p.max_blocks, p.bt_stride)) : 0;
+    }
+    s_scan[tid] = nb;
+    __syncthreads();
+    for (int off = 1; off < kScoreThreads; off <<= 1) {
+      const int v = tid >= off ? s_scan[tid - off] : 0;
+      __syncthreads();
+      s_scan[tid] += v;
+      __syncthreads();
+    }
+    if (r < p.batch) s_pref[r + 1] = carry + s_scan[tid];
+    carry += s_scan[kScoreThreads - 1];
+    __syncthreads();
   }
+  // Values read from LDS are made wavefront-uniform (readfirstlane) so that
+  // the walk below runs on scalar registers and its table reads are scalar.
+  const int per_head = __builtin_amdgcn_readfirstlane(s_pref[p.batch]);
+  const int64_t total = (int64_t)per_head * p.hkv;
 
-  const int seq = p.seq_lens[r];
-  const int t0 = r * p.dql;
-  const int pos_last = seq - 1;
-  bool vis = b < p.bt_stride && (int64_t)b * kPage <= pos_last;
-  int pg = 0;
-  if (vis) {
-    pg = p.block_table[(int64_t)r * p.bt_stride + b];
-    vis = pg >= 0 && pg < p.num_kv_blocks;
-  }
-  if (!vis) {
-    for (int l = lane; l < p.dql; l += 64) sc[(int64_t)(t0 + l) * p.sc_s2] = -INFINITY;
-    return;
-  }
-  const int nvis_max = min(kPage, pos_last - b * kPage + 1);
-  const uint8_t* page_head = p.kv + pg * p.kv_s0 + h * p.kv_s1;
-
-  BlockK<kFp8> kb;
-#pragma unroll
-  for (int tile = 0; tile < 8; ++tile) {
-    const int kr = min(16 * tile + n, nvis_max - 1);
-    const uint8_t* row = page_head + kr * p.kv_s2;
-    if constexpr (kFp8) {
-      kb.k[tile][0] = *reinterpret_cast<const u32x4_t*>(row + 16 * g);
-      kb.k[tile][1] = *reinterpret_cast<const u32x4_t*>(row + 64 + 16 * g);
-    } else {
-      kb.k[tile][0] = *reinterpret_cast<const u32x4_t*>(row + 2 * (16 * g));
-      kb.k[tile][1] = *reinterpret_cast<const u32x4_t*>(row + 2 * (16 * g + 8));
-      kb.k[tile][2] = *reinterpret_cast<const u32x4_t*>(row + 2 * (64 + 16 * g));
-      kb.k[tile][3] = *reinterpret_cast<const u32x4_t*>(row + 2 * (64 + 16 * g + 8));
+  // -inf for cells of blocks past a request's last block and for padding rows,
+  // visited with the smaller of the block and token strides innermost so the
+  // stores coalesce for either buffer orientation.
+  {
+    const int64_t cells = (int64_t)p.hkv * p.max_blocks * p.num_rows;
+    const bool b_inner = p.sc_s1 < p.sc_s2;
+    const int inner = b_inner ? p.max_blocks : p.num_rows;
+    const int outer = b_inner ? p.num_rows : p.max_blocks;
+    for (int64_t c = (int64_t)blockIdx.x * kScoreThreads + tid; c < cells;
+         c += (int64_t)gridDim.x * kScoreThreads) {
+      const int i_in = (int)(c % inner);
+      const int64_t rest = c / inner;
+      const int i_out = (int)(rest % outer);
+      const int h = (int)(rest / outer);
+      const int b = b_inner ? i_in : i_out;
+      const int t = b_inner ? i_out : i_in;
+      bool dead = t >= p.real_rows;
+      if (!dead) {
+        const int r = t / p.dql;
+        dead = b >= s_pref[r + 1] - s_pref[r];
+      }
+      if (dead) p.score[h * p.sc_s0 + (int64_t)b * p.sc_s1 + (int64_t)t * p.sc_s2] = -INFINITY;
     }
   }
 
-  for (int l = 0; l < p.dql; ++l) {
-    const int pos = seq - p.dql + l;
-    const int nvis = min(kPage, pos - b * kPage + 1);
-    float* dst = sc + (int64_t)(t0 + l) * p.sc_s2;
-    if (nvis <= 0) {
-      if (lane == 0) *dst = -INFINITY;
-      continue;
+  // This workgroup's slice of the visible items [i0, i1).
+  const int64_t i0 = total * blockIdx.x / gridDim.x;
+  const int64_t i1 = total * (blockIdx.x + 1) / gridDim.x;
+  if (i0 >= i1) return;
+
+  const int kbase = wave * kScoreKeys;
+  const uint32_t row_stride = (uint32_t)p.kv_s2;
+  int nflush = 0;
+
+  // Walk the slice as segments of one (kv head, request).
+  int64_t item = i0;
+  int h = (int)(item / per_head);
+  int rem = (int)(item - (int64_t)h * per_head);
+  int r = 0;
+  {  // first request with s_pref[r+1] > rem
+    int lo = 0, hi = p.batch - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi) >> 1;
+      if (s_pref[mid + 1] > rem) hi = mid; else lo = mid + 1;
     }
+    r = __builtin_amdgcn_readfirstlane(lo);
+  }
+  int b = __builtin_amdgcn_readfirstlane(rem - s_pref[r]);
+
+  while (item < i1) {
+    r = __builtin_amdgcn_readfirstlane(r);
+    b = __builtin_amdgcn_readfirstlane(b);
+    h = __builtin_amdgcn_readfirstlane(h);
+    const int nb_r = __builtin_amdgcn_readfirstlane(s_pref[r + 1] - s_pref[r]);
+    const int seg = (int)min((int64_t)(nb_r - b), i1 - item);
+    const int seq = ((const const_i32*)p.seq_lens)[r];
+    const int t0 = r * p.dql;
+    const int32_t* bt_row = p.block_table + (int64_t)r * p.bt_stride;
+    const uint8_t* head_base = p.kv + h * p.kv_s1;
     bf16x8_t qf[4];
-    if (n < p.group) {
-      const uint16_t* qp =
-          p.q + ((int64_t)(t0 + l) * p.hq + h * p.group + n) * kHeadDim;
-      qf[0] = as_bf16x8(*reinterpret_cast<const u32x4_t*>(qp + 16 * g));
-      qf[1] = as_bf16x8(*reinterpret_cast<const u32x4_t*>(qp + 16 * g + 8));
-      qf[2] = as_bf16x8(*reinterpret_cast<const u32x4_t*>(qp + 64 + 16 * g));
-      qf[3] = as_bf16x8(*reinterpret_cast<const u32x4_t*>(qp + 64 + 16 * g + 8));
-    } else {
+    load_q(qf, p, t0 + p.dql - 1, h, n, g);
+    const int b_last = b + seg - 1;
+
+    // Block-table entries are read through the scalar cache (uniform index,
+    // constant address space), so no vector load sits in the ring.
+    const const_i32* bt_c = (const const_i32*)(bt_row);
+    auto page_of = [&](int bb, int& lim) -> const uint8_t* {
+      int pg = bt_c[__builtin_amdgcn_readfirstlane(bb)];
+      if (pg < 0 || pg >= p.num_kv_blocks) pg = -1;
+      const int nvis = min(kPage, seq - 1 - bb * kPage + 1);
+      lim = nvis - 1;
+      return pg < 0 ? nullptr : head_base + (int64_t)pg * p.kv_s0;
+    };
+
+    KHalf<kFp8> buf[kScoreDepth];
+    const uint8_t* pages[kScoreDepth];
+    int lims[kScoreDepth];
 #pragma unroll
-      for (int c = 0; c < 4; ++c) qf[c] = as_bf16x8(u32x4_t{0u, 0u, 0u, 0u});
+    for (int j = 0; j < kScoreDepth - 1; ++j) {
+      const int bb = min(b + j, b_last);
+      pages[j] = page_of(bb, lims[j]);
+      load_khalf<kFp8>(buf[j], pages[j] ? pages[j] : head_base, row_stride,
+                       pages[j] ? lims[j] : 0, kbase, n, g);
     }
-    float best = -INFINITY;
+    for (int i = 0;; i += kScoreDepth) {
 #pragma unroll
-    for (int tile = 0; tile < 8; ++tile) {
-      bf16x8_t kf[4];
-      k_operands<kFp8>(kb, tile, kf);
-      f32x4_t s = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      for (int j = 0; j < kScoreDepth; ++j) {
+        if (i + j >= seg) goto segment_done;
+        {
+          const int jn = (j + kScoreDepth - 1) % kScoreDepth;
+          const int bn = min(b + i + j + kScoreDepth - 1, b_last);
+          pages[jn] = page_of(bn, lims[jn]);
+          load_khalf<kFp8>(buf[jn], pages[jn] ? pages[jn] : head_base, row_stride,
+                           pages[jn] ? lims[jn] : 0, kbase, n, g);
+          const int bb = b + i + j;
+          const bool ok_page = pages[j] != nullptr;
+          // token loop: the last token sees the most; earlier tokens fewer keys
+          for (int l = 0; l < p.dql; ++l) {
+            const int pos = seq - p.dql + l;
+            const int nvis = pos - bb * kPage + 1;
+            float m = -INFINITY;
+            if (ok_page && nvis > 0 && kbase < nvis) {
+              if constexpr (kOneToken) {
+                m = block_max<kFp8>(buf[j], qf, kbase, min(nvis, kPage), n, g, p.group,
+                                    p.k_scale);
+              } else {
+                bf16x8_t ql[4];
+                load_q(ql, p, t0 + l, h, n, g);
+                m = block_max<kFp8>(buf[j], ql, kbase, min(nvis, kPage), n, g, p.group,
+                                    p.k_scale);
+              }
+            }
+            if (lane == 0) s_part[wave][nflush * p.dql + l] = m;
+          }
+          if (tid == 0) {
+            s_item_r[nflush] = r;
+            s_item_h[nflush] = h;
+            s_item_b[nflush] = bb;
+          }
+          ++nflush;
+          if (nflush == kFlush) {
+            __syncthreads();
+            for (int e = tid; e < kFlush * p.dql; e += kScoreThreads) {
+              const int it = e / p.dql, l = e - it * p.dql;
+              float m = s_part[0][e];
 #pragma unroll
-      for (int c = 0; c < 4; ++c) s = mfma_bf16_16x16x32(kf[c], qf[c], s);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int key = 16 * tile + 4 * g + i;
-        if (key < nvis && n < p.group) best = fmaxf(best, s[i] * p.k_scale);
+              for (int w = 1; w < kScoreWaves; ++w) m = fmaxf(m, s_part[w][e]);
+              p.score[s_item_h[it] * p.sc_s0 + (int64_t)s_item_b[it] * p.sc_s1 +
+                      (int64_t)(s_item_r[it] * p.dql + l) * p.sc_s2] = m;
+            }
+            __syncthreads();
+            nflush = 0;
+          }
+        }
       }
     }
+  segment_done:
+    item += seg;
+    b += seg;
+    if (b >= nb_r) {  // next request (skipping empty ones), then next head
+      b = 0;
+      do {
+        if (++r == p.batch) {
+          r = 0;
+          ++h;
+        }
+      } while (item < i1 && __builtin_amdgcn_readfirstlane(s_pref[r + 1] - s_pref[r]) == 0);
+    }
+  }
+  __syncthreads();
+  for (int e = tid; e < nflush * p.dql; e += kScoreThreads) {
+    const int it = e / p.dql, l = e - it * p.dql;
+    float m = s_part[0][e];
 #pragma unroll
-    for (int off = 32; off > 0; off >>= 1) best = fmaxf(best, __shfl_xor(best, off));
-    if (lane == 0) *dst = best;
+    for (int w = 1; w < kScoreWaves; ++w) m = fmaxf(m, s_part[w][e]);
+    p.score[s_item_h[it] * p.sc_s0 + (int64_t)s_item_b[it] * p.sc_s1 +
+            (int64_t)(s_item_r[it] * p.dql + l) * p.sc_s2] = m;
   }
 }
 
-__global__ __launch_bounds__(64) void select_kernel(SelectParams p) {
-  const int lane = threadIdx.x;
+constexpr int kSelThreads = 256;
+
+// Order-preserving unsigned image of a score: larger score -> larger key.
+// -inf and NaN map to 0 (never selected); -0 maps like +0 so that the two rank
+// as equal, as they compare.
+__device__ __forceinline__ uint32_t order_key(float v) {
+  if (!(v > -INFINITY)) return 0u;
+  uint32_t u = __float_as_uint(v);
+  if (v == 0.f) u = 0u;
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+// Wavefront 0 of a radix-select pass: hist holds 256 digit counts; finds the
+// digit d such that the `need`-th largest counted element has digit d.
+// ctl[0] = d, ctl[1] = elements still needed inside bin d, ctl[2] = count of
+// bin d, ctl[3] = total counted.  Writes ctl[0..2] only if total >= need.
+__device__ __forceinline__ void pick_digit(const uint32_t* hist, int lane, uint32_t need,
+                                           uint32_t* ctl) {
+  uint32_t h[4];
+  uint32_t sum = 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    h[i] = hist[4 * lane + i];
+    sum += h[i];
+  }
+  uint32_t suffix = sum;  // count in this lane's bins and every higher bin
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const uint32_t v = __shfl_down(suffix, off);
+    if (lane + off < 64) suffix += v;
+  }
+  const uint32_t above = suffix - sum;
+  if (suffix >= need && above < need) {
+    uint32_t acc = above;
+#pragma unroll
+    for (int i = 3; i >= 0; --i) {
+      if (acc + h[i] >= need) {
+        ctl[0] = 4 * lane + i;
+        ctl[1] = need - acc;
+        ctl[2] = h[i];
+        break;
+      }
+      acc += h[i];
+    }
+  }
+  if (lane == 0) ctl[3] = suffix;
+}
+
+// One workgroup per (token row, kv head).  The row's scores live in registers
+// (kPer per thread, block b = tid + 256 i).  A most-significant-digit radix
+// select over the 32-bit keys (four 8-bit passes with LDS histograms) finds
+// the k-th largest key T exactly; if only some of the blocks whose key equals
+// T fit, two 7-bit passes over (16383 - block) pick the lowest block ids
+// among them.  The at most k chosen blocks are then ranked by (key desc,
+// block asc) with one comparison per pair.
+template <int kPer>
+__global__ __launch_bounds__(kSelThreads) void select_kernel(SelectParams p) {
+  __shared__ uint32_t s_hist[256];
+  __shared__ uint32_t s_ctl[4];
+  __shared__ uint32_t s_nsel;
+  __shared__ uint32_t s_sel_key[kMaxTopk];
+  __shared__ int32_t s_sel_blk[kMaxTopk];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
   const int t = blockIdx.x / p.hkv;
   const int h = blockIdx.x - t * p.hkv;
-  const float* s = p.score + h * p.sc_s0 + (int64_t)t * p.sc_s2;
-  int32_t* out = p.topk_out + ((int64_t)t * p.hkv + h) * p.k;
-  float pv = INFINITY;  // previous winner (score, block); nothing precedes it yet
-  int pi = -1;
-  for (int round = 0; round < p.k; ++round) {
-    float bv = -INFINITY;
-    int bi = INT_MAX;  // INT_MAX: no candidate
-    for (int b = lane; b < p.max_blocks; b += 64) {
-      const float v = s[(int64_t)b * p.sc_s1];
-      if (!(v > -INFINITY)) continue;
-      const bool after = v < pv || (v == pv && b > pi);
-      if (!after) continue;
-      if (v > bv || (v == bv && b < bi)) {
-        bv = v;
-        bi = b;
-      }
-    }
+  const float* srow = p.score + h * p.sc_s0 + (int64_t)t * p.sc_s2;
+  const int nblk = p.max_blocks;
+  const uint32_t k = (uint32_t)p.k;
+
+  uint32_t key[kPer];
 #pragma unroll
-    for (int off = 32; off > 0; off >>= 1) {
-      const float ov = __shfl_xor(bv, off);
-      const int oi = __shfl_xor(bi, off);
-      if (ov > bv || (ov == bv && oi < bi)) {
-        bv = ov;
-        bi = oi;
-      }
+  for (int i = 0; i < kPer; ++i) {
+    const int b = tid + kSelThreads * i;
+    key[i] = b < nblk ? order_key(srow[(int64_t)b * p.sc_s1]) : 0u;
+  }
+
+  uint32_t prefix = 0, mask = 0, need = k, ties = 0;
+  bool take_all = false;
+#pragma unroll 1
+  for (int pass = 0; pass < 4; ++pass) {
+    const int shift = 24 - 8 * pass;
+    s_hist[tid] = 0u;
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+      if (key[i] != 0u && (key[i] & mask) == prefix)
+        atomicAdd(&s_hist[(key[i] >> shift) & 255u], 1u);
     }
-    if (bi == INT_MAX) {
-      for (int rr = round + lane; rr < p.k; rr += 64) out[rr] = -1;
+    __syncthreads();
+    if (tid < 64) pick_digit(s_hist, lane, need, s_ctl);
+    __syncthreads();
+    if (pass == 0 && s_ctl[3] <= k) {  // at most k selectable blocks: all of them
+      take_all = true;
       break;
     }
-    if (lane == 0) out[round] = bi;
-    pv = bv;
-    pi = bi;
+    prefix |= s_ctl[0] << shift;
+    mask |= 0xFFu << shift;
+    need = s_ctl[1];
+    ties = s_ctl[2];
+    __syncthreads();
+  }
+
+  // Ties at the threshold key: keep the `need` lowest block ids (largest
+  // inverted ids), found by radix select over the 14-bit inverted id.
+  uint32_t inv_min = 0;
+  if (!take_all && need < ties) {
+    uint32_t ipref = 0, imask = 0;
+#pragma unroll 1
+    for (int pass = 0; pass < 2; ++pass) {
+      const int shift = pass == 0 ? 7 : 0;
+      s_hist[tid] = 0u;
+      __syncthreads();
+#pragma unroll
+      for (int i = 0; i < kPer; ++i) {
+        const uint32_t inv = (uint32_t)(kMaxScoreBlocks - 1 - (tid + kSelThreads * i));
+        if (key[i] == prefix && (inv & imask) == ipref)
+          atomicAdd(&s_hist[(inv >> shift) & 127u], 1u);
+      }
+      __syncthreads();
+      if (tid < 64) pick_digit(s_hist, lane, need, s_ctl);
+      __syncthreads();
+      ipref |= s_ctl[0] << shift;
+      imask |= 127u << shift;
+      need = s_ctl[1];
+      __syncthreads();
+    }
+    inv_min = ipref;
+  }
+
+  if (tid == 0) s_nsel = 0u;
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < kPer; ++i) {
+    const int b = tid + kSelThreads * i;
+    const uint32_t inv = (uint32_t)(kMaxScoreBlocks - 1 - b);
+    const bool take = take_all ? key[i] != 0u
+                               : (key[i] > prefix || (key[i] == prefix && inv >= inv_min));
+    if (take) {
+      const uint32_t slot = atomicAdd(&s_nsel, 1u);
+      if (slot < (uint32_t)kMaxTopk) {  // at most k <= kMaxTopk are taken
+        s_sel_key[slot] = key[i];
+        s_sel_blk[slot] = b;
+      }
+    }
+  }
+  __syncthreads();
+  if (tid < 64) {
+    const int nsel = min((int)s_nsel, p.k);
+    int32_t* out = p.topk_out + ((int64_t)t * p.hkv + h) * p.k;
+    if (lane < nsel) {
+      const uint32_t mk = s_sel_key[lane];
+      const int mb = s_sel_blk[lane];
+      int rank = 0;
+      for (int j = 0; j < nsel; ++j) {
+        const uint32_t kj = s_sel_key[j];
+        const int bj = s_sel_blk[j];
+        rank += (kj > mk || (kj == mk && bj < mb)) ? 1 : 0;
+      }
+      out[rank] = mb;
+    } else if (lane < p.k) {
+      out[lane] = -1;
+    }
   }
 }
 
 }  // namespace
 
 hipError_t launch_score(const ScoreParams& p, bool fp8, hipStream_t stream) {
-  const int pad = p.num_rows > p.real_rows ? 1 : 0;
-  const dim3 grid((uint32_t)((p.max_blocks + kScoreWaves - 1) / kScoreWaves),
-                  (uint32_t)p.hkv, (uint32_t)(p.batch + pad));
+  // A persistent grid: about four workgroups per CU, never more than there
+  // are possible items.
+  const int64_t upper = (int64_t)p.batch * p.hkv * p.max_blocks;
+  const int64_t grid = upper < 1024 ? (upper > 0 ? upper : 1) : 1024;
+  const dim3 g((uint32_t)grid), b(kScoreThreads);
   if (fp8) {
-    hipLaunchKernelGGL(score_kernel<true>, grid, dim3(64 * kScoreWaves), 0, stream, p);
+    if (p.dql == 1) hipLaunchKernelGGL((score_kernel<true, true>), g, b, 0, stream, p);
+    else hipLaunchKernelGGL((score_kernel<true, false>), g, b, 0, stream, p);
   } else {
-    hipLaunchKernelGGL(score_kernel<false>, grid, dim3(64 * kScoreWaves), 0, stream, p);
+    if (p.dql == 1) hipLaunchKernelGGL((score_kernel<false, true>), g, b, 0, stream, p);
+    else hipLaunchKernelGGL((score_kernel<false, false>), g, b, 0, stream, p);
   }
   return hipGetLastError();
 }
@@ -198,7 +508,12 @@ hipError_t launch_score(const ScoreParams& p, bool fp8, hipStream_t stream) {
 hipError_t launch_select(const SelectParams& p, hipStream_t stream) {
   const int64_t grid = (int64_t)p.num_rows * p.hkv;
   if (grid <= 0) return hipSuccess;
-  hipLaunchKernelGGL(select_kernel, dim3((uint32_t)grid), dim3(64), 0, stream, p);
+  const dim3 g((uint32_t)grid), b(kSelThreads);
+  const int per = (p.max_blocks + kSelThreads - 1) / kSelThreads;
+  if (per <= 2) hipLaunchKernelGGL((select_kernel<2>), g, b, 0, stream, p);
+  else if (per <= 8) hipLaunchKernelGGL((select_kernel<8>), g, b, 0, stream, p);
+  else if (per <= 32) hipLaunchKernelGGL((select_kernel<32>), g, b, 0, stream, p);
+  else hipLaunchKernelGGL((select_kernel<64>), g, b, 0, stream, p);
   return hipGetLastError();
 }
 

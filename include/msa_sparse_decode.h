@@ -163,7 +163,7 @@ msa_status msa_sparse_decode_merge(msa_plan plan, void* out, float v_scale, void
  * -inf for blocks b < max_blocks that start after the token's position; then
  * topk_out[t, h, :] = the topk_k blocks with the largest score > -inf, in
  * descending score order with ties to the lower block id, padded with -1.
- *   shape        batch, decode_query_len, num_token_rows (padding rows get
+ *   shape        batch (1..4096), decode_query_len, num_token_rows (padding rows get
  *                -inf scores and all -1 selections), heads, page_table_stride,
  *                page_size, head_dim, kv_dtype are used; topk_blocks and
  *                num_splits are ignored.

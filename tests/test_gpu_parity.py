@@ -281,6 +281,34 @@ def test_scorer_matches_oracle(kvd, dql, hq, hkv, transposed):
     assert np.all(np.isneginf(score[:, :, case.real_rows:]))
 
 
+@pytest.mark.parametrize("name,transposed", [("c2_tp4_fp8", True), ("c3_tp1_fp8", False),
+                                              ("bf16_long", True)])
+def test_scorer_full_size_sampled_rows(name, transposed):
+    """Scores of long sequences, where every workgroup of the persistent scorer
+    walks many blocks across request and head boundaries: all cells are
+    checked for -inf placement and sampled token rows against the oracle."""
+    _banner(f"scorer full size {name} transposed={transposed}")
+    if name == "bf16_long":
+        case = gen.make_random_case(141, 6, 2, 16, 2, 16, 60000, 131072, kv_dtype=gen.KV_BF16,
+                                    pad_rows=3)
+    else:
+        case = gen.make_config(name)
+    d = DevCase(case)
+    mb = case.max_blocks
+    score, _ = _run_scorer(d, mb, 16, transposed)
+    pos = case.positions()
+    visible = np.arange(mb)[None, :] * 128 <= pos[:, None]                 # [rows, mb]
+    for h in range(case.num_kv_heads):
+        assert np.array_equal(np.isneginf(score[h, :, :case.real_rows]), ~visible.T)
+    assert np.all(np.isneginf(score[:, :, case.real_rows:]))
+    rng = np.random.default_rng(7)
+    rows = sorted(set(rng.choice(case.real_rows, 4, replace=False).tolist()
+                      + [case.real_rows - 1]))
+    ref = om.block_max_scores(case.q, case.kv, case.kv_dtype, case.k_scale, case.block_table,
+                              case.seq_lens, case.dql, case.num_kv_heads, mb, rows=rows)
+    _scores_close(score[:, :, rows], ref)
+
+
 @pytest.mark.parametrize("tie_frac,transposed,k", [(0.0, False, 16), (0.4, False, 16),
                                                    (0.4, True, 5), (0.0, True, 64)])
 def test_selector_bit_exact_on_given_scores(tie_frac, transposed, k):
@@ -297,6 +325,39 @@ def test_selector_bit_exact_on_given_scores(tie_frac, transposed, k):
     torch.cuda.synchronize()
     ref = om.select_topk(sc.astype(np.float64), k)
     assert np.array_equal(out.cpu().numpy(), ref)
+
+
+@pytest.mark.parametrize("nb,k", [(2048, 16), (8000, 64), (16384, 7)])
+def test_selector_long_rows(nb, k):
+    """Rows of up to 16384 blocks (every per-thread register width of the
+    selector), with planted ties."""
+    _banner(f"selector long rows nb={nb} k={k}")
+    seq = np.array([nb * 128, nb * 64, 3 * 128 + 5], dtype=np.int32)
+    sc = gen.make_scores(151, 2, nb, 3, seq, 1, tie_frac=0.3)
+    dev = torch.from_numpy(np.ascontiguousarray(sc.transpose(0, 2, 1))).cuda().transpose(1, 2)
+    out = torch.full((3, 2, k), -7, dtype=torch.int32, device="cuda")
+    msa.msa_topk_select(dev, out)
+    torch.cuda.synchronize()
+    assert np.array_equal(out.cpu().numpy(), om.select_topk(sc.astype(np.float64), k))
+
+
+def test_selector_special_values():
+    """+-0 rank as equal (ties to the lower block), +inf is selectable, -inf and
+    NaN never are, subnormals and the extreme finite values keep their order."""
+    _banner("selector special values")
+    vals = np.array([0.0, -0.0, np.inf, -np.inf, np.nan, 1.0, -1.0, 3.0e38, -3.0e38, 1e-40,
+                     -1e-40, 2.0], dtype=np.float32)
+    rng = np.random.default_rng(161)
+    sc = rng.choice(vals, size=(2, 300, 5)).astype(np.float32)
+    sc[1, :, 4] = np.nan                       # a row with nothing selectable
+    sc[0, :, 3] = -0.0
+    sc[0, 7, 3] = 0.0                          # all equal once -0 == +0
+    dev = torch.from_numpy(sc).cuda()
+    for k in (1, 16, 64):
+        out = torch.full((5, 2, k), -7, dtype=torch.int32, device="cuda")
+        msa.msa_topk_select(dev, out)
+        torch.cuda.synchronize()
+        assert np.array_equal(out.cpu().numpy(), om.select_topk(sc.astype(np.float64), k)), k
 
 
 def _gap_ok_rows(ref_scores, k, eps):
@@ -357,3 +418,50 @@ def test_attend_then_merge_equals_run():
         msa.msa_sparse_decode_merge(plan, b, v_scale=case.v_scale)
         torch.cuda.synchronize()
         assert torch.equal(a.view(torch.int16), b.view(torch.int16)), splits
+
+
+def test_c5_full_step_full_size_sampled_rows():
+    """The full decode step with the indexer at full size (B=64, 64/4 heads,
+    seq up to 262144): GPU scores, top-16 and attend checked on sampled token
+    rows that the oracle evaluates one by one."""
+    _banner("c5 full step, full size")
+    case = gen.make_config("c5_full_step")
+    d = DevCase(case)
+    mb = case.max_blocks
+    rows_all = case.num_token_rows
+    # the timed layout: physical [Hkv, rows, blocks] seen as logical [Hkv, blocks, rows]
+    score = torch.full((case.num_kv_heads, rows_all, mb), float("nan"),
+                       device="cuda").transpose(1, 2)
+    sel = torch.full((rows_all, case.num_kv_heads, 16), -7, dtype=torch.int32, device="cuda")
+    msa.msa_block_score_topk(d.q, d.kv, d.block_table, d.seq_lens, decode_query_len=case.dql,
+                             num_kv_heads=case.num_kv_heads, max_blocks=mb, score=score,
+                             topk_out=sel, k_scale=case.k_scale)
+    out = torch.full_like(d.q, float("nan"))
+    plan = msa.msa_sparse_decode_plan(
+        case.batch, case.dql, num_q_heads=case.num_q_heads, num_kv_heads=case.num_kv_heads,
+        page_table_stride=d.block_table.stride(0), topk_blocks=16, kv_dtype=msa.KV_FP8_E4M3,
+        device=d.dev)
+    msa.msa_sparse_decode_run(plan, d.q, d.kv, d.block_table, d.seq_lens, sel, out,
+                              sm_scale=case.sm_scale)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(5)
+    # the longest and shortest requests plus random ones
+    order = np.argsort(case.seq_lens)
+    rows = sorted(set([int(order[0]), int(order[-1])] + rng.choice(64, 4, replace=False).tolist()))
+    ref_scores = om.block_max_scores(case.q, case.kv, case.kv_dtype, case.k_scale,
+                                     case.block_table, case.seq_lens, case.dql,
+                                     case.num_kv_heads, mb, rows=rows)
+    got_scores = score.cpu().numpy().astype(np.float64)[:, :, rows]
+    tol = _scores_close(got_scores, ref_scores)
+    ref_sel = om.select_topk(ref_scores, 16)                      # [len(rows), Hkv, 16]
+    got_sel = sel.cpu().numpy()[rows]
+    ok = _gap_ok_rows(ref_scores, 16, 4 * tol)
+    assert ok.mean() > 0.8
+    assert np.array_equal(got_sel[ok], ref_sel[ok])
+    full_sel = sel.cpu().numpy().copy()
+    for i, t in enumerate(rows):
+        full_sel[t] = ref_sel[i]
+    ok_rows = [t for i, t in enumerate(rows) if ok[i].all()]
+    assert ok_rows
+    ref_out = oracle_attend(case, rows=ok_rows, topk=full_sel)
+    assert_parity(to_f64(out)[ok_rows], ref_out, what=f"c5 attend on {len(ok_rows)} rows")
