@@ -42,10 +42,17 @@ HBM_PEAK_GBS = 8000.0
 DEFAULT_CONFIG = "c2_tp4_fp8"
 OTHER_CONFIGS = ("c3_tp1_fp8", "c4_spec_ragged")
 FULL_STEP_CONFIG = "c5_full_step"
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attend_traffic.json")
-KERNEL_SOURCES = ("block_sparse_gqa_decode_amd/csrc/msa_attend.hip",
-                  "block_sparse_gqa_decode_amd/csrc/msa_device.h",
-                  "block_sparse_gqa_decode_amd/csrc/msa_internal.h")
+# rocprofv3 counter summaries, each valid for the kernel sources it was taken on
+TRAFFIC_FILES = {"attend": os.path.join(ROOT, "profiles", "attend_traffic.json"),
+                 "score": os.path.join(ROOT, "profiles", "score_traffic.json")}
+KERNEL_SOURCES = {
+    "attend": ("block_sparse_gqa_decode_amd/csrc/msa_attend.hip",
+               "block_sparse_gqa_decode_amd/csrc/msa_device.h",
+               "block_sparse_gqa_decode_amd/csrc/msa_internal.h"),
+    "score": ("block_sparse_gqa_decode_amd/csrc/msa_score.hip",
+              "block_sparse_gqa_decode_amd/csrc/msa_device.h",
+              "block_sparse_gqa_decode_amd/csrc/msa_internal.h"),
+}
 
 CONFIG_TEXT = {
     "c1_tiny_bf16": "tiny bf16 decode: B=2, dql=1, 16/1 heads, top-4, seq {512,1000}",
@@ -60,9 +67,9 @@ CONFIG_TEXT = {
 }
 
 
-def kernel_source_hash() -> str:
+def kernel_source_hash(kernel: str = "attend") -> str:
     h = hashlib.sha256()
-    for rel in KERNEL_SOURCES:
+    for rel in KERNEL_SOURCES[kernel]:
         with open(os.path.join(ROOT, rel), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
@@ -274,8 +281,10 @@ def scorer_bytes(case):
     topk_bytes = case.num_token_rows * case.num_kv_heads * case.topk_k * 4
     table_bytes = int(np.sum((case.seq_lens.astype(np.int64) + 127) // 128)) * 4 * \
         case.num_kv_heads
-    return {"k_half": k_bytes, "algorithmic": k_bytes + q_bytes + 2 * score_bytes +
-            topk_bytes + table_bytes}
+    scorer = k_bytes + q_bytes + score_bytes + table_bytes
+    selector = score_bytes + topk_bytes
+    return {"k_half": k_bytes, "scorer": scorer, "selector": selector,
+            "algorithmic": scorer + selector}
 
 
 class FullStepSet:
@@ -330,6 +339,10 @@ class FullStepSet:
                                        sm_scale=c.sm_scale, k_scale=c.k_scale,
                                        v_scale=c.v_scale)
 
+    def run_select(self, i):
+        _, _, score, sel, _ = self.sets[i]
+        self.msa.msa_topk_select(score, sel)
+
     def run_step(self, i):
         self.run_score(i)
         self.run_attend(i)
@@ -382,6 +395,7 @@ def time_full_step(name, steps, warmup, replicas, dev, verbose=True):
               f"{case.max_blocks})", file=sys.stderr, flush=True)
     step_ms, n = _graph_time(fs.run_step, replicas, steps, warmup)
     score_ms, _ = _graph_time(fs.run_score, replicas, steps, warmup)
+    select_ms, _ = _graph_time(fs.run_select, replicas, steps, warmup)
     attend_ms, _ = _graph_time(fs.run_attend, replicas, steps, warmup)
     torch.cuda.synchronize()
     sb = scorer_bytes(case)
@@ -395,10 +409,15 @@ def time_full_step(name, steps, warmup, replicas, dev, verbose=True):
     res = {
         "config": name, "steps": n, "ms_per_step": step_ms,
         "tokens_per_s": case.real_rows / (step_ms / 1e3),
-        "score_topk_ms": score_ms, "attend_ms": attend_ms,
+        "score_topk_ms": score_ms, "select_ms": select_ms, "attend_ms": attend_ms,
         "score_k_half_bytes": sb["k_half"], "score_algorithmic_bytes": sb["algorithmic"],
-        "score_algorithmic_gbs": sb["algorithmic"] / (score_ms / 1e3) / 1e9,
-        "score_pct_hbm_peak": 100 * sb["algorithmic"] / (score_ms / 1e3) / 1e9 / HBM_PEAK_GBS,
+        # scorer alone: the score+select launch pair minus the selector's own time
+        "scorer_bytes": sb["scorer"],
+        "scorer_gbs": sb["scorer"] / ((score_ms - select_ms) / 1e3) / 1e9,
+        "scorer_pct_hbm_peak": 100 * sb["scorer"] / ((score_ms - select_ms) / 1e3) / 1e9
+                               / HBM_PEAK_GBS,
+        "score_traffic_bytes": (lambda t: None if t is None else t.get("hbm_bytes_per_launch"))(
+            load_traffic(kernel_source_hash("score"), "score")),
         "attend_algorithmic_bytes": att, "attend_effective_kv_bytes": eff,
         "attend_algorithmic_gbs": att / (attend_ms / 1e3) / 1e9,
         "step_algorithmic_gbs": (att + sb["algorithmic"]) / (step_ms / 1e3) / 1e9,
@@ -456,11 +475,11 @@ def cpu_baseline(case, seconds: float):
     }
 
 
-def load_traffic(src_hash):
+def load_traffic(src_hash, kernel: str = "attend"):
     """HBM bytes per launch from the committed rocprofv3 counter summary, if it
     was taken on the current kernel source; else None."""
     try:
-        with open(TRAFFIC_FILE) as f:
+        with open(TRAFFIC_FILES[kernel]) as f:
             rec = json.load(f)
     except (OSError, ValueError):
         return None
@@ -476,6 +495,16 @@ def profile_mode(name, launches, splits, dev):
     from workloads import gen
 
     case = gen.make_config(name, replicas=1)
+    if name == FULL_STEP_CONFIG:
+        fs = FullStepSet(case, 2, dev)
+        for i in range(launches):
+            fs.run_step(i % 2)
+        torch.cuda.synchronize()
+        print(json.dumps({"profile_mode": name, "launches": launches,
+                          "scorer_bytes_per_launch": scorer_bytes(case)["scorer"],
+                          "selector_bytes_per_launch": scorer_bytes(case)["selector"],
+                          "kernel_source_sha": kernel_source_hash("score")}), flush=True)
+        return
     ds = DeviceSet(case, 2, splits, dev)
     for i in range(launches):
         ds.run_step(i % 2)
@@ -543,7 +572,8 @@ def main():
         copy_calibration(dev)
         return
     if args.profile_mode:
-        profile_mode(args.config, args.profile_launches, args.splits, dev)
+        profile_mode(FULL_STEP_CONFIG if args.full_step_only else args.config,
+                     args.profile_launches, args.splits, dev)
         return
 
     if args.full_step_only:
