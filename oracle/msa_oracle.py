@@ -36,13 +36,21 @@ design notes):
    outputs exact zeros (PR #17171, flash-decoding commit: zeroed, not NaN,
    output for padding rows).
 5. q head ``j`` reads kv head ``j // G`` with ``G = Hq / Hkv``.
-6. KV bytes are OCP fp8 e4m3fn (``torch.float8_e4m3fn`` in the test file) or
-   bf16; K is the first 128 entries of the packed last dim, V the last 128
-   (``msa_cutlass_sparse_decode``: ``kv_cache.split(_HEAD_DIM, dim=-1)``).
-   ``k_scale``/``v_scale`` multiply the decoded values.
+6. KV bytes are OCP fp8 e4m3fn (``torch.float8_e4m3fn`` in the test file),
+   OCP fp8 e5m2 (the backend's ``supported_kv_cache_dtypes`` lists
+   ``fp8_e5m2``; ``MiniMaxM3SparseTritonImpl`` picks ``torch.float8_e5m2`` off
+   fnuz platforms, and gfx950 uses the OCP formats) or bf16; K is the first 128
+   entries of the packed last dim, V the last 128 (``msa_cutlass_sparse_decode``:
+   ``kv_cache.split(_HEAD_DIM, dim=-1)``).  ``k_scale``/``v_scale`` multiply the
+   decoded values.
 7. The scorer uses the attention q and the K half of the same cache, raw dot
    product (no softmax scale), ``-inf`` for blocks that start after ``pos``.
 8. The selector ranks blocks with score ``> -inf`` by (score desc, block asc).
+9. q is bf16, or OCP fp8 e4m3fn codes with a per-tensor ``q_scale``: the value
+   is ``decode(code) * q_scale`` (``msa_cutlass_sparse_decode(query_fp8, ...,
+   q_scale_float, ...)``; the test file compares it with the bf16 path fed
+   ``query_fp8.to(bfloat16) * q_scale``).  A bf16 q is multiplied by
+   ``q_scale`` too (1 by default).
 
 Pins: every function here is checked in ``tests/test_oracle_pins.py`` against
 something other than itself (torch's fp8/bf16 casts, dense causal attention
@@ -86,6 +94,30 @@ def decode_e4m3fn(codes) -> np.ndarray:
 _E4M3_TABLE = decode_e4m3fn(np.arange(256))
 
 
+def decode_e5m2(codes) -> np.ndarray:
+    """OCP fp8 e5m2 code -> float64 value.
+
+    Bit fields: sign s (bit 7), exponent E (bits 6..2, bias 15), mantissa M
+    (bits 1..0).  E == 31 is +-inf when M == 0 and NaN otherwise; E == 0 is
+    subnormal ``M/4 * 2^-14``; otherwise ``(1 + M/4) * 2^(E-15)``.  Largest
+    finite magnitude 57344.
+    """
+    c = np.asarray(codes).astype(np.int64)
+    s = (c >> 7) & 1
+    e = (c >> 2) & 0x1F
+    m = c & 0x3
+    sign = np.where(s == 1, -1.0, 1.0)
+    sub = sign * (m / 4.0) * 2.0 ** -14
+    nor = sign * (1.0 + m / 4.0) * np.exp2(e.astype(np.float64) - 15.0)
+    v = np.where(e == 0, sub, nor)
+    v = np.where((e == 31) & (m == 0), sign * np.inf, v)
+    v = np.where((e == 31) & (m != 0), np.nan, v)
+    return v.astype(np.float64)
+
+
+_E5M2_TABLE = decode_e5m2(np.arange(256))
+
+
 def decode_bf16(bits) -> np.ndarray:
     """bf16 bit pattern (uint16) -> float64 (exact: bf16 is the top half of an
     fp32)."""
@@ -98,9 +130,21 @@ def dequant(raw: np.ndarray, kv_dtype: str, scale: float) -> np.ndarray:
     """Stored KV entries -> float64 values times the per-tensor scale."""
     if kv_dtype == "fp8_e4m3":
         return _E4M3_TABLE[np.asarray(raw, dtype=np.uint8)] * float(scale)
+    if kv_dtype == "fp8_e5m2":
+        return _E5M2_TABLE[np.asarray(raw, dtype=np.uint8)] * float(scale)
     if kv_dtype == "bf16":
         return decode_bf16(raw) * float(scale)
     raise ValueError(f"unknown kv dtype {kv_dtype!r}")
+
+
+def decode_query(q, q_dtype: str, q_scale: float) -> np.ndarray:
+    """Stored q entries (bf16 bits, or fp8 e4m3fn codes) -> float64 values
+    times the per-tensor q scale (reading 9)."""
+    if q_dtype == "bf16":
+        return decode_bf16(q) * float(q_scale)
+    if q_dtype == "fp8_e4m3":
+        return _E4M3_TABLE[np.asarray(q, dtype=np.uint8)] * float(q_scale)
+    raise ValueError(f"unknown q dtype {q_dtype!r}")
 
 
 # ---------------------------------------------------------------------------
@@ -164,10 +208,12 @@ def gather_live(kv, kv_dtype, k_scale, v_scale, block_table_row, pos, head,
 
 
 def sparse_decode(q_bits, kv, kv_dtype, k_scale, v_scale, block_table, seq_lens,
-                  topk, decode_query_len, num_kv_heads, sm_scale, rows=None):
+                  topk, decode_query_len, num_kv_heads, sm_scale, rows=None,
+                  q_dtype="bf16", q_scale=1.0):
     """Block-sparse GQA decode, float64.
 
-    q_bits   uint16 bf16 bits [num_token_rows, Hq, 128]
+    q_bits   uint16 bf16 bits, or uint8 fp8 e4m3fn codes (``q_dtype``),
+             [num_token_rows, Hq, 128]; values times ``q_scale``
     kv       uint8 (fp8 codes) or uint16 (bf16 bits) [num_blocks, Hkv, 128, 256]
     topk     int32 [num_token_rows, Hkv, k] logical block ids (-1 = none)
     rows     optional iterable of token rows to evaluate (default: all)
@@ -197,7 +243,8 @@ def sparse_decode(q_bits, kv, kv_dtype, k_scale, v_scale, block_table, seq_lens,
             k, v = gathered[h]
             if k is None:
                 continue
-            out[i, j] = softmax_attend(decode_bf16(q_bits[t, j]), k, v, sm_scale)
+            qv = decode_query(q_bits[t, j], q_dtype, q_scale)
+            out[i, j] = softmax_attend(qv, k, v, sm_scale)
     return out
 
 
@@ -206,7 +253,8 @@ def sparse_decode(q_bits, kv, kv_dtype, k_scale, v_scale, block_table, seq_lens,
 # ---------------------------------------------------------------------------
 
 def block_max_scores(q_bits, kv, kv_dtype, k_scale, block_table, seq_lens,
-                     decode_query_len, num_kv_heads, max_blocks, rows=None):
+                     decode_query_len, num_kv_heads, max_blocks, rows=None,
+                     q_dtype="bf16", q_scale=1.0):
     """score[h, b, t] = max over the group's q heads g and the visible keys j
     of block b of q[t, h*G+g] . K[page(b), h, j]; -inf where block b starts
     after token t's position.  Raw dot product (no softmax scale).
@@ -226,7 +274,8 @@ def block_max_scores(q_bits, kv, kv_dtype, k_scale, block_table, seq_lens,
         r, loc = divmod(int(t), dql)
         pos = token_position(seq_lens[r], dql, loc)
         for h in range(num_kv_heads):
-            qs = decode_bf16(q_bits[t, h * group:(h + 1) * group])   # [G, D]
+            qs = decode_query(q_bits[t, h * group:(h + 1) * group], q_dtype,
+                              q_scale)                               # [G, D]
             for b in range(max_blocks):
                 n = visible_rows(pos, b)
                 if n <= 0:

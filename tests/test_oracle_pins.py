@@ -35,13 +35,23 @@ def torch_values(kv: np.ndarray, kv_dtype: str) -> torch.Tensor:
     if kv_dtype == gen.KV_FP8:
         return torch.from_numpy(np.ascontiguousarray(kv)).view(torch.float8_e4m3fn).to(
             torch.float64)
+    if kv_dtype == gen.KV_E5M2:
+        return torch.from_numpy(np.ascontiguousarray(kv)).view(torch.float8_e5m2).to(
+            torch.float64)
     return torch.from_numpy(np.ascontiguousarray(kv).view(np.int16)).view(
         torch.bfloat16).to(torch.float64)
 
 
-def torch_q(q_bits: np.ndarray) -> torch.Tensor:
-    return torch.from_numpy(np.ascontiguousarray(q_bits).view(np.int16)).view(
-        torch.bfloat16).to(torch.float64)
+def torch_q(q_bits: np.ndarray, q_dtype: str = gen.Q_BF16, q_scale: float = 1.0
+            ) -> torch.Tensor:
+    """q values through torch's casts: bf16 bits, or e4m3fn codes, times q_scale
+    (the test page feeds its reference ``query_fp8.to(bfloat16) * q_scale``)."""
+    if q_dtype == gen.Q_FP8:
+        v = torch.from_numpy(np.ascontiguousarray(q_bits)).view(torch.float8_e4m3fn)
+    else:
+        v = torch.from_numpy(np.ascontiguousarray(q_bits).view(np.int16)).view(
+            torch.bfloat16)
+    return v.to(torch.float64) * q_scale
 
 
 def dense_reference(case: gen.DecodeCase) -> np.ndarray:
@@ -51,7 +61,7 @@ def dense_reference(case: gen.DecodeCase) -> np.ndarray:
     hq, hkv = case.num_q_heads, case.num_kv_heads
     g = hq // hkv
     vals = torch_values(case.kv, case.kv_dtype)
-    q = torch_q(case.q)
+    q = torch_q(case.q, case.q_dtype, case.q_scale)
     out = torch.zeros(case.num_token_rows, hq, 128, dtype=torch.float64)
     for r in range(case.batch):
         s = int(case.seq_lens[r])
@@ -74,7 +84,8 @@ def run_oracle(case: gen.DecodeCase, topk=None, **over) -> np.ndarray:
     kw = dict(q_bits=case.q, kv=case.kv, kv_dtype=case.kv_dtype, k_scale=case.k_scale,
               v_scale=case.v_scale, block_table=case.block_table, seq_lens=case.seq_lens,
               topk=case.topk if topk is None else topk, decode_query_len=case.dql,
-              num_kv_heads=case.num_kv_heads, sm_scale=case.sm_scale)
+              num_kv_heads=case.num_kv_heads, sm_scale=case.sm_scale,
+              q_dtype=case.q_dtype, q_scale=case.q_scale)
     kw.update(over)
     return om.sparse_decode(**kw)
 
@@ -86,9 +97,10 @@ def dense_pin_error(case: gen.DecodeCase) -> float:
 
 
 def small_dense_case(hq=16, hkv=1, dql=4, kv_dtype=gen.KV_FP8, pattern=(257, 513),
-                     pairs=1, seed=0, k_scale=1.0, v_scale=1.0):
+                     pairs=1, seed=0, k_scale=1.0, v_scale=1.0, q_dtype=gen.Q_BF16,
+                     q_scale=1.0):
     case = gen.make_p3_case(hq, hkv, pairs, dql, seq_pattern=pattern, seed=seed,
-                            kv_dtype=kv_dtype, topk_k=8)
+                            kv_dtype=kv_dtype, topk_k=8, q_dtype=q_dtype, q_scale=q_scale)
     case.k_scale, case.v_scale = k_scale, v_scale
     return case
 
@@ -106,6 +118,18 @@ def test_e4m3fn_decode_exhaustive_vs_torch():
     assert np.all(both_nan | (mine == ref))
     # sign of zero too
     assert np.array_equal(np.signbit(mine[~both_nan]), np.signbit(ref[~both_nan]))
+
+
+def test_e5m2_decode_exhaustive_vs_torch():
+    codes = np.arange(256, dtype=np.uint8)
+    mine = om.decode_e5m2(codes)
+    ref = torch.from_numpy(codes).view(torch.float8_e5m2).to(torch.float64).numpy()
+    assert np.array_equal(np.isnan(mine), np.isnan(ref))
+    ok = ~np.isnan(ref)
+    assert np.array_equal(mine[ok], ref[ok])           # includes +-inf
+    assert np.array_equal(np.signbit(mine[ok]), np.signbit(ref[ok]))
+    fin = np.isfinite(mine)
+    assert np.max(mine[fin]) == 57344.0 and np.sum(np.isinf(mine)) == 2
 
 
 def test_e4m3fn_golden_codes():
@@ -131,6 +155,17 @@ def test_bf16_decode_exhaustive_vs_torch():
 def test_dequant_applies_scale():
     codes = np.arange(0, 0x7E, dtype=np.uint8)
     assert np.array_equal(om.dequant(codes, "fp8_e4m3", 0.5), om.decode_e4m3fn(codes) * 0.5)
+    codes = np.arange(0, 0x7C, dtype=np.uint8)
+    assert np.array_equal(om.dequant(codes, "fp8_e5m2", 0.25), om.decode_e5m2(codes) * 0.25)
+
+
+def test_fp8_query_decode_vs_torch():
+    codes = np.arange(256, dtype=np.uint8)
+    mine = om.decode_query(codes, "fp8_e4m3", 0.5)
+    ref = torch_q(codes, gen.Q_FP8, 0.5).numpy()
+    assert np.array_equal(np.isnan(mine), np.isnan(ref))
+    ok = ~np.isnan(ref)
+    assert np.array_equal(mine[ok], ref[ok])
 
 
 # ---------------------------------------------------------------------------
@@ -168,6 +203,25 @@ def test_generator_stride_and_scale_facts():
 def test_dense_equivalence(dql, heads, kv_dtype):
     case = small_dense_case(heads[0], heads[1], dql, kv_dtype)
     assert dense_pin_error(case) < 1e-12
+
+
+@pytest.mark.parametrize("dql", [1, 4])
+@pytest.mark.parametrize("fmt", [(gen.KV_E5M2, gen.Q_BF16, 1.0), (gen.KV_FP8, gen.Q_FP8, 1.0),
+                                 (gen.KV_FP8, gen.Q_FP8, 0.5), (gen.KV_E5M2, gen.Q_FP8, 0.25)])
+def test_dense_equivalence_other_formats(dql, fmt):
+    """e5m2 KV and fp8 q with a q scale, against SDPA on torch-decoded values."""
+    kv_dtype, q_dtype, q_scale = fmt
+    case = small_dense_case(8, 2, dql, kv_dtype, q_dtype=q_dtype, q_scale=q_scale)
+    assert dense_pin_error(case) < 1e-12
+
+
+def test_q_scale_is_a_softmax_temperature():
+    """softmax(c * (s q) . k) == softmax((c s) q . k): a q scale acts exactly
+    like the same factor on sm_scale (the definition, reading 9)."""
+    case = small_dense_case(8, 2, 3, q_dtype=gen.Q_FP8, q_scale=0.75)
+    a = run_oracle(case)
+    b = run_oracle(case, q_scale=1.0, sm_scale=case.sm_scale * 0.75)
+    assert np.allclose(a, b, rtol=1e-12, atol=1e-13)
 
 
 @pytest.mark.parametrize("pattern", [(129, 385), (1, 128), (127, 130)])
@@ -261,7 +315,7 @@ def test_large_scale_picks_argmax_key():
     scale = 1e4
     out = run_oracle(case, sm_scale=scale)
     vals = torch_values(case.kv, case.kv_dtype).numpy()
-    q = torch_q(case.q).numpy()
+    q = torch_q(case.q, case.q_dtype, case.q_scale).numpy()
     g = case.num_q_heads // case.num_kv_heads
     checked = 0
     for t in range(case.real_rows):
@@ -378,7 +432,7 @@ def test_row_subset_matches_full():
 def brute_scores(case, max_blocks):
     """Triple loop over (h, b, t) and every (g, j) pair, torch-decoded K."""
     vals = torch_values(case.kv, case.kv_dtype).numpy()
-    q = torch_q(case.q).numpy()
+    q = torch_q(case.q, case.q_dtype, case.q_scale).numpy()
     g = case.num_q_heads // case.num_kv_heads
     out = np.full((case.num_kv_heads, max_blocks, case.real_rows), -np.inf)
     for t in range(case.real_rows):
@@ -400,15 +454,19 @@ def run_scores(case, max_blocks=None, **over):
     kw = dict(q_bits=case.q, kv=case.kv, kv_dtype=case.kv_dtype, k_scale=case.k_scale,
               block_table=case.block_table, seq_lens=case.seq_lens,
               decode_query_len=case.dql, num_kv_heads=case.num_kv_heads,
-              max_blocks=max_blocks or case.max_blocks)
+              max_blocks=max_blocks or case.max_blocks, q_dtype=case.q_dtype,
+              q_scale=case.q_scale)
     kw.update(over)
     return om.block_max_scores(**kw)
 
 
-@pytest.mark.parametrize("kv_dtype", [gen.KV_FP8, gen.KV_BF16])
-def test_scorer_brute_force(kv_dtype):
+@pytest.mark.parametrize("kv_dtype,q_dtype,q_scale", [
+    (gen.KV_FP8, gen.Q_BF16, 1.0), (gen.KV_BF16, gen.Q_BF16, 1.0),
+    (gen.KV_E5M2, gen.Q_BF16, 1.0), (gen.KV_FP8, gen.Q_FP8, 0.5)])
+def test_scorer_brute_force(kv_dtype, q_dtype, q_scale):
     case = gen.make_random_case(seed=21, batch=2, dql=2, num_q_heads=4, num_kv_heads=2,
-                                topk_k=4, seq_lo=129, seq_hi=400, kv_dtype=kv_dtype)
+                                topk_k=4, seq_lo=129, seq_hi=400, kv_dtype=kv_dtype,
+                                q_dtype=q_dtype, q_scale=q_scale)
     case.k_scale = 0.5
     mb = case.max_blocks + 1
     a = run_scores(case, mb)
@@ -513,13 +571,22 @@ MUTANTS = {
                                           / np.exp(z - z.max()).sum())(k @ qv)),
     "scale_ignored": ("dequant", lambda raw, dt, scale: (
         om._E4M3_TABLE[np.asarray(raw, dtype=np.uint8)] if dt == "fp8_e4m3"
+        else om._E5M2_TABLE[np.asarray(raw, dtype=np.uint8)] if dt == "fp8_e5m2"
         else om.decode_bf16(raw))),
+    "q_scale_ignored": ("decode_query", lambda q, dt, scale: (
+        om._E4M3_TABLE[np.asarray(q, dtype=np.uint8)] if dt == "fp8_e4m3"
+        else om.decode_bf16(q))),
+    "e5m2_bias_16": ("dequant", lambda raw, dt, scale: (
+        om.decode_e5m2(raw) * 0.5 * scale if dt == "fp8_e5m2"
+        else om._E4M3_TABLE[np.asarray(raw, dtype=np.uint8)] * scale if dt == "fp8_e4m3"
+        else om.decode_bf16(raw) * scale)),
 }
 
 
 def _pins_pass():
     cases = [small_dense_case(8, 2, 4), small_dense_case(8, 2, 1),
-             small_dense_case(8, 2, 3, k_scale=0.5, v_scale=2.0)]
+             small_dense_case(8, 2, 3, k_scale=0.5, v_scale=2.0),
+             small_dense_case(8, 2, 2, gen.KV_E5M2, q_dtype=gen.Q_FP8, q_scale=0.5)]
     return all(dense_pin_error(c) < 1e-12 for c in cases)
 
 

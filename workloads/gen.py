@@ -18,9 +18,12 @@ Shapes and structure follow the workloads the pages describe:
   ``_make_paged_layout`` and ``_make_topk``.
 * Token row ``t = request * dql + local`` at position
   ``seq_len - dql + local`` (same test file, ``_make_topk``).
+* An fp8 query: e4m3fn codes of ``q / q_scale`` with a per-tensor scale (the
+  test file quantizes the bf16 query with ``scaled_fp8_quant`` and a given
+  scale before ``msa_cutlass_sparse_decode``).
 
 Every array is plain NumPy: fp8 codes as ``uint8``, bf16 as ``uint16`` bit
-patterns, indices as ``int32``.
+patterns, indices as ``int32``.  fp8 e5m2 KV codes are ``uint8`` too.
 """
 from __future__ import annotations
 
@@ -34,11 +37,16 @@ import numpy as np
 PAGE = 128
 HEAD_DIM = 128
 FP8_MAX = 448.0
+E5M2_MAX = 57344.0
 BF16_NAN_BITS = 0x7FC0
-FP8_NAN_CODE = 0x7F
+FP8_NAN_CODE = 0x7F      # NaN in both e4m3fn (E=15, M=7) and e5m2 (E=31, M=3)
 
 KV_FP8 = "fp8_e4m3"
+KV_E5M2 = "fp8_e5m2"
 KV_BF16 = "bf16"
+KV_8BIT = (KV_FP8, KV_E5M2)
+Q_BF16 = "bf16"
+Q_FP8 = "fp8_e4m3"
 
 
 # ---------------------------------------------------------------------------
@@ -62,6 +70,15 @@ def encode_e4m3fn(x: np.ndarray) -> np.ndarray:
     return t.to(torch.float8_e4m3fn).view(torch.uint8).numpy().copy()
 
 
+def encode_e5m2(x: np.ndarray) -> np.ndarray:
+    """float array -> OCP fp8 e5m2 codes (uint8), clipped to +-57344 first."""
+    import torch
+
+    t = torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32))
+    t = t.clamp(-E5M2_MAX, E5M2_MAX)
+    return t.to(torch.float8_e5m2).view(torch.uint8).numpy().copy()
+
+
 def _normal_f32(rng: np.random.Generator, shape, std: float) -> np.ndarray:
     x = rng.standard_normal(size=shape, dtype=np.float32)
     if std != 1.0:
@@ -70,7 +87,11 @@ def _normal_f32(rng: np.random.Generator, shape, std: float) -> np.ndarray:
 
 
 def _encode(x: np.ndarray, kv_dtype: str) -> np.ndarray:
-    return encode_e4m3fn(x) if kv_dtype == KV_FP8 else encode_bf16(x)
+    if kv_dtype == KV_FP8:
+        return encode_e4m3fn(x)
+    if kv_dtype == KV_E5M2:
+        return encode_e5m2(x)
+    return encode_bf16(x)
 
 
 # ---------------------------------------------------------------------------
@@ -93,11 +114,13 @@ class DecodeCase:
     seq_lens: np.ndarray           # int32 [batch]
     block_table: np.ndarray        # int32 [batch, stride]
     kv: np.ndarray                 # uint8 / uint16 [num_blocks, Hkv, 128, 256]
-    q: np.ndarray                  # uint16 bf16 bits [rows, Hq, 128]
+    q: np.ndarray                  # uint16 bf16 bits / uint8 e4m3 codes [rows, Hq, 128]
     topk: np.ndarray | None        # int32 [rows, Hkv, k] logical block ids, -1 pad
     sm_scale: float = HEAD_DIM ** -0.5
     k_scale: float = 1.0
     v_scale: float = 1.0
+    q_dtype: str = Q_BF16
+    q_scale: float = 1.0
     max_blocks: int = 0            # ceil(max seq / 128)
     replicas: list = field(default_factory=list)   # [(q, topk)] extra sets
     notes: str = ""
@@ -197,7 +220,7 @@ def every_visible_topk(seq_lens, num_kv_heads: int, dql: int, k: int) -> np.ndar
 
 def poison_tail_slots(kv: np.ndarray, block_table, seq_lens, kv_dtype: str) -> None:
     """Write NaN patterns into the slots past seq_len of every last page."""
-    bad = FP8_NAN_CODE if kv_dtype == KV_FP8 else BF16_NAN_BITS
+    bad = FP8_NAN_CODE if kv_dtype in KV_8BIT else BF16_NAN_BITS
     for r, s in enumerate(seq_lens):
         n = pages_for(s)
         used = int(s) - (n - 1) * PAGE
@@ -206,7 +229,7 @@ def poison_tail_slots(kv: np.ndarray, block_table, seq_lens, kv_dtype: str) -> N
 
 
 def fill_pages(kv: np.ndarray, pages, kv_dtype: str) -> None:
-    bad = FP8_NAN_CODE if kv_dtype == KV_FP8 else BF16_NAN_BITS
+    bad = FP8_NAN_CODE if kv_dtype in KV_8BIT else BF16_NAN_BITS
     for p in pages:
         kv[int(p)] = bad
 
@@ -219,7 +242,7 @@ def make_pool(rng: np.random.Generator, num_pages: int, num_kv_heads: int,
     from ``default_rng([pool_seed, i])``, so chunks are independent,
     reproducible one at a time, and generated on several threads.
     """
-    dt = np.uint8 if kv_dtype == KV_FP8 else np.uint16
+    dt = np.uint8 if kv_dtype in KV_8BIT else np.uint16
     kv = np.empty((num_pages, num_kv_heads, PAGE, 2 * HEAD_DIM), dtype=dt)
     pool_seed = int(rng.integers(0, 2 ** 63 - 1))
 
@@ -241,8 +264,13 @@ def make_pool(rng: np.random.Generator, num_pages: int, num_kv_heads: int,
     return kv
 
 
-def make_q(rng: np.random.Generator, rows: int, num_q_heads: int, std: float = 1.0):
-    return encode_bf16(_normal_f32(rng, (rows, num_q_heads, HEAD_DIM), std))
+def make_q(rng: np.random.Generator, rows: int, num_q_heads: int, std: float = 1.0,
+           q_dtype: str = Q_BF16, q_scale: float = 1.0):
+    """Q ~ N(0, std): bf16 bits, or e4m3fn codes of q / q_scale."""
+    x = _normal_f32(rng, (rows, num_q_heads, HEAD_DIM), std)
+    if q_dtype == Q_FP8:
+        return encode_e4m3fn(x / np.float32(q_scale))
+    return encode_bf16(x)
 
 
 # ---------------------------------------------------------------------------
@@ -251,6 +279,10 @@ def make_q(rng: np.random.Generator, rows: int, num_q_heads: int, std: float = 1
 
 CONFIG_NAMES = ("c1_tiny_bf16", "c2_tp4_fp8", "c3_tp1_fp8", "c4_spec_ragged",
                 "c5_full_step")
+# The c2 shape through the two other input formats: fp8 q with a per-tensor
+# q_scale over the fp8 e4m3 cache, and bf16 q over an fp8 e5m2 cache.
+FORMAT_CONFIG_NAMES = ("c2_tp4_fp8q", "c2_tp4_e5m2")
+C2_FP8Q_SCALE = 0.5
 
 
 def _topk_rows(rng, seq_lens, dql, hkv, k, rule, per_head, pad_rows=0):
@@ -275,6 +307,11 @@ def make_config(name: str, replicas: int = 0, poison: bool = True) -> DecodeCase
         return _make_c1(replicas, poison)
     if name == "c2_tp4_fp8":
         return _make_c2(replicas, poison)
+    if name == "c2_tp4_fp8q":
+        return _make_c2(replicas, poison, q_dtype=Q_FP8, q_scale=C2_FP8Q_SCALE,
+                        name=name)
+    if name == "c2_tp4_e5m2":
+        return _make_c2(replicas, poison, kv_dtype=KV_E5M2, name=name)
     if name == "c3_tp1_fp8":
         return _make_c3(replicas, poison)
     if name == "c4_spec_ragged":
@@ -306,26 +343,28 @@ def _make_c1(replicas: int, poison: bool) -> DecodeCase:
                       q, topk, max_blocks=int(bt.shape[1]), replicas=reps)
 
 
-def _make_c2(replicas: int, poison: bool) -> DecodeCase:
+def _make_c2(replicas: int, poison: bool, q_dtype: str = Q_BF16, q_scale: float = 1.0,
+             kv_dtype: str = KV_FP8, name: str = "c2_tp4_fp8") -> DecodeCase:
     rng = np.random.default_rng(2)
     B, dql, hq, hkv, k = 32, 4, 16, 1, 16
     seq = rng.integers(16384, 65536, size=B, endpoint=True).astype(np.int32)
     bt, total, spare = paged_layout(rng, seq, spare_pages=1)
-    kv = make_pool(rng, total, hkv, KV_FP8, 0.5)
+    kv = make_pool(rng, total, hkv, kv_dtype, 0.5)
     if poison:
-        fill_pages(kv, spare, KV_FP8)
-        poison_tail_slots(kv, bt, seq, KV_FP8)
+        fill_pages(kv, spare, kv_dtype)
+        poison_tail_slots(kv, bt, seq, kv_dtype)
 
     def one(rng_):
-        q = make_q(rng_, B * dql, hq)
+        q = make_q(rng_, B * dql, hq, q_dtype=q_dtype, q_scale=q_scale)
         topk = _topk_rows(rng_, seq, dql, hkv, k,
                           lambda r, last: pick_uniform(rng_, last, k), False)
         return q, topk
 
     q, topk = one(rng)
     reps = [one(rng) for _ in range(replicas)]
-    return DecodeCase("c2_tp4_fp8", 2, B, dql, B * dql, hq, hkv, k, KV_FP8, seq, bt,
-                      kv, q, topk, max_blocks=int(bt.shape[1]), replicas=reps)
+    return DecodeCase(name, 2, B, dql, B * dql, hq, hkv, k, kv_dtype, seq, bt,
+                      kv, q, topk, q_dtype=q_dtype, q_scale=q_scale,
+                      max_blocks=int(bt.shape[1]), replicas=reps)
 
 
 def _make_c3(replicas: int, poison: bool) -> DecodeCase:
@@ -412,7 +451,8 @@ def _make_c5(replicas: int, poison: bool) -> DecodeCase:
 
 def make_p3_case(num_q_heads: int, num_kv_heads: int, pairs: int, dql: int,
                  seq_pattern=(257, 513), seed: int = 0, kv_dtype: str = KV_FP8,
-                 std: float = 0.25, topk_k: int = 16, poison: bool = True) -> DecodeCase:
+                 std: float = 0.25, topk_k: int = 16, poison: bool = True,
+                 q_dtype: str = Q_BF16, q_scale: float = 1.0) -> DecodeCase:
     """The test page's parity shape: seq_lens = pattern * pairs, every visible
     page selected (``_make_topk``), K and V ~ N(0, std) encoded, Q ~ N(0,1)."""
     rng = np.random.default_rng(1000 + seed)
@@ -423,11 +463,12 @@ def make_p3_case(num_q_heads: int, num_kv_heads: int, pairs: int, dql: int,
         fill_pages(kv, spare, kv_dtype)
         poison_tail_slots(kv, bt, seq, kv_dtype)
     rows = len(seq) * dql
-    q = make_q(rng, rows, num_q_heads)
+    q = make_q(rng, rows, num_q_heads, q_dtype=q_dtype, q_scale=q_scale)
     topk = every_visible_topk(seq, num_kv_heads, dql, topk_k)
     return DecodeCase(f"p3_h{num_q_heads}_{num_kv_heads}_pairs{pairs}_dql{dql}", seed,
                       len(seq), dql, rows, num_q_heads, num_kv_heads, topk_k, kv_dtype,
-                      seq, bt, kv, q, topk, max_blocks=int(bt.shape[1]))
+                      seq, bt, kv, q, topk, q_dtype=q_dtype, q_scale=q_scale,
+                      max_blocks=int(bt.shape[1]))
 
 
 def make_random_case(seed: int, batch: int, dql: int, num_q_heads: int,
@@ -435,7 +476,8 @@ def make_random_case(seed: int, batch: int, dql: int, num_q_heads: int,
                      kv_dtype: str = KV_FP8, std: float = 0.5, pad_rows: int = 0,
                      per_head: bool = True, rule: str = "uniform",
                      neg_frac: float = 0.0, poison: bool = True,
-                     stride_extra: int = 0) -> DecodeCase:
+                     stride_extra: int = 0, q_dtype: str = Q_BF16,
+                     q_scale: float = 1.0) -> DecodeCase:
     """A generic seeded case: uniform seq lens, random distinct blocks that
     include each token's causal last block, optional extra -1 entries."""
     rng = np.random.default_rng(seed)
@@ -449,7 +491,7 @@ def make_random_case(seed: int, batch: int, dql: int, num_q_heads: int,
         fill_pages(kv, spare, kv_dtype)
         poison_tail_slots(kv, bt, seq, kv_dtype)
     rows = batch * dql
-    q = make_q(rng, rows + pad_rows, num_q_heads)
+    q = make_q(rng, rows + pad_rows, num_q_heads, q_dtype=q_dtype, q_scale=q_scale)
     pick = pick_uniform if rule == "uniform" else pick_zipf_recent
     topk = _topk_rows(rng, seq, dql, num_kv_heads, topk_k,
                       lambda r, last: pick(rng, last, topk_k), per_head,
@@ -459,7 +501,7 @@ def make_random_case(seed: int, batch: int, dql: int, num_q_heads: int,
         topk[mask] = -1
     return DecodeCase(f"rand_s{seed}", seed, batch, dql, rows + pad_rows, num_q_heads,
                       num_kv_heads, topk_k, kv_dtype, seq, bt, kv, q, topk,
-                      max_blocks=int(bt.shape[1]))
+                      q_dtype=q_dtype, q_scale=q_scale, max_blocks=int(bt.shape[1]))
 
 
 def make_scores(seed: int, num_kv_heads: int, max_blocks: int, rows: int, seq_lens,
