@@ -40,7 +40,7 @@ if ROOT not in sys.path:
 METRIC = "decode tokens/s and effective KV GB/s (% HBM peak), sparse GQA attend, 1 GPU"
 HBM_PEAK_GBS = 8000.0
 DEFAULT_CONFIG = "c2_tp4_fp8"
-OTHER_CONFIGS = ("c3_tp1_fp8", "c4_spec_ragged")
+OTHER_CONFIGS = ("c3_tp1_fp8", "c4_spec_ragged", "c2_tp4_fp8q", "c2_tp4_e5m2")
 FULL_STEP_CONFIG = "c5_full_step"
 # rocprofv3 counter summaries, each valid for the kernel sources it was taken on
 TRAFFIC_FILES = {"attend": os.path.join(ROOT, "profiles", "attend_traffic.json"),
@@ -64,6 +64,9 @@ CONFIG_TEXT = {
                       "8 requests at 131072 + 8 in [200,1900], 4 padding rows",
     "c5_full_step": "full decode step with indexer: B=64, dql=1, 64/4 heads, fp8, seq "
                     "log-normal in [8192,262144]; block-max scores -> top-16 -> attend",
+    "c2_tp4_fp8q": "c2 with an fp8 e4m3 query (q_scale 0.5) over the fp8 e4m3 cache: "
+                   "fp8 x fp8 MFMA for QK^T",
+    "c2_tp4_e5m2": "c2 with a bf16 query over an fp8 e5m2 cache",
 }
 
 
@@ -83,7 +86,7 @@ def step_bytes(case, q, topk):
     """Algorithmic bytes of one attend step (see module docstring)."""
     import numpy as np
 
-    e = 1 if case.kv_dtype == "fp8_e4m3" else 2
+    e = 2 if case.kv_dtype == "bf16" else 1
     row_bytes = 2 * 128 * e
     real = case.real_rows
     t = np.arange(real)
@@ -104,7 +107,7 @@ def step_bytes(case, q, topk):
     first[1:] = ks[1:] != ks[:-1]
     uniq_kv = int(nv[first].sum()) * row_bytes
     n_live = int(live.sum())
-    q_bytes = real * case.num_q_heads * 128 * 2
+    q_bytes = real * case.num_q_heads * 128 * (1 if case.q_dtype == "fp8_e4m3" else 2)
     out_bytes = case.num_token_rows * case.num_q_heads * 128 * 2
     idx_bytes = real * case.num_kv_heads * case.topk_k * 4
     meta = idx_bytes + n_live * 4 + case.batch * 4
@@ -121,6 +124,40 @@ def step_bytes(case, q, topk):
 # device setup
 # ---------------------------------------------------------------------------
 
+def _host_kv(case):
+    """The case's KV pool as a CPU tensor of the cache's dtype."""
+    import numpy as np
+    import torch
+
+    if case.kv_dtype == "fp8_e4m3":
+        return torch.from_numpy(case.kv)
+    if case.kv_dtype == "fp8_e5m2":
+        return torch.from_numpy(case.kv).view(torch.float8_e5m2)
+    return torch.from_numpy(case.kv.view(np.int16)).view(torch.bfloat16)
+
+
+def _host_q(case, qh):
+    import numpy as np
+    import torch
+
+    if case.q_dtype == "fp8_e4m3":
+        return torch.from_numpy(qh).view(torch.float8_e4m3fn)
+    return torch.from_numpy(qh.view(np.int16)).view(torch.bfloat16)
+
+
+def _kv_code(case):
+    import block_sparse_gqa_decode_amd as msa
+
+    return {"fp8_e4m3": msa.KV_FP8_E4M3, "fp8_e5m2": msa.KV_FP8_E5M2,
+            "bf16": msa.KV_BF16}[case.kv_dtype]
+
+
+def _q_code(case):
+    import block_sparse_gqa_decode_amd as msa
+
+    return msa.Q_FP8_E4M3 if case.q_dtype == "fp8_e4m3" else msa.Q_BF16
+
+
 class DeviceSet:
     """R replicas of one step's inputs, each over its own copy of the pool."""
 
@@ -131,9 +168,7 @@ class DeviceSet:
         import block_sparse_gqa_decode_amd as msa
 
         self.case = case
-        fp8 = case.kv_dtype == "fp8_e4m3"
-        host = torch.from_numpy(case.kv) if fp8 else \
-            torch.from_numpy(case.kv.view(np.int16)).view(torch.bfloat16)
+        host = _host_kv(case)
         nb = case.num_blocks
         self.kv = torch.empty((replicas * nb,) + tuple(host.shape[1:]), dtype=host.dtype,
                               device=dev)
@@ -149,16 +184,15 @@ class DeviceSet:
             qh, tk = sets[i]
             bt = torch.from_numpy((case.block_table.astype(np.int64) + i * nb).astype(
                 np.int32)).to(dev)
-            q = torch.from_numpy(qh.view(np.int16)).view(torch.bfloat16).to(dev)
+            q = _host_q(case, qh).to(dev)
             topk = torch.from_numpy(tk).to(dev)
-            out = torch.empty_like(q)
+            out = torch.empty(tuple(q.shape), dtype=torch.bfloat16, device=dev)
             self.steps.append((q, bt, topk, out))
             self.bytes.append(step_bytes(case, qh, tk))
         self.plan = msa.msa_sparse_decode_plan(
             case.batch, case.dql, num_q_heads=case.num_q_heads,
             num_kv_heads=case.num_kv_heads, page_table_stride=case.block_table.shape[1],
-            topk_blocks=case.topk_k,
-            kv_dtype=msa.KV_FP8_E4M3 if fp8 else msa.KV_BF16,
+            topk_blocks=case.topk_k, kv_dtype=_kv_code(case), q_dtype=_q_code(case),
             num_token_rows=case.num_token_rows, num_splits=splits, device=dev)
         self.msa = msa
 
@@ -167,14 +201,14 @@ class DeviceSet:
         c = self.case
         self.msa.msa_sparse_decode_run(self.plan, q, self.kv, bt, self.seq_lens, topk, out,
                                        sm_scale=c.sm_scale, k_scale=c.k_scale,
-                                       v_scale=c.v_scale)
+                                       v_scale=c.v_scale, q_scale=c.q_scale)
 
     def run_attend(self, i):
         q, bt, topk, out = self.steps[i]
         c = self.case
         self.msa.msa_sparse_decode_attend(self.plan, q, self.kv, bt, self.seq_lens, topk, out,
                                           sm_scale=c.sm_scale, k_scale=c.k_scale,
-                                          v_scale=c.v_scale)
+                                          v_scale=c.v_scale, q_scale=c.q_scale)
 
     def mean_bytes(self, key):
         return sum(b[key] for b in self.bytes) / len(self.bytes)
@@ -269,14 +303,14 @@ def scorer_bytes(case):
     selector, and the top-k write."""
     import numpy as np
 
-    e = 1 if case.kv_dtype == "fp8_e4m3" else 2
+    e = 2 if case.kv_dtype == "bf16" else 1
     kv_rows = 0
     for r in range(case.batch):
         pos_last = int(case.seq_lens[r]) - 1
         nb = pos_last // 128 + 1
         kv_rows += (nb - 1) * 128 + (pos_last - (nb - 1) * 128 + 1)
     k_bytes = kv_rows * case.num_kv_heads * 128 * e
-    q_bytes = case.real_rows * case.num_q_heads * 128 * 2
+    q_bytes = case.real_rows * case.num_q_heads * 128 * (1 if case.q_dtype == "fp8_e4m3" else 2)
     score_bytes = case.num_kv_heads * case.max_blocks * case.num_token_rows * 4
     topk_bytes = case.num_token_rows * case.num_kv_heads * case.topk_k * 4
     table_bytes = int(np.sum((case.seq_lens.astype(np.int64) + 127) // 128)) * 4 * \
@@ -298,7 +332,7 @@ class FullStepSet:
         import block_sparse_gqa_decode_amd as msa
 
         self.case, self.msa = case, msa
-        host = torch.from_numpy(case.kv)
+        host = _host_kv(case)
         nb = case.num_blocks
         self.kv = torch.empty((replicas * nb,) + tuple(host.shape[1:]), dtype=host.dtype,
                               device=dev)
@@ -312,32 +346,35 @@ class FullStepSet:
         for i in range(replicas):
             bt = torch.from_numpy((case.block_table.astype(np.int64) + i * nb).astype(
                 np.int32)).to(dev)
-            q = torch.from_numpy(qs[i].view(np.int16)).view(torch.bfloat16).to(dev)
+            q = _host_q(case, qs[i]).to(dev)
             # physical [Hkv, rows, blocks] so that the selector's row reads are
             # contiguous; passed as the logical [Hkv, blocks, rows] view
             score = torch.empty((case.num_kv_heads, rows, case.max_blocks), dtype=torch.float32,
                                 device=dev).transpose(1, 2)
             sel = torch.empty((rows, case.num_kv_heads, case.topk_k), dtype=torch.int32,
                               device=dev)
-            self.sets.append((q, bt, score, sel, torch.empty_like(q)))
+            self.sets.append((q, bt, score, sel, torch.empty(tuple(q.shape),
+                                                             dtype=torch.bfloat16, device=dev)))
         self.plan = msa.msa_sparse_decode_plan(
             case.batch, case.dql, num_q_heads=case.num_q_heads,
             num_kv_heads=case.num_kv_heads, page_table_stride=case.block_table.shape[1],
-            topk_blocks=case.topk_k, kv_dtype=msa.KV_FP8_E4M3, device=dev)
+            topk_blocks=case.topk_k, kv_dtype=_kv_code(case), q_dtype=_q_code(case),
+            device=dev)
 
     def run_score(self, i):
         q, bt, score, sel, _ = self.sets[i]
         c = self.case
         self.msa.msa_block_score_topk(q, self.kv, bt, self.seq_lens, decode_query_len=c.dql,
                                       num_kv_heads=c.num_kv_heads, max_blocks=c.max_blocks,
-                                      score=score, topk_out=sel, k_scale=c.k_scale)
+                                      score=score, topk_out=sel, k_scale=c.k_scale,
+                                      q_scale=c.q_scale, kv_dtype=_kv_code(case=c))
 
     def run_attend(self, i):
         q, bt, _, sel, out = self.sets[i]
         c = self.case
         self.msa.msa_sparse_decode_run(self.plan, q, self.kv, bt, self.seq_lens, sel, out,
                                        sm_scale=c.sm_scale, k_scale=c.k_scale,
-                                       v_scale=c.v_scale)
+                                       v_scale=c.v_scale, q_scale=c.q_scale)
 
     def run_select(self, i):
         _, _, score, sel, _ = self.sets[i]
@@ -451,7 +488,8 @@ def cpu_baseline(case, seconds: float):
             for t in order:
                 om.sparse_decode(case.q, case.kv, case.kv_dtype, case.k_scale,
                                  case.v_scale, case.block_table, case.seq_lens, case.topk,
-                                 case.dql, case.num_kv_heads, case.sm_scale, rows=[int(t)])
+                                 case.dql, case.num_kv_heads, case.sm_scale, rows=[int(t)],
+                                 q_dtype=case.q_dtype, q_scale=case.q_scale)
                 rows_done += 1
                 if time.perf_counter() - t0 >= seconds:
                     done = True
@@ -607,8 +645,7 @@ def main():
         "unit": "GB/s",
         "frac": round(achieved / HBM_PEAK_GBS, 4),
         "traffic": None if traffic is None else traffic.get("hbm_bytes_per_launch"),
-        "kernel": "attend_kernel<fp8>" if case.kv_dtype == "fp8_e4m3" else
-                  "attend_kernel<bf16>",
+        "kernel": f"attend_kernel<kv {case.kv_dtype}, q {case.q_dtype}>",
         "algorithmic_bytes_per_launch": int(res["algorithmic_bytes"]),
         "avg_launch_us": round(kernel_s * 1e6, 3),
         "timing": "HIP events around graph replays of the attend launches alone, on "

@@ -14,13 +14,16 @@ Entry points carry the C names:
 * ``msa_sparse_decode_run``   -- one sparse decode step (the attend).
 * ``msa_block_score_topk``    -- indexer block-max scores, then the top-k.
 * ``msa_topk_select``         -- the top-k selector alone.
-* ``msa_fp8_e4m3_to_bf16``    -- the in-register fp8 conversion, as a check.
+* ``msa_fp8_e4m3_to_bf16`` / ``msa_fp8_e5m2_to_bf16`` -- the in-register fp8
+  conversions, as a check.
 
 Tensor checks follow ``MSACutlassDecodePlanCache.prepare`` (contiguous int32
 block table with one row per request, contiguous int32 sequence lengths on the
 same device) and the backend contract of the vLLM API page
 ``vllm.models.minimax_m3.common.sparse_attention`` (head size 128, page size
-128, bf16 or fp8 e4m3 KV in a packed ``(num_blocks, Hkv, 128, 256)`` cache).
+128, bf16, fp8 e4m3 or fp8 e5m2 KV in a packed ``(num_blocks, Hkv, 128, 256)``
+cache).  q is bf16, or fp8 e4m3 codes with a per-tensor ``q_scale`` (the
+``query_fp8`` / ``q_scale_float`` arguments of ``msa_cutlass_sparse_decode``).
 """
 from __future__ import annotations
 
@@ -34,14 +37,19 @@ __all__ = [
     "MsaError", "MsaInvalidArgument", "MsaUnsupported", "DecodePlan", "PlanCache",
     "msa_sparse_decode_plan", "msa_sparse_decode_run", "msa_sparse_decode_attend",
     "msa_sparse_decode_merge", "msa_block_score_topk",
-    "msa_topk_select", "msa_fp8_e4m3_to_bf16", "library_path", "load_library",
-    "KV_BF16", "KV_FP8_E4M3", "PAGE_SIZE", "HEAD_DIM",
+    "msa_topk_select", "msa_fp8_e4m3_to_bf16", "msa_fp8_e5m2_to_bf16", "library_path",
+    "load_library", "KV_BF16", "KV_FP8_E4M3", "KV_FP8_E5M2", "Q_BF16", "Q_FP8_E4M3",
+    "PAGE_SIZE", "HEAD_DIM", "ABI_VERSION",
 ]
 
+ABI_VERSION = 2
 PAGE_SIZE = 128
 HEAD_DIM = 128
 KV_BF16 = 0
 KV_FP8_E4M3 = 1
+KV_FP8_E5M2 = 2
+Q_BF16 = 0
+Q_FP8_E4M3 = 1
 
 MSA_OK = 0
 MSA_ERR_INVALID_ARG = -1
@@ -71,7 +79,7 @@ class _Shape(ctypes.Structure):
     _fields_ = [(name, ctypes.c_int32) for name in (
         "batch", "decode_query_len", "num_token_rows", "page_table_stride",
         "num_q_heads", "num_kv_heads", "page_size", "head_dim", "topk_blocks",
-        "kv_dtype", "num_splits")]
+        "kv_dtype", "num_splits", "q_dtype")]
 
 
 _I64x4 = ctypes.c_int64 * 4
@@ -102,15 +110,16 @@ def load_library():
         "msa_sparse_decode_plan_destroy": (i32, [vp]),
         "msa_sparse_decode_plan_info": (i32, [vp, ctypes.POINTER(i32), ctypes.POINTER(i64),
                                               ctypes.POINTER(_Shape)]),
-        "msa_sparse_decode_run": (i32, [vp, vp, vp, pi64, i64, f32, f32, vp, vp, vp,
+        "msa_sparse_decode_run": (i32, [vp, vp, vp, pi64, i64, f32, f32, f32, vp, vp, vp,
                                         pi64, vp, f32, vp]),
-        "msa_sparse_decode_attend": (i32, [vp, vp, vp, pi64, i64, f32, f32, vp, vp, vp,
-                                           pi64, vp, f32, vp]),
+        "msa_sparse_decode_attend": (i32, [vp, vp, vp, pi64, i64, f32, f32, f32, vp, vp,
+                                           vp, pi64, vp, f32, vp]),
         "msa_sparse_decode_merge": (i32, [vp, vp, f32, vp]),
-        "msa_block_score_topk": (i32, [ctypes.POINTER(_Shape), vp, vp, pi64, i64, f32,
+        "msa_block_score_topk": (i32, [ctypes.POINTER(_Shape), vp, vp, pi64, i64, f32, f32,
                                        vp, vp, i32, vp, pi64, vp, i32, vp]),
         "msa_topk_select": (i32, [vp, pi64, i32, i32, i32, vp, i32, vp]),
         "msa_fp8_e4m3_to_bf16": (i32, [vp, vp, i64, vp]),
+        "msa_fp8_e5m2_to_bf16": (i32, [vp, vp, i64, vp]),
         "msa_last_error": (ctypes.c_char_p, []),
         "msa_abi_version": (i32, []),
     }
@@ -118,6 +127,9 @@ def load_library():
         fn = getattr(lib, name)
         fn.restype = res
         fn.argtypes = args
+    if lib.msa_abi_version() != ABI_VERSION:
+        raise RuntimeError(f"{path} has ABI version {lib.msa_abi_version()}, the binding "
+                           f"expects {ABI_VERSION}: rebuild the library")
     _LIB = lib
     return lib
 
@@ -141,13 +153,27 @@ def _stream_handle(stream, device) -> Optional[int]:
     return stream.cuda_stream
 
 
-def _kv_dtype_of(kv: torch.Tensor) -> int:
-    if kv.dtype in (torch.uint8, torch.float8_e4m3fn):
-        return KV_FP8_E4M3
-    if kv.dtype == torch.bfloat16:
-        return KV_BF16
-    raise ValueError(f"unsupported kv cache dtype {kv.dtype}: expected uint8/float8_e4m3fn "
-                     "(fp8 e4m3) or bfloat16")
+def _kv_dtype_of(kv: torch.Tensor, declared: Optional[int] = None) -> int:
+    """The KV format of a cache tensor.  ``uint8`` holds either fp8 format and
+    takes ``declared`` (default e4m3); typed fp8 tensors must agree with it."""
+    if kv.dtype == torch.uint8:
+        return KV_FP8_E4M3 if declared is None else declared
+    found = {torch.float8_e4m3fn: KV_FP8_E4M3, torch.float8_e5m2: KV_FP8_E5M2,
+             torch.bfloat16: KV_BF16}.get(kv.dtype)
+    if found is None:
+        raise ValueError(f"unsupported kv cache dtype {kv.dtype}: expected bfloat16, "
+                         "float8_e4m3fn, float8_e5m2 or uint8")
+    if declared is not None and found != declared:
+        raise ValueError("kv_cache dtype does not match the declared kv_dtype")
+    return found
+
+
+def _q_dtype_of(q: torch.Tensor) -> int:
+    if q.dtype == torch.bfloat16:
+        return Q_BF16
+    if q.dtype in (torch.float8_e4m3fn, torch.uint8):
+        return Q_FP8_E4M3
+    raise ValueError(f"unsupported q dtype {q.dtype}: expected bfloat16 or float8_e4m3fn")
 
 
 def _check_kv(kv: torch.Tensor, num_kv_heads: int):
@@ -173,9 +199,12 @@ def _check_tables(block_table: torch.Tensor, seq_lens: torch.Tensor, batch: int)
                          "lengths on the block table device")
 
 
-def _check_q(q: torch.Tensor, name: str, rows: int, hq: int):
-    if q.device.type != "cuda" or q.dtype != torch.bfloat16 or not q.is_contiguous():
-        raise ValueError(f"{name} must be a contiguous device bfloat16 tensor")
+def _check_q(q: torch.Tensor, name: str, rows: int, hq: int, q_dtype: int = Q_BF16):
+    ok_dtype = q.dtype == torch.bfloat16 if q_dtype == Q_BF16 else \
+        q.dtype in (torch.float8_e4m3fn, torch.uint8)
+    if q.device.type != "cuda" or not ok_dtype or not q.is_contiguous():
+        kind = "bfloat16" if q_dtype == Q_BF16 else "float8_e4m3fn (or uint8 codes)"
+        raise ValueError(f"{name} must be a contiguous device {kind} tensor")
     if tuple(q.shape) != (rows, hq, HEAD_DIM):
         raise ValueError(f"{name} must have shape ({rows}, {hq}, {HEAD_DIM}), "
                          f"got {tuple(q.shape)}")
@@ -200,6 +229,7 @@ class DecodePlan:
         self.num_kv_heads = shape.num_kv_heads
         self.topk_blocks = shape.topk_blocks
         self.kv_dtype = shape.kv_dtype
+        self.q_dtype = shape.q_dtype
         self.num_splits = splits.value
         self.arena_bytes = arena.value
 
@@ -223,10 +253,11 @@ def msa_sparse_decode_plan(batch: int, decode_query_len: int, *, num_q_heads: in
                            num_kv_heads: int, page_table_stride: int, topk_blocks: int,
                            kv_dtype: int, num_token_rows: int = 0, num_splits: int = 0,
                            page_size: int = PAGE_SIZE, head_dim: int = HEAD_DIM,
-                           device=None) -> DecodePlan:
+                           q_dtype: int = Q_BF16, device=None) -> DecodePlan:
     lib = load_library()
     shape = _Shape(batch, decode_query_len, num_token_rows, page_table_stride, num_q_heads,
-                   num_kv_heads, page_size, head_dim, topk_blocks, kv_dtype, num_splits)
+                   num_kv_heads, page_size, head_dim, topk_blocks, kv_dtype, num_splits,
+                   q_dtype)
     if device is None:
         dev = torch.cuda.current_device() if torch.cuda.is_available() else 0
     elif isinstance(device, int):
@@ -242,11 +273,10 @@ def msa_sparse_decode_plan(batch: int, decode_query_len: int, *, num_q_heads: in
 
 def _run_args(plan, q, kv_cache, block_table, seq_lens, topk, out):
     rows = plan.num_token_rows
-    _check_q(q, "q", rows, plan.num_q_heads)
+    _check_q(q, "q", rows, plan.num_q_heads, plan.q_dtype)
     _check_q(out, "out", rows, plan.num_q_heads)
     _check_kv(kv_cache, plan.num_kv_heads)
-    if _kv_dtype_of(kv_cache) != plan.kv_dtype:
-        raise ValueError("kv_cache dtype does not match the plan's kv_dtype")
+    _kv_dtype_of(kv_cache, plan.kv_dtype)
     _check_tables(block_table, seq_lens, plan.batch)
     if block_table.stride(0) != plan.page_table_stride:
         raise ValueError("block_table row stride does not match the plan")
@@ -265,11 +295,12 @@ def _run_args(plan, q, kv_cache, block_table, seq_lens, topk, out):
 def msa_sparse_decode_run(plan: DecodePlan, q: torch.Tensor, kv_cache: torch.Tensor,
                           block_table: torch.Tensor, seq_lens: torch.Tensor,
                           topk: torch.Tensor, out: torch.Tensor, *, sm_scale: float,
-                          k_scale: float = 1.0, v_scale: float = 1.0, stream=None) -> None:
+                          k_scale: float = 1.0, v_scale: float = 1.0, q_scale: float = 1.0,
+                          stream=None) -> None:
     """out[t, j] = sparse causal attention of q[t, j] over the selected pages."""
     head = _run_args(plan, q, kv_cache, block_table, seq_lens, topk, out)
     _check(load_library().msa_sparse_decode_run(
-        *head, float(k_scale), float(v_scale), block_table.data_ptr(), seq_lens.data_ptr(),
+        *head, float(q_scale), float(k_scale), float(v_scale), block_table.data_ptr(), seq_lens.data_ptr(),
         topk.data_ptr(), _I64x3(*topk.stride()), out.data_ptr(), float(sm_scale),
         _stream_handle(stream, q.device)))
 
@@ -277,11 +308,12 @@ def msa_sparse_decode_run(plan: DecodePlan, q: torch.Tensor, kv_cache: torch.Ten
 def msa_sparse_decode_attend(plan: DecodePlan, q: torch.Tensor, kv_cache: torch.Tensor,
                              block_table: torch.Tensor, seq_lens: torch.Tensor,
                              topk: torch.Tensor, out: torch.Tensor, *, sm_scale: float,
-                             k_scale: float = 1.0, v_scale: float = 1.0, stream=None) -> None:
+                             k_scale: float = 1.0, v_scale: float = 1.0,
+                             q_scale: float = 1.0, stream=None) -> None:
     """First launch of a step (see ``msa_sparse_decode_run``)."""
     head = _run_args(plan, q, kv_cache, block_table, seq_lens, topk, out)
     _check(load_library().msa_sparse_decode_attend(
-        *head, float(k_scale), float(v_scale), block_table.data_ptr(), seq_lens.data_ptr(),
+        *head, float(q_scale), float(k_scale), float(v_scale), block_table.data_ptr(), seq_lens.data_ptr(),
         topk.data_ptr(), _I64x3(*topk.stride()), out.data_ptr(), float(sm_scale),
         _stream_handle(stream, q.device)))
 
@@ -297,11 +329,15 @@ def msa_sparse_decode_merge(plan: DecodePlan, out: torch.Tensor, *, v_scale: flo
 def msa_block_score_topk(q: torch.Tensor, kv_cache: torch.Tensor, block_table: torch.Tensor,
                          seq_lens: torch.Tensor, *, decode_query_len: int, num_kv_heads: int,
                          max_blocks: int, score: torch.Tensor, topk_out: torch.Tensor,
-                         k_scale: float = 1.0, num_token_rows: int = 0, stream=None) -> None:
-    """score[h, b, t] (logical; any strides) and topk_out[t, h, :] for every row."""
+                         k_scale: float = 1.0, q_scale: float = 1.0, num_token_rows: int = 0,
+                         kv_dtype: Optional[int] = None, stream=None) -> None:
+    """score[h, b, t] (logical; any strides) and topk_out[t, h, :] for every row.
+    The q format follows q's dtype; a uint8 cache is e4m3 unless ``kv_dtype``
+    says otherwise."""
     batch = int(seq_lens.shape[0])
     rows = num_token_rows or batch * decode_query_len
-    _check_q(q, "q", rows, q.shape[1] if q.dim() == 3 else -1)
+    q_dtype = _q_dtype_of(q)
+    _check_q(q, "q", rows, q.shape[1] if q.dim() == 3 else -1, q_dtype)
     _check_kv(kv_cache, num_kv_heads)
     _check_tables(block_table, seq_lens, batch)
     if score.dtype != torch.float32 or score.dim() != 3 or \
@@ -312,10 +348,10 @@ def msa_block_score_topk(q: torch.Tensor, kv_cache: torch.Tensor, block_table: t
         raise ValueError(f"topk_out must be contiguous int32 [{rows}, {num_kv_heads}, k]")
     shape = _Shape(batch, decode_query_len, rows, block_table.stride(0), q.shape[1],
                    num_kv_heads, PAGE_SIZE, HEAD_DIM, topk_out.shape[2],
-                   _kv_dtype_of(kv_cache), 0)
+                   _kv_dtype_of(kv_cache, kv_dtype), 0, q_dtype)
     _check(load_library().msa_block_score_topk(
         ctypes.byref(shape), q.data_ptr(), kv_cache.data_ptr(), _I64x4(*kv_cache.stride()),
-        kv_cache.shape[0], float(k_scale), block_table.data_ptr(), seq_lens.data_ptr(),
+        kv_cache.shape[0], float(q_scale), float(k_scale), block_table.data_ptr(), seq_lens.data_ptr(),
         int(max_blocks), score.data_ptr(), _I64x3(*score.stride()), topk_out.data_ptr(),
         int(topk_out.shape[2]), _stream_handle(stream, q.device)))
 
@@ -333,19 +369,28 @@ def msa_topk_select(score: torch.Tensor, topk_out: torch.Tensor, stream=None) ->
         int(topk_out.shape[2]), _stream_handle(stream, score.device)))
 
 
-def msa_fp8_e4m3_to_bf16(inp: torch.Tensor, out: torch.Tensor, stream=None) -> None:
-    if inp.dtype not in (torch.uint8, torch.float8_e4m3fn) or not inp.is_contiguous():
-        raise ValueError("inp must be contiguous uint8 / float8_e4m3fn")
+def _fp8_to_bf16(fn_name, typed, inp: torch.Tensor, out: torch.Tensor, stream) -> None:
+    if inp.dtype not in (torch.uint8, typed) or not inp.is_contiguous():
+        raise ValueError(f"inp must be contiguous uint8 / {typed}")
     if out.dtype != torch.bfloat16 or not out.is_contiguous() or out.numel() != inp.numel():
         raise ValueError("out must be contiguous bfloat16 with inp's element count")
-    _check(load_library().msa_fp8_e4m3_to_bf16(inp.data_ptr(), out.data_ptr(), inp.numel(),
-                                               _stream_handle(stream, inp.device)))
+    _check(getattr(load_library(), fn_name)(inp.data_ptr(), out.data_ptr(), inp.numel(),
+                                            _stream_handle(stream, inp.device)))
+
+
+def msa_fp8_e4m3_to_bf16(inp: torch.Tensor, out: torch.Tensor, stream=None) -> None:
+    _fp8_to_bf16("msa_fp8_e4m3_to_bf16", torch.float8_e4m3fn, inp, out, stream)
+
+
+def msa_fp8_e5m2_to_bf16(inp: torch.Tensor, out: torch.Tensor, stream=None) -> None:
+    _fp8_to_bf16("msa_fp8_e5m2_to_bf16", torch.float8_e5m2, inp, out, stream)
 
 
 class PlanCache:
     """Plans keyed by (batch, decode_query_len, page_table_stride, num_q_heads,
-    num_kv_heads, page_size, topk_blocks) plus kv dtype, padding rows and split
-    count -- the key of ``MSACutlassDecodePlanCache.prepare``."""
+    num_kv_heads, page_size, topk_blocks) -- the key of
+    ``MSACutlassDecodePlanCache.prepare`` -- plus kv and q dtypes, padding rows
+    and split count."""
 
     def __init__(self):
         self.plans = {}
@@ -353,18 +398,19 @@ class PlanCache:
     def prepare(self, block_table: torch.Tensor, seq_lens: torch.Tensor,
                 decode_query_len: int, *, num_q_heads: int, num_kv_heads: int,
                 topk_blocks: int, kv_dtype: int, page_size: int = PAGE_SIZE,
-                num_token_rows: int = 0, num_splits: int = 0) -> DecodePlan:
+                num_token_rows: int = 0, num_splits: int = 0,
+                q_dtype: int = Q_BF16) -> DecodePlan:
         batch = int(seq_lens.shape[0])
         _check_tables(block_table, seq_lens, batch)
         stride = int(block_table.stride(0))
         key = (batch, decode_query_len, stride, num_q_heads, num_kv_heads, page_size,
-               topk_blocks, kv_dtype, num_token_rows, num_splits)
+               topk_blocks, kv_dtype, num_token_rows, num_splits, q_dtype)
         plan = self.plans.get(key)
         if plan is None:
             plan = msa_sparse_decode_plan(
                 batch, decode_query_len, num_q_heads=num_q_heads, num_kv_heads=num_kv_heads,
                 page_table_stride=stride, topk_blocks=topk_blocks, kv_dtype=kv_dtype,
                 num_token_rows=num_token_rows, num_splits=num_splits, page_size=page_size,
-                device=block_table.device)
+                q_dtype=q_dtype, device=block_table.device)
             self.plans[key] = plan
         return plan

@@ -56,6 +56,16 @@ int64_t elem_bytes(int32_t kv_dtype) { return kv_dtype == MSA_KV_BF16 ? 2 : 1; }
 
 bool aligned16(const void* ptr) { return (reinterpret_cast<uintptr_t>(ptr) & 15u) == 0; }
 
+// Scale arguments: finite, and q/k scales positive (the kernels take maxima
+// of raw dot products before applying them).
+msa_status check_scales(float q_scale, float k_scale) {
+  if (!std::isfinite(q_scale) || !std::isfinite(k_scale))
+    return fail(MSA_ERR_INVALID_ARG, "scales must be finite");
+  if (!(q_scale > 0.f) || !(k_scale > 0.f))
+    return fail(MSA_ERR_INVALID_ARG, "q_scale and k_scale must be positive");
+  return MSA_OK;
+}
+
 // Checks shared by the plan and the indexer entry point.
 msa_status check_common_shape(const msa_decode_shape* s) {
   if (s == nullptr) return fail(MSA_ERR_INVALID_ARG, "shape is NULL");
@@ -91,8 +101,13 @@ msa_status check_common_shape(const msa_decode_shape* s) {
     return fail(MSA_ERR_UNSUPPORTED, "page_size must be 128 (got %d)", s->page_size);
   if (s->head_dim != msa::kHeadDim)
     return fail(MSA_ERR_UNSUPPORTED, "head_dim must be 128 (got %d)", s->head_dim);
-  if (s->kv_dtype != MSA_KV_BF16 && s->kv_dtype != MSA_KV_FP8_E4M3)
+  if (s->kv_dtype != MSA_KV_BF16 && s->kv_dtype != MSA_KV_FP8_E4M3 &&
+      s->kv_dtype != MSA_KV_FP8_E5M2)
     return fail(MSA_ERR_INVALID_ARG, "unknown kv_dtype %d", s->kv_dtype);
+  if (s->q_dtype != MSA_Q_BF16 && s->q_dtype != MSA_Q_FP8_E4M3)
+    return fail(MSA_ERR_INVALID_ARG, "unknown q_dtype %d", s->q_dtype);
+  if (s->q_dtype == MSA_Q_FP8_E4M3 && s->kv_dtype == MSA_KV_BF16)
+    return fail(MSA_ERR_UNSUPPORTED, "an fp8 q needs an fp8 (e4m3 or e5m2) KV cache");
   return MSA_OK;
 }
 
@@ -248,8 +263,8 @@ msa_status msa_sparse_decode_plan_info(msa_plan plan, int32_t* num_splits, int64
 }
 
 static msa_status run_phases(msa_plan plan, const void* q, const void* kv_cache,
-                             const int64_t kv_strides[4], int64_t num_kv_blocks, float k_scale,
-                             float v_scale, const int32_t* block_table,
+                             const int64_t kv_strides[4], int64_t num_kv_blocks, float q_scale,
+                             float k_scale, float v_scale, const int32_t* block_table,
                              const int32_t* seq_lens, const int32_t* topk,
                              const int64_t topk_strides[3], void* out, float sm_scale,
                              void* stream, bool merge) {
@@ -265,14 +280,15 @@ static msa_status run_phases(msa_plan plan, const void* q, const void* kv_cache,
     if (topk_strides[d] < 0) return fail(MSA_ERR_INVALID_ARG, "topk strides must be >= 0");
   msa_status st = check_kv(kv_cache, kv_strides, num_kv_blocks, s.kv_dtype);
   if (st != MSA_OK) return st;
-  if (!std::isfinite(k_scale) || !std::isfinite(v_scale) || !std::isfinite(sm_scale))
+  st = check_scales(q_scale, k_scale);
+  if (st != MSA_OK) return st;
+  if (!std::isfinite(v_scale) || !std::isfinite(sm_scale))
     return fail(MSA_ERR_INVALID_ARG, "scales must be finite");
-  if (!(sm_scale > 0.f) || !(k_scale > 0.f))
-    return fail(MSA_ERR_INVALID_ARG, "sm_scale and k_scale must be positive");
+  if (!(sm_scale > 0.f)) return fail(MSA_ERR_INVALID_ARG, "sm_scale must be positive");
 
   const int64_t eb = elem_bytes(s.kv_dtype);
   msa::AttendParams p{};
-  p.q = static_cast<const uint16_t*>(q);
+  p.q = static_cast<const uint8_t*>(q);
   p.kv = static_cast<const uint8_t*>(kv_cache);
   p.kv_s0 = kv_strides[0] * eb;
   p.kv_s1 = kv_strides[1] * eb;
@@ -288,7 +304,8 @@ static msa_status run_phases(msa_plan plan, const void* q, const void* kv_cache,
   p.out = static_cast<uint16_t*>(out);
   p.part_o = plan->part_o;
   p.part_ml = plan->part_ml;
-  p.scale_log2 = (float)((double)sm_scale * (double)k_scale * 1.4426950408889634);
+  p.scale_log2 =
+      (float)((double)sm_scale * (double)q_scale * (double)k_scale * 1.4426950408889634);
   p.v_scale = v_scale;
   p.dql = s.decode_query_len;
   p.real_rows = plan->real_rows;
@@ -304,7 +321,7 @@ static msa_status run_phases(msa_plan plan, const void* q, const void* kv_cache,
   hipError_t e = guard.enter(plan->device);
   if (e != hipSuccess) return device_fail(e, "hipSetDevice");
   hipStream_t st_ = static_cast<hipStream_t>(stream);
-  e = msa::launch_attend(p, s.kv_dtype == MSA_KV_FP8_E4M3, st_);
+  e = msa::launch_attend(p, s.kv_dtype, s.q_dtype, st_);
   if (e != hipSuccess) return device_fail(e, "attend launch");
   if (merge && plan->splits > 1) {
     e = msa::launch_merge(p, st_);
@@ -315,21 +332,21 @@ static msa_status run_phases(msa_plan plan, const void* q, const void* kv_cache,
 
 msa_status msa_sparse_decode_run(msa_plan plan, const void* q, const void* kv_cache,
                                  const int64_t kv_strides[4], int64_t num_kv_blocks,
-                                 float k_scale, float v_scale, const int32_t* block_table,
-                                 const int32_t* seq_lens, const int32_t* topk,
-                                 const int64_t topk_strides[3], void* out, float sm_scale,
-                                 void* stream) {
-  return run_phases(plan, q, kv_cache, kv_strides, num_kv_blocks, k_scale, v_scale,
+                                 float q_scale, float k_scale, float v_scale,
+                                 const int32_t* block_table, const int32_t* seq_lens,
+                                 const int32_t* topk, const int64_t topk_strides[3], void* out,
+                                 float sm_scale, void* stream) {
+  return run_phases(plan, q, kv_cache, kv_strides, num_kv_blocks, q_scale, k_scale, v_scale,
                     block_table, seq_lens, topk, topk_strides, out, sm_scale, stream, true);
 }
 
 msa_status msa_sparse_decode_attend(msa_plan plan, const void* q, const void* kv_cache,
                                     const int64_t kv_strides[4], int64_t num_kv_blocks,
-                                    float k_scale, float v_scale, const int32_t* block_table,
-                                    const int32_t* seq_lens, const int32_t* topk,
-                                    const int64_t topk_strides[3], void* out, float sm_scale,
-                                    void* stream) {
-  return run_phases(plan, q, kv_cache, kv_strides, num_kv_blocks, k_scale, v_scale,
+                                    float q_scale, float k_scale, float v_scale,
+                                    const int32_t* block_table, const int32_t* seq_lens,
+                                    const int32_t* topk, const int64_t topk_strides[3],
+                                    void* out, float sm_scale, void* stream) {
+  return run_phases(plan, q, kv_cache, kv_strides, num_kv_blocks, q_scale, k_scale, v_scale,
                     block_table, seq_lens, topk, topk_strides, out, sm_scale, stream, false);
 }
 
@@ -396,7 +413,7 @@ msa_status msa_topk_select(const float* score, const int64_t score_strides[3],
 
 msa_status msa_block_score_topk(const msa_decode_shape* shape, const void* q,
                                 const void* kv_cache, const int64_t kv_strides[4],
-                                int64_t num_kv_blocks, float k_scale,
+                                int64_t num_kv_blocks, float q_scale, float k_scale,
                                 const int32_t* block_table, const int32_t* seq_lens,
                                 int32_t max_blocks, float* score,
                                 const int64_t score_strides[3], int32_t* topk_out,
@@ -418,7 +435,8 @@ msa_status msa_block_score_topk(const msa_decode_shape* shape, const void* q,
                 msa::kMaxScoreBlocks, max_blocks);
   if (topk_k < 1 || topk_k > msa::kMaxTopk)
     return fail(MSA_ERR_INVALID_ARG, "topk_k must be in 1..%d (got %d)", msa::kMaxTopk, topk_k);
-  if (!std::isfinite(k_scale)) return fail(MSA_ERR_INVALID_ARG, "k_scale must be finite");
+  st = check_scales(q_scale, k_scale);
+  if (st != MSA_OK) return st;
   if (shape->batch > msa::kMaxScoreBatch)
     return fail(MSA_ERR_UNSUPPORTED, "the scorer supports batch <= %d (got %d)",
                 msa::kMaxScoreBatch, shape->batch);
@@ -427,7 +445,7 @@ msa_status msa_block_score_topk(const msa_decode_shape* shape, const void* q,
   const int32_t num_rows = shape->num_token_rows ? shape->num_token_rows : real_rows;
   const int64_t eb = elem_bytes(shape->kv_dtype);
   msa::ScoreParams p{};
-  p.q = static_cast<const uint16_t*>(q);
+  p.q = static_cast<const uint8_t*>(q);
   p.kv = static_cast<const uint8_t*>(kv_cache);
   p.kv_s0 = kv_strides[0] * eb;
   p.kv_s1 = kv_strides[1] * eb;
@@ -440,7 +458,7 @@ msa_status msa_block_score_topk(const msa_decode_shape* shape, const void* q,
   p.sc_s0 = score_strides[0];
   p.sc_s1 = score_strides[1];
   p.sc_s2 = score_strides[2];
-  p.k_scale = k_scale;
+  p.qk_scale = (float)((double)q_scale * (double)k_scale);
   p.batch = shape->batch;
   p.dql = shape->decode_query_len;
   p.real_rows = real_rows;
@@ -450,20 +468,28 @@ msa_status msa_block_score_topk(const msa_decode_shape* shape, const void* q,
   p.group = shape->num_q_heads / shape->num_kv_heads;
   p.max_blocks = max_blocks;
   hipStream_t hs = static_cast<hipStream_t>(stream);
-  hipError_t e = msa::launch_score(p, shape->kv_dtype == MSA_KV_FP8_E4M3, hs);
+  hipError_t e = msa::launch_score(p, shape->kv_dtype, shape->q_dtype, hs);
   if (e != hipSuccess) return device_fail(e, "score launch");
   return msa_topk_select(score, score_strides, shape->num_kv_heads, max_blocks, num_rows,
                          topk_out, topk_k, stream);
 }
 
-msa_status msa_fp8_e4m3_to_bf16(const void* in, void* out, int64_t n, void* stream) {
+static msa_status fp8_to_bf16(const void* in, void* out, int64_t n, int fmt, void* stream) {
   if (in == nullptr || out == nullptr) return fail(MSA_ERR_INVALID_ARG, "in and out must be non-NULL");
   if (n < 1 || n > ((int64_t)1 << 40)) return fail(MSA_ERR_INVALID_ARG, "n out of range");
   hipError_t e = msa::launch_fp8_to_bf16(static_cast<const uint8_t*>(in),
-                                         static_cast<uint16_t*>(out), n,
+                                         static_cast<uint16_t*>(out), n, fmt,
                                          static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return device_fail(e, "fp8 conversion launch");
   return ok();
+}
+
+msa_status msa_fp8_e4m3_to_bf16(const void* in, void* out, int64_t n, void* stream) {
+  return fp8_to_bf16(in, out, n, msa::kKvE4m3, stream);
+}
+
+msa_status msa_fp8_e5m2_to_bf16(const void* in, void* out, int64_t n, void* stream) {
+  return fp8_to_bf16(in, out, n, msa::kKvE5m2, stream);
 }
 
 }  // extern "C"

@@ -44,6 +44,17 @@
 // over half the q heads each measured no faster: with one workgroup per CU
 // the step is bound by HBM latency and bandwidth, not by issue.)
 //
+// Formats: K|V entries are bf16, OCP fp8 e4m3fn or OCP fp8 e5m2; q is bf16 or
+// fp8 e4m3fn with a per-tensor q scale (vLLM API page
+// "vllm.models.minimax_m3.nvidia.msa_cutlass_sparse_decode":
+// msa_cutlass_sparse_decode(query_fp8, ..., q_scale_float, ...)).  With a bf16
+// q the 8-bit K is widened to bf16 in registers and S^T uses the bf16 MFMA
+// above.  With an fp8 q, S^T of a 16-key tile is one 16x16x128 fp8 MFMA on the
+// K bytes as loaded: both operands take head dims 16g..16g+15 then
+// 64+16g..64+16g+15 in lane group g, the same runs the K loads already fetch.
+// The q, k and softmax scales fold into one log2-domain factor.  P V stays a
+// bf16 MFMA (V widened to bf16).
+//
 // NaN safety: rows past a page's visible count are never loaded (row index
 // clamped to the last visible row) and their scores are set to -inf, so stale
 // cache bytes cannot reach the MFMAs.
@@ -130,30 +141,42 @@ __device__ __forceinline__ void load_page(PageRegs<kFp8>& r, const uint8_t* page
   }
 }
 
-template <bool kFp8>
-__device__ __forceinline__ void attend_page(const PageRegs<kFp8>& r,
-                                            const bf16x8_t (&qf)[4], int kbase,
+// S^T tile tau (16 keys x 16 q rows) of one page.
+template <int kKv, int kQ>
+__device__ __forceinline__ f32x4_t score_tile(const PageRegs<kKv != kKvBf16>& r,
+                                              const QRegs<kQ>& q, int tau) {
+  const f32x4_t zero = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  if constexpr (kQ == kQE4m3) {
+    return mfma_f8_16x16x128<kKv == kKvE5m2 ? 1 : 0, 0>(cat_i32x8(r.k[tau][0], r.k[tau][1]),
+                                                         q.b, zero);
+  } else {
+    bf16x8_t kf[4];
+    if constexpr (kKv != kKvBf16) {
+      kf[0] = as_bf16x8(f8x8_to_bf16x8<kKv>(r.k[tau][0].x, r.k[tau][0].y));
+      kf[1] = as_bf16x8(f8x8_to_bf16x8<kKv>(r.k[tau][0].z, r.k[tau][0].w));
+      kf[2] = as_bf16x8(f8x8_to_bf16x8<kKv>(r.k[tau][1].x, r.k[tau][1].y));
+      kf[3] = as_bf16x8(f8x8_to_bf16x8<kKv>(r.k[tau][1].z, r.k[tau][1].w));
+    } else {
+#pragma unroll
+      for (int c = 0; c < 4; ++c) kf[c] = as_bf16x8(r.k[tau][c]);
+    }
+    f32x4_t s = zero;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) s = mfma_bf16_16x16x32(kf[c], q.f[c], s);
+    return s;
+  }
+}
+
+template <int kKv, int kQ>
+__device__ __forceinline__ void attend_page(const PageRegs<kKv != kKvBf16>& r,
+                                            const QRegs<kQ>& qf, int kbase,
                                             int nvis, int g, float scale_log2,
                                             float& m_run, float& l_part,
                                             f32x4_t (&o)[8]) {
   // S^T for the wavefront's two 16-key tiles.
   f32x4_t s[2];
 #pragma unroll
-  for (int tau = 0; tau < 2; ++tau) {
-    bf16x8_t kf[4];
-    if constexpr (kFp8) {
-      kf[0] = as_bf16x8(fp8x8_to_bf16x8(r.k[tau][0].x, r.k[tau][0].y));
-      kf[1] = as_bf16x8(fp8x8_to_bf16x8(r.k[tau][0].z, r.k[tau][0].w));
-      kf[2] = as_bf16x8(fp8x8_to_bf16x8(r.k[tau][1].x, r.k[tau][1].y));
-      kf[3] = as_bf16x8(fp8x8_to_bf16x8(r.k[tau][1].z, r.k[tau][1].w));
-    } else {
-#pragma unroll
-      for (int c = 0; c < 4; ++c) kf[c] = as_bf16x8(r.k[tau][c]);
-    }
-    s[tau] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int c = 0; c < 4; ++c) s[tau] = mfma_bf16_16x16x32(kf[c], qf[c], s[tau]);
-  }
+  for (int tau = 0; tau < 2; ++tau) s[tau] = score_tile<kKv, kQ>(r, qf, tau);
 
   // Raw scores; keys past the visible count (only on a token's last page)
   // become -inf.  The positive scale is applied after the max.
@@ -205,8 +228,8 @@ __device__ __forceinline__ void attend_page(const PageRegs<kFp8>& r,
   u32x4_t vd[8];
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
-    if constexpr (kFp8) {
-      vd[j] = fp8x8_to_bf16x8(r.v[j].x, r.v[j].y);
+    if constexpr (kKv != kKvBf16) {
+      vd[j] = f8x8_to_bf16x8<kKv>(r.v[j].x, r.v[j].y);
     } else {
       vd[j] = r.v[j];
     }
@@ -265,8 +288,9 @@ __device__ __forceinline__ void merge_splits(const AttendParams& p, int64_t row,
   store_row(p.out + row * kHeadDim + d0, acc, L, p.v_scale);
 }
 
-template <bool kFp8>
+template <int kKv, int kQ>
 __global__ __launch_bounds__(kThreads) void attend_kernel(AttendParams p) {
+  constexpr bool kFp8 = kKv != kKvBf16;  // 8-bit K|V entries
   __shared__ int32_t s_page[kMaxTopk];
   __shared__ int32_t s_nvis[kMaxTopk];
   __shared__ int32_t s_nlive;
@@ -331,16 +355,27 @@ __global__ __launch_bounds__(kThreads) void attend_kernel(AttendParams p) {
   }
 
   // Q^T operand: q row n, head dims 16g.. and 64+16g.. (see header comment).
-  bf16x8_t qf[4];
-  if (n < rows) {
-    const uint16_t* qp = p.q + ((int64_t)t * p.hq + head0 + n) * kHeadDim;
-    qf[0] = as_bf16x8(*reinterpret_cast<const u32x4_t*>(qp + 16 * g));
-    qf[1] = as_bf16x8(*reinterpret_cast<const u32x4_t*>(qp + 16 * g + 8));
-    qf[2] = as_bf16x8(*reinterpret_cast<const u32x4_t*>(qp + 64 + 16 * g));
-    qf[3] = as_bf16x8(*reinterpret_cast<const u32x4_t*>(qp + 64 + 16 * g + 8));
+  QRegs<kQ> qf;
+  const int64_t q_row = (int64_t)t * p.hq + head0 + n;
+  if constexpr (kQ == kQE4m3) {
+    u32x4_t lo = u32x4_t{0u, 0u, 0u, 0u}, hi = lo;
+    if (n < rows) {
+      const uint8_t* qp = p.q + q_row * kHeadDim;
+      lo = *reinterpret_cast<const u32x4_t*>(qp + 16 * g);
+      hi = *reinterpret_cast<const u32x4_t*>(qp + 64 + 16 * g);
+    }
+    qf.b = cat_i32x8(lo, hi);
   } else {
+    if (n < rows) {
+      const uint16_t* qp = reinterpret_cast<const uint16_t*>(p.q) + q_row * kHeadDim;
+      qf.f[0] = as_bf16x8(*reinterpret_cast<const u32x4_t*>(qp + 16 * g));
+      qf.f[1] = as_bf16x8(*reinterpret_cast<const u32x4_t*>(qp + 16 * g + 8));
+      qf.f[2] = as_bf16x8(*reinterpret_cast<const u32x4_t*>(qp + 64 + 16 * g));
+      qf.f[3] = as_bf16x8(*reinterpret_cast<const u32x4_t*>(qp + 64 + 16 * g + 8));
+    } else {
 #pragma unroll
-    for (int c = 0; c < 4; ++c) qf[c] = as_bf16x8(u32x4_t{0u, 0u, 0u, 0u});
+      for (int c = 0; c < 4; ++c) qf.f[c] = as_bf16x8(u32x4_t{0u, 0u, 0u, 0u});
+    }
   }
   __syncthreads();
 
@@ -385,7 +420,7 @@ __global__ __launch_bounds__(kThreads) void attend_kernel(AttendParams p) {
                         row_stride, nvn - 1, lr);
         const int nv = __builtin_amdgcn_readfirstlane(s_nvis[cur]);
         if (kbase < nv)
-          attend_page<kFp8>(buf[j], qf, kbase, nv, g, p.scale_log2, m_run, l_part, o);
+          attend_page<kKv, kQ>(buf[j], qf, kbase, nv, g, p.scale_log2, m_run, l_part, o);
       }
     }
   }
@@ -500,7 +535,8 @@ __global__ __launch_bounds__(256) void merge_kernel(AttendParams p) {
   }
 }
 
-// fp8 -> bf16 through the same conversion helper the attend uses.
+// 8-bit codes -> bf16 through the same conversion helper the attend uses.
+template <int kFmt>
 __global__ __launch_bounds__(256) void fp8_to_bf16_kernel(const uint8_t* in, uint16_t* out,
                                                           int64_t n) {
   const int64_t base = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;
@@ -509,7 +545,7 @@ __global__ __launch_bounds__(256) void fp8_to_bf16_kernel(const uint8_t* in, uin
 #pragma unroll
   for (int b = 0; b < 4; ++b)
     if (base + b < n) w |= (uint32_t)in[base + b] << (8 * b);
-  const u32x4_t v = fp8x8_to_bf16x8(w, 0u);
+  const u32x4_t v = f8x8_to_bf16x8<kFmt>(w, 0u);
   const uint16_t vals[4] = {(uint16_t)(v.x & 0xffffu), (uint16_t)(v.x >> 16),
                             (uint16_t)(v.y & 0xffffu), (uint16_t)(v.y >> 16)};
 #pragma unroll
@@ -519,16 +555,25 @@ __global__ __launch_bounds__(256) void fp8_to_bf16_kernel(const uint8_t* in, uin
 
 }  // namespace
 
-hipError_t launch_attend(const AttendParams& p, bool fp8, hipStream_t stream) {
+hipError_t launch_attend(const AttendParams& p, int kv_fmt, int q_fmt, hipStream_t stream) {
   const int64_t groups = ((int64_t)p.num_units + kXcdSlots - 1) / kXcdSlots;
   const int64_t grid = groups * kXcdSlots * p.splits;
   if (grid <= 0) return hipSuccess;
-  if (fp8) {
-    hipLaunchKernelGGL(attend_kernel<true>, dim3((uint32_t)grid), dim3(kThreads), 0, stream,
-                       p);
+  const dim3 gd((uint32_t)grid), bd(kThreads);
+  if (q_fmt == kQE4m3) {
+    if (kv_fmt == kKvE4m3)
+      hipLaunchKernelGGL((attend_kernel<kKvE4m3, kQE4m3>), gd, bd, 0, stream, p);
+    else if (kv_fmt == kKvE5m2)
+      hipLaunchKernelGGL((attend_kernel<kKvE5m2, kQE4m3>), gd, bd, 0, stream, p);
+    else
+      return hipErrorInvalidValue;
   } else {
-    hipLaunchKernelGGL(attend_kernel<false>, dim3((uint32_t)grid), dim3(kThreads), 0, stream,
-                       p);
+    if (kv_fmt == kKvE4m3)
+      hipLaunchKernelGGL((attend_kernel<kKvE4m3, kQBf16>), gd, bd, 0, stream, p);
+    else if (kv_fmt == kKvE5m2)
+      hipLaunchKernelGGL((attend_kernel<kKvE5m2, kQBf16>), gd, bd, 0, stream, p);
+    else
+      hipLaunchKernelGGL((attend_kernel<kKvBf16, kQBf16>), gd, bd, 0, stream, p);
   }
   return hipGetLastError();
 }
@@ -542,11 +587,15 @@ hipError_t launch_merge(const AttendParams& p, hipStream_t stream) {
   return hipGetLastError();
 }
 
-hipError_t launch_fp8_to_bf16(const uint8_t* in, uint16_t* out, int64_t n,
+hipError_t launch_fp8_to_bf16(const uint8_t* in, uint16_t* out, int64_t n, int fmt,
                               hipStream_t stream) {
   const int64_t grid = (n + 1023) / 1024;
-  hipLaunchKernelGGL(fp8_to_bf16_kernel, dim3((uint32_t)grid), dim3(256), 0, stream, in,
-                     out, n);
+  if (fmt == kKvE5m2)
+    hipLaunchKernelGGL((fp8_to_bf16_kernel<kKvE5m2>), dim3((uint32_t)grid), dim3(256), 0,
+                       stream, in, out, n);
+  else
+    hipLaunchKernelGGL((fp8_to_bf16_kernel<kKvE4m3>), dim3((uint32_t)grid), dim3(256), 0,
+                       stream, in, out, n);
   return hipGetLastError();
 }
 

@@ -1,5 +1,5 @@
-// Device-side helpers for gfx950: vector types, the bf16 MFMA tile, fp8
-// e4m3fn -> bf16 conversion and wavefront reductions.
+// Device-side helpers for gfx950: vector types, the bf16 and fp8 MFMA tiles,
+// fp8 (e4m3fn / e5m2) -> bf16 conversion and wavefront reductions.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -13,6 +13,7 @@ typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef float f32x2_t __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+typedef int32_t i32x8_t __attribute__((ext_vector_type(8)));
 
 // D = A(16x32) * B(32x16) + C with bf16 operands and fp32 accumulate.
 // Operand layout (wave64): lane l holds row/column (l % 16) and eight
@@ -21,6 +22,23 @@ typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ f32x4_t mfma_bf16_16x16x32(bf16x8_t a, bf16x8_t b,
                                                        f32x4_t c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+// D = A(16x128) * B(128x16) + C with 8-bit float operands (32 per lane) and
+// fp32 accumulate; kAFmt / kBFmt: 0 = e4m3fn, 1 = e5m2.  The block scales are
+// 2^0 (E8M0 code 127), so the products are the plain fp8 values.  A and B
+// share one lane / byte -> contraction index map, so any fixed assignment of
+// head dims to (lane group, byte) that both operands follow gives the full
+// dot product.
+template <int kAFmt, int kBFmt>
+__device__ __forceinline__ f32x4_t mfma_f8_16x16x128(i32x8_t a, i32x8_t b, f32x4_t c) {
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, kAFmt, kBFmt, 0, 127, 0,
+                                                          127);
+}
+
+__device__ __forceinline__ i32x8_t cat_i32x8(u32x4_t lo, u32x4_t hi) {
+  return i32x8_t{(int32_t)lo.x, (int32_t)lo.y, (int32_t)lo.z, (int32_t)lo.w,
+                 (int32_t)hi.x, (int32_t)hi.y, (int32_t)hi.z, (int32_t)hi.w};
 }
 
 __device__ __forceinline__ bf16x8_t as_bf16x8(u32x4_t v) {
@@ -35,13 +53,30 @@ __device__ __forceinline__ uint32_t fp8x2_to_bf16x2(uint32_t w) {
   return __builtin_bit_cast(uint32_t, r);
 }
 
-// Eight fp8 codes (two dwords, little-endian byte order) -> eight bf16.
-__device__ __forceinline__ u32x4_t fp8x8_to_bf16x8(uint32_t lo, uint32_t hi) {
+// The same for OCP fp8 e5m2 codes (exact too: e5m2 values, +-inf and NaN
+// included, are bf16 values).
+template <bool kHi>
+__device__ __forceinline__ uint32_t bf8x2_to_bf16x2(uint32_t w) {
+  bf16x2_t r = __builtin_amdgcn_cvt_scalef32_pk_bf16_bf8(w, 1.0f, kHi);
+  return __builtin_bit_cast(uint32_t, r);
+}
+
+// Eight 8-bit codes (two dwords, little-endian byte order) -> eight bf16;
+// kFmt: 1 = e4m3fn, 2 = e5m2 (the KV format values).
+template <int kFmt>
+__device__ __forceinline__ u32x4_t f8x8_to_bf16x8(uint32_t lo, uint32_t hi) {
   u32x4_t r;
-  r.x = fp8x2_to_bf16x2<false>(lo);
-  r.y = fp8x2_to_bf16x2<true>(lo);
-  r.z = fp8x2_to_bf16x2<false>(hi);
-  r.w = fp8x2_to_bf16x2<true>(hi);
+  if constexpr (kFmt == 2) {
+    r.x = bf8x2_to_bf16x2<false>(lo);
+    r.y = bf8x2_to_bf16x2<true>(lo);
+    r.z = bf8x2_to_bf16x2<false>(hi);
+    r.w = bf8x2_to_bf16x2<true>(hi);
+  } else {
+    r.x = fp8x2_to_bf16x2<false>(lo);
+    r.y = fp8x2_to_bf16x2<true>(lo);
+    r.z = fp8x2_to_bf16x2<false>(hi);
+    r.w = fp8x2_to_bf16x2<true>(hi);
+  }
   return r;
 }
 
@@ -57,6 +92,22 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   r[1] = (__bf16)hi;
   return __builtin_bit_cast(uint32_t, r);
 }
+
+// The Q^T (B) operand of an S^T = K Q^T tile for one q row per lane: four
+// bf16 chunks (format 0), or the 32 fp8 e4m3fn bytes of the row's two 16-dim
+// runs (format 1).
+template <int kQ>
+struct QRegs;
+
+template <>
+struct QRegs<0> {
+  bf16x8_t f[4];
+};
+
+template <>
+struct QRegs<1> {
+  i32x8_t b;
+};
 
 // Byte permute: bytes of {src0 (bytes 4..7), src1 (bytes 0..3)} by selector.
 __device__ __forceinline__ uint32_t byte_perm(uint32_t src0, uint32_t src1,

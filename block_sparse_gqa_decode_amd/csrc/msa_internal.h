@@ -18,8 +18,15 @@ constexpr int kMaxScoreBatch = 4096;   // requests per scorer launch (LDS prefix
 constexpr int kMaxScoreDql = 32;
 constexpr int kXcdSlots = 8;   // XCDs a launch is dealt across, round robin
 
+// Element formats (the values of msa_kv_dtype / msa_q_dtype).
+constexpr int kKvBf16 = 0;
+constexpr int kKvE4m3 = 1;     // OCP fp8 e4m3fn
+constexpr int kKvE5m2 = 2;     // OCP fp8 e5m2
+constexpr int kQBf16 = 0;
+constexpr int kQE4m3 = 1;
+
 struct AttendParams {
-  const uint16_t* q;        // bf16 [rows, hq, 128]
+  const uint8_t* q;         // bf16 or fp8 e4m3fn [rows, hq, 128] (bytes)
   const uint8_t* kv;        // packed K|V base (bytes)
   int64_t kv_s0, kv_s1, kv_s2;  // strides in bytes (page, head, row)
   int64_t num_kv_blocks;
@@ -31,13 +38,13 @@ struct AttendParams {
   uint16_t* out;            // bf16 [rows, hq, 128]
   float* part_o;            // fp32 [rows, hq, splits, 128]
   float* part_ml;           // fp32 [rows, hq, splits, 2] = (max, sum) in log2 units
-  float scale_log2;         // sm_scale * k_scale * log2(e)
+  float scale_log2;         // sm_scale * q_scale * k_scale * log2(e)
   float v_scale;
   int32_t dql, real_rows, num_rows, hq, hkv, group, topk_k, splits, num_units;
 };
 
 struct ScoreParams {
-  const uint16_t* q;        // bf16 [rows, hq, 128]
+  const uint8_t* q;         // bf16 or fp8 e4m3fn [rows, hq, 128] (bytes)
   const uint8_t* kv;
   int64_t kv_s0, kv_s1, kv_s2;  // bytes
   int64_t num_kv_blocks;
@@ -46,7 +53,7 @@ struct ScoreParams {
   const int32_t* seq_lens;
   float* score;             // fp32 logical [hkv, max_blocks, rows]
   int64_t sc_s0, sc_s1, sc_s2;  // elements
-  float k_scale;
+  float qk_scale;           // q_scale * k_scale
   int32_t batch, dql, real_rows, num_rows, hq, hkv, group, max_blocks;
 };
 
@@ -57,11 +64,13 @@ struct SelectParams {
   int32_t hkv, max_blocks, num_rows, k;
 };
 
-hipError_t launch_attend(const AttendParams& p, bool fp8, hipStream_t stream);
+// kv_fmt: kKv*; q_fmt: kQ*.  An fp8 q needs an 8-bit KV format.
+hipError_t launch_attend(const AttendParams& p, int kv_fmt, int q_fmt, hipStream_t stream);
 hipError_t launch_merge(const AttendParams& p, hipStream_t stream);
-hipError_t launch_score(const ScoreParams& p, bool fp8, hipStream_t stream);
+hipError_t launch_score(const ScoreParams& p, int kv_fmt, int q_fmt, hipStream_t stream);
 hipError_t launch_select(const SelectParams& p, hipStream_t stream);
-hipError_t launch_fp8_to_bf16(const uint8_t* in, uint16_t* out, int64_t n,
+// fmt: kKvE4m3 or kKvE5m2
+hipError_t launch_fp8_to_bf16(const uint8_t* in, uint16_t* out, int64_t n, int fmt,
                               hipStream_t stream);
 
 }  // namespace msa

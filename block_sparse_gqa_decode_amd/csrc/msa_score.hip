@@ -7,6 +7,12 @@
 // of Q.K, here with the q heads as the 16 columns of the same S^T = K Q^T MFMA
 // tile the attend uses).
 //
+// Formats as in the attend: K is bf16, e4m3fn or e5m2; q is bf16 or fp8
+// e4m3fn with a per-tensor q scale.  With an fp8 q each 16-key tile is one
+// 16x16x128 fp8 MFMA on the K bytes as loaded; with a bf16 q the K bytes are
+// widened to bf16 for the bf16 MFMA.  q_scale * k_scale multiplies every dot
+// product before the max.
+//
 // Work decomposition.  The visible (kv head, request, block) items -- every
 // block a request's last token can see -- are counted on the device from
 // seq_lens (a prefix sum over the batch in LDS), and each workgroup of a
@@ -70,46 +76,63 @@ __device__ __forceinline__ void load_khalf(KHalf<kFp8>& r, const uint8_t* page,
   }
 }
 
-__device__ __forceinline__ void load_q(bf16x8_t (&qf)[4], const ScoreParams& p, int t, int h,
+template <int kQ>
+__device__ __forceinline__ void load_q(QRegs<kQ>& qf, const ScoreParams& p, int t, int h,
                                        int n, int g) {
-  if (n < p.group) {
-    const uint16_t* qp = p.q + ((int64_t)t * p.hq + h * p.group + n) * kHeadDim;
-    qf[0] = as_bf16x8(*reinterpret_cast<const u32x4_t*>(qp + 16 * g));
-    qf[1] = as_bf16x8(*reinterpret_cast<const u32x4_t*>(qp + 16 * g + 8));
-    qf[2] = as_bf16x8(*reinterpret_cast<const u32x4_t*>(qp + 64 + 16 * g));
-    qf[3] = as_bf16x8(*reinterpret_cast<const u32x4_t*>(qp + 64 + 16 * g + 8));
+  const int64_t row = (int64_t)t * p.hq + h * p.group + n;
+  if constexpr (kQ == kQE4m3) {
+    u32x4_t lo = u32x4_t{0u, 0u, 0u, 0u}, hi = lo;
+    if (n < p.group) {
+      const uint8_t* qp = p.q + row * kHeadDim;
+      lo = *reinterpret_cast<const u32x4_t*>(qp + 16 * g);
+      hi = *reinterpret_cast<const u32x4_t*>(qp + 64 + 16 * g);
+    }
+    qf.b = cat_i32x8(lo, hi);
   } else {
+    if (n < p.group) {
+      const uint16_t* qp = reinterpret_cast<const uint16_t*>(p.q) + row * kHeadDim;
+      qf.f[0] = as_bf16x8(*reinterpret_cast<const u32x4_t*>(qp + 16 * g));
+      qf.f[1] = as_bf16x8(*reinterpret_cast<const u32x4_t*>(qp + 16 * g + 8));
+      qf.f[2] = as_bf16x8(*reinterpret_cast<const u32x4_t*>(qp + 64 + 16 * g));
+      qf.f[3] = as_bf16x8(*reinterpret_cast<const u32x4_t*>(qp + 64 + 16 * g + 8));
+    } else {
 #pragma unroll
-    for (int c = 0; c < 4; ++c) qf[c] = as_bf16x8(u32x4_t{0u, 0u, 0u, 0u});
+      for (int c = 0; c < 4; ++c) qf.f[c] = as_bf16x8(u32x4_t{0u, 0u, 0u, 0u});
+    }
   }
 }
 
 // The wavefront's max over its 32 keys (those < nvis) and the group's rows of
-// k_scale * q.k for one block and one token.
-template <bool kFp8>
-__device__ __forceinline__ float block_max(const KHalf<kFp8>& r, const bf16x8_t (&qf)[4],
-                                           int kbase, int nvis, int n, int g, int group,
-                                           float k_scale) {
+// qk_scale * q.k for one block and one token.
+template <int kKv, int kQ>
+__device__ __forceinline__ float block_max(const KHalf<kKv != kKvBf16>& r,
+                                           const QRegs<kQ>& qf, int kbase, int nvis, int n,
+                                           int g, int group, float qk_scale) {
   float best = -INFINITY;
 #pragma unroll
   for (int tau = 0; tau < 2; ++tau) {
-    bf16x8_t kf[4];
-    if constexpr (kFp8) {
-      kf[0] = as_bf16x8(fp8x8_to_bf16x8(r.k[tau][0].x, r.k[tau][0].y));
-      kf[1] = as_bf16x8(fp8x8_to_bf16x8(r.k[tau][0].z, r.k[tau][0].w));
-      kf[2] = as_bf16x8(fp8x8_to_bf16x8(r.k[tau][1].x, r.k[tau][1].y));
-      kf[3] = as_bf16x8(fp8x8_to_bf16x8(r.k[tau][1].z, r.k[tau][1].w));
-    } else {
-#pragma unroll
-      for (int c = 0; c < 4; ++c) kf[c] = as_bf16x8(r.k[tau][c]);
-    }
     f32x4_t s = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    if constexpr (kQ == kQE4m3) {
+      s = mfma_f8_16x16x128<kKv == kKvE5m2 ? 1 : 0, 0>(cat_i32x8(r.k[tau][0], r.k[tau][1]),
+                                                        qf.b, s);
+    } else {
+      bf16x8_t kf[4];
+      if constexpr (kKv != kKvBf16) {
+        kf[0] = as_bf16x8(f8x8_to_bf16x8<kKv>(r.k[tau][0].x, r.k[tau][0].y));
+        kf[1] = as_bf16x8(f8x8_to_bf16x8<kKv>(r.k[tau][0].z, r.k[tau][0].w));
+        kf[2] = as_bf16x8(f8x8_to_bf16x8<kKv>(r.k[tau][1].x, r.k[tau][1].y));
+        kf[3] = as_bf16x8(f8x8_to_bf16x8<kKv>(r.k[tau][1].z, r.k[tau][1].w));
+      } else {
 #pragma unroll
-    for (int c = 0; c < 4; ++c) s = mfma_bf16_16x16x32(kf[c], qf[c], s);
+        for (int c = 0; c < 4; ++c) kf[c] = as_bf16x8(r.k[tau][c]);
+      }
+#pragma unroll
+      for (int c = 0; c < 4; ++c) s = mfma_bf16_16x16x32(kf[c], qf.f[c], s);
+    }
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int key = kbase + 16 * tau + 4 * g + i;
-      if (key < nvis && n < group) best = fmaxf(best, s[i] * k_scale);
+      if (key < nvis && n < group) best = fmaxf(best, s[i] * qk_scale);
     }
   }
 #pragma unroll
@@ -119,8 +142,9 @@ __device__ __forceinline__ float block_max(const KHalf<kFp8>& r, const bf16x8_t 
 
 typedef __attribute__((address_space(4))) const int32_t const_i32;
 
-template <bool kFp8, bool kOneToken>
+template <int kKv, int kQ, bool kOneToken>
 __global__ __launch_bounds__(kScoreThreads) void score_kernel(ScoreParams p) {
+  constexpr bool kFp8 = kKv != kKvBf16;  // 8-bit K entries
   __shared__ int32_t s_pref[kMaxScoreBatch + 1];       // blocks before request r
   __shared__ int32_t s_scan[kScoreThreads];
   __shared__ float s_part[kScoreWaves][kFlush * kMaxScoreDql];
@@ -219,8 +243,8 @@ __global__ __launch_bounds__(kScoreThreads) void score_kernel(ScoreParams p) {
     const int t0 = r * p.dql;
     const int32_t* bt_row = p.block_table + (int64_t)r * p.bt_stride;
     const uint8_t* head_base = p.kv + h * p.kv_s1;
-    bf16x8_t qf[4];
-    load_q(qf, p, t0 + p.dql - 1, h, n, g);
+    QRegs<kQ> qf;
+    load_q<kQ>(qf, p, t0 + p.dql - 1, h, n, g);
     const int b_last = b + seg - 1;
 
     // Block-table entries are read through the scalar cache (uniform index,
@@ -263,13 +287,13 @@ __global__ __launch_bounds__(kScoreThreads) void score_kernel(ScoreParams p) {
             float m = -INFINITY;
             if (ok_page && nvis > 0 && kbase < nvis) {
               if constexpr (kOneToken) {
-                m = block_max<kFp8>(buf[j], qf, kbase, min(nvis, kPage), n, g, p.group,
-                                    p.k_scale);
+                m = block_max<kKv, kQ>(buf[j], qf, kbase, min(nvis, kPage), n, g, p.group,
+                                       p.qk_scale);
               } else {
-                bf16x8_t ql[4];
-                load_q(ql, p, t0 + l, h, n, g);
-                m = block_max<kFp8>(buf[j], ql, kbase, min(nvis, kPage), n, g, p.group,
-                                    p.k_scale);
+                QRegs<kQ> ql;
+                load_q<kQ>(ql, p, t0 + l, h, n, g);
+                m = block_max<kKv, kQ>(buf[j], ql, kbase, min(nvis, kPage), n, g, p.group,
+                                       p.qk_scale);
               }
             }
             if (lane == 0) s_part[wave][nflush * p.dql + l] = m;
@@ -489,18 +513,26 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(SelectParams p) {
 
 }  // namespace
 
-hipError_t launch_score(const ScoreParams& p, bool fp8, hipStream_t stream) {
+template <int kKv, int kQ>
+static void launch_score_fmt(const ScoreParams& p, dim3 g, dim3 b, hipStream_t stream) {
+  if (p.dql == 1) hipLaunchKernelGGL((score_kernel<kKv, kQ, true>), g, b, 0, stream, p);
+  else hipLaunchKernelGGL((score_kernel<kKv, kQ, false>), g, b, 0, stream, p);
+}
+
+hipError_t launch_score(const ScoreParams& p, int kv_fmt, int q_fmt, hipStream_t stream) {
   // A persistent grid: about four workgroups per CU, never more than there
   // are possible items.
   const int64_t upper = (int64_t)p.batch * p.hkv * p.max_blocks;
   const int64_t grid = upper < 1024 ? (upper > 0 ? upper : 1) : 1024;
   const dim3 g((uint32_t)grid), b(kScoreThreads);
-  if (fp8) {
-    if (p.dql == 1) hipLaunchKernelGGL((score_kernel<true, true>), g, b, 0, stream, p);
-    else hipLaunchKernelGGL((score_kernel<true, false>), g, b, 0, stream, p);
+  if (q_fmt == kQE4m3) {
+    if (kv_fmt == kKvE4m3) launch_score_fmt<kKvE4m3, kQE4m3>(p, g, b, stream);
+    else if (kv_fmt == kKvE5m2) launch_score_fmt<kKvE5m2, kQE4m3>(p, g, b, stream);
+    else return hipErrorInvalidValue;
   } else {
-    if (p.dql == 1) hipLaunchKernelGGL((score_kernel<false, true>), g, b, 0, stream, p);
-    else hipLaunchKernelGGL((score_kernel<false, false>), g, b, 0, stream, p);
+    if (kv_fmt == kKvE4m3) launch_score_fmt<kKvE4m3, kQBf16>(p, g, b, stream);
+    else if (kv_fmt == kKvE5m2) launch_score_fmt<kKvE5m2, kQBf16>(p, g, b, stream);
+    else launch_score_fmt<kKvBf16, kQBf16>(p, g, b, stream);
   }
   return hipGetLastError();
 }

@@ -7,11 +7,12 @@
  *  - vLLM API page "vllm.models.minimax_m3.nvidia.msa_cutlass_sparse_decode":
  *    MSACutlassDecodePlanCache.prepare / _build_plan (plan keyed by the static
  *    shape, graph-stable mutable state, argument checks), msa_cutlass_sparse_decode
- *    (packed cache split into K = first 128, V = last 128 of the last dim;
- *    sm_scale, k/v scales), prepare_decode_metadata.
+ *    (fp8 query with q_scale_float; packed cache split into K = first 128,
+ *    V = last 128 of the last dim; sm_scale, k/v scales), prepare_decode_metadata.
  *  - vLLM API page "vllm.models.minimax_m3.common.sparse_attention":
- *    MiniMaxM3SparseBackend (head size 128, block size 128, bf16 / fp8 KV,
- *    cache shape (num_blocks, num_kv_heads, 128, 2*128) in HND order),
+ *    MiniMaxM3SparseBackend (head size 128, block size 128, bf16 / fp8 e4m3 /
+ *    fp8 e5m2 KV, cache shape (num_blocks, num_kv_heads, 128, 2*128) in HND
+ *    order),
  *    MiniMaxM3SparseImpl (each query attends only the indexer-selected
  *    blocks), MiniMaxM3SparseTritonImpl.forward (decode call arguments).
  *  - vLLM test file test_minimax_m3_msa_cutlass_sparse_decode.py: _make_topk
@@ -49,7 +50,7 @@
 extern "C" {
 #endif
 
-#define MSA_ABI_VERSION 1
+#define MSA_ABI_VERSION 2
 
 typedef enum msa_status {
   MSA_OK = 0,
@@ -61,13 +62,20 @@ typedef enum msa_status {
 
 typedef enum msa_kv_dtype {
   MSA_KV_BF16 = 0,            /* bf16 K|V entries                              */
-  MSA_KV_FP8_E4M3 = 1         /* OCP fp8 e4m3fn K|V entries, per-tensor scale  */
+  MSA_KV_FP8_E4M3 = 1,        /* OCP fp8 e4m3fn K|V entries, per-tensor scale  */
+  MSA_KV_FP8_E5M2 = 2         /* OCP fp8 e5m2 K|V entries, per-tensor scale    */
 } msa_kv_dtype;
+
+typedef enum msa_q_dtype {
+  MSA_Q_BF16 = 0,             /* bf16 q                                        */
+  MSA_Q_FP8_E4M3 = 1          /* OCP fp8 e4m3fn q codes; value = code * q_scale
+                                 (needs an fp8 KV cache)                       */
+} msa_q_dtype;
 
 /* Static shape of one decode step: the plan key (batch, decode query length,
  * page-table stride, q heads, kv heads, page size, top-k) of the plan cache in
- * MSACutlassDecodePlanCache.prepare, plus KV dtype, padding rows and split
- * count. */
+ * MSACutlassDecodePlanCache.prepare, plus KV and q dtypes, padding rows and
+ * split count. */
 typedef struct msa_decode_shape {
   int32_t batch;              /* requests, >= 1                                  */
   int32_t decode_query_len;   /* query tokens per request, 1..32                 */
@@ -83,6 +91,7 @@ typedef struct msa_decode_shape {
   int32_t kv_dtype;           /* msa_kv_dtype                                    */
   int32_t num_splits;         /* split-K factor over a row's live blocks; 0 lets
                                  the plan choose, else 1..16                     */
+  int32_t q_dtype;            /* msa_q_dtype                                     */
 } msa_decode_shape;
 
 typedef struct msa_plan_s* msa_plan;
@@ -112,11 +121,12 @@ msa_status msa_sparse_decode_plan_info(msa_plan plan, int32_t* num_splits,
  *   out[t, j, :] = softmax_k( sm_scale * q[t,j,:] . K[k,:] ) V[k,:]
  * over the keys k = b*128 + i of every selected logical block b =
  * topk[t, h, s] with b >= 0 and b*128 <= pos, i < min(128, pos - b*128 + 1),
- * read from physical page block_table[r, b].  K and V are the decoded cache
- * entries times k_scale / v_scale.  Rows with no visible key, and padding
- * rows, are written as exact zeros.
+ * read from physical page block_table[r, b].  q is the decoded q times
+ * q_scale; K and V are the decoded cache entries times k_scale / v_scale.
+ * Rows with no visible key, and padding rows, are written as exact zeros.
  *
- *   q            bf16 [num_token_rows, Hq, 128], contiguous.
+ *   q            [num_token_rows, Hq, 128], contiguous: bf16, or fp8 e4m3fn
+ *                codes when the plan's q_dtype is MSA_Q_FP8_E4M3.
  *   kv_cache     packed K|V entries, logical [num_kv_blocks, Hkv, 128, 256]
  *                with strides kv_strides (elements); kv_strides[3] must be 1
  *                and the other strides must be positive multiples of 16 bytes.
@@ -128,12 +138,13 @@ msa_status msa_sparse_decode_plan_info(msa_plan plan, int32_t* num_splits,
  *   topk         int32 logical [num_token_rows, Hkv, topk_blocks] with
  *                topk_strides (elements), -1 = no block.
  *   out          bf16 [num_token_rows, Hq, 128], contiguous.
- *   sm_scale, k_scale must be finite and > 0 (the kernel takes each row's
- *   maximum before applying them); v_scale must be finite.
+ *   sm_scale, q_scale, k_scale must be finite and > 0 (the kernel takes each
+ *   row's maximum before applying them); v_scale must be finite.  For a bf16
+ *   q pass q_scale = 1 unless the q values are to be scaled.
  */
 msa_status msa_sparse_decode_run(msa_plan plan, const void* q, const void* kv_cache,
                                  const int64_t kv_strides[4], int64_t num_kv_blocks,
-                                 float k_scale, float v_scale,
+                                 float q_scale, float k_scale, float v_scale,
                                  const int32_t* block_table, const int32_t* seq_lens,
                                  const int32_t* topk, const int64_t topk_strides[3],
                                  void* out, float sm_scale, void* stream);
@@ -150,7 +161,7 @@ msa_status msa_sparse_decode_run(msa_plan plan, const void* q, const void* kv_ca
  * of the plan may come between them. */
 msa_status msa_sparse_decode_attend(msa_plan plan, const void* q, const void* kv_cache,
                                     const int64_t kv_strides[4], int64_t num_kv_blocks,
-                                    float k_scale, float v_scale,
+                                    float q_scale, float k_scale, float v_scale,
                                     const int32_t* block_table, const int32_t* seq_lens,
                                     const int32_t* topk, const int64_t topk_strides[3],
                                     void* out, float sm_scale, void* stream);
@@ -159,14 +170,15 @@ msa_status msa_sparse_decode_merge(msa_plan plan, void* out, float v_scale, void
 /* Indexer step of a full decode: per-block causal max score, then top-k.
  *   score[h, b, t] = max over g < G and visible keys i of block b of
  *                    q[t, h*G+g, :] . K[block_table[r,b], h, i, :]
- * (raw dot product with K = decoded entries * k_scale, no softmax scale),
+ * (raw dot product with q = decoded q * q_scale and K = decoded entries *
+ * k_scale, no softmax scale; q_scale and k_scale finite and > 0),
  * -inf for blocks b < max_blocks that start after the token's position; then
  * topk_out[t, h, :] = the topk_k blocks with the largest score > -inf, in
  * descending score order with ties to the lower block id, padded with -1.
  *   shape        batch (1..4096), decode_query_len, num_token_rows (padding rows get
  *                -inf scores and all -1 selections), heads, page_table_stride,
- *                page_size, head_dim, kv_dtype are used; topk_blocks and
- *                num_splits are ignored.
+ *                page_size, head_dim, kv_dtype, q_dtype are used; topk_blocks
+ *                and num_splits are ignored.
  *   score        float32 logical [Hkv, max_blocks, num_token_rows] with
  *                score_strides (elements); caller-owned scratch, required.
  *   max_blocks   1..16384, at least ceil(max seq_len / 128).
@@ -174,7 +186,7 @@ msa_status msa_sparse_decode_merge(msa_plan plan, void* out, float v_scale, void
  */
 msa_status msa_block_score_topk(const msa_decode_shape* shape, const void* q,
                                 const void* kv_cache, const int64_t kv_strides[4],
-                                int64_t num_kv_blocks, float k_scale,
+                                int64_t num_kv_blocks, float q_scale, float k_scale,
                                 const int32_t* block_table, const int32_t* seq_lens,
                                 int32_t max_blocks, float* score,
                                 const int64_t score_strides[3], int32_t* topk_out,
@@ -190,6 +202,8 @@ msa_status msa_topk_select(const float* score, const int64_t score_strides[3],
  * the attend uses (a self-check of the conversion path).  in: uint8[n],
  * out: bf16 bits uint16[n], device pointers, n >= 1. */
 msa_status msa_fp8_e4m3_to_bf16(const void* in, void* out, int64_t n, void* stream);
+/* The same for OCP fp8 e5m2 codes. */
+msa_status msa_fp8_e5m2_to_bf16(const void* in, void* out, int64_t n, void* stream);
 
 /* Message for the last non-OK status returned on this thread ("" if none). */
 const char* msa_last_error(void);

@@ -10,13 +10,18 @@ from workloads import gen
 ATOL = 1e-2
 RTOL = 1e-2
 
+KV_CODES = {gen.KV_FP8: msa.KV_FP8_E4M3, gen.KV_E5M2: msa.KV_FP8_E5M2, gen.KV_BF16: msa.KV_BF16}
+Q_CODES = {gen.Q_BF16: msa.Q_BF16, gen.Q_FP8: msa.Q_FP8_E4M3}
+
 
 class DevCase:
     def __init__(self, case: gen.DecodeCase, dev="cuda:0", layout="hnd"):
         self.case = case
         self.dev = torch.device(dev)
         if case.kv_dtype == gen.KV_FP8:
-            kv = torch.from_numpy(case.kv)
+            kv = torch.from_numpy(case.kv)                       # uint8 codes
+        elif case.kv_dtype == gen.KV_E5M2:
+            kv = torch.from_numpy(case.kv).view(torch.float8_e5m2)
         else:
             kv = torch.from_numpy(case.kv.view(np.int16)).view(torch.bfloat16)
         if layout == "nhd":
@@ -25,16 +30,28 @@ class DevCase:
         else:
             kv = kv.to(self.dev)
         self.kv = kv
-        self.q = torch.from_numpy(case.q.view(np.int16)).view(torch.bfloat16).to(self.dev)
+        if case.q_dtype == gen.Q_FP8:
+            self.q = torch.from_numpy(case.q).view(torch.float8_e4m3fn).to(self.dev)
+        else:
+            self.q = torch.from_numpy(case.q.view(np.int16)).view(torch.bfloat16).to(self.dev)
         self.block_table = torch.from_numpy(case.block_table).to(self.dev)
         self.seq_lens = torch.from_numpy(case.seq_lens).to(self.dev)
         self.topk = (torch.from_numpy(case.topk).to(self.dev)
                      if case.topk is not None else None)
-        self.out = torch.full_like(self.q, float("nan"))
+        self.out = self.new_out()
+
+    def new_out(self):
+        """A bf16 output tensor of q's shape, filled with NaN."""
+        return torch.full(tuple(self.q.shape), float("nan"), dtype=torch.bfloat16,
+                          device=self.dev)
 
     @property
     def kv_dtype(self):
-        return msa.KV_FP8_E4M3 if self.case.kv_dtype == gen.KV_FP8 else msa.KV_BF16
+        return KV_CODES[self.case.kv_dtype]
+
+    @property
+    def q_dtype(self):
+        return Q_CODES[self.case.q_dtype]
 
     def plan(self, num_splits=0):
         c = self.case
@@ -42,7 +59,7 @@ class DevCase:
             c.batch, c.dql, num_q_heads=c.num_q_heads, num_kv_heads=c.num_kv_heads,
             page_table_stride=self.block_table.stride(0), topk_blocks=c.topk_k,
             kv_dtype=self.kv_dtype, num_token_rows=c.num_token_rows, num_splits=num_splits,
-            device=self.dev)
+            q_dtype=self.q_dtype, device=self.dev)
 
     def run(self, plan, topk=None, out=None, stream=None):
         c = self.case
@@ -50,15 +67,32 @@ class DevCase:
         msa.msa_sparse_decode_run(plan, self.q, self.kv, self.block_table, self.seq_lens,
                                   self.topk if topk is None else topk, out,
                                   sm_scale=c.sm_scale, k_scale=c.k_scale, v_scale=c.v_scale,
-                                  stream=stream)
+                                  q_scale=c.q_scale, stream=stream)
         return out
+
+    def score(self, score, topk_out, max_blocks, num_token_rows=0, stream=None):
+        """Indexer scores + top-k through the C ABI with the case's formats."""
+        c = self.case
+        msa.msa_block_score_topk(self.q, self.kv, self.block_table, self.seq_lens,
+                                 decode_query_len=c.dql, num_kv_heads=c.num_kv_heads,
+                                 max_blocks=max_blocks, score=score, topk_out=topk_out,
+                                 k_scale=c.k_scale, q_scale=c.q_scale,
+                                 num_token_rows=num_token_rows, kv_dtype=self.kv_dtype,
+                                 stream=stream)
 
 
 def oracle_attend(case: gen.DecodeCase, rows=None, topk=None):
     return om.sparse_decode(case.q, case.kv, case.kv_dtype, case.k_scale, case.v_scale,
                             case.block_table, case.seq_lens,
                             case.topk if topk is None else topk, case.dql,
-                            case.num_kv_heads, case.sm_scale, rows=rows)
+                            case.num_kv_heads, case.sm_scale, rows=rows,
+                            q_dtype=case.q_dtype, q_scale=case.q_scale)
+
+
+def oracle_scores(case: gen.DecodeCase, max_blocks, rows=None):
+    return om.block_max_scores(case.q, case.kv, case.kv_dtype, case.k_scale, case.block_table,
+                               case.seq_lens, case.dql, case.num_kv_heads, max_blocks,
+                               rows=rows, q_dtype=case.q_dtype, q_scale=case.q_scale)
 
 
 def to_f64(x: torch.Tensor) -> np.ndarray:

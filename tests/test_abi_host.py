@@ -35,7 +35,7 @@ def lib():
 def shape(**kw):
     base = dict(batch=32, decode_query_len=4, num_token_rows=0, page_table_stride=512,
                 num_q_heads=16, num_kv_heads=1, page_size=128, head_dim=128, topk_blocks=16,
-                kv_dtype=msa.KV_FP8_E4M3, num_splits=1)
+                kv_dtype=msa.KV_FP8_E4M3, num_splits=1, q_dtype=msa.Q_BF16)
     base.update(kw)
     return msa._Shape(*[base[f] for f, _ in msa._Shape._fields_])
 
@@ -105,12 +105,28 @@ def test_decode_query_len_bounds(lib, batch, dql, hq, hkv, ok):
     ("page_table_stride", 0, msa.MSA_ERR_INVALID_ARG, "page_table_stride"),
     ("num_token_rows", 5, msa.MSA_ERR_INVALID_ARG, "num_token_rows"),
     ("kv_dtype", 7, msa.MSA_ERR_INVALID_ARG, "kv_dtype"),
+    ("q_dtype", 2, msa.MSA_ERR_INVALID_ARG, "q_dtype"),
     ("num_splits", 17, msa.MSA_ERR_INVALID_ARG, "num_splits"),
     ("num_splits", -1, msa.MSA_ERR_INVALID_ARG, "num_splits"),
 ])
 def test_plan_rejects_bad_shapes(lib, field, value, status, fragment):
     st, msg = plan_status(lib, shape(**{field: value}))
     assert st == status and fragment in msg, (st, msg)
+
+
+@pytest.mark.parametrize("kv,q,ok", [
+    (msa.KV_BF16, msa.Q_BF16, True), (msa.KV_FP8_E4M3, msa.Q_BF16, True),
+    (msa.KV_FP8_E5M2, msa.Q_BF16, True), (msa.KV_FP8_E4M3, msa.Q_FP8_E4M3, True),
+    (msa.KV_FP8_E5M2, msa.Q_FP8_E4M3, True), (msa.KV_BF16, msa.Q_FP8_E4M3, False),
+])
+def test_plan_format_pairs(lib, kv, q, ok):
+    """An fp8 q runs the fp8 x fp8 MFMA and needs an fp8 cache; every other
+    pair is accepted."""
+    st, msg = plan_status(lib, shape(kv_dtype=kv, q_dtype=q))
+    if ok:
+        assert st == 0, msg
+    else:
+        assert st == msa.MSA_ERR_UNSUPPORTED and "fp8 q" in msg
 
 
 def test_plan_null_arguments(lib):
@@ -157,15 +173,15 @@ def _plan(lib, **kw):
 
 
 def _run(lib, h, **over):
-    args = dict(q=FAKE, kv=FAKE, kvs=(256 * 128, 256 * 128, 256, 1), nb=10, ks=1.0,
+    args = dict(q=FAKE, kv=FAKE, kvs=(256 * 128, 256 * 128, 256, 1), nb=10, qs=1.0, ks=1.0,
                 vs=1.0, bt=FAKE, sl=FAKE, tk=FAKE, tks=(16, 16, 1), out=FAKE, sm=0.088,
                 stream=None)
     args.update(over)
     kvs = msa._I64x4(*args["kvs"]) if args["kvs"] is not None else None
     tks = msa._I64x3(*args["tks"]) if args["tks"] is not None else None
-    st = lib.msa_sparse_decode_run(h, args["q"], args["kv"], kvs, args["nb"], args["ks"],
-                                   args["vs"], args["bt"], args["sl"], args["tk"], tks,
-                                   args["out"], args["sm"], args["stream"])
+    st = lib.msa_sparse_decode_run(h, args["q"], args["kv"], kvs, args["nb"], args["qs"],
+                                   args["ks"], args["vs"], args["bt"], args["sl"], args["tk"],
+                                   tks, args["out"], args["sm"], args["stream"])
     return st, lib.msa_last_error().decode()
 
 
@@ -187,6 +203,11 @@ def _run(lib, h, **over):
     (dict(nb=0), "num_kv_blocks"),
     (dict(sm=float("nan")), "finite"),
     (dict(ks=float("inf")), "finite"),
+    (dict(qs=float("nan")), "finite"),
+    (dict(qs=0.0), "positive"),
+    (dict(qs=-0.5), "positive"),
+    (dict(ks=-1.0), "positive"),
+    (dict(sm=0.0), "positive"),
 ])
 def test_run_rejects_bad_arguments(lib, over, fragment):
     h = _plan(lib)
@@ -213,13 +234,13 @@ def test_bf16_strides_are_checked_in_bytes(lib):
 
 
 def _score(lib, s, **over):
-    args = dict(q=FAKE, kv=FAKE, kvs=(256 * 128, 256 * 128, 256, 1), nb=10, ks=1.0, bt=FAKE,
-                sl=FAKE, mb=64, sc=FAKE, scs=(64 * 8, 8, 1), to=FAKE, k=16)
+    args = dict(q=FAKE, kv=FAKE, kvs=(256 * 128, 256 * 128, 256, 1), nb=10, qs=1.0, ks=1.0,
+                bt=FAKE, sl=FAKE, mb=64, sc=FAKE, scs=(64 * 8, 8, 1), to=FAKE, k=16)
     args.update(over)
     st = lib.msa_block_score_topk(ctypes.byref(s), args["q"], args["kv"],
-                                  msa._I64x4(*args["kvs"]), args["nb"], args["ks"], args["bt"],
-                                  args["sl"], args["mb"], args["sc"], msa._I64x3(*args["scs"]),
-                                  args["to"], args["k"], None)
+                                  msa._I64x4(*args["kvs"]), args["nb"], args["qs"], args["ks"],
+                                  args["bt"], args["sl"], args["mb"], args["sc"],
+                                  msa._I64x3(*args["scs"]), args["to"], args["k"], None)
     return st, lib.msa_last_error().decode()
 
 
@@ -231,7 +252,9 @@ def _score(lib, s, **over):
     (dict(k=0), "topk_k"),
     (dict(k=65), "topk_k"),
     (dict(scs=(1, -1, 1)), "score strides"),
-    (dict(ks=float("nan")), "k_scale"),
+    (dict(ks=float("nan")), "finite"),
+    (dict(qs=float("inf")), "finite"),
+    (dict(qs=0.0), "positive"),
     (dict(q=FAKE + 2), "q must be"),
 ])
 def test_score_topk_rejects_bad_arguments(lib, over, fragment):
@@ -242,6 +265,10 @@ def test_score_topk_rejects_bad_arguments(lib, over, fragment):
 def test_score_topk_validates_shape(lib):
     st, msg = _score(lib, shape(decode_query_len=40))
     assert st == msa.MSA_ERR_INVALID_ARG and "decode_query_len" in msg
+    st, msg = _score(lib, shape(kv_dtype=msa.KV_BF16, q_dtype=msa.Q_FP8_E4M3))
+    assert st == msa.MSA_ERR_UNSUPPORTED and "fp8 q" in msg
+    st, msg = _score(lib, shape(batch=4097))
+    assert st == msa.MSA_ERR_UNSUPPORTED and "batch" in msg
 
 
 def test_topk_select_rejects_bad_arguments(lib):
@@ -253,8 +280,9 @@ def test_topk_select_rejects_bad_arguments(lib):
 
 
 def test_fp8_conversion_rejects_bad_arguments(lib):
-    assert lib.msa_fp8_e4m3_to_bf16(None, FAKE, 4, None) == msa.MSA_ERR_INVALID_ARG
-    assert lib.msa_fp8_e4m3_to_bf16(FAKE, FAKE, 0, None) == msa.MSA_ERR_INVALID_ARG
+    for fn in (lib.msa_fp8_e4m3_to_bf16, lib.msa_fp8_e5m2_to_bf16):
+        assert fn(None, FAKE, 4, None) == msa.MSA_ERR_INVALID_ARG
+        assert fn(FAKE, FAKE, 0, None) == msa.MSA_ERR_INVALID_ARG
 
 
 def test_destroy_null_is_ok(lib):
@@ -281,11 +309,26 @@ def test_attend_rejects_bad_arguments(lib):
     try:
         kvs = msa._I64x4(256 * 128, 256 * 128, 256, 1)
         tks = msa._I64x3(16, 16, 1)
-        st = lib.msa_sparse_decode_attend(h, FAKE, FAKE, kvs, 10, 1.0, 1.0, FAKE, FAKE, FAKE,
-                                          tks, None, 0.08, None)
+        st = lib.msa_sparse_decode_attend(h, FAKE, FAKE, kvs, 10, 1.0, 1.0, 1.0, FAKE, FAKE,
+                                          FAKE, tks, None, 0.08, None)
         assert st == msa.MSA_ERR_INVALID_ARG
-        st = lib.msa_sparse_decode_attend(h, FAKE, FAKE, kvs, 10, -1.0, 1.0, FAKE, FAKE, FAKE,
-                                          tks, FAKE, 0.08, None)
+        st = lib.msa_sparse_decode_attend(h, FAKE, FAKE, kvs, 10, 1.0, -1.0, 1.0, FAKE, FAKE,
+                                          FAKE, tks, FAKE, 0.08, None)
         assert st == msa.MSA_ERR_INVALID_ARG and "positive" in lib.msa_last_error().decode()
     finally:
         lib.msa_sparse_decode_plan_destroy(h)
+
+
+def test_binding_format_checks():
+    """The binding maps tensor dtypes to formats and refuses mismatches before
+    calling the library (CPU tensors suffice: the checks come first)."""
+    import torch
+    assert msa._q_dtype_of(torch.empty(1, dtype=torch.bfloat16)) == msa.Q_BF16
+    assert msa._q_dtype_of(torch.empty(1, dtype=torch.float8_e4m3fn)) == msa.Q_FP8_E4M3
+    with pytest.raises(ValueError):
+        msa._q_dtype_of(torch.empty(1, dtype=torch.float16))
+    assert msa._kv_dtype_of(torch.empty(1, dtype=torch.float8_e5m2)) == msa.KV_FP8_E5M2
+    assert msa._kv_dtype_of(torch.empty(1, dtype=torch.uint8), msa.KV_FP8_E5M2) == \
+        msa.KV_FP8_E5M2
+    with pytest.raises(ValueError, match="does not match"):
+        msa._kv_dtype_of(torch.empty(1, dtype=torch.float8_e4m3fn), msa.KV_FP8_E5M2)
