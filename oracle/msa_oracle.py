@@ -21,6 +21,13 @@ fusion or reordering:
 * ``select_topk`` -- top-k blocks per (token, kv head) by score, ties to the
   lower block index, padded with -1 (same PR, selector; tie rule from the
   full-decode-step workload statement).
+* ``sparse_prefill`` -- the same attend for ragged prefill chunks: request r
+  owns token rows ``cu_seqlens_q[r] .. cu_seqlens_q[r+1]-1`` and its local
+  token i sits at ``context_lens[r] + i`` (vLLM sparse-attention page,
+  ``MiniMaxM3SparsePrefillMetadata`` and the prefill call of
+  ``MiniMaxM3SparseTritonImpl.forward``; the test page's prefill test builds
+  ``context_lens = seq_lens - q_lens`` and selects every visible page up to
+  ``(seq_len - q_len + local_q) // 128``).
 
 Readings taken where the pages leave a step open (each is also listed in the
 design notes):
@@ -51,6 +58,8 @@ design notes):
    q_scale_float, ...)``; the test file compares it with the bf16 path fed
    ``query_fp8.to(bfloat16) * q_scale``).  A bf16 q is multiplied by
    ``q_scale`` too (1 by default).
+10. Prefill token rows at or past ``cu_seqlens_q[-1]`` are padding rows
+    (zeros); a request with ``q_len = 0`` owns no row.
 
 Pins: every function here is checked in ``tests/test_oracle_pins.py`` against
 something other than itself (torch's fp8/bf16 casts, dense causal attention
@@ -234,6 +243,57 @@ def sparse_decode(q_bits, kv, kv_dtype, k_scale, v_scale, block_table, seq_lens,
             continue
         r, loc = divmod(int(t), dql)
         pos = token_position(seq_lens[r], dql, loc)
+        gathered = {}
+        for j in range(hq):
+            h = kv_head_of(j, group)
+            if h not in gathered:
+                gathered[h] = gather_live(kv, kv_dtype, k_scale, v_scale,
+                                          block_table[r], pos, h, topk[t, h, :])
+            k, v = gathered[h]
+            if k is None:
+                continue
+            qv = decode_query(q_bits[t, j], q_dtype, q_scale)
+            out[i, j] = softmax_attend(qv, k, v, sm_scale)
+    return out
+
+
+def prefill_request_of(cu_seqlens_q, t: int):
+    """The request whose row range [cu[r], cu[r+1]) holds token row t, or
+    None for a padding row."""
+    cu = [int(x) for x in cu_seqlens_q]
+    for r in range(len(cu) - 1):
+        if cu[r] <= t < cu[r + 1]:
+            return r
+    return None
+
+
+def prefill_position(context_len: int, row_start: int, t: int) -> int:
+    """Absolute position of prefill token row t of a request whose rows start
+    at ``row_start`` after ``context_len`` cached tokens."""
+    return int(context_len) + int(t) - int(row_start)
+
+
+def sparse_prefill(q_bits, kv, kv_dtype, k_scale, v_scale, block_table, cu_seqlens_q,
+                   context_lens, topk, num_kv_heads, sm_scale, rows=None,
+                   q_dtype="bf16", q_scale=1.0):
+    """Block-sparse GQA attend over ragged prefill chunks, float64.
+
+    Token row t of request r (``cu_seqlens_q[r] <= t < cu_seqlens_q[r+1]``)
+    sits at ``pos = context_lens[r] + t - cu_seqlens_q[r]`` and attends the
+    keys 0..pos of its selected blocks; everything else is as in
+    ``sparse_decode``.  Returns float64 [len(rows), Hq, 128].
+    """
+    q_bits = np.asarray(q_bits)
+    num_rows, hq, d = q_bits.shape
+    assert d == HEAD_DIM and hq % num_kv_heads == 0
+    group = hq // num_kv_heads
+    row_list = range(num_rows) if rows is None else list(rows)
+    out = np.zeros((len(row_list), hq, HEAD_DIM), dtype=np.float64)
+    for i, t in enumerate(row_list):
+        r = prefill_request_of(cu_seqlens_q, int(t))
+        if r is None:
+            continue
+        pos = prefill_position(context_lens[r], cu_seqlens_q[r], t)
         gathered = {}
         for j in range(hq):
             h = kv_head_of(j, group)

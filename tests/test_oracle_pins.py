@@ -623,3 +623,96 @@ def test_planted_selector_mistake_is_caught():
     cand = [b for b in range(len(s)) if s[b] > -math.inf]
     cand.sort(key=lambda b: (-s[b], -b))
     assert cand[: g["k"]] != g["expected"]
+
+
+# ---------------------------------------------------------------------------
+# prefill (ragged query chunks over a cached context)
+# ---------------------------------------------------------------------------
+
+def dense_prefill_reference(case: gen.PrefillCase) -> np.ndarray:
+    """Causal GQA attention of each request's prefill chunk over its whole
+    un-paged sequence via SDPA in float64: local token i sees keys 0..ctx+i."""
+    hq, hkv = case.num_q_heads, case.num_kv_heads
+    g = hq // hkv
+    vals = torch_values(case.kv, case.kv_dtype)
+    q = torch_q(case.q, case.q_dtype, case.q_scale)
+    out = torch.zeros(case.num_token_rows, hq, 128, dtype=torch.float64)
+    for r in range(case.batch):
+        s, ql, c0 = int(case.seq_lens[r]), int(case.q_lens[r]), int(case.cu_seqlens_q[r])
+        if ql == 0:
+            continue
+        n = gen.pages_for(s)
+        pages = torch.from_numpy(case.block_table[r, :n].astype(np.int64))
+        seqkv = vals[pages].permute(1, 0, 2, 3).reshape(hkv, n * 128, 256)[:, :s]
+        k = (seqkv[..., :128] * case.k_scale).repeat_interleave(g, dim=0)
+        v = (seqkv[..., 128:] * case.v_scale).repeat_interleave(g, dim=0)
+        qh = q[c0:c0 + ql].permute(1, 0, 2)
+        pos = int(case.context_lens[r]) + torch.arange(ql)
+        mask = torch.arange(s)[None, :] <= pos[:, None]
+        o = torch.nn.functional.scaled_dot_product_attention(
+            qh, k, v, attn_mask=mask, scale=case.sm_scale)
+        out[c0:c0 + ql] = o.permute(1, 0, 2)
+    return out.numpy()
+
+
+def run_prefill_oracle(case: gen.PrefillCase, **over):
+    kw = dict(q_bits=case.q, kv=case.kv, kv_dtype=case.kv_dtype, k_scale=case.k_scale,
+              v_scale=case.v_scale, block_table=case.block_table,
+              cu_seqlens_q=case.cu_seqlens_q, context_lens=case.context_lens, topk=case.topk,
+              num_kv_heads=case.num_kv_heads, sm_scale=case.sm_scale, q_dtype=case.q_dtype,
+              q_scale=case.q_scale)
+    kw.update(over)
+    return om.sparse_prefill(**kw)
+
+
+def _prefill_pin_error(case):
+    return float(np.max(np.abs(run_prefill_oracle(case) - dense_prefill_reference(case))))
+
+
+@pytest.mark.parametrize("heads", [(8, 2), (16, 1)])
+@pytest.mark.parametrize("fmt", [(gen.KV_FP8, gen.Q_BF16, 1.0), (gen.KV_FP8, gen.Q_FP8, 0.5),
+                                 (gen.KV_BF16, gen.Q_BF16, 1.0)])
+def test_prefill_dense_equivalence_test_page_shape(heads, fmt):
+    """The test page's prefill shape: q_lens (300, 128, 77) over seq_lens
+    (300, 640, 1100), every causally visible page selected."""
+    kv_dtype, q_dtype, q_scale = fmt
+    case = gen.make_prefill_case(31, [300, 128, 77], [300, 640, 1100], heads[0], heads[1],
+                                 kv_dtype=kv_dtype, q_dtype=q_dtype, q_scale=q_scale)
+    case.k_scale, case.v_scale = 0.5, 2.0
+    assert _prefill_pin_error(case) < 1e-12
+
+
+def test_prefill_chunks_with_empty_request_and_padding():
+    case = gen.make_prefill_case(32, [5, 0, 64, 1], [700, 300, 129, 1], 8, 2, pad_rows=3)
+    assert _prefill_pin_error(case) < 1e-12
+    out = run_prefill_oracle(case)
+    assert np.all(out[case.real_rows:] == 0.0)
+    assert om.prefill_request_of(case.cu_seqlens_q, 5) == 2      # request 1 owns no row
+
+
+def test_prefill_with_uniform_chunks_is_decode():
+    """cu = r*dql and context = seq - dql make the prefill definition the
+    decode one: the two functions agree exactly."""
+    dcase = gen.make_random_case(seed=33, batch=3, dql=3, num_q_heads=8, num_kv_heads=2,
+                                 topk_k=8, seq_lo=129, seq_hi=900, pad_rows=2)
+    cu = np.arange(dcase.batch + 1, dtype=np.int32) * dcase.dql
+    ctx = dcase.seq_lens - dcase.dql
+    a = run_oracle(dcase)
+    b = om.sparse_prefill(dcase.q, dcase.kv, dcase.kv_dtype, dcase.k_scale, dcase.v_scale,
+                          dcase.block_table, cu, ctx, dcase.topk, dcase.num_kv_heads,
+                          dcase.sm_scale)
+    assert np.array_equal(a, b)
+
+
+def test_planted_prefill_mistakes_are_caught(monkeypatch):
+    case = gen.make_prefill_case(34, [40, 9], [300, 200], 8, 2)
+    assert _prefill_pin_error(case) < 1e-12
+    monkeypatch.setattr(om, "prefill_position", lambda c, s, t: int(c) + int(t) - int(s) + 1)
+    with np.errstate(invalid="ignore"):
+        assert not _prefill_pin_error(case) < 1e-12
+    monkeypatch.undo()
+    real = om.prefill_request_of
+    monkeypatch.setattr(om, "prefill_request_of",
+                        lambda cu, t: (lambda r: None if r is None else max(0, r - 1))(real(cu, t)))
+    with np.errstate(invalid="ignore"):
+        assert not _prefill_pin_error(case) < 1e-12

@@ -504,6 +504,95 @@ def make_random_case(seed: int, batch: int, dql: int, num_q_heads: int,
                       q_dtype=q_dtype, q_scale=q_scale, max_blocks=int(bt.shape[1]))
 
 
+@dataclass
+class PrefillCase:
+    """One ragged prefill step: request r owns q rows cu[r]..cu[r+1]-1 and its
+    local token i sits at context_lens[r] + i."""
+
+    name: str
+    seed: int
+    q_lens: np.ndarray             # int32 [batch]
+    seq_lens: np.ndarray           # int32 [batch], context + q_len
+    context_lens: np.ndarray       # int32 [batch]
+    cu_seqlens_q: np.ndarray       # int32 [batch + 1]
+    num_token_rows: int            # >= cu[-1]; rows past it are padding
+    num_q_heads: int
+    num_kv_heads: int
+    topk_k: int
+    kv_dtype: str
+    block_table: np.ndarray
+    kv: np.ndarray
+    q: np.ndarray
+    topk: np.ndarray               # int32 [rows, Hkv, k]
+    sm_scale: float = HEAD_DIM ** -0.5
+    k_scale: float = 1.0
+    v_scale: float = 1.0
+    q_dtype: str = Q_BF16
+    q_scale: float = 1.0
+    max_blocks: int = 0
+    replicas: list = field(default_factory=list)   # [(q, topk)] extra sets
+
+    @property
+    def batch(self) -> int:
+        return int(len(self.q_lens))
+
+    @property
+    def real_rows(self) -> int:
+        return int(self.cu_seqlens_q[-1])
+
+    def positions(self) -> np.ndarray:
+        """pos[t] for the real token rows."""
+        r = np.repeat(np.arange(self.batch), self.q_lens)
+        local = np.arange(self.real_rows) - self.cu_seqlens_q[r]
+        return self.context_lens[r].astype(np.int64) + local
+
+
+def make_prefill_case(seed: int, q_lens, seq_lens, num_q_heads: int, num_kv_heads: int,
+                      topk_k: int = 16, kv_dtype: str = KV_FP8, q_dtype: str = Q_BF16,
+                      q_scale: float = 1.0, rule: str = "every_visible", std: float = 0.25,
+                      pad_rows: int = 0, replicas: int = 0, poison: bool = True,
+                      name: str = "") -> PrefillCase:
+    """A seeded ragged prefill step.  rule "every_visible" selects blocks
+    0..last for each token (the test page's prefill test, which needs
+    last < topk_k); "zipf" picks topk_k distinct blocks per (token, kv head)
+    with the recent bias, always including the token's own block."""
+    rng = np.random.default_rng(seed)
+    q_lens = np.asarray(q_lens, dtype=np.int32)
+    seq = np.asarray(seq_lens, dtype=np.int32)
+    ctx = (seq - q_lens).astype(np.int32)
+    assert np.all(ctx >= 0)
+    cu = np.zeros(len(q_lens) + 1, dtype=np.int32)
+    cu[1:] = np.cumsum(q_lens)
+    bt, total, spare = paged_layout(rng, seq, spare_pages=1)
+    kv = make_pool(rng, total, num_kv_heads, kv_dtype, std)
+    if poison:
+        fill_pages(kv, spare, kv_dtype)
+        poison_tail_slots(kv, bt, seq, kv_dtype)
+    rows = int(cu[-1]) + pad_rows
+
+    def one(rng_):
+        q = make_q(rng_, rows, num_q_heads, q_dtype=q_dtype, q_scale=q_scale)
+        topk = np.full((rows, num_kv_heads, topk_k), -1, dtype=np.int32)
+        for r in range(len(q_lens)):
+            for i in range(int(q_lens[r])):
+                t = int(cu[r]) + i
+                last = last_visible_block(int(ctx[r]) + i)
+                if rule == "every_visible":
+                    assert last < topk_k
+                    topk[t, :, :last + 1] = np.arange(last + 1, dtype=np.int32)
+                else:
+                    for h in range(num_kv_heads):
+                        topk[t, h] = pad_row(pick_zipf_recent(rng_, last, topk_k), topk_k)
+        return q, topk
+
+    q, topk = one(rng)
+    reps = [one(rng) for _ in range(replicas)]
+    return PrefillCase(name or f"prefill_s{seed}", seed, q_lens, seq, ctx, cu, rows,
+                       num_q_heads, num_kv_heads, topk_k, kv_dtype, bt, kv, q, topk,
+                       q_dtype=q_dtype, q_scale=q_scale, max_blocks=int(bt.shape[1]),
+                       replicas=reps)
+
+
 def make_scores(seed: int, num_kv_heads: int, max_blocks: int, rows: int, seq_lens,
                 dql: int, tie_frac: float = 0.0) -> np.ndarray:
     """fp32 score buffer [Hkv, max_blocks, rows] for selector tests: N(0,1)
