@@ -40,7 +40,8 @@ if ROOT not in sys.path:
 METRIC = "decode tokens/s and effective KV GB/s (% HBM peak), sparse GQA attend, 1 GPU"
 HBM_PEAK_GBS = 8000.0
 DEFAULT_CONFIG = "c2_tp4_fp8"
-OTHER_CONFIGS = ("c3_tp1_fp8", "c4_spec_ragged", "c2_tp4_fp8q", "c2_tp4_e5m2")
+OTHER_CONFIGS = ("c3_tp1_fp8", "c4_spec_ragged", "c2_tp4_fp8q", "c2_tp4_e5m2",
+                 "pf1_chunked_prefill")
 FULL_STEP_CONFIG = "c5_full_step"
 # rocprofv3 counter summaries, each valid for the kernel sources it was taken on
 TRAFFIC_FILES = {"attend": os.path.join(ROOT, "profiles", "attend_traffic.json"),
@@ -67,6 +68,9 @@ CONFIG_TEXT = {
     "c2_tp4_fp8q": "c2 with an fp8 e4m3 query (q_scale 0.5) over the fp8 e4m3 cache: "
                    "fp8 x fp8 MFMA for QK^T",
     "c2_tp4_e5m2": "c2 with a bf16 query over an fp8 e5m2 cache",
+    "pf1_chunked_prefill": "chunked prefill: 4 requests x 1024-token chunks after a cached "
+                           "context of U[16384,65536], 64/4 heads, fp8, top-16 per (token, "
+                           "kv head), recent-biased",
 }
 
 
@@ -90,8 +94,12 @@ def step_bytes(case, q, topk):
     row_bytes = 2 * 128 * e
     real = case.real_rows
     t = np.arange(real)
-    r = t // case.dql
-    pos = case.seq_lens[r].astype(np.int64) - case.dql + (t % case.dql)
+    if hasattr(case, "cu_seqlens_q"):       # ragged prefill rows
+        r = np.repeat(np.arange(case.batch), case.q_lens)
+        pos = case.positions()
+    else:
+        r = t // case.dql
+        pos = case.seq_lens[r].astype(np.int64) - case.dql + (t % case.dql)
     b = topk[:real].astype(np.int64)                       # [T, Hkv, k]
     start = b * 128
     live = (b >= 0) & (start <= pos[:, None, None]) & (b < case.block_table.shape[1])
@@ -168,14 +176,18 @@ class DeviceSet:
         import block_sparse_gqa_decode_amd as msa
 
         self.case = case
+        self.prefill = hasattr(case, "cu_seqlens_q")
         host = _host_kv(case)
-        nb = case.num_blocks
+        nb = int(case.kv.shape[0])
         self.kv = torch.empty((replicas * nb,) + tuple(host.shape[1:]), dtype=host.dtype,
                               device=dev)
         self.kv[:nb].copy_(host)
         for i in range(1, replicas):
             self.kv[i * nb:(i + 1) * nb].copy_(self.kv[:nb])
         self.seq_lens = torch.from_numpy(case.seq_lens).to(dev)
+        if self.prefill:
+            self.cu = torch.from_numpy(case.cu_seqlens_q).to(dev)
+            self.ctx = torch.from_numpy(case.context_lens).to(dev)
         sets = [(case.q, case.topk)] + list(case.replicas)
         assert len(sets) >= replicas, "not enough replicas generated"
         self.steps = []
@@ -189,21 +201,36 @@ class DeviceSet:
             out = torch.empty(tuple(q.shape), dtype=torch.bfloat16, device=dev)
             self.steps.append((q, bt, topk, out))
             self.bytes.append(step_bytes(case, qh, tk))
-        self.plan = msa.msa_sparse_decode_plan(
-            case.batch, case.dql, num_q_heads=case.num_q_heads,
-            num_kv_heads=case.num_kv_heads, page_table_stride=case.block_table.shape[1],
-            topk_blocks=case.topk_k, kv_dtype=_kv_code(case), q_dtype=_q_code(case),
-            num_token_rows=case.num_token_rows, num_splits=splits, device=dev)
+        if self.prefill:
+            self.plan = msa.msa_sparse_prefill_plan(
+                case.batch, case.num_token_rows, num_q_heads=case.num_q_heads,
+                num_kv_heads=case.num_kv_heads, page_table_stride=case.block_table.shape[1],
+                topk_blocks=case.topk_k, kv_dtype=_kv_code(case), q_dtype=_q_code(case),
+                num_splits=splits, device=dev)
+        else:
+            self.plan = msa.msa_sparse_decode_plan(
+                case.batch, case.dql, num_q_heads=case.num_q_heads,
+                num_kv_heads=case.num_kv_heads, page_table_stride=case.block_table.shape[1],
+                topk_blocks=case.topk_k, kv_dtype=_kv_code(case), q_dtype=_q_code(case),
+                num_token_rows=case.num_token_rows, num_splits=splits, device=dev)
         self.msa = msa
 
     def run_step(self, i):
         q, bt, topk, out = self.steps[i]
         c = self.case
+        if self.prefill:
+            self.msa.msa_sparse_prefill_run(self.plan, q, self.kv, bt, self.cu, self.ctx, topk,
+                                            out, sm_scale=c.sm_scale, k_scale=c.k_scale,
+                                            v_scale=c.v_scale, q_scale=c.q_scale)
+            return
         self.msa.msa_sparse_decode_run(self.plan, q, self.kv, bt, self.seq_lens, topk, out,
                                        sm_scale=c.sm_scale, k_scale=c.k_scale,
                                        v_scale=c.v_scale, q_scale=c.q_scale)
 
     def run_attend(self, i):
+        if self.prefill:   # one launch unless split; the step is the attend
+            self.run_step(i)
+            return
         q, bt, topk, out = self.steps[i]
         c = self.case
         self.msa.msa_sparse_decode_attend(self.plan, q, self.kv, bt, self.seq_lens, topk, out,
@@ -220,7 +247,10 @@ def time_config(name, steps, warmup, replicas, splits, dev, verbose=True):
     from workloads import gen
 
     t0 = time.time()
-    case = gen.make_config(name, replicas=replicas - 1)
+    if name in gen.PREFILL_CONFIG_NAMES:
+        case = gen.make_prefill_config(name, replicas=replicas - 1)
+    else:
+        case = gen.make_config(name, replicas=replicas - 1)
     ds = DeviceSet(case, replicas, splits, dev)
     if verbose:
         print(f"[bench] {name}: generated + uploaded in {time.time() - t0:.1f}s "

@@ -12,6 +12,8 @@ Entry points carry the C names:
   vLLM API page ``vllm.models.minimax_m3.nvidia.msa_cutlass_sparse_decode``
   (``MSACutlassDecodePlanCache.prepare``).
 * ``msa_sparse_decode_run``   -- one sparse decode step (the attend).
+* ``msa_sparse_prefill_plan`` / ``msa_sparse_prefill_run`` -- the same attend
+  over ragged prefill chunks (``cu_seqlens_q``, ``context_lens``).
 * ``msa_block_score_topk``    -- indexer block-max scores, then the top-k.
 * ``msa_topk_select``         -- the top-k selector alone.
 * ``msa_fp8_e4m3_to_bf16`` / ``msa_fp8_e5m2_to_bf16`` -- the in-register fp8
@@ -36,7 +38,8 @@ import torch
 __all__ = [
     "MsaError", "MsaInvalidArgument", "MsaUnsupported", "DecodePlan", "PlanCache",
     "msa_sparse_decode_plan", "msa_sparse_decode_run", "msa_sparse_decode_attend",
-    "msa_sparse_decode_merge", "msa_block_score_topk",
+    "msa_sparse_decode_merge", "msa_block_score_topk", "msa_sparse_prefill_plan",
+    "msa_sparse_prefill_run",
     "msa_topk_select", "msa_fp8_e4m3_to_bf16", "msa_fp8_e5m2_to_bf16", "library_path",
     "load_library", "KV_BF16", "KV_FP8_E4M3", "KV_FP8_E5M2", "Q_BF16", "Q_FP8_E4M3",
     "PAGE_SIZE", "HEAD_DIM", "ABI_VERSION",
@@ -82,6 +85,13 @@ class _Shape(ctypes.Structure):
         "kv_dtype", "num_splits", "q_dtype")]
 
 
+class _PrefillShape(ctypes.Structure):
+    _fields_ = [(name, ctypes.c_int32) for name in (
+        "num_prefills", "num_token_rows", "page_table_stride", "num_q_heads",
+        "num_kv_heads", "page_size", "head_dim", "topk_blocks", "kv_dtype", "q_dtype",
+        "num_splits")]
+
+
 _I64x4 = ctypes.c_int64 * 4
 _I64x3 = ctypes.c_int64 * 3
 _LIB = None
@@ -115,6 +125,10 @@ def load_library():
         "msa_sparse_decode_attend": (i32, [vp, vp, vp, pi64, i64, f32, f32, f32, vp, vp,
                                            vp, pi64, vp, f32, vp]),
         "msa_sparse_decode_merge": (i32, [vp, vp, f32, vp]),
+        "msa_sparse_prefill_plan": (i32, [ctypes.POINTER(_PrefillShape), ctypes.c_int,
+                                          ctypes.POINTER(vp)]),
+        "msa_sparse_prefill_run": (i32, [vp, vp, vp, pi64, i64, f32, f32, f32, vp, vp, vp,
+                                         vp, pi64, vp, f32, vp]),
         "msa_block_score_topk": (i32, [ctypes.POINTER(_Shape), vp, vp, pi64, i64, f32, f32,
                                        vp, vp, i32, vp, pi64, vp, i32, vp]),
         "msa_topk_select": (i32, [vp, pi64, i32, i32, i32, vp, i32, vp]),
@@ -222,7 +236,8 @@ class DecodePlan:
         _check(load_library().msa_sparse_decode_plan_info(
             self._handle, ctypes.byref(splits), ctypes.byref(arena), ctypes.byref(shape)))
         self.batch = shape.batch
-        self.decode_query_len = shape.decode_query_len
+        self.decode_query_len = shape.decode_query_len   # 0 for a prefill plan
+        self.prefill = shape.decode_query_len == 0
         self.num_token_rows = shape.num_token_rows
         self.page_table_stride = shape.page_table_stride
         self.num_q_heads = shape.num_q_heads
@@ -271,13 +286,71 @@ def msa_sparse_decode_plan(batch: int, decode_query_len: int, *, num_q_heads: in
     return DecodePlan(handle.value, int(dev))
 
 
-def _run_args(plan, q, kv_cache, block_table, seq_lens, topk, out):
+def _device_index(device) -> int:
+    if device is None:
+        return torch.cuda.current_device() if torch.cuda.is_available() else 0
+    if isinstance(device, int):
+        return device
+    dev = torch.device(device).index
+    return torch.cuda.current_device() if dev is None else dev
+
+
+def msa_sparse_prefill_plan(num_prefills: int, num_token_rows: int, *, num_q_heads: int,
+                            num_kv_heads: int, page_table_stride: int, topk_blocks: int,
+                            kv_dtype: int, q_dtype: int = Q_BF16, num_splits: int = 0,
+                            page_size: int = PAGE_SIZE, head_dim: int = HEAD_DIM,
+                            device=None) -> DecodePlan:
+    """A plan for ragged prefill chunks over ``num_token_rows`` q rows."""
+    lib = load_library()
+    shape = _PrefillShape(num_prefills, num_token_rows, page_table_stride, num_q_heads,
+                          num_kv_heads, page_size, head_dim, topk_blocks, kv_dtype, q_dtype,
+                          num_splits)
+    dev = _device_index(device)
+    handle = ctypes.c_void_p()
+    _check(lib.msa_sparse_prefill_plan(ctypes.byref(shape), int(dev), ctypes.byref(handle)))
+    return DecodePlan(handle.value, int(dev))
+
+
+def msa_sparse_prefill_run(plan: DecodePlan, q: torch.Tensor, kv_cache: torch.Tensor,
+                           block_table: torch.Tensor, cu_seqlens_q: torch.Tensor,
+                           context_lens: torch.Tensor, topk: torch.Tensor, out: torch.Tensor,
+                           *, sm_scale: float, k_scale: float = 1.0, v_scale: float = 1.0,
+                           q_scale: float = 1.0, stream=None) -> None:
+    """out[t, j] for ragged prefill chunks: row t of request r (cu[r] <= t <
+    cu[r+1]) attends as a decode token at context_lens[r] + t - cu[r]."""
+    if not plan.prefill:
+        raise ValueError("msa_sparse_prefill_run needs a prefill plan")
+    n = plan.batch
+    if (cu_seqlens_q.dtype != torch.int32 or not cu_seqlens_q.is_contiguous()
+            or tuple(cu_seqlens_q.shape) != (n + 1,)):
+        raise ValueError(f"cu_seqlens_q must be contiguous int32 [{n + 1}]")
+    if (context_lens.dtype != torch.int32 or not context_lens.is_contiguous()
+            or tuple(context_lens.shape) != (n,)):
+        raise ValueError(f"context_lens must be contiguous int32 [{n}]")
+    for name, t in (("cu_seqlens_q", cu_seqlens_q), ("context_lens", context_lens)):
+        if t.device != block_table.device:
+            raise ValueError(f"{name} is not on the block table device")
+    head = _run_args(plan, q, kv_cache, block_table, context_lens, topk, out, tables=False)
+    if (block_table.device.type != "cuda" or block_table.dtype != torch.int32
+            or not block_table.is_contiguous() or block_table.dim() != 2
+            or block_table.shape[0] != n):
+        raise ValueError("MSA sparse prefill requires a contiguous device int32 block "
+                         "table with one row per request")
+    _check(load_library().msa_sparse_prefill_run(
+        *head, float(q_scale), float(k_scale), float(v_scale), block_table.data_ptr(),
+        cu_seqlens_q.data_ptr(), context_lens.data_ptr(), topk.data_ptr(),
+        _I64x3(*topk.stride()), out.data_ptr(), float(sm_scale),
+        _stream_handle(stream, q.device)))
+
+
+def _run_args(plan, q, kv_cache, block_table, seq_lens, topk, out, tables=True):
     rows = plan.num_token_rows
     _check_q(q, "q", rows, plan.num_q_heads, plan.q_dtype)
     _check_q(out, "out", rows, plan.num_q_heads)
     _check_kv(kv_cache, plan.num_kv_heads)
     _kv_dtype_of(kv_cache, plan.kv_dtype)
-    _check_tables(block_table, seq_lens, plan.batch)
+    if tables:
+        _check_tables(block_table, seq_lens, plan.batch)
     if block_table.stride(0) != plan.page_table_stride:
         raise ValueError("block_table row stride does not match the plan")
     if (topk.dtype != torch.int32 or topk.dim() != 3
@@ -292,12 +365,18 @@ def _run_args(plan, q, kv_cache, block_table, seq_lens, topk, out):
             kv_cache.shape[0])
 
 
+def _require_decode_plan(plan: DecodePlan):
+    if plan.prefill:
+        raise ValueError("a prefill plan runs through msa_sparse_prefill_run")
+
+
 def msa_sparse_decode_run(plan: DecodePlan, q: torch.Tensor, kv_cache: torch.Tensor,
                           block_table: torch.Tensor, seq_lens: torch.Tensor,
                           topk: torch.Tensor, out: torch.Tensor, *, sm_scale: float,
                           k_scale: float = 1.0, v_scale: float = 1.0, q_scale: float = 1.0,
                           stream=None) -> None:
     """out[t, j] = sparse causal attention of q[t, j] over the selected pages."""
+    _require_decode_plan(plan)
     head = _run_args(plan, q, kv_cache, block_table, seq_lens, topk, out)
     _check(load_library().msa_sparse_decode_run(
         *head, float(q_scale), float(k_scale), float(v_scale), block_table.data_ptr(), seq_lens.data_ptr(),
@@ -311,6 +390,7 @@ def msa_sparse_decode_attend(plan: DecodePlan, q: torch.Tensor, kv_cache: torch.
                              k_scale: float = 1.0, v_scale: float = 1.0,
                              q_scale: float = 1.0, stream=None) -> None:
     """First launch of a step (see ``msa_sparse_decode_run``)."""
+    _require_decode_plan(plan)
     head = _run_args(plan, q, kv_cache, block_table, seq_lens, topk, out)
     _check(load_library().msa_sparse_decode_attend(
         *head, float(q_scale), float(k_scale), float(v_scale), block_table.data_ptr(), seq_lens.data_ptr(),

@@ -18,7 +18,8 @@
 #include "msa_sparse_decode.h"
 
 struct msa_plan_s {
-  msa_decode_shape shape;
+  msa_decode_shape shape;   // for a prefill plan: decode_query_len = 0
+  bool prefill;
   int device;
   int32_t splits;
   int32_t real_rows;
@@ -176,11 +177,56 @@ int32_t msa_abi_version(void) { return MSA_ABI_VERSION; }
 
 const char* msa_last_error(void) { return g_last_error.c_str(); }
 
+static msa_status make_plan(const msa_decode_shape* shape, bool prefill, int32_t real_rows,
+                            int device, msa_plan* plan_out);
+
 msa_status msa_sparse_decode_plan(const msa_decode_shape* shape, int device, msa_plan* plan_out) {
   if (plan_out == nullptr) return fail(MSA_ERR_INVALID_ARG, "plan_out is NULL");
   *plan_out = nullptr;
   msa_status st = check_common_shape(shape);
   if (st != MSA_OK) return st;
+  return make_plan(shape, false, shape->batch * shape->decode_query_len, device, plan_out);
+}
+
+msa_status msa_sparse_prefill_plan(const msa_prefill_shape* pshape, int device,
+                                   msa_plan* plan_out) {
+  if (plan_out == nullptr) return fail(MSA_ERR_INVALID_ARG, "plan_out is NULL");
+  *plan_out = nullptr;
+  if (pshape == nullptr) return fail(MSA_ERR_INVALID_ARG, "shape is NULL");
+  if (pshape->num_prefills < 1)
+    return fail(MSA_ERR_INVALID_ARG, "num_prefills must be >= 1 (got %d)", pshape->num_prefills);
+  if (pshape->num_prefills > msa::kMaxPrefills)
+    return fail(MSA_ERR_UNSUPPORTED, "num_prefills exceeds %d", msa::kMaxPrefills);
+  if (pshape->num_token_rows < 1)
+    return fail(MSA_ERR_INVALID_ARG, "num_token_rows must be >= 1 (got %d)",
+                pshape->num_token_rows);
+  // The shared shape checks, with a placeholder query length: every row is
+  // potentially real until cu_seqlens_q says otherwise on the device.
+  msa_decode_shape s{};
+  s.batch = pshape->num_prefills;
+  s.decode_query_len = 1;
+  s.num_token_rows = pshape->num_token_rows;
+  s.page_table_stride = pshape->page_table_stride;
+  s.num_q_heads = pshape->num_q_heads;
+  s.num_kv_heads = pshape->num_kv_heads;
+  s.page_size = pshape->page_size;
+  s.head_dim = pshape->head_dim;
+  s.topk_blocks = pshape->topk_blocks;
+  s.kv_dtype = pshape->kv_dtype;
+  s.num_splits = pshape->num_splits;
+  s.q_dtype = pshape->q_dtype;
+  if (s.num_token_rows > (1 << 24)) return fail(MSA_ERR_UNSUPPORTED, "num_token_rows exceeds 2^24");
+  const int32_t keep_rows = s.num_token_rows;
+  s.num_token_rows = 0;  // batch*1 may exceed the rows; checked above instead
+  msa_status st = check_common_shape(&s);
+  if (st != MSA_OK) return st;
+  s.num_token_rows = keep_rows;
+  s.decode_query_len = 0;
+  return make_plan(&s, true, keep_rows, device, plan_out);
+}
+
+static msa_status make_plan(const msa_decode_shape* shape, bool prefill, int32_t real_rows,
+                            int device, msa_plan* plan_out) {
   if (shape->topk_blocks < 1)
     return fail(MSA_ERR_INVALID_ARG, "topk_blocks must be >= 1 (got %d)", shape->topk_blocks);
   if (shape->topk_blocks > msa::kMaxTopk)
@@ -191,7 +237,6 @@ msa_status msa_sparse_decode_plan(const msa_decode_shape* shape, int device, msa
                 msa::kMaxSplits, shape->num_splits);
   if (device < 0) return fail(MSA_ERR_INVALID_ARG, "device must be >= 0 (got %d)", device);
 
-  const int32_t real_rows = shape->batch * shape->decode_query_len;
   const int32_t num_rows = shape->num_token_rows ? shape->num_token_rows : real_rows;
   const int32_t splits = choose_splits(shape, real_rows);
   const int64_t units = (int64_t)num_rows * shape->num_kv_heads;
@@ -205,6 +250,7 @@ msa_status msa_sparse_decode_plan(const msa_decode_shape* shape, int device, msa
   msa_plan plan = new (std::nothrow) msa_plan_s();
   if (plan == nullptr) return fail(MSA_ERR_OUT_OF_MEMORY, "host allocation failed");
   plan->shape = *shape;
+  plan->prefill = prefill;
   plan->shape.num_token_rows = num_rows;
   plan->shape.num_splits = splits;
   plan->device = device;
@@ -262,19 +308,26 @@ msa_status msa_sparse_decode_plan_info(msa_plan plan, int32_t* num_splits, int64
   return ok();
 }
 
+// seq_lens is the decode position source; cu_q / ctx the prefill one (a
+// prefill plan passes seq_lens = NULL).
 static msa_status run_phases(msa_plan plan, const void* q, const void* kv_cache,
                              const int64_t kv_strides[4], int64_t num_kv_blocks, float q_scale,
                              float k_scale, float v_scale, const int32_t* block_table,
-                             const int32_t* seq_lens, const int32_t* topk,
-                             const int64_t topk_strides[3], void* out, float sm_scale,
-                             void* stream, bool merge) {
+                             const int32_t* seq_lens, const int32_t* cu_q, const int32_t* ctx,
+                             const int32_t* topk, const int64_t topk_strides[3], void* out,
+                             float sm_scale, void* stream, bool merge) {
   if (plan == nullptr) return fail(MSA_ERR_INVALID_ARG, "plan is NULL");
   const msa_decode_shape& s = plan->shape;
   if (q == nullptr || out == nullptr) return fail(MSA_ERR_INVALID_ARG, "q and out must be non-NULL");
   if (!aligned16(q) || !aligned16(out))
     return fail(MSA_ERR_INVALID_ARG, "q and out must be 16-byte aligned");
-  if (block_table == nullptr || seq_lens == nullptr || topk == nullptr)
+  if (plan->prefill) {
+    if (block_table == nullptr || cu_q == nullptr || ctx == nullptr || topk == nullptr)
+      return fail(MSA_ERR_INVALID_ARG,
+                  "block_table, cu_seqlens_q, context_lens and topk must be non-NULL");
+  } else if (block_table == nullptr || seq_lens == nullptr || topk == nullptr) {
     return fail(MSA_ERR_INVALID_ARG, "block_table, seq_lens and topk must be non-NULL");
+  }
   if (topk_strides == nullptr) return fail(MSA_ERR_INVALID_ARG, "topk_strides is NULL");
   for (int d = 0; d < 3; ++d)
     if (topk_strides[d] < 0) return fail(MSA_ERR_INVALID_ARG, "topk strides must be >= 0");
@@ -316,6 +369,13 @@ static msa_status run_phases(msa_plan plan, const void* q, const void* kv_cache,
   p.topk_k = s.topk_blocks;
   p.splits = plan->splits;
   p.num_units = plan->num_rows * s.num_kv_heads;
+  if (plan->prefill) {
+    p.cu_q = cu_q;
+    p.ctx_lens = ctx;
+    p.num_reqs = s.batch;
+    p.dql = 1;
+    p.real_rows = plan->num_rows;
+  }
 
   DeviceGuard guard;
   hipError_t e = guard.enter(plan->device);
@@ -336,8 +396,25 @@ msa_status msa_sparse_decode_run(msa_plan plan, const void* q, const void* kv_ca
                                  const int32_t* block_table, const int32_t* seq_lens,
                                  const int32_t* topk, const int64_t topk_strides[3], void* out,
                                  float sm_scale, void* stream) {
+  if (plan != nullptr && plan->prefill)
+    return fail(MSA_ERR_INVALID_ARG, "a prefill plan runs through msa_sparse_prefill_run");
   return run_phases(plan, q, kv_cache, kv_strides, num_kv_blocks, q_scale, k_scale, v_scale,
-                    block_table, seq_lens, topk, topk_strides, out, sm_scale, stream, true);
+                    block_table, seq_lens, nullptr, nullptr, topk, topk_strides, out, sm_scale,
+                    stream, true);
+}
+
+msa_status msa_sparse_prefill_run(msa_plan plan, const void* q, const void* kv_cache,
+                                  const int64_t kv_strides[4], int64_t num_kv_blocks,
+                                  float q_scale, float k_scale, float v_scale,
+                                  const int32_t* block_table, const int32_t* cu_seqlens_q,
+                                  const int32_t* context_lens, const int32_t* topk,
+                                  const int64_t topk_strides[3], void* out, float sm_scale,
+                                  void* stream) {
+  if (plan != nullptr && !plan->prefill)
+    return fail(MSA_ERR_INVALID_ARG, "a decode plan runs through msa_sparse_decode_run");
+  return run_phases(plan, q, kv_cache, kv_strides, num_kv_blocks, q_scale, k_scale, v_scale,
+                    block_table, nullptr, cu_seqlens_q, context_lens, topk, topk_strides, out,
+                    sm_scale, stream, true);
 }
 
 msa_status msa_sparse_decode_attend(msa_plan plan, const void* q, const void* kv_cache,
@@ -346,12 +423,17 @@ msa_status msa_sparse_decode_attend(msa_plan plan, const void* q, const void* kv
                                     const int32_t* block_table, const int32_t* seq_lens,
                                     const int32_t* topk, const int64_t topk_strides[3],
                                     void* out, float sm_scale, void* stream) {
+  if (plan != nullptr && plan->prefill)
+    return fail(MSA_ERR_INVALID_ARG, "a prefill plan runs through msa_sparse_prefill_run");
   return run_phases(plan, q, kv_cache, kv_strides, num_kv_blocks, q_scale, k_scale, v_scale,
-                    block_table, seq_lens, topk, topk_strides, out, sm_scale, stream, false);
+                    block_table, seq_lens, nullptr, nullptr, topk, topk_strides, out, sm_scale,
+                    stream, false);
 }
 
 msa_status msa_sparse_decode_merge(msa_plan plan, void* out, float v_scale, void* stream) {
   if (plan == nullptr) return fail(MSA_ERR_INVALID_ARG, "plan is NULL");
+  if (plan->prefill)
+    return fail(MSA_ERR_INVALID_ARG, "a prefill plan runs through msa_sparse_prefill_run");
   if (out == nullptr || !aligned16(out))
     return fail(MSA_ERR_INVALID_ARG, "out must be non-NULL and 16-byte aligned");
   if (!std::isfinite(v_scale)) return fail(MSA_ERR_INVALID_ARG, "scales must be finite");

@@ -7,6 +7,16 @@
 // _make_topk), with split-K over the selected blocks, fp32 partials and zeroed
 // padding rows (TensorRT-LLM PR #17171, flash-decoding commit).
 //
+// Decode and prefill share the kernel: a decode token row t belongs to
+// request t / dql at position seq_len - dql + t % dql (vLLM test file
+// test_minimax_m3_msa_cutlass_sparse_decode.py, _make_topk); a ragged prefill
+// row belongs to the request r with cu_seqlens_q[r] <= t < cu_seqlens_q[r+1]
+// (found by a wave-uniform binary search) at position context_lens[r] +
+// t - cu_seqlens_q[r] (vLLM API page
+// "vllm.models.minimax_m3.common.sparse_attention",
+// MiniMaxM3SparsePrefillMetadata and the prefill call of
+// MiniMaxM3SparseTritonImpl.forward).
+//
 // Work decomposition.  A unit is one (token row t, kv head h); its G q heads
 // are the 16 rows of one MFMA tile.  A workgroup of 4 wavefronts handles one
 // unit's share (split) of its live pages; wavefront w owns keys
@@ -70,6 +80,27 @@ constexpr int kDepth = 2;      // pages per wavefront in the register ring
 constexpr int kKeysPerWave = 32;
 constexpr int kOPad = 4;
 constexpr float kRescaleSlack = 8.0f;
+
+// The request of token row t and the token's position, or false for a
+// padding row.  Wave-uniform: t comes from the workgroup id.
+__device__ __forceinline__ bool locate_row(const AttendParams& p, int t, int& r, int& pos) {
+  if (p.cu_q == nullptr) {
+    if (t >= p.real_rows) return false;
+    r = t / p.dql;
+    pos = p.seq_lens[r] - p.dql + (t - r * p.dql);
+    return true;
+  }
+  if (t >= p.cu_q[p.num_reqs]) return false;
+  int lo = 0, hi = p.num_reqs - 1;  // the last r with cu_q[r] <= t
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (p.cu_q[mid] <= t) lo = mid;
+    else hi = mid - 1;
+  }
+  r = lo;
+  pos = p.ctx_lens[r] + (t - p.cu_q[r]);
+  return true;
+}
 
 template <bool kFp8>
 struct PageRegs;
@@ -313,7 +344,8 @@ __global__ __launch_bounds__(kThreads) void attend_kernel(AttendParams p) {
   const int rows = p.group;  // q heads of the unit = MFMA rows in use
   const int head0 = h * p.group;
 
-  if (t >= p.real_rows) {
+  int r = 0, pos = 0;
+  if (!locate_row(p, t, r, pos)) {
     // Padding row: exact zeros, written once.
     if (split == 0) {
       const int qr = tid >> 4;
@@ -325,10 +357,6 @@ __global__ __launch_bounds__(kThreads) void attend_kernel(AttendParams p) {
     }
     return;
   }
-
-  const int r = t / p.dql;
-  const int loc = t - r * p.dql;
-  const int pos = p.seq_lens[r] - p.dql + loc;
 
   // Resolve the top-k row into the ordered list of live pages.
   if (wave == 0) {
@@ -523,7 +551,8 @@ __global__ __launch_bounds__(256) void merge_kernel(AttendParams p) {
   const int t = unit / p.hkv;
   const int h = unit - t * p.hkv;
   const int qr = threadIdx.x >> 4;
-  if (t >= p.real_rows || qr >= p.group) return;
+  int r = 0, pos = 0;
+  if (!locate_row(p, t, r, pos) || qr >= p.group) return;
   const int64_t row = (int64_t)t * p.hq + h * p.group + qr;
   const int d0 = (threadIdx.x & 15) * 8;
   switch (p.splits) {

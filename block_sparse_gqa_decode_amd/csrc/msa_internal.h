@@ -16,6 +16,7 @@ constexpr int kMaxSplits = 16;
 constexpr int kMaxScoreBlocks = 16384;
 constexpr int kMaxScoreBatch = 4096;   // requests per scorer launch (LDS prefix sum)
 constexpr int kMaxScoreDql = 32;
+constexpr int kMaxPrefills = 1 << 20;   // requests of one prefill plan
 constexpr int kXcdSlots = 8;   // XCDs a launch is dealt across, round robin
 
 // Element formats (the values of msa_kv_dtype / msa_q_dtype).
@@ -41,6 +42,12 @@ struct AttendParams {
   float scale_log2;         // sm_scale * q_scale * k_scale * log2(e)
   float v_scale;
   int32_t dql, real_rows, num_rows, hq, hkv, group, topk_k, splits, num_units;
+  // Ragged prefill (null for decode): request r owns rows cu_q[r]..cu_q[r+1]-1,
+  // its local token i sits at ctx_lens[r] + i; rows >= cu_q[num_reqs] are
+  // padding.  real_rows is then num_rows and seq_lens / dql are unused.
+  const int32_t* cu_q;
+  const int32_t* ctx_lens;
+  int32_t num_reqs;
 };
 
 struct ScoreParams {

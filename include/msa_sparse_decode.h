@@ -15,6 +15,9 @@
  *    order),
  *    MiniMaxM3SparseImpl (each query attends only the indexer-selected
  *    blocks), MiniMaxM3SparseTritonImpl.forward (decode call arguments).
+ *  - The same sparse-attention page: MiniMaxM3SparsePrefillMetadata
+ *    (cu_seqlens_q rebased to 0, context_lens of cached tokens) and the
+ *    prefill call of MiniMaxM3SparseTritonImpl.forward.
  *  - vLLM test file test_minimax_m3_msa_cutlass_sparse_decode.py: _make_topk
  *    (logical block ids per (token, kv head), -1 padding, token position
  *    seq_len - query_len + local), _make_paged_layout (one block-table row
@@ -94,6 +97,26 @@ typedef struct msa_decode_shape {
   int32_t q_dtype;            /* msa_q_dtype                                     */
 } msa_decode_shape;
 
+/* Static shape of one ragged prefill step (the prefill call of
+ * MiniMaxM3SparseTritonImpl.forward): num_prefills requests whose query
+ * chunks occupy consecutive rows of q / topk / out, as cu_seqlens_q says at
+ * run time. */
+typedef struct msa_prefill_shape {
+  int32_t num_prefills;       /* requests, >= 1                                  */
+  int32_t num_token_rows;     /* rows of q/topk/out, >= 1; rows at or past
+                                 cu_seqlens_q[num_prefills] are padding rows
+                                 and produce exact zeros                         */
+  int32_t page_table_stride;  /* elements between block-table rows, >= 1         */
+  int32_t num_q_heads;        /* as in msa_decode_shape                          */
+  int32_t num_kv_heads;
+  int32_t page_size;          /* must be 128                                     */
+  int32_t head_dim;           /* must be 128                                     */
+  int32_t topk_blocks;        /* entries per top-k row, 1..64                    */
+  int32_t kv_dtype;           /* msa_kv_dtype                                    */
+  int32_t q_dtype;            /* msa_q_dtype                                     */
+  int32_t num_splits;         /* 0 = plan's choice, else 1..16                   */
+} msa_prefill_shape;
+
 typedef struct msa_plan_s* msa_plan;
 
 /* Validate `shape`, choose the launch configuration and allocate the plan's
@@ -110,7 +133,8 @@ msa_status msa_sparse_decode_plan(const msa_decode_shape* shape, int device,
 msa_status msa_sparse_decode_plan_destroy(msa_plan plan);
 
 /* Report the plan's split factor, partial-arena size in bytes and the
- * shape it was built for (any output pointer may be NULL). */
+ * shape it was built for (any output pointer may be NULL).  For a prefill
+ * plan, shape_out->decode_query_len is 0 and batch is num_prefills. */
 msa_status msa_sparse_decode_plan_info(msa_plan plan, int32_t* num_splits,
                                        int64_t* arena_bytes,
                                        msa_decode_shape* shape_out);
@@ -166,6 +190,35 @@ msa_status msa_sparse_decode_attend(msa_plan plan, const void* q, const void* kv
                                     const int32_t* topk, const int64_t topk_strides[3],
                                     void* out, float sm_scale, void* stream);
 msa_status msa_sparse_decode_merge(msa_plan plan, void* out, float v_scale, void* stream);
+
+/* A prefill plan: the same validation, split choice and arena as
+ * msa_sparse_decode_plan (destroyed by msa_sparse_decode_plan_destroy). */
+msa_status msa_sparse_prefill_plan(const msa_prefill_shape* shape, int device,
+                                   msa_plan* plan_out);
+
+/* One ragged prefill attend (vLLM sparse-attention page, prefill call of
+ * MiniMaxM3SparseTritonImpl.forward): token row t with
+ * cu_seqlens_q[r] <= t < cu_seqlens_q[r+1] belongs to request r and sits at
+ * pos = context_lens[r] + t - cu_seqlens_q[r]; it attends exactly as a decode
+ * token at pos does (see msa_sparse_decode_run).
+ *   cu_seqlens_q  int32 [num_prefills + 1] device, non-decreasing, starting at
+ *                 0, last entry <= num_token_rows (a request may own no row).
+ *   context_lens  int32 [num_prefills] device: cached tokens before the chunk,
+ *                 so the request's keys are 0 .. context_lens[r] + q_len - 1.
+ *   q, kv_cache, block_table ([num_prefills, stride]), topk, out and the
+ *   scales as in msa_sparse_decode_run.  Both launches (attend, merge) are
+ *   made; the inputs are read on the device, so a captured run can be
+ *   replayed with new chunk boundaries.
+ * Out-of-contract cu_seqlens_q (decreasing, or past num_token_rows) cannot be
+ * detected on the host; the kernels stay in bounds for any values whose
+ * request lookup lands in [0, num_prefills). */
+msa_status msa_sparse_prefill_run(msa_plan plan, const void* q, const void* kv_cache,
+                                  const int64_t kv_strides[4], int64_t num_kv_blocks,
+                                  float q_scale, float k_scale, float v_scale,
+                                  const int32_t* block_table, const int32_t* cu_seqlens_q,
+                                  const int32_t* context_lens, const int32_t* topk,
+                                  const int64_t topk_strides[3], void* out, float sm_scale,
+                                  void* stream);
 
 /* Indexer step of a full decode: per-block causal max score, then top-k.
  *   score[h, b, t] = max over g < G and visible keys i of block b of

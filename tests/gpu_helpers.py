@@ -114,3 +114,51 @@ def assert_parity(got: np.ndarray, ref: np.ndarray, atol=ATOL, rtol=RTOL, what="
     assert rel <= rtol, f"{what}: relative L2 err {rel}"
     assert np.all(diff <= atol + rtol * np.abs(ref)), f"{what}: elementwise tolerance"
     return max_abs, rel
+
+
+class PrefillDevCase:
+    """A gen.PrefillCase on the device, run through msa_sparse_prefill_run."""
+
+    def __init__(self, case: gen.PrefillCase, dev="cuda:0"):
+        self.case = case
+        self.dev = torch.device(dev)
+        if case.kv_dtype == gen.KV_FP8:
+            kv = torch.from_numpy(case.kv)
+        elif case.kv_dtype == gen.KV_E5M2:
+            kv = torch.from_numpy(case.kv).view(torch.float8_e5m2)
+        else:
+            kv = torch.from_numpy(case.kv.view(np.int16)).view(torch.bfloat16)
+        self.kv = kv.to(self.dev)
+        if case.q_dtype == gen.Q_FP8:
+            self.q = torch.from_numpy(case.q).view(torch.float8_e4m3fn).to(self.dev)
+        else:
+            self.q = torch.from_numpy(case.q.view(np.int16)).view(torch.bfloat16).to(self.dev)
+        self.block_table = torch.from_numpy(case.block_table).to(self.dev)
+        self.cu = torch.from_numpy(case.cu_seqlens_q).to(self.dev)
+        self.ctx = torch.from_numpy(case.context_lens).to(self.dev)
+        self.topk = torch.from_numpy(case.topk).to(self.dev)
+        self.out = torch.full(tuple(self.q.shape), float("nan"), dtype=torch.bfloat16,
+                              device=self.dev)
+
+    def plan(self, num_splits=0):
+        c = self.case
+        return msa.msa_sparse_prefill_plan(
+            c.batch, c.num_token_rows, num_q_heads=c.num_q_heads, num_kv_heads=c.num_kv_heads,
+            page_table_stride=self.block_table.stride(0), topk_blocks=c.topk_k,
+            kv_dtype=KV_CODES[c.kv_dtype], q_dtype=Q_CODES[c.q_dtype], num_splits=num_splits,
+            device=self.dev)
+
+    def run(self, plan, out=None, stream=None):
+        c = self.case
+        out = self.out if out is None else out
+        msa.msa_sparse_prefill_run(plan, self.q, self.kv, self.block_table, self.cu, self.ctx,
+                                   self.topk, out, sm_scale=c.sm_scale, k_scale=c.k_scale,
+                                   v_scale=c.v_scale, q_scale=c.q_scale, stream=stream)
+        return out
+
+
+def oracle_prefill(case: gen.PrefillCase, rows=None):
+    return om.sparse_prefill(case.q, case.kv, case.kv_dtype, case.k_scale, case.v_scale,
+                             case.block_table, case.cu_seqlens_q, case.context_lens, case.topk,
+                             case.num_kv_heads, case.sm_scale, rows=rows, q_dtype=case.q_dtype,
+                             q_scale=case.q_scale)

@@ -332,3 +332,84 @@ def test_binding_format_checks():
         msa.KV_FP8_E5M2
     with pytest.raises(ValueError, match="does not match"):
         msa._kv_dtype_of(torch.empty(1, dtype=torch.float8_e4m3fn), msa.KV_FP8_E5M2)
+
+
+# ---------------------------------------------------------------------------
+# prefill plans
+# ---------------------------------------------------------------------------
+
+def test_prefill_shape_struct_matches_header():
+    text = open(HEADER).read()
+    body = re.search(r"typedef struct msa_prefill_shape \{(.*?)\} msa_prefill_shape;", text,
+                     flags=re.S).group(1)
+    body = re.sub(r"/\*.*?\*/", "", body, flags=re.S)
+    names = [n.strip() for grp in re.findall(r"int32_t\s+([\w\s,]+);", body)
+             for n in grp.split(",")]
+    assert names == [f for f, _ in msa._PrefillShape._fields_]
+
+
+def prefill_shape(**kw):
+    base = dict(num_prefills=3, num_token_rows=505, page_table_stride=9, num_q_heads=64,
+                num_kv_heads=4, page_size=128, head_dim=128, topk_blocks=16,
+                kv_dtype=msa.KV_FP8_E4M3, q_dtype=msa.Q_BF16, num_splits=1)
+    base.update(kw)
+    return msa._PrefillShape(*[base[f] for f, _ in msa._PrefillShape._fields_])
+
+
+def prefill_plan_status(lib, s):
+    h = ctypes.c_void_p()
+    st = lib.msa_sparse_prefill_plan(ctypes.byref(s), 0, ctypes.byref(h))
+    msg = lib.msa_last_error().decode()
+    if st == 0:
+        lib.msa_sparse_decode_plan_destroy(h)
+    return st, msg
+
+
+@pytest.mark.parametrize("field,value,status,fragment", [
+    ("num_prefills", 0, msa.MSA_ERR_INVALID_ARG, "num_prefills"),
+    ("num_token_rows", 0, msa.MSA_ERR_INVALID_ARG, "num_token_rows"),
+    ("page_size", 64, msa.MSA_ERR_UNSUPPORTED, "page_size"),
+    ("topk_blocks", 65, msa.MSA_ERR_UNSUPPORTED, "topk_blocks"),
+    ("num_kv_heads", 3, msa.MSA_ERR_INVALID_ARG, "multiple"),
+    ("kv_dtype", msa.KV_BF16, None, None),
+])
+def test_prefill_plan_validation(lib, field, value, status, fragment):
+    st, msg = prefill_plan_status(lib, prefill_shape(**{field: value}))
+    if status is None:
+        assert st == 0, msg
+    else:
+        assert st == status and fragment in msg, (st, msg)
+
+
+def test_prefill_plan_fp8_q_needs_fp8_cache(lib):
+    st, msg = prefill_plan_status(lib, prefill_shape(kv_dtype=msa.KV_BF16,
+                                                     q_dtype=msa.Q_FP8_E4M3))
+    assert st == msa.MSA_ERR_UNSUPPORTED and "fp8 q" in msg
+
+
+def test_prefill_and_decode_plans_do_not_mix(lib):
+    kvs = msa._I64x4(256 * 128, 256 * 128, 256, 1)
+    tks = msa._I64x3(16 * 4, 16, 1)
+    hp = ctypes.c_void_p()
+    s = prefill_shape()
+    assert lib.msa_sparse_prefill_plan(ctypes.byref(s), 0, ctypes.byref(hp)) == 0
+    hd = _plan(lib)
+    try:
+        # a prefill plan refuses the decode entry points, and vice versa
+        st = lib.msa_sparse_decode_run(hp, FAKE, FAKE, kvs, 10, 1.0, 1.0, 1.0, FAKE, FAKE, FAKE,
+                                       tks, FAKE, 0.08, None)
+        assert st == msa.MSA_ERR_INVALID_ARG and "prefill" in lib.msa_last_error().decode()
+        assert lib.msa_sparse_decode_merge(hp, FAKE, 1.0, None) == msa.MSA_ERR_INVALID_ARG
+        st = lib.msa_sparse_prefill_run(hd, FAKE, FAKE, kvs, 10, 1.0, 1.0, 1.0, FAKE, FAKE,
+                                        FAKE, FAKE, tks, FAKE, 0.08, None)
+        assert st == msa.MSA_ERR_INVALID_ARG and "decode plan" in lib.msa_last_error().decode()
+        # NULL chunk boundaries are rejected before any launch
+        st = lib.msa_sparse_prefill_run(hp, FAKE, FAKE, kvs, 10, 1.0, 1.0, 1.0, FAKE, None,
+                                        FAKE, FAKE, tks, FAKE, 0.08, None)
+        assert st == msa.MSA_ERR_INVALID_ARG and "cu_seqlens_q" in lib.msa_last_error().decode()
+        info = msa._Shape()
+        assert lib.msa_sparse_decode_plan_info(hp, None, None, ctypes.byref(info)) == 0
+        assert info.decode_query_len == 0 and info.batch == 3 and info.num_token_rows == 505
+    finally:
+        lib.msa_sparse_decode_plan_destroy(hp)
+        lib.msa_sparse_decode_plan_destroy(hd)

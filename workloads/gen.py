@@ -198,6 +198,26 @@ def pick_zipf_recent(rng: np.random.Generator, last: int, k: int) -> np.ndarray:
     return rng.permutation(sel).astype(np.int32)
 
 
+def pick_zipf_recent_heads(rng: np.random.Generator, last: int, k: int,
+                           num_kv_heads: int) -> np.ndarray:
+    """``pick_zipf_recent`` for several kv heads at once, by Gumbel top-k:
+    the k-1 largest of log(1/(last-b)) + Gumbel noise over b < last are a draw
+    without replacement with weights 1/(last-b).  Returns int32 [heads, k],
+    -1 padded."""
+    out = np.full((num_kv_heads, k), -1, dtype=np.int32)
+    if last + 1 <= k:
+        for h in range(num_kv_heads):
+            out[h, :last + 1] = rng.permutation(np.arange(last + 1))
+        return out
+    logw = -np.log(np.arange(last, 0, -1, dtype=np.float64))        # block b = 0..last-1
+    key = logw[None, :] + rng.gumbel(size=(num_kv_heads, last))
+    others = np.argpartition(-key, k - 2, axis=1)[:, : k - 1]
+    sel = np.concatenate([others, np.full((num_kv_heads, 1), last)], axis=1)
+    for h in range(num_kv_heads):
+        out[h] = rng.permutation(sel[h])
+    return out
+
+
 def pad_row(sel: np.ndarray, k: int) -> np.ndarray:
     out = np.full(k, -1, dtype=np.int32)
     out[: len(sel)] = sel[:k]
@@ -581,8 +601,7 @@ def make_prefill_case(seed: int, q_lens, seq_lens, num_q_heads: int, num_kv_head
                     assert last < topk_k
                     topk[t, :, :last + 1] = np.arange(last + 1, dtype=np.int32)
                 else:
-                    for h in range(num_kv_heads):
-                        topk[t, h] = pad_row(pick_zipf_recent(rng_, last, topk_k), topk_k)
+                    topk[t] = pick_zipf_recent_heads(rng_, last, topk_k, num_kv_heads)
         return q, topk
 
     q, topk = one(rng)
@@ -591,6 +610,26 @@ def make_prefill_case(seed: int, q_lens, seq_lens, num_q_heads: int, num_kv_head
                        num_q_heads, num_kv_heads, topk_k, kv_dtype, bt, kv, q, topk,
                        q_dtype=q_dtype, q_scale=q_scale, max_blocks=int(bt.shape[1]),
                        replicas=reps)
+
+
+PREFILL_CONFIG_NAMES = ("pf1_chunked_prefill",)
+
+
+def make_prefill_config(name: str, replicas: int = 0, poison: bool = True) -> PrefillCase:
+    """Chunked prefill: 4 requests each adding a 1024-token chunk after a
+    cached context of U[16384, 65536] tokens, 64/4 heads, fp8 e4m3 cache,
+    top-16 per (token, kv head) with the recent bias and the token's own
+    block (the shape the pages' prefill path serves; they print no prefill
+    benchmark)."""
+    if name != "pf1_chunked_prefill":
+        raise KeyError(name)
+    rng = np.random.default_rng(6)
+    B, chunk = 4, 1024
+    ctx = rng.integers(16384, 65536, size=B, endpoint=True).astype(np.int32)
+    q_lens = np.full(B, chunk, dtype=np.int32)
+    return make_prefill_case(int(rng.integers(0, 2 ** 31 - 1)), q_lens, ctx + q_lens, 64, 4,
+                             topk_k=16, kv_dtype=KV_FP8, rule="zipf", std=0.5,
+                             replicas=replicas, poison=poison, name=name)
 
 
 def make_scores(seed: int, num_kv_heads: int, max_blocks: int, rows: int, seq_lens,
