@@ -45,7 +45,7 @@ __all__ = [
     "PAGE_SIZE", "HEAD_DIM", "ABI_VERSION",
 ]
 
-ABI_VERSION = 2
+ABI_VERSION = 3
 PAGE_SIZE = 128
 HEAD_DIM = 128
 KV_BF16 = 0
@@ -82,14 +82,14 @@ class _Shape(ctypes.Structure):
     _fields_ = [(name, ctypes.c_int32) for name in (
         "batch", "decode_query_len", "num_token_rows", "page_table_stride",
         "num_q_heads", "num_kv_heads", "page_size", "head_dim", "topk_blocks",
-        "kv_dtype", "num_splits", "q_dtype")]
+        "kv_dtype", "num_splits", "q_dtype", "tile_rows")]
 
 
 class _PrefillShape(ctypes.Structure):
     _fields_ = [(name, ctypes.c_int32) for name in (
         "num_prefills", "num_token_rows", "page_table_stride", "num_q_heads",
         "num_kv_heads", "page_size", "head_dim", "topk_blocks", "kv_dtype", "q_dtype",
-        "num_splits")]
+        "num_splits", "tile_rows")]
 
 
 _I64x4 = ctypes.c_int64 * 4
@@ -245,6 +245,8 @@ class DecodePlan:
         self.topk_blocks = shape.topk_blocks
         self.kv_dtype = shape.kv_dtype
         self.q_dtype = shape.q_dtype
+        self.tile_rows = shape.tile_rows
+        self.dense = shape.topk_blocks == 0
         self.num_splits = splits.value
         self.arena_bytes = arena.value
 
@@ -268,11 +270,15 @@ def msa_sparse_decode_plan(batch: int, decode_query_len: int, *, num_q_heads: in
                            num_kv_heads: int, page_table_stride: int, topk_blocks: int,
                            kv_dtype: int, num_token_rows: int = 0, num_splits: int = 0,
                            page_size: int = PAGE_SIZE, head_dim: int = HEAD_DIM,
-                           q_dtype: int = Q_BF16, device=None) -> DecodePlan:
+                           q_dtype: int = Q_BF16, tile_rows: int = 0,
+                           device=None) -> DecodePlan:
+    """topk_blocks = 0 plans dense decode (every visible block; run with
+    topk=None).  tile_rows: 0 = the plan's choice, 1 = one token row per
+    workgroup, 4 / 8 = multi-row tiles."""
     lib = load_library()
     shape = _Shape(batch, decode_query_len, num_token_rows, page_table_stride, num_q_heads,
                    num_kv_heads, page_size, head_dim, topk_blocks, kv_dtype, num_splits,
-                   q_dtype)
+                   q_dtype, tile_rows)
     if device is None:
         dev = torch.cuda.current_device() if torch.cuda.is_available() else 0
     elif isinstance(device, int):
@@ -299,12 +305,12 @@ def msa_sparse_prefill_plan(num_prefills: int, num_token_rows: int, *, num_q_hea
                             num_kv_heads: int, page_table_stride: int, topk_blocks: int,
                             kv_dtype: int, q_dtype: int = Q_BF16, num_splits: int = 0,
                             page_size: int = PAGE_SIZE, head_dim: int = HEAD_DIM,
-                            device=None) -> DecodePlan:
+                            tile_rows: int = 0, device=None) -> DecodePlan:
     """A plan for ragged prefill chunks over ``num_token_rows`` q rows."""
     lib = load_library()
     shape = _PrefillShape(num_prefills, num_token_rows, page_table_stride, num_q_heads,
                           num_kv_heads, page_size, head_dim, topk_blocks, kv_dtype, q_dtype,
-                          num_splits)
+                          num_splits, tile_rows)
     dev = _device_index(device)
     handle = ctypes.c_void_p()
     _check(lib.msa_sparse_prefill_plan(ctypes.byref(shape), int(dev), ctypes.byref(handle)))
@@ -343,6 +349,14 @@ def msa_sparse_prefill_run(plan: DecodePlan, q: torch.Tensor, kv_cache: torch.Te
         _stream_handle(stream, q.device)))
 
 
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else t.data_ptr()
+
+
+def _strides3(t: Optional[torch.Tensor]):
+    return None if t is None else _I64x3(*t.stride())
+
+
 def _run_args(plan, q, kv_cache, block_table, seq_lens, topk, out, tables=True):
     rows = plan.num_token_rows
     _check_q(q, "q", rows, plan.num_q_heads, plan.q_dtype)
@@ -353,12 +367,18 @@ def _run_args(plan, q, kv_cache, block_table, seq_lens, topk, out, tables=True):
         _check_tables(block_table, seq_lens, plan.batch)
     if block_table.stride(0) != plan.page_table_stride:
         raise ValueError("block_table row stride does not match the plan")
-    if (topk.dtype != torch.int32 or topk.dim() != 3
+    if plan.dense:
+        if topk is not None:
+            raise ValueError("a dense plan attends every visible block: pass topk=None")
+    elif (topk is None or topk.dtype != torch.int32 or topk.dim() != 3
             or tuple(topk.shape) != (rows, plan.num_kv_heads, plan.topk_blocks)):
         raise ValueError(f"topk must be int32 [{rows}, {plan.num_kv_heads}, "
-                         f"{plan.topk_blocks}], got {topk.dtype} {tuple(topk.shape)}")
+                         f"{plan.topk_blocks}], got "
+                         f"{None if topk is None else (topk.dtype, tuple(topk.shape))}")
     for name, t in (("kv_cache", kv_cache), ("block_table", block_table), ("topk", topk),
                     ("q", q), ("out", out)):
+        if t is None:
+            continue
         if t.device != seq_lens.device:
             raise ValueError(f"{name} is not on the sequence-length device")
     return (plan.handle, q.data_ptr(), kv_cache.data_ptr(), _I64x4(*kv_cache.stride()),
@@ -372,15 +392,16 @@ def _require_decode_plan(plan: DecodePlan):
 
 def msa_sparse_decode_run(plan: DecodePlan, q: torch.Tensor, kv_cache: torch.Tensor,
                           block_table: torch.Tensor, seq_lens: torch.Tensor,
-                          topk: torch.Tensor, out: torch.Tensor, *, sm_scale: float,
+                          topk: Optional[torch.Tensor], out: torch.Tensor, *, sm_scale: float,
                           k_scale: float = 1.0, v_scale: float = 1.0, q_scale: float = 1.0,
                           stream=None) -> None:
-    """out[t, j] = sparse causal attention of q[t, j] over the selected pages."""
+    """out[t, j] = sparse causal attention of q[t, j] over the selected pages
+    (every visible page with a dense plan and topk=None)."""
     _require_decode_plan(plan)
     head = _run_args(plan, q, kv_cache, block_table, seq_lens, topk, out)
     _check(load_library().msa_sparse_decode_run(
         *head, float(q_scale), float(k_scale), float(v_scale), block_table.data_ptr(), seq_lens.data_ptr(),
-        topk.data_ptr(), _I64x3(*topk.stride()), out.data_ptr(), float(sm_scale),
+        _ptr(topk), _strides3(topk), out.data_ptr(), float(sm_scale),
         _stream_handle(stream, q.device)))
 
 
@@ -394,7 +415,7 @@ def msa_sparse_decode_attend(plan: DecodePlan, q: torch.Tensor, kv_cache: torch.
     head = _run_args(plan, q, kv_cache, block_table, seq_lens, topk, out)
     _check(load_library().msa_sparse_decode_attend(
         *head, float(q_scale), float(k_scale), float(v_scale), block_table.data_ptr(), seq_lens.data_ptr(),
-        topk.data_ptr(), _I64x3(*topk.stride()), out.data_ptr(), float(sm_scale),
+        _ptr(topk), _strides3(topk), out.data_ptr(), float(sm_scale),
         _stream_handle(stream, q.device)))
 
 

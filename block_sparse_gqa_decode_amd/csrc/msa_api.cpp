@@ -20,6 +20,9 @@
 struct msa_plan_s {
   msa_decode_shape shape;   // for a prefill plan: decode_query_len = 0
   bool prefill;
+  bool dense;               // every visible block (topk_blocks == 0)
+  int32_t tile_rows;        // 1: one row per workgroup; 4 / 8: multi-row tiles
+  int32_t num_units;        // workgroups per split
   int device;
   int32_t splits;
   int32_t real_rows;
@@ -138,16 +141,16 @@ msa_status check_kv(const void* kv_cache, const int64_t kv_strides[4], int64_t n
   return MSA_OK;
 }
 
-// Split-K only when there are too few (token, kv head) units to give every CU
-// a workgroup: each split costs a partial write plus a merge launch, which
-// pays off only below one unit per CU.
-int32_t choose_splits(const msa_decode_shape* s, int32_t real_rows) {
+// Split-K only when there are too few work units to give every CU a
+// workgroup: each split costs a partial write plus a merge launch, which pays
+// off only below one unit per CU.  Dense page lists are long (every visible
+// block), so they split further.
+int32_t choose_splits(const msa_decode_shape* s, int64_t units, bool dense) {
   if (s->num_splits > 0) return s->num_splits;
-  const int64_t units = (int64_t)real_rows * s->num_kv_heads;
-  constexpr int64_t kTargetWorkgroups = 256;
+  const int64_t target = dense ? 512 : 256;
+  const int32_t cap = dense ? msa::kMaxSplits : (s->topk_blocks < 8 ? s->topk_blocks : 8);
   int32_t splits = 1;
-  const int32_t cap = s->topk_blocks < 8 ? s->topk_blocks : 8;
-  while (units * splits < kTargetWorkgroups && splits * 2 <= cap) splits *= 2;
+  while (units * splits < target && splits * 2 <= cap) splits *= 2;
   return splits;
 }
 
@@ -188,6 +191,31 @@ msa_status msa_sparse_decode_plan(const msa_decode_shape* shape, int device, msa
   return make_plan(shape, false, shape->batch * shape->decode_query_len, device, plan_out);
 }
 
+// The kernel a plan uses: rows per workgroup (1 = the single-row attend) and
+// the number of workgroups per split.
+static msa_status choose_tiles(const msa_decode_shape* s, bool prefill, bool dense,
+                               int32_t num_rows, int32_t* tile_rows, int64_t* units) {
+  int32_t tr = s->tile_rows;
+  if (tr != 0 && tr != 1 && tr != 4 && tr != 8)
+    return fail(MSA_ERR_INVALID_ARG, "tile_rows must be 0 (auto), 1, 4 or 8 (got %d)", tr);
+  if (tr == 0) {
+    if (dense) tr = s->decode_query_len <= 4 ? 4 : 8;
+    else if (prefill || s->decode_query_len >= 8) tr = 8;
+    else tr = 1;
+  }
+  if (dense && tr == 1)
+    return fail(MSA_ERR_UNSUPPORTED, "dense decode runs on multi-row tiles (tile_rows 4 or 8)");
+  int64_t tiles;
+  if (tr == 1) tiles = num_rows;
+  else if (dense)  // request-aligned tiles, then tiles of padding rows
+    tiles = (int64_t)s->batch * ((s->decode_query_len + tr - 1) / tr) +
+            ((int64_t)num_rows - (int64_t)s->batch * s->decode_query_len + tr - 1) / tr;
+  else tiles = ((int64_t)num_rows + tr - 1) / tr;
+  *tile_rows = tr;
+  *units = tiles * s->num_kv_heads;
+  return MSA_OK;
+}
+
 msa_status msa_sparse_prefill_plan(const msa_prefill_shape* pshape, int device,
                                    msa_plan* plan_out) {
   if (plan_out == nullptr) return fail(MSA_ERR_INVALID_ARG, "plan_out is NULL");
@@ -215,6 +243,7 @@ msa_status msa_sparse_prefill_plan(const msa_prefill_shape* pshape, int device,
   s.kv_dtype = pshape->kv_dtype;
   s.num_splits = pshape->num_splits;
   s.q_dtype = pshape->q_dtype;
+  s.tile_rows = pshape->tile_rows;
   if (s.num_token_rows > (1 << 24)) return fail(MSA_ERR_UNSUPPORTED, "num_token_rows exceeds 2^24");
   const int32_t keep_rows = s.num_token_rows;
   s.num_token_rows = 0;  // batch*1 may exceed the rows; checked above instead
@@ -227,8 +256,12 @@ msa_status msa_sparse_prefill_plan(const msa_prefill_shape* pshape, int device,
 
 static msa_status make_plan(const msa_decode_shape* shape, bool prefill, int32_t real_rows,
                             int device, msa_plan* plan_out) {
-  if (shape->topk_blocks < 1)
-    return fail(MSA_ERR_INVALID_ARG, "topk_blocks must be >= 1 (got %d)", shape->topk_blocks);
+  const bool dense = shape->topk_blocks == 0;
+  if (dense && prefill)
+    return fail(MSA_ERR_UNSUPPORTED, "a prefill plan needs top-k selections (topk_blocks >= 1)");
+  if (shape->topk_blocks < 0)
+    return fail(MSA_ERR_INVALID_ARG, "topk_blocks must be >= 1, or 0 for dense decode (got %d)",
+                shape->topk_blocks);
   if (shape->topk_blocks > msa::kMaxTopk)
     return fail(MSA_ERR_UNSUPPORTED, "topk_blocks %d exceeds %d", shape->topk_blocks,
                 msa::kMaxTopk);
@@ -238,8 +271,12 @@ static msa_status make_plan(const msa_decode_shape* shape, bool prefill, int32_t
   if (device < 0) return fail(MSA_ERR_INVALID_ARG, "device must be >= 0 (got %d)", device);
 
   const int32_t num_rows = shape->num_token_rows ? shape->num_token_rows : real_rows;
-  const int32_t splits = choose_splits(shape, real_rows);
-  const int64_t units = (int64_t)num_rows * shape->num_kv_heads;
+  int32_t tile_rows = 1;
+  int64_t units = 0;
+  msa_status st = choose_tiles(shape, prefill, dense, num_rows, &tile_rows, &units);
+  if (st != MSA_OK) return st;
+  if (units > INT32_MAX) return fail(MSA_ERR_UNSUPPORTED, "launch grid too large");
+  const int32_t splits = choose_splits(shape, units, dense);
   const int64_t grid =
       (units + msa::kXcdSlots - 1) / msa::kXcdSlots * msa::kXcdSlots * splits;
   if (grid > INT32_MAX) return fail(MSA_ERR_UNSUPPORTED, "launch grid too large");
@@ -251,8 +288,12 @@ static msa_status make_plan(const msa_decode_shape* shape, bool prefill, int32_t
   if (plan == nullptr) return fail(MSA_ERR_OUT_OF_MEMORY, "host allocation failed");
   plan->shape = *shape;
   plan->prefill = prefill;
+  plan->dense = dense;
+  plan->tile_rows = tile_rows;
+  plan->num_units = (int32_t)units;
   plan->shape.num_token_rows = num_rows;
   plan->shape.num_splits = splits;
+  plan->shape.tile_rows = tile_rows;
   plan->device = device;
   plan->splits = splits;
   plan->real_rows = real_rows;
@@ -325,12 +366,18 @@ static msa_status run_phases(msa_plan plan, const void* q, const void* kv_cache,
     if (block_table == nullptr || cu_q == nullptr || ctx == nullptr || topk == nullptr)
       return fail(MSA_ERR_INVALID_ARG,
                   "block_table, cu_seqlens_q, context_lens and topk must be non-NULL");
-  } else if (block_table == nullptr || seq_lens == nullptr || topk == nullptr) {
-    return fail(MSA_ERR_INVALID_ARG, "block_table, seq_lens and topk must be non-NULL");
+  } else if (block_table == nullptr || seq_lens == nullptr) {
+    return fail(MSA_ERR_INVALID_ARG, "block_table and seq_lens must be non-NULL");
+  } else if (plan->dense != (topk == nullptr)) {
+    return fail(MSA_ERR_INVALID_ARG, plan->dense ? "a dense plan takes topk = NULL"
+                                                 : "block_table, seq_lens and topk must be "
+                                                   "non-NULL");
   }
-  if (topk_strides == nullptr) return fail(MSA_ERR_INVALID_ARG, "topk_strides is NULL");
-  for (int d = 0; d < 3; ++d)
-    if (topk_strides[d] < 0) return fail(MSA_ERR_INVALID_ARG, "topk strides must be >= 0");
+  if (!plan->dense) {
+    if (topk_strides == nullptr) return fail(MSA_ERR_INVALID_ARG, "topk_strides is NULL");
+    for (int d = 0; d < 3; ++d)
+      if (topk_strides[d] < 0) return fail(MSA_ERR_INVALID_ARG, "topk strides must be >= 0");
+  }
   msa_status st = check_kv(kv_cache, kv_strides, num_kv_blocks, s.kv_dtype);
   if (st != MSA_OK) return st;
   st = check_scales(q_scale, k_scale);
@@ -351,9 +398,11 @@ static msa_status run_phases(msa_plan plan, const void* q, const void* kv_cache,
   p.bt_stride = s.page_table_stride;
   p.seq_lens = seq_lens;
   p.topk = topk;
-  p.tk_s0 = topk_strides[0];
-  p.tk_s1 = topk_strides[1];
-  p.tk_s2 = topk_strides[2];
+  if (!plan->dense) {
+    p.tk_s0 = topk_strides[0];
+    p.tk_s1 = topk_strides[1];
+    p.tk_s2 = topk_strides[2];
+  }
   p.out = static_cast<uint16_t*>(out);
   p.part_o = plan->part_o;
   p.part_ml = plan->part_ml;
@@ -368,7 +417,8 @@ static msa_status run_phases(msa_plan plan, const void* q, const void* kv_cache,
   p.group = s.num_q_heads / s.num_kv_heads;
   p.topk_k = s.topk_blocks;
   p.splits = plan->splits;
-  p.num_units = plan->num_rows * s.num_kv_heads;
+  p.num_units = plan->num_units;
+  p.tile_dense = plan->dense ? 1 : 0;
   if (plan->prefill) {
     p.cu_q = cu_q;
     p.ctx_lens = ctx;
@@ -381,7 +431,8 @@ static msa_status run_phases(msa_plan plan, const void* q, const void* kv_cache,
   hipError_t e = guard.enter(plan->device);
   if (e != hipSuccess) return device_fail(e, "hipSetDevice");
   hipStream_t st_ = static_cast<hipStream_t>(stream);
-  e = msa::launch_attend(p, s.kv_dtype, s.q_dtype, st_);
+  e = plan->tile_rows > 1 ? msa::launch_tile(p, s.kv_dtype, s.q_dtype, plan->tile_rows, st_)
+                          : msa::launch_attend(p, s.kv_dtype, s.q_dtype, st_);
   if (e != hipSuccess) return device_fail(e, "attend launch");
   if (merge && plan->splits > 1) {
     e = msa::launch_merge(p, st_);

@@ -70,6 +70,7 @@
 // cache bytes cannot reach the MFMAs.
 #include "msa_device.h"
 #include "msa_internal.h"
+#include "msa_rows.h"
 
 namespace msa {
 namespace {
@@ -80,27 +81,6 @@ constexpr int kDepth = 2;      // pages per wavefront in the register ring
 constexpr int kKeysPerWave = 32;
 constexpr int kOPad = 4;
 constexpr float kRescaleSlack = 8.0f;
-
-// The request of token row t and the token's position, or false for a
-// padding row.  Wave-uniform: t comes from the workgroup id.
-__device__ __forceinline__ bool locate_row(const AttendParams& p, int t, int& r, int& pos) {
-  if (p.cu_q == nullptr) {
-    if (t >= p.real_rows) return false;
-    r = t / p.dql;
-    pos = p.seq_lens[r] - p.dql + (t - r * p.dql);
-    return true;
-  }
-  if (t >= p.cu_q[p.num_reqs]) return false;
-  int lo = 0, hi = p.num_reqs - 1;  // the last r with cu_q[r] <= t
-  while (lo < hi) {
-    const int mid = (lo + hi + 1) >> 1;
-    if (p.cu_q[mid] <= t) lo = mid;
-    else hi = mid - 1;
-  }
-  r = lo;
-  pos = p.ctx_lens[r] + (t - p.cu_q[r]);
-  return true;
-}
 
 template <bool kFp8>
 struct PageRegs;
@@ -345,7 +325,7 @@ __global__ __launch_bounds__(kThreads) void attend_kernel(AttendParams p) {
   const int head0 = h * p.group;
 
   int r = 0, pos = 0;
-  if (!locate_row(p, t, r, pos)) {
+  if (!locate_token(p, t, r, pos)) {
     // Padding row: exact zeros, written once.
     if (split == 0) {
       const int qr = tid >> 4;
@@ -552,7 +532,7 @@ __global__ __launch_bounds__(256) void merge_kernel(AttendParams p) {
   const int h = unit - t * p.hkv;
   const int qr = threadIdx.x >> 4;
   int r = 0, pos = 0;
-  if (!locate_row(p, t, r, pos) || qr >= p.group) return;
+  if (!locate_token(p, t, r, pos) || qr >= p.group) return;
   const int64_t row = (int64_t)t * p.hq + h * p.group + qr;
   const int d0 = (threadIdx.x & 15) * 8;
   switch (p.splits) {

@@ -17,6 +17,8 @@ constexpr int kMaxScoreBlocks = 16384;
 constexpr int kMaxScoreBatch = 4096;   // requests per scorer launch (LDS prefix sum)
 constexpr int kMaxScoreDql = 32;
 constexpr int kMaxPrefills = 1 << 20;   // requests of one prefill plan
+constexpr int kMaxTileRows = 8;        // token rows of a multi-row tile
+constexpr int kMaxUnion = kMaxTileRows * kMaxTopk;   // pages of a tile's union
 constexpr int kXcdSlots = 8;   // XCDs a launch is dealt across, round robin
 
 // Element formats (the values of msa_kv_dtype / msa_q_dtype).
@@ -48,6 +50,9 @@ struct AttendParams {
   const int32_t* cu_q;
   const int32_t* ctx_lens;
   int32_t num_reqs;
+  // Multi-row tiles (tile kernel only): tile_dense selects every visible
+  // block of request-aligned tiles instead of the rows' top-k union.
+  int32_t tile_dense;
 };
 
 struct ScoreParams {
@@ -74,6 +79,9 @@ struct SelectParams {
 // kv_fmt: kKv*; q_fmt: kQ*.  An fp8 q needs an 8-bit KV format.
 hipError_t launch_attend(const AttendParams& p, int kv_fmt, int q_fmt, hipStream_t stream);
 hipError_t launch_merge(const AttendParams& p, hipStream_t stream);
+// Multi-row tiles of tile_rows (4 or 8) token rows; p.num_units = tiles * hkv.
+hipError_t launch_tile(const AttendParams& p, int kv_fmt, int q_fmt, int tile_rows,
+                       hipStream_t stream);
 hipError_t launch_score(const ScoreParams& p, int kv_fmt, int q_fmt, hipStream_t stream);
 hipError_t launch_select(const SelectParams& p, hipStream_t stream);
 // fmt: kKvE4m3 or kKvE5m2

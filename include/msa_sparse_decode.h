@@ -53,7 +53,7 @@
 extern "C" {
 #endif
 
-#define MSA_ABI_VERSION 2
+#define MSA_ABI_VERSION 3
 
 typedef enum msa_status {
   MSA_OK = 0,
@@ -90,11 +90,17 @@ typedef struct msa_decode_shape {
   int32_t num_kv_heads;       /* Hkv; Hq/Hkv (the GQA group) must be 1..16       */
   int32_t page_size;          /* must be 128 (one sparse block per KV page)      */
   int32_t head_dim;           /* must be 128                                     */
-  int32_t topk_blocks;        /* entries per top-k row, 1..64                    */
+  int32_t topk_blocks;        /* entries per top-k row, 1..64; 0 = dense decode:
+                                 every visible block, run with topk = NULL
+                                 (TensorRT-LLM PR #17171, dense-decode commit)   */
   int32_t kv_dtype;           /* msa_kv_dtype                                    */
   int32_t num_splits;         /* split-K factor over a row's live blocks; 0 lets
                                  the plan choose, else 1..16                     */
   int32_t q_dtype;            /* msa_q_dtype                                     */
+  int32_t tile_rows;          /* token rows per workgroup: 0 lets the plan
+                                 choose; 1 = one row per workgroup (sparse only);
+                                 4 or 8 = multi-row tiles that read each page
+                                 shared by their rows once                       */
 } msa_decode_shape;
 
 /* Static shape of one ragged prefill step (the prefill call of
@@ -115,6 +121,7 @@ typedef struct msa_prefill_shape {
   int32_t kv_dtype;           /* msa_kv_dtype                                    */
   int32_t q_dtype;            /* msa_q_dtype                                     */
   int32_t num_splits;         /* 0 = plan's choice, else 1..16                   */
+  int32_t tile_rows;          /* as in msa_decode_shape (0 = plan's choice)      */
 } msa_prefill_shape;
 
 typedef struct msa_plan_s* msa_plan;
@@ -160,7 +167,9 @@ msa_status msa_sparse_decode_plan_info(msa_plan plan, int32_t* num_splits,
  *                the device, so runs are graph-capturable and may change
  *                between replays.
  *   topk         int32 logical [num_token_rows, Hkv, topk_blocks] with
- *                topk_strides (elements), -1 = no block.
+ *                topk_strides (elements), -1 = no block.  NULL (and
+ *                topk_strides ignored) for a dense plan, which attends every
+ *                block b with b*128 <= pos.
  *   out          bf16 [num_token_rows, Hq, 128], contiguous.
  *   sm_scale, q_scale, k_scale must be finite and > 0 (the kernel takes each
  *   row's maximum before applying them); v_scale must be finite.  For a bf16

@@ -21,6 +21,9 @@ fusion or reordering:
 * ``select_topk`` -- top-k blocks per (token, kv head) by score, ties to the
   lower block index, padded with -1 (same PR, selector; tie rule from the
   full-decode-step workload statement).
+* ``dense_decode`` -- the decode attend over every causally visible block
+  (TensorRT-LLM PR #17171, dense-decode commit: M3's first layers attend the
+  whole page table).
 * ``sparse_prefill`` -- the same attend for ragged prefill chunks: request r
   owns token rows ``cu_seqlens_q[r] .. cu_seqlens_q[r+1]-1`` and its local
   token i sits at ``context_lens[r] + i`` (vLLM sparse-attention page,
@@ -252,6 +255,37 @@ def sparse_decode(q_bits, kv, kv_dtype, k_scale, v_scale, block_table, seq_lens,
             k, v = gathered[h]
             if k is None:
                 continue
+            qv = decode_query(q_bits[t, j], q_dtype, q_scale)
+            out[i, j] = softmax_attend(qv, k, v, sm_scale)
+    return out
+
+
+def dense_decode(q_bits, kv, kv_dtype, k_scale, v_scale, block_table, seq_lens,
+                 decode_query_len, num_kv_heads, sm_scale, rows=None, q_dtype="bf16",
+                 q_scale=1.0):
+    """Decode attend over all keys 0..pos of the request's pages (no top-k),
+    float64; padding rows are zeros.  Returns float64 [len(rows), Hq, 128]."""
+    q_bits = np.asarray(q_bits)
+    num_rows, hq, d = q_bits.shape
+    assert d == HEAD_DIM and hq % num_kv_heads == 0
+    group = hq // num_kv_heads
+    dql = int(decode_query_len)
+    real = len(seq_lens) * dql
+    row_list = range(num_rows) if rows is None else list(rows)
+    out = np.zeros((len(row_list), hq, HEAD_DIM), dtype=np.float64)
+    for i, t in enumerate(row_list):
+        if t >= real:
+            continue
+        r, loc = divmod(int(t), dql)
+        pos = token_position(seq_lens[r], dql, loc)
+        every = range(pos // PAGE + 1)
+        gathered = {}
+        for j in range(hq):
+            h = kv_head_of(j, group)
+            if h not in gathered:
+                gathered[h] = gather_live(kv, kv_dtype, k_scale, v_scale,
+                                          block_table[r], pos, h, every)
+            k, v = gathered[h]
             qv = decode_query(q_bits[t, j], q_dtype, q_scale)
             out[i, j] = softmax_attend(qv, k, v, sm_scale)
     return out

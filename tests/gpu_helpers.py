@@ -53,19 +53,20 @@ class DevCase:
     def q_dtype(self):
         return Q_CODES[self.case.q_dtype]
 
-    def plan(self, num_splits=0):
+    def plan(self, num_splits=0, tile_rows=0, dense=False):
         c = self.case
         return msa.msa_sparse_decode_plan(
             c.batch, c.dql, num_q_heads=c.num_q_heads, num_kv_heads=c.num_kv_heads,
-            page_table_stride=self.block_table.stride(0), topk_blocks=c.topk_k,
+            page_table_stride=self.block_table.stride(0), topk_blocks=0 if dense else c.topk_k,
             kv_dtype=self.kv_dtype, num_token_rows=c.num_token_rows, num_splits=num_splits,
-            q_dtype=self.q_dtype, device=self.dev)
+            q_dtype=self.q_dtype, tile_rows=tile_rows, device=self.dev)
 
     def run(self, plan, topk=None, out=None, stream=None):
         c = self.case
         out = self.out if out is None else out
+        tk = None if plan.dense else (self.topk if topk is None else topk)
         msa.msa_sparse_decode_run(plan, self.q, self.kv, self.block_table, self.seq_lens,
-                                  self.topk if topk is None else topk, out,
+                                  tk, out,
                                   sm_scale=c.sm_scale, k_scale=c.k_scale, v_scale=c.v_scale,
                                   q_scale=c.q_scale, stream=stream)
         return out
@@ -87,6 +88,13 @@ def oracle_attend(case: gen.DecodeCase, rows=None, topk=None):
                             case.topk if topk is None else topk, case.dql,
                             case.num_kv_heads, case.sm_scale, rows=rows,
                             q_dtype=case.q_dtype, q_scale=case.q_scale)
+
+
+def oracle_dense(case: gen.DecodeCase, rows=None):
+    return om.dense_decode(case.q, case.kv, case.kv_dtype, case.k_scale, case.v_scale,
+                           case.block_table, case.seq_lens, case.dql, case.num_kv_heads,
+                           case.sm_scale, rows=rows, q_dtype=case.q_dtype,
+                           q_scale=case.q_scale)
 
 
 def oracle_scores(case: gen.DecodeCase, max_blocks, rows=None):
@@ -140,13 +148,13 @@ class PrefillDevCase:
         self.out = torch.full(tuple(self.q.shape), float("nan"), dtype=torch.bfloat16,
                               device=self.dev)
 
-    def plan(self, num_splits=0):
+    def plan(self, num_splits=0, tile_rows=0):
         c = self.case
         return msa.msa_sparse_prefill_plan(
             c.batch, c.num_token_rows, num_q_heads=c.num_q_heads, num_kv_heads=c.num_kv_heads,
             page_table_stride=self.block_table.stride(0), topk_blocks=c.topk_k,
             kv_dtype=KV_CODES[c.kv_dtype], q_dtype=Q_CODES[c.q_dtype], num_splits=num_splits,
-            device=self.dev)
+            tile_rows=tile_rows, device=self.dev)
 
     def run(self, plan, out=None, stream=None):
         c = self.case

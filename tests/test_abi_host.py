@@ -35,7 +35,7 @@ def lib():
 def shape(**kw):
     base = dict(batch=32, decode_query_len=4, num_token_rows=0, page_table_stride=512,
                 num_q_heads=16, num_kv_heads=1, page_size=128, head_dim=128, topk_blocks=16,
-                kv_dtype=msa.KV_FP8_E4M3, num_splits=1, q_dtype=msa.Q_BF16)
+                kv_dtype=msa.KV_FP8_E4M3, num_splits=1, q_dtype=msa.Q_BF16, tile_rows=0)
     base.update(kw)
     return msa._Shape(*[base[f] for f, _ in msa._Shape._fields_])
 
@@ -99,7 +99,8 @@ def test_decode_query_len_bounds(lib, batch, dql, hq, hkv, ok):
     ("num_kv_heads", 3, msa.MSA_ERR_INVALID_ARG, "multiple"),
     ("num_kv_heads", 0, msa.MSA_ERR_INVALID_ARG, "head counts"),
     ("num_q_heads", 64, msa.MSA_ERR_UNSUPPORTED, "GQA group"),
-    ("topk_blocks", 0, msa.MSA_ERR_INVALID_ARG, "topk_blocks"),
+    ("topk_blocks", -1, msa.MSA_ERR_INVALID_ARG, "topk_blocks"),
+    ("tile_rows", 3, msa.MSA_ERR_INVALID_ARG, "tile_rows"),
     ("topk_blocks", 65, msa.MSA_ERR_UNSUPPORTED, "topk_blocks"),
     ("batch", 0, msa.MSA_ERR_INVALID_ARG, "batch"),
     ("page_table_stride", 0, msa.MSA_ERR_INVALID_ARG, "page_table_stride"),
@@ -351,7 +352,7 @@ def test_prefill_shape_struct_matches_header():
 def prefill_shape(**kw):
     base = dict(num_prefills=3, num_token_rows=505, page_table_stride=9, num_q_heads=64,
                 num_kv_heads=4, page_size=128, head_dim=128, topk_blocks=16,
-                kv_dtype=msa.KV_FP8_E4M3, q_dtype=msa.Q_BF16, num_splits=1)
+                kv_dtype=msa.KV_FP8_E4M3, q_dtype=msa.Q_BF16, num_splits=1, tile_rows=0)
     base.update(kw)
     return msa._PrefillShape(*[base[f] for f, _ in msa._PrefillShape._fields_])
 
@@ -413,3 +414,52 @@ def test_prefill_and_decode_plans_do_not_mix(lib):
     finally:
         lib.msa_sparse_decode_plan_destroy(hp)
         lib.msa_sparse_decode_plan_destroy(hd)
+
+
+# ---------------------------------------------------------------------------
+# dense decode and multi-row tiles
+# ---------------------------------------------------------------------------
+
+def test_dense_plan_rules(lib):
+    # dense decode: topk_blocks = 0, on multi-row tiles only
+    st, msg = plan_status(lib, shape(topk_blocks=0))
+    assert st == 0, msg
+    st, msg = plan_status(lib, shape(topk_blocks=0, tile_rows=1))
+    assert st == msa.MSA_ERR_UNSUPPORTED and "dense" in msg
+    st, msg = prefill_plan_status(lib, prefill_shape(topk_blocks=0))
+    assert st == msa.MSA_ERR_UNSUPPORTED and "prefill" in msg
+
+
+def test_plan_tile_choice_is_reported():
+    """The plan's kernel choice: single rows for short sparse decode, 8-row tiles
+    for long decode query lengths and prefill, 4-row tiles for short dense."""
+    cases = [(dict(dql=4, topk=16), 1), (dict(dql=32, topk=16), 8), (dict(dql=4, topk=0), 4),
+             (dict(dql=1, topk=0), 4), (dict(dql=8, topk=0), 8)]
+    for kw, rows in cases:
+        plan = msa.msa_sparse_decode_plan(16, kw["dql"], num_q_heads=64, num_kv_heads=4,
+                                          page_table_stride=64, topk_blocks=kw["topk"],
+                                          kv_dtype=msa.KV_FP8_E4M3, num_splits=1, device=0)
+        assert plan.tile_rows == rows and plan.dense == (kw["topk"] == 0), kw
+        plan.close()
+    plan = msa.msa_sparse_prefill_plan(3, 505, num_q_heads=16, num_kv_heads=1,
+                                       page_table_stride=9, topk_blocks=16,
+                                       kv_dtype=msa.KV_FP8_E4M3, num_splits=1, device=0)
+    assert plan.tile_rows == 8 and plan.prefill
+    plan.close()
+
+
+def test_dense_and_sparse_runs_check_topk(lib):
+    kvs = msa._I64x4(256 * 128, 256 * 128, 256, 1)
+    tks = msa._I64x3(16, 16, 1)
+    hd = _plan(lib, topk_blocks=0)
+    hs = _plan(lib)
+    try:
+        st = lib.msa_sparse_decode_run(hd, FAKE, FAKE, kvs, 10, 1.0, 1.0, 1.0, FAKE, FAKE, FAKE,
+                                       tks, FAKE, 0.08, None)
+        assert st == msa.MSA_ERR_INVALID_ARG and "topk = NULL" in lib.msa_last_error().decode()
+        st = lib.msa_sparse_decode_run(hs, FAKE, FAKE, kvs, 10, 1.0, 1.0, 1.0, FAKE, FAKE, None,
+                                       tks, FAKE, 0.08, None)
+        assert st == msa.MSA_ERR_INVALID_ARG and "topk" in lib.msa_last_error().decode()
+    finally:
+        lib.msa_sparse_decode_plan_destroy(hd)
+        lib.msa_sparse_decode_plan_destroy(hs)

@@ -35,13 +35,14 @@ def test_prefill_test_page_shape(heads, qfmt, splits):
     assert_parity(to_f64(d.out), oracle_prefill(case), what="prefill test-page shape")
 
 
+@pytest.mark.parametrize("tile_rows", [1, 4, 8])
 @pytest.mark.parametrize("kvd", [gen.KV_FP8, gen.KV_BF16, gen.KV_E5M2])
-def test_prefill_chunks_over_context_with_empty_request_and_padding(kvd):
-    _banner(f"chunked prefill kv={kvd}")
+def test_prefill_chunks_over_context_with_empty_request_and_padding(kvd, tile_rows):
+    _banner(f"chunked prefill kv={kvd} tile_rows={tile_rows}")
     case = gen.make_prefill_case(42, [37, 0, 200, 1, 64], [5000, 900, 3000, 129, 64], 32, 4,
                                  kv_dtype=kvd, rule="zipf", pad_rows=5)
     d = PrefillDevCase(case)
-    d.run(d.plan())
+    d.run(d.plan(tile_rows=tile_rows))
     torch.cuda.synchronize()
     got = to_f64(d.out)
     assert_parity(got, oracle_prefill(case), what=f"chunked prefill {kvd}")

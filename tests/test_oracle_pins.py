@@ -716,3 +716,35 @@ def test_planted_prefill_mistakes_are_caught(monkeypatch):
                         lambda cu, t: (lambda r: None if r is None else max(0, r - 1))(real(cu, t)))
     with np.errstate(invalid="ignore"):
         assert not _prefill_pin_error(case) < 1e-12
+
+
+
+# ---------------------------------------------------------------------------
+# dense decode (every visible block)
+# ---------------------------------------------------------------------------
+
+def run_dense_oracle(case, **over):
+    kw = dict(q_bits=case.q, kv=case.kv, kv_dtype=case.kv_dtype, k_scale=case.k_scale,
+              v_scale=case.v_scale, block_table=case.block_table, seq_lens=case.seq_lens,
+              decode_query_len=case.dql, num_kv_heads=case.num_kv_heads,
+              sm_scale=case.sm_scale, q_dtype=case.q_dtype, q_scale=case.q_scale)
+    kw.update(over)
+    return om.dense_decode(**kw)
+
+
+@pytest.mark.parametrize("dql", [1, 4])
+@pytest.mark.parametrize("fmt", [(gen.KV_FP8, gen.Q_BF16, 1.0), (gen.KV_E5M2, gen.Q_FP8, 0.5)])
+def test_dense_decode_equals_sdpa(dql, fmt):
+    """No top-k: causal attention over the whole un-paged sequence."""
+    kv_dtype, q_dtype, q_scale = fmt
+    case = small_dense_case(8, 2, dql, kv_dtype, pattern=(257, 1300), q_dtype=q_dtype,
+                            q_scale=q_scale)
+    got = run_dense_oracle(case)
+    assert float(np.max(np.abs(got - dense_reference(case)))) < 1e-12
+
+
+def test_dense_decode_planted_mistake_is_caught(monkeypatch):
+    case = small_dense_case(8, 2, 3, pattern=(300, 700))
+    monkeypatch.setattr(om, "visible_rows",
+                        lambda pos, b: 0 if b < 0 or b * 128 > pos else min(128, pos - b * 128))
+    assert not float(np.max(np.abs(run_dense_oracle(case) - dense_reference(case)))) < 1e-12

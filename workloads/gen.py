@@ -442,6 +442,30 @@ def _make_c4(replicas: int, poison: bool) -> DecodeCase:
                       notes="rows 512..515 are padding rows")
 
 
+def make_dense_config(name: str, replicas: int = 0, poison: bool = True) -> DecodeCase:
+    """Dense decode (every visible block; M3's first layers): the TP1 decode
+    shape -- B=16, dql=4, 64/4 heads, fp8 e4m3, seq U[32768, 131072] -- with
+    no top-k (seed 7)."""
+    if name != "d1_dense_tp1":
+        raise KeyError(name)
+    rng = np.random.default_rng(7)
+    B, dql, hq, hkv = 16, 4, 64, 4
+    seq = rng.integers(32768, 131072, size=B, endpoint=True).astype(np.int32)
+    bt, total, spare = paged_layout(rng, seq, spare_pages=1)
+    kv = make_pool(rng, total, hkv, KV_FP8, 0.5)
+    if poison:
+        fill_pages(kv, spare, KV_FP8)
+        poison_tail_slots(kv, bt, seq, KV_FP8)
+    q = make_q(rng, B * dql, hq)
+    reps = [(make_q(rng, B * dql, hq), None) for _ in range(replicas)]
+    return DecodeCase(name, 7, B, dql, B * dql, hq, hkv, 0, KV_FP8, seq, bt, kv, q, None,
+                      max_blocks=int(bt.shape[1]), replicas=reps,
+                      notes="dense: every visible block, no top-k")
+
+
+DENSE_CONFIG_NAMES = ("d1_dense_tp1",)
+
+
 def c5_seq_lens(rng: np.random.Generator, B: int = 64) -> np.ndarray:
     mu = math.log(math.sqrt(8192.0 * 262144.0))
     sigma = math.log(32.0) / 4.0
