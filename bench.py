@@ -41,7 +41,7 @@ METRIC = "decode tokens/s and effective KV GB/s (% HBM peak), sparse GQA attend,
 HBM_PEAK_GBS = 8000.0
 DEFAULT_CONFIG = "c2_tp4_fp8"
 OTHER_CONFIGS = ("c3_tp1_fp8", "c4_spec_ragged", "c2_tp4_fp8q", "c2_tp4_e5m2",
-                 "pf1_chunked_prefill")
+                 "pf1_chunked_prefill", "d1_dense_tp1")
 FULL_STEP_CONFIG = "c5_full_step"
 # rocprofv3 counter summaries, each valid for the kernel sources it was taken on
 TRAFFIC_FILES = {"attend": os.path.join(ROOT, "profiles", "attend_traffic.json"),
@@ -71,6 +71,8 @@ CONFIG_TEXT = {
     "pf1_chunked_prefill": "chunked prefill: 4 requests x 1024-token chunks after a cached "
                            "context of U[16384,65536], 64/4 heads, fp8, top-16 per (token, "
                            "kv head), recent-biased",
+    "d1_dense_tp1": "dense decode (every visible block): B=16, dql=4, 64/4 heads, fp8, "
+                    "seq U[32768,131072]",
 }
 
 
@@ -100,7 +102,12 @@ def step_bytes(case, q, topk):
     else:
         r = t // case.dql
         pos = case.seq_lens[r].astype(np.int64) - case.dql + (t % case.dql)
-    b = topk[:real].astype(np.int64)                       # [T, Hkv, k]
+    if topk is None:   # dense: every visible block of every (row, kv head)
+        nb_all = int(pos.max()) // 128 + 1 if real else 0
+        b = np.broadcast_to(np.arange(nb_all, dtype=np.int64)[None, None, :],
+                            (real, case.num_kv_heads, nb_all))
+    else:
+        b = topk[:real].astype(np.int64)                   # [T, Hkv, k]
     start = b * 128
     live = (b >= 0) & (start <= pos[:, None, None]) & (b < case.block_table.shape[1])
     nvis = np.where(live, np.minimum(128, pos[:, None, None] - start + 1), 0)
@@ -117,7 +124,7 @@ def step_bytes(case, q, topk):
     n_live = int(live.sum())
     q_bytes = real * case.num_q_heads * 128 * (1 if case.q_dtype == "fp8_e4m3" else 2)
     out_bytes = case.num_token_rows * case.num_q_heads * 128 * 2
-    idx_bytes = real * case.num_kv_heads * case.topk_k * 4
+    idx_bytes = 0 if topk is None else real * case.num_kv_heads * case.topk_k * 4
     meta = idx_bytes + n_live * 4 + case.batch * 4
     return {
         "effective_kv": eff_kv,
@@ -169,7 +176,7 @@ def _q_code(case):
 class DeviceSet:
     """R replicas of one step's inputs, each over its own copy of the pool."""
 
-    def __init__(self, case, replicas: int, splits: int, dev):
+    def __init__(self, case, replicas: int, splits: int, dev, tile_rows: int = 0):
         import numpy as np
         import torch
 
@@ -177,6 +184,7 @@ class DeviceSet:
 
         self.case = case
         self.prefill = hasattr(case, "cu_seqlens_q")
+        self.dense = case.topk is None
         host = _host_kv(case)
         nb = int(case.kv.shape[0])
         self.kv = torch.empty((replicas * nb,) + tuple(host.shape[1:]), dtype=host.dtype,
@@ -197,7 +205,7 @@ class DeviceSet:
             bt = torch.from_numpy((case.block_table.astype(np.int64) + i * nb).astype(
                 np.int32)).to(dev)
             q = _host_q(case, qh).to(dev)
-            topk = torch.from_numpy(tk).to(dev)
+            topk = None if tk is None else torch.from_numpy(tk).to(dev)
             out = torch.empty(tuple(q.shape), dtype=torch.bfloat16, device=dev)
             self.steps.append((q, bt, topk, out))
             self.bytes.append(step_bytes(case, qh, tk))
@@ -206,13 +214,14 @@ class DeviceSet:
                 case.batch, case.num_token_rows, num_q_heads=case.num_q_heads,
                 num_kv_heads=case.num_kv_heads, page_table_stride=case.block_table.shape[1],
                 topk_blocks=case.topk_k, kv_dtype=_kv_code(case), q_dtype=_q_code(case),
-                num_splits=splits, device=dev)
+                num_splits=splits, tile_rows=tile_rows, device=dev)
         else:
             self.plan = msa.msa_sparse_decode_plan(
                 case.batch, case.dql, num_q_heads=case.num_q_heads,
                 num_kv_heads=case.num_kv_heads, page_table_stride=case.block_table.shape[1],
-                topk_blocks=case.topk_k, kv_dtype=_kv_code(case), q_dtype=_q_code(case),
-                num_token_rows=case.num_token_rows, num_splits=splits, device=dev)
+                topk_blocks=0 if self.dense else case.topk_k, kv_dtype=_kv_code(case),
+                q_dtype=_q_code(case), num_token_rows=case.num_token_rows, num_splits=splits,
+                tile_rows=tile_rows, device=dev)
         self.msa = msa
 
     def run_step(self, i):
@@ -241,7 +250,7 @@ class DeviceSet:
         return sum(b[key] for b in self.bytes) / len(self.bytes)
 
 
-def time_config(name, steps, warmup, replicas, splits, dev, verbose=True):
+def time_config(name, steps, warmup, replicas, splits, dev, verbose=True, tile_rows=0):
     import torch
 
     from workloads import gen
@@ -249,9 +258,11 @@ def time_config(name, steps, warmup, replicas, splits, dev, verbose=True):
     t0 = time.time()
     if name in gen.PREFILL_CONFIG_NAMES:
         case = gen.make_prefill_config(name, replicas=replicas - 1)
+    elif name in gen.DENSE_CONFIG_NAMES:
+        case = gen.make_dense_config(name, replicas=replicas - 1)
     else:
         case = gen.make_config(name, replicas=replicas - 1)
-    ds = DeviceSet(case, replicas, splits, dev)
+    ds = DeviceSet(case, replicas, splits, dev, tile_rows=tile_rows)
     if verbose:
         print(f"[bench] {name}: generated + uploaded in {time.time() - t0:.1f}s "
               f"(pool {case.kv.nbytes / 2**20:.0f} MiB x {replicas}, splits "
@@ -317,6 +328,7 @@ def time_config(name, steps, warmup, replicas, splits, dev, verbose=True):
         "unique_kv_bytes": uniq,
         "algorithmic_bytes": alg,
         "splits": ds.plan.num_splits,
+        "tile_rows": ds.plan.tile_rows,
         "launches_per_step": 1 if ds.plan.num_splits == 1 else 2,
         "attend_ms": attend_ms,
         "real_rows": case.real_rows,
@@ -611,6 +623,8 @@ def main():
                     help="time only the full step with the indexer and print its record")
     ap.add_argument("--replicas", type=int, default=8)
     ap.add_argument("--splits", type=int, default=0, help="0 = the plan's choice")
+    ap.add_argument("--tile-rows", type=int, default=0,
+                    help="token rows per workgroup: 0 = the plan's choice, 1, 2 or 4")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-other-configs", action="store_true")
@@ -650,7 +664,7 @@ def main():
         print(json.dumps(r5), flush=True)
         return
     res, case = time_config(args.config, args.steps, args.warmup, args.replicas,
-                            args.splits, dev)
+                            args.splits, dev, tile_rows=args.tile_rows)
     others = {}
     if not args.no_other_configs:
         for name in OTHER_CONFIGS:

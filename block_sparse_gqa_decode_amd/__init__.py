@@ -274,7 +274,7 @@ def msa_sparse_decode_plan(batch: int, decode_query_len: int, *, num_q_heads: in
                            device=None) -> DecodePlan:
     """topk_blocks = 0 plans dense decode (every visible block; run with
     topk=None).  tile_rows: 0 = the plan's choice, 1 = one token row per
-    workgroup, 4 / 8 = multi-row tiles."""
+    workgroup, 2 / 4 = multi-row tiles."""
     lib = load_library()
     shape = _Shape(batch, decode_query_len, num_token_rows, page_table_stride, num_q_heads,
                    num_kv_heads, page_size, head_dim, topk_blocks, kv_dtype, num_splits,

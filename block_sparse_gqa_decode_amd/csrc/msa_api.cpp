@@ -147,7 +147,7 @@ msa_status check_kv(const void* kv_cache, const int64_t kv_strides[4], int64_t n
 // block), so they split further.
 int32_t choose_splits(const msa_decode_shape* s, int64_t units, bool dense) {
   if (s->num_splits > 0) return s->num_splits;
-  const int64_t target = dense ? 512 : 256;
+  const int64_t target = dense ? 1024 : 256;
   const int32_t cap = dense ? msa::kMaxSplits : (s->topk_blocks < 8 ? s->topk_blocks : 8);
   int32_t splits = 1;
   while (units * splits < target && splits * 2 <= cap) splits *= 2;
@@ -196,15 +196,18 @@ msa_status msa_sparse_decode_plan(const msa_decode_shape* shape, int device, msa
 static msa_status choose_tiles(const msa_decode_shape* s, bool prefill, bool dense,
                                int32_t num_rows, int32_t* tile_rows, int64_t* units) {
   int32_t tr = s->tile_rows;
-  if (tr != 0 && tr != 1 && tr != 4 && tr != 8)
-    return fail(MSA_ERR_INVALID_ARG, "tile_rows must be 0 (auto), 1, 4 or 8 (got %d)", tr);
+  if (tr != 0 && tr != 1 && tr != 2 && tr != 4)
+    return fail(MSA_ERR_INVALID_ARG, "tile_rows must be 0 (auto), 1, 2 or 4 (got %d)", tr);
   if (tr == 0) {
-    if (dense) tr = s->decode_query_len <= 4 ? 4 : 8;
-    else if (prefill || s->decode_query_len >= 8) tr = 8;
-    else tr = 1;
+    // Measured on one MI355X: rows that share many pages (long decode query
+    // lengths, prefill chunks) gain from 2-row tiles; dense decode, where every
+    // row of a request shares every page, from 4-row tiles; rows that share
+    // few pages run faster one per workgroup.
+    if (dense) tr = s->decode_query_len <= 2 ? 2 : 4;
+    else tr = (prefill || s->decode_query_len >= 8) ? 2 : 1;
   }
   if (dense && tr == 1)
-    return fail(MSA_ERR_UNSUPPORTED, "dense decode runs on multi-row tiles (tile_rows 4 or 8)");
+    return fail(MSA_ERR_UNSUPPORTED, "dense decode runs on multi-row tiles (tile_rows 2 or 4)");
   int64_t tiles;
   if (tr == 1) tiles = num_rows;
   else if (dense)  // request-aligned tiles, then tiles of padding rows

@@ -70,208 +70,11 @@
 // cache bytes cannot reach the MFMAs.
 #include "msa_device.h"
 #include "msa_internal.h"
+#include "msa_page.h"
 #include "msa_rows.h"
 
 namespace msa {
 namespace {
-
-constexpr int kWaves = 4;      // wavefronts sharing one page (32 keys each)
-constexpr int kThreads = 64 * kWaves;
-constexpr int kDepth = 2;      // pages per wavefront in the register ring
-constexpr int kKeysPerWave = 32;
-constexpr int kOPad = 4;
-constexpr float kRescaleSlack = 8.0f;
-
-template <bool kFp8>
-struct PageRegs;
-
-template <>
-struct PageRegs<true> {
-  u32x4_t k[2][2];  // [key tile][run]: 16 fp8 each (head dims 16g.., 64+16g..)
-  u32x2_t v[8];     // 8 fp8 (head dims 8n..8n+7) of key slot j
-};
-
-template <>
-struct PageRegs<false> {
-  u32x4_t k[2][4];  // [key tile][chunk]: 8 bf16 each
-  u32x4_t v[8];     // 8 bf16 of key slot j
-};
-
-__device__ __forceinline__ int key_of_slot(int g, int j) {
-  return j < 4 ? 4 * g + j : 16 + 4 * g + (j - 4);
-}
-
-// Per-lane constants of the page loads: the page rows a lane reads for the two
-// S^T tiles and the eight P^T / V^T slots, and its byte columns.
-struct LaneRows {
-  int rk[2];
-  int rv[8];
-  uint32_t ck;  // first K byte of the lane's runs
-  uint32_t cv;  // first V byte of the lane's run
-};
-
-template <bool kFp8>
-__device__ __forceinline__ LaneRows lane_rows(int kbase, int n, int g) {
-  LaneRows lr;
-#pragma unroll
-  for (int tau = 0; tau < 2; ++tau) lr.rk[tau] = kbase + 16 * tau + n;
-#pragma unroll
-  for (int j = 0; j < 8; ++j) lr.rv[j] = kbase + key_of_slot(g, j);
-  lr.ck = kFp8 ? 16u * g : 32u * g;
-  lr.cv = kFp8 ? kHeadDim + 8u * n : 2 * kHeadDim + 16u * n;
-  return lr;
-}
-
-// Loads of one page into registers.  `page` is wave-uniform (SGPRs); rows are
-// clamped to the last visible row `lim`, so rows past it are never read; the
-// per-lane part of every address is a 32-bit offset.
-template <bool kFp8>
-__device__ __forceinline__ void load_page(PageRegs<kFp8>& r, const uint8_t* page,
-                                          uint32_t row_stride, int lim, const LaneRows& lr) {
-#pragma unroll
-  for (int tau = 0; tau < 2; ++tau) {
-    const uint32_t off = (uint32_t)min(lr.rk[tau], lim) * row_stride + lr.ck;
-    if constexpr (kFp8) {
-      r.k[tau][0] = *reinterpret_cast<const u32x4_t*>(page + off);
-      r.k[tau][1] = *reinterpret_cast<const u32x4_t*>(page + off + 64);
-    } else {
-      r.k[tau][0] = *reinterpret_cast<const u32x4_t*>(page + off);
-      r.k[tau][1] = *reinterpret_cast<const u32x4_t*>(page + off + 16);
-      r.k[tau][2] = *reinterpret_cast<const u32x4_t*>(page + off + 128);
-      r.k[tau][3] = *reinterpret_cast<const u32x4_t*>(page + off + 144);
-    }
-  }
-#pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    const uint32_t off = (uint32_t)min(lr.rv[j], lim) * row_stride + lr.cv;
-    if constexpr (kFp8) {
-      r.v[j] = *reinterpret_cast<const u32x2_t*>(page + off);
-    } else {
-      r.v[j] = *reinterpret_cast<const u32x4_t*>(page + off);
-    }
-  }
-}
-
-// S^T tile tau (16 keys x 16 q rows) of one page.
-template <int kKv, int kQ>
-__device__ __forceinline__ f32x4_t score_tile(const PageRegs<kKv != kKvBf16>& r,
-                                              const QRegs<kQ>& q, int tau) {
-  const f32x4_t zero = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  if constexpr (kQ == kQE4m3) {
-    return mfma_f8_16x16x128<kKv == kKvE5m2 ? 1 : 0, 0>(cat_i32x8(r.k[tau][0], r.k[tau][1]),
-                                                         q.b, zero);
-  } else {
-    bf16x8_t kf[4];
-    if constexpr (kKv != kKvBf16) {
-      kf[0] = as_bf16x8(f8x8_to_bf16x8<kKv>(r.k[tau][0].x, r.k[tau][0].y));
-      kf[1] = as_bf16x8(f8x8_to_bf16x8<kKv>(r.k[tau][0].z, r.k[tau][0].w));
-      kf[2] = as_bf16x8(f8x8_to_bf16x8<kKv>(r.k[tau][1].x, r.k[tau][1].y));
-      kf[3] = as_bf16x8(f8x8_to_bf16x8<kKv>(r.k[tau][1].z, r.k[tau][1].w));
-    } else {
-#pragma unroll
-      for (int c = 0; c < 4; ++c) kf[c] = as_bf16x8(r.k[tau][c]);
-    }
-    f32x4_t s = zero;
-#pragma unroll
-    for (int c = 0; c < 4; ++c) s = mfma_bf16_16x16x32(kf[c], q.f[c], s);
-    return s;
-  }
-}
-
-template <int kKv, int kQ>
-__device__ __forceinline__ void attend_page(const PageRegs<kKv != kKvBf16>& r,
-                                            const QRegs<kQ>& qf, int kbase,
-                                            int nvis, int g, float scale_log2,
-                                            float& m_run, float& l_part,
-                                            f32x4_t (&o)[8]) {
-  // S^T for the wavefront's two 16-key tiles.
-  f32x4_t s[2];
-#pragma unroll
-  for (int tau = 0; tau < 2; ++tau) s[tau] = score_tile<kKv, kQ>(r, qf, tau);
-
-  // Raw scores; keys past the visible count (only on a token's last page)
-  // become -inf.  The positive scale is applied after the max.
-  float z[8];
-#pragma unroll
-  for (int tau = 0; tau < 2; ++tau) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) z[4 * tau + i] = s[tau][i];
-  }
-  if (kbase + kKeysPerWave > nvis) {
-#pragma unroll
-    for (int tau = 0; tau < 2; ++tau) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        if (kbase + 16 * tau + 4 * g + i >= nvis) z[4 * tau + i] = -INFINITY;
-      }
-    }
-  }
-  // Lazy rescaling: the reference point m_run of a row only moves when one of
-  // its scores exceeds it by more than kRescaleSlack (log2 units); then
-  // probabilities stay <= 2^kRescaleSlack, far inside fp32 / bf16 range.  The
-  // test uses each lane's own maximum and one wave vote, so the cross-lane row
-  // maximum is only formed on the (rare) pages that move a reference point;
-  // m_run = -inf (no key yet) always moves.
-  const float mx = fmaxf(fmaxf(fmaxf(z[0], z[1]), fmaxf(z[2], z[3])),
-                         fmaxf(fmaxf(z[4], z[5]), fmaxf(z[6], z[7]))) * scale_log2;
-  if (__any(mx > m_run + kRescaleSlack)) {
-    const float mrow = wave_max_xor_16_32(mx);
-    const float m_new = mrow > m_run + kRescaleSlack ? mrow : m_run;
-    const float alpha = fast_exp2(m_run - m_new);
-    l_part *= alpha;
-#pragma unroll
-    for (int t8 = 0; t8 < 8; ++t8) o[t8] *= alpha;
-    m_run = m_new;
-  }
-  float pz[8];
-#pragma unroll
-  for (int e = 0; e < 8; ++e) pz[e] = fast_exp2(fmaf(z[e], scale_log2, -m_run));
-  l_part += ((pz[0] + pz[1]) + (pz[2] + pz[3])) + ((pz[4] + pz[5]) + (pz[6] + pz[7]));
-
-  u32x4_t pw;
-  pw.x = pack_bf16x2(pz[0], pz[1]);
-  pw.y = pack_bf16x2(pz[2], pz[3]);
-  pw.z = pack_bf16x2(pz[4], pz[5]);
-  pw.w = pack_bf16x2(pz[6], pz[7]);
-  const bf16x8_t pb = as_bf16x8(pw);
-
-  // V rows as bf16 pairs along the head dim: vd[j][w] = dims (8n+2w, 8n+2w+1).
-  u32x4_t vd[8];
-#pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    if constexpr (kKv != kKvBf16) {
-      vd[j] = f8x8_to_bf16x8<kKv>(r.v[j].x, r.v[j].y);
-    } else {
-      vd[j] = r.v[j];
-    }
-  }
-#pragma unroll
-  for (int t8 = 0; t8 < 8; ++t8) {
-    const uint32_t sel = (t8 & 1) ? 0x07060302u : 0x05040100u;
-    const int w = t8 >> 1;
-    u32x4_t a;
-    a.x = byte_perm(vd[1][w], vd[0][w], sel);
-    a.y = byte_perm(vd[3][w], vd[2][w], sel);
-    a.z = byte_perm(vd[5][w], vd[4][w], sel);
-    a.w = byte_perm(vd[7][w], vd[6][w], sel);
-    o[t8] = mfma_bf16_16x16x32(as_bf16x8(a), pb, o[t8]);
-  }
-}
-
-// bf16 store of one output row chunk: acc / L * v_scale, or exact zeros when
-// the row saw no key (L == 0).
-__device__ __forceinline__ void store_row(uint16_t* dst, const float (&acc)[8], float L,
-                                          float v_scale) {
-  u32x4_t ov = u32x4_t{0u, 0u, 0u, 0u};
-  if (L > 0.f) {
-    const float inv = v_scale / L;
-    ov.x = pack_bf16x2(acc[0] * inv, acc[1] * inv);
-    ov.y = pack_bf16x2(acc[2] * inv, acc[3] * inv);
-    ov.z = pack_bf16x2(acc[4] * inv, acc[5] * inv);
-    ov.w = pack_bf16x2(acc[6] * inv, acc[7] * inv);
-  }
-  *reinterpret_cast<u32x4_t*>(dst) = ov;
-}
 
 // Log-sum-exp merge of the split partials of one (token row, q head) and the
 // bf16 store of head dims d0..d0+7.

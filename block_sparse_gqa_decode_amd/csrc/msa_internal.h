@@ -17,7 +17,7 @@ constexpr int kMaxScoreBlocks = 16384;
 constexpr int kMaxScoreBatch = 4096;   // requests per scorer launch (LDS prefix sum)
 constexpr int kMaxScoreDql = 32;
 constexpr int kMaxPrefills = 1 << 20;   // requests of one prefill plan
-constexpr int kMaxTileRows = 8;        // token rows of a multi-row tile
+constexpr int kMaxTileRows = 4;        // token rows of a multi-row tile
 constexpr int kMaxUnion = kMaxTileRows * kMaxTopk;   // pages of a tile's union
 constexpr int kXcdSlots = 8;   // XCDs a launch is dealt across, round robin
 
@@ -79,7 +79,7 @@ struct SelectParams {
 // kv_fmt: kKv*; q_fmt: kQ*.  An fp8 q needs an 8-bit KV format.
 hipError_t launch_attend(const AttendParams& p, int kv_fmt, int q_fmt, hipStream_t stream);
 hipError_t launch_merge(const AttendParams& p, hipStream_t stream);
-// Multi-row tiles of tile_rows (4 or 8) token rows; p.num_units = tiles * hkv.
+// Multi-row tiles of tile_rows (2 or 4) token rows; p.num_units = tiles * hkv.
 hipError_t launch_tile(const AttendParams& p, int kv_fmt, int q_fmt, int tile_rows,
                        hipStream_t stream);
 hipError_t launch_score(const ScoreParams& p, int kv_fmt, int q_fmt, hipStream_t stream);

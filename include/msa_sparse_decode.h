@@ -99,8 +99,8 @@ typedef struct msa_decode_shape {
   int32_t q_dtype;            /* msa_q_dtype                                     */
   int32_t tile_rows;          /* token rows per workgroup: 0 lets the plan
                                  choose; 1 = one row per workgroup (sparse only);
-                                 4 or 8 = multi-row tiles that read each page
-                                 shared by their rows once                       */
+                                 2 or 4 = multi-row tiles that read and widen
+                                 each page shared by their rows once             */
 } msa_decode_shape;
 
 /* Static shape of one ragged prefill step (the prefill call of

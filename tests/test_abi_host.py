@@ -101,6 +101,7 @@ def test_decode_query_len_bounds(lib, batch, dql, hq, hkv, ok):
     ("num_q_heads", 64, msa.MSA_ERR_UNSUPPORTED, "GQA group"),
     ("topk_blocks", -1, msa.MSA_ERR_INVALID_ARG, "topk_blocks"),
     ("tile_rows", 3, msa.MSA_ERR_INVALID_ARG, "tile_rows"),
+    ("tile_rows", 8, msa.MSA_ERR_INVALID_ARG, "tile_rows"),
     ("topk_blocks", 65, msa.MSA_ERR_UNSUPPORTED, "topk_blocks"),
     ("batch", 0, msa.MSA_ERR_INVALID_ARG, "batch"),
     ("page_table_stride", 0, msa.MSA_ERR_INVALID_ARG, "page_table_stride"),
@@ -431,10 +432,11 @@ def test_dense_plan_rules(lib):
 
 
 def test_plan_tile_choice_is_reported():
-    """The plan's kernel choice: single rows for short sparse decode, 8-row tiles
-    for long decode query lengths and prefill, 4-row tiles for short dense."""
-    cases = [(dict(dql=4, topk=16), 1), (dict(dql=32, topk=16), 8), (dict(dql=4, topk=0), 4),
-             (dict(dql=1, topk=0), 4), (dict(dql=8, topk=0), 8)]
+    """The plan's kernel choice (the measured faster one): single rows for short
+    sparse decode, 2-row tiles for long decode query lengths and prefill, 4-row
+    tiles for dense decode."""
+    cases = [(dict(dql=4, topk=16), 1), (dict(dql=32, topk=16), 2), (dict(dql=4, topk=0), 4),
+             (dict(dql=1, topk=0), 2), (dict(dql=8, topk=0), 4)]
     for kw, rows in cases:
         plan = msa.msa_sparse_decode_plan(16, kw["dql"], num_q_heads=64, num_kv_heads=4,
                                           page_table_stride=64, topk_blocks=kw["topk"],
@@ -444,7 +446,7 @@ def test_plan_tile_choice_is_reported():
     plan = msa.msa_sparse_prefill_plan(3, 505, num_q_heads=16, num_kv_heads=1,
                                        page_table_stride=9, topk_blocks=16,
                                        kv_dtype=msa.KV_FP8_E4M3, num_splits=1, device=0)
-    assert plan.tile_rows == 8 and plan.prefill
+    assert plan.tile_rows == 2 and plan.prefill
     plan.close()
 
 
