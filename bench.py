@@ -48,6 +48,8 @@ TRAFFIC_FILES = {"attend": os.path.join(ROOT, "profiles", "attend_traffic.json")
                  "score": os.path.join(ROOT, "profiles", "score_traffic.json")}
 KERNEL_SOURCES = {
     "attend": ("block_sparse_gqa_decode_amd/csrc/msa_attend.hip",
+               "block_sparse_gqa_decode_amd/csrc/msa_page.h",
+               "block_sparse_gqa_decode_amd/csrc/msa_rows.h",
                "block_sparse_gqa_decode_amd/csrc/msa_device.h",
                "block_sparse_gqa_decode_amd/csrc/msa_internal.h"),
     "score": ("block_sparse_gqa_decode_amd/csrc/msa_score.hip",
