@@ -530,10 +530,23 @@ def cpu_baseline(case, seconds: float):
         done = False
         while not done:
             for t in order:
-                om.sparse_decode(case.q, case.kv, case.kv_dtype, case.k_scale,
-                                 case.v_scale, case.block_table, case.seq_lens, case.topk,
-                                 case.dql, case.num_kv_heads, case.sm_scale, rows=[int(t)],
-                                 q_dtype=case.q_dtype, q_scale=case.q_scale)
+                if hasattr(case, "cu_seqlens_q"):
+                    om.sparse_prefill(case.q, case.kv, case.kv_dtype, case.k_scale,
+                                      case.v_scale, case.block_table, case.cu_seqlens_q,
+                                      case.context_lens, case.topk, case.num_kv_heads,
+                                      case.sm_scale, rows=[int(t)], q_dtype=case.q_dtype,
+                                      q_scale=case.q_scale)
+                elif case.topk is None:
+                    om.dense_decode(case.q, case.kv, case.kv_dtype, case.k_scale,
+                                    case.v_scale, case.block_table, case.seq_lens, case.dql,
+                                    case.num_kv_heads, case.sm_scale, rows=[int(t)],
+                                    q_dtype=case.q_dtype, q_scale=case.q_scale)
+                else:
+                    om.sparse_decode(case.q, case.kv, case.kv_dtype, case.k_scale,
+                                     case.v_scale, case.block_table, case.seq_lens, case.topk,
+                                     case.dql, case.num_kv_heads, case.sm_scale,
+                                     rows=[int(t)], q_dtype=case.q_dtype,
+                                     q_scale=case.q_scale)
                 rows_done += 1
                 if time.perf_counter() - t0 >= seconds:
                     done = True
@@ -691,7 +704,10 @@ def main():
         "unit": "GB/s",
         "frac": round(achieved / HBM_PEAK_GBS, 4),
         "traffic": None if traffic is None else traffic.get("hbm_bytes_per_launch"),
-        "kernel": f"attend_kernel<kv {case.kv_dtype}, q {case.q_dtype}>",
+        "kernel": (f"attend_kernel<kv {case.kv_dtype}, q {case.q_dtype}>"
+                   if res["tile_rows"] == 1 else
+                   f"multi_kernel<kv {case.kv_dtype}, q {case.q_dtype}, rows "
+                   f"{res['tile_rows']}>"),
         "algorithmic_bytes_per_launch": int(res["algorithmic_bytes"]),
         "avg_launch_us": round(kernel_s * 1e6, 3),
         "timing": "HIP events around graph replays of the attend launches alone, on "
@@ -717,10 +733,10 @@ def main():
             "workload": f"{args.config}: {CONFIG_TEXT[args.config]}",
             "kv_cache": case.kv_dtype,
             "global_batch": case.batch,
-            "decode_query_len": case.dql,
+            "decode_query_len": getattr(case, "dql", 0),
             "num_q_heads": case.num_q_heads,
             "num_kv_heads": case.num_kv_heads,
-            "topk_blocks": case.topk_k,
+            "topk_blocks": case.topk_k if case.topk is not None else "dense",
             "page_size": 128,
             "head_dim": 128,
             "replicas": args.replicas,

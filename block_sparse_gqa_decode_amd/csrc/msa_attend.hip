@@ -102,7 +102,7 @@ __device__ __forceinline__ void merge_splits(const AttendParams& p, int64_t row,
   store_row(p.out + row * kHeadDim + d0, acc, L, p.v_scale);
 }
 
-template <int kKv, int kQ>
+template <int kKv, int kQ, bool kVarlen>
 __global__ __launch_bounds__(kThreads) void attend_kernel(AttendParams p) {
   constexpr bool kFp8 = kKv != kKvBf16;  // 8-bit K|V entries
   __shared__ int32_t s_page[kMaxTopk];
@@ -127,8 +127,20 @@ __global__ __launch_bounds__(kThreads) void attend_kernel(AttendParams p) {
   const int rows = p.group;  // q heads of the unit = MFMA rows in use
   const int head0 = h * p.group;
 
+  // Decode rows are computed inline (the request index stays a scalar, so
+  // seq_lens[r] is a scalar load); prefill rows use the binary search.
   int r = 0, pos = 0;
-  if (!locate_token(p, t, r, pos)) {
+  bool live;
+  if constexpr (!kVarlen) {
+    live = t < p.real_rows;
+    if (live) {
+      r = t / p.dql;
+      pos = p.seq_lens[r] - p.dql + (t - r * p.dql);
+    }
+  } else {
+    live = locate_token<1>(p, t, r, pos);
+  }
+  if (!live) {
     // Padding row: exact zeros, written once.
     if (split == 0) {
       const int qr = tid >> 4;
@@ -367,27 +379,35 @@ __global__ __launch_bounds__(256) void fp8_to_bf16_kernel(const uint8_t* in, uin
 
 }  // namespace
 
-hipError_t launch_attend(const AttendParams& p, int kv_fmt, int q_fmt, hipStream_t stream) {
-  const int64_t groups = ((int64_t)p.num_units + kXcdSlots - 1) / kXcdSlots;
-  const int64_t grid = groups * kXcdSlots * p.splits;
-  if (grid <= 0) return hipSuccess;
-  const dim3 gd((uint32_t)grid), bd(kThreads);
+template <bool kVarlen>
+static hipError_t launch_attend_rows(const AttendParams& p, int kv_fmt, int q_fmt, dim3 gd,
+                                     hipStream_t stream) {
+  const dim3 bd(kThreads);
   if (q_fmt == kQE4m3) {
     if (kv_fmt == kKvE4m3)
-      hipLaunchKernelGGL((attend_kernel<kKvE4m3, kQE4m3>), gd, bd, 0, stream, p);
+      hipLaunchKernelGGL((attend_kernel<kKvE4m3, kQE4m3, kVarlen>), gd, bd, 0, stream, p);
     else if (kv_fmt == kKvE5m2)
-      hipLaunchKernelGGL((attend_kernel<kKvE5m2, kQE4m3>), gd, bd, 0, stream, p);
+      hipLaunchKernelGGL((attend_kernel<kKvE5m2, kQE4m3, kVarlen>), gd, bd, 0, stream, p);
     else
       return hipErrorInvalidValue;
   } else {
     if (kv_fmt == kKvE4m3)
-      hipLaunchKernelGGL((attend_kernel<kKvE4m3, kQBf16>), gd, bd, 0, stream, p);
+      hipLaunchKernelGGL((attend_kernel<kKvE4m3, kQBf16, kVarlen>), gd, bd, 0, stream, p);
     else if (kv_fmt == kKvE5m2)
-      hipLaunchKernelGGL((attend_kernel<kKvE5m2, kQBf16>), gd, bd, 0, stream, p);
+      hipLaunchKernelGGL((attend_kernel<kKvE5m2, kQBf16, kVarlen>), gd, bd, 0, stream, p);
     else
-      hipLaunchKernelGGL((attend_kernel<kKvBf16, kQBf16>), gd, bd, 0, stream, p);
+      hipLaunchKernelGGL((attend_kernel<kKvBf16, kQBf16, kVarlen>), gd, bd, 0, stream, p);
   }
   return hipGetLastError();
+}
+
+hipError_t launch_attend(const AttendParams& p, int kv_fmt, int q_fmt, hipStream_t stream) {
+  const int64_t groups = ((int64_t)p.num_units + kXcdSlots - 1) / kXcdSlots;
+  const int64_t grid = groups * kXcdSlots * p.splits;
+  if (grid <= 0) return hipSuccess;
+  const dim3 gd((uint32_t)grid);
+  return p.cu_q != nullptr ? launch_attend_rows<true>(p, kv_fmt, q_fmt, gd, stream)
+                           : launch_attend_rows<false>(p, kv_fmt, q_fmt, gd, stream);
 }
 
 hipError_t launch_merge(const AttendParams& p, hipStream_t stream) {

@@ -15,8 +15,13 @@ namespace msa {
 // "vllm.models.minimax_m3.common.sparse_attention",
 // MiniMaxM3SparsePrefillMetadata).  The lookup is a binary search, so r stays
 // in [0, num_reqs) whatever the device data holds.
+// kVarlen selects the form at compile time (false: decode rows, true: ragged
+// prefill rows) so a decode kernel carries no prefill code; the default reads
+// the form from the parameters.
+template <int kVarlen = -1>
 __device__ __forceinline__ bool locate_token(const AttendParams& p, int t, int& r, int& pos) {
-  if (p.cu_q == nullptr) {
+  const bool varlen = kVarlen < 0 ? p.cu_q != nullptr : kVarlen != 0;
+  if (!varlen) {
     if (t >= p.real_rows) return false;
     r = t / p.dql;
     pos = p.seq_lens[r] - p.dql + (t - r * p.dql);
