@@ -63,9 +63,25 @@ design notes):
    ``q_scale`` too (1 by default).
 10. Prefill token rows at or past ``cu_seqlens_q[-1]`` are padding rows
     (zeros); a request with ``q_len = 0`` owns no row.
+11. The 4-bit cache is an MXFP4 analogue of the pages' NVFP4 cache (vLLM
+    test file, ``_make_nvfp4_kv_cache`` and
+    ``test_nvfp4_kv_cache_views_address_head_slots``).  Kept from the pages:
+    a page holds ``2*Hkv`` head slots; slot ``2h`` is K of kv head h and slot
+    ``2h+1`` its V, so a head is one contiguous run of the page; a slot holds
+    the 128 rows' packed 4-bit data, then the 128 rows' block scales; a
+    per-tensor global ``k_scale`` / ``v_scale`` applies on top.  Changed for
+    the OCP MX formats gfx950 decodes natively: elements are OCP e2m1
+    (``±{0, 0.5, 1, 1.5, 2, 3, 4, 6}``), one E8M0 scale ``2^(E-127)``
+    (``E = 255`` is NaN) covers 32 consecutive head dims of a row (4 bytes
+    per row instead of NVFP4's 8 e4m3 scales per 16), V scales are stored
+    row-linear like K's (NVFP4's swizzle is a tensor-core layout), element
+    ``2i`` of a row sits in the low nibble of byte ``i``, and the global
+    scales multiply, as ``k_scale`` / ``v_scale`` do for fp8.  A value is
+    ``e2m1 * 2^(E-127) * k_scale`` (resp. ``v_scale``).
 
 Pins: every function here is checked in ``tests/test_oracle_pins.py`` against
-something other than itself (torch's fp8/bf16 casts, dense causal attention
+something other than itself (torch's fp8/bf16/E8M0 casts, the OCP MX FP4
+value table, dense causal attention
 through ``torch.nn.functional.scaled_dot_product_attention``, closed forms,
 invariances, brute-force loops).
 """
@@ -136,6 +152,67 @@ def decode_bf16(bits) -> np.ndarray:
     b = np.asarray(bits).astype(np.uint32) << np.uint32(16)
     with np.errstate(invalid="ignore"):
         return b.view(np.float32).astype(np.float64)
+
+
+def decode_e2m1(codes) -> np.ndarray:
+    """OCP FP4 e2m1 code (low 4 bits) -> float64 value.
+
+    Bit fields: sign s (bit 3), exponent E (bits 2..1, bias 1), mantissa M
+    (bit 0).  E == 0 is subnormal ``M/2``; otherwise ``(1 + M/2) * 2^(E-1)``.
+    No infinities or NaN; largest magnitude 6.
+    """
+    c = np.asarray(codes).astype(np.int64) & 0xF
+    s = (c >> 3) & 1
+    e = (c >> 1) & 0x3
+    m = c & 0x1
+    sign = np.where(s == 1, -1.0, 1.0)
+    sub = sign * (m / 2.0)
+    nor = sign * (1.0 + m / 2.0) * np.exp2(e.astype(np.float64) - 1.0)
+    return np.where(e == 0, sub, nor).astype(np.float64)
+
+
+def decode_e8m0(codes) -> np.ndarray:
+    """OCP E8M0 scale code -> float64 ``2^(E-127)``; code 255 is NaN."""
+    c = np.asarray(codes).astype(np.int64)
+    v = np.exp2(c.astype(np.float64) - 127.0)
+    return np.where(c == 255, np.nan, v)
+
+
+MXFP4_BLOCK = 32                                   # head dims per E8M0 scale
+MXFP4_DATA_BYTES = PAGE * HEAD_DIM // 2            # 128 rows x 64 bytes
+MXFP4_SLOT_BYTES = MXFP4_DATA_BYTES + PAGE * HEAD_DIM // MXFP4_BLOCK   # + 128 x 4
+
+
+def mxfp4_slot(kv: np.ndarray, page: int, head: int, side: int):
+    """The (data [128, 64], scales [128, 4]) bytes of one head slot of a 4-bit
+    page (reading 11): slot ``2*head + side``, side 0 = K, 1 = V."""
+    flat = np.asarray(kv[int(page), 2 * int(head) + int(side)]).reshape(-1)
+    assert flat.size == MXFP4_SLOT_BYTES
+    data = flat[:MXFP4_DATA_BYTES].reshape(PAGE, HEAD_DIM // 2)
+    scales = flat[MXFP4_DATA_BYTES:].reshape(PAGE, HEAD_DIM // MXFP4_BLOCK)
+    return data, scales
+
+
+def mxfp4_rows(data: np.ndarray, scales: np.ndarray, n: int) -> np.ndarray:
+    """The first n rows of a 4-bit slot as float64 [n, 128]: element d of a
+    row is nibble ``d % 2`` (low first) of byte ``d // 2``, times the scale
+    of block ``d // 32``."""
+    d = np.arange(HEAD_DIM)
+    byte = data[:n, d // 2].astype(np.int64)
+    code = (byte >> (4 * (d % 2))) & 0xF
+    return decode_e2m1(code) * decode_e8m0(scales[:n, d // MXFP4_BLOCK])
+
+
+def page_kv(kv, kv_dtype: str, k_scale: float, v_scale: float, page: int, head: int,
+            n: int):
+    """Dequantized K and V rows 0..n-1 of one (page, kv head), float64."""
+    if kv_dtype == "mxfp4":
+        kd, ks = mxfp4_slot(kv, page, head, 0)
+        vd, vs = mxfp4_slot(kv, page, head, 1)
+        return (mxfp4_rows(kd, ks, n) * float(k_scale),
+                mxfp4_rows(vd, vs, n) * float(v_scale))
+    kraw, vraw = split_kv(kv[page, head, :n, :])
+    return dequant(kraw, kv_dtype, k_scale), dequant(vraw, kv_dtype, v_scale)
 
 
 def dequant(raw: np.ndarray, kv_dtype: str, scale: float) -> np.ndarray:
@@ -211,9 +288,9 @@ def gather_live(kv, kv_dtype, k_scale, v_scale, block_table_row, pos, head,
             assert b not in seen, f"duplicate block index {b}"
             seen.add(b)
         p = int(block_table_row[b])
-        kraw, vraw = split_kv(kv[p, head, :n, :])
-        ks.append(dequant(kraw, kv_dtype, k_scale))
-        vs.append(dequant(vraw, kv_dtype, v_scale))
+        k, v = page_kv(kv, kv_dtype, k_scale, v_scale, p, head, n)
+        ks.append(k)
+        vs.append(v)
     if not ks:
         return None, None
     return np.concatenate(ks, axis=0), np.concatenate(vs, axis=0)
@@ -226,7 +303,8 @@ def sparse_decode(q_bits, kv, kv_dtype, k_scale, v_scale, block_table, seq_lens,
 
     q_bits   uint16 bf16 bits, or uint8 fp8 e4m3fn codes (``q_dtype``),
              [num_token_rows, Hq, 128]; values times ``q_scale``
-    kv       uint8 (fp8 codes) or uint16 (bf16 bits) [num_blocks, Hkv, 128, 256]
+    kv       uint8 (fp8 codes) or uint16 (bf16 bits) [num_blocks, Hkv, 128, 256],
+             or uint8 [num_blocks, 2*Hkv, 128, 68] 4-bit head slots (reading 11)
     topk     int32 [num_token_rows, Hkv, k] logical block ids (-1 = none)
     rows     optional iterable of token rows to evaluate (default: all)
 
@@ -375,8 +453,7 @@ def block_max_scores(q_bits, kv, kv_dtype, k_scale, block_table, seq_lens,
                 if n <= 0:
                     continue
                 p = int(block_table[r, b])
-                kraw, _ = split_kv(kv[p, h, :n, :])
-                k = dequant(kraw, kv_dtype, k_scale)                 # [n, D]
+                k, _ = page_kv(kv, kv_dtype, k_scale, 1.0, p, h, n)  # [n, D]
                 score[h, b, i] = np.max(qs @ k.T)
     return score
 

@@ -54,13 +54,16 @@ def torch_q(q_bits: np.ndarray, q_dtype: str = gen.Q_BF16, q_scale: float = 1.0
     return v.to(torch.float64) * q_scale
 
 
-def dense_reference(case: gen.DecodeCase) -> np.ndarray:
+def dense_reference(case: gen.DecodeCase, values=None) -> np.ndarray:
     """Textbook causal GQA attention over each request's whole (un-paged)
     sequence, via SDPA in float64.  Equals the sparse attend when the index
-    lists cover every visible block."""
+    lists cover every visible block.  ``values`` (float [blocks, Hkv, 128,
+    256], K|V before the per-tensor scales) replaces torch's decode of the
+    stored entries, for a cache built from known values."""
     hq, hkv = case.num_q_heads, case.num_kv_heads
     g = hq // hkv
-    vals = torch_values(case.kv, case.kv_dtype)
+    vals = (torch_values(case.kv, case.kv_dtype) if values is None
+            else torch.from_numpy(np.asarray(values, dtype=np.float64)))
     q = torch_q(case.q, case.q_dtype, case.q_scale)
     out = torch.zeros(case.num_token_rows, hq, 128, dtype=torch.float64)
     for r in range(case.batch):
@@ -553,8 +556,192 @@ def test_select_topk_pads_when_few_visible():
 
 
 # ---------------------------------------------------------------------------
+# the 4-bit (MXFP4 head-slot) cache
+# ---------------------------------------------------------------------------
+
+# OCP Microscaling Formats (MX) v1.0 specification, FP4 (E2M1) element
+# encoding: the 16 codes' values (sign bit 3).
+OCP_E2M1_VALUES = [0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0,
+                   -0.0, -0.5, -1.0, -1.5, -2.0, -3.0, -4.0, -6.0]
+
+
+def test_e2m1_decode_matches_ocp_table():
+    got = om.decode_e2m1(np.arange(16))
+    assert np.array_equal(got, np.array(OCP_E2M1_VALUES))
+    assert np.array_equal(np.signbit(got), np.signbit(np.array(OCP_E2M1_VALUES)))
+    # only the low nibble is a code
+    assert np.array_equal(om.decode_e2m1(np.arange(16) + 0xA0), got)
+
+
+def test_e8m0_decode_exhaustive_vs_torch():
+    ref = torch.arange(256, dtype=torch.uint8).view(torch.float8_e8m0fnu).to(torch.float64)
+    got = om.decode_e8m0(np.arange(256))
+    assert np.array_equal(np.isnan(got), torch.isnan(ref).numpy())
+    fin = ~np.isnan(got)
+    assert np.array_equal(got[fin], ref.numpy()[fin])
+    assert got[127] == 1.0 and np.isnan(got[255])
+
+
+def test_mxfp4_head_slots_tile_each_head_run():
+    """As the test page's head-slot test: slot 2h (K) and 2h+1 (V) hold head
+    h's data then scales, so each head is one contiguous run of the page."""
+    hkv = 4
+    rng = np.random.default_rng(5)
+    kv = rng.integers(0, 256, size=(3, 2 * hkv, 128, 68), dtype=np.uint8)
+    runs = kv.reshape(3, hkv, 2 * om.MXFP4_SLOT_BYTES)
+    assert om.MXFP4_SLOT_BYTES == 128 * (128 // 2 + 128 // 32)
+    for p in range(3):
+        for h in range(hkv):
+            parts = []
+            for side in (0, 1):
+                data, scales = om.mxfp4_slot(kv, p, h, side)
+                assert data.shape == (128, 64) and scales.shape == (128, 4)
+                parts += [data.reshape(-1), scales.reshape(-1)]
+            assert np.array_equal(np.concatenate(parts), runs[p, h])
+
+
+def fp4_values(rng, shape):
+    """Values an MXFP4 block holds exactly: e2m1 grid values times 2^k per
+    32-block, with one +-6 per block so the block scale is exactly 2^k."""
+    mags = np.array([0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0])
+    vals = mags[rng.integers(0, 8, size=shape)] * rng.choice([-1.0, 1.0], size=shape)
+    blocks = vals.reshape(shape[:-1] + (shape[-1] // 32, 32))
+    lead = blocks.shape[:-1]
+    at = rng.integers(0, 32, size=lead)
+    np.put_along_axis(blocks, at[..., None],
+                      (6.0 * rng.choice([-1.0, 1.0], size=lead))[..., None], axis=-1)
+    blocks *= np.exp2(rng.integers(-6, 4, size=lead))[..., None]
+    return blocks.reshape(shape)
+
+
+def test_mxfp4_pack_round_trip_is_exact():
+    rng = np.random.default_rng(6)
+    x = fp4_values(rng, (3, 2, 128, 256))
+    kv = gen.pack_mxfp4_pages(x)
+    assert kv.shape == (3, 4, 128, 68)
+    for p in range(3):
+        for h in range(2):
+            k, v = om.page_kv(kv, "mxfp4", 0.5, 2.0, p, h, 128)
+            assert np.array_equal(k, x[p, h, :, :128] * 0.5)
+            assert np.array_equal(v, x[p, h, :, 128:] * 2.0)
+            k7, _ = om.page_kv(kv, "mxfp4", 1.0, 1.0, p, h, 7)
+            assert np.array_equal(k7, x[p, h, :7, :128])
+
+
+def small_fp4_case(hq=8, hkv=2, dql=2, pattern=(257, 513), seed=0, q_dtype=gen.Q_BF16,
+                   q_scale=1.0, k_scale=0.5, v_scale=2.0):
+    """A p3-shaped case whose 4-bit pool is packed from known values (returned
+    beside the case), with NaN poison past seq_len and on the spare page."""
+    case = gen.make_p3_case(hq, hkv, 1, dql, seq_pattern=pattern, seed=seed,
+                            kv_dtype=gen.KV_MXFP4, topk_k=8, q_dtype=q_dtype,
+                            q_scale=q_scale, k_scale=k_scale, v_scale=v_scale)
+    rng = np.random.default_rng(77 + seed)
+    vals = fp4_values(rng, (case.num_blocks, hkv, 128, 256))
+    case.kv = gen.pack_mxfp4_pages(vals)
+    used = set(int(x) for r, s in enumerate(case.seq_lens)
+               for x in case.block_table[r, :gen.pages_for(s)])
+    gen.fill_pages(case.kv, [p for p in range(case.num_blocks) if p not in used], gen.KV_MXFP4)
+    gen.poison_tail_slots(case.kv, case.block_table, case.seq_lens, gen.KV_MXFP4)
+    return case, vals
+
+
+def fp4_pin_error(case, vals) -> float:
+    return float(np.max(np.abs(run_oracle(case) - dense_reference(case, vals))))
+
+
+@pytest.mark.parametrize("dql", [1, 4])
+@pytest.mark.parametrize("heads", [(8, 2), (16, 1)])
+@pytest.mark.parametrize("qfmt", [(gen.Q_BF16, 1.0), (gen.Q_FP8, 0.5)])
+def test_mxfp4_dense_equivalence(dql, heads, qfmt):
+    case, vals = small_fp4_case(heads[0], heads[1], dql, q_dtype=qfmt[0], q_scale=qfmt[1])
+    assert fp4_pin_error(case, vals) < 1e-12
+
+
+def test_mxfp4_poisoned_pool_has_nan_scales_past_seq_len():
+    case, _ = small_fp4_case()
+    r, s = 0, int(case.seq_lens[0])
+    page = case.block_table[r, gen.pages_for(s) - 1]
+    used = s - (gen.pages_for(s) - 1) * 128
+    _, scales = om.mxfp4_slot(case.kv, page, 0, 1)
+    assert np.isnan(om.decode_e8m0(scales[used:])).all()
+    assert not np.isnan(om.decode_e8m0(scales[:used])).any()
+
+
+def test_mxfp4_scorer_brute_force():
+    case, vals = small_fp4_case(8, 2, 2, pattern=(300, 700))
+    mb = int(case.block_table.shape[1])
+    got = om.block_max_scores(case.q, case.kv, case.kv_dtype, case.k_scale, case.block_table,
+                              case.seq_lens, case.dql, case.num_kv_heads, mb)
+    q = torch_q(case.q).numpy()
+    g = case.num_q_heads // case.num_kv_heads
+    for t in range(case.real_rows):
+        r, loc = divmod(t, case.dql)
+        pos = int(case.seq_lens[r]) - case.dql + loc
+        for h in range(case.num_kv_heads):
+            for b in range(mb):
+                if b * 128 > pos:
+                    assert got[h, b, t] == -np.inf
+                    continue
+                n = min(128, pos - b * 128 + 1)
+                k = vals[case.block_table[r, b], h, :n, :128] * case.k_scale
+                want = max(float(np.dot(q[t, h * g + j], k[i])) for j in range(g)
+                           for i in range(n))
+                assert abs(got[h, b, t] - want) <= 1e-12 * max(1.0, abs(want))
+
+
+# ---------------------------------------------------------------------------
 # planted mistakes: each must trip at least one pin
 # ---------------------------------------------------------------------------
+
+_mxfp4_slot = om.mxfp4_slot
+_page_kv = om.page_kv
+
+
+def _rows_high_nibble_first(data, scales, n):
+    d = np.arange(128)
+    code = (data[:n, d // 2].astype(np.int64) >> (4 * (1 - d % 2))) & 0xF
+    return om.decode_e2m1(code) * om.decode_e8m0(scales[:n, d // 32])
+
+
+def _rows_scale_by_byte_block(data, scales, n):
+    d = np.arange(128)
+    code = (data[:n, d // 2].astype(np.int64) >> (4 * (d % 2))) & 0xF
+    return om.decode_e2m1(code) * om.decode_e8m0(scales[:n, (d // 2) // 32])
+
+
+def _slot_writer_order(kv, page, head, side):
+    """The writer's order (every head's slot of one side, then the other)."""
+    hkv = kv.shape[1] // 2
+    flat = np.asarray(kv[int(page), side * hkv + int(head)]).reshape(-1)
+    return (flat[:om.MXFP4_DATA_BYTES].reshape(128, 64),
+            flat[om.MXFP4_DATA_BYTES:].reshape(128, 4))
+
+
+def _e2m1_bias_0(codes):
+    """e2m1 read with exponent bias 0 instead of 1."""
+    c = np.asarray(codes).astype(np.int64) & 0xF
+    e, m = (c >> 1) & 3, c & 1
+    sign = np.where((c >> 3) & 1 == 1, -1.0, 1.0)
+    return sign * np.where(e == 0, m / 2.0, (1.0 + m / 2.0) * np.exp2(e.astype(float)))
+
+
+def _page_kv_no_global_scale(kv, kv_dtype, k_scale, v_scale, page, head, n):
+    if kv_dtype == "mxfp4":
+        return _page_kv(kv, kv_dtype, 1.0, 1.0, page, head, n)
+    return _page_kv(kv, kv_dtype, k_scale, v_scale, page, head, n)
+
+
+FP4_MUTANTS = {
+    "fp4_high_nibble_first": ("mxfp4_rows", _rows_high_nibble_first),
+    "fp4_scale_block_of_byte": ("mxfp4_rows", _rows_scale_by_byte_block),
+    "fp4_kv_slots_swapped": ("mxfp4_slot",
+                             lambda kv, page, head, side: _mxfp4_slot(kv, page, head, 1 - side)),
+    "fp4_writer_slot_order": ("mxfp4_slot", _slot_writer_order),
+    "e8m0_bias_128": ("decode_e8m0", lambda c: np.where(np.asarray(c) == 255, np.nan,
+                                                        np.exp2(np.asarray(c, float) - 128))),
+    "e2m1_bias_0": ("decode_e2m1", _e2m1_bias_0),
+    "fp4_global_scale_ignored": ("page_kv", _page_kv_no_global_scale),
+}
 
 MUTANTS = {
     "visible_rows_off_by_one": ("visible_rows",
@@ -587,16 +774,19 @@ def _pins_pass():
     cases = [small_dense_case(8, 2, 4), small_dense_case(8, 2, 1),
              small_dense_case(8, 2, 3, k_scale=0.5, v_scale=2.0),
              small_dense_case(8, 2, 2, gen.KV_E5M2, q_dtype=gen.Q_FP8, q_scale=0.5)]
-    return all(dense_pin_error(c) < 1e-12 for c in cases)
+    if not all(dense_pin_error(c) < 1e-12 for c in cases):
+        return False
+    case, vals = small_fp4_case(8, 2, 2)
+    return fp4_pin_error(case, vals) < 1e-12
 
 
 def test_pins_pass_on_clean_oracle():
     assert _pins_pass()
 
 
-@pytest.mark.parametrize("name", sorted(MUTANTS))
+@pytest.mark.parametrize("name", sorted(MUTANTS) + sorted(FP4_MUTANTS))
 def test_planted_mistake_is_caught(name, monkeypatch):
-    attr, fn = MUTANTS[name]
+    attr, fn = MUTANTS[name] if name in MUTANTS else FP4_MUTANTS[name]
     monkeypatch.setattr(om, attr, fn)
     try:
         ok = _pins_pass()

@@ -22,8 +22,17 @@ Shapes and structure follow the workloads the pages describe:
   test file quantizes the bf16 query with ``scaled_fp8_quant`` and a given
   scale before ``msa_cutlass_sparse_decode``).
 
+* A 4-bit cache: the pages' NVFP4 head-slot page (test file,
+  ``_make_nvfp4_kv_cache``: slot 2h = K of head h, slot 2h+1 = V, each the
+  rows' packed data then their block scales), with OCP MXFP4 elements (e2m1,
+  one E8M0 scale per 32 head dims, element 2i in the low nibble of byte i).
+  The block scale of 32 values is the OCP MX choice
+  ``2^(floor(log2(amax)) - 2)``; elements round to the nearest e2m1 value
+  (ties to the smaller magnitude), saturating at 6.
+
 Every array is plain NumPy: fp8 codes as ``uint8``, bf16 as ``uint16`` bit
-patterns, indices as ``int32``.  fp8 e5m2 KV codes are ``uint8`` too.
+patterns, indices as ``int32``.  fp8 e5m2 KV codes are ``uint8`` too; a 4-bit
+pool is ``uint8 [num_blocks, 2*Hkv, 128, 68]`` (each slot's 8704 bytes).
 """
 from __future__ import annotations
 
@@ -45,6 +54,12 @@ KV_FP8 = "fp8_e4m3"
 KV_E5M2 = "fp8_e5m2"
 KV_BF16 = "bf16"
 KV_8BIT = (KV_FP8, KV_E5M2)
+KV_MXFP4 = "mxfp4"
+MXFP4_BLOCK = 32
+MXFP4_DATA_BYTES = PAGE * HEAD_DIM // 2
+MXFP4_SLOT_BYTES = MXFP4_DATA_BYTES + PAGE * HEAD_DIM // MXFP4_BLOCK
+MXFP4_NAN_SCALE = 0xFF
+_E2M1_MIDPOINTS = np.array([0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0], dtype=np.float32)
 Q_BF16 = "bf16"
 Q_FP8 = "fp8_e4m3"
 
@@ -77,6 +92,40 @@ def encode_e5m2(x: np.ndarray) -> np.ndarray:
     t = torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32))
     t = t.clamp(-E5M2_MAX, E5M2_MAX)
     return t.to(torch.float8_e5m2).view(torch.uint8).numpy().copy()
+
+
+def encode_mxfp4(x: np.ndarray):
+    """float rows [..., 128] -> (packed e2m1 data uint8 [..., 64], E8M0 block
+    scales uint8 [..., 4]).  Input generation only: any valid encoding is a
+    valid input, and the oracle decodes whatever bytes this writes."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    lead = x.shape[:-1]
+    blk = x.reshape(lead + (HEAD_DIM // MXFP4_BLOCK, MXFP4_BLOCK))
+    amax = np.abs(blk).max(axis=-1)
+    _, ex = np.frexp(np.where(amax > 0, amax, 1.0))     # amax = f * 2^ex, f in [0.5, 1)
+    e = np.clip(ex.astype(np.int64) - 1 - 2 + 127, 1, 254)
+    e = np.where(amax > 0, e, 127)
+    y = blk / np.exp2(e - 127).astype(np.float32)[..., None]
+    mag = np.searchsorted(_E2M1_MIDPOINTS, np.abs(y), side="left").astype(np.uint8)
+    code = mag | np.where((y < 0) & (mag > 0), 8, 0).astype(np.uint8)
+    code = code.reshape(lead + (HEAD_DIM,))
+    data = (code[..., 0::2] | (code[..., 1::2] << 4)).astype(np.uint8)
+    return data, e.astype(np.uint8)
+
+
+def pack_mxfp4_pages(x: np.ndarray, out: np.ndarray | None = None) -> np.ndarray:
+    """Packed K|V values ``[pages, Hkv, 128, 256]`` -> 4-bit head-slot pages
+    ``uint8 [pages, 2*Hkv, 128, 68]``: slot 2h holds head h's K rows, slot
+    2h+1 its V rows, each as 128 x 64 data bytes then 128 x 4 scale bytes."""
+    pages, hkv = x.shape[0], x.shape[1]
+    if out is None:
+        out = np.empty((pages, 2 * hkv, PAGE, MXFP4_SLOT_BYTES // PAGE), dtype=np.uint8)
+    slots = out.reshape(pages, hkv, 2, MXFP4_SLOT_BYTES)
+    for side in range(2):
+        data, scales = encode_mxfp4(x[..., side * HEAD_DIM:(side + 1) * HEAD_DIM])
+        slots[:, :, side, :MXFP4_DATA_BYTES] = data.reshape(pages, hkv, -1)
+        slots[:, :, side, MXFP4_DATA_BYTES:] = scales.reshape(pages, hkv, -1)
+    return out
 
 
 def _normal_f32(rng: np.random.Generator, shape, std: float) -> np.ndarray:
@@ -239,31 +288,49 @@ def every_visible_topk(seq_lens, num_kv_heads: int, dql: int, k: int) -> np.ndar
 
 
 def poison_tail_slots(kv: np.ndarray, block_table, seq_lens, kv_dtype: str) -> None:
-    """Write NaN patterns into the slots past seq_len of every last page."""
+    """Write NaN patterns into the slots past seq_len of every last page (a
+    4-bit page: NaN block scales and all-ones data for those rows)."""
     bad = FP8_NAN_CODE if kv_dtype in KV_8BIT else BF16_NAN_BITS
     for r, s in enumerate(seq_lens):
         n = pages_for(s)
         used = int(s) - (n - 1) * PAGE
-        if used < PAGE:
-            kv[block_table[r, n - 1], :, used:, :] = bad
+        if used >= PAGE:
+            continue
+        page = block_table[r, n - 1]
+        if kv_dtype == KV_MXFP4:
+            slots = kv[page].reshape(kv.shape[1], MXFP4_SLOT_BYTES)
+            slots[:, used * (HEAD_DIM // 2):MXFP4_DATA_BYTES] = 0xFF
+            slots[:, MXFP4_DATA_BYTES + used * (HEAD_DIM // MXFP4_BLOCK):] = MXFP4_NAN_SCALE
+        else:
+            kv[page, :, used:, :] = bad
 
 
 def fill_pages(kv: np.ndarray, pages, kv_dtype: str) -> None:
     bad = FP8_NAN_CODE if kv_dtype in KV_8BIT else BF16_NAN_BITS
+    if kv_dtype == KV_MXFP4:
+        bad = 0xFF            # -6 data, NaN scales
     for p in pages:
         kv[int(p)] = bad
 
 
 def make_pool(rng: np.random.Generator, num_pages: int, num_kv_heads: int,
-              kv_dtype: str, std: float, chunk_pages: int = 256) -> np.ndarray:
-    """Packed K|V pool ``(num_pages, Hkv, 128, 256)``; values N(0, std) encoded.
+              kv_dtype: str, std: float, chunk_pages: int = 256, k_scale: float = 1.0,
+              v_scale: float = 1.0) -> np.ndarray:
+    """Packed K|V pool ``(num_pages, Hkv, 128, 256)``; values N(0, std), K
+    divided by ``k_scale`` and V by ``v_scale``, encoded.  A 4-bit pool is
+    ``(num_pages, 2*Hkv, 128, 68)`` head slots (module docstring).
 
     One 63-bit pool seed is drawn from ``rng``; page chunk ``i`` is then drawn
     from ``default_rng([pool_seed, i])``, so chunks are independent,
     reproducible one at a time, and generated on several threads.
     """
-    dt = np.uint8 if kv_dtype in KV_8BIT else np.uint16
-    kv = np.empty((num_pages, num_kv_heads, PAGE, 2 * HEAD_DIM), dtype=dt)
+    fp4 = kv_dtype == KV_MXFP4
+    if fp4:
+        kv = np.empty((num_pages, 2 * num_kv_heads, PAGE, MXFP4_SLOT_BYTES // PAGE),
+                      dtype=np.uint8)
+    else:
+        dt = np.uint8 if kv_dtype in KV_8BIT else np.uint16
+        kv = np.empty((num_pages, num_kv_heads, PAGE, 2 * HEAD_DIM), dtype=dt)
     pool_seed = int(rng.integers(0, 2 ** 63 - 1))
 
     def fill(i):
@@ -271,7 +338,14 @@ def make_pool(rng: np.random.Generator, num_pages: int, num_kv_heads: int,
         p1 = min(num_pages, p0 + chunk_pages)
         crng = np.random.default_rng([pool_seed, i])
         x = _normal_f32(crng, (p1 - p0, num_kv_heads, PAGE, 2 * HEAD_DIM), std)
-        kv[p0:p1] = _encode(x, kv_dtype)
+        if k_scale != 1.0:
+            x[..., :HEAD_DIM] /= np.float32(k_scale)
+        if v_scale != 1.0:
+            x[..., HEAD_DIM:] /= np.float32(v_scale)
+        if fp4:
+            pack_mxfp4_pages(x, kv[p0:p1])
+        else:
+            kv[p0:p1] = _encode(x, kv_dtype)
 
     n_chunks = (num_pages + chunk_pages - 1) // chunk_pages
     workers = max(1, min(8, os.cpu_count() or 1, n_chunks))
@@ -301,8 +375,12 @@ CONFIG_NAMES = ("c1_tiny_bf16", "c2_tp4_fp8", "c3_tp1_fp8", "c4_spec_ragged",
                 "c5_full_step")
 # The c2 shape through the two other input formats: fp8 q with a per-tensor
 # q_scale over the fp8 e4m3 cache, and bf16 q over an fp8 e5m2 cache.
-FORMAT_CONFIG_NAMES = ("c2_tp4_fp8q", "c2_tp4_e5m2")
+# The 4-bit cache on the same shape, with the global scales of the test page's
+# NVFP4 decode test (k 0.5, v 2.0), under a bf16 and an fp8 q.
+FORMAT_CONFIG_NAMES = ("c2_tp4_fp8q", "c2_tp4_e5m2", "c2_tp4_mxfp4", "c2_tp4_mxfp4_fp8q")
 C2_FP8Q_SCALE = 0.5
+MXFP4_K_SCALE = 0.5
+MXFP4_V_SCALE = 2.0
 
 
 def _topk_rows(rng, seq_lens, dql, hkv, k, rule, per_head, pad_rows=0):
@@ -332,6 +410,13 @@ def make_config(name: str, replicas: int = 0, poison: bool = True) -> DecodeCase
                         name=name)
     if name == "c2_tp4_e5m2":
         return _make_c2(replicas, poison, kv_dtype=KV_E5M2, name=name)
+    if name == "c2_tp4_mxfp4":
+        return _make_c2(replicas, poison, kv_dtype=KV_MXFP4, name=name,
+                        k_scale=MXFP4_K_SCALE, v_scale=MXFP4_V_SCALE)
+    if name == "c2_tp4_mxfp4_fp8q":
+        return _make_c2(replicas, poison, kv_dtype=KV_MXFP4, name=name, q_dtype=Q_FP8,
+                        q_scale=C2_FP8Q_SCALE, k_scale=MXFP4_K_SCALE,
+                        v_scale=MXFP4_V_SCALE)
     if name == "c3_tp1_fp8":
         return _make_c3(replicas, poison)
     if name == "c4_spec_ragged":
@@ -364,12 +449,13 @@ def _make_c1(replicas: int, poison: bool) -> DecodeCase:
 
 
 def _make_c2(replicas: int, poison: bool, q_dtype: str = Q_BF16, q_scale: float = 1.0,
-             kv_dtype: str = KV_FP8, name: str = "c2_tp4_fp8") -> DecodeCase:
+             kv_dtype: str = KV_FP8, name: str = "c2_tp4_fp8", k_scale: float = 1.0,
+             v_scale: float = 1.0) -> DecodeCase:
     rng = np.random.default_rng(2)
     B, dql, hq, hkv, k = 32, 4, 16, 1, 16
     seq = rng.integers(16384, 65536, size=B, endpoint=True).astype(np.int32)
     bt, total, spare = paged_layout(rng, seq, spare_pages=1)
-    kv = make_pool(rng, total, hkv, kv_dtype, 0.5)
+    kv = make_pool(rng, total, hkv, kv_dtype, 0.5, k_scale=k_scale, v_scale=v_scale)
     if poison:
         fill_pages(kv, spare, kv_dtype)
         poison_tail_slots(kv, bt, seq, kv_dtype)
@@ -383,8 +469,8 @@ def _make_c2(replicas: int, poison: bool, q_dtype: str = Q_BF16, q_scale: float 
     q, topk = one(rng)
     reps = [one(rng) for _ in range(replicas)]
     return DecodeCase(name, 2, B, dql, B * dql, hq, hkv, k, kv_dtype, seq, bt,
-                      kv, q, topk, q_dtype=q_dtype, q_scale=q_scale,
-                      max_blocks=int(bt.shape[1]), replicas=reps)
+                      kv, q, topk, q_dtype=q_dtype, q_scale=q_scale, k_scale=k_scale,
+                      v_scale=v_scale, max_blocks=int(bt.shape[1]), replicas=reps)
 
 
 def _make_c3(replicas: int, poison: bool) -> DecodeCase:
@@ -496,13 +582,14 @@ def _make_c5(replicas: int, poison: bool) -> DecodeCase:
 def make_p3_case(num_q_heads: int, num_kv_heads: int, pairs: int, dql: int,
                  seq_pattern=(257, 513), seed: int = 0, kv_dtype: str = KV_FP8,
                  std: float = 0.25, topk_k: int = 16, poison: bool = True,
-                 q_dtype: str = Q_BF16, q_scale: float = 1.0) -> DecodeCase:
+                 q_dtype: str = Q_BF16, q_scale: float = 1.0, k_scale: float = 1.0,
+                 v_scale: float = 1.0) -> DecodeCase:
     """The test page's parity shape: seq_lens = pattern * pairs, every visible
     page selected (``_make_topk``), K and V ~ N(0, std) encoded, Q ~ N(0,1)."""
     rng = np.random.default_rng(1000 + seed)
     seq = np.array(list(seq_pattern) * pairs, dtype=np.int32)
     bt, total, spare = paged_layout(rng, seq, spare_pages=1)
-    kv = make_pool(rng, total, num_kv_heads, kv_dtype, std)
+    kv = make_pool(rng, total, num_kv_heads, kv_dtype, std, k_scale=k_scale, v_scale=v_scale)
     if poison:
         fill_pages(kv, spare, kv_dtype)
         poison_tail_slots(kv, bt, seq, kv_dtype)
@@ -512,7 +599,7 @@ def make_p3_case(num_q_heads: int, num_kv_heads: int, pairs: int, dql: int,
     return DecodeCase(f"p3_h{num_q_heads}_{num_kv_heads}_pairs{pairs}_dql{dql}", seed,
                       len(seq), dql, rows, num_q_heads, num_kv_heads, topk_k, kv_dtype,
                       seq, bt, kv, q, topk, q_dtype=q_dtype, q_scale=q_scale,
-                      max_blocks=int(bt.shape[1]))
+                      k_scale=k_scale, v_scale=v_scale, max_blocks=int(bt.shape[1]))
 
 
 def make_random_case(seed: int, batch: int, dql: int, num_q_heads: int,
@@ -521,7 +608,8 @@ def make_random_case(seed: int, batch: int, dql: int, num_q_heads: int,
                      per_head: bool = True, rule: str = "uniform",
                      neg_frac: float = 0.0, poison: bool = True,
                      stride_extra: int = 0, q_dtype: str = Q_BF16,
-                     q_scale: float = 1.0) -> DecodeCase:
+                     q_scale: float = 1.0, k_scale: float = 1.0,
+                     v_scale: float = 1.0) -> DecodeCase:
     """A generic seeded case: uniform seq lens, random distinct blocks that
     include each token's causal last block, optional extra -1 entries."""
     rng = np.random.default_rng(seed)
@@ -530,7 +618,7 @@ def make_random_case(seed: int, batch: int, dql: int, num_q_heads: int,
     if stride_extra:
         bt = np.concatenate(
             [bt, np.full((batch, stride_extra), bt[0, 0], dtype=np.int32)], axis=1)
-    kv = make_pool(rng, total, num_kv_heads, kv_dtype, std)
+    kv = make_pool(rng, total, num_kv_heads, kv_dtype, std, k_scale=k_scale, v_scale=v_scale)
     if poison:
         fill_pages(kv, spare, kv_dtype)
         poison_tail_slots(kv, bt, seq, kv_dtype)
@@ -545,7 +633,8 @@ def make_random_case(seed: int, batch: int, dql: int, num_q_heads: int,
         topk[mask] = -1
     return DecodeCase(f"rand_s{seed}", seed, batch, dql, rows + pad_rows, num_q_heads,
                       num_kv_heads, topk_k, kv_dtype, seq, bt, kv, q, topk,
-                      q_dtype=q_dtype, q_scale=q_scale, max_blocks=int(bt.shape[1]))
+                      q_dtype=q_dtype, q_scale=q_scale, k_scale=k_scale, v_scale=v_scale,
+                      max_blocks=int(bt.shape[1]))
 
 
 @dataclass
@@ -595,7 +684,8 @@ def make_prefill_case(seed: int, q_lens, seq_lens, num_q_heads: int, num_kv_head
                       topk_k: int = 16, kv_dtype: str = KV_FP8, q_dtype: str = Q_BF16,
                       q_scale: float = 1.0, rule: str = "every_visible", std: float = 0.25,
                       pad_rows: int = 0, replicas: int = 0, poison: bool = True,
-                      name: str = "") -> PrefillCase:
+                      name: str = "", k_scale: float = 1.0,
+                      v_scale: float = 1.0) -> PrefillCase:
     """A seeded ragged prefill step.  rule "every_visible" selects blocks
     0..last for each token (the test page's prefill test, which needs
     last < topk_k); "zipf" picks topk_k distinct blocks per (token, kv head)
@@ -608,7 +698,7 @@ def make_prefill_case(seed: int, q_lens, seq_lens, num_q_heads: int, num_kv_head
     cu = np.zeros(len(q_lens) + 1, dtype=np.int32)
     cu[1:] = np.cumsum(q_lens)
     bt, total, spare = paged_layout(rng, seq, spare_pages=1)
-    kv = make_pool(rng, total, num_kv_heads, kv_dtype, std)
+    kv = make_pool(rng, total, num_kv_heads, kv_dtype, std, k_scale=k_scale, v_scale=v_scale)
     if poison:
         fill_pages(kv, spare, kv_dtype)
         poison_tail_slots(kv, bt, seq, kv_dtype)
@@ -632,8 +722,8 @@ def make_prefill_case(seed: int, q_lens, seq_lens, num_q_heads: int, num_kv_head
     reps = [one(rng) for _ in range(replicas)]
     return PrefillCase(name or f"prefill_s{seed}", seed, q_lens, seq, ctx, cu, rows,
                        num_q_heads, num_kv_heads, topk_k, kv_dtype, bt, kv, q, topk,
-                       q_dtype=q_dtype, q_scale=q_scale, max_blocks=int(bt.shape[1]),
-                       replicas=reps)
+                       q_dtype=q_dtype, q_scale=q_scale, k_scale=k_scale, v_scale=v_scale,
+                       max_blocks=int(bt.shape[1]), replicas=reps)
 
 
 PREFILL_CONFIG_NAMES = ("pf1_chunked_prefill",)
