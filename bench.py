@@ -41,7 +41,7 @@ METRIC = "decode tokens/s and effective KV GB/s (% HBM peak), sparse GQA attend,
 HBM_PEAK_GBS = 8000.0
 DEFAULT_CONFIG = "c2_tp4_fp8"
 OTHER_CONFIGS = ("c3_tp1_fp8", "c4_spec_ragged", "c2_tp4_fp8q", "c2_tp4_e5m2",
-                 "pf1_chunked_prefill", "d1_dense_tp1")
+                 "c2_tp4_mxfp4", "c2_tp4_mxfp4_fp8q", "pf1_chunked_prefill", "d1_dense_tp1")
 FULL_STEP_CONFIG = "c5_full_step"
 # rocprofv3 counter summaries, each valid for the kernel sources it was taken on
 TRAFFIC_FILES = {"attend": os.path.join(ROOT, "profiles", "attend_traffic.json"),
@@ -53,6 +53,7 @@ KERNEL_SOURCES = {
                "block_sparse_gqa_decode_amd/csrc/msa_device.h",
                "block_sparse_gqa_decode_amd/csrc/msa_internal.h"),
     "score": ("block_sparse_gqa_decode_amd/csrc/msa_score.hip",
+              "block_sparse_gqa_decode_amd/csrc/msa_page.h",
               "block_sparse_gqa_decode_amd/csrc/msa_device.h",
               "block_sparse_gqa_decode_amd/csrc/msa_internal.h"),
 }
@@ -70,6 +71,10 @@ CONFIG_TEXT = {
     "c2_tp4_fp8q": "c2 with an fp8 e4m3 query (q_scale 0.5) over the fp8 e4m3 cache: "
                    "fp8 x fp8 MFMA for QK^T",
     "c2_tp4_e5m2": "c2 with a bf16 query over an fp8 e5m2 cache",
+    "c2_tp4_mxfp4": "c2 with a bf16 query over a 4-bit MXFP4 head-slot cache (e2m1 + E8M0 "
+                    "per 32 dims; k_scale 0.5, v_scale 2.0)",
+    "c2_tp4_mxfp4_fp8q": "c2 with an fp8 e4m3 query (q_scale 0.5) over the 4-bit MXFP4 "
+                         "cache: fp4 x fp8 scaled MFMA for QK^T",
     "pf1_chunked_prefill": "chunked prefill: 4 requests x 1024-token chunks after a cached "
                            "context of U[16384,65536], 64/4 heads, fp8, top-16 per (token, "
                            "kv head), recent-biased",
@@ -90,12 +95,17 @@ def kernel_source_hash(kernel: str = "attend") -> str:
 # byte accounting
 # ---------------------------------------------------------------------------
 
+def kv_half_row_bytes(kv_dtype: str) -> int:
+    """Bytes of one key's K (or V) entry: 128 elements, plus the four E8M0
+    block scales of a 4-bit row."""
+    return {"bf16": 256, "fp8_e4m3": 128, "fp8_e5m2": 128, "mxfp4": 64 + 4}[kv_dtype]
+
+
 def step_bytes(case, q, topk):
     """Algorithmic bytes of one attend step (see module docstring)."""
     import numpy as np
 
-    e = 2 if case.kv_dtype == "bf16" else 1
-    row_bytes = 2 * 128 * e
+    row_bytes = 2 * kv_half_row_bytes(case.kv_dtype)
     real = case.real_rows
     t = np.arange(real)
     if hasattr(case, "cu_seqlens_q"):       # ragged prefill rows
@@ -146,7 +156,7 @@ def _host_kv(case):
     import numpy as np
     import torch
 
-    if case.kv_dtype == "fp8_e4m3":
+    if case.kv_dtype in ("fp8_e4m3", "mxfp4"):
         return torch.from_numpy(case.kv)
     if case.kv_dtype == "fp8_e5m2":
         return torch.from_numpy(case.kv).view(torch.float8_e5m2)
@@ -166,7 +176,7 @@ def _kv_code(case):
     import block_sparse_gqa_decode_amd as msa
 
     return {"fp8_e4m3": msa.KV_FP8_E4M3, "fp8_e5m2": msa.KV_FP8_E5M2,
-            "bf16": msa.KV_BF16}[case.kv_dtype]
+            "bf16": msa.KV_BF16, "mxfp4": msa.KV_MXFP4}[case.kv_dtype]
 
 
 def _q_code(case):
@@ -347,13 +357,12 @@ def scorer_bytes(case):
     selector, and the top-k write."""
     import numpy as np
 
-    e = 2 if case.kv_dtype == "bf16" else 1
     kv_rows = 0
     for r in range(case.batch):
         pos_last = int(case.seq_lens[r]) - 1
         nb = pos_last // 128 + 1
         kv_rows += (nb - 1) * 128 + (pos_last - (nb - 1) * 128 + 1)
-    k_bytes = kv_rows * case.num_kv_heads * 128 * e
+    k_bytes = kv_rows * case.num_kv_heads * kv_half_row_bytes(case.kv_dtype)
     q_bytes = case.real_rows * case.num_q_heads * 128 * (1 if case.q_dtype == "fp8_e4m3" else 2)
     score_bytes = case.num_kv_heads * case.max_blocks * case.num_token_rows * 4
     topk_bytes = case.num_token_rows * case.num_kv_heads * case.topk_k * 4

@@ -18,14 +18,20 @@ Entry points carry the C names:
 * ``msa_topk_select``         -- the top-k selector alone.
 * ``msa_fp8_e4m3_to_bf16`` / ``msa_fp8_e5m2_to_bf16`` -- the in-register fp8
   conversions, as a check.
+* ``msa_mxfp4_to_bf16``       -- a 4-bit (MXFP4 head-slot) cache dequantized to
+  packed bf16 K|V rows with the attend's own conversion.
 
 Tensor checks follow ``MSACutlassDecodePlanCache.prepare`` (contiguous int32
 block table with one row per request, contiguous int32 sequence lengths on the
 same device) and the backend contract of the vLLM API page
 ``vllm.models.minimax_m3.common.sparse_attention`` (head size 128, page size
 128, bf16, fp8 e4m3 or fp8 e5m2 KV in a packed ``(num_blocks, Hkv, 128, 256)``
-cache).  q is bf16, or fp8 e4m3 codes with a per-tensor ``q_scale`` (the
-``query_fp8`` / ``q_scale_float`` arguments of ``msa_cutlass_sparse_decode``).
+cache).  A 4-bit cache (``KV_MXFP4``) is a ``uint8 (num_blocks, 2*Hkv, 128,
+68)`` tensor of head slots -- slot 2h holds K of kv head h, slot 2h+1 its V,
+each as 128 rows of 64 e2m1 code bytes then 128 rows of 4 E8M0 scales (the
+NVFP4 head-slot page of vLLM's MSA test file, with OCP MX blocks of 32).  q is
+bf16, or fp8 e4m3 codes with a per-tensor ``q_scale`` (the ``query_fp8`` /
+``q_scale_float`` arguments of ``msa_cutlass_sparse_decode``).
 """
 from __future__ import annotations
 
@@ -40,17 +46,20 @@ __all__ = [
     "msa_sparse_decode_plan", "msa_sparse_decode_run", "msa_sparse_decode_attend",
     "msa_sparse_decode_merge", "msa_block_score_topk", "msa_sparse_prefill_plan",
     "msa_sparse_prefill_run",
-    "msa_topk_select", "msa_fp8_e4m3_to_bf16", "msa_fp8_e5m2_to_bf16", "library_path",
-    "load_library", "KV_BF16", "KV_FP8_E4M3", "KV_FP8_E5M2", "Q_BF16", "Q_FP8_E4M3",
+    "msa_topk_select", "msa_fp8_e4m3_to_bf16", "msa_fp8_e5m2_to_bf16", "msa_mxfp4_to_bf16",
+    "library_path", "load_library", "KV_BF16", "KV_FP8_E4M3", "KV_FP8_E5M2", "KV_MXFP4",
+    "Q_BF16", "Q_FP8_E4M3",
     "PAGE_SIZE", "HEAD_DIM", "ABI_VERSION",
 ]
 
-ABI_VERSION = 3
+ABI_VERSION = 4
 PAGE_SIZE = 128
 HEAD_DIM = 128
 KV_BF16 = 0
 KV_FP8_E4M3 = 1
 KV_FP8_E5M2 = 2
+KV_MXFP4 = 3
+MXFP4_SLOT_ROW_BYTES = 68   # a slot's 8704 bytes viewed as 128 x 68
 Q_BF16 = 0
 Q_FP8_E4M3 = 1
 
@@ -134,6 +143,7 @@ def load_library():
         "msa_topk_select": (i32, [vp, pi64, i32, i32, i32, vp, i32, vp]),
         "msa_fp8_e4m3_to_bf16": (i32, [vp, vp, i64, vp]),
         "msa_fp8_e5m2_to_bf16": (i32, [vp, vp, i64, vp]),
+        "msa_mxfp4_to_bf16": (i32, [vp, pi64, i64, i32, vp, vp]),
         "msa_last_error": (ctypes.c_char_p, []),
         "msa_abi_version": (i32, []),
     }
@@ -168,8 +178,9 @@ def _stream_handle(stream, device) -> Optional[int]:
 
 
 def _kv_dtype_of(kv: torch.Tensor, declared: Optional[int] = None) -> int:
-    """The KV format of a cache tensor.  ``uint8`` holds either fp8 format and
-    takes ``declared`` (default e4m3); typed fp8 tensors must agree with it."""
+    """The KV format of a cache tensor.  ``uint8`` holds either fp8 format or
+    4-bit head slots and takes ``declared`` (default e4m3); typed fp8 tensors
+    must agree with it."""
     if kv.dtype == torch.uint8:
         return KV_FP8_E4M3 if declared is None else declared
     found = {torch.float8_e4m3fn: KV_FP8_E4M3, torch.float8_e5m2: KV_FP8_E5M2,
@@ -190,15 +201,31 @@ def _q_dtype_of(q: torch.Tensor) -> int:
     raise ValueError(f"unsupported q dtype {q.dtype}: expected bfloat16 or float8_e4m3fn")
 
 
-def _check_kv(kv: torch.Tensor, num_kv_heads: int):
+def _check_kv(kv: torch.Tensor, num_kv_heads: int, kv_dtype: Optional[int] = None):
     if kv.device.type != "cuda":
         raise ValueError("kv_cache must be a device tensor")
+    if kv_dtype == KV_MXFP4:
+        if kv.dtype != torch.uint8 or kv.dim() != 4 or kv.shape[1] != 2 * num_kv_heads \
+                or kv.shape[2] != PAGE_SIZE or kv.shape[3] != MXFP4_SLOT_ROW_BYTES:
+            raise ValueError(f"an MXFP4 kv_cache must be uint8 (num_blocks, "
+                             f"{2 * num_kv_heads}, 128, 68), got {kv.dtype} {tuple(kv.shape)}")
+        if kv.stride(3) != 1 or kv.stride(2) != MXFP4_SLOT_ROW_BYTES:
+            raise ValueError("each MXFP4 head slot must be one contiguous 8704-byte run")
+        return
     if kv.dim() != 4 or kv.shape[1] != num_kv_heads or kv.shape[2] != PAGE_SIZE \
             or kv.shape[3] != 2 * HEAD_DIM:
         raise ValueError(f"kv_cache must be logically (num_blocks, {num_kv_heads}, 128, 256), "
                          f"got {tuple(kv.shape)}")
     if kv.stride(3) != 1:
         raise ValueError("kv_cache last dimension must be contiguous")
+
+
+def _kv_strides(kv: torch.Tensor, kv_dtype: int):
+    """kv_strides for the C ABI: element strides, or for 4-bit head slots the
+    byte strides (page, head = two slots, K slot -> V slot, 1)."""
+    if kv_dtype == KV_MXFP4:
+        return _I64x4(kv.stride(0), 2 * kv.stride(1), kv.stride(1), 1)
+    return _I64x4(*kv.stride())
 
 
 def _check_tables(block_table: torch.Tensor, seq_lens: torch.Tensor, batch: int):
@@ -361,8 +388,8 @@ def _run_args(plan, q, kv_cache, block_table, seq_lens, topk, out, tables=True):
     rows = plan.num_token_rows
     _check_q(q, "q", rows, plan.num_q_heads, plan.q_dtype)
     _check_q(out, "out", rows, plan.num_q_heads)
-    _check_kv(kv_cache, plan.num_kv_heads)
     _kv_dtype_of(kv_cache, plan.kv_dtype)
+    _check_kv(kv_cache, plan.num_kv_heads, plan.kv_dtype)
     if tables:
         _check_tables(block_table, seq_lens, plan.batch)
     if block_table.stride(0) != plan.page_table_stride:
@@ -381,8 +408,8 @@ def _run_args(plan, q, kv_cache, block_table, seq_lens, topk, out, tables=True):
             continue
         if t.device != seq_lens.device:
             raise ValueError(f"{name} is not on the sequence-length device")
-    return (plan.handle, q.data_ptr(), kv_cache.data_ptr(), _I64x4(*kv_cache.stride()),
-            kv_cache.shape[0])
+    return (plan.handle, q.data_ptr(), kv_cache.data_ptr(),
+            _kv_strides(kv_cache, plan.kv_dtype), kv_cache.shape[0])
 
 
 def _require_decode_plan(plan: DecodePlan):
@@ -439,7 +466,8 @@ def msa_block_score_topk(q: torch.Tensor, kv_cache: torch.Tensor, block_table: t
     rows = num_token_rows or batch * decode_query_len
     q_dtype = _q_dtype_of(q)
     _check_q(q, "q", rows, q.shape[1] if q.dim() == 3 else -1, q_dtype)
-    _check_kv(kv_cache, num_kv_heads)
+    kvd = _kv_dtype_of(kv_cache, kv_dtype)
+    _check_kv(kv_cache, num_kv_heads, kvd)
     _check_tables(block_table, seq_lens, batch)
     if score.dtype != torch.float32 or score.dim() != 3 or \
             tuple(score.shape) != (num_kv_heads, max_blocks, rows):
@@ -448,10 +476,9 @@ def msa_block_score_topk(q: torch.Tensor, kv_cache: torch.Tensor, block_table: t
             or topk_out.shape[0] != rows or topk_out.shape[1] != num_kv_heads:
         raise ValueError(f"topk_out must be contiguous int32 [{rows}, {num_kv_heads}, k]")
     shape = _Shape(batch, decode_query_len, rows, block_table.stride(0), q.shape[1],
-                   num_kv_heads, PAGE_SIZE, HEAD_DIM, topk_out.shape[2],
-                   _kv_dtype_of(kv_cache, kv_dtype), 0, q_dtype)
+                   num_kv_heads, PAGE_SIZE, HEAD_DIM, topk_out.shape[2], kvd, 0, q_dtype)
     _check(load_library().msa_block_score_topk(
-        ctypes.byref(shape), q.data_ptr(), kv_cache.data_ptr(), _I64x4(*kv_cache.stride()),
+        ctypes.byref(shape), q.data_ptr(), kv_cache.data_ptr(), _kv_strides(kv_cache, kvd),
         kv_cache.shape[0], float(q_scale), float(k_scale), block_table.data_ptr(), seq_lens.data_ptr(),
         int(max_blocks), score.data_ptr(), _I64x3(*score.stride()), topk_out.data_ptr(),
         int(topk_out.shape[2]), _stream_handle(stream, q.device)))
@@ -485,6 +512,21 @@ def msa_fp8_e4m3_to_bf16(inp: torch.Tensor, out: torch.Tensor, stream=None) -> N
 
 def msa_fp8_e5m2_to_bf16(inp: torch.Tensor, out: torch.Tensor, stream=None) -> None:
     _fp8_to_bf16("msa_fp8_e5m2_to_bf16", torch.float8_e5m2, inp, out, stream)
+
+
+def msa_mxfp4_to_bf16(kv_cache: torch.Tensor, out: torch.Tensor, *, num_kv_heads: int,
+                      stream=None) -> None:
+    """out[p, h, i, :] = packed bf16 K|V row i of head h on page p of a 4-bit
+    head-slot cache (block scales applied, global scales not)."""
+    _check_kv(kv_cache, num_kv_heads, KV_MXFP4)
+    nb = kv_cache.shape[0]
+    if (out.dtype != torch.bfloat16 or not out.is_contiguous() or out.device != kv_cache.device
+            or tuple(out.shape) != (nb, num_kv_heads, PAGE_SIZE, 2 * HEAD_DIM)):
+        raise ValueError(f"out must be contiguous bfloat16 ({nb}, {num_kv_heads}, 128, 256) "
+                         "on the cache's device")
+    _check(load_library().msa_mxfp4_to_bf16(
+        kv_cache.data_ptr(), _kv_strides(kv_cache, KV_MXFP4), nb, int(num_kv_heads),
+        out.data_ptr(), _stream_handle(stream, kv_cache.device)))
 
 
 class PlanCache:

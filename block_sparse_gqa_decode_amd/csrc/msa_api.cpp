@@ -56,7 +56,11 @@ msa_status device_fail(hipError_t e, const char* what) {
   return fail(MSA_ERR_DEVICE, "%s failed: %s", what, hipGetErrorString(e));
 }
 
+// Bytes per kv_strides unit: bf16 elements, fp8 codes, or (MXFP4) bytes.
 int64_t elem_bytes(int32_t kv_dtype) { return kv_dtype == MSA_KV_BF16 ? 2 : 1; }
+
+// One MXFP4 head slot: 128 rows x 64 code bytes + 128 rows x 4 scale bytes.
+constexpr int64_t kMxfp4SlotBytes = msa::kPage * (msa::kHeadDim / 2 + msa::kHeadDim / 32);
 
 bool aligned16(const void* ptr) { return (reinterpret_cast<uintptr_t>(ptr) & 15u) == 0; }
 
@@ -106,12 +110,12 @@ msa_status check_common_shape(const msa_decode_shape* s) {
   if (s->head_dim != msa::kHeadDim)
     return fail(MSA_ERR_UNSUPPORTED, "head_dim must be 128 (got %d)", s->head_dim);
   if (s->kv_dtype != MSA_KV_BF16 && s->kv_dtype != MSA_KV_FP8_E4M3 &&
-      s->kv_dtype != MSA_KV_FP8_E5M2)
+      s->kv_dtype != MSA_KV_FP8_E5M2 && s->kv_dtype != MSA_KV_MXFP4)
     return fail(MSA_ERR_INVALID_ARG, "unknown kv_dtype %d", s->kv_dtype);
   if (s->q_dtype != MSA_Q_BF16 && s->q_dtype != MSA_Q_FP8_E4M3)
     return fail(MSA_ERR_INVALID_ARG, "unknown q_dtype %d", s->q_dtype);
   if (s->q_dtype == MSA_Q_FP8_E4M3 && s->kv_dtype == MSA_KV_BF16)
-    return fail(MSA_ERR_UNSUPPORTED, "an fp8 q needs an fp8 (e4m3 or e5m2) KV cache");
+    return fail(MSA_ERR_UNSUPPORTED, "an fp8 q needs an fp8 (e4m3 or e5m2) or MXFP4 KV cache");
   return MSA_OK;
 }
 
@@ -124,6 +128,20 @@ msa_status check_kv(const void* kv_cache, const int64_t kv_strides[4], int64_t n
   if (kv_strides[3] != 1)
     return fail(MSA_ERR_INVALID_ARG, "kv_cache last-dim stride must be 1 (got %lld)",
                 (long long)kv_strides[3]);
+  if (!aligned16(kv_cache)) return fail(MSA_ERR_INVALID_ARG, "kv_cache is not 16-byte aligned");
+  if (kv_dtype == MSA_KV_MXFP4) {
+    for (int d = 0; d < 3; ++d) {
+      if (kv_strides[d] < 1 || kv_strides[d] % 16 != 0)
+        return fail(MSA_ERR_INVALID_ARG, "MXFP4 kv_cache stride %d (%lld bytes) must be a "
+                    "positive multiple of 16", d, (long long)kv_strides[d]);
+    }
+    if (kv_strides[2] < kMxfp4SlotBytes)
+      return fail(MSA_ERR_INVALID_ARG, "MXFP4 K -> V slot offset %lld is shorter than a slot "
+                  "(8704 bytes)", (long long)kv_strides[2]);
+    if (kv_strides[2] > (1 << 24))
+      return fail(MSA_ERR_UNSUPPORTED, "MXFP4 K -> V slot offset above 16 MiB");
+    return MSA_OK;
+  }
   const int64_t eb = elem_bytes(kv_dtype);
   for (int d = 0; d < 3; ++d) {
     if (kv_strides[d] < 1)
@@ -137,7 +155,6 @@ msa_status check_kv(const void* kv_cache, const int64_t kv_strides[4], int64_t n
   if (kv_strides[2] < 2 * msa::kHeadDim)
     return fail(MSA_ERR_INVALID_ARG, "kv_cache row stride %lld is shorter than a packed K|V "
                 "row (256 elements)", (long long)kv_strides[2]);
-  if (!aligned16(kv_cache)) return fail(MSA_ERR_INVALID_ARG, "kv_cache is not 16-byte aligned");
   return MSA_OK;
 }
 
@@ -626,6 +643,25 @@ msa_status msa_fp8_e4m3_to_bf16(const void* in, void* out, int64_t n, void* stre
 
 msa_status msa_fp8_e5m2_to_bf16(const void* in, void* out, int64_t n, void* stream) {
   return fp8_to_bf16(in, out, n, msa::kKvE5m2, stream);
+}
+
+msa_status msa_mxfp4_to_bf16(const void* kv_cache, const int64_t kv_strides[4],
+                             int64_t num_kv_blocks, int32_t num_kv_heads, void* out,
+                             void* stream) {
+  msa_status st = check_kv(kv_cache, kv_strides, num_kv_blocks, MSA_KV_MXFP4);
+  if (st != MSA_OK) return st;
+  if (out == nullptr) return fail(MSA_ERR_INVALID_ARG, "out is NULL");
+  if (!aligned16(out)) return fail(MSA_ERR_INVALID_ARG, "out is not 16-byte aligned");
+  if (num_kv_heads < 1 || num_kv_heads > 1024)
+    return fail(MSA_ERR_INVALID_ARG, "num_kv_heads must be in 1..1024 (got %d)", num_kv_heads);
+  if (num_kv_blocks * num_kv_heads * msa::kPage * 8 > ((int64_t)1 << 39))
+    return fail(MSA_ERR_UNSUPPORTED, "cache too large for one conversion launch");
+  hipError_t e = msa::launch_mxfp4_to_bf16(static_cast<const uint8_t*>(kv_cache), kv_strides[0],
+                                           kv_strides[1], kv_strides[2], num_kv_blocks,
+                                           num_kv_heads, static_cast<uint16_t*>(out),
+                                           static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return device_fail(e, "MXFP4 conversion launch");
+  return ok();
 }
 
 }  // extern "C"

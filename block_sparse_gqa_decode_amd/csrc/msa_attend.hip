@@ -54,7 +54,7 @@
 // over half the q heads each measured no faster: with one workgroup per CU
 // the step is bound by HBM latency and bandwidth, not by issue.)
 //
-// Formats: K|V entries are bf16, OCP fp8 e4m3fn or OCP fp8 e5m2; q is bf16 or
+// Formats: K|V entries are bf16, OCP fp8 e4m3fn, OCP fp8 e5m2 or MXFP4; q is bf16 or
 // fp8 e4m3fn with a per-tensor q scale (vLLM API page
 // "vllm.models.minimax_m3.nvidia.msa_cutlass_sparse_decode":
 // msa_cutlass_sparse_decode(query_fp8, ..., q_scale_float, ...)).  With a bf16
@@ -64,6 +64,17 @@
 // 64+16g..64+16g+15 in lane group g, the same runs the K loads already fetch.
 // The q, k and softmax scales fold into one log2-domain factor.  P V stays a
 // bf16 MFMA (V widened to bf16).
+//
+// 4-bit pages (an MXFP4 analogue of the NVFP4 head-slot page of the vLLM test
+// file, _make_nvfp4_kv_cache): head h's K slot holds 128 rows of 64 bytes of
+// e2m1 codes, then 128 rows of four E8M0 scales, one per 32 head dims; its V
+// slot follows at a fixed offset.  A K lane takes the 32 contiguous head dims
+// 32g..32g+31 of its key row, which is one MX block: with an fp8 q they are
+// the A operand of the scaled 16x16x128 MFMA (fp4 A, fp8 B) with the block's
+// scale code as the lane's A scale; with a bf16 q they widen to bf16 with that
+// scale, and q takes the same 32-dim chunks.  A V lane widens the 8 dims
+// 8n..8n+7 of each of its keys with the key's block scale, then the byte
+// permute transposes them as for 8-bit V.
 //
 // NaN safety: rows past a page's visible count are never loaded (row index
 // clamped to the last visible row) and their scores are set to -inf, so stale
@@ -104,7 +115,7 @@ __device__ __forceinline__ void merge_splits(const AttendParams& p, int64_t row,
 
 template <int kKv, int kQ, bool kVarlen>
 __global__ __launch_bounds__(kThreads) void attend_kernel(AttendParams p) {
-  constexpr bool kFp8 = kKv != kKvBf16;  // 8-bit K|V entries
+  constexpr int kKind = kv_kind(kKv);
   __shared__ int32_t s_page[kMaxTopk];
   __shared__ int32_t s_nvis[kMaxTopk];
   __shared__ int32_t s_nlive;
@@ -177,29 +188,11 @@ __global__ __launch_bounds__(kThreads) void attend_kernel(AttendParams p) {
     if (lane == 0) s_nlive = __popcll(mask);
   }
 
-  // Q^T operand: q row n, head dims 16g.. and 64+16g.. (see header comment).
+  // Q^T operand of q row n (see load_q_operand for the head-dim slots).
   QRegs<kQ> qf;
   const int64_t q_row = (int64_t)t * p.hq + head0 + n;
-  if constexpr (kQ == kQE4m3) {
-    u32x4_t lo = u32x4_t{0u, 0u, 0u, 0u}, hi = lo;
-    if (n < rows) {
-      const uint8_t* qp = p.q + q_row * kHeadDim;
-      lo = *reinterpret_cast<const u32x4_t*>(qp + 16 * g);
-      hi = *reinterpret_cast<const u32x4_t*>(qp + 64 + 16 * g);
-    }
-    qf.b = cat_i32x8(lo, hi);
-  } else {
-    if (n < rows) {
-      const uint16_t* qp = reinterpret_cast<const uint16_t*>(p.q) + q_row * kHeadDim;
-      qf.f[0] = as_bf16x8(*reinterpret_cast<const u32x4_t*>(qp + 16 * g));
-      qf.f[1] = as_bf16x8(*reinterpret_cast<const u32x4_t*>(qp + 16 * g + 8));
-      qf.f[2] = as_bf16x8(*reinterpret_cast<const u32x4_t*>(qp + 64 + 16 * g));
-      qf.f[3] = as_bf16x8(*reinterpret_cast<const u32x4_t*>(qp + 64 + 16 * g + 8));
-    } else {
-#pragma unroll
-      for (int c = 0; c < 4; ++c) qf.f[c] = as_bf16x8(u32x4_t{0u, 0u, 0u, 0u});
-    }
-  }
+  load_q_operand<kKind, kQ>(qf, p.q + q_row * kHeadDim * (kQ == kQE4m3 ? 1 : 2), n < rows,
+                            g);
   __syncthreads();
 
   const int nlive = s_nlive;
@@ -209,7 +202,7 @@ __global__ __launch_bounds__(kThreads) void attend_kernel(AttendParams p) {
   const int kbase = wave * kKeysPerWave;
   const uint8_t* head_base = p.kv + h * p.kv_s1;
   const uint32_t row_stride = (uint32_t)p.kv_s2;
-  const LaneRows lr = lane_rows<kFp8>(kbase, n, g);
+  const LaneRows lr = lane_rows<kKind>(kbase, n, g);
 
   float m_run = -INFINITY;
   float l_part = 0.f;
@@ -223,13 +216,13 @@ __global__ __launch_bounds__(kThreads) void attend_kernel(AttendParams p) {
   // visible row, so no load sits on a conditional path before a wait.  Page
   // ids and visible counts are wave-uniform and live in scalar registers.
   if (lo < hi) {
-    PageRegs<kFp8> buf[kDepth];
+    PageRegs<kKind> buf[kDepth];
 #pragma unroll
     for (int j = 0; j < kDepth - 1; ++j) {
       const int pi = min(lo + j, hi - 1);
       const int pg = __builtin_amdgcn_readfirstlane(s_page[pi]);
       const int nv = __builtin_amdgcn_readfirstlane(s_nvis[pi]);
-      load_page<kFp8>(buf[j], head_base + (int64_t)pg * p.kv_s0, row_stride, nv - 1, lr);
+      load_page<kKind>(buf[j], head_base + (int64_t)pg * p.kv_s0, row_stride, nv - 1, lr);
     }
     for (int i = lo;; i += kDepth) {
 #pragma unroll
@@ -239,11 +232,11 @@ __global__ __launch_bounds__(kThreads) void attend_kernel(AttendParams p) {
         const int pn = min(cur + kDepth - 1, hi - 1);
         const int pg = __builtin_amdgcn_readfirstlane(s_page[pn]);
         const int nvn = __builtin_amdgcn_readfirstlane(s_nvis[pn]);
-        load_page<kFp8>(buf[(j + kDepth - 1) % kDepth], head_base + (int64_t)pg * p.kv_s0,
-                        row_stride, nvn - 1, lr);
+        load_page<kKind>(buf[(j + kDepth - 1) % kDepth], head_base + (int64_t)pg * p.kv_s0,
+                         row_stride, nvn - 1, lr);
         const int nv = __builtin_amdgcn_readfirstlane(s_nvis[cur]);
         if (kbase < nv)
-          attend_page<kKv, kQ>(buf[j], qf, kbase, nv, g, p.scale_log2, m_run, l_part, o);
+          attend_page<kKv, kQ>(buf[j], qf, lr, kbase, nv, g, p.scale_log2, m_run, l_part, o);
       }
     }
   }
@@ -377,6 +370,32 @@ __global__ __launch_bounds__(256) void fp8_to_bf16_kernel(const uint8_t* in, uin
     if (base + b < n) out[base + b] = vals[b];
 }
 
+// MXFP4 head-slot pages -> packed bf16 K|V rows [num_blocks, hkv, 128, 256]
+// (block scales applied, global scales not).  Item = (page, head, row, side,
+// 32-dim block): 16 data bytes and one scale in, 64 bytes out.
+__global__ __launch_bounds__(256) void mxfp4_to_bf16_kernel(const uint8_t* kv, int64_t s0,
+                                                            int64_t s1, int64_t s2,
+                                                            int64_t num_blocks, int hkv,
+                                                            uint16_t* out) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= num_blocks * hkv * kPage * 8) return;
+  const int blk = (int)(i & 3);
+  const int side = (int)((i >> 2) & 1);
+  const int64_t rowid = i >> 3;                     // (page * hkv + head) * 128 + row
+  const int row = (int)(rowid % kPage);
+  const int64_t ph = rowid / kPage;
+  const int h = (int)(ph % hkv);
+  const int64_t page = ph / hkv;
+  const uint8_t* slot = kv + page * s0 + h * s1 + side * s2;
+  const u32x4_t d = *reinterpret_cast<const u32x4_t*>(slot + row * kF4RowBytes + 16 * blk);
+  const float sc = e8m0_to_f32(slot[kF4ScaleBase + row * 4 + blk]);
+  uint16_t* dst = out + rowid * (2 * kHeadDim) + side * kHeadDim + 32 * blk;
+  *reinterpret_cast<u32x4_t*>(dst) = f4x8_to_bf16x8(d.x, sc);
+  *reinterpret_cast<u32x4_t*>(dst + 8) = f4x8_to_bf16x8(d.y, sc);
+  *reinterpret_cast<u32x4_t*>(dst + 16) = f4x8_to_bf16x8(d.z, sc);
+  *reinterpret_cast<u32x4_t*>(dst + 24) = f4x8_to_bf16x8(d.w, sc);
+}
+
 }  // namespace
 
 template <bool kVarlen>
@@ -388,6 +407,8 @@ static hipError_t launch_attend_rows(const AttendParams& p, int kv_fmt, int q_fm
       hipLaunchKernelGGL((attend_kernel<kKvE4m3, kQE4m3, kVarlen>), gd, bd, 0, stream, p);
     else if (kv_fmt == kKvE5m2)
       hipLaunchKernelGGL((attend_kernel<kKvE5m2, kQE4m3, kVarlen>), gd, bd, 0, stream, p);
+    else if (kv_fmt == kKvMxfp4)
+      hipLaunchKernelGGL((attend_kernel<kKvMxfp4, kQE4m3, kVarlen>), gd, bd, 0, stream, p);
     else
       return hipErrorInvalidValue;
   } else {
@@ -395,6 +416,8 @@ static hipError_t launch_attend_rows(const AttendParams& p, int kv_fmt, int q_fm
       hipLaunchKernelGGL((attend_kernel<kKvE4m3, kQBf16, kVarlen>), gd, bd, 0, stream, p);
     else if (kv_fmt == kKvE5m2)
       hipLaunchKernelGGL((attend_kernel<kKvE5m2, kQBf16, kVarlen>), gd, bd, 0, stream, p);
+    else if (kv_fmt == kKvMxfp4)
+      hipLaunchKernelGGL((attend_kernel<kKvMxfp4, kQBf16, kVarlen>), gd, bd, 0, stream, p);
     else
       hipLaunchKernelGGL((attend_kernel<kKvBf16, kQBf16, kVarlen>), gd, bd, 0, stream, p);
   }
@@ -416,6 +439,16 @@ hipError_t launch_merge(const AttendParams& p, hipStream_t stream) {
   const int64_t grid = (int64_t)p.real_rows * p.hkv;
   if (grid <= 0) return hipSuccess;
   hipLaunchKernelGGL(merge_kernel, dim3((uint32_t)grid), dim3(256), 0, stream, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_mxfp4_to_bf16(const uint8_t* kv, int64_t s0, int64_t s1, int64_t s2,
+                                int64_t num_blocks, int hkv, uint16_t* out, hipStream_t stream) {
+  const int64_t items = num_blocks * hkv * kPage * 8;
+  if (items <= 0) return hipSuccess;
+  const int64_t grid = (items + 255) / 256;
+  hipLaunchKernelGGL(mxfp4_to_bf16_kernel, dim3((uint32_t)grid), dim3(256), 0, stream, kv, s0,
+                     s1, s2, num_blocks, hkv, out);
   return hipGetLastError();
 }
 

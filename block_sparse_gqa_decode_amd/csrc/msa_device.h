@@ -1,5 +1,6 @@
-// Device-side helpers for gfx950: vector types, the bf16 and fp8 MFMA tiles,
-// fp8 (e4m3fn / e5m2) -> bf16 conversion and wavefront reductions.
+// Device-side helpers for gfx950: vector types, the bf16, fp8 and fp4 x fp8
+// MFMA tiles, fp8 (e4m3fn / e5m2) and MXFP4 -> bf16 conversion and wavefront
+// reductions.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -34,6 +35,19 @@ template <int kAFmt, int kBFmt>
 __device__ __forceinline__ f32x4_t mfma_f8_16x16x128(i32x8_t a, i32x8_t b, f32x4_t c) {
   return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, kAFmt, kBFmt, 0, 127, 0,
                                                           127);
+}
+
+// D = A(16x128) * B(128x16) + C with an MXFP4 A (32 e2m1 codes per lane in
+// the low four dwords) and an fp8 e4m3fn B.  The fp4 A lane (n, g) holds row n,
+// contraction indexes 32g..32g+31 in order, and its E8M0 scale code a_scale
+// multiplies exactly those 32; the fp8 B lane (n, g) holds column n,
+// contraction indexes 16g..16g+15 (bytes 0..15) and 64+16g..64+16g+15 (bytes
+// 16..31), at unit scale (both layouts measured on gfx950).
+__device__ __forceinline__ f32x4_t mfma_f4f8_16x16x128(u32x4_t a, int a_scale, i32x8_t b,
+                                                        f32x4_t c) {
+  const i32x8_t a8 = i32x8_t{(int32_t)a.x, (int32_t)a.y, (int32_t)a.z, (int32_t)a.w,
+                             0, 0, 0, 0};
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a8, b, c, 4, 0, 0, a_scale, 0, 127);
 }
 
 __device__ __forceinline__ i32x8_t cat_i32x8(u32x4_t lo, u32x4_t hi) {
@@ -77,6 +91,25 @@ __device__ __forceinline__ u32x4_t f8x8_to_bf16x8(uint32_t lo, uint32_t hi) {
     r.z = fp8x2_to_bf16x2<false>(hi);
     r.w = fp8x2_to_bf16x2<true>(hi);
   }
+  return r;
+}
+
+// OCP E8M0 block-scale code -> fp32 2^(code-127): code 0 is the subnormal
+// 2^-127, code 255 NaN.
+__device__ __forceinline__ float e8m0_to_f32(uint32_t code) {
+  const uint32_t bits = code == 0u ? 0x00400000u : (code == 255u ? 0x7fc00000u : code << 23);
+  return __builtin_bit_cast(float, bits);
+}
+
+// Eight OCP e2m1 codes (one dword; element 2i is the low nibble of byte i)
+// times a block scale -> eight bf16, in element order.  Exact: an e2m1 value
+// times a power of two is a bf16 value.
+__device__ __forceinline__ u32x4_t f4x8_to_bf16x8(uint32_t w, float scale) {
+  u32x4_t r;
+  r.x = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 0));
+  r.y = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 1));
+  r.z = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 2));
+  r.w = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 3));
   return r;
 }
 

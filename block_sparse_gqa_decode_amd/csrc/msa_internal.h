@@ -25,13 +25,16 @@ constexpr int kXcdSlots = 8;   // XCDs a launch is dealt across, round robin
 constexpr int kKvBf16 = 0;
 constexpr int kKvE4m3 = 1;     // OCP fp8 e4m3fn
 constexpr int kKvE5m2 = 2;     // OCP fp8 e5m2
+constexpr int kKvMxfp4 = 3;    // OCP MXFP4 head slots (e2m1 + E8M0 per 32 dims)
 constexpr int kQBf16 = 0;
 constexpr int kQE4m3 = 1;
 
 struct AttendParams {
   const uint8_t* q;         // bf16 or fp8 e4m3fn [rows, hq, 128] (bytes)
   const uint8_t* kv;        // packed K|V base (bytes)
-  int64_t kv_s0, kv_s1, kv_s2;  // strides in bytes (page, head, row)
+  // Strides in bytes: page, head, row.  For MXFP4 head slots: page, head
+  // (to the head's K slot), and the K slot -> V slot offset.
+  int64_t kv_s0, kv_s1, kv_s2;
   int64_t num_kv_blocks;
   const int32_t* block_table;
   int32_t bt_stride;
@@ -58,7 +61,7 @@ struct AttendParams {
 struct ScoreParams {
   const uint8_t* q;         // bf16 or fp8 e4m3fn [rows, hq, 128] (bytes)
   const uint8_t* kv;
-  int64_t kv_s0, kv_s1, kv_s2;  // bytes
+  int64_t kv_s0, kv_s1, kv_s2;  // bytes, as in AttendParams
   int64_t num_kv_blocks;
   const int32_t* block_table;
   int32_t bt_stride;
@@ -76,7 +79,7 @@ struct SelectParams {
   int32_t hkv, max_blocks, num_rows, k;
 };
 
-// kv_fmt: kKv*; q_fmt: kQ*.  An fp8 q needs an 8-bit KV format.
+// kv_fmt: kKv*; q_fmt: kQ*.  An fp8 q needs an 8-bit or 4-bit KV format.
 hipError_t launch_attend(const AttendParams& p, int kv_fmt, int q_fmt, hipStream_t stream);
 hipError_t launch_merge(const AttendParams& p, hipStream_t stream);
 // Multi-row tiles of tile_rows (2 or 4) token rows; p.num_units = tiles * hkv.
@@ -87,5 +90,9 @@ hipError_t launch_select(const SelectParams& p, hipStream_t stream);
 // fmt: kKvE4m3 or kKvE5m2
 hipError_t launch_fp8_to_bf16(const uint8_t* in, uint16_t* out, int64_t n, int fmt,
                               hipStream_t stream);
+// MXFP4 head-slot pages (strides in bytes: page, head, K -> V slot) -> bf16
+// packed K|V rows [num_blocks, hkv, 128, 256], unscaled.
+hipError_t launch_mxfp4_to_bf16(const uint8_t* kv, int64_t s0, int64_t s1, int64_t s2,
+                                int64_t num_blocks, int hkv, uint16_t* out, hipStream_t stream);
 
 }  // namespace msa

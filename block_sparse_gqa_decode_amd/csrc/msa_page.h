@@ -30,19 +30,31 @@ constexpr int kKeysPerWave = 32;
 constexpr int kOPad = 4;
 constexpr float kRescaleSlack = 8.0f;
 
-template <bool kFp8>
+// KV element kinds: 0 = 16-bit (bf16), 1 = 8-bit (fp8 e4m3fn / e5m2),
+// 2 = 4-bit (MXFP4 head slots).
+constexpr int kv_kind(int kKv) { return kKv == kKvBf16 ? 0 : (kKv == kKvMxfp4 ? 2 : 1); }
+
+template <int kKind>
 struct PageRegs;
 
 template <>
-struct PageRegs<true> {
+struct PageRegs<1> {
   u32x4_t k[2][2];  // [key tile][run]: 16 fp8 each (head dims 16g.., 64+16g..)
   u32x2_t v[8];     // 8 fp8 (head dims 8n..8n+7) of key slot j
 };
 
 template <>
-struct PageRegs<false> {
+struct PageRegs<0> {
   u32x4_t k[2][4];  // [key tile][chunk]: 8 bf16 each
   u32x4_t v[8];     // 8 bf16 of key slot j
+};
+
+template <>
+struct PageRegs<2> {
+  u32x4_t k[2];     // [key tile]: 32 e2m1 codes, head dims 32g..32g+31
+  uint32_t ks[2];   // [key tile]: the key row's four K block-scale codes
+  uint32_t v[8];    // 8 e2m1 codes (head dims 8n..8n+7) of key slot j
+  uint32_t vs[8];   // key slot j's four V block-scale codes
 };
 
 __device__ __forceinline__ int key_of_slot(int g, int j) {
@@ -50,76 +62,181 @@ __device__ __forceinline__ int key_of_slot(int g, int j) {
 }
 
 // Per-lane constants of the page loads: the page rows a lane reads for the two
-// S^T tiles and the eight P^T / V^T slots, and its byte columns.
+// S^T tiles and the eight P^T / V^T slots, its byte columns, and (4-bit pages)
+// the bit offsets of its K and V block scales within a row's scale dword.
 struct LaneRows {
   int rk[2];
   int rv[8];
   uint32_t ck;  // first K byte of the lane's runs
   uint32_t cv;  // first V byte of the lane's run
+  uint32_t ksh; // 8 * (K block of head dims 32g..32g+31) = 8g
+  uint32_t vsh; // 8 * (V block of head dims 8n..8n+7) = 8 * (n / 4)
 };
 
-template <bool kFp8>
+template <int kKind>
 __device__ __forceinline__ LaneRows lane_rows(int kbase, int n, int g) {
   LaneRows lr;
 #pragma unroll
   for (int tau = 0; tau < 2; ++tau) lr.rk[tau] = kbase + 16 * tau + n;
 #pragma unroll
   for (int j = 0; j < 8; ++j) lr.rv[j] = kbase + key_of_slot(g, j);
-  lr.ck = kFp8 ? 16u * g : 32u * g;
-  lr.cv = kFp8 ? kHeadDim + 8u * n : 2 * kHeadDim + 16u * n;
+  lr.ck = kKind == 0 ? 32u * g : 16u * g;
+  lr.cv = kKind == 0 ? 2 * kHeadDim + 16u * n : (kKind == 1 ? kHeadDim + 8u * n : 4u * n);
+  lr.ksh = 8u * g;
+  lr.vsh = 8u * (n >> 2);
   return lr;
 }
 
+// 4-bit head slot: 128 rows x 64 data bytes, then 128 rows x 4 scale bytes.
+constexpr uint32_t kF4RowBytes = kHeadDim / 2;
+constexpr uint32_t kF4ScaleBase = kPage * kF4RowBytes;
+
 // Loads of one page into registers.  `page` is wave-uniform (SGPRs); rows are
 // clamped to the last visible row `lim`, so rows past it are never read; the
-// per-lane part of every address is a 32-bit offset.
-template <bool kFp8>
-__device__ __forceinline__ void load_page(PageRegs<kFp8>& r, const uint8_t* page,
+// per-lane part of every address is a 32-bit offset.  `row_stride` is the
+// byte stride of packed K|V rows, or for 4-bit pages the K slot -> V slot
+// offset.
+template <int kKind>
+__device__ __forceinline__ void load_page(PageRegs<kKind>& r, const uint8_t* page,
                                           uint32_t row_stride, int lim, const LaneRows& lr) {
+  if constexpr (kKind == 2) {
+    const uint8_t* vpage = page + row_stride;
 #pragma unroll
-  for (int tau = 0; tau < 2; ++tau) {
-    const uint32_t off = (uint32_t)min(lr.rk[tau], lim) * row_stride + lr.ck;
-    if constexpr (kFp8) {
-      r.k[tau][0] = *reinterpret_cast<const u32x4_t*>(page + off);
-      r.k[tau][1] = *reinterpret_cast<const u32x4_t*>(page + off + 64);
-    } else {
-      r.k[tau][0] = *reinterpret_cast<const u32x4_t*>(page + off);
-      r.k[tau][1] = *reinterpret_cast<const u32x4_t*>(page + off + 16);
-      r.k[tau][2] = *reinterpret_cast<const u32x4_t*>(page + off + 128);
-      r.k[tau][3] = *reinterpret_cast<const u32x4_t*>(page + off + 144);
+    for (int tau = 0; tau < 2; ++tau) {
+      const uint32_t row = (uint32_t)min(lr.rk[tau], lim);
+      r.k[tau] = *reinterpret_cast<const u32x4_t*>(page + row * kF4RowBytes + lr.ck);
+      r.ks[tau] = *reinterpret_cast<const uint32_t*>(page + kF4ScaleBase + row * 4u);
+    }
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const uint32_t row = (uint32_t)min(lr.rv[j], lim);
+      r.v[j] = *reinterpret_cast<const uint32_t*>(vpage + row * kF4RowBytes + lr.cv);
+      r.vs[j] = *reinterpret_cast<const uint32_t*>(vpage + kF4ScaleBase + row * 4u);
+    }
+    return;
+  } else {
+#pragma unroll
+    for (int tau = 0; tau < 2; ++tau) {
+      const uint32_t off = (uint32_t)min(lr.rk[tau], lim) * row_stride + lr.ck;
+      if constexpr (kKind == 1) {
+        r.k[tau][0] = *reinterpret_cast<const u32x4_t*>(page + off);
+        r.k[tau][1] = *reinterpret_cast<const u32x4_t*>(page + off + 64);
+      } else {
+        r.k[tau][0] = *reinterpret_cast<const u32x4_t*>(page + off);
+        r.k[tau][1] = *reinterpret_cast<const u32x4_t*>(page + off + 16);
+        r.k[tau][2] = *reinterpret_cast<const u32x4_t*>(page + off + 128);
+        r.k[tau][3] = *reinterpret_cast<const u32x4_t*>(page + off + 144);
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const uint32_t off = (uint32_t)min(lr.rv[j], lim) * row_stride + lr.cv;
+      if constexpr (kKind == 1) {
+        r.v[j] = *reinterpret_cast<const u32x2_t*>(page + off);
+      } else {
+        r.v[j] = *reinterpret_cast<const u32x4_t*>(page + off);
+      }
     }
   }
+}
+
+// The Q^T operand of q row `qp` (bytes; `load` false gives zeros).  A bf16 q
+// takes the contraction slots the widened K of the KV kind holds: chunk c of
+// lane group g is head dims 64*(c/2) + 16g + 8*(c%2) .. +7 (16/8-bit K), or
+// 32g + 8c .. +7 (4-bit K, the lane's MX block).  An fp8 q takes the fp8
+// MFMA's own layout, head dims 16g.. and 64+16g.. (both K kinds meet it).
+template <int kKind, int kQ>
+__device__ __forceinline__ void load_q_operand(QRegs<kQ>& qf, const uint8_t* qp, bool load,
+                                               int g) {
+  if constexpr (kQ == kQE4m3) {
+    u32x4_t lo = u32x4_t{0u, 0u, 0u, 0u}, hi = lo;
+    if (load) {
+      lo = *reinterpret_cast<const u32x4_t*>(qp + 16 * g);
+      hi = *reinterpret_cast<const u32x4_t*>(qp + 64 + 16 * g);
+    }
+    qf.b = cat_i32x8(lo, hi);
+  } else {
+    if (load) {
+      const uint16_t* q16 = reinterpret_cast<const uint16_t*>(qp);
+      if constexpr (kKind == 2) {
+#pragma unroll
+        for (int c = 0; c < 4; ++c)
+          qf.f[c] = as_bf16x8(*reinterpret_cast<const u32x4_t*>(q16 + 32 * g + 8 * c));
+      } else {
+        qf.f[0] = as_bf16x8(*reinterpret_cast<const u32x4_t*>(q16 + 16 * g));
+        qf.f[1] = as_bf16x8(*reinterpret_cast<const u32x4_t*>(q16 + 16 * g + 8));
+        qf.f[2] = as_bf16x8(*reinterpret_cast<const u32x4_t*>(q16 + 64 + 16 * g));
+        qf.f[3] = as_bf16x8(*reinterpret_cast<const u32x4_t*>(q16 + 64 + 16 * g + 8));
+      }
+    } else {
+#pragma unroll
+      for (int c = 0; c < 4; ++c) qf.f[c] = as_bf16x8(u32x4_t{0u, 0u, 0u, 0u});
+    }
+  }
+}
+
+// K tile tau widened to the four bf16 operand chunks of the bf16 MFMA.  `R`
+// is any register set with the K members of PageRegs<kv_kind(kKv)>.
+template <int kKv, class R>
+__device__ __forceinline__ void widen_k_tile(const R& r, int tau, uint32_t ksh,
+                                             bf16x8_t (&kf)[4]) {
+  if constexpr (kv_kind(kKv) == 2) {
+    const float sc = e8m0_to_f32((r.ks[tau] >> ksh) & 0xffu);
+    kf[0] = as_bf16x8(f4x8_to_bf16x8(r.k[tau].x, sc));
+    kf[1] = as_bf16x8(f4x8_to_bf16x8(r.k[tau].y, sc));
+    kf[2] = as_bf16x8(f4x8_to_bf16x8(r.k[tau].z, sc));
+    kf[3] = as_bf16x8(f4x8_to_bf16x8(r.k[tau].w, sc));
+  } else if constexpr (kv_kind(kKv) == 1) {
+    kf[0] = as_bf16x8(f8x8_to_bf16x8<kKv>(r.k[tau][0].x, r.k[tau][0].y));
+    kf[1] = as_bf16x8(f8x8_to_bf16x8<kKv>(r.k[tau][0].z, r.k[tau][0].w));
+    kf[2] = as_bf16x8(f8x8_to_bf16x8<kKv>(r.k[tau][1].x, r.k[tau][1].y));
+    kf[3] = as_bf16x8(f8x8_to_bf16x8<kKv>(r.k[tau][1].z, r.k[tau][1].w));
+  } else {
+#pragma unroll
+    for (int c = 0; c < 4; ++c) kf[c] = as_bf16x8(r.k[tau][c]);
+  }
+}
+
+// S^T tile tau with an fp8 q: one 16x16x128 MFMA on the K codes as loaded.
+template <int kKv, class R>
+__device__ __forceinline__ f32x4_t score_tile_fp8q(const R& r, const QRegs<kQE4m3>& q,
+                                                   int tau, uint32_t ksh) {
+  const f32x4_t zero = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  if constexpr (kv_kind(kKv) == 2) {
+    return mfma_f4f8_16x16x128(r.k[tau], (int)((r.ks[tau] >> ksh) & 0xffu), q.b, zero);
+  } else {
+    return mfma_f8_16x16x128<kKv == kKvE5m2 ? 1 : 0, 0>(cat_i32x8(r.k[tau][0], r.k[tau][1]),
+                                                         q.b, zero);
+  }
+}
+
+// V rows of the eight key slots as bf16 pairs along the head dim:
+// vd[j][w] = dims (8n+2w, 8n+2w+1) of key slot j.
+template <int kKv>
+__device__ __forceinline__ void widen_v(const PageRegs<kv_kind(kKv)>& r, uint32_t vsh,
+                                        u32x4_t (&vd)[8]) {
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
-    const uint32_t off = (uint32_t)min(lr.rv[j], lim) * row_stride + lr.cv;
-    if constexpr (kFp8) {
-      r.v[j] = *reinterpret_cast<const u32x2_t*>(page + off);
+    if constexpr (kv_kind(kKv) == 2) {
+      vd[j] = f4x8_to_bf16x8(r.v[j], e8m0_to_f32((r.vs[j] >> vsh) & 0xffu));
+    } else if constexpr (kv_kind(kKv) == 1) {
+      vd[j] = f8x8_to_bf16x8<kKv>(r.v[j].x, r.v[j].y);
     } else {
-      r.v[j] = *reinterpret_cast<const u32x4_t*>(page + off);
+      vd[j] = r.v[j];
     }
   }
 }
 
 // S^T tile tau (16 keys x 16 q rows) of one page.
 template <int kKv, int kQ>
-__device__ __forceinline__ f32x4_t score_tile(const PageRegs<kKv != kKvBf16>& r,
-                                              const QRegs<kQ>& q, int tau) {
-  const f32x4_t zero = f32x4_t{0.f, 0.f, 0.f, 0.f};
+__device__ __forceinline__ f32x4_t score_tile(const PageRegs<kv_kind(kKv)>& r,
+                                              const QRegs<kQ>& q, int tau, uint32_t ksh) {
   if constexpr (kQ == kQE4m3) {
-    return mfma_f8_16x16x128<kKv == kKvE5m2 ? 1 : 0, 0>(cat_i32x8(r.k[tau][0], r.k[tau][1]),
-                                                         q.b, zero);
+    return score_tile_fp8q<kKv>(r, q, tau, ksh);
   } else {
     bf16x8_t kf[4];
-    if constexpr (kKv != kKvBf16) {
-      kf[0] = as_bf16x8(f8x8_to_bf16x8<kKv>(r.k[tau][0].x, r.k[tau][0].y));
-      kf[1] = as_bf16x8(f8x8_to_bf16x8<kKv>(r.k[tau][0].z, r.k[tau][0].w));
-      kf[2] = as_bf16x8(f8x8_to_bf16x8<kKv>(r.k[tau][1].x, r.k[tau][1].y));
-      kf[3] = as_bf16x8(f8x8_to_bf16x8<kKv>(r.k[tau][1].z, r.k[tau][1].w));
-    } else {
-#pragma unroll
-      for (int c = 0; c < 4; ++c) kf[c] = as_bf16x8(r.k[tau][c]);
-    }
-    f32x4_t s = zero;
+    widen_k_tile<kKv>(r, tau, ksh, kf);
+    f32x4_t s = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int c = 0; c < 4; ++c) s = mfma_bf16_16x16x32(kf[c], q.f[c], s);
     return s;
@@ -127,15 +244,15 @@ __device__ __forceinline__ f32x4_t score_tile(const PageRegs<kKv != kKvBf16>& r,
 }
 
 template <int kKv, int kQ>
-__device__ __forceinline__ void attend_page(const PageRegs<kKv != kKvBf16>& r,
-                                            const QRegs<kQ>& qf, int kbase,
-                                            int nvis, int g, float scale_log2,
+__device__ __forceinline__ void attend_page(const PageRegs<kv_kind(kKv)>& r,
+                                            const QRegs<kQ>& qf, const LaneRows& lr,
+                                            int kbase, int nvis, int g, float scale_log2,
                                             float& m_run, float& l_part,
                                             f32x4_t (&o)[8]) {
   // S^T for the wavefront's two 16-key tiles.
   f32x4_t s[2];
 #pragma unroll
-  for (int tau = 0; tau < 2; ++tau) s[tau] = score_tile<kKv, kQ>(r, qf, tau);
+  for (int tau = 0; tau < 2; ++tau) s[tau] = score_tile<kKv, kQ>(r, qf, tau, lr.ksh);
 
   // Raw scores; keys past the visible count (only on a token's last page)
   // become -inf.  The positive scale is applied after the max.
@@ -185,14 +302,7 @@ __device__ __forceinline__ void attend_page(const PageRegs<kKv != kKvBf16>& r,
 
   // V rows as bf16 pairs along the head dim: vd[j][w] = dims (8n+2w, 8n+2w+1).
   u32x4_t vd[8];
-#pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    if constexpr (kKv != kKvBf16) {
-      vd[j] = f8x8_to_bf16x8<kKv>(r.v[j].x, r.v[j].y);
-    } else {
-      vd[j] = r.v[j];
-    }
-  }
+  widen_v<kKv>(r, lr.vsh, vd);
 #pragma unroll
   for (int t8 = 0; t8 < 8; ++t8) {
     const uint32_t sel = (t8 & 1) ? 0x07060302u : 0x05040100u;

@@ -7,7 +7,7 @@
 // of Q.K, here with the q heads as the 16 columns of the same S^T = K Q^T MFMA
 // tile the attend uses).
 //
-// Formats as in the attend: K is bf16, e4m3fn or e5m2; q is bf16 or fp8
+// Formats as in the attend: K is bf16, e4m3fn, e5m2 or MXFP4; q is bf16 or fp8
 // e4m3fn with a per-tensor q scale.  With an fp8 q each 16-key tile is one
 // 16x16x128 fp8 MFMA on the K bytes as loaded; with a bf16 q the K bytes are
 // widened to bf16 for the bf16 MFMA.  q_scale * k_scale multiplies every dot
@@ -33,6 +33,7 @@
 
 #include "msa_device.h"
 #include "msa_internal.h"
+#include "msa_page.h"
 
 namespace msa {
 namespace {
@@ -43,69 +44,65 @@ constexpr int kScoreKeys = 32;     // keys of a block per wavefront
 constexpr int kScoreDepth = 4;     // blocks in flight per wavefront
 constexpr int kFlush = 32;         // items between LDS flushes of the maxima
 
-template <bool kFp8>
+// The K halves of one block for one wavefront (its 32 keys), by KV kind; the
+// members follow PageRegs so the page header's widening helpers apply.
+template <int kKind>
 struct KHalf;
 
 template <>
-struct KHalf<true> {
+struct KHalf<1> {
   u32x4_t k[2][2];  // [key tile][run of 16 fp8]
 };
 
 template <>
-struct KHalf<false> {
+struct KHalf<0> {
   u32x4_t k[2][4];  // [key tile][chunk of 8 bf16]
 };
 
-template <bool kFp8>
-__device__ __forceinline__ void load_khalf(KHalf<kFp8>& r, const uint8_t* page,
+template <>
+struct KHalf<2> {
+  u32x4_t k[2];     // [key tile]: 32 e2m1 codes, head dims 32g..32g+31
+  uint32_t ks[2];   // [key tile]: the key row's four block-scale codes
+};
+
+// `row_stride`: byte stride of packed K|V rows (unused for a 4-bit K slot).
+template <int kKind>
+__device__ __forceinline__ void load_khalf(KHalf<kKind>& r, const uint8_t* page,
                                            uint32_t row_stride, int lim, int kbase, int n,
                                            int g) {
 #pragma unroll
   for (int tau = 0; tau < 2; ++tau) {
-    const uint32_t off = (uint32_t)min(kbase + 16 * tau + n, lim) * row_stride +
-                         (kFp8 ? 16u * g : 32u * g);
-    if constexpr (kFp8) {
-      r.k[tau][0] = *reinterpret_cast<const u32x4_t*>(page + off);
-      r.k[tau][1] = *reinterpret_cast<const u32x4_t*>(page + off + 64);
+    const uint32_t row = (uint32_t)min(kbase + 16 * tau + n, lim);
+    if constexpr (kKind == 2) {
+      r.k[tau] = *reinterpret_cast<const u32x4_t*>(page + row * kF4RowBytes + 16u * g);
+      r.ks[tau] = *reinterpret_cast<const uint32_t*>(page + kF4ScaleBase + row * 4u);
     } else {
-      r.k[tau][0] = *reinterpret_cast<const u32x4_t*>(page + off);
-      r.k[tau][1] = *reinterpret_cast<const u32x4_t*>(page + off + 16);
-      r.k[tau][2] = *reinterpret_cast<const u32x4_t*>(page + off + 128);
-      r.k[tau][3] = *reinterpret_cast<const u32x4_t*>(page + off + 144);
+      const uint32_t off = row * row_stride + (kKind == 1 ? 16u * g : 32u * g);
+      if constexpr (kKind == 1) {
+        r.k[tau][0] = *reinterpret_cast<const u32x4_t*>(page + off);
+        r.k[tau][1] = *reinterpret_cast<const u32x4_t*>(page + off + 64);
+      } else {
+        r.k[tau][0] = *reinterpret_cast<const u32x4_t*>(page + off);
+        r.k[tau][1] = *reinterpret_cast<const u32x4_t*>(page + off + 16);
+        r.k[tau][2] = *reinterpret_cast<const u32x4_t*>(page + off + 128);
+        r.k[tau][3] = *reinterpret_cast<const u32x4_t*>(page + off + 144);
+      }
     }
   }
 }
 
-template <int kQ>
+template <int kKind, int kQ>
 __device__ __forceinline__ void load_q(QRegs<kQ>& qf, const ScoreParams& p, int t, int h,
                                        int n, int g) {
   const int64_t row = (int64_t)t * p.hq + h * p.group + n;
-  if constexpr (kQ == kQE4m3) {
-    u32x4_t lo = u32x4_t{0u, 0u, 0u, 0u}, hi = lo;
-    if (n < p.group) {
-      const uint8_t* qp = p.q + row * kHeadDim;
-      lo = *reinterpret_cast<const u32x4_t*>(qp + 16 * g);
-      hi = *reinterpret_cast<const u32x4_t*>(qp + 64 + 16 * g);
-    }
-    qf.b = cat_i32x8(lo, hi);
-  } else {
-    if (n < p.group) {
-      const uint16_t* qp = reinterpret_cast<const uint16_t*>(p.q) + row * kHeadDim;
-      qf.f[0] = as_bf16x8(*reinterpret_cast<const u32x4_t*>(qp + 16 * g));
-      qf.f[1] = as_bf16x8(*reinterpret_cast<const u32x4_t*>(qp + 16 * g + 8));
-      qf.f[2] = as_bf16x8(*reinterpret_cast<const u32x4_t*>(qp + 64 + 16 * g));
-      qf.f[3] = as_bf16x8(*reinterpret_cast<const u32x4_t*>(qp + 64 + 16 * g + 8));
-    } else {
-#pragma unroll
-      for (int c = 0; c < 4; ++c) qf.f[c] = as_bf16x8(u32x4_t{0u, 0u, 0u, 0u});
-    }
-  }
+  load_q_operand<kKind, kQ>(qf, p.q + row * kHeadDim * (kQ == kQE4m3 ? 1 : 2), n < p.group,
+                            g);
 }
 
 // The wavefront's max over its 32 keys (those < nvis) and the group's rows of
 // qk_scale * q.k for one block and one token.
 template <int kKv, int kQ>
-__device__ __forceinline__ float block_max(const KHalf<kKv != kKvBf16>& r,
+__device__ __forceinline__ float block_max(const KHalf<kv_kind(kKv)>& r,
                                            const QRegs<kQ>& qf, int kbase, int nvis, int n,
                                            int g, int group, float qk_scale) {
   float best = -INFINITY;
@@ -113,19 +110,10 @@ __device__ __forceinline__ float block_max(const KHalf<kKv != kKvBf16>& r,
   for (int tau = 0; tau < 2; ++tau) {
     f32x4_t s = f32x4_t{0.f, 0.f, 0.f, 0.f};
     if constexpr (kQ == kQE4m3) {
-      s = mfma_f8_16x16x128<kKv == kKvE5m2 ? 1 : 0, 0>(cat_i32x8(r.k[tau][0], r.k[tau][1]),
-                                                        qf.b, s);
+      s = score_tile_fp8q<kKv>(r, qf, tau, 8u * g);
     } else {
       bf16x8_t kf[4];
-      if constexpr (kKv != kKvBf16) {
-        kf[0] = as_bf16x8(f8x8_to_bf16x8<kKv>(r.k[tau][0].x, r.k[tau][0].y));
-        kf[1] = as_bf16x8(f8x8_to_bf16x8<kKv>(r.k[tau][0].z, r.k[tau][0].w));
-        kf[2] = as_bf16x8(f8x8_to_bf16x8<kKv>(r.k[tau][1].x, r.k[tau][1].y));
-        kf[3] = as_bf16x8(f8x8_to_bf16x8<kKv>(r.k[tau][1].z, r.k[tau][1].w));
-      } else {
-#pragma unroll
-        for (int c = 0; c < 4; ++c) kf[c] = as_bf16x8(r.k[tau][c]);
-      }
+      widen_k_tile<kKv>(r, tau, 8u * g, kf);
 #pragma unroll
       for (int c = 0; c < 4; ++c) s = mfma_bf16_16x16x32(kf[c], qf.f[c], s);
     }
@@ -144,7 +132,7 @@ typedef __attribute__((address_space(4))) const int32_t const_i32;
 
 template <int kKv, int kQ, bool kOneToken>
 __global__ __launch_bounds__(kScoreThreads) void score_kernel(ScoreParams p) {
-  constexpr bool kFp8 = kKv != kKvBf16;  // 8-bit K entries
+  constexpr int kKind = kv_kind(kKv);
   __shared__ int32_t s_pref[kMaxScoreBatch + 1];       // blocks before request r
   __shared__ int32_t s_scan[kScoreThreads];
   __shared__ float s_part[kScoreWaves][kFlush * kMaxScoreDql];
@@ -244,7 +232,7 @@ __global__ __launch_bounds__(kScoreThreads) void score_kernel(ScoreParams p) {
     const int32_t* bt_row = p.block_table + (int64_t)r * p.bt_stride;
     const uint8_t* head_base = p.kv + h * p.kv_s1;
     QRegs<kQ> qf;
-    load_q<kQ>(qf, p, t0 + p.dql - 1, h, n, g);
+    load_q<kKind, kQ>(qf, p, t0 + p.dql - 1, h, n, g);
     const int b_last = b + seg - 1;
 
     // Block-table entries are read through the scalar cache (uniform index,
@@ -258,15 +246,15 @@ __global__ __launch_bounds__(kScoreThreads) void score_kernel(ScoreParams p) {
       return pg < 0 ? nullptr : head_base + (int64_t)pg * p.kv_s0;
     };
 
-    KHalf<kFp8> buf[kScoreDepth];
+    KHalf<kKind> buf[kScoreDepth];
     const uint8_t* pages[kScoreDepth];
     int lims[kScoreDepth];
 #pragma unroll
     for (int j = 0; j < kScoreDepth - 1; ++j) {
       const int bb = min(b + j, b_last);
       pages[j] = page_of(bb, lims[j]);
-      load_khalf<kFp8>(buf[j], pages[j] ? pages[j] : head_base, row_stride,
-                       pages[j] ? lims[j] : 0, kbase, n, g);
+      load_khalf<kKind>(buf[j], pages[j] ? pages[j] : head_base, row_stride,
+                        pages[j] ? lims[j] : 0, kbase, n, g);
     }
     for (int i = 0;; i += kScoreDepth) {
 #pragma unroll
@@ -276,8 +264,8 @@ __global__ __launch_bounds__(kScoreThreads) void score_kernel(ScoreParams p) {
           const int jn = (j + kScoreDepth - 1) % kScoreDepth;
           const int bn = min(b + i + j + kScoreDepth - 1, b_last);
           pages[jn] = page_of(bn, lims[jn]);
-          load_khalf<kFp8>(buf[jn], pages[jn] ? pages[jn] : head_base, row_stride,
-                           pages[jn] ? lims[jn] : 0, kbase, n, g);
+          load_khalf<kKind>(buf[jn], pages[jn] ? pages[jn] : head_base, row_stride,
+                            pages[jn] ? lims[jn] : 0, kbase, n, g);
           const int bb = b + i + j;
           const bool ok_page = pages[j] != nullptr;
           // token loop: the last token sees the most; earlier tokens fewer keys
@@ -291,7 +279,7 @@ __global__ __launch_bounds__(kScoreThreads) void score_kernel(ScoreParams p) {
                                        p.qk_scale);
               } else {
                 QRegs<kQ> ql;
-                load_q<kQ>(ql, p, t0 + l, h, n, g);
+                load_q<kKind, kQ>(ql, p, t0 + l, h, n, g);
                 m = block_max<kKv, kQ>(buf[j], ql, kbase, min(nvis, kPage), n, g, p.group,
                                        p.qk_scale);
               }
@@ -528,10 +516,12 @@ hipError_t launch_score(const ScoreParams& p, int kv_fmt, int q_fmt, hipStream_t
   if (q_fmt == kQE4m3) {
     if (kv_fmt == kKvE4m3) launch_score_fmt<kKvE4m3, kQE4m3>(p, g, b, stream);
     else if (kv_fmt == kKvE5m2) launch_score_fmt<kKvE5m2, kQE4m3>(p, g, b, stream);
+    else if (kv_fmt == kKvMxfp4) launch_score_fmt<kKvMxfp4, kQE4m3>(p, g, b, stream);
     else return hipErrorInvalidValue;
   } else {
     if (kv_fmt == kKvE4m3) launch_score_fmt<kKvE4m3, kQBf16>(p, g, b, stream);
     else if (kv_fmt == kKvE5m2) launch_score_fmt<kKvE5m2, kQBf16>(p, g, b, stream);
+    else if (kv_fmt == kKvMxfp4) launch_score_fmt<kKvMxfp4, kQBf16>(p, g, b, stream);
     else launch_score_fmt<kKvBf16, kQBf16>(p, g, b, stream);
   }
   return hipGetLastError();

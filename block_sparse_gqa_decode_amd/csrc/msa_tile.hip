@@ -57,19 +57,18 @@ __device__ __forceinline__ int tile_row(const AttendParams& p, int tile, int w, 
 // row's mask, the online softmax and P V (the single-row attend_page with the
 // K operands and V^T tiles hoisted out of the per-row work).
 template <int kKv, int kQ>
-__device__ __forceinline__ void multi_row_page(const PageRegs<kKv != kKvBf16>& r,
+__device__ __forceinline__ void multi_row_page(const PageRegs<kv_kind(kKv)>& r,
                                                const bf16x8_t (&kf)[2][4],
                                                const u32x4_t (&vt)[8], const QRegs<kQ>& q,
-                                               int kbase, int nvis, int g, float scale_log2,
-                                               float& m_run, float& l_part,
+                                               uint32_t ksh, int kbase, int nvis, int g,
+                                               float scale_log2, float& m_run, float& l_part,
                                                f32x4_t (&o)[8]) {
   const f32x4_t zero = f32x4_t{0.f, 0.f, 0.f, 0.f};
   f32x4_t s[2];
 #pragma unroll
   for (int tau = 0; tau < 2; ++tau) {
     if constexpr (kQ == kQE4m3) {
-      s[tau] = mfma_f8_16x16x128<kKv == kKvE5m2 ? 1 : 0, 0>(
-          cat_i32x8(r.k[tau][0], r.k[tau][1]), q.b, zero);
+      s[tau] = score_tile_fp8q<kKv>(r, q, tau, ksh);
     } else {
       s[tau] = zero;
 #pragma unroll
@@ -117,7 +116,7 @@ __device__ __forceinline__ void multi_row_page(const PageRegs<kKv != kKvBf16>& r
 
 template <int kKv, int kQ, int kM>
 __global__ __launch_bounds__(kThreads) void multi_kernel(AttendParams p) {
-  constexpr bool kFp8 = kKv != kKvBf16;
+  constexpr int kKind = kv_kind(kKv);
   __shared__ int32_t s_upage[kMaxUnion];                // page list: physical page or -1
   __shared__ uint8_t s_unv[kMaxUnion][kMaxTileRows];    // visible rows for each tile row
   __shared__ uint8_t s_umax[kMaxUnion];                 // largest of those (0: skip)
@@ -246,26 +245,8 @@ __global__ __launch_bounds__(kThreads) void multi_kernel(AttendParams p) {
   for (int w = 0; w < kM; ++w) {
     const bool load = s_row_r[w] >= 0 && n < p.group;
     const int64_t q_row = (int64_t)(load ? tile_row(p, tile, w, kM) : 0) * p.hq + head0 + n;
-    if constexpr (kQ == kQE4m3) {
-      u32x4_t a = u32x4_t{0u, 0u, 0u, 0u}, b = a;
-      if (load) {
-        const uint8_t* qp = p.q + q_row * kHeadDim;
-        a = *reinterpret_cast<const u32x4_t*>(qp + 16 * g);
-        b = *reinterpret_cast<const u32x4_t*>(qp + 64 + 16 * g);
-      }
-      qf[w].b = cat_i32x8(a, b);
-    } else {
-      if (load) {
-        const uint16_t* qp = reinterpret_cast<const uint16_t*>(p.q) + q_row * kHeadDim;
-        qf[w].f[0] = as_bf16x8(*reinterpret_cast<const u32x4_t*>(qp + 16 * g));
-        qf[w].f[1] = as_bf16x8(*reinterpret_cast<const u32x4_t*>(qp + 16 * g + 8));
-        qf[w].f[2] = as_bf16x8(*reinterpret_cast<const u32x4_t*>(qp + 64 + 16 * g));
-        qf[w].f[3] = as_bf16x8(*reinterpret_cast<const u32x4_t*>(qp + 64 + 16 * g + 8));
-      } else {
-#pragma unroll
-        for (int c = 0; c < 4; ++c) qf[w].f[c] = as_bf16x8(u32x4_t{0u, 0u, 0u, 0u});
-      }
-    }
+    load_q_operand<kKind, kQ>(qf[w], p.q + q_row * kHeadDim * (kQ == kQE4m3 ? 1 : 2), load,
+                              g);
   }
 
   float m_run[kM], l_part[kM];
@@ -281,7 +262,7 @@ __global__ __launch_bounds__(kThreads) void multi_kernel(AttendParams p) {
   const int kbase = wave * kKeysPerWave;
   const uint8_t* head_base = p.kv + h * p.kv_s1;
   const uint32_t row_stride = (uint32_t)p.kv_s2;
-  const LaneRows lr = lane_rows<kFp8>(kbase, n, g);
+  const LaneRows lr = lane_rows<kKind>(kbase, n, g);
   const int32_t* dense_row =
       p.block_table + (int64_t)(dense_r >= 0 ? dense_r : 0) * p.bt_stride;
 
@@ -316,14 +297,14 @@ __global__ __launch_bounds__(kThreads) void multi_kernel(AttendParams p) {
       lim = max(v, 1) - 1;
     };
 
-    PageRegs<kFp8> buf[kDepth];
+    PageRegs<kKind> buf[kDepth];
 #pragma unroll
     for (int j = 0; j < kDepth - 1; ++j) {
       int pg, lim;
       entry(min(c0 + j, c1 - 1), pg, lim);
       pg = __builtin_amdgcn_readfirstlane(pg);
       lim = __builtin_amdgcn_readfirstlane(lim);
-      load_page<kFp8>(buf[j], head_base + (int64_t)pg * p.kv_s0, row_stride, lim, lr);
+      load_page<kKind>(buf[j], head_base + (int64_t)pg * p.kv_s0, row_stride, lim, lr);
     }
     for (int i = c0;; i += kDepth) {
 #pragma unroll
@@ -335,36 +316,18 @@ __global__ __launch_bounds__(kThreads) void multi_kernel(AttendParams p) {
           entry(min(cur + kDepth - 1, c1 - 1), pg, lim);
           pg = __builtin_amdgcn_readfirstlane(pg);
           lim = __builtin_amdgcn_readfirstlane(lim);
-          load_page<kFp8>(buf[(j + kDepth - 1) % kDepth], head_base + (int64_t)pg * p.kv_s0,
-                          row_stride, lim, lr);
+          load_page<kKind>(buf[(j + kDepth - 1) % kDepth], head_base + (int64_t)pg * p.kv_s0,
+                           row_stride, lim, lr);
           const int li = cur - base;
           if (__builtin_amdgcn_readfirstlane((int)s_umax[li]) > kbase) {
             // Widen this wavefront's keys once for all rows of the tile.
             bf16x8_t kf[2][4];
             if constexpr (kQ != kQE4m3) {
 #pragma unroll
-              for (int tau = 0; tau < 2; ++tau) {
-                if constexpr (kFp8) {
-                  kf[tau][0] = as_bf16x8(f8x8_to_bf16x8<kKv>(buf[j].k[tau][0].x,
-                                                             buf[j].k[tau][0].y));
-                  kf[tau][1] = as_bf16x8(f8x8_to_bf16x8<kKv>(buf[j].k[tau][0].z,
-                                                             buf[j].k[tau][0].w));
-                  kf[tau][2] = as_bf16x8(f8x8_to_bf16x8<kKv>(buf[j].k[tau][1].x,
-                                                             buf[j].k[tau][1].y));
-                  kf[tau][3] = as_bf16x8(f8x8_to_bf16x8<kKv>(buf[j].k[tau][1].z,
-                                                             buf[j].k[tau][1].w));
-                } else {
-#pragma unroll
-                  for (int c = 0; c < 4; ++c) kf[tau][c] = as_bf16x8(buf[j].k[tau][c]);
-                }
-              }
+              for (int tau = 0; tau < 2; ++tau) widen_k_tile<kKv>(buf[j], tau, lr.ksh, kf[tau]);
             }
             u32x4_t vd[8];
-#pragma unroll
-            for (int jj = 0; jj < 8; ++jj) {
-              if constexpr (kFp8) vd[jj] = f8x8_to_bf16x8<kKv>(buf[j].v[jj].x, buf[j].v[jj].y);
-              else vd[jj] = buf[j].v[jj];
-            }
+            widen_v<kKv>(buf[j], lr.vsh, vd);
             u32x4_t vt[8];
 #pragma unroll
             for (int t8 = 0; t8 < 8; ++t8) {
@@ -379,8 +342,8 @@ __global__ __launch_bounds__(kThreads) void multi_kernel(AttendParams p) {
             for (int w = 0; w < kM; ++w) {
               const int nv = __builtin_amdgcn_readfirstlane((int)s_unv[li][w]);
               if (nv > kbase)
-                multi_row_page<kKv, kQ>(buf[j], kf, vt, qf[w], kbase, nv, g, p.scale_log2,
-                                        m_run[w], l_part[w], o[w]);
+                multi_row_page<kKv, kQ>(buf[j], kf, vt, qf[w], lr.ksh, kbase, nv, g,
+                                        p.scale_log2, m_run[w], l_part[w], o[w]);
             }
           }
         }
@@ -471,10 +434,12 @@ hipError_t launch_tile(const AttendParams& p, int kv_fmt, int q_fmt, int tile_ro
   if (q_fmt == kQE4m3) {
     if (kv_fmt == kKvE4m3) return launch_tile_fmt<kKvE4m3, kQE4m3>(p, tile_rows, gd, stream);
     if (kv_fmt == kKvE5m2) return launch_tile_fmt<kKvE5m2, kQE4m3>(p, tile_rows, gd, stream);
+    if (kv_fmt == kKvMxfp4) return launch_tile_fmt<kKvMxfp4, kQE4m3>(p, tile_rows, gd, stream);
     return hipErrorInvalidValue;
   }
   if (kv_fmt == kKvE4m3) return launch_tile_fmt<kKvE4m3, kQBf16>(p, tile_rows, gd, stream);
   if (kv_fmt == kKvE5m2) return launch_tile_fmt<kKvE5m2, kQBf16>(p, tile_rows, gd, stream);
+  if (kv_fmt == kKvMxfp4) return launch_tile_fmt<kKvMxfp4, kQBf16>(p, tile_rows, gd, stream);
   return launch_tile_fmt<kKvBf16, kQBf16>(p, tile_rows, gd, stream);
 }
 

@@ -53,7 +53,7 @@
 extern "C" {
 #endif
 
-#define MSA_ABI_VERSION 3
+#define MSA_ABI_VERSION 4
 
 typedef enum msa_status {
   MSA_OK = 0,
@@ -66,13 +66,31 @@ typedef enum msa_status {
 typedef enum msa_kv_dtype {
   MSA_KV_BF16 = 0,            /* bf16 K|V entries                              */
   MSA_KV_FP8_E4M3 = 1,        /* OCP fp8 e4m3fn K|V entries, per-tensor scale  */
-  MSA_KV_FP8_E5M2 = 2         /* OCP fp8 e5m2 K|V entries, per-tensor scale    */
+  MSA_KV_FP8_E5M2 = 2,        /* OCP fp8 e5m2 K|V entries, per-tensor scale    */
+  MSA_KV_MXFP4 = 3            /* 4-bit head slots, see below                   */
 } msa_kv_dtype;
+
+/* MSA_KV_MXFP4: an OCP-MX analogue of the NVFP4 head-slot page of vLLM's
+ * MiniMax-M3 MSA test file (_make_nvfp4_kv_cache,
+ * test_nvfp4_kv_cache_views_address_head_slots).  Each page holds, per kv head
+ * h, a K slot and a V slot of 8704 bytes each:
+ *   bytes [0, 8192)     128 rows x 64 bytes of OCP e2m1 codes; head dim d of a
+ *                       row is the low (d even) or high (d odd) nibble of
+ *                       byte d/2;
+ *   bytes [8192, 8704)  128 rows x 4 OCP E8M0 block-scale codes; code s of a
+ *                       row scales head dims 32s..32s+31 by 2^(code-127)
+ *                       (code 255 is NaN).
+ * An entry's value is e2m1 * 2^(code-127) * k_scale (K) or * v_scale (V).
+ * The vLLM page layout is the cache tensor uint8 [num_blocks, 2*Hkv, 128, 68]
+ * (slot 2h = K of head h, slot 2h+1 = V), i.e. kv_strides (bytes)
+ * {2*Hkv*8704, 2*8704, 8704, 1}: [0] page stride, [1] head stride (K slot to
+ * the next head's K slot), [2] K slot -> V slot offset, [3] must be 1; [0..2]
+ * positive multiples of 16, [2] >= 8704 and <= 16 MiB. */
 
 typedef enum msa_q_dtype {
   MSA_Q_BF16 = 0,             /* bf16 q                                        */
   MSA_Q_FP8_E4M3 = 1          /* OCP fp8 e4m3fn q codes; value = code * q_scale
-                                 (needs an fp8 KV cache)                       */
+                                 (needs an fp8 or MXFP4 KV cache)              */
 } msa_q_dtype;
 
 /* Static shape of one decode step: the plan key (batch, decode query length,
@@ -162,6 +180,8 @@ msa_status msa_sparse_decode_plan_info(msa_plan plan, int32_t* num_splits,
  *                with strides kv_strides (elements); kv_strides[3] must be 1
  *                and the other strides must be positive multiples of 16 bytes.
  *                HND (vLLM's default) is {Hkv*128*256, 128*256, 256, 1}.
+ *                An MSA_KV_MXFP4 cache is 4-bit head slots instead, with the
+ *                byte strides described at msa_kv_dtype.
  *   block_table  int32 [batch, page_table_stride] physical page ids.
  *   seq_lens     int32 [batch] device copy, including the new tokens; read on
  *                the device, so runs are graph-capturable and may change
@@ -266,6 +286,18 @@ msa_status msa_topk_select(const float* score, const int64_t score_strides[3],
 msa_status msa_fp8_e4m3_to_bf16(const void* in, void* out, int64_t n, void* stream);
 /* The same for OCP fp8 e5m2 codes. */
 msa_status msa_fp8_e5m2_to_bf16(const void* in, void* out, int64_t n, void* stream);
+
+/* Dequantize an MSA_KV_MXFP4 cache (layout and kv_strides as described at
+ * msa_kv_dtype) to packed bf16 K|V rows, with the block scales applied and
+ * the global k/v scales not: out is bf16 bits, contiguous
+ * [num_kv_blocks, num_kv_heads, 128, 256] (K = entries 0..127, V = 128..255),
+ * computed with the attend's own in-register conversion.  The result is exact
+ * (e2m1 times a power of two is a bf16 value).  The vLLM test file's NVFP4
+ * tests compare the MSA kernels against a Triton path run on such a
+ * dequantized cache. */
+msa_status msa_mxfp4_to_bf16(const void* kv_cache, const int64_t kv_strides[4],
+                             int64_t num_kv_blocks, int32_t num_kv_heads, void* out,
+                             void* stream);
 
 /* Message for the last non-OK status returned on this thread ("" if none). */
 const char* msa_last_error(void);

@@ -10,7 +10,8 @@ from workloads import gen
 ATOL = 1e-2
 RTOL = 1e-2
 
-KV_CODES = {gen.KV_FP8: msa.KV_FP8_E4M3, gen.KV_E5M2: msa.KV_FP8_E5M2, gen.KV_BF16: msa.KV_BF16}
+KV_CODES = {gen.KV_FP8: msa.KV_FP8_E4M3, gen.KV_E5M2: msa.KV_FP8_E5M2, gen.KV_BF16: msa.KV_BF16,
+            gen.KV_MXFP4: msa.KV_MXFP4}
 Q_CODES = {gen.Q_BF16: msa.Q_BF16, gen.Q_FP8: msa.Q_FP8_E4M3}
 
 
@@ -18,13 +19,14 @@ class DevCase:
     def __init__(self, case: gen.DecodeCase, dev="cuda:0", layout="hnd"):
         self.case = case
         self.dev = torch.device(dev)
-        if case.kv_dtype == gen.KV_FP8:
-            kv = torch.from_numpy(case.kv)                       # uint8 codes
+        if case.kv_dtype in (gen.KV_FP8, gen.KV_MXFP4):
+            kv = torch.from_numpy(case.kv)                       # uint8 codes / head slots
         elif case.kv_dtype == gen.KV_E5M2:
             kv = torch.from_numpy(case.kv).view(torch.float8_e5m2)
         else:
             kv = torch.from_numpy(case.kv.view(np.int16)).view(torch.bfloat16)
         if layout == "nhd":
+            assert case.kv_dtype != gen.KV_MXFP4, "4-bit pages have one layout"
             # physical (num_blocks, 128, Hkv, 256), viewed logically as HND
             kv = kv.permute(0, 2, 1, 3).contiguous().to(self.dev).permute(0, 2, 1, 3)
         else:
@@ -130,7 +132,7 @@ class PrefillDevCase:
     def __init__(self, case: gen.PrefillCase, dev="cuda:0"):
         self.case = case
         self.dev = torch.device(dev)
-        if case.kv_dtype == gen.KV_FP8:
+        if case.kv_dtype in (gen.KV_FP8, gen.KV_MXFP4):
             kv = torch.from_numpy(case.kv)
         elif case.kv_dtype == gen.KV_E5M2:
             kv = torch.from_numpy(case.kv).view(torch.float8_e5m2)

@@ -120,6 +120,7 @@ def test_plan_rejects_bad_shapes(lib, field, value, status, fragment):
     (msa.KV_BF16, msa.Q_BF16, True), (msa.KV_FP8_E4M3, msa.Q_BF16, True),
     (msa.KV_FP8_E5M2, msa.Q_BF16, True), (msa.KV_FP8_E4M3, msa.Q_FP8_E4M3, True),
     (msa.KV_FP8_E5M2, msa.Q_FP8_E4M3, True), (msa.KV_BF16, msa.Q_FP8_E4M3, False),
+    (msa.KV_MXFP4, msa.Q_BF16, True), (msa.KV_MXFP4, msa.Q_FP8_E4M3, True),
 ])
 def test_plan_format_pairs(lib, kv, q, ok):
     """An fp8 q runs the fp8 x fp8 MFMA and needs an fp8 cache; every other
@@ -233,6 +234,51 @@ def test_bf16_strides_are_checked_in_bytes(lib):
         assert st == msa.MSA_ERR_INVALID_ARG and "16 bytes" in msg
     finally:
         lib.msa_sparse_decode_plan_destroy(h)
+
+
+MXFP4_SLOT = 128 * (64 + 4)
+
+
+@pytest.mark.parametrize("kvs,fragment", [
+    ((2 * MXFP4_SLOT, 2 * MXFP4_SLOT, MXFP4_SLOT, 2), "last-dim stride"),
+    ((2 * MXFP4_SLOT, 2 * MXFP4_SLOT, MXFP4_SLOT + 4, 1), "multiple of 16"),
+    ((2 * MXFP4_SLOT, 2 * MXFP4_SLOT, MXFP4_SLOT // 2, 1), "shorter than a slot"),
+    ((0, 2 * MXFP4_SLOT, MXFP4_SLOT, 1), "positive"),
+    ((2 * MXFP4_SLOT, -16, MXFP4_SLOT, 1), "positive"),
+])
+def test_mxfp4_strides_are_byte_strides_of_head_slots(lib, kvs, fragment):
+    h = _plan(lib, kv_dtype=msa.KV_MXFP4)
+    try:
+        st, msg = _run(lib, h, kvs=kvs)
+        assert st == msa.MSA_ERR_INVALID_ARG and fragment in msg, (st, msg)
+    finally:
+        lib.msa_sparse_decode_plan_destroy(h)
+
+
+def test_mxfp4_conversion_rejects_bad_arguments(lib):
+    good = msa._I64x4(2 * MXFP4_SLOT, 2 * MXFP4_SLOT, MXFP4_SLOT, 1)
+    fn = lib.msa_mxfp4_to_bf16
+    assert fn(None, good, 4, 1, FAKE, None) == msa.MSA_ERR_INVALID_ARG
+    assert fn(FAKE, good, 4, 1, None, None) == msa.MSA_ERR_INVALID_ARG
+    assert fn(FAKE, good, 4, 0, FAKE, None) == msa.MSA_ERR_INVALID_ARG
+    assert fn(FAKE, good, 0, 1, FAKE, None) == msa.MSA_ERR_INVALID_ARG
+    assert fn(FAKE, good, 4, 1, FAKE + 8, None) == msa.MSA_ERR_INVALID_ARG
+    bad = msa._I64x4(2 * MXFP4_SLOT, 2 * MXFP4_SLOT, 100, 1)
+    assert fn(FAKE, bad, 4, 1, FAKE, None) == msa.MSA_ERR_INVALID_ARG
+
+
+def test_binding_mxfp4_cache_view():
+    """A (blocks, 2*Hkv, 128, 68) uint8 cache passes byte strides (page, two
+    slots per head, K -> V slot, 1) and must be declared as MXFP4."""
+    import torch
+    kv = torch.empty(3, 8, 128, 68, dtype=torch.uint8)
+    assert tuple(msa._kv_strides(kv, msa.KV_MXFP4)) == (8 * MXFP4_SLOT, 2 * MXFP4_SLOT,
+                                                         MXFP4_SLOT, 1)
+    assert msa._kv_dtype_of(kv, msa.KV_MXFP4) == msa.KV_MXFP4
+    with pytest.raises(ValueError, match="does not match"):
+        msa._kv_dtype_of(torch.empty(1, dtype=torch.float8_e4m3fn), msa.KV_MXFP4)
+    with pytest.raises(ValueError, match="device"):
+        msa._check_kv(kv, 4, msa.KV_MXFP4)
 
 
 def _score(lib, s, **over):
