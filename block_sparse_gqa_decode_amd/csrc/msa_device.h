@@ -101,6 +101,15 @@ __device__ __forceinline__ float e8m0_to_f32(uint32_t code) {
   return __builtin_bit_cast(float, bits);
 }
 
+// The block scale of byte `shift / 8` of a row's scale dword, as the fp32
+// bit pattern code << 23: exactly 2^(code-127) for codes 1..254.  Code 0
+// (2^-127) reads as 0 and code 255 (NaN) as +inf, a difference of at most
+// 6 * 2^-127 per element, or a non-finite result either way; two operations
+// where the exact e8m0_to_f32 takes six, on the per-page path.
+__device__ __forceinline__ float e8m0_scale_of(uint32_t word, uint32_t shift) {
+  return __builtin_bit_cast(float, ((word >> shift) & 0xffu) << 23);
+}
+
 // Eight OCP e2m1 codes (one dword; element 2i is the low nibble of byte i)
 // times a block scale -> eight bf16, in element order.  Exact: an e2m1 value
 // times a power of two is a bf16 value.

@@ -26,6 +26,7 @@ namespace msa {
 constexpr int kWaves = 4;      // wavefronts sharing one page (32 keys each)
 constexpr int kThreads = 64 * kWaves;
 constexpr int kDepth = 2;      // pages per wavefront in the register ring
+
 constexpr int kKeysPerWave = 32;
 constexpr int kOPad = 4;
 constexpr float kRescaleSlack = 8.0f;
@@ -181,7 +182,7 @@ template <int kKv, class R>
 __device__ __forceinline__ void widen_k_tile(const R& r, int tau, uint32_t ksh,
                                              bf16x8_t (&kf)[4]) {
   if constexpr (kv_kind(kKv) == 2) {
-    const float sc = e8m0_to_f32((r.ks[tau] >> ksh) & 0xffu);
+    const float sc = e8m0_scale_of(r.ks[tau], ksh);
     kf[0] = as_bf16x8(f4x8_to_bf16x8(r.k[tau].x, sc));
     kf[1] = as_bf16x8(f4x8_to_bf16x8(r.k[tau].y, sc));
     kf[2] = as_bf16x8(f4x8_to_bf16x8(r.k[tau].z, sc));
@@ -218,7 +219,7 @@ __device__ __forceinline__ void widen_v(const PageRegs<kv_kind(kKv)>& r, uint32_
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
     if constexpr (kv_kind(kKv) == 2) {
-      vd[j] = f4x8_to_bf16x8(r.v[j], e8m0_to_f32((r.vs[j] >> vsh) & 0xffu));
+      vd[j] = f4x8_to_bf16x8(r.v[j], e8m0_scale_of(r.vs[j], vsh));
     } else if constexpr (kv_kind(kKv) == 1) {
       vd[j] = f8x8_to_bf16x8<kKv>(r.v[j].x, r.v[j].y);
     } else {

@@ -85,7 +85,12 @@ typedef enum msa_kv_dtype {
  * (slot 2h = K of head h, slot 2h+1 = V), i.e. kv_strides (bytes)
  * {2*Hkv*8704, 2*8704, 8704, 1}: [0] page stride, [1] head stride (K slot to
  * the next head's K slot), [2] K slot -> V slot offset, [3] must be 1; [0..2]
- * positive multiples of 16, [2] >= 8704 and <= 16 MiB. */
+ * positive multiples of 16, [2] >= 8704 and <= 16 MiB.
+ * Where the attend and the scorer widen 4-bit entries to bf16 they read a
+ * scale code as the fp32 bit pattern code << 23: code 0 then counts as 0
+ * (not 2^-127, a difference below 2^-124 per element) and code 255 as +inf
+ * (a non-finite result, as NaN gives).  The fp8-q MFMA and msa_mxfp4_to_bf16
+ * decode every code exactly. */
 
 typedef enum msa_q_dtype {
   MSA_Q_BF16 = 0,             /* bf16 q                                        */
