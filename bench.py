@@ -318,7 +318,8 @@ def time_config(name, steps, warmup, replicas, splits, dev, verbose=True, tile_r
         graph.replay()
     gpu_ms, host_s = timed(graph, replays)
     ms_step = gpu_ms / n_steps
-    # The attend kernel alone: same launches, without the merge pass.
+    # The attend kernel alone: same launches, without the merge pass (which
+    # a single-row plan with 2..4 splits does inside the attend).
     for _ in range(warm_replays):
         attend_graph.replay()
     attend_ms, _ = timed(attend_graph, replays)
@@ -341,7 +342,7 @@ def time_config(name, steps, warmup, replicas, splits, dev, verbose=True, tile_r
         "algorithmic_bytes": alg,
         "splits": ds.plan.num_splits,
         "tile_rows": ds.plan.tile_rows,
-        "launches_per_step": 1 if ds.plan.num_splits == 1 else 2,
+        "launches_per_step": 1 if ds.plan.num_splits == 1 or ds.plan.merges_in_attend else 2,
         "attend_ms": attend_ms,
         "real_rows": case.real_rows,
     }

@@ -276,6 +276,9 @@ class DecodePlan:
         self.dense = shape.topk_blocks == 0
         self.num_splits = splits.value
         self.arena_bytes = arena.value
+        # Single-row plans with 2..4 splits combine them inside the attend
+        # (msa_sparse_decode_attend / _merge in the C header).
+        self.merges_in_attend = self.tile_rows == 1 and 2 <= self.num_splits <= 4
 
     @property
     def handle(self):

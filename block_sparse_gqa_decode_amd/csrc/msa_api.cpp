@@ -27,10 +27,12 @@ struct msa_plan_s {
   int32_t splits;
   int32_t real_rows;
   int32_t num_rows;
+  bool fused;               // splits merged inside the attend (2..4 splits, 1 row)
   int64_t arena_bytes;
   void* arena;
   float* part_o;
   float* part_ml;
+  int32_t* arrivals;        // per-unit arrival counters of the fused merge
 };
 
 namespace {
@@ -303,6 +305,10 @@ static msa_status make_plan(const msa_decode_shape* shape, bool prefill, int32_t
   const int64_t per_row = (int64_t)shape->num_q_heads * splits;
   const int64_t o_bytes = splits > 1 ? (int64_t)num_rows * per_row * msa::kHeadDim * 4 : 0;
   const int64_t ml_bytes = splits > 1 ? (int64_t)num_rows * per_row * 2 * 4 : 0;
+  // The single-row attend merges 2..4 splits itself (the last split of a unit
+  // to finish combines them); other plans launch the merge kernel.
+  const bool fused = tile_rows == 1 && splits > 1 && splits <= msa::kMaxFusedSplits;
+  const int64_t arrival_bytes = fused ? (units * 4 + 255) / 256 * 256 : 0;
 
   msa_plan plan = new (std::nothrow) msa_plan_s();
   if (plan == nullptr) return fail(MSA_ERR_OUT_OF_MEMORY, "host allocation failed");
@@ -318,10 +324,12 @@ static msa_status make_plan(const msa_decode_shape* shape, bool prefill, int32_t
   plan->splits = splits;
   plan->real_rows = real_rows;
   plan->num_rows = num_rows;
-  plan->arena_bytes = o_bytes + ml_bytes;
+  plan->fused = fused;
+  plan->arena_bytes = arrival_bytes + o_bytes + ml_bytes;
   plan->arena = nullptr;
   plan->part_o = nullptr;
   plan->part_ml = nullptr;
+  plan->arrivals = nullptr;
   if (plan->arena_bytes > 0) {
     // The arena is the plan's only device state; a plan without one makes no
     // HIP call here.
@@ -340,6 +348,18 @@ static msa_status make_plan(const msa_decode_shape* shape, bool prefill, int32_t
       return device_fail(e, "hipMalloc");
     }
     char* base = static_cast<char*>(plan->arena);
+    if (fused) {
+      // Counters start at zero; every fused run leaves them at zero.
+      plan->arrivals = reinterpret_cast<int32_t*>(base);
+      e = hipMemset(plan->arrivals, 0, (size_t)arrival_bytes);
+      if (e == hipSuccess) e = hipDeviceSynchronize();
+      if (e != hipSuccess) {
+        (void)hipFree(plan->arena);
+        delete plan;
+        return device_fail(e, "arrival counter initialisation");
+      }
+      base += arrival_bytes;
+    }
     plan->part_o = reinterpret_cast<float*>(base);
     plan->part_ml = reinterpret_cast<float*>(base + o_bytes);
   }
@@ -439,6 +459,7 @@ static msa_status run_phases(msa_plan plan, const void* q, const void* kv_cache,
   p.splits = plan->splits;
   p.num_units = plan->num_units;
   p.tile_dense = plan->dense ? 1 : 0;
+  p.arrivals = plan->fused ? plan->arrivals : nullptr;
   if (plan->prefill) {
     p.cu_q = cu_q;
     p.ctx_lens = ctx;
@@ -454,7 +475,7 @@ static msa_status run_phases(msa_plan plan, const void* q, const void* kv_cache,
   e = plan->tile_rows > 1 ? msa::launch_tile(p, s.kv_dtype, s.q_dtype, plan->tile_rows, st_)
                           : msa::launch_attend(p, s.kv_dtype, s.q_dtype, st_);
   if (e != hipSuccess) return device_fail(e, "attend launch");
-  if (merge && plan->splits > 1) {
+  if (merge && plan->splits > 1 && !plan->fused) {
     e = msa::launch_merge(p, st_);
     if (e != hipSuccess) return device_fail(e, "merge launch");
   }
@@ -508,7 +529,7 @@ msa_status msa_sparse_decode_merge(msa_plan plan, void* out, float v_scale, void
   if (out == nullptr || !aligned16(out))
     return fail(MSA_ERR_INVALID_ARG, "out must be non-NULL and 16-byte aligned");
   if (!std::isfinite(v_scale)) return fail(MSA_ERR_INVALID_ARG, "scales must be finite");
-  if (plan->splits == 1) return ok();
+  if (plan->splits == 1 || plan->fused) return ok();
   const msa_decode_shape& s = plan->shape;
   msa::AttendParams p{};
   p.out = static_cast<uint16_t*>(out);

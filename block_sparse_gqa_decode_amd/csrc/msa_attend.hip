@@ -113,12 +113,100 @@ __device__ __forceinline__ void merge_splits(const AttendParams& p, int64_t row,
   store_row(p.out + row * kHeadDim + d0, acc, L, p.v_scale);
 }
 
+// In-kernel split merge.  Every split writes its partial with system-scope
+// stores (sc0 sc1: written through to memory, acknowledged there), waits for
+// them, and bumps the unit's arrival counter with a system-scope atomic; the
+// split that arrives last reads every partial back with system-scope loads
+// (sc0 sc1: no cache keeps a stale copy), combines them in split order with
+// the merge kernel's arithmetic, writes the bf16 row and resets the counter.
+// No workgroup waits for another and no cache is written back or invalidated
+// (a device-scope release fence writes back the whole L2 on this part).
+constexpr int kSysCoherent = 0x11;        // buffer cache policy: sc0 | sc1
+constexpr int kRsrcWord3 = 0x00020000;    // raw buffer descriptor, gfx9 family
+constexpr int kWaitVmem = 0x0F70;         // s_waitcnt vmcnt(0)
+
+template <int kS>
+__device__ __forceinline__ void combine_splits(__amdgpu_buffer_rsrc_t ro,
+                                               __amdgpu_buffer_rsrc_t rm, int qr, int d0,
+                                               uint16_t* dst, float v_scale) {
+  f32x2_t m_l[kS];
+  f32x4_t a[kS], b[kS];
+#pragma unroll
+  for (int s = 0; s < kS; ++s) {
+    const int slot = qr * kS + s;
+    m_l[s] = __builtin_bit_cast(
+        f32x2_t, __builtin_amdgcn_raw_buffer_load_b64(rm, slot * 8, 0, kSysCoherent));
+    a[s] = __builtin_bit_cast(f32x4_t, __builtin_amdgcn_raw_buffer_load_b128(
+                                           ro, (slot * kHeadDim + d0) * 4, 0, kSysCoherent));
+    b[s] = __builtin_bit_cast(f32x4_t, __builtin_amdgcn_raw_buffer_load_b128(
+                                           ro, (slot * kHeadDim + d0 + 4) * 4, 0, kSysCoherent));
+  }
+  float M = -INFINITY;
+#pragma unroll
+  for (int s = 0; s < kS; ++s) M = fmaxf(M, m_l[s].x);
+  float L = 0.f;
+  float acc[8];
+#pragma unroll
+  for (int k = 0; k < 8; ++k) acc[k] = 0.f;
+  if (M != -INFINITY) {
+#pragma unroll
+    for (int s = 0; s < kS; ++s) {
+      const float e = m_l[s].x == -INFINITY ? 0.f : fast_exp2(m_l[s].x - M);
+      L += e * m_l[s].y;
+      acc[0] += e * a[s].x; acc[1] += e * a[s].y; acc[2] += e * a[s].z; acc[3] += e * a[s].w;
+      acc[4] += e * b[s].x; acc[5] += e * b[s].y; acc[6] += e * b[s].z; acc[7] += e * b[s].w;
+    }
+  }
+  store_row(dst, acc, L, v_scale);
+}
+
+// The fused epilogue of one split workgroup of `unit`, whose q rows are
+// urow0 .. urow0 + rows - 1; thread (qr, d0) owns head dims d0..d0+7 of row
+// qr when `owner`.  s_last is a workgroup-shared flag.
+__device__ __forceinline__ void fused_merge(const AttendParams& p, int unit, int64_t urow0,
+                                            int rows, int split, bool owner, int qr, int d0,
+                                            const float (&acc)[8], float M, float L,
+                                            int& s_last) {
+  const int S = p.splits;
+  const __amdgpu_buffer_rsrc_t ro = __builtin_amdgcn_make_buffer_rsrc(
+      p.part_o + urow0 * S * kHeadDim, (short)0, rows * S * kHeadDim * 4, kRsrcWord3);
+  const __amdgpu_buffer_rsrc_t rm = __builtin_amdgcn_make_buffer_rsrc(
+      p.part_ml + urow0 * S * 2, (short)0, rows * S * 2 * 4, kRsrcWord3);
+  if (owner) {
+    const int slot = qr * S + split;
+    const f32x4_t lo = f32x4_t{acc[0], acc[1], acc[2], acc[3]};
+    const f32x4_t hi = f32x4_t{acc[4], acc[5], acc[6], acc[7]};
+    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, lo), ro,
+                                           (slot * kHeadDim + d0) * 4, 0, kSysCoherent);
+    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, hi), ro,
+                                           (slot * kHeadDim + d0 + 4) * 4, 0, kSysCoherent);
+    if (d0 == 0)
+      __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2_t, f32x2_t{M, L}), rm,
+                                            slot * 8, 0, kSysCoherent);
+  }
+  __builtin_amdgcn_s_waitcnt(kWaitVmem);
+  __syncthreads();
+  if (threadIdx.x == 0)
+    s_last = __hip_atomic_fetch_add(p.arrivals + unit, 1, __ATOMIC_RELAXED,
+                                    __HIP_MEMORY_SCOPE_SYSTEM) == S - 1;
+  __syncthreads();
+  if (!s_last) return;
+  if (threadIdx.x == 0)
+    __hip_atomic_store(p.arrivals + unit, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+  if (!owner) return;
+  uint16_t* dst = p.out + (urow0 + qr) * kHeadDim + d0;
+  if (S == 2) combine_splits<2>(ro, rm, qr, d0, dst, p.v_scale);
+  else if (S == 3) combine_splits<3>(ro, rm, qr, d0, dst, p.v_scale);
+  else combine_splits<4>(ro, rm, qr, d0, dst, p.v_scale);
+}
+
 template <int kKv, int kQ, bool kVarlen>
 __global__ __launch_bounds__(kThreads) void attend_kernel(AttendParams p) {
   constexpr int kKind = kv_kind(kKv);
   __shared__ int32_t s_page[kMaxTopk];
   __shared__ int32_t s_nvis[kMaxTopk];
   __shared__ int32_t s_nlive;
+  __shared__ int s_last;
   __shared__ float s_m[kWaves][16];
   __shared__ float s_l[kWaves][16];
   __shared__ float s_o[kWaves][16][kHeadDim + kOPad];
@@ -283,6 +371,11 @@ pages_done:
   const int64_t row = (int64_t)t * p.hq + head0 + qr;
   if (p.splits == 1) {
     if (owner) store_row(p.out + row * kHeadDim + d0, acc, L, p.v_scale);
+    return;
+  }
+  if (p.arrivals != nullptr) {
+    fused_merge(p, unit, (int64_t)t * p.hq + head0, rows, split, owner, qr, d0, acc, M, L,
+                s_last);
     return;
   }
 

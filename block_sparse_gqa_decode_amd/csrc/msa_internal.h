@@ -56,7 +56,13 @@ struct AttendParams {
   // Multi-row tiles (tile kernel only): tile_dense selects every visible
   // block of request-aligned tiles instead of the rows' top-k union.
   int32_t tile_dense;
+  // In-kernel split merge (single-row attend, 2..kMaxFusedSplits splits):
+  // one arrival counter per unit, zero between launches; null = the merge
+  // kernel combines the partials instead.
+  int32_t* arrivals;
 };
+
+constexpr int kMaxFusedSplits = 4;
 
 struct ScoreParams {
   const uint8_t* q;         // bf16 or fp8 e4m3fn [rows, hq, 128] (bytes)

@@ -153,7 +153,10 @@ typedef struct msa_plan_s* msa_plan;
  * persistent fp32 split-K partial arena on HIP device `device` (the only
  * allocation the library makes).  On success *plan_out owns that arena until
  * msa_sparse_decode_plan_destroy.  A plan must not be run concurrently on two
- * streams (the arena is shared).  Shape errors return MSA_ERR_INVALID_ARG or
+ * streams (the arena is shared).  A plan that merges its splits inside the
+ * attend also keeps one int32 arrival counter per work unit in the arena,
+ * zeroed here (a hipMemset and a device synchronisation) and left at zero by
+ * every completed run.  Shape errors return MSA_ERR_INVALID_ARG or
  * MSA_ERR_UNSUPPORTED before any HIP call. */
 msa_status msa_sparse_decode_plan(const msa_decode_shape* shape, int device,
                                   msa_plan* plan_out);
@@ -210,11 +213,13 @@ msa_status msa_sparse_decode_run(msa_plan plan, const void* q, const void* kv_ca
 /* The two launches of msa_sparse_decode_run, for callers that schedule or
  * time them apart.  msa_sparse_decode_run(...) is exactly
  * msa_sparse_decode_attend(...) followed by msa_sparse_decode_merge(...) on the
- * same stream.  With one split (msa_sparse_decode_plan_info) the attend writes
- * `out` itself and the merge launches nothing; with more, the attend leaves
- * fp32 split partials in the plan's arena and the merge combines them by
- * log-sum-exp into `out` (TensorRT-LLM PR #17171, flash-decoding commit:
- * split-K with fp32 partials, zeroed padding rows).  The merge must use the
+ * same stream.  With one split (msa_sparse_decode_plan_info), and for
+ * single-row plans (tile_rows 1) with 2 to 4 splits, whose last split to
+ * finish combines the partials itself, the attend writes `out` and the merge
+ * launches nothing; otherwise the attend leaves fp32 split partials in the
+ * plan's arena and the merge combines them by log-sum-exp into `out`
+ * (TensorRT-LLM PR #17171, flash-decoding commit: split-K with fp32
+ * partials, zeroed padding rows).  The merge must use the
  * same `out`, `v_scale` and stream as the attend before it, and no other run
  * of the plan may come between them. */
 msa_status msa_sparse_decode_attend(msa_plan plan, const void* q, const void* kv_cache,

@@ -516,6 +516,52 @@ def test_attend_then_merge_equals_run():
         assert torch.equal(a.view(torch.int16), b.view(torch.int16)), splits
 
 
+def test_fused_merge_counters_return_to_zero():
+    """Single-row plans with 2..4 splits merge inside the attend through
+    per-unit arrival counters that every run leaves at zero: repeated eager
+    runs with changing inputs, then a captured graph replayed with eager runs
+    in between, each checked against the oracle (a counter left non-zero
+    would skip or double a combine)."""
+    _banner("fused split merge: repeated runs and graph replays")
+    case = gen.make_random_case(117, 6, 2, 16, 2, 8, 500, 9000, pad_rows=1)
+    other = gen.make_random_case(117, 6, 2, 16, 2, 8, 500, 9000, pad_rows=1)
+    other.q = gen.make_q(np.random.default_rng(5), other.num_token_rows, other.num_q_heads)
+    refs = [oracle_attend(case), oracle_attend(other)]
+    q_sets = [torch.from_numpy(c.q.view(np.int16)).view(torch.bfloat16).cuda()
+              for c in (case, other)]
+    d = DevCase(case)
+    for splits in (2, 3, 4):
+        plan = d.plan(splits)
+        assert plan.merges_in_attend and plan.num_splits == splits
+        for rep in range(4):
+            d.q.copy_(q_sets[rep % 2])
+            out = d.new_out()
+            d.run(plan, out=out)
+            torch.cuda.synchronize()
+            assert_parity(to_f64(out), refs[rep % 2], what=f"splits={splits} run {rep}")
+        g = torch.cuda.CUDAGraph()
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s):
+            d.run(plan)
+        torch.cuda.current_stream().wait_stream(s)
+        torch.cuda.synchronize()
+        with torch.cuda.graph(g):
+            d.run(plan)
+        for rep in range(3):
+            d.q.copy_(q_sets[rep % 2])
+            d.out.fill_(float("nan"))
+            torch.cuda.synchronize()
+            g.replay()
+            torch.cuda.synchronize()
+            assert_parity(to_f64(d.out), refs[rep % 2], what=f"splits={splits} replay {rep}")
+            eager = d.new_out()
+            d.q.copy_(q_sets[(rep + 1) % 2])
+            d.run(plan, out=eager)
+            torch.cuda.synchronize()
+            assert_parity(to_f64(eager), refs[(rep + 1) % 2], what=f"eager between {rep}")
+
+
 def test_c5_full_step_full_size_sampled_rows():
     """The full decode step with the indexer at full size (B=64, 64/4 heads,
     seq up to 262144): GPU scores, top-16 and attend checked on sampled token
