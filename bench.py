@@ -20,6 +20,11 @@ zeroed padding rows: one kernel launch) over one batch.  Timing:
   visible K|V rows + q + out + indices + block-table entries (the bytes the
   attend must move as defined per token), and the unique-page lower bound.
 
+Cross-checks in the same line: one step replayed alone right after a 1 GiB
+scrub write (cold) and again straight after (warm), and the float64 oracle
+timed on host cores, single-threaded and over a process pool (the pool runs
+in a child process started before this one touches the GPU).
+
 With --profile-mode the script instead launches eagerly (no graph) a few
 steps for rocprofv3 kernel traces and counters; --copy-calibration runs a
 plain device copy of known size for the counter scale factor.
@@ -262,18 +267,56 @@ class DeviceSet:
         return sum(b[key] for b in self.bytes) / len(self.bytes)
 
 
-def time_config(name, steps, warmup, replicas, splits, dev, verbose=True, tile_rows=0):
+def cold_and_warm(ds, n: int = 5):
+    """One step (replica 0, captured alone) timed right after a 1 GiB scrub
+    write (cold: pages come from HBM) and again straight after (warm: pages
+    in L2 / MALL); medians over n trials, in ms.  Cross-checks of the rotated
+    graph timing, not the reported value."""
+    import statistics
+
+    import torch
+
+    g1 = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g1):
+        ds.run_step(0)
+    torch.cuda.synchronize()
+    scrub = torch.empty(1 << 28, dtype=torch.float32, device=ds.kv.device)
+    cold, warm = [], []
+    for i in range(n):
+        scrub.fill_(float(i))
+        torch.cuda.synchronize()
+        e = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+        e[0].record()
+        g1.replay()
+        e[1].record()
+        g1.replay()
+        e[2].record()
+        torch.cuda.synchronize()
+        cold.append(e[0].elapsed_time(e[1]))
+        warm.append(e[1].elapsed_time(e[2]))
+    del scrub, g1
+    return statistics.median(cold), statistics.median(warm)
+
+
+def make_case(name, extra_replicas):
+    """The named workload with extra (q, top-k) replicas."""
+    from workloads import gen
+
+    if name in gen.PREFILL_CONFIG_NAMES:
+        return gen.make_prefill_config(name, replicas=extra_replicas)
+    if name in gen.DENSE_CONFIG_NAMES:
+        return gen.make_dense_config(name, replicas=extra_replicas)
+    return gen.make_config(name, replicas=extra_replicas)
+
+
+def time_config(name, steps, warmup, replicas, splits, dev, verbose=True, tile_rows=0,
+                cold=False):
     import torch
 
     from workloads import gen
 
     t0 = time.time()
-    if name in gen.PREFILL_CONFIG_NAMES:
-        case = gen.make_prefill_config(name, replicas=replicas - 1)
-    elif name in gen.DENSE_CONFIG_NAMES:
-        case = gen.make_dense_config(name, replicas=replicas - 1)
-    else:
-        case = gen.make_config(name, replicas=replicas - 1)
+    case = make_case(name, replicas - 1)
     ds = DeviceSet(case, replicas, splits, dev, tile_rows=tile_rows)
     if verbose:
         print(f"[bench] {name}: generated + uploaded in {time.time() - t0:.1f}s "
@@ -349,6 +392,8 @@ def time_config(name, steps, warmup, replicas, splits, dev, verbose=True, tile_r
     res["effective_pct_peak"] = 100.0 * res["effective_kv_gbs"] / HBM_PEAK_GBS
     res["unique_pct_peak"] = 100.0 * res["unique_kv_gbs"] / HBM_PEAK_GBS
     del graph, attend_graph
+    if cold:
+        res["cold_ms_per_step"], res["warm_ms_per_step"] = cold_and_warm(ds)
     return res, case
 
 
@@ -519,51 +564,58 @@ def time_full_step(name, steps, warmup, replicas, dev, verbose=True):
     return res
 
 
+def _oracle_row(case, t: int):
+    """The oracle on one token row of the case (all its kv heads)."""
+    from oracle import msa_oracle as om
+
+    if hasattr(case, "cu_seqlens_q"):
+        return om.sparse_prefill(case.q, case.kv, case.kv_dtype, case.k_scale, case.v_scale,
+                                 case.block_table, case.cu_seqlens_q, case.context_lens,
+                                 case.topk, case.num_kv_heads, case.sm_scale, rows=[t],
+                                 q_dtype=case.q_dtype, q_scale=case.q_scale)
+    if case.topk is None:
+        return om.dense_decode(case.q, case.kv, case.kv_dtype, case.k_scale, case.v_scale,
+                               case.block_table, case.seq_lens, case.dql, case.num_kv_heads,
+                               case.sm_scale, rows=[t], q_dtype=case.q_dtype,
+                               q_scale=case.q_scale)
+    return om.sparse_decode(case.q, case.kv, case.kv_dtype, case.k_scale, case.v_scale,
+                            case.block_table, case.seq_lens, case.topk, case.dql,
+                            case.num_kv_heads, case.sm_scale, rows=[t], q_dtype=case.q_dtype,
+                            q_scale=case.q_scale)
+
+
+def _oracle_rows_for(case, order, seconds: float) -> int:
+    """Rows of `order` (cycled) through the oracle for about `seconds`, with
+    BLAS limited to one thread; returns the count done."""
+    try:
+        from threadpoolctl import threadpool_limits
+    except ImportError:  # pragma: no cover
+        threadpool_limits = None
+    ctx = threadpool_limits(limits=1) if threadpool_limits else None
+    if ctx is not None:
+        ctx.__enter__()
+    done = 0
+    t0 = time.perf_counter()
+    try:
+        while True:
+            for t in order:
+                _oracle_row(case, int(t))
+                done += 1
+                if time.perf_counter() - t0 >= seconds:
+                    return done
+    finally:
+        if ctx is not None:
+            ctx.__exit__(None, None, None)
+
+
 def cpu_baseline(case, seconds: float):
     """The float64 oracle, single-threaded, on a bounded sample of the same
     workload's token rows; scaled to tokens/s."""
     import numpy as np
 
-    try:
-        from threadpoolctl import threadpool_limits
-    except ImportError:  # pragma: no cover
-        threadpool_limits = None
-    from oracle import msa_oracle as om
-
-    rows_done = 0
+    order = np.random.default_rng(0).permutation(case.real_rows)
     t0 = time.perf_counter()
-    ctx = threadpool_limits(limits=1) if threadpool_limits else None
-    if ctx is not None:
-        ctx.__enter__()
-    try:
-        order = np.random.default_rng(0).permutation(case.real_rows)
-        done = False
-        while not done:
-            for t in order:
-                if hasattr(case, "cu_seqlens_q"):
-                    om.sparse_prefill(case.q, case.kv, case.kv_dtype, case.k_scale,
-                                      case.v_scale, case.block_table, case.cu_seqlens_q,
-                                      case.context_lens, case.topk, case.num_kv_heads,
-                                      case.sm_scale, rows=[int(t)], q_dtype=case.q_dtype,
-                                      q_scale=case.q_scale)
-                elif case.topk is None:
-                    om.dense_decode(case.q, case.kv, case.kv_dtype, case.k_scale,
-                                    case.v_scale, case.block_table, case.seq_lens, case.dql,
-                                    case.num_kv_heads, case.sm_scale, rows=[int(t)],
-                                    q_dtype=case.q_dtype, q_scale=case.q_scale)
-                else:
-                    om.sparse_decode(case.q, case.kv, case.kv_dtype, case.k_scale,
-                                     case.v_scale, case.block_table, case.seq_lens, case.topk,
-                                     case.dql, case.num_kv_heads, case.sm_scale,
-                                     rows=[int(t)], q_dtype=case.q_dtype,
-                                     q_scale=case.q_scale)
-                rows_done += 1
-                if time.perf_counter() - t0 >= seconds:
-                    done = True
-                    break
-    finally:
-        if ctx is not None:
-            ctx.__exit__(None, None, None)
+    rows_done = _oracle_rows_for(case, order, seconds)
     el = time.perf_counter() - t0
     b = step_bytes(case, case.q, case.topk)
     per_row_bytes = b["effective_kv"] / case.real_rows
@@ -577,6 +629,47 @@ def cpu_baseline(case, seconds: float):
                   f"(token, kv head) units), {el:.1f} s, one thread (BLAS limited to 1)",
         "effective_kv_gbs": rows_done * per_row_bytes / el / 1e9,
         "host_cpus": len(os.sched_getaffinity(0)),
+    }
+
+
+_POOL_CASE = None
+
+
+def _pool_worker(args):
+    order, seconds = args
+    return _oracle_rows_for(_POOL_CASE, order, seconds)
+
+
+def cpu_pool_baseline(name: str, seconds: float, max_workers: int = 16):
+    """The same oracle on every core of the host's share: the workload's rows
+    dealt round-robin to a process pool (one BLAS thread each), each worker
+    busy for about `seconds`.  Runs in a process that never touches the GPU
+    (the bench starts it before its own GPU work)."""
+    import multiprocessing as mp
+
+    import numpy as np
+
+    global _POOL_CASE
+    _POOL_CASE = make_case(name, 0)
+    case = _POOL_CASE
+    workers = max(1, min(max_workers, len(os.sched_getaffinity(0))))
+    order = np.random.default_rng(0).permutation(case.real_rows)
+    parts = [(order[i::workers], seconds) for i in range(workers)]
+    t0 = time.perf_counter()
+    with mp.get_context("fork").Pool(workers) as pool:
+        counts = pool.map(_pool_worker, parts)
+    el = time.perf_counter() - t0
+    rows_done = int(sum(counts))
+    b = step_bytes(case, case.q, case.topk)
+    per_row_bytes = b["effective_kv"] / case.real_rows
+    return {
+        "value": rows_done / el,
+        "unit": "tokens/s",
+        "cores": workers,
+        "kind": "oracle",
+        "sample": f"{rows_done} token rows of replica 0 dealt round-robin to {workers} "
+                  f"worker processes (one BLAS thread each), {el:.1f} s wall",
+        "effective_kv_gbs": rows_done * per_row_bytes / el / 1e9,
     }
 
 
@@ -599,7 +692,7 @@ def profile_mode(name, launches, splits, dev):
 
     from workloads import gen
 
-    case = gen.make_config(name, replicas=1)
+    case = make_case(name, 1)
     if name == FULL_STEP_CONFIG:
         fs = FullStepSet(case, 2, dev)
         for i in range(launches):
@@ -656,7 +749,12 @@ def main():
     ap.add_argument("--profile-mode", action="store_true")
     ap.add_argument("--profile-launches", type=int, default=20)
     ap.add_argument("--copy-calibration", action="store_true")
+    ap.add_argument("--cpu-pool-child", action="store_true", help=argparse.SUPPRESS)
     args = ap.parse_args()
+
+    if args.cpu_pool_child:
+        print(json.dumps(cpu_pool_baseline(args.config, args.cpu_seconds)), flush=True)
+        return
 
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only: this build has no multi-GPU path "
@@ -664,6 +762,28 @@ def main():
               f"request with no exchange, so each GPU would run this same kernel on its "
               f"share.", file=sys.stderr)
         sys.exit(2)
+
+    # The all-core oracle baseline runs in a child process started before this
+    # process touches the GPU (a process pool must not be forked from one that
+    # has).
+    cpu_pool = None
+    if not (args.no_cpu_baseline or args.profile_mode or args.copy_calibration
+            or args.full_step_only):
+        import subprocess
+
+        try:
+            child = subprocess.run(
+                [sys.executable, os.path.abspath(__file__), "--cpu-pool-child", "--config",
+                 args.config, "--cpu-seconds", str(args.cpu_seconds)],
+                capture_output=True, text=True, timeout=args.cpu_seconds * 4 + 120)
+            lines = [ln for ln in child.stdout.splitlines() if ln.startswith("{")]
+            if child.returncode == 0 and lines:
+                cpu_pool = json.loads(lines[-1])
+            else:
+                print(f"[bench] all-core oracle baseline failed: {child.stderr[-500:]}",
+                      file=sys.stderr)
+        except subprocess.TimeoutExpired:
+            print("[bench] all-core oracle baseline timed out", file=sys.stderr)
 
     import torch
 
@@ -689,7 +809,7 @@ def main():
         print(json.dumps(r5), flush=True)
         return
     res, case = time_config(args.config, args.steps, args.warmup, args.replicas,
-                            args.splits, dev, tile_rows=args.tile_rows)
+                            args.splits, dev, tile_rows=args.tile_rows, cold=True)
     others = {}
     if not args.no_other_configs:
         for name in OTHER_CONFIGS:
@@ -758,8 +878,15 @@ def main():
         "unique_kv_gbs": round(res["unique_kv_gbs"], 1),
         "unique_pct_hbm_peak": round(res["unique_pct_peak"], 2),
         "host_ms_per_step": round(res["host_ms_per_step"], 5),
+        "cold_ms_per_step": round(res["cold_ms_per_step"], 5),
+        "warm_ms_per_step": round(res["warm_ms_per_step"], 5),
+        "cold_warm_note": "one step replayed alone as its own graph right after a 1 GiB "
+                          "scrub write (cold) and again straight after (warm: pages in "
+                          "L2/MALL), medians of 5, each including one graph launch; "
+                          "cross-checks, not the value",
         "roofline": roofline,
         "cpu_baseline": cpu,
+        "cpu_baseline_all_cores": cpu_pool,
         "other_configs": others,
         "kernel_source_sha": src_hash,
     }

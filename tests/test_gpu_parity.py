@@ -152,6 +152,10 @@ RANDOM_CASES = [
     (106, 2, 32, 64, 4, 16, 200, 1900, gen.KV_FP8, 4, 0.0, 0, "hnd"),
     (107, 6, 1, 12, 3, 64, 5000, 9000, gen.KV_FP8, 0, 0.5, 2, "nhd"),
     (108, 2, 5, 16, 1, 16, 1, 40, gen.KV_BF16, 2, 0.0, 8, "hnd"),
+    # top-1 (the causal last block only); forced to 2 splits every unit has
+    # an empty split, which the in-kernel merge must weigh as zero
+    (109, 4, 2, 16, 2, 1, 1, 3000, gen.KV_FP8, 1, 0.0, 0, "hnd"),
+    (110, 4, 2, 16, 2, 1, 1, 3000, gen.KV_FP8, 1, 0.0, 2, "hnd"),
 ]
 
 
