@@ -629,7 +629,19 @@ def cpu_baseline(case, seconds: float):
                   f"(token, kv head) units), {el:.1f} s, one thread (BLAS limited to 1)",
         "effective_kv_gbs": rows_done * per_row_bytes / el / 1e9,
         "host_cpus": len(os.sched_getaffinity(0)),
+        "cpu_model": _cpu_model(),
     }
+
+
+def _cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
 
 
 _POOL_CASE = None
@@ -815,8 +827,17 @@ def main():
         for name in OTHER_CONFIGS:
             if name == args.config:
                 continue
-            r2, _ = time_config(name, max(64, args.steps // 4), args.warmup,
-                                args.replicas, args.splits, dev)
+            r2, case2 = time_config(name, max(64, args.steps // 4), args.warmup,
+                                    args.replicas, args.splits, dev)
+            if not args.no_cpu_baseline:
+                # a short single-thread oracle sample beside each GPU number
+                import numpy as np
+
+                order = np.random.default_rng(0).permutation(case2.real_rows)
+                t0 = time.perf_counter()
+                n_rows = _oracle_rows_for(case2, order, 2.0)
+                r2["oracle_tokens_per_s_1thread"] = n_rows / (time.perf_counter() - t0)
+                r2["gpu_over_oracle"] = r2["tokens_per_s"] / r2["oracle_tokens_per_s_1thread"]
             others[name] = {k: (round(v, 4) if isinstance(v, float) else v)
                             for k, v in r2.items()}
         r5 = time_full_step(FULL_STEP_CONFIG, max(32, args.steps // 8), args.warmup,
