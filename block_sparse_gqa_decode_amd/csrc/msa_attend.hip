@@ -38,14 +38,16 @@
 //    transposes them into the 8 d-tiles.  The accumulator then holds
 //    O[q row n][32g + 8i + t8] for i < 4, t8 < 8: 32 contiguous outputs.
 //
-// Split-K: with S > 1 splits every workgroup writes its fp32 partial
-// (unnormalised O, running max and sum in log2 units) to the plan's arena and a
-// second, small kernel merges the S partials of each row by log-sum-exp.  (A
-// merge by the last-arriving workgroup needs a device-scope release, which on
-// this part is a walk of the whole L2 per workgroup: slower than a second
-// launch even without the acquire-side invalidate.)  Workgroup ids are laid
-// out so all splits of a unit get the same XCD slot (the dispatcher deals
-// consecutive workgroups to the 8 XCDs in turn), so they share its L2.
+// Split-K: with S > 1 splits every workgroup produces an fp32 partial
+// (unnormalised O, running max and sum in log2 units) in the plan's arena.
+// With 2..4 splits the last split of a unit to finish merges them in this
+// kernel (fused_merge: system-scope stores and loads of the partials, a
+// system-scope arrival counter; a device-scope fence would write back the
+// whole L2 on this part); with more, a second small kernel merges them by
+// log-sum-exp.  Workgroup ids are laid out so each XCD slot takes a
+// contiguous range of units with all their splits (the dispatcher deals
+// consecutive workgroups to the 8 XCDs in turn), so a request's tokens and
+// heads, which share pages, meet in one L2.
 //
 // Pipeline: each wavefront keeps two pages in registers, one in flight while
 // it computes the other, as a ring unrolled twice so every buffer index is
@@ -216,10 +218,15 @@ __global__ __launch_bounds__(kThreads) void attend_kernel(AttendParams p) {
   const int wave = tid >> 6;
   const int n = lane & 15;
   const int g = lane >> 4;
+  // Workgroups are dealt to the 8 XCDs in turn; XCD slot x takes the
+  // contiguous range of units [x*G, (x+1)*G), G = ceil(units / 8), with all
+  // splits of a unit.  Neighbouring units are a request's tokens and heads,
+  // which share pages and the block-table row, so they meet in one XCD's L2
+  // (every unit has about the same work: its top-k pages).
   const int xslot = blockIdx.x % kXcdSlots;
   const int q8 = blockIdx.x / kXcdSlots;
   const int split = q8 % p.splits;
-  const int unit = (q8 / p.splits) * kXcdSlots + xslot;
+  const int unit = xslot * ((p.num_units + kXcdSlots - 1) / kXcdSlots) + q8 / p.splits;
   if (unit >= p.num_units) return;
   const int t = unit / p.hkv;
   const int h = unit - t * p.hkv;
@@ -391,10 +398,11 @@ pages_done:
   }
 }
 
-// Merge pass: one workgroup per (token row, kv head) unit, placed on the same
-// XCD slot as that unit's attend workgroups so the partials come from the
-// L2 they were written through; thread (q row, 8 head dims).  All of a row's
-// partial loads are issued before any is used.
+// Merge pass: one workgroup per (token row, kv head) unit, placed on the XCD
+// slot that holds the unit in the single-row attend (the contiguous range
+// mapping) so the partials come from the L2 they were written through;
+// thread (q row, 8 head dims).  All of a row's partial loads are issued
+// before any is used.
 template <int kS>
 __device__ __forceinline__ void merge_fixed(const AttendParams& p, int64_t row, int d0) {
   const float* ml = p.part_ml + row * kS * 2;
@@ -428,7 +436,10 @@ __device__ __forceinline__ void merge_fixed(const AttendParams& p, int64_t row, 
 }
 
 __global__ __launch_bounds__(256) void merge_kernel(AttendParams p) {
-  const int unit = blockIdx.x;
+  const int units = p.num_rows * p.hkv;
+  const int unit = (int)(blockIdx.x % kXcdSlots) * ((units + kXcdSlots - 1) / kXcdSlots) +
+                   (int)(blockIdx.x / kXcdSlots);
+  if (unit >= units) return;
   const int t = unit / p.hkv;
   const int h = unit - t * p.hkv;
   const int qr = threadIdx.x >> 4;
@@ -527,10 +538,11 @@ hipError_t launch_attend(const AttendParams& p, int kv_fmt, int q_fmt, hipStream
 }
 
 hipError_t launch_merge(const AttendParams& p, hipStream_t stream) {
-  // Unit u's attend workgroups sit on XCD slot u % 8; merge workgroup u is
-  // dealt to the same slot.
-  const int64_t grid = (int64_t)p.real_rows * p.hkv;
-  if (grid <= 0) return hipSuccess;
+  // Units (token row, kv head), padding rows included (they return at once),
+  // dealt to XCD slots in contiguous ranges as in the single-row attend.
+  const int64_t units = (int64_t)p.num_rows * p.hkv;
+  const int64_t grid = (units + kXcdSlots - 1) / kXcdSlots * kXcdSlots;
+  if (units <= 0) return hipSuccess;
   hipLaunchKernelGGL(merge_kernel, dim3((uint32_t)grid), dim3(256), 0, stream, p);
   return hipGetLastError();
 }
