@@ -44,10 +44,10 @@
 // kernel (fused_merge: system-scope stores and loads of the partials, a
 // system-scope arrival counter; a device-scope fence would write back the
 // whole L2 on this part); with more, a second small kernel merges them by
-// log-sum-exp.  Workgroup ids are laid out so each XCD slot takes a
-// contiguous range of units with all their splits (the dispatcher deals
-// consecutive workgroups to the 8 XCDs in turn), so a request's tokens and
-// heads, which share pages, meet in one L2.
+// log-sum-exp.  Workgroup ids are laid out so each XCD slot takes chunks of
+// consecutive units with all their splits (the dispatcher deals consecutive
+// workgroups to the 8 XCDs in turn), so a request's tokens and heads, which
+// share pages, meet in one L2.
 //
 // Pipeline: each wavefront keeps two pages in registers, one in flight while
 // it computes the other, as a ring unrolled twice so every buffer index is
@@ -218,15 +218,14 @@ __global__ __launch_bounds__(kThreads) void attend_kernel(AttendParams p) {
   const int wave = tid >> 6;
   const int n = lane & 15;
   const int g = lane >> 4;
-  // Workgroups are dealt to the 8 XCDs in turn; XCD slot x takes the
-  // contiguous range of units [x*G, (x+1)*G), G = ceil(units / 8), with all
-  // splits of a unit.  Neighbouring units are a request's tokens and heads,
-  // which share pages and the block-table row, so they meet in one XCD's L2
-  // (every unit has about the same work: its top-k pages).
+  // Workgroups are dealt to the 8 XCDs in turn; each XCD slot takes chunks of
+  // consecutive units (xcd_chunk) with all splits of a unit.  Neighbouring
+  // units are a request's tokens and heads, which share pages and the
+  // block-table row, so they meet in one XCD's L2.
   const int xslot = blockIdx.x % kXcdSlots;
   const int q8 = blockIdx.x / kXcdSlots;
   const int split = q8 % p.splits;
-  const int unit = xslot * ((p.num_units + kXcdSlots - 1) / kXcdSlots) + q8 / p.splits;
+  const int unit = xcd_unit(p.num_units, p.hkv, xslot, q8 / p.splits);
   if (unit >= p.num_units) return;
   const int t = unit / p.hkv;
   const int h = unit - t * p.hkv;
@@ -399,8 +398,8 @@ pages_done:
 }
 
 // Merge pass: one workgroup per (token row, kv head) unit, placed on the XCD
-// slot that holds the unit in the single-row attend (the contiguous range
-// mapping) so the partials come from the L2 they were written through;
+// slot that holds the unit in the single-row attend (xcd_unit) so the
+// partials come from the L2 they were written through;
 // thread (q row, 8 head dims).  All of a row's partial loads are issued
 // before any is used.
 template <int kS>
@@ -437,8 +436,8 @@ __device__ __forceinline__ void merge_fixed(const AttendParams& p, int64_t row, 
 
 __global__ __launch_bounds__(256) void merge_kernel(AttendParams p) {
   const int units = p.num_rows * p.hkv;
-  const int unit = (int)(blockIdx.x % kXcdSlots) * ((units + kXcdSlots - 1) / kXcdSlots) +
-                   (int)(blockIdx.x / kXcdSlots);
+  const int unit = xcd_unit(units, p.hkv, (int)(blockIdx.x % kXcdSlots),
+                            (int)(blockIdx.x / kXcdSlots));
   if (unit >= units) return;
   const int t = unit / p.hkv;
   const int h = unit - t * p.hkv;
@@ -529,8 +528,7 @@ static hipError_t launch_attend_rows(const AttendParams& p, int kv_fmt, int q_fm
 }
 
 hipError_t launch_attend(const AttendParams& p, int kv_fmt, int q_fmt, hipStream_t stream) {
-  const int64_t groups = ((int64_t)p.num_units + kXcdSlots - 1) / kXcdSlots;
-  const int64_t grid = groups * kXcdSlots * p.splits;
+  const int64_t grid = xcd_groups(p.num_units, p.hkv) * kXcdSlots * p.splits;
   if (grid <= 0) return hipSuccess;
   const dim3 gd((uint32_t)grid);
   return p.cu_q != nullptr ? launch_attend_rows<true>(p, kv_fmt, q_fmt, gd, stream)
@@ -539,10 +537,10 @@ hipError_t launch_attend(const AttendParams& p, int kv_fmt, int q_fmt, hipStream
 
 hipError_t launch_merge(const AttendParams& p, hipStream_t stream) {
   // Units (token row, kv head), padding rows included (they return at once),
-  // dealt to XCD slots in contiguous ranges as in the single-row attend.
+  // dealt to XCD slots in chunks as in the single-row attend.
   const int64_t units = (int64_t)p.num_rows * p.hkv;
-  const int64_t grid = (units + kXcdSlots - 1) / kXcdSlots * kXcdSlots;
   if (units <= 0) return hipSuccess;
+  const int64_t grid = xcd_groups(units, p.hkv) * kXcdSlots;
   hipLaunchKernelGGL(merge_kernel, dim3((uint32_t)grid), dim3(256), 0, stream, p);
   return hipGetLastError();
 }

@@ -1,6 +1,6 @@
 // Launch parameters and launcher declarations shared by the C-ABI layer
-// (msa_api.cpp) and the kernel translation units.  Host-visible only: no
-// device code here.
+// (msa_api.cpp) and the kernel translation units, and the unit -> XCD slot
+// chunk size both the launchers and the kernels use.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -20,6 +20,28 @@ constexpr int kMaxPrefills = 1 << 20;   // requests of one prefill plan
 constexpr int kMaxTileRows = 4;        // token rows of a multi-row tile
 constexpr int kMaxUnion = kMaxTileRows * kMaxTopk;   // pages of a tile's union
 constexpr int kXcdSlots = 8;   // XCDs a launch is dealt across, round robin
+
+// Single-row attend and merge: units are dealt to the XCD slots in chunks of
+// consecutive units, so a request's neighbouring tokens and kv heads share
+// one L2.  A chunk is up to 16 token rows' units (all kv heads) and at most
+// an eighth of the launch, so work stays spread when requests differ in
+// cost.  The launch then has ceil(units / (8 * chunk)) * chunk workgroups
+// per slot and split; unit of (slot x, k-th workgroup) =
+// ((k / chunk) * 8 + x) * chunk + k % chunk, each unit exactly once.
+__host__ __device__ inline int xcd_chunk(int units, int hkv) {
+  const int c = units / kXcdSlots < hkv * 16 ? units / kXcdSlots : hkv * 16;
+  return c > 1 ? c : 1;
+}
+
+__host__ __device__ inline int xcd_unit(int units, int hkv, int slot, int k) {
+  const int c = xcd_chunk(units, hkv);
+  return ((k / c) * kXcdSlots + slot) * c + k % c;
+}
+
+inline int64_t xcd_groups(int64_t units, int hkv) {
+  const int64_t c = xcd_chunk((int)units, hkv);
+  return (units + kXcdSlots * c - 1) / (kXcdSlots * c) * c;
+}
 
 // Element formats (the values of msa_kv_dtype / msa_q_dtype).
 constexpr int kKvBf16 = 0;

@@ -511,3 +511,23 @@ def test_dense_and_sparse_runs_check_topk(lib):
     finally:
         lib.msa_sparse_decode_plan_destroy(hd)
         lib.msa_sparse_decode_plan_destroy(hs)
+
+
+def test_xcd_deal_visits_every_unit_once(tmp_path):
+    """The single-row attend and the merge kernel map workgroups to units
+    through msa_internal.h's chunked XCD deal: compiled for the host, it must
+    visit every unit exactly once (a unit it skipped would never be written)."""
+    import shutil
+    import subprocess
+
+    hipcc = shutil.which("hipcc") or "/opt/rocm/bin/hipcc"
+    if not os.path.exists(hipcc):
+        pytest.skip("hipcc not found")
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    exe = tmp_path / "xcd_cover"
+    subprocess.run([hipcc, "-std=c++17", "-O1",
+                    "-I", os.path.join(root, "block_sparse_gqa_decode_amd", "csrc"),
+                    os.path.join(root, "tests", "host", "xcd_cover.cpp"), "-o", str(exe)],
+                   check=True, capture_output=True, timeout=300)
+    out = subprocess.run([str(exe)], check=True, capture_output=True, text=True, timeout=300)
+    assert out.stdout.strip() == "ok"
