@@ -44,6 +44,8 @@ if ROOT not in sys.path:
 
 METRIC = "decode tokens/s and effective KV GB/s (% HBM peak), sparse GQA attend, 1 GPU"
 HBM_PEAK_GBS = 8000.0
+# MI355X dense matrix-core peaks (TFLOP/s): index False = bf16, True = fp8.
+MFMA_PEAK_TFLOPS = {False: 2500.0, True: 5000.0}
 DEFAULT_CONFIG = "c2_tp4_fp8"
 OTHER_CONFIGS = ("c3_tp1_fp8", "c4_spec_ragged", "c2_tp4_fp8q", "c2_tp4_e5m2",
                  "c2_tp4_mxfp4", "c2_tp4_mxfp4_fp8q", "pf1_chunked_prefill", "d1_dense_tp1")
@@ -416,8 +418,13 @@ def scorer_bytes(case):
         case.num_kv_heads
     scorer = k_bytes + q_bytes + score_bytes + table_bytes
     selector = score_bytes + topk_bytes
+    # Matrix-core work: one 16-row S^T tile (the group's q heads, padded to
+    # the MFMA's 16 rows) against all 128 keys of every scored block.
+    items = int(np.sum((case.seq_lens.astype(np.int64) + 127) // 128)) * \
+        case.num_kv_heads * case.dql
+    mfma_flops = items * 2 * 16 * 128 * 128
     return {"k_half": k_bytes, "scorer": scorer, "selector": selector,
-            "algorithmic": scorer + selector}
+            "algorithmic": scorer + selector, "mfma_flops": mfma_flops}
 
 
 class FullStepSet:
@@ -554,6 +561,13 @@ def time_full_step(name, steps, warmup, replicas, dev, verbose=True):
                                / HBM_PEAK_GBS,
         "score_traffic_bytes": (lambda t: None if t is None else t.get("hbm_bytes_per_launch"))(
             load_traffic(kernel_source_hash("score"), "score")),
+        # MFMA use of the HBM-bound scorer: its matrix-core flops over its
+        # time, against the dense peak of the MFMA it issues (bf16 q: bf16,
+        # fp8 q: fp8).
+        "scorer_mfma_tflops": sb["mfma_flops"] / ((score_ms - select_ms) / 1e3) / 1e12,
+        "scorer_mfma_peak_tflops": MFMA_PEAK_TFLOPS[case.q_dtype == "fp8_e4m3"],
+        "scorer_mfma_pct_peak": 100 * sb["mfma_flops"] / ((score_ms - select_ms) / 1e3) / 1e12
+                                / MFMA_PEAK_TFLOPS[case.q_dtype == "fp8_e4m3"],
         "attend_algorithmic_bytes": att, "attend_effective_kv_bytes": eff,
         "attend_algorithmic_gbs": att / (attend_ms / 1e3) / 1e9,
         "step_algorithmic_gbs": (att + sb["algorithmic"]) / (step_ms / 1e3) / 1e9,
