@@ -116,9 +116,10 @@ __device__ __forceinline__ void load_page(PageRegs<kKind>& r, const uint8_t* pag
     }
     return;
   } else {
+    // Row offsets by 24-bit multiplies (rows < 128, row strides < 2^24).
 #pragma unroll
     for (int tau = 0; tau < 2; ++tau) {
-      const uint32_t off = (uint32_t)min(lr.rk[tau], lim) * row_stride + lr.ck;
+      const uint32_t off = __umul24((uint32_t)min(lr.rk[tau], lim), row_stride) + lr.ck;
       if constexpr (kKind == 1) {
         r.k[tau][0] = *reinterpret_cast<const u32x4_t*>(page + off);
         r.k[tau][1] = *reinterpret_cast<const u32x4_t*>(page + off + 64);
@@ -131,7 +132,7 @@ __device__ __forceinline__ void load_page(PageRegs<kKind>& r, const uint8_t* pag
     }
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-      const uint32_t off = (uint32_t)min(lr.rv[j], lim) * row_stride + lr.cv;
+      const uint32_t off = __umul24((uint32_t)min(lr.rv[j], lim), row_stride) + lr.cv;
       if constexpr (kKind == 1) {
         r.v[j] = *reinterpret_cast<const u32x2_t*>(page + off);
       } else {
@@ -228,6 +229,53 @@ __device__ __forceinline__ void widen_v(const PageRegs<kv_kind(kKv)>& r, uint32_
   }
 }
 
+// The eight V^T A operands of O^T += V^T P^T: vt[t8] holds, for head dim
+// 8n + t8, the bf16 values of the lane's eight key slots in pairs
+// (slot 2i, slot 2i+1) = dword i.  8-bit V: one byte permute gathers the two
+// slots' bytes of dims t8 and t8+1, and the two halves of that dword convert
+// straight into dword i of d-tiles t8 and t8+1 (16 permutes, 32 conversions).
+// Other kinds widen each slot's eight dims first (per-key block scales for
+// 4-bit V) and then transpose the bf16 pairs (32 permutes).
+template <int kKv>
+__device__ __forceinline__ void build_vt(const PageRegs<kv_kind(kKv)>& r, uint32_t vsh,
+                                         u32x4_t (&vt)[8]) {
+  if constexpr (kv_kind(kKv) == 1) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const uint32_t lo = h ? r.v[2 * i].y : r.v[2 * i].x;
+        const uint32_t hi = h ? r.v[2 * i + 1].y : r.v[2 * i + 1].x;
+#pragma unroll
+        for (int b = 0; b < 4; b += 2) {
+          // bytes: slot 2i dim b, slot 2i+1 dim b, slot 2i dim b+1, slot 2i+1 dim b+1
+          const uint32_t w = byte_perm(hi, lo, b == 0 ? 0x05010400u : 0x07030602u);
+          const int t8 = 4 * h + b;
+          if constexpr (kKv == kKvE5m2) {
+            vt[t8][i] = bf8x2_to_bf16x2<false>(w);
+            vt[t8 + 1][i] = bf8x2_to_bf16x2<true>(w);
+          } else {
+            vt[t8][i] = fp8x2_to_bf16x2<false>(w);
+            vt[t8 + 1][i] = fp8x2_to_bf16x2<true>(w);
+          }
+        }
+      }
+    }
+  } else {
+    u32x4_t vd[8];
+    widen_v<kKv>(r, vsh, vd);
+#pragma unroll
+    for (int t8 = 0; t8 < 8; ++t8) {
+      const uint32_t sel = (t8 & 1) ? 0x07060302u : 0x05040100u;
+      const int w = t8 >> 1;
+      vt[t8].x = byte_perm(vd[1][w], vd[0][w], sel);
+      vt[t8].y = byte_perm(vd[3][w], vd[2][w], sel);
+      vt[t8].z = byte_perm(vd[5][w], vd[4][w], sel);
+      vt[t8].w = byte_perm(vd[7][w], vd[6][w], sel);
+    }
+  }
+}
+
 // S^T tile tau (16 keys x 16 q rows) of one page.
 template <int kKv, int kQ>
 __device__ __forceinline__ f32x4_t score_tile(const PageRegs<kv_kind(kKv)>& r,
@@ -244,6 +292,51 @@ __device__ __forceinline__ f32x4_t score_tile(const PageRegs<kv_kind(kKv)>& r,
   }
 }
 
+// One page of the online softmax for the lane's eight scores z (raw S^T
+// values, -inf where masked) of q row n: the probabilities
+// 2^(z * scale_log2 - m_run) as the bf16 P^T operand, with l_part and the O
+// accumulators kept consistent with the reference point m_run.
+//
+// Lazy rescaling: a row's reference only moves when its probabilities would
+// grow too large.  The test is on the sum of the lane's eight probabilities,
+// which the step needs anyway: while every lane's sum stays <= 8 * 2^kRescaleSlack
+// (so each probability is bounded), nothing else is computed.  Otherwise (a
+// score more than about kRescaleSlack above the reference, or the row's first
+// keys with m_run = -inf, which gives inf / NaN sums) the wave forms the row
+// maxima, moves the reference of every row whose maximum exceeds it by more
+// than kRescaleSlack, rescales O and l and recomputes the probabilities.
+__device__ __forceinline__ bf16x8_t softmax_step(const float (&z)[8], float scale_log2,
+                                                 float& m_run, float& l_part,
+                                                 f32x4_t (&o)[8]) {
+  constexpr float kLaneSumCap = 8.0f * 256.0f;  // 8 * 2^kRescaleSlack
+  float pz[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) pz[e] = fast_exp2(fmaf(z[e], scale_log2, -m_run));
+  float ls = ((pz[0] + pz[1]) + (pz[2] + pz[3])) + ((pz[4] + pz[5]) + (pz[6] + pz[7]));
+  if (__any(!(ls <= kLaneSumCap))) {
+    const float mx = fmaxf(fmaxf(fmaxf(z[0], z[1]), fmaxf(z[2], z[3])),
+                           fmaxf(fmaxf(z[4], z[5]), fmaxf(z[6], z[7]))) * scale_log2;
+    const float mrow = wave_max_xor_16_32(mx);
+    if (mrow > m_run + kRescaleSlack) {
+      const float alpha = fast_exp2(m_run - mrow);
+      l_part *= alpha;
+#pragma unroll
+      for (int t8 = 0; t8 < 8; ++t8) o[t8] *= alpha;
+      m_run = mrow;
+    }
+#pragma unroll
+    for (int e = 0; e < 8; ++e) pz[e] = fast_exp2(fmaf(z[e], scale_log2, -m_run));
+    ls = ((pz[0] + pz[1]) + (pz[2] + pz[3])) + ((pz[4] + pz[5]) + (pz[6] + pz[7]));
+  }
+  l_part += ls;
+  u32x4_t pw;
+  pw.x = pack_bf16x2(pz[0], pz[1]);
+  pw.y = pack_bf16x2(pz[2], pz[3]);
+  pw.z = pack_bf16x2(pz[4], pz[5]);
+  pw.w = pack_bf16x2(pz[6], pz[7]);
+  return as_bf16x8(pw);
+}
+
 template <int kKv, int kQ>
 __device__ __forceinline__ void attend_page(const PageRegs<kv_kind(kKv)>& r,
                                             const QRegs<kQ>& qf, const LaneRows& lr,
@@ -256,7 +349,7 @@ __device__ __forceinline__ void attend_page(const PageRegs<kv_kind(kKv)>& r,
   for (int tau = 0; tau < 2; ++tau) s[tau] = score_tile<kKv, kQ>(r, qf, tau, lr.ksh);
 
   // Raw scores; keys past the visible count (only on a token's last page)
-  // become -inf.  The positive scale is applied after the max.
+  // become -inf.  The softmax step applies the positive scale.
   float z[8];
 #pragma unroll
   for (int tau = 0; tau < 2; ++tau) {
@@ -272,49 +365,12 @@ __device__ __forceinline__ void attend_page(const PageRegs<kv_kind(kKv)>& r,
       }
     }
   }
-  // Lazy rescaling: the reference point m_run of a row only moves when one of
-  // its scores exceeds it by more than kRescaleSlack (log2 units); then
-  // probabilities stay <= 2^kRescaleSlack, far inside fp32 / bf16 range.  The
-  // test uses each lane's own maximum and one wave vote, so the cross-lane row
-  // maximum is only formed on the (rare) pages that move a reference point;
-  // m_run = -inf (no key yet) always moves.
-  const float mx = fmaxf(fmaxf(fmaxf(z[0], z[1]), fmaxf(z[2], z[3])),
-                         fmaxf(fmaxf(z[4], z[5]), fmaxf(z[6], z[7]))) * scale_log2;
-  if (__any(mx > m_run + kRescaleSlack)) {
-    const float mrow = wave_max_xor_16_32(mx);
-    const float m_new = mrow > m_run + kRescaleSlack ? mrow : m_run;
-    const float alpha = fast_exp2(m_run - m_new);
-    l_part *= alpha;
-#pragma unroll
-    for (int t8 = 0; t8 < 8; ++t8) o[t8] *= alpha;
-    m_run = m_new;
-  }
-  float pz[8];
-#pragma unroll
-  for (int e = 0; e < 8; ++e) pz[e] = fast_exp2(fmaf(z[e], scale_log2, -m_run));
-  l_part += ((pz[0] + pz[1]) + (pz[2] + pz[3])) + ((pz[4] + pz[5]) + (pz[6] + pz[7]));
+  const bf16x8_t pb = softmax_step(z, scale_log2, m_run, l_part, o);
 
-  u32x4_t pw;
-  pw.x = pack_bf16x2(pz[0], pz[1]);
-  pw.y = pack_bf16x2(pz[2], pz[3]);
-  pw.z = pack_bf16x2(pz[4], pz[5]);
-  pw.w = pack_bf16x2(pz[6], pz[7]);
-  const bf16x8_t pb = as_bf16x8(pw);
-
-  // V rows as bf16 pairs along the head dim: vd[j][w] = dims (8n+2w, 8n+2w+1).
-  u32x4_t vd[8];
-  widen_v<kKv>(r, lr.vsh, vd);
+  u32x4_t vt[8];
+  build_vt<kKv>(r, lr.vsh, vt);
 #pragma unroll
-  for (int t8 = 0; t8 < 8; ++t8) {
-    const uint32_t sel = (t8 & 1) ? 0x07060302u : 0x05040100u;
-    const int w = t8 >> 1;
-    u32x4_t a;
-    a.x = byte_perm(vd[1][w], vd[0][w], sel);
-    a.y = byte_perm(vd[3][w], vd[2][w], sel);
-    a.z = byte_perm(vd[5][w], vd[4][w], sel);
-    a.w = byte_perm(vd[7][w], vd[6][w], sel);
-    o[t8] = mfma_bf16_16x16x32(as_bf16x8(a), pb, o[t8]);
-  }
+  for (int t8 = 0; t8 < 8; ++t8) o[t8] = mfma_bf16_16x16x32(as_bf16x8(vt[t8]), pb, o[t8]);
 }
 
 // bf16 store of one output row chunk: acc / L * v_scale, or exact zeros when

@@ -89,27 +89,7 @@ __device__ __forceinline__ void multi_row_page(const PageRegs<kv_kind(kKv)>& r,
         if (kbase + 16 * tau + 4 * g + i >= nvis) z[4 * tau + i] = -INFINITY;
     }
   }
-  const float mx = fmaxf(fmaxf(fmaxf(z[0], z[1]), fmaxf(z[2], z[3])),
-                         fmaxf(fmaxf(z[4], z[5]), fmaxf(z[6], z[7]))) * scale_log2;
-  if (__any(mx > m_run + kRescaleSlack)) {
-    const float mrow = wave_max_xor_16_32(mx);
-    const float m_new = mrow > m_run + kRescaleSlack ? mrow : m_run;
-    const float alpha = fast_exp2(m_run - m_new);
-    l_part *= alpha;
-#pragma unroll
-    for (int t8 = 0; t8 < 8; ++t8) o[t8] *= alpha;
-    m_run = m_new;
-  }
-  float pz[8];
-#pragma unroll
-  for (int e = 0; e < 8; ++e) pz[e] = fast_exp2(fmaf(z[e], scale_log2, -m_run));
-  l_part += ((pz[0] + pz[1]) + (pz[2] + pz[3])) + ((pz[4] + pz[5]) + (pz[6] + pz[7]));
-  u32x4_t pw;
-  pw.x = pack_bf16x2(pz[0], pz[1]);
-  pw.y = pack_bf16x2(pz[2], pz[3]);
-  pw.z = pack_bf16x2(pz[4], pz[5]);
-  pw.w = pack_bf16x2(pz[6], pz[7]);
-  const bf16x8_t pb = as_bf16x8(pw);
+  const bf16x8_t pb = softmax_step(z, scale_log2, m_run, l_part, o);
 #pragma unroll
   for (int t8 = 0; t8 < 8; ++t8) o[t8] = mfma_bf16_16x16x32(as_bf16x8(vt[t8]), pb, o[t8]);
 }
@@ -326,18 +306,8 @@ __global__ __launch_bounds__(kThreads) void multi_kernel(AttendParams p) {
 #pragma unroll
               for (int tau = 0; tau < 2; ++tau) widen_k_tile<kKv>(buf[j], tau, lr.ksh, kf[tau]);
             }
-            u32x4_t vd[8];
-            widen_v<kKv>(buf[j], lr.vsh, vd);
             u32x4_t vt[8];
-#pragma unroll
-            for (int t8 = 0; t8 < 8; ++t8) {
-              const uint32_t sel = (t8 & 1) ? 0x07060302u : 0x05040100u;
-              const int w = t8 >> 1;
-              vt[t8].x = byte_perm(vd[1][w], vd[0][w], sel);
-              vt[t8].y = byte_perm(vd[3][w], vd[2][w], sel);
-              vt[t8].z = byte_perm(vd[5][w], vd[4][w], sel);
-              vt[t8].w = byte_perm(vd[7][w], vd[6][w], sel);
-            }
+            build_vt<kKv>(buf[j], lr.vsh, vt);
 #pragma unroll
             for (int w = 0; w < kM; ++w) {
               const int nv = __builtin_amdgcn_readfirstlane((int)s_unv[li][w]);
