@@ -310,13 +310,16 @@ __global__ __launch_bounds__(kThreads) void attend_kernel(AttendParams p) {
   // visible row, so no load sits on a conditional path before a wait.  Page
   // ids and visible counts are wave-uniform and live in scalar registers.
   if (lo < hi) {
+    // A page's visible count is read with its page id when its loads are
+    // issued and kept in a scalar register until the page is used.
     PageRegs<kKind> buf[kDepth];
+    int bnv[kDepth];
 #pragma unroll
     for (int j = 0; j < kDepth - 1; ++j) {
       const int pi = min(lo + j, hi - 1);
       const int pg = __builtin_amdgcn_readfirstlane(s_page[pi]);
-      const int nv = __builtin_amdgcn_readfirstlane(s_nvis[pi]);
-      load_page<kKind>(buf[j], head_base + (int64_t)pg * p.kv_s0, row_stride, nv - 1, lr);
+      bnv[j] = __builtin_amdgcn_readfirstlane(s_nvis[pi]);
+      load_page<kKind>(buf[j], head_base + (int64_t)pg * p.kv_s0, row_stride, bnv[j] - 1, lr);
     }
     for (int i = lo;; i += kDepth) {
 #pragma unroll
@@ -324,11 +327,12 @@ __global__ __launch_bounds__(kThreads) void attend_kernel(AttendParams p) {
         const int cur = i + j;
         if (cur >= hi) goto pages_done;
         const int pn = min(cur + kDepth - 1, hi - 1);
+        const int nx = (j + kDepth - 1) % kDepth;
         const int pg = __builtin_amdgcn_readfirstlane(s_page[pn]);
-        const int nvn = __builtin_amdgcn_readfirstlane(s_nvis[pn]);
-        load_page<kKind>(buf[(j + kDepth - 1) % kDepth], head_base + (int64_t)pg * p.kv_s0,
-                         row_stride, nvn - 1, lr);
-        const int nv = __builtin_amdgcn_readfirstlane(s_nvis[cur]);
+        bnv[nx] = __builtin_amdgcn_readfirstlane(s_nvis[pn]);
+        load_page<kKind>(buf[nx], head_base + (int64_t)pg * p.kv_s0, row_stride, bnv[nx] - 1,
+                         lr);
+        const int nv = bnv[j];
         if (kbase < nv)
           attend_page<kKv, kQ>(buf[j], qf, lr, kbase, nv, g, p.scale_log2, m_run, l_part, o);
       }

@@ -97,9 +97,10 @@ __device__ __forceinline__ void multi_row_page(const PageRegs<kv_kind(kKv)>& r,
 template <int kKv, int kQ, int kM>
 __global__ __launch_bounds__(kThreads) void multi_kernel(AttendParams p) {
   constexpr int kKind = kv_kind(kKv);
-  __shared__ int32_t s_upage[kMaxUnion];                // page list: physical page or -1
-  __shared__ uint8_t s_unv[kMaxUnion][kMaxTileRows];    // visible rows for each tile row
-  __shared__ uint8_t s_umax[kMaxUnion];                 // largest of those (0: skip)
+  // Page list entry: (physical page, or 0 when no row sees the entry;
+  // byte w = visible rows of the page for tile row w, 0 when it does not see
+  // it).  One 8-byte LDS read per page gives its loads and every row's mask.
+  __shared__ int2 s_list[kMaxUnion];
   __shared__ int32_t s_ent_page[kMaxUnion];
   __shared__ int32_t s_ent_nv[kMaxUnion];
   __shared__ int32_t s_row_r[kMaxTileRows], s_row_pos[kMaxTileRows];
@@ -186,18 +187,16 @@ __global__ __launch_bounds__(kThreads) void multi_kernel(AttendParams p) {
     for (int w2 = 0; w2 < wave; ++w2) base += s_wave_cnt[w2];
     if (first) {
       const int slot = base + __popcll(bal & ((1ull << lane) - 1ull));
-      s_upage[slot] = page;
-      int vmax = 0;
+      uint32_t nv4 = 0;
       for (int w = 0; w < kM; ++w) {
         int v = 0;
         for (int j = 0; j < k; ++j) {
           const int e2 = w * k + j;
           if (s_ent_page[e2] == page) v = max(v, s_ent_nv[e2]);
         }
-        s_unv[slot][w] = (uint8_t)v;
-        vmax = max(vmax, v);
+        nv4 |= (uint32_t)v << (8 * w);
       }
-      s_umax[slot] = (uint8_t)vmax;
+      s_list[slot] = make_int2(page, (int)nv4);
     }
     if (tid == 0) {
       int tot = 0;
@@ -255,51 +254,49 @@ __global__ __launch_bounds__(kThreads) void multi_kernel(AttendParams p) {
       for (int u = c0 + tid; u < c1; u += kThreads) {
         const int raw = dense_row[u];
         const bool ok = raw >= 0 && raw < p.num_kv_blocks;
-        int vmax = 0;
+        uint32_t nv4 = 0;
 #pragma unroll
-        for (int w = 0; w < kMaxTileRows; ++w) {
+        for (int w = 0; w < kM; ++w) {
           int v = 0;
-          if (w < kM && ok && s_row_pos[w] >= 0)
-            v = max(0, min(kPage, s_row_pos[w] - u * kPage + 1));
-          s_unv[u - c0][w] = (uint8_t)v;
-          vmax = max(vmax, v);
+          if (ok && s_row_pos[w] >= 0) v = max(0, min(kPage, s_row_pos[w] - u * kPage + 1));
+          nv4 |= (uint32_t)v << (8 * w);
         }
-        s_upage[u - c0] = ok ? raw : -1;
-        s_umax[u - c0] = (uint8_t)vmax;
+        s_list[u - c0] = make_int2(nv4 != 0 ? raw : 0, (int)nv4);
       }
       __syncthreads();
     }
     const int base = p.tile_dense ? c0 : 0;  // list index of LDS entry 0
-    auto entry = [&](int u, int& pg, int& lim) {
-      const int i = u - base;
-      const int v = s_umax[i];
-      pg = v > 0 ? s_upage[i] : 0;
-      lim = max(v, 1) - 1;
+    // Issues the loads of list entry u into `r` and returns the entry's row
+    // bytes (wave-uniform), kept in scalar registers until the page is used.
+    auto fetch = [&](int u, PageRegs<kKind>& r) -> uint32_t {
+      const int2 e = s_list[u - base];
+      const int pg = __builtin_amdgcn_readfirstlane(e.x);
+      const uint32_t nv4 = (uint32_t)__builtin_amdgcn_readfirstlane(e.y);
+      uint32_t vmax = 0;
+#pragma unroll
+      for (int w = 0; w < kM; ++w) vmax = max(vmax, (nv4 >> (8 * w)) & 0xffu);
+      load_page<kKind>(r, head_base + (int64_t)pg * p.kv_s0, row_stride,
+                       (int)max(vmax, 1u) - 1, lr);
+      return nv4;
     };
 
     PageRegs<kKind> buf[kDepth];
+    uint32_t bnv[kDepth];
 #pragma unroll
-    for (int j = 0; j < kDepth - 1; ++j) {
-      int pg, lim;
-      entry(min(c0 + j, c1 - 1), pg, lim);
-      pg = __builtin_amdgcn_readfirstlane(pg);
-      lim = __builtin_amdgcn_readfirstlane(lim);
-      load_page<kKind>(buf[j], head_base + (int64_t)pg * p.kv_s0, row_stride, lim, lr);
-    }
+    for (int j = 0; j < kDepth - 1; ++j) bnv[j] = fetch(min(c0 + j, c1 - 1), buf[j]);
     for (int i = c0;; i += kDepth) {
 #pragma unroll
       for (int j = 0; j < kDepth; ++j) {
         const int cur = i + j;
         if (cur >= c1) goto chunk_done;
         {
-          int pg, lim;
-          entry(min(cur + kDepth - 1, c1 - 1), pg, lim);
-          pg = __builtin_amdgcn_readfirstlane(pg);
-          lim = __builtin_amdgcn_readfirstlane(lim);
-          load_page<kKind>(buf[(j + kDepth - 1) % kDepth], head_base + (int64_t)pg * p.kv_s0,
-                           row_stride, lim, lr);
-          const int li = cur - base;
-          if (__builtin_amdgcn_readfirstlane((int)s_umax[li]) > kbase) {
+          const int nx = (j + kDepth - 1) % kDepth;
+          bnv[nx] = fetch(min(cur + kDepth - 1, c1 - 1), buf[nx]);
+          const uint32_t nv4 = bnv[j];
+          bool any = false;
+#pragma unroll
+          for (int w = 0; w < kM; ++w) any |= (int)((nv4 >> (8 * w)) & 0xffu) > kbase;
+          if (any) {
             // Widen this wavefront's keys once for all rows of the tile.
             bf16x8_t kf[2][4];
             if constexpr (kQ != kQE4m3) {
@@ -310,7 +307,7 @@ __global__ __launch_bounds__(kThreads) void multi_kernel(AttendParams p) {
             build_vt<kKv>(buf[j], lr.vsh, vt);
 #pragma unroll
             for (int w = 0; w < kM; ++w) {
-              const int nv = __builtin_amdgcn_readfirstlane((int)s_unv[li][w]);
+              const int nv = (int)((nv4 >> (8 * w)) & 0xffu);
               if (nv > kbase)
                 multi_row_page<kKv, kQ>(buf[j], kf, vt, qf[w], lr.ksh, kbase, nv, g,
                                         p.scale_log2, m_run[w], l_part[w], o[w]);
