@@ -101,8 +101,9 @@ __global__ __launch_bounds__(kThreads) void multi_kernel(AttendParams p) {
   // byte w = visible rows of the page for tile row w, 0 when it does not see
   // it).  One 8-byte LDS read per page gives its loads and every row's mask.
   __shared__ int2 s_list[kMaxUnion];
-  __shared__ int32_t s_ent_page[kMaxUnion];
-  __shared__ int32_t s_ent_nv[kMaxUnion];
+  // The rows' selections: entry (row w, slot j) at w * kMaxTopk + j.
+  __shared__ __align__(16) int32_t s_ent_page[kMaxUnion];
+  __shared__ __align__(16) int32_t s_ent_nv[kMaxUnion];
   __shared__ int32_t s_row_r[kMaxTileRows], s_row_pos[kMaxTileRows];
   __shared__ int32_t s_wave_cnt[kWaves];
   __shared__ int32_t s_nlist;
@@ -145,16 +146,18 @@ __global__ __launch_bounds__(kThreads) void multi_kernel(AttendParams p) {
   int npages;
   int dense_r = -1, dense_pos_max = -1;
   if (!p.tile_dense) {
-    // Union of the rows' selections: entry e = (row e / k, slot e % k).
+    // Union of the rows' selections.  Thread (row w, slot j) = (tid / 64,
+    // tid % 64) stages its entry (page -1 for an empty, invalid or padding
+    // slot); row w's slots sit at w * kMaxTopk.
     const int k = p.topk_k;
-    const int e = tid;
+    const int kq = (k + 3) & ~3;  // slots scanned per row (the pad is -1)
     int page = -1, nv = 0;
-    if (e < kM * k) {
-      const int w = e / k;
-      const int j = e - w * k;
+    if (tid < kM * kMaxTopk) {
+      const int w = tid / kMaxTopk;
+      const int j = tid - w * kMaxTopk;
       const int r = s_row_r[w];
       const int pos = s_row_pos[w];
-      if (r >= 0) {
+      if (j < k && r >= 0) {
         const int t = tile_row(p, tile, w, kM);
         const int b = p.topk[t * p.tk_s0 + h * p.tk_s1 + j * p.tk_s2];
         if (b >= 0 && b < p.bt_stride && (int64_t)b * kPage <= pos) {
@@ -165,20 +168,33 @@ __global__ __launch_bounds__(kThreads) void multi_kernel(AttendParams p) {
           }
         }
       }
-      s_ent_page[e] = page;
-      s_ent_nv[e] = nv;
+      s_ent_page[tid] = page;
+      s_ent_nv[tid] = nv;
     }
     __syncthreads();
-    // The first occurrence of a page opens a list slot; slots follow entry
-    // order (a prefix count over the waves).
+    // One pass over every staged entry, four at a time: the first entry (in
+    // (row, slot) order) naming this entry's page, and each row's largest
+    // visible count for that page.  The first occurrence opens a list slot;
+    // slots follow entry order (a prefix count over the waves).
     bool first = false;
-    if (e < kM * k && page >= 0) {
-      first = true;
-      for (int e2 = 0; e2 < e; ++e2)
-        if (s_ent_page[e2] == page) {
-          first = false;
-          break;
+    uint32_t nv4 = 0;
+    if (page >= 0) {
+      int first_e = tid;
+#pragma unroll
+      for (int w = 0; w < kM; ++w) {
+        int v = 0;
+        for (int j = 0; j < kq; j += 4) {
+          const int e2 = w * kMaxTopk + j;
+          const int4 pg4 = *reinterpret_cast<const int4*>(&s_ent_page[e2]);
+          const int4 nv4v = *reinterpret_cast<const int4*>(&s_ent_nv[e2]);
+          if (pg4.x == page) { first_e = min(first_e, e2); v = max(v, nv4v.x); }
+          if (pg4.y == page) { first_e = min(first_e, e2 + 1); v = max(v, nv4v.y); }
+          if (pg4.z == page) { first_e = min(first_e, e2 + 2); v = max(v, nv4v.z); }
+          if (pg4.w == page) { first_e = min(first_e, e2 + 3); v = max(v, nv4v.w); }
         }
+        nv4 |= (uint32_t)v << (8 * w);
+      }
+      first = first_e == tid;
     }
     const uint64_t bal = __ballot(first);
     if (lane == 0) s_wave_cnt[wave] = __popcll(bal);
@@ -187,15 +203,6 @@ __global__ __launch_bounds__(kThreads) void multi_kernel(AttendParams p) {
     for (int w2 = 0; w2 < wave; ++w2) base += s_wave_cnt[w2];
     if (first) {
       const int slot = base + __popcll(bal & ((1ull << lane) - 1ull));
-      uint32_t nv4 = 0;
-      for (int w = 0; w < kM; ++w) {
-        int v = 0;
-        for (int j = 0; j < k; ++j) {
-          const int e2 = w * k + j;
-          if (s_ent_page[e2] == page) v = max(v, s_ent_nv[e2]);
-        }
-        nv4 |= (uint32_t)v << (8 * w);
-      }
       s_list[slot] = make_int2(page, (int)nv4);
     }
     if (tid == 0) {

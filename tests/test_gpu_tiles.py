@@ -2,7 +2,7 @@
 
 The tile kernel (several token rows per workgroup, each page shared by its
 rows read once) must give what the oracle gives for any tile size: the
-randomized decode cases and the format cases are rerun on 4- and 8-row tiles,
+randomized decode cases and the format cases are rerun on 2- and 4-row tiles,
 the single-row kernel is checked on a long decode query length, and dense
 decode (every visible block, no top-k) is checked on the test page's shapes,
 randomized shapes (query lengths 1..8, padding rows, NHD, every split count,
