@@ -12,11 +12,11 @@
 //
 // Work decomposition.  A workgroup takes a tile of kM token rows for one kv
 // head.  As in the single-row attend, wavefront w owns keys [32w, 32w+32) of
-// every page and streams them through the same two-deep register ring; per
-// page it widens its K and V quarter once (the V^T operands once, the K
-// operands once when q is bf16) and then, for each row of the tile that sees
-// the page, runs S^T = K Q^T, the mask, the lazily rescaled online softmax and
-// O^T += V^T P^T with that row's Q^T and state.  The rows' states from the four
+// every page and streams them through the same two-deep register ring.  Per
+// page it widens its K quarter once (when q is bf16) and runs, for each row
+// of the tile that sees the page, S^T = K Q^T, the mask and the lazily
+// rescaled online softmax; it then builds its V^T operands once and runs
+// O^T += V^T P^T for those rows.  The rows' states from the four
 // wavefronts are merged through LDS at the end, row by row.
 // The tile's page list is
 //  * sparse: the union of the rows' top-k selections, keyed by physical page
@@ -53,13 +53,13 @@ __device__ __forceinline__ int tile_row(const AttendParams& p, int tile, int w, 
   return tile * kM + w;
 }
 
-// One page for one row of the tile, from operands already widened: S^T, the
-// row's mask, the online softmax and P V (the single-row attend_page with the
-// K operands and V^T tiles hoisted out of the per-row work).
+// The first half of one page for one row of the tile: S^T from the widened
+// K operands (or the K codes, fp8 q), the row's mask and the online softmax
+// step; returns the row's P^T operand.  The P V half runs after every row's
+// first half, so the widened K and the V^T operands are never live together.
 template <int kKv, int kQ>
-__device__ __forceinline__ void multi_row_page(const PageRegs<kv_kind(kKv)>& r,
-                                               const bf16x8_t (&kf)[2][4],
-                                               const u32x4_t (&vt)[8], const QRegs<kQ>& q,
+__device__ __forceinline__ bf16x8_t row_scores(const PageRegs<kv_kind(kKv)>& r,
+                                               const bf16x8_t (&kf)[2][4], const QRegs<kQ>& q,
                                                uint32_t ksh, int kbase, int nvis, int g,
                                                float scale_log2, float& m_run, float& l_part,
                                                f32x4_t (&o)[8]) {
@@ -89,9 +89,7 @@ __device__ __forceinline__ void multi_row_page(const PageRegs<kv_kind(kKv)>& r,
         if (kbase + 16 * tau + 4 * g + i >= nvis) z[4 * tau + i] = -INFINITY;
     }
   }
-  const bf16x8_t pb = softmax_step(z, scale_log2, m_run, l_part, o);
-#pragma unroll
-  for (int t8 = 0; t8 < 8; ++t8) o[t8] = mfma_bf16_16x16x32(as_bf16x8(vt[t8]), pb, o[t8]);
+  return softmax_step(z, scale_log2, m_run, l_part, o);
 }
 
 template <int kKv, int kQ, int kM>
@@ -304,20 +302,34 @@ __global__ __launch_bounds__(kThreads) void multi_kernel(AttendParams p) {
 #pragma unroll
           for (int w = 0; w < kM; ++w) any |= (int)((nv4 >> (8 * w)) & 0xffu) > kbase;
           if (any) {
-            // Widen this wavefront's keys once for all rows of the tile.
-            bf16x8_t kf[2][4];
-            if constexpr (kQ != kQE4m3) {
+            // This wavefront's keys are widened once for all rows of the
+            // tile: K first, for every row's S^T and softmax; then V, for
+            // every row's P V.
+            bf16x8_t pb[kM];
+            {
+              bf16x8_t kf[2][4];
+              if constexpr (kQ != kQE4m3) {
 #pragma unroll
-              for (int tau = 0; tau < 2; ++tau) widen_k_tile<kKv>(buf[j], tau, lr.ksh, kf[tau]);
+                for (int tau = 0; tau < 2; ++tau)
+                  widen_k_tile<kKv>(buf[j], tau, lr.ksh, kf[tau]);
+              }
+#pragma unroll
+              for (int w = 0; w < kM; ++w) {
+                const int nv = (int)((nv4 >> (8 * w)) & 0xffu);
+                if (nv > kbase)
+                  pb[w] = row_scores<kKv, kQ>(buf[j], kf, qf[w], lr.ksh, kbase, nv, g,
+                                              p.scale_log2, m_run[w], l_part[w], o[w]);
+              }
             }
             u32x4_t vt[8];
             build_vt<kKv>(buf[j], lr.vsh, vt);
 #pragma unroll
             for (int w = 0; w < kM; ++w) {
-              const int nv = (int)((nv4 >> (8 * w)) & 0xffu);
-              if (nv > kbase)
-                multi_row_page<kKv, kQ>(buf[j], kf, vt, qf[w], lr.ksh, kbase, nv, g,
-                                        p.scale_log2, m_run[w], l_part[w], o[w]);
+              if ((int)((nv4 >> (8 * w)) & 0xffu) > kbase) {
+#pragma unroll
+                for (int t8 = 0; t8 < 8; ++t8)
+                  o[w][t8] = mfma_bf16_16x16x32(as_bf16x8(vt[t8]), pb[w], o[w][t8]);
+              }
             }
           }
         }
