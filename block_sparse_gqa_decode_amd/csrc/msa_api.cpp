@@ -21,7 +21,7 @@ struct msa_plan_s {
   msa_decode_shape shape;   // for a prefill plan: decode_query_len = 0
   bool prefill;
   bool dense;               // every visible block (topk_blocks == 0)
-  int32_t tile_rows;        // 1: one row per workgroup; 4 / 8: multi-row tiles
+  int32_t tile_rows;        // 1: one row per workgroup; 2 / 4: multi-row tiles
   int32_t num_units;        // workgroups per split
   int device;
   int32_t splits;
@@ -152,8 +152,9 @@ msa_status check_kv(const void* kv_cache, const int64_t kv_strides[4], int64_t n
       return fail(MSA_ERR_INVALID_ARG, "kv_cache stride %d (%lld elements) is not a multiple "
                   "of 16 bytes", d, (long long)kv_strides[d]);
   }
-  if (kv_strides[2] * eb > (1 << 24))
-    return fail(MSA_ERR_UNSUPPORTED, "kv_cache row stride above 16 MiB");
+  // The kernels form row offsets with 24-bit multiplies.
+  if (kv_strides[2] * eb >= (1 << 24))
+    return fail(MSA_ERR_UNSUPPORTED, "kv_cache row stride must be below 16 MiB");
   if (kv_strides[2] < 2 * msa::kHeadDim)
     return fail(MSA_ERR_INVALID_ARG, "kv_cache row stride %lld is shorter than a packed K|V "
                 "row (256 elements)", (long long)kv_strides[2]);

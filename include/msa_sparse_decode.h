@@ -186,7 +186,9 @@ msa_status msa_sparse_decode_plan_info(msa_plan plan, int32_t* num_splits,
  *                codes when the plan's q_dtype is MSA_Q_FP8_E4M3.
  *   kv_cache     packed K|V entries, logical [num_kv_blocks, Hkv, 128, 256]
  *                with strides kv_strides (elements); kv_strides[3] must be 1
- *                and the other strides must be positive multiples of 16 bytes.
+ *                and the other strides must be positive multiples of 16 bytes;
+ *                the row stride kv_strides[2] must be >= 256 elements and
+ *                below 16 MiB (MSA_ERR_UNSUPPORTED above).
  *                HND (vLLM's default) is {Hkv*128*256, 128*256, 256, 1}.
  *                An MSA_KV_MXFP4 cache is 4-bit head slots instead, with the
  *                byte strides described at msa_kv_dtype.

@@ -236,6 +236,26 @@ def test_bf16_strides_are_checked_in_bytes(lib):
         lib.msa_sparse_decode_plan_destroy(h)
 
 
+@pytest.mark.parametrize("row_elems,ok", [((1 << 24) - 16, True), (1 << 24, False)])
+def test_row_stride_limit_fits_24_bit_offsets(lib, row_elems, ok):
+    """The kernels form page-row offsets with 24-bit multiplies, so an fp8 row
+    stride of 2^24 bytes (whose low 24 bits are zero) must be rejected, and
+    one 16 bytes shorter accepted.  The plan names a device index no machine
+    has (a one-split plan makes no HIP call), so an accepted run stops at
+    selecting that device, past every argument check, and nothing launches."""
+    h = ctypes.c_void_p()
+    s = shape()
+    assert lib.msa_sparse_decode_plan(ctypes.byref(s), 4096, ctypes.byref(h)) == 0
+    try:
+        st, msg = _run(lib, h, kvs=(row_elems * 128, row_elems * 128, row_elems, 1))
+        if ok:
+            assert st == msa.MSA_ERR_DEVICE, (st, msg)
+        else:
+            assert st == msa.MSA_ERR_UNSUPPORTED and "16 MiB" in msg, (st, msg)
+    finally:
+        lib.msa_sparse_decode_plan_destroy(h)
+
+
 MXFP4_SLOT = 128 * (64 + 4)
 
 
