@@ -108,6 +108,15 @@ __global__ __launch_bounds__(kThreads) void multi_kernel(AttendParams p) {
   __shared__ float s_m[kWaves][16];
   __shared__ float s_l[kWaves][16];
   __shared__ float s_o[kWaves][16][kHeadDim + kOPad];
+  // 2-row tiles read q per row and page from LDS ([row][q head][bytes], each
+  // head's row padded by 16 bytes so the 16 heads' 16-byte operand reads fall
+  // in different banks), so q holds no registers across the page loop: pf1
+  // 652 -> 637 us.  4-row tiles keep q in registers (reading it from LDS made
+  // d1 6% slower).
+  constexpr bool kQInLds = kM == 2;
+  constexpr int kQBytes = kHeadDim * (kQ == kQE4m3 ? 1 : 2);
+  constexpr int kQStride = kQBytes + 16;
+  __shared__ __align__(16) uint8_t s_q[kQInLds ? kM : 1][16][kQStride];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -140,6 +149,20 @@ __global__ __launch_bounds__(kThreads) void multi_kernel(AttendParams p) {
     s_row_pos[tid] = pos;
   }
   __syncthreads();
+  // Stage q (zeros for dead rows and q heads >= G); the barriers of the page
+  // list staging below order these writes before the first read.
+  for (int c = tid; kQInLds && c < kM * 16 * (kQBytes / 16); c += kThreads) {
+    const int w = c / (16 * (kQBytes / 16));
+    const int rem = c - w * (16 * (kQBytes / 16));
+    const int qh = rem / (kQBytes / 16);
+    const int off = (rem - qh * (kQBytes / 16)) * 16;
+    u32x4_t v = u32x4_t{0u, 0u, 0u, 0u};
+    if (s_row_r[w] >= 0 && qh < p.group) {
+      const int64_t q_row = (int64_t)tile_row(p, tile, w, kM) * p.hq + head0 + qh;
+      v = *reinterpret_cast<const u32x4_t*>(p.q + q_row * kQBytes + off);
+    }
+    *reinterpret_cast<u32x4_t*>(&s_q[kQInLds ? w : 0][qh][off]) = v;
+  }
 
   int npages;
   int dense_r = -1, dense_pos_max = -1;
@@ -224,13 +247,17 @@ __global__ __launch_bounds__(kThreads) void multi_kernel(AttendParams p) {
   const int hi = (int)((int64_t)npages * (split + 1) / p.splits);
 
   // Q^T of every row of the tile (zeros for dead rows and q rows >= G).
-  QRegs<kQ> qf[kM];
+
+  // 4-row tiles: Q^T of every row in registers (zeros for dead rows and q
+  // rows >= G).
+  QRegs<kQ> qf[kQInLds ? 1 : kM];
+  if constexpr (!kQInLds) {
 #pragma unroll
-  for (int w = 0; w < kM; ++w) {
-    const bool load = s_row_r[w] >= 0 && n < p.group;
-    const int64_t q_row = (int64_t)(load ? tile_row(p, tile, w, kM) : 0) * p.hq + head0 + n;
-    load_q_operand<kKind, kQ>(qf[w], p.q + q_row * kHeadDim * (kQ == kQE4m3 ? 1 : 2), load,
-                              g);
+    for (int w = 0; w < kM; ++w) {
+      const bool load = s_row_r[w] >= 0 && n < p.group;
+      const int64_t q_row = (int64_t)(load ? tile_row(p, tile, w, kM) : 0) * p.hq + head0 + n;
+      load_q_operand<kKind, kQ>(qf[w], p.q + q_row * kQBytes, load, g);
+    }
   }
 
   float m_run[kM], l_part[kM];
@@ -316,9 +343,17 @@ __global__ __launch_bounds__(kThreads) void multi_kernel(AttendParams p) {
 #pragma unroll
               for (int w = 0; w < kM; ++w) {
                 const int nv = (int)((nv4 >> (8 * w)) & 0xffu);
-                if (nv > kbase)
-                  pb[w] = row_scores<kKv, kQ>(buf[j], kf, qf[w], lr.ksh, kbase, nv, g,
-                                              p.scale_log2, m_run[w], l_part[w], o[w]);
+                if (nv > kbase) {
+                  if constexpr (kQInLds) {
+                    QRegs<kQ> qw;
+                    load_q_operand<kKind, kQ>(qw, &s_q[w][n][0], true, g);
+                    pb[w] = row_scores<kKv, kQ>(buf[j], kf, qw, lr.ksh, kbase, nv, g,
+                                                p.scale_log2, m_run[w], l_part[w], o[w]);
+                  } else {
+                    pb[w] = row_scores<kKv, kQ>(buf[j], kf, qf[w], lr.ksh, kbase, nv, g,
+                                                p.scale_log2, m_run[w], l_part[w], o[w]);
+                  }
+                }
               }
             }
             u32x4_t vt[8];
