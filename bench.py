@@ -63,6 +63,12 @@ KERNEL_SOURCES = {
               "block_sparse_gqa_decode_amd/csrc/msa_page.h",
               "block_sparse_gqa_decode_amd/csrc/msa_device.h",
               "block_sparse_gqa_decode_amd/csrc/msa_internal.h"),
+    # the multi-row tile kernel (c4, pf1, d1 plans)
+    "tile": ("block_sparse_gqa_decode_amd/csrc/msa_tile.hip",
+             "block_sparse_gqa_decode_amd/csrc/msa_page.h",
+             "block_sparse_gqa_decode_amd/csrc/msa_rows.h",
+             "block_sparse_gqa_decode_amd/csrc/msa_device.h",
+             "block_sparse_gqa_decode_amd/csrc/msa_internal.h"),
 }
 
 CONFIG_TEXT = {
@@ -924,6 +930,7 @@ def main():
         "cpu_baseline_all_cores": cpu_pool,
         "other_configs": others,
         "kernel_source_sha": src_hash,
+        "tile_kernel_source_sha": kernel_source_hash("tile"),
     }
     print(json.dumps(line), flush=True)
 
