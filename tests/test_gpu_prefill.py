@@ -3,7 +3,7 @@
 Shapes: the test page's prefill test (q_lens 300/128/77 over seq_lens
 300/640/1100, every causally visible page selected, bf16 q and an fp8 q with
 q_scale 0.5), chunked prefill over long contexts with an empty request and
-padding rows, a graph replayed with new chunk boundaries, and the chunked
+padding rows, 63 / 64 / 70 short requests, a graph replayed with new chunk boundaries, and the chunked
 prefill workload at full size on sampled rows.  Tolerance as for decode.
 """
 import numpy as np
@@ -46,6 +46,27 @@ def test_prefill_chunks_over_context_with_empty_request_and_padding(kvd, tile_ro
     torch.cuda.synchronize()
     got = to_f64(d.out)
     assert_parity(got, oracle_prefill(case), what=f"chunked prefill {kvd}")
+    assert np.all(got[case.real_rows:] == 0.0)
+
+
+@pytest.mark.parametrize("num_prefills", [63, 64, 70])
+@pytest.mark.parametrize("tile_rows", [1, 2])
+def test_prefill_many_requests(num_prefills, tile_rows):
+    """The row -> request binary search over many requests (63, 64, 70):
+    chunks of 0..4 rows (some requests empty) over contexts of up to 600
+    tokens, plus padding rows, on single-row and 2-row tiles."""
+    _banner(f"prefill {num_prefills} requests tile_rows={tile_rows}")
+    rng = np.random.default_rng(44 + num_prefills)
+    q_lens = rng.integers(0, 5, size=num_prefills)
+    seq = q_lens + rng.integers(0, 600, size=num_prefills)
+    seq = np.maximum(seq, 1)
+    case = gen.make_prefill_case(45 + num_prefills, q_lens.tolist(), seq.tolist(), 16, 1,
+                                 rule="zipf", pad_rows=3)
+    d = PrefillDevCase(case)
+    d.run(d.plan(tile_rows=tile_rows))
+    torch.cuda.synchronize()
+    got = to_f64(d.out)
+    assert_parity(got, oracle_prefill(case), what=f"{num_prefills} prefills")
     assert np.all(got[case.real_rows:] == 0.0)
 
 
