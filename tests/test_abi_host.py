@@ -551,3 +551,22 @@ def test_xcd_deal_visits_every_unit_once(tmp_path):
                    check=True, capture_output=True, timeout=300)
     out = subprocess.run([str(exe)], check=True, capture_output=True, text=True, timeout=300)
     assert out.stdout.strip() == "ok"
+
+
+def test_c_consumer_links_and_reports_misuse():
+    """The plain C consumer of the ABI (tests/host/c_abi_decode.c, built by
+    build()) links against the library, checks msa_abi_version and sees a
+    decode_query_len of 33 rejected with a message, all before touching a
+    device.  Without a GPU it then stops at its first hipMalloc (exit 2); on a
+    GPU machine the GPU test runs it to the end."""
+    import subprocess
+
+    from block_sparse_gqa_decode_amd import build_lib
+
+    exe = build_lib.C_CONSUMER_BIN
+    if not os.path.exists(exe):
+        build_lib.build_c_consumer()
+    env = dict(os.environ, HIP_VISIBLE_DEVICES="-1")
+    res = subprocess.run([exe], capture_output=True, text=True, timeout=120, env=env)
+    assert res.returncode == 2, (res.returncode, res.stdout, res.stderr)
+    assert "hipMalloc" in res.stderr and "not rejected" not in res.stderr, res.stderr
