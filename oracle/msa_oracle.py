@@ -41,7 +41,12 @@ design notes):
    ``0..pos`` (``_make_topk``: ``visible_tokens = seq_len - query_len +
    local_query + 1``).
 3. A negative index, or a block that starts after ``pos``, contributes nothing
-   and its block-table entry is not read.
+   and its block-table entry is not read.  So does a block id at or beyond
+   the block-table row, or a block whose table entry is not a page of the
+   pool (outside ``[0, num_blocks)``); the scorer leaves such a block at
+   ``-inf``.  The pages do not say what a bad table entry means; this is the
+   library boundary's rule for data-dependent inputs, which never index out
+   of the pool.
 4. A row with no visible key (all -1, or a padding row ``t >= batch*dql``)
    outputs exact zeros (PR #17171, flash-decoding commit: zeroed, not NaN,
    output for padding rows).
@@ -287,7 +292,11 @@ def gather_live(kv, kv_dtype, k_scale, v_scale, block_table_row, pos, head,
         if check_distinct:
             assert b not in seen, f"duplicate block index {b}"
             seen.add(b)
+        if b >= len(block_table_row):
+            continue
         p = int(block_table_row[b])
+        if p < 0 or p >= kv.shape[0]:
+            continue
         k, v = page_kv(kv, kv_dtype, k_scale, v_scale, p, head, n)
         ks.append(k)
         vs.append(v)
@@ -452,7 +461,9 @@ def block_max_scores(q_bits, kv, kv_dtype, k_scale, block_table, seq_lens,
                 n = visible_rows(pos, b)
                 if n <= 0:
                     continue
-                p = int(block_table[r, b])
+                p = int(block_table[r, b]) if b < block_table.shape[1] else -1
+                if p < 0 or p >= kv.shape[0]:
+                    continue                                     # stays -inf
                 k, _ = page_kv(kv, kv_dtype, k_scale, 1.0, p, h, n)  # [n, D]
                 score[h, b, i] = np.max(qs @ k.T)
     return score

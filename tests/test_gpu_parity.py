@@ -18,7 +18,7 @@ import block_sparse_gqa_decode_amd as msa
 from oracle import msa_oracle as om
 from workloads import gen
 
-from gpu_helpers import DevCase, assert_parity, oracle_attend, oracle_scores, to_f64
+from gpu_helpers import DevCase, assert_parity, oracle_attend, oracle_dense, oracle_scores, to_f64
 
 pytestmark = pytest.mark.gpu
 
@@ -222,6 +222,38 @@ def test_invisible_indices_and_out_of_range_blocks_are_skipped():
     d.run(d.plan(), topk=torch.from_numpy(topk).cuda())
     torch.cuda.synchronize()
     assert_parity(to_f64(d.out), oracle_attend(case_ref), what="skipped indices")
+
+
+def test_out_of_pool_table_entries_are_skipped():
+    """Block-table entries that name no page of the pool (-1, num_blocks,
+    num_blocks + 1000) for about a third of each request's used blocks: the
+    attend skips those blocks (single-row with and without the in-kernel
+    merge, 2-row tiles, dense decode on 4-row tiles) and the scorer leaves
+    them at -inf, as the oracle does on the same table."""
+    _banner("out-of-pool block-table entries")
+    case = gen.make_random_case(114, 3, 4, 32, 2, 12, 300, 3000, pad_rows=2)
+    rng = np.random.default_rng(9)
+    nb = case.kv.shape[0]
+    bt = case.block_table.copy()
+    for r, s in enumerate(case.seq_lens):
+        used = gen.pages_for(int(s))
+        for b in rng.choice(used, size=max(1, used // 3), replace=False):
+            bt[r, b] = rng.choice([-1, nb, nb + 1000])
+    case.block_table = bt
+    d = DevCase(case)
+    ref = oracle_attend(case)
+    for splits, tile_rows in ((1, 1), (2, 1), (8, 1), (0, 2)):
+        d.out.fill_(float("nan"))
+        d.run(d.plan(splits, tile_rows=tile_rows))
+        torch.cuda.synchronize()
+        assert_parity(to_f64(d.out), ref, what=f"out-of-pool splits={splits} tiles={tile_rows}")
+    d.out.fill_(float("nan"))
+    d.run(d.plan(0, tile_rows=4, dense=True))
+    torch.cuda.synchronize()
+    assert_parity(to_f64(d.out), oracle_dense(case), what="out-of-pool dense")
+    mb = case.max_blocks
+    score, _ = _run_scorer(d, mb, 12)
+    _scores_close(score[:, :, :case.real_rows], oracle_scores(case, mb), case)
 
 
 FORMAT_RANDOM_CASES = [

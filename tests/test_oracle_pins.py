@@ -411,6 +411,54 @@ def test_invisible_indices_change_nothing():
     assert np.array_equal(a, b)
 
 
+def _bad_table(case, seed):
+    """The block table with about a third of each request's used entries
+    naming no page of the pool (-1, num_blocks, num_blocks + 1000); returns
+    it with the (request, block) pairs it spoiled."""
+    rng = np.random.default_rng(seed)
+    bt = case.block_table.copy()
+    nb = case.kv.shape[0]
+    spoiled = set()
+    for r, s in enumerate(case.seq_lens):
+        used = gen.pages_for(int(s))
+        for b in rng.choice(used, size=max(1, used // 3), replace=False):
+            bt[r, b] = rng.choice([-1, nb, nb + 1000])
+            spoiled.add((r, int(b)))
+    return bt, spoiled
+
+
+def test_out_of_pool_table_entries_change_nothing_but_their_block():
+    """A selected block whose table entry is no page of the pool contributes
+    nothing: the same as a -1 in its place."""
+    case = _rand_case(dql=2)
+    bt, spoiled = _bad_table(case, 5)
+    masked = case.topk.copy()
+    for t in range(case.real_rows):
+        r = t // case.dql
+        for h in range(masked.shape[1]):
+            for j in range(masked.shape[2]):
+                if (r, int(masked[t, h, j])) in spoiled:
+                    masked[t, h, j] = -1
+    assert (masked != case.topk).any()
+    a = run_oracle(case, block_table=bt)
+    b = run_oracle(case, topk=masked)
+    assert np.array_equal(a, b)
+
+
+def test_scorer_out_of_pool_table_entries_score_minus_inf():
+    case = _rand_case(dql=2)
+    bt, spoiled = _bad_table(case, 6)
+    good = run_scores(case)
+    bad = run_scores(case, block_table=bt)
+    for i in range(case.real_rows):
+        r = i // case.dql
+        for b in range(good.shape[1]):
+            if (r, b) in spoiled:
+                assert np.all(bad[:, b, i] == -np.inf)
+            else:
+                assert np.array_equal(bad[:, b, i], good[:, b, i])
+
+
 def test_all_minus_one_and_padding_rows_are_zero():
     case = _rand_case(pad_rows=3)
     topk = case.topk.copy()
