@@ -150,14 +150,14 @@ __device__ __forceinline__ void combine_splits(__amdgpu_buffer_rsrc_t ro,
   float acc[8];
 #pragma unroll
   for (int k = 0; k < 8; ++k) acc[k] = 0.f;
-  if (M != -INFINITY) {
+  // Unconditional (an empty split weighs 0, see merge_fixed), so the O and
+  // (m, l) read-backs go out together: one memory round trip, not two.
 #pragma unroll
-    for (int s = 0; s < kS; ++s) {
-      const float e = m_l[s].x == -INFINITY ? 0.f : fast_exp2(m_l[s].x - M);
-      L += e * m_l[s].y;
-      acc[0] += e * a[s].x; acc[1] += e * a[s].y; acc[2] += e * a[s].z; acc[3] += e * a[s].w;
-      acc[4] += e * b[s].x; acc[5] += e * b[s].y; acc[6] += e * b[s].z; acc[7] += e * b[s].w;
-    }
+  for (int s = 0; s < kS; ++s) {
+    const float e = m_l[s].x == -INFINITY ? 0.f : fast_exp2(m_l[s].x - M);
+    L += e * m_l[s].y;
+    acc[0] += e * a[s].x; acc[1] += e * a[s].y; acc[2] += e * a[s].z; acc[3] += e * a[s].w;
+    acc[4] += e * b[s].x; acc[5] += e * b[s].y; acc[6] += e * b[s].z; acc[7] += e * b[s].w;
   }
   store_row(dst, acc, L, v_scale);
 }
@@ -425,20 +425,20 @@ __device__ __forceinline__ void merge_fixed(const AttendParams& p, int64_t row, 
   float acc[8];
 #pragma unroll
   for (int k = 0; k < 8; ++k) acc[k] = 0.f;
-  if (M != -INFINITY) {
+  // Unconditional, so every partial load is issued before the first use: a
+  // split with no key has max -inf, sum 0 and zero O, so weight 0, and a row
+  // whose splits all saw nothing sums to L = 0 (stored as zeros).
 #pragma unroll
-    for (int s = 0; s < kS; ++s) {
-      // A split with no key has max -inf, sum 0 and zero O: weight 0.
-      const float e = m_l[s].x == -INFINITY ? 0.f : fast_exp2(m_l[s].x - M);
-      L += e * m_l[s].y;
-      acc[0] += e * a[s].x; acc[1] += e * a[s].y; acc[2] += e * a[s].z; acc[3] += e * a[s].w;
-      acc[4] += e * b[s].x; acc[5] += e * b[s].y; acc[6] += e * b[s].z; acc[7] += e * b[s].w;
-    }
+  for (int s = 0; s < kS; ++s) {
+    const float e = m_l[s].x == -INFINITY ? 0.f : fast_exp2(m_l[s].x - M);
+    L += e * m_l[s].y;
+    acc[0] += e * a[s].x; acc[1] += e * a[s].y; acc[2] += e * a[s].z; acc[3] += e * a[s].w;
+    acc[4] += e * b[s].x; acc[5] += e * b[s].y; acc[6] += e * b[s].z; acc[7] += e * b[s].w;
   }
   store_row(p.out + row * kHeadDim + d0, acc, L, p.v_scale);
 }
 
-__global__ __launch_bounds__(256) void merge_kernel(AttendParams p) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 2))) void merge_kernel(AttendParams p) {
   const int units = p.num_rows * p.hkv;
   const int unit = xcd_unit(units, p.hkv, (int)(blockIdx.x % kXcdSlots),
                             (int)(blockIdx.x / kXcdSlots));
@@ -455,6 +455,7 @@ __global__ __launch_bounds__(256) void merge_kernel(AttendParams p) {
     case 3: merge_fixed<3>(p, row, d0); break;
     case 4: merge_fixed<4>(p, row, d0); break;
     case 8: merge_fixed<8>(p, row, d0); break;
+    case 16: merge_fixed<16>(p, row, d0); break;
     default: merge_splits(p, row, d0); break;
   }
 }

@@ -375,16 +375,21 @@ __device__ __forceinline__ void attend_page(const PageRegs<kv_kind(kKv)>& r,
 
 // bf16 store of one output row chunk: acc / L * v_scale, or exact zeros when
 // the row saw no key (L == 0).
+// Branch-free (selects, not a branch), so a caller's loads that feed acc are
+// not sunk behind the test of L and stay issued together.
 __device__ __forceinline__ void store_row(uint16_t* dst, const float (&acc)[8], float L,
                                           float v_scale) {
-  u32x4_t ov = u32x4_t{0u, 0u, 0u, 0u};
-  if (L > 0.f) {
-    const float inv = v_scale / L;
-    ov.x = pack_bf16x2(acc[0] * inv, acc[1] * inv);
-    ov.y = pack_bf16x2(acc[2] * inv, acc[3] * inv);
-    ov.z = pack_bf16x2(acc[4] * inv, acc[5] * inv);
-    ov.w = pack_bf16x2(acc[6] * inv, acc[7] * inv);
-  }
+  const bool live = L > 0.f;
+  const float inv = live ? v_scale / L : 0.f;
+  u32x4_t ov;
+  ov.x = pack_bf16x2(acc[0] * inv, acc[1] * inv);
+  ov.y = pack_bf16x2(acc[2] * inv, acc[3] * inv);
+  ov.z = pack_bf16x2(acc[4] * inv, acc[5] * inv);
+  ov.w = pack_bf16x2(acc[6] * inv, acc[7] * inv);
+  ov.x = live ? ov.x : 0u;
+  ov.y = live ? ov.y : 0u;
+  ov.z = live ? ov.z : 0u;
+  ov.w = live ? ov.w : 0u;
   *reinterpret_cast<u32x4_t*>(dst) = ov;
 }
 
