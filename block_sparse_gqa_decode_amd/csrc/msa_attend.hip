@@ -438,6 +438,8 @@ __device__ __forceinline__ void merge_fixed(const AttendParams& p, int64_t row, 
   store_row(p.out + row * kHeadDim + d0, acc, L, p.v_scale);
 }
 
+// At most two wavefronts per SIMD asked of the compiler, so a 16-split row keeps
+// all its partial loads in flight (150 VGPRs) instead of batching them.
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 2))) void merge_kernel(AttendParams p) {
   const int units = p.num_rows * p.hkv;
   const int unit = xcd_unit(units, p.hkv, (int)(blockIdx.x % kXcdSlots),
