@@ -604,6 +604,51 @@ def _oracle_row(case, t: int):
                             q_scale=case.q_scale)
 
 
+def _oracle_full_step_row(case, t: int):
+    """The oracle's full decode step for one token row: its block-max scores,
+    their top-k, and the attend over that selection (all kv heads)."""
+    import numpy as np
+
+    from oracle import msa_oracle as om
+
+    score = om.block_max_scores(case.q, case.kv, case.kv_dtype, case.k_scale, case.block_table,
+                                case.seq_lens, case.dql, case.num_kv_heads, case.max_blocks,
+                                rows=[t], q_dtype=case.q_dtype, q_scale=case.q_scale)
+    topk = np.full((case.num_token_rows, case.num_kv_heads, case.topk_k), -1, dtype=np.int32)
+    topk[t] = om.select_topk(score, case.topk_k)[0]
+    return om.sparse_decode(case.q, case.kv, case.kv_dtype, case.k_scale, case.v_scale,
+                            case.block_table, case.seq_lens, topk, case.dql, case.num_kv_heads,
+                            case.sm_scale, rows=[t], q_dtype=case.q_dtype, q_scale=case.q_scale)
+
+
+def oracle_full_step_rate(case, seconds: float):
+    """Token rows per second of the oracle's full step (score -> top-k ->
+    attend), one BLAS thread, over rows in a seeded order for about
+    `seconds`; returns (rows done, rows per second)."""
+    import numpy as np
+
+    try:
+        from threadpoolctl import threadpool_limits
+    except ImportError:  # pragma: no cover
+        threadpool_limits = None
+    ctx = threadpool_limits(limits=1) if threadpool_limits else None
+    if ctx is not None:
+        ctx.__enter__()
+    order = np.random.default_rng(0).permutation(case.real_rows)
+    done = 0
+    t0 = time.perf_counter()
+    try:
+        for t in order:
+            _oracle_full_step_row(case, int(t))
+            done += 1
+            if time.perf_counter() - t0 >= seconds:
+                break
+    finally:
+        if ctx is not None:
+            ctx.__exit__(None, None, None)
+    return done, done / (time.perf_counter() - t0)
+
+
 def _oracle_rows_for(case, order, seconds: float) -> int:
     """Rows of `order` (cycled) through the oracle for about `seconds`, with
     BLAS limited to one thread; returns the count done."""
@@ -862,6 +907,14 @@ def main():
                             for k, v in r2.items()}
         r5 = time_full_step(FULL_STEP_CONFIG, max(32, args.steps // 8), args.warmup,
                             args.replicas, dev)
+        if not args.no_cpu_baseline:
+            from workloads import gen
+
+            n5, rate5 = oracle_full_step_rate(gen.make_config(FULL_STEP_CONFIG), 3.0)
+            r5["oracle_tokens_per_s_1thread"] = rate5
+            r5["oracle_sample"] = (f"{n5} token rows through the oracle's score -> top-16 -> "
+                                   "attend, one thread")
+            r5["gpu_over_oracle"] = r5["tokens_per_s"] / rate5
         others[FULL_STEP_CONFIG] = {k: (round(v, 4) if isinstance(v, float) else v)
                                     for k, v in r5.items()}
     src_hash = kernel_source_hash()
