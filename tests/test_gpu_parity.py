@@ -598,6 +598,65 @@ def test_fused_merge_counters_return_to_zero():
             assert_parity(to_f64(eager), refs[(rep + 1) % 2], what=f"eager between {rep}")
 
 
+def test_indexer_step_graph_replays():
+    """The indexer step (block-max scores, top-k) and the attend over its
+    selection captured in one graph, replayed with q changed in place and an
+    eager step between replays; every replay's scores, selections and output
+    are checked (scores against the oracle, selections on rows with a clear
+    score gap, the output against the oracle fed the GPU's selection)."""
+    _banner("indexer step in a graph: replays")
+    case = gen.make_random_case(118, 4, 1, 32, 2, 16, 3000, 20000)
+    qs = [case.q, gen.make_q(np.random.default_rng(8), case.num_token_rows, case.num_q_heads)]
+    q_dev = [torch.from_numpy(q.view(np.int16)).view(torch.bfloat16).cuda() for q in qs]
+    d = DevCase(case)
+    mb = case.max_blocks
+    rows = case.num_token_rows
+    score = torch.full((case.num_kv_heads, mb, rows), float("nan"), device="cuda")
+    sel = torch.full((rows, case.num_kv_heads, 16), -7, dtype=torch.int32, device="cuda")
+    plan = d.plan()
+
+    def step(out):
+        d.score(score, sel, mb, num_token_rows=rows)
+        d.run(plan, topk=sel, out=out)
+
+    def check(out, qi, what):
+        c = gen.make_random_case(118, 4, 1, 32, 2, 16, 3000, 20000)
+        c.q = qs[qi]
+        ref_scores = oracle_scores(c, mb)
+        got_scores = score.cpu().numpy().astype(np.float64)
+        tol = _scores_close(got_scores, ref_scores)
+        got_sel = sel.cpu().numpy()
+        ok = _gap_ok_rows(ref_scores, 16, 4 * tol)
+        assert ok.mean() > 0.8, what
+        assert np.array_equal(got_sel[ok], om.select_topk(ref_scores, 16)[ok]), what
+        assert_parity(to_f64(out), oracle_attend(c, topk=got_sel), what=what)
+
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        step(d.out)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step(d.out)
+    for rep in range(3):
+        qi = rep % 2
+        d.q.copy_(q_dev[qi])
+        d.out.fill_(float("nan"))
+        score.fill_(float("nan"))
+        sel.fill_(-7)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        check(d.out, qi, f"replay {rep}")
+        eager = d.new_out()
+        d.q.copy_(q_dev[1 - qi])
+        step(eager)
+        torch.cuda.synchronize()
+        check(eager, 1 - qi, f"eager between {rep}")
+
+
 def test_c5_full_step_full_size_sampled_rows():
     """The full decode step with the indexer at full size (B=64, 64/4 heads,
     seq up to 262144): GPU scores, top-16 and attend checked on sampled token
