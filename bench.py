@@ -318,7 +318,7 @@ def make_case(name, extra_replicas):
 
 
 def time_config(name, steps, warmup, replicas, splits, dev, verbose=True, tile_rows=0,
-                cold=False):
+                cold=False, ceiling=False):
     import torch
 
     from workloads import gen
@@ -400,9 +400,169 @@ def time_config(name, steps, warmup, replicas, splits, dev, verbose=True, tile_r
     res["effective_pct_peak"] = 100.0 * res["effective_kv_gbs"] / HBM_PEAK_GBS
     res["unique_pct_peak"] = 100.0 * res["unique_kv_gbs"] / HBM_PEAK_GBS
     del graph, attend_graph
+    if ceiling and not ds.prefill and not ds.dense and ds.plan.tile_rows == 1 \
+            and case.kv_dtype != "mxfp4":
+        res["measured_ceiling"] = gather_ceiling(ds, replicas, steps, warmup, attend_ms)
     if cold:
         res["cold_ms_per_step"], res["warm_ms_per_step"] = cold_and_warm(ds)
     return res, case
+
+
+def _xcd_chunk(units: int, hkv: int) -> int:
+    c = units // 8 if units // 8 < hkv * 16 else hkv * 16
+    return c if c > 1 else 1
+
+
+def attend_page_runs(ds, replica: int):
+    """The byte runs the single-row attend reads for one replica, per
+    workgroup id of its launch: the visible K|V rows of each live page of the
+    workgroup's (unit, split) share, in the order it streams them.  Mirrors
+    the launch's deal of units to XCD slots (chunks of consecutive units, all
+    splits of a unit in one slot) and the split of a unit's live list into
+    equal consecutive shares."""
+    import numpy as np
+
+    case = ds.case
+    kv = ds.kv
+    es = kv.element_size()
+    s0, s1, s2 = (kv.stride(i) * es for i in range(3))
+    row_bytes = 2 * kv_half_row_bytes(case.kv_dtype)
+    assert s2 == row_bytes, "rows of a page-head must be contiguous"
+    nb_total = kv.shape[0]
+    _, bt, _, _ = ds.steps[replica]
+    bt = bt.cpu().numpy()
+    topk = ([case.topk] + [tk for _, tk in case.replicas])[replica]
+    hkv, k, dql = case.num_kv_heads, case.topk_k, case.dql
+    units = case.num_token_rows * hkv
+    S = ds.plan.num_splits
+    c = _xcd_chunk(units, hkv)
+    groups = (units + 8 * c - 1) // (8 * c) * c
+    grid = groups * 8 * S
+    offs, lens, first = [], [], [0]
+    for wg in range(grid):
+        xslot, q8 = wg % 8, wg // 8
+        split, kk = q8 % S, q8 // S
+        unit = ((kk // c) * 8 + xslot) * c + kk % c
+        if unit < units and unit // hkv < case.real_rows:
+            t, h = divmod(unit, hkv)
+            r = t // dql
+            pos = int(case.seq_lens[r]) - dql + t % dql
+            live = []
+            for b in topk[t, h, :k]:
+                b = int(b)
+                if 0 <= b < bt.shape[1] and b * 128 <= pos:
+                    pg = int(bt[r, b])
+                    if 0 <= pg < nb_total:
+                        live.append((pg, min(128, pos - b * 128 + 1)))
+            per = (len(live) + S - 1) // S
+            lo = min(len(live), split * per)
+            for pg, nvis in live[lo:min(len(live), lo + per)]:
+                base, n = pg * s0 + h * s1, nvis * row_bytes
+                for o in range(0, n, 32768):
+                    offs.append(base + o)
+                    lens.append(min(32768, n - o))
+        first.append(len(offs))
+    return (np.array(offs, dtype=np.int64), np.array(lens, dtype=np.int32),
+            np.array(first, dtype=np.int32))
+
+
+def contiguous_runs(lens, first, base: int, span: int):
+    """Runs of the same per-workgroup byte counts laid end to end from base
+    (wrapping inside [base, base + span)), cut at 32 KiB: a plain streaming
+    read."""
+    import numpy as np
+
+    offs, clens, cfirst = [], [], [0]
+    cur = 0
+    for w in range(len(first) - 1):
+        n = int(lens[first[w]:first[w + 1]].astype(np.int64).sum())
+        for o in range(0, n, 32768):
+            if cur + 32768 > span:
+                cur = 0
+            offs.append(base + cur)
+            clens.append(min(32768, n - o))
+            cur += clens[-1]
+        cfirst.append(len(offs))
+    return (np.array(offs, dtype=np.int64), np.array(clens, dtype=np.int32),
+            np.array(cfirst, dtype=np.int32))
+
+
+def gather_ceiling(ds, replicas: int, steps: int, warmup: int, attend_ms: float):
+    """Time the memory-rate probe over exactly the attend's K|V rows (same
+    workgroup ids, pages and order; no top-k or block-table lookups, no
+    compute, no merge), then over contiguous runs of the same sizes.  The
+    probe's checksums for replica 0 are checked against numpy first."""
+    import numpy as np
+    import torch
+
+    import block_sparse_gqa_decode_amd as msa
+
+    dev = ds.kv.device
+    kvb = ds.kv.view(torch.uint8) if ds.kv.dtype != torch.uint8 else ds.kv
+    kvb = kvb.reshape(-1)
+    pool_bytes = kvb.numel() // replicas
+    sets = {"gather": [], "contiguous": []}
+    kv_bytes = []
+    for i in range(replicas):
+        offs, lens, first = attend_page_runs(ds, i)
+        kv_bytes.append(float(lens.astype(np.int64).sum()))
+        sets["gather"].append((offs, lens, first))
+        sets["contiguous"].append(contiguous_runs(lens, first, i * pool_bytes, pool_bytes))
+    host0 = None
+    res = {"kv_bytes_per_step": sum(kv_bytes) / replicas}
+    for kind, lists in sets.items():
+        dev_sets = []
+        for offs, lens, first in lists:
+            out = torch.zeros(2 * (len(first) - 1), dtype=torch.int32, device=dev)
+            dev_sets.append((torch.from_numpy(offs).to(dev), torch.from_numpy(lens).to(dev),
+                             torch.from_numpy(first).to(dev), out))
+
+        def launch(i):
+            o, ln, f, out = dev_sets[i]
+            msa.msa_probe_read_runs(kvb, o, ln, f, out)
+
+        for i in range(replicas):
+            launch(i)
+        torch.cuda.synchronize()
+        if kind == "gather":
+            # bit-exact check of what replica 0's probe read
+            if host0 is None:
+                host0 = kvb[:pool_bytes].cpu().numpy()
+            offs, lens, first = lists[0]
+            words = host0.view(np.uint32)
+            got = dev_sets[0][3].cpu().numpy().view(np.uint32)
+            for w in range(len(first) - 1):
+                x = np.uint32(0)
+                for j in range(first[w], first[w + 1]):
+                    x ^= np.bitwise_xor.reduce(words[offs[j] // 4:(offs[j] + lens[j]) // 4])
+                assert got[2 * w] == x and got[2 * w + 1] == 0, "probe read other bytes"
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for i in range(replicas):
+                launch(i)
+        reps = max(1, (steps + replicas - 1) // replicas)
+        for _ in range(max(1, (warmup + replicas - 1) // replicas)):
+            g.replay()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(reps):
+            g.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) * 1e3 / (reps * replicas)
+        res[f"{kind}_us"] = round(us, 3)
+        res[f"{kind}_gbs"] = round(res["kv_bytes_per_step"] / us / 1e3, 1)
+        del g
+    res["attend_us"] = round(attend_ms * 1e3, 3)
+    res["gather_share_of_attend"] = round(res["gather_us"] / res["attend_us"], 4)
+    res["note"] = ("msa_probe_read_runs, graph replays over the same replicas: 'gather' "
+                   "reads exactly the attend's live K|V rows with the attend's workgroup "
+                   "ids and page order and nothing else; 'contiguous' reads the same "
+                   "per-workgroup byte counts as a plain streaming read. Checksums of "
+                   "replica 0 verified against numpy.")
+    return res
 
 
 def scorer_bytes(case):
@@ -834,7 +994,7 @@ def main():
         return
 
     if args.gpus != 1:
-        print(f"bench.py runs on one GPU only: this build has no multi-GPU path "
+        print(f"bench.py runs on one GPU only: the library has no multi-GPU path "
               f"(--gpus {args.gpus} requested). The decode step shards by kv head or by "
               f"request with no exchange, so each GPU would run this same kernel on its "
               f"share.", file=sys.stderr)
@@ -886,14 +1046,16 @@ def main():
         print(json.dumps(r5), flush=True)
         return
     res, case = time_config(args.config, args.steps, args.warmup, args.replicas,
-                            args.splits, dev, tile_rows=args.tile_rows, cold=True)
+                            args.splits, dev, tile_rows=args.tile_rows, cold=True,
+                            ceiling=True)
     others = {}
     if not args.no_other_configs:
         for name in OTHER_CONFIGS:
             if name == args.config:
                 continue
             r2, case2 = time_config(name, max(64, args.steps // 4), args.warmup,
-                                    args.replicas, args.splits, dev)
+                                    args.replicas, args.splits, dev,
+                                    ceiling=name == "c3_tp1_fp8")
             if not args.no_cpu_baseline:
                 # a short single-thread oracle sample beside each GPU number
                 import numpy as np
@@ -936,6 +1098,7 @@ def main():
         "avg_launch_us": round(kernel_s * 1e6, 3),
         "timing": "HIP events around graph replays of the attend launches alone, on "
                   "the stream they run on",
+        "measured_ceiling": res.get("measured_ceiling"),
     }
     cpu = None
     if not args.no_cpu_baseline:

@@ -47,12 +47,13 @@ __all__ = [
     "msa_sparse_decode_merge", "msa_block_score_topk", "msa_sparse_prefill_plan",
     "msa_sparse_prefill_run",
     "msa_topk_select", "msa_fp8_e4m3_to_bf16", "msa_fp8_e5m2_to_bf16", "msa_mxfp4_to_bf16",
+    "msa_probe_read_runs",
     "library_path", "load_library", "KV_BF16", "KV_FP8_E4M3", "KV_FP8_E5M2", "KV_MXFP4",
     "Q_BF16", "Q_FP8_E4M3",
     "PAGE_SIZE", "HEAD_DIM", "ABI_VERSION",
 ]
 
-ABI_VERSION = 4
+ABI_VERSION = 5
 PAGE_SIZE = 128
 HEAD_DIM = 128
 KV_BF16 = 0
@@ -144,6 +145,7 @@ def load_library():
         "msa_fp8_e4m3_to_bf16": (i32, [vp, vp, i64, vp]),
         "msa_fp8_e5m2_to_bf16": (i32, [vp, vp, i64, vp]),
         "msa_mxfp4_to_bf16": (i32, [vp, pi64, i64, i32, vp, vp]),
+        "msa_probe_read_runs": (i32, [vp, i64, vp, vp, i32, vp, i32, vp, vp]),
         "msa_last_error": (ctypes.c_char_p, []),
         "msa_abi_version": (i32, []),
     }
@@ -560,3 +562,31 @@ class PlanCache:
                 q_dtype=q_dtype, device=block_table.device)
             self.plans[key] = plan
         return plan
+
+
+def msa_probe_read_runs(buffer: torch.Tensor, run_offsets: torch.Tensor,
+                        run_bytes: torch.Tensor, wg_first_run: torch.Tensor,
+                        out: torch.Tensor, stream=None) -> None:
+    """Memory-rate probe: workgroup w reads the byte runs
+    wg_first_run[w] .. wg_first_run[w+1]-1 of ``buffer`` (offsets int64, sizes
+    int32) and writes the XOR of the 32-bit words it read to out[2w] and its
+    count of skipped runs to out[2w+1] (out int32 [2 * workgroups])."""
+    dev = buffer.device
+    if dev.type != "cuda" or not buffer.is_contiguous():
+        raise ValueError("buffer must be a contiguous device tensor")
+    for name, t, dt in (("run_offsets", run_offsets, torch.int64),
+                        ("run_bytes", run_bytes, torch.int32),
+                        ("wg_first_run", wg_first_run, torch.int32),
+                        ("out", out, torch.int32)):
+        if t.dtype != dt or t.dim() != 1 or not t.is_contiguous() or t.device != dev:
+            raise ValueError(f"{name} must be a contiguous 1-D {dt} tensor on the buffer's "
+                             "device")
+    if run_offsets.numel() != run_bytes.numel():
+        raise ValueError("run_offsets and run_bytes must have the same length")
+    wgs = wg_first_run.numel() - 1
+    if wgs < 0 or out.numel() != 2 * wgs:
+        raise ValueError("wg_first_run needs workgroups + 1 entries and out 2 * workgroups")
+    _check(load_library().msa_probe_read_runs(
+        buffer.data_ptr(), buffer.numel() * buffer.element_size(), run_offsets.data_ptr(),
+        run_bytes.data_ptr(), run_offsets.numel(), wg_first_run.data_ptr(), wgs,
+        out.data_ptr(), _stream_handle(stream, dev)))

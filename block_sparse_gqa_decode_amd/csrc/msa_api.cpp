@@ -17,6 +17,13 @@
 #include "msa_internal.h"
 #include "msa_sparse_decode.h"
 
+namespace msa {
+// Defined in msa_probe.hip.
+hipError_t launch_read_runs(const uint8_t* base, int64_t buffer_bytes, const int64_t* run_off,
+                            const int32_t* run_len, const int32_t* wg_first, int32_t num_runs,
+                            int32_t num_workgroups, uint32_t* out, hipStream_t stream);
+}  // namespace msa
+
 struct msa_plan_s {
   msa_decode_shape shape;   // for a prefill plan: decode_query_len = 0
   bool prefill;
@@ -657,6 +664,27 @@ static msa_status fp8_to_bf16(const void* in, void* out, int64_t n, int fmt, voi
                                          static_cast<uint16_t*>(out), n, fmt,
                                          static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return device_fail(e, "fp8 conversion launch");
+  return ok();
+}
+
+msa_status msa_probe_read_runs(const void* base, int64_t buffer_bytes,
+                               const int64_t* run_offsets, const int32_t* run_bytes,
+                               int32_t num_runs, const int32_t* wg_first_run,
+                               int32_t num_workgroups, uint32_t* out, void* stream) {
+  if (num_workgroups < 0) return fail(MSA_ERR_INVALID_ARG, "num_workgroups must be >= 0");
+  if (num_workgroups > (1 << 24)) return fail(MSA_ERR_UNSUPPORTED, "num_workgroups exceeds 2^24");
+  if (num_runs < 0) return fail(MSA_ERR_INVALID_ARG, "num_runs must be >= 0");
+  if (num_workgroups == 0) return ok();
+  if (base == nullptr || wg_first_run == nullptr || out == nullptr)
+    return fail(MSA_ERR_INVALID_ARG, "base, wg_first_run and out must be non-NULL");
+  if (num_runs > 0 && (run_offsets == nullptr || run_bytes == nullptr))
+    return fail(MSA_ERR_INVALID_ARG, "run_offsets and run_bytes must be non-NULL");
+  if (!aligned16(base)) return fail(MSA_ERR_INVALID_ARG, "base is not 16-byte aligned");
+  if (buffer_bytes < 16) return fail(MSA_ERR_INVALID_ARG, "buffer_bytes must be >= 16");
+  hipError_t e = msa::launch_read_runs(
+      static_cast<const uint8_t*>(base), buffer_bytes, run_offsets, run_bytes, wg_first_run,
+      num_runs, num_workgroups, out, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return device_fail(e, "read-runs probe launch");
   return ok();
 }
 

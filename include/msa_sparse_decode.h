@@ -53,7 +53,7 @@
 extern "C" {
 #endif
 
-#define MSA_ABI_VERSION 4
+#define MSA_ABI_VERSION 5
 
 typedef enum msa_status {
   MSA_OK = 0,
@@ -310,6 +310,27 @@ msa_status msa_fp8_e5m2_to_bf16(const void* in, void* out, int64_t n, void* stre
 msa_status msa_mxfp4_to_bf16(const void* kv_cache, const int64_t kv_strides[4],
                              int64_t num_kv_blocks, int32_t num_kv_heads, void* out,
                              void* stream);
+
+/* Memory-rate probe (a measurement aid, not part of the attend): reads byte
+ * runs of a device buffer and nothing else, so that the rate of the attend's
+ * own page gathers can be measured apart from its compute and fixed costs.
+ *   base, buffer_bytes: the buffer (16-byte aligned, buffer_bytes >= 16).
+ *   run_offsets: int64 [num_runs], byte offsets from base; run_bytes: int32
+ *     [num_runs], each a multiple of 16 in 16..32768.  A run that is
+ *     misaligned, out of that range or not inside the buffer is skipped
+ *     (nothing read) and counted.
+ *   wg_first_run: int32 [num_workgroups + 1]; workgroup w reads runs
+ *     wg_first_run[w] .. wg_first_run[w+1]-1 in order (the range is clamped
+ *     into [0, num_runs]; at most 512 runs per workgroup, the rest counted as
+ *     skipped).
+ *   out: uint32 [2 * num_workgroups]; out[2w] = XOR of every 32-bit word
+ *     workgroup w read, out[2w+1] = its number of skipped runs.
+ * All arrays are device memory owned by the caller; asynchronous on stream
+ * (hipStream_t or NULL).  num_workgroups = 0 launches nothing. */
+msa_status msa_probe_read_runs(const void* base, int64_t buffer_bytes,
+                               const int64_t* run_offsets, const int32_t* run_bytes,
+                               int32_t num_runs, const int32_t* wg_first_run,
+                               int32_t num_workgroups, uint32_t* out, void* stream);
 
 /* Message for the last non-OK status returned on this thread ("" if none). */
 const char* msa_last_error(void);

@@ -570,3 +570,27 @@ def test_c_consumer_links_and_reports_misuse():
     res = subprocess.run([exe], capture_output=True, text=True, timeout=120, env=env)
     assert res.returncode == 2, (res.returncode, res.stdout, res.stderr)
     assert "hipMalloc" in res.stderr and "not rejected" not in res.stderr, res.stderr
+
+
+def test_read_runs_probe_rejects_bad_arguments(lib):
+    f = lib.msa_probe_read_runs
+    ok = dict(base=FAKE, nbytes=1 << 20, off=FAKE, ln=FAKE, nruns=4, first=FAKE, wgs=2,
+              out=FAKE)
+
+    def call(**kw):
+        a = dict(ok, **kw)
+        return f(a["base"], a["nbytes"], a["off"], a["ln"], a["nruns"], a["first"], a["wgs"],
+                 a["out"], None)
+
+    assert call(wgs=-1) == msa.MSA_ERR_INVALID_ARG
+    assert call(nruns=-1) == msa.MSA_ERR_INVALID_ARG
+    assert call(base=None) == msa.MSA_ERR_INVALID_ARG
+    assert call(out=None) == msa.MSA_ERR_INVALID_ARG
+    assert call(first=None) == msa.MSA_ERR_INVALID_ARG
+    assert call(off=None) == msa.MSA_ERR_INVALID_ARG
+    assert call(base=FAKE + 8) == msa.MSA_ERR_INVALID_ARG
+    assert "aligned" in lib.msa_last_error().decode()
+    assert call(nbytes=8) == msa.MSA_ERR_INVALID_ARG
+    assert call(wgs=1 << 25) == msa.MSA_ERR_UNSUPPORTED
+    # No workgroups: nothing to launch, so no HIP call and no error.
+    assert call(wgs=0, base=None) == msa.MSA_OK
