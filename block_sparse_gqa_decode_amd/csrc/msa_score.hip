@@ -381,14 +381,36 @@ __device__ __forceinline__ void pick_digit(const uint32_t* hist, int lane, uint3
 }
 
 // One workgroup per (token row, kv head).  The row's scores live in registers
-// (kPer per thread, block b = tid + 256 i).  A most-significant-digit radix
-// select over the 32-bit keys (four 8-bit passes with LDS histograms) finds
-// the k-th largest key T exactly; if only some of the blocks whose key equals
-// T fit, two 7-bit passes over (16383 - block) pick the lowest block ids
-// among them.  The at most k chosen blocks are then ranked by (key desc,
-// block asc) with one comparison per pair.
+// (kPer per thread, block b = tid + 256 i).
+//
+// Prefilter, exact: let T0 be the k-th largest of the 256 per-thread maxima
+// (0 when fewer than k threads hold a selectable key).  The k maxima ranked
+// at or above it are k distinct keys >= T0, so the k-th largest key of the
+// row is >= T0 and every block the selection keeps (ties at the k-th key
+// included) has a key >= T0.  Wavefront 0 finds T0 bit by bit with ballot
+// counts; the blocks with keys >= T0 (about k of them on unequal scores, at
+// most kPer * k when the maxima are distinct) are compacted into LDS and each
+// is ranked by (key desc, block asc) with one 64-bit comparison per pair.
+//
+// If ties leave more than kSelCap candidates, a most-significant-digit radix
+// select over all keys (four 8-bit passes with LDS histograms) finds the k-th
+// largest key T exactly; if only some of the blocks whose key equals T fit,
+// two 7-bit passes over (16383 - block) pick the lowest block ids among them.
+// The at most k chosen blocks are then ranked as above.
+constexpr int kSelCap = 512;
+
+// (key desc, block asc) as one unsigned order: the key above the inverted
+// 14-bit block id, so a larger packed value ranks first.
+__device__ __forceinline__ uint64_t pack_rank_key(uint32_t key, int block) {
+  return ((uint64_t)key << 14) | (uint64_t)(kMaxScoreBlocks - 1 - block);
+}
+
 template <int kPer>
 __global__ __launch_bounds__(kSelThreads) void select_kernel(SelectParams p) {
+  __shared__ uint32_t s_max[kSelThreads];
+  __shared__ uint32_t s_t0;
+  __shared__ uint32_t s_wcnt[kSelThreads / 64];
+  __shared__ uint64_t s_cand[kSelCap];
   __shared__ uint32_t s_hist[256];
   __shared__ uint32_t s_ctl[4];
   __shared__ uint32_t s_nsel;
@@ -403,11 +425,85 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(SelectParams p) {
   const int nblk = p.max_blocks;
   const uint32_t k = (uint32_t)p.k;
 
-  uint32_t key[kPer];
+  // Loads are unconditional (blocks past the row re-read its last block and
+  // count as key 0), so all kPer of them are in flight together; a load
+  // under a branch was waited for before the next one was issued.
+  float v[kPer];
 #pragma unroll
   for (int i = 0; i < kPer; ++i) {
-    const int b = tid + kSelThreads * i;
-    key[i] = b < nblk ? order_key(srow[(int64_t)b * p.sc_s1]) : 0u;
+    const int b = min(tid + kSelThreads * i, nblk - 1);
+    v[i] = srow[(int64_t)b * p.sc_s1];
+  }
+  uint32_t key[kPer];
+#pragma unroll
+  for (int i = 0; i < kPer; ++i)
+    key[i] = tid + kSelThreads * i < nblk ? order_key(v[i]) : 0u;
+
+  // Prefilter threshold T0: the k-th largest thread maximum.
+  {
+    uint32_t m = 0u;
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) m = max(m, key[i]);
+    s_max[tid] = m;
+  }
+  __syncthreads();
+  if (tid < 64) {
+    uint32_t mm[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) mm[j] = s_max[4 * lane + j];
+    uint32_t t0 = 0u;
+#pragma unroll 1
+    for (int bit = 31; bit >= 0; --bit) {
+      const uint32_t c = t0 | (1u << bit);
+      uint32_t cnt = 0u;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) cnt += (uint32_t)__popcll(__ballot(mm[j] >= c));
+      if (cnt >= k) t0 = c;
+    }
+    if (lane == 0) s_t0 = t0;
+  }
+  __syncthreads();
+  const uint32_t t0 = s_t0;
+  const int wave = tid >> 6;
+  {
+    uint32_t cnt = 0u;
+#pragma unroll
+    for (int i = 0; i < kPer; ++i)
+      cnt += (uint32_t)__popcll(__ballot(key[i] != 0u && key[i] >= t0));
+    if (lane == 0) s_wcnt[wave] = cnt;
+  }
+  __syncthreads();
+  uint32_t base = 0u, total = 0u;
+#pragma unroll
+  for (int w = 0; w < kSelThreads / 64; ++w) {
+    base += w < wave ? s_wcnt[w] : 0u;
+    total += s_wcnt[w];
+  }
+  if (total <= (uint32_t)kSelCap) {
+    // Compact the candidates (any order), then rank each against all.
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+      const bool c = key[i] != 0u && key[i] >= t0;
+      const uint64_t bl = __ballot(c);
+      if (c) {
+        const uint32_t at = base + __builtin_amdgcn_mbcnt_hi(
+                                       (uint32_t)(bl >> 32),
+                                       __builtin_amdgcn_mbcnt_lo((uint32_t)bl, 0u));
+        s_cand[at] = pack_rank_key(key[i], tid + kSelThreads * i);
+      }
+      base += (uint32_t)__popcll(bl);
+    }
+    __syncthreads();
+    int32_t* out = p.topk_out + ((int64_t)t * p.hkv + h) * p.k;
+    for (int c = tid; c < (int)total; c += kSelThreads) {
+      const uint64_t mine = s_cand[c];
+      int rank = 0;
+#pragma unroll 4
+      for (int j = 0; j < (int)total; ++j) rank += s_cand[j] > mine ? 1 : 0;
+      if (rank < p.k) out[rank] = kMaxScoreBlocks - 1 - (int)(mine & (kMaxScoreBlocks - 1));
+    }
+    if (tid >= (int)total && tid < p.k) out[tid] = -1;
+    return;
   }
 
   uint32_t prefix = 0, mask = 0, need = k, ties = 0;

@@ -484,6 +484,36 @@ def test_selector_special_values():
         assert np.array_equal(out.cpu().numpy(), om.select_topk(sc.astype(np.float64), k)), k
 
 
+@pytest.mark.parametrize("k", [1, 16, 64])
+def test_selector_prefilter_and_radix_fallback(k):
+    """Rows whose candidate set (blocks at or above the k-th largest
+    per-thread maximum) stays small take the compare-and-rank path; rows
+    where ties leave more than 512 candidates (all 2048 equal, 600 tied at the
+    top, 600 tied at the k-th place) take the radix select.  Both must equal
+    the oracle's ranking, ties going to the lower block."""
+    _banner(f"selector prefilter / radix fallback k={k}")
+    rng = np.random.default_rng(171)
+    nb, rows = 2048, 8
+    sc = rng.standard_normal((1, nb, rows)).astype(np.float32)
+    sc[0, :, 1] = 0.5                                        # all equal: fallback
+    top = rng.choice(nb, 600, replace=False)
+    sc[0, top, 2] = 9.0                                      # 600 tied at the top
+    sc[0, :, 3] = rng.standard_normal(nb).astype(np.float32) - 10.0
+    sc[0, top[:k - 1], 3] = 5.0                              # k-1 clear winners ...
+    sc[0, top[k - 1:], 3] = 4.0                              # ... then 600-k+1 tied
+    tie = rng.choice(nb, 400, replace=False)
+    sc[0, tie, 4] = 7.0                                      # 400 tied: fast path
+    sc[0, :, 5] = np.round(sc[0, :, 5] * 2) / 2              # coarse ties
+    sc[0, rng.random(nb) < 0.9, 6] = -np.inf                 # ~200 selectable
+    sc[0, :, 7] = -np.inf
+    sc[0, :5, 7] = 1.0                                       # fewer than k selectable
+    dev = torch.from_numpy(np.ascontiguousarray(sc.transpose(0, 2, 1))).cuda().transpose(1, 2)
+    out = torch.full((rows, 1, k), -7, dtype=torch.int32, device="cuda")
+    msa.msa_topk_select(dev, out)
+    torch.cuda.synchronize()
+    assert np.array_equal(out.cpu().numpy(), om.select_topk(sc.astype(np.float64), k))
+
+
 def _gap_ok_rows(ref_scores, k, eps):
     """(t, h) pairs whose oracle k-th and (k+1)-th scores differ by > eps."""
     hkv, nb, nt = ref_scores.shape
