@@ -89,6 +89,10 @@
 namespace msa {
 namespace {
 
+// Reads through this pointer type go to the scalar cache when the index is
+// wave-uniform.
+typedef __attribute__((address_space(4))) const int32_t const_i32;
+
 // Log-sum-exp merge of the split partials of one (token row, q head) and the
 // bf16 store of head dims d0..d0+7.
 __device__ __forceinline__ void merge_splits(const AttendParams& p, int64_t row, int d0) {
@@ -213,6 +217,14 @@ __global__ __launch_bounds__(kThreads) void attend_kernel(AttendParams p) {
   __shared__ float s_l[kWaves][16];
   __shared__ float s_o[kWaves][16][kHeadDim + kOPad];
 
+  // Every kernel argument the prologue reads, fetched as one batch of scalar
+  // loads: left to itself the compiler loads them in three dependent
+  // batches, each a scalar-cache miss at the start of the launch.
+  asm volatile("" ::"s"(p.q), "s"(p.kv), "s"(p.kv_s0), "s"(p.kv_s1), "s"(p.kv_s2),
+               "s"(p.num_kv_blocks), "s"(p.block_table), "s"(p.seq_lens), "s"(p.topk));
+  asm volatile("" ::"s"(p.tk_s0), "s"(p.tk_s1), "s"(p.tk_s2), "s"(p.bt_stride), "s"(p.dql),
+               "s"(p.real_rows), "s"(p.hq), "s"(p.hkv), "s"(p.group), "s"(p.topk_k),
+               "s"(p.splits), "s"(p.num_units));
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
@@ -232,16 +244,14 @@ __global__ __launch_bounds__(kThreads) void attend_kernel(AttendParams p) {
   const int rows = p.group;  // q heads of the unit = MFMA rows in use
   const int head0 = h * p.group;
 
-  // Decode rows are computed inline (the request index stays a scalar, so
-  // seq_lens[r] is a scalar load); prefill rows use the binary search.
+  // Decode rows are computed inline (the request index stays a scalar; the
+  // position is read with the top-k row below); prefill rows use the binary
+  // search.
   int r = 0, pos = 0;
   bool live;
   if constexpr (!kVarlen) {
     live = t < p.real_rows;
-    if (live) {
-      r = t / p.dql;
-      pos = p.seq_lens[r] - p.dql + (t - r * p.dql);
-    }
+    r = live ? t / p.dql : 0;
   } else {
     live = locate_token<1>(p, t, r, pos);
   }
@@ -258,19 +268,26 @@ __global__ __launch_bounds__(kThreads) void attend_kernel(AttendParams p) {
     return;
   }
 
-  // Resolve the top-k row into the ordered list of live pages.
+  // Resolve the top-k row into the ordered list of live pages.  The lane's
+  // top-k entry (a vector load at a clamped lane: a single-row plan always
+  // has a top-k row) and a decode row's length (a scalar load through the
+  // constant address space) are both in flight before either is used, and
+  // the filter takes no short cuts, so neither read waits behind the other:
+  // top-k and length, then the block table, then the pages.
   if (wave == 0) {
     bool live = false;
     int page = 0, nvis = 0;
-    if (lane < p.topk_k) {
-      const int b = p.topk[t * p.tk_s0 + h * p.tk_s1 + lane * p.tk_s2];
-      if (b >= 0 && b < p.bt_stride && (int64_t)b * kPage <= pos) {
-        const int pg = p.block_table[(int64_t)r * p.bt_stride + b];
-        if (pg >= 0 && pg < p.num_kv_blocks) {
-          live = true;
-          page = pg;
-          nvis = min(kPage, pos - b * kPage + 1);
-        }
+    const int li = lane < p.topk_k ? lane : 0;
+    const int b_raw = p.topk[t * p.tk_s0 + h * p.tk_s1 + li * p.tk_s2];
+    if constexpr (!kVarlen)
+      pos = ((const const_i32*)p.seq_lens)[r] - p.dql + (t - r * p.dql);
+    const int b = lane < p.topk_k ? b_raw : -1;
+    if ((b >= 0) & (b < p.bt_stride) & ((int64_t)b * kPage <= pos)) {
+      const int pg = p.block_table[(int64_t)r * p.bt_stride + b];
+      if (pg >= 0 && pg < p.num_kv_blocks) {
+        live = true;
+        page = pg;
+        nvis = min(kPage, pos - b * kPage + 1);
       }
     }
     const uint64_t mask = __ballot(live);
