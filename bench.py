@@ -46,13 +46,18 @@ METRIC = "decode tokens/s and effective KV GB/s (% HBM peak), sparse GQA attend,
 HBM_PEAK_GBS = 8000.0
 # MI355X dense matrix-core peaks (TFLOP/s): index False = bf16, True = fp8.
 MFMA_PEAK_TFLOPS = {False: 2500.0, True: 5000.0}
-DEFAULT_CONFIG = "c2_tp4_fp8"
-OTHER_CONFIGS = ("c3_tp1_fp8", "c4_spec_ragged", "c2_tp4_fp8q", "c2_tp4_e5m2",
+# The headline workload is the largest attend workload (dql 32, ragged,
+# 516 token rows); every other workload is reported beside it.
+DEFAULT_CONFIG = "c4_spec_ragged"
+OTHER_CONFIGS = ("c2_tp4_fp8", "c3_tp1_fp8", "c2_tp4_fp8q", "c2_tp4_e5m2",
                  "c2_tp4_mxfp4", "c2_tp4_mxfp4_fp8q", "pf1_chunked_prefill", "d1_dense_tp1")
 FULL_STEP_CONFIG = "c5_full_step"
-# rocprofv3 counter summaries, each valid for the kernel sources it was taken on
-TRAFFIC_FILES = {"attend": os.path.join(ROOT, "profiles", "attend_traffic.json"),
-                 "score": os.path.join(ROOT, "profiles", "score_traffic.json")}
+# Fewest steps ever timed, whatever --steps asks (the timed window then spans
+# at least this many step replays).
+MIN_TIMED_STEPS = 200
+# rocprofv3 counter summaries (HBM bytes per launch), one file per workload,
+# each valid only for the kernel sources it was taken on.
+TRAFFIC_DIR = os.path.join(ROOT, "profiles")
 KERNEL_SOURCES = {
     "attend": ("block_sparse_gqa_decode_amd/csrc/msa_attend.hip",
                "block_sparse_gqa_decode_amd/csrc/msa_page.h",
@@ -147,6 +152,8 @@ def step_bytes(case, q, topk):
     first[1:] = ks[1:] != ks[:-1]
     uniq_kv = int(nv[first].sum()) * row_bytes
     n_live = int(live.sum())
+    key_units = int(nvis.sum())           # (visible key, token row, kv head) triples
+    group = case.num_q_heads // case.num_kv_heads
     q_bytes = real * case.num_q_heads * 128 * (1 if case.q_dtype == "fp8_e4m3" else 2)
     out_bytes = case.num_token_rows * case.num_q_heads * 128 * 2
     idx_bytes = 0 if topk is None else real * case.num_kv_heads * case.topk_k * 4
@@ -156,7 +163,10 @@ def step_bytes(case, q, topk):
         "unique_kv": uniq_kv,
         "q_out_meta": q_bytes + out_bytes + meta,
         "algorithmic": eff_kv + q_bytes + out_bytes + meta,
+        "unique_algorithmic": uniq_kv + q_bytes + out_bytes + meta,
         "live_pages": n_live,
+        # S = q K^T and O += P V: 2 * 128 flops each per (q head, visible key)
+        "flops": key_units * 4 * group * 128,
     }
 
 
@@ -363,7 +373,7 @@ def time_config(name, steps, warmup, replicas, splits, dev, verbose=True, tile_r
         return ev0.elapsed_time(ev1), time.perf_counter() - h0
 
     warm_replays = max(1, (warmup + replicas - 1) // replicas)
-    replays = max(1, (steps + replicas - 1) // replicas)
+    replays = max(1, (max(steps, MIN_TIMED_STEPS) + replicas - 1) // replicas)
     n_steps = replays * replicas
     for _ in range(warm_replays):
         graph.replay()
@@ -382,6 +392,7 @@ def time_config(name, steps, warmup, replicas, splits, dev, verbose=True, tile_r
     res = {
         "config": name,
         "steps": n_steps,
+        "steps_requested": steps,
         "ms_per_step": ms_step,
         "host_ms_per_step": host_s * 1e3 / n_steps,
         "tokens_per_s": case.real_rows / s,
@@ -391,13 +402,14 @@ def time_config(name, steps, warmup, replicas, splits, dev, verbose=True, tile_r
         "effective_kv_bytes": eff,
         "unique_kv_bytes": uniq,
         "algorithmic_bytes": alg,
+        "unique_algorithmic_bytes": ds.mean_bytes("unique_algorithmic"),
+        "attend_flops": ds.mean_bytes("flops"),
         "splits": ds.plan.num_splits,
         "tile_rows": ds.plan.tile_rows,
         "launches_per_step": 1 if ds.plan.num_splits == 1 or ds.plan.merges_in_attend else 2,
         "attend_ms": attend_ms,
         "real_rows": case.real_rows,
     }
-    res["effective_pct_peak"] = 100.0 * res["effective_kv_gbs"] / HBM_PEAK_GBS
     res["unique_pct_peak"] = 100.0 * res["unique_kv_gbs"] / HBM_PEAK_GBS
     del graph, attend_graph
     if ceiling and not ds.prefill and not ds.dense and ds.plan.tile_rows == 1 \
@@ -673,7 +685,7 @@ def _graph_time(fns, replicas, steps, warmup):
         for i in range(replicas):
             fns(i)
     torch.cuda.synchronize()
-    replays = max(1, (steps + replicas - 1) // replicas)
+    replays = max(1, (max(steps, MIN_TIMED_STEPS) + replicas - 1) // replicas)
     for _ in range(max(1, (warmup + replicas - 1) // replicas)):
         g.replay()
     torch.cuda.synchronize()
@@ -716,7 +728,7 @@ def time_full_step(name, steps, warmup, replicas, dev, verbose=True):
     att = sum(b["algorithmic"] for b in ab) / len(ab)
     eff = sum(b["effective_kv"] for b in ab) / len(ab)
     res = {
-        "config": name, "steps": n, "ms_per_step": step_ms,
+        "config": name, "steps": n, "steps_requested": steps, "ms_per_step": step_ms,
         "tokens_per_s": case.real_rows / (step_ms / 1e3),
         "score_topk_ms": score_ms, "select_ms": select_ms, "attend_ms": attend_ms,
         "score_k_half_bytes": sb["k_half"], "score_algorithmic_bytes": sb["algorithmic"],
@@ -726,7 +738,7 @@ def time_full_step(name, steps, warmup, replicas, dev, verbose=True):
         "scorer_pct_hbm_peak": 100 * sb["scorer"] / ((score_ms - select_ms) / 1e3) / 1e9
                                / HBM_PEAK_GBS,
         "score_traffic_bytes": (lambda t: None if t is None else t.get("hbm_bytes_per_launch"))(
-            load_traffic(kernel_source_hash("score"), "score")),
+            load_traffic(name, "score")),
         # MFMA use of the HBM-bound scorer: its matrix-core flops over its
         # time, against the dense peak of the MFMA it issues (bf16 q: bf16,
         # fp8 q: fp8).
@@ -739,6 +751,23 @@ def time_full_step(name, steps, warmup, replicas, dev, verbose=True):
         "step_algorithmic_gbs": (att + sb["algorithmic"]) / (step_ms / 1e3) / 1e9,
         "splits": fs.plan.num_splits, "real_rows": case.real_rows,
     }
+    ts = (score_ms - select_ms) / 1e3
+    res["roofline"] = _roofline(
+        sb["scorer"], sb["mfma_flops"], ts, MFMA_PEAK_TFLOPS[case.q_dtype == "fp8_e4m3"],
+        res["score_traffic_bytes"],
+        {"kernel": f"score_kernel<kv {case.kv_dtype}, q {case.q_dtype}>",
+         "basis": "K half of every visible row of every (request, kv head) + q + the score "
+                  "write + block-table entries",
+         "timing": "HIP events: graph replays of score + select minus select alone"})
+    uq = sum(b["unique_algorithmic"] for b in ab) / len(ab)
+    fl = sum(b["flops"] for b in ab) / len(ab)
+    at = load_traffic(name, "attend")
+    res["attend_roofline"] = _roofline(
+        uq, fl, attend_ms / 1e3, MFMA_PEAK_TFLOPS[False],
+        None if at is None else at.get("hbm_bytes_per_launch"),
+        {"kernel": f"attend_kernel<kv {case.kv_dtype}, q {case.q_dtype}>",
+         "basis": UNIQUE_BASIS, "timing": "HIP events around graph replays of the attend"})
+    res["step_pct_hbm_peak"] = 100 * res["step_algorithmic_gbs"] / HBM_PEAK_GBS
     del fs
     torch.cuda.empty_cache()
     return res
@@ -910,17 +939,77 @@ def cpu_pool_baseline(name: str, seconds: float, max_workers: int = 16):
     }
 
 
-def load_traffic(src_hash, kernel: str = "attend"):
-    """HBM bytes per launch from the committed rocprofv3 counter summary, if it
-    was taken on the current kernel source; else None."""
+def kernel_key(res) -> str:
+    """The kernel family that runs a workload's attend: the single-row attend
+    or the multi-row tile kernel."""
+    return "attend" if res.get("tile_rows", 1) == 1 else "tile"
+
+
+def traffic_path(config: str, kernel: str) -> str:
+    return os.path.join(TRAFFIC_DIR, f"{kernel}_{config}_traffic.json")
+
+
+def load_traffic(config: str, kernel: str):
+    """HBM bytes per launch of `kernel` on `config` from the committed
+    rocprofv3 counter summary, if it was taken on the current sources of that
+    kernel; else None."""
     try:
-        with open(TRAFFIC_FILES[kernel]) as f:
+        with open(traffic_path(config, kernel)) as f:
             rec = json.load(f)
     except (OSError, ValueError):
         return None
-    if rec.get("kernel_source_sha") != src_hash:
+    if rec.get("kernel_source_sha") != kernel_source_hash(kernel):
         return None
     return rec
+
+
+UNIQUE_BASIS = ("unique K|V page rows (each distinct (request, kv head, page) once, at the "
+                "largest visible count any of its token rows has) + q + out + top-k entries "
+                "+ block-table entries, per attend launch: the least the launch must move "
+                "from HBM")
+
+
+def _roofline(bytes_per_launch, flops_per_launch, seconds, mfma_peak, traffic, extra):
+    """A roofline record for one kernel launch: HBM rate against 8 TB/s and
+    matrix-core rate against the dense MFMA peak; `bound`, `achieved`, `peak`
+    and `frac` are the binding one (the larger fraction)."""
+    gbs = bytes_per_launch / seconds / 1e9
+    tflops = flops_per_launch / seconds / 1e12
+    hbm_frac, mfma_frac = gbs / HBM_PEAK_GBS, tflops / mfma_peak
+    hbm = {"achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+           "frac": round(hbm_frac, 4)}
+    mfma = {"achieved": round(tflops, 2), "peak": mfma_peak, "unit": "TFLOP/s",
+            "frac": round(mfma_frac, 4)}
+    top = hbm if hbm_frac >= mfma_frac else mfma
+    rec = {"bound": "hbm" if hbm_frac >= mfma_frac else "mfma", **top,
+           "traffic": traffic, "hbm": hbm, "mfma": mfma,
+           "bytes_per_launch": int(bytes_per_launch), "flops_per_launch": int(flops_per_launch),
+           "avg_launch_us": round(seconds * 1e6, 3)}
+    rec.update(extra)
+    return rec
+
+
+def attend_roofline(res, case):
+    """The attend launch's roofline on unique bytes (see UNIQUE_BASIS), with
+    the per-token (effective) rate beside it."""
+    kernel = kernel_key(res)
+    t = res["attend_ms"] / 1e3
+    traffic = load_traffic(res["config"], kernel)
+    label = (f"attend_kernel<kv {case.kv_dtype}, q {case.q_dtype}>" if kernel == "attend" else
+             f"multi_kernel<kv {case.kv_dtype}, q {case.q_dtype}, rows {res['tile_rows']}>")
+    return _roofline(
+        res["unique_algorithmic_bytes"], res["attend_flops"], t, MFMA_PEAK_TFLOPS[False],
+        None if traffic is None else traffic.get("hbm_bytes_per_launch"),
+        {"kernel": label, "basis": UNIQUE_BASIS,
+         "effective_gbs": round(res["algorithmic_bytes"] / t / 1e9, 1),
+         "effective_note": "per-token logical bytes over the launch: pages shared by a "
+                           "request's token rows count once per row, and the L2 / MALL serve "
+                           "the repeats, so this is not an HBM bandwidth and can exceed 8 TB/s",
+         "mfma_note": "attend flops = 4 * G * 128 per (visible key, token row, kv head); "
+                      "bf16 dense peak (P V is a bf16 MFMA whatever the q format)",
+         "timing": "HIP events around graph replays of the attend launches alone, on the "
+                   "stream they run on",
+         "traffic_source": None if traffic is None else traffic.get("source")})
 
 
 def profile_mode(name, launches, splits, dev):
@@ -949,7 +1038,10 @@ def profile_mode(name, launches, splits, dev):
                       "algorithmic_bytes_per_launch": b,
                       "effective_kv_bytes_per_launch": ds.mean_bytes("effective_kv"),
                       "unique_kv_bytes_per_launch": ds.mean_bytes("unique_kv"),
-                      "kernel_source_sha": kernel_source_hash()}), flush=True)
+                      "unique_algorithmic_bytes_per_launch": ds.mean_bytes("unique_algorithmic"),
+                      "tile_rows": ds.plan.tile_rows, "splits": ds.plan.num_splits,
+                      "kernel_source_sha": kernel_source_hash(
+                          "attend" if ds.plan.tile_rows == 1 else "tile")}), flush=True)
 
 
 def copy_calibration(dev, mib=1024, launches=4):
@@ -1053,9 +1145,10 @@ def main():
         for name in OTHER_CONFIGS:
             if name == args.config:
                 continue
-            r2, case2 = time_config(name, max(64, args.steps // 4), args.warmup,
+            r2, case2 = time_config(name, args.steps, args.warmup,
                                     args.replicas, args.splits, dev,
-                                    ceiling=name == "c3_tp1_fp8")
+                                    ceiling=name in ("c2_tp4_fp8", "c3_tp1_fp8"))
+            r2["roofline"] = attend_roofline(r2, case2)
             if not args.no_cpu_baseline:
                 # a short single-thread oracle sample beside each GPU number
                 import numpy as np
@@ -1067,8 +1160,7 @@ def main():
                 r2["gpu_over_oracle"] = r2["tokens_per_s"] / r2["oracle_tokens_per_s_1thread"]
             others[name] = {k: (round(v, 4) if isinstance(v, float) else v)
                             for k, v in r2.items()}
-        r5 = time_full_step(FULL_STEP_CONFIG, max(32, args.steps // 8), args.warmup,
-                            args.replicas, dev)
+        r5 = time_full_step(FULL_STEP_CONFIG, args.steps, args.warmup, args.replicas, dev)
         if not args.no_cpu_baseline:
             from workloads import gen
 
@@ -1079,27 +1171,8 @@ def main():
             r5["gpu_over_oracle"] = r5["tokens_per_s"] / rate5
         others[FULL_STEP_CONFIG] = {k: (round(v, 4) if isinstance(v, float) else v)
                                     for k, v in r5.items()}
-    src_hash = kernel_source_hash()
-    traffic = load_traffic(src_hash)
-    kernel_s = res["attend_ms"] / 1e3
-    achieved = res["algorithmic_bytes"] / kernel_s / 1e9
-    roofline = {
-        "bound": "hbm",
-        "achieved": round(achieved, 1),
-        "peak": HBM_PEAK_GBS,
-        "unit": "GB/s",
-        "frac": round(achieved / HBM_PEAK_GBS, 4),
-        "traffic": None if traffic is None else traffic.get("hbm_bytes_per_launch"),
-        "kernel": (f"attend_kernel<kv {case.kv_dtype}, q {case.q_dtype}>"
-                   if res["tile_rows"] == 1 else
-                   f"multi_kernel<kv {case.kv_dtype}, q {case.q_dtype}, rows "
-                   f"{res['tile_rows']}>"),
-        "algorithmic_bytes_per_launch": int(res["algorithmic_bytes"]),
-        "avg_launch_us": round(kernel_s * 1e6, 3),
-        "timing": "HIP events around graph replays of the attend launches alone, on "
-                  "the stream they run on",
-        "measured_ceiling": res.get("measured_ceiling"),
-    }
+    roofline = attend_roofline(res, case)
+    roofline["measured_ceiling"] = res.get("measured_ceiling")
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(case, args.cpu_seconds)
@@ -1109,6 +1182,9 @@ def main():
         "unit": "tokens/s",
         "n_gpus": 1,
         "steps": res["steps"],
+        "steps_requested": args.steps,
+        "steps_note": f"timed steps = --steps rounded up to at least {MIN_TIMED_STEPS} and to "
+                      f"whole cycles of the {args.replicas} replicas captured in one graph",
         "warmup": args.warmup,
         "ms_per_step": round(res["ms_per_step"], 5),
         "higher_is_better": True,
@@ -1121,6 +1197,7 @@ def main():
             "kv_cache": case.kv_dtype,
             "global_batch": case.batch,
             "decode_query_len": getattr(case, "dql", 0),
+            "num_token_rows": case.num_token_rows,
             "num_q_heads": case.num_q_heads,
             "num_kv_heads": case.num_kv_heads,
             "topk_blocks": case.topk_k if case.topk is not None else "dense",
@@ -1128,10 +1205,13 @@ def main():
             "head_dim": 128,
             "replicas": args.replicas,
             "splits": res["splits"],
+            "tile_rows": res["tile_rows"],
             "parallelism": "single GPU",
         },
         "effective_kv_gbs": round(res["effective_kv_gbs"], 1),
-        "effective_pct_hbm_peak": round(res["effective_pct_peak"], 2),
+        "effective_kv_note": "per-token logical K|V bytes per step time; repeats of a page "
+                             "across a request's token rows count each time (the L2 / MALL "
+                             "serve them), so this is not an HBM bandwidth",
         "unique_kv_gbs": round(res["unique_kv_gbs"], 1),
         "unique_pct_hbm_peak": round(res["unique_pct_peak"], 2),
         "host_ms_per_step": round(res["host_ms_per_step"], 5),
@@ -1145,8 +1225,7 @@ def main():
         "cpu_baseline": cpu,
         "cpu_baseline_all_cores": cpu_pool,
         "other_configs": others,
-        "kernel_source_sha": src_hash,
-        "tile_kernel_source_sha": kernel_source_hash("tile"),
+        "kernel_source_sha": {k: kernel_source_hash(k) for k in KERNEL_SOURCES},
     }
     print(json.dumps(line), flush=True)
 

@@ -465,8 +465,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 2))) voi
   const int t = unit / p.hkv;
   const int h = unit - t * p.hkv;
   const int qr = threadIdx.x >> 4;
-  int r = 0, pos = 0;
-  if (!locate_token(p, t, r, pos) || qr >= p.group) return;
+  // Padding rows were written as zeros by the attend.  A row is real when it
+  // lies below the real rows (decode) or below the last chunk boundary
+  // (prefill); no position is needed here.
+  const bool real = p.cu_q != nullptr ? t < p.cu_q[p.num_reqs] : t < p.real_rows;
+  if (!real || qr >= p.group) return;
   const int64_t row = (int64_t)t * p.hq + h * p.group + qr;
   const int d0 = (threadIdx.x & 15) * 8;
   switch (p.splits) {

@@ -151,13 +151,21 @@ typedef struct msa_plan_s* msa_plan;
 
 /* Validate `shape`, choose the launch configuration and allocate the plan's
  * persistent fp32 split-K partial arena on HIP device `device` (the only
- * allocation the library makes).  On success *plan_out owns that arena until
- * msa_sparse_decode_plan_destroy.  A plan must not be run concurrently on two
- * streams (the arena is shared).  A plan that merges its splits inside the
- * attend also keeps one int32 arrival counter per work unit in the arena,
- * zeroed here (a hipMemset and a device synchronisation) and left at zero by
- * every completed run.  Shape errors return MSA_ERR_INVALID_ARG or
- * MSA_ERR_UNSUPPORTED before any HIP call. */
+ * allocation the library makes).
+ * Defined by: vLLM MSA decode page, MSACutlassDecodePlanCache.prepare and
+ * _build_plan (one plan per static shape, validated up front, whose device
+ * state keeps stable addresses across graph replays); TensorRT-LLM PR #17171,
+ * flash-decoding commit (split-K partials in a persistent buffer arena).
+ * On success *plan_out owns that arena until msa_sparse_decode_plan_destroy.
+ * A plan must not be run concurrently on two streams (the arena is shared).
+ * A plan that merges its splits inside the attend also keeps one int32
+ * arrival counter per work unit in the arena, zeroed here (a hipMemset and a
+ * device synchronisation) and left at zero by every run that completes.  A
+ * run that does not complete (its stream torn down, its process or kernel
+ * killed mid-way) can leave counters non-zero, after which later runs of the
+ * plan would merge wrongly without an error: destroy such a plan and make a
+ * new one.  Shape errors return MSA_ERR_INVALID_ARG or MSA_ERR_UNSUPPORTED
+ * before any HIP call. */
 msa_status msa_sparse_decode_plan(const msa_decode_shape* shape, int device,
                                   msa_plan* plan_out);
 
@@ -172,7 +180,16 @@ msa_status msa_sparse_decode_plan_info(msa_plan plan, int32_t* num_splits,
                                        int64_t* arena_bytes,
                                        msa_decode_shape* shape_out);
 
-/* One sparse decode step (the attend).  For token row t = r*dql + l (request r,
+/* One sparse decode step (the attend).
+ * Defined by: vLLM sparse-attention page, MiniMaxM3SparseImpl (each query
+ * attends only its indexer-selected KV blocks) and the decode call of
+ * MiniMaxM3SparseTritonImpl.forward; vLLM MSA decode page,
+ * msa_cutlass_sparse_decode (packed cache split into K = first 128 and V =
+ * last 128 entries, sm_scale and the q/k/v scales); vLLM test page, _make_topk
+ * (logical block ids per (token, kv head), -1 padding, token position
+ * seq_len - query_len + local); TensorRT-LLM PR #17171, flash-decoding commit
+ * (zeroed, not NaN, padding rows).
+ * For token row t = r*dql + l (request r,
  * local token l) at position pos = seq_lens[r] - dql + l, kv head h and each q
  * head j = h*G + g (G = Hq/Hkv):
  *   out[t, j, :] = softmax_k( sm_scale * q[t,j,:] . K[k,:] ) V[k,:]
@@ -213,7 +230,10 @@ msa_status msa_sparse_decode_run(msa_plan plan, const void* q, const void* kv_ca
                                  void* out, float sm_scale, void* stream);
 
 /* The two launches of msa_sparse_decode_run, for callers that schedule or
- * time them apart.  msa_sparse_decode_run(...) is exactly
+ * time them apart.
+ * Defined by: TensorRT-LLM PR #17171, flash-decoding commit (split-K over the
+ * selected blocks with fp32 partials, combined by log-sum-exp, padding rows
+ * zeroed).  msa_sparse_decode_run(...) is exactly
  * msa_sparse_decode_attend(...) followed by msa_sparse_decode_merge(...) on the
  * same stream.  With one split (msa_sparse_decode_plan_info), and for
  * single-row plans (tile_rows 1) with 2 to 4 splits, whose last split to
@@ -233,7 +253,9 @@ msa_status msa_sparse_decode_attend(msa_plan plan, const void* q, const void* kv
 msa_status msa_sparse_decode_merge(msa_plan plan, void* out, float v_scale, void* stream);
 
 /* A prefill plan: the same validation, split choice and arena as
- * msa_sparse_decode_plan (destroyed by msa_sparse_decode_plan_destroy). */
+ * msa_sparse_decode_plan (destroyed by msa_sparse_decode_plan_destroy).
+ * Defined by: vLLM sparse-attention page, MiniMaxM3SparsePrefillMetadata and
+ * the prefill call of MiniMaxM3SparseTritonImpl.forward. */
 msa_status msa_sparse_prefill_plan(const msa_prefill_shape* shape, int device,
                                    msa_plan* plan_out);
 
@@ -262,6 +284,11 @@ msa_status msa_sparse_prefill_run(msa_plan plan, const void* q, const void* kv_c
                                   void* stream);
 
 /* Indexer step of a full decode: per-block causal max score, then top-k.
+ * Defined by: TensorRT-LLM PR #17171, indexer-scorer commit (per block, the
+ * causal max of q.k over the kv head's q heads and the block's visible keys,
+ * one launch sized to the batch) and its selector (a top-k over a score
+ * buffer of arbitrary strides); the tie rule (the lower block id first) is
+ * the full-decode-step workload statement's.
  *   score[h, b, t] = max over g < G and visible keys i of block b of
  *                    q[t, h*G+g, :] . K[block_table[r,b], h, i, :]
  * (raw dot product with q = decoded q * q_scale and K = decoded entries *
@@ -274,7 +301,10 @@ msa_status msa_sparse_prefill_run(msa_plan plan, const void* q, const void* kv_c
  *                page_size, head_dim, kv_dtype, q_dtype are used; topk_blocks
  *                and num_splits are ignored.
  *   score        float32 logical [Hkv, max_blocks, num_token_rows] with
- *                score_strides (elements); caller-owned scratch, required.
+ *                score_strides (elements): caller-owned scratch, required
+ *                (NULL is MSA_ERR_INVALID_ARG).  The call takes no plan and
+ *                allocates nothing, so it has no buffer of its own to fall
+ *                back on; the scores stay readable after the call.
  *   max_blocks   1..16384, at least ceil(max seq_len / 128).
  *   topk_out     int32 [num_token_rows, Hkv, topk_k], contiguous; topk_k 1..64.
  */
@@ -287,16 +317,22 @@ msa_status msa_block_score_topk(const msa_decode_shape* shape, const void* q,
                                 int32_t topk_k, void* stream);
 
 /* The selector alone: topk_out[t, h, :] from score (same layout and rule as
- * msa_block_score_topk) for num_rows rows and num_kv_heads heads. */
+ * msa_block_score_topk) for num_rows rows and num_kv_heads heads.
+ * Defined by: TensorRT-LLM PR #17171, indexer-scorer commit (the selector
+ * reads a score buffer of arbitrary strides); ties to the lower block id as
+ * in the full-decode-step workload statement.  NaN and -inf scores are never
+ * selected; -0 and +0 tie. */
 msa_status msa_topk_select(const float* score, const int64_t score_strides[3],
                            int32_t num_kv_heads, int32_t max_blocks, int32_t num_rows,
                            int32_t* topk_out, int32_t topk_k, void* stream);
 
 /* Decode n OCP fp8 e4m3fn codes to bf16 with the same in-register conversion
- * the attend uses (a self-check of the conversion path).  in: uint8[n],
+ * the attend uses (a self-check of the conversion path).  The format is the
+ * vLLM test page's torch.float8_e4m3fn cache.  in: uint8[n],
  * out: bf16 bits uint16[n], device pointers, n >= 1. */
 msa_status msa_fp8_e4m3_to_bf16(const void* in, void* out, int64_t n, void* stream);
-/* The same for OCP fp8 e5m2 codes. */
+/* The same for OCP fp8 e5m2 codes (the vLLM sparse-attention page lists an
+ * fp8_e5m2 KV cache among the backend's cache dtypes). */
 msa_status msa_fp8_e5m2_to_bf16(const void* in, void* out, int64_t n, void* stream);
 
 /* Dequantize an MSA_KV_MXFP4 cache (layout and kv_strides as described at
@@ -310,27 +346,6 @@ msa_status msa_fp8_e5m2_to_bf16(const void* in, void* out, int64_t n, void* stre
 msa_status msa_mxfp4_to_bf16(const void* kv_cache, const int64_t kv_strides[4],
                              int64_t num_kv_blocks, int32_t num_kv_heads, void* out,
                              void* stream);
-
-/* Memory-rate probe (a measurement aid, not part of the attend): reads byte
- * runs of a device buffer and nothing else, so that the rate of the attend's
- * own page gathers can be measured apart from its compute and fixed costs.
- *   base, buffer_bytes: the buffer (16-byte aligned, buffer_bytes >= 16).
- *   run_offsets: int64 [num_runs], byte offsets from base; run_bytes: int32
- *     [num_runs], each a multiple of 16 in 16..32768.  A run that is
- *     misaligned, out of that range or not inside the buffer is skipped
- *     (nothing read) and counted.
- *   wg_first_run: int32 [num_workgroups + 1]; workgroup w reads runs
- *     wg_first_run[w] .. wg_first_run[w+1]-1 in order (the range is clamped
- *     into [0, num_runs]; at most 512 runs per workgroup, the rest counted as
- *     skipped).
- *   out: uint32 [2 * num_workgroups]; out[2w] = XOR of every 32-bit word
- *     workgroup w read, out[2w+1] = its number of skipped runs.
- * All arrays are device memory owned by the caller; asynchronous on stream
- * (hipStream_t or NULL).  num_workgroups = 0 launches nothing. */
-msa_status msa_probe_read_runs(const void* base, int64_t buffer_bytes,
-                               const int64_t* run_offsets, const int32_t* run_bytes,
-                               int32_t num_runs, const int32_t* wg_first_run,
-                               int32_t num_workgroups, uint32_t* out, void* stream);
 
 /* Message for the last non-OK status returned on this thread ("" if none). */
 const char* msa_last_error(void);

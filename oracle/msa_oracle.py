@@ -351,7 +351,9 @@ def dense_decode(q_bits, kv, kv_dtype, k_scale, v_scale, block_table, seq_lens,
                  decode_query_len, num_kv_heads, sm_scale, rows=None, q_dtype="bf16",
                  q_scale=1.0):
     """Decode attend over all keys 0..pos of the request's pages (no top-k),
-    float64; padding rows are zeros.  Returns float64 [len(rows), Hq, 128]."""
+    float64.  Padding rows, and rows with no live key (a position before the
+    first key, or every visible block outside the pool), are zeros, as in
+    ``sparse_decode``.  Returns float64 [len(rows), Hq, 128]."""
     q_bits = np.asarray(q_bits)
     num_rows, hq, d = q_bits.shape
     assert d == HEAD_DIM and hq % num_kv_heads == 0
@@ -373,6 +375,8 @@ def dense_decode(q_bits, kv, kv_dtype, k_scale, v_scale, block_table, seq_lens,
                 gathered[h] = gather_live(kv, kv_dtype, k_scale, v_scale,
                                           block_table[r], pos, h, every)
             k, v = gathered[h]
+            if k is None:      # no live key (pos < 0, or no block in the pool)
+                continue
             qv = decode_query(q_bits[t, j], q_dtype, q_scale)
             out[i, j] = softmax_attend(qv, k, v, sm_scale)
     return out
@@ -483,26 +487,3 @@ def select_topk(score, k: int) -> np.ndarray:
             sel = cand[:k]
             out[t, h, :len(sel)] = sel
     return out
-
-
-# ---------------------------------------------------------------------------
-# byte accounting (the quantities the throughput figures are built from)
-# ---------------------------------------------------------------------------
-
-def live_rows_per_unit(block_table, seq_lens, topk, decode_query_len):
-    """For every real (token, kv head) unit: list of (block, visible rows)."""
-    dql = int(decode_query_len)
-    real = len(seq_lens) * dql
-    hkv = topk.shape[1]
-    res = {}
-    for t in range(real):
-        r, loc = divmod(t, dql)
-        pos = token_position(seq_lens[r], dql, loc)
-        for h in range(hkv):
-            lst = []
-            for b in topk[t, h, :]:
-                n = visible_rows(pos, int(b))
-                if n > 0:
-                    lst.append((int(b), n))
-            res[(t, h)] = lst
-    return res

@@ -161,3 +161,54 @@ def test_mxfp4_prefill_test_page_shape(hq, hkv, tile_rows):
                   | {0, 299, 300, 427, 428, 504, 505, 506, 507})
     got = to_f64(d.out)[rows]
     assert_parity(got, oracle_prefill(case, rows=rows), what="prefill rows")
+
+
+def _extreme_scale_case(q_dtype, q_scale):
+    """A 4-bit case whose visible rows carry E8M0 codes 0 and 255: request 0's
+    first selected page of kv head 0 has K scale code 255 on row 0, request
+    1's of kv head 1 has V scale code 255 on row 0, and request 2's of kv
+    head 0 has K scale code 0 on rows 0..9 and V scale code 0 on rows
+    10..19.  Returns the case and the oracle's output."""
+    case = gen.make_random_case(431, 4, 2, 16, 2, 8, 2600, 4000, kv_dtype=gen.KV_MXFP4,
+                                q_dtype=q_dtype, q_scale=q_scale, k_scale=K_SCALE,
+                                v_scale=V_SCALE)
+    case.kv = case.kv.copy()
+    flat = case.kv.reshape(case.kv.shape[0], case.kv.shape[1], -1)
+    base = om.MXFP4_DATA_BYTES
+
+    def first_page(r, h):
+        t = r * case.dql                         # the request's first token row
+        b = int(case.topk[t, h, 0])
+        assert b >= 0
+        return int(case.block_table[r, b])
+
+    flat[first_page(0, 0), 0, base + 4 * 0 + 1] = 255                 # K, head 0
+    flat[first_page(1, 1), 2 * 1 + 1, base + 4 * 0 + 2] = 255         # V, head 1
+    p2 = first_page(2, 0)
+    flat[p2, 0, base:base + 4 * 10] = 0                               # K rows 0..9
+    flat[p2, 1, base + 4 * 10:base + 4 * 20] = 0                      # V rows 10..19
+    return case, oracle_attend(case)
+
+
+@pytest.mark.parametrize("qd,qs", [(gen.Q_BF16, 1.0), (gen.Q_FP8, 0.5)])
+@pytest.mark.parametrize("tile_rows", [1, 2])
+def test_mxfp4_attend_extreme_scale_codes(qd, qs, tile_rows):
+    """Where the attend widens 4-bit entries to bf16 it reads an E8M0 code as
+    the fp32 pattern code << 23: code 0 counts as 0 instead of 2^-127 (a
+    difference far below the tolerance) and code 255 (NaN) as +inf.  So rows
+    whose visible keys carry code 0 match the oracle, and exactly the (row,
+    q head) outputs that the oracle makes NaN (a visible K or V block scale
+    of 255) come out non-finite."""
+    _banner(f"mxfp4 attend with E8M0 codes 0 and 255 on visible rows, q={qd} "
+            f"tile_rows={tile_rows}")
+    case, ref = _extreme_scale_case(qd, qs)
+    nan_ref = np.isnan(ref).any(axis=2)                 # [rows, Hq]
+    assert nan_ref.any() and not nan_ref.all()
+    d = DevCase(case)
+    d.run(d.plan(tile_rows=tile_rows))
+    torch.cuda.synchronize()
+    got = to_f64(d.out)
+    bad = ~np.isfinite(got).all(axis=2)
+    assert np.array_equal(bad, nan_ref)
+    rows = [t for t in range(case.num_token_rows) if not nan_ref[t].any()]
+    assert_parity(got[rows], ref[rows], what="extreme scale codes")

@@ -545,17 +545,31 @@ def test_full_step_score_select_attend(kvd, qd, qs):
     ref_sel = om.select_topk(ref_scores, 16)
     ok = _gap_ok_rows(ref_scores, 16, 4 * tol)
     # Rows with a clear top-16 / 17th gap must match exactly; the rest are
-    # checked for validity below.  The fp8-q bound is a worst case (~200x the
-    # error measured here), so fewer of the 24 (row, head) units have a clear
-    # gap under it.
-    assert ok.mean() > (0.3 if qd == gen.Q_FP8 else 0.5)
+    # checked for validity below.  Which units have a clear gap depends only
+    # on the oracle's scores and the error bound, not on the GPU: with a bf16
+    # q (bound 2e-5 of the largest score) 23 or 24 of the 24 (row, head)
+    # units do on these inputs; the fp8-q bound is a worst case (~200x the
+    # error measured here), under which 14 (e4m3) and 10 (MXFP4) do.
+    assert ok.mean() > (0.3 if qd == gen.Q_FP8 else 0.8)
     assert np.array_equal(sel[ok], ref_sel[ok])
-    # Rows without a clear gap: every GPU pick scores within tolerance of the
-    # oracle's k-th best.
+    # Rows without a clear gap get a valid top-16 by the oracle's scores:
+    # distinct visible blocks, -1 only as trailing padding and only when
+    # fewer than 16 blocks are visible, in non-increasing score order up to
+    # twice the bound (the GPU ranks by its own scores), and each pick within
+    # the bound of the oracle's 16th best.
     for t, h in zip(*np.nonzero(~ok)):
-        kth = np.sort(ref_scores[h, :, t][np.isfinite(ref_scores[h, :, t])])[::-1][15]
-        for b in sel[t, h]:
-            assert b >= 0 and ref_scores[h, b, t] >= kth - 4 * tol
+        row = ref_scores[h, :, t]
+        n_vis = int(np.isfinite(row).sum())
+        picks = sel[t, h]
+        n_sel = int((picks >= 0).sum())
+        assert n_sel == min(16, n_vis), (t, h, picks)
+        assert np.all(picks[:n_sel] >= 0) and np.all(picks[n_sel:] == -1), (t, h, picks)
+        got_b = picks[:n_sel]
+        assert len(np.unique(got_b)) == n_sel, (t, h, picks)
+        assert np.all(np.isfinite(row[got_b])), (t, h, picks)
+        assert np.all(np.diff(row[got_b]) <= 2 * tol), (t, h, picks)
+        kth = np.sort(row[np.isfinite(row)])[::-1][n_sel - 1]
+        assert np.all(row[got_b] >= kth - 4 * tol), (t, h, picks)
     # Attend over the GPU's own selection, compared where it equals the oracle's.
     case.topk = ref_sel
     out = d.new_out()
@@ -565,21 +579,29 @@ def test_full_step_score_select_attend(kvd, qd, qs):
     assert_parity(to_f64(out)[rows], oracle_attend(case, rows=rows), what="full step")
 
 
-def test_attend_then_merge_equals_run():
-    _banner("attend + merge == run")
+@pytest.mark.parametrize("tile_rows,splits", [(1, 1), (1, 2), (1, 4), (1, 6), (1, 16),
+                                               (2, 3), (2, 8), (4, 5)])
+def test_attend_then_merge_equals_run(tile_rows, splits):
+    """The two halves of a run equal the run, bitwise, for the fused in-attend
+    merge (single-row, 2..4 splits), the merge kernel's unrolled counts and
+    its generic loop (6 and 5 splits), and row-tile plans (which always merge
+    in a second launch); the merged rows also match the oracle."""
+    _banner(f"attend + merge == run, tile_rows={tile_rows} splits={splits}")
     case = gen.make_random_case(115, 4, 4, 16, 1, 16, 2000, 20000, pad_rows=2)
     d = DevCase(case)
-    for splits in (1, 2, 4):
-        plan = d.plan(splits)
-        a = d.new_out()
-        b = d.new_out()
-        d.run(plan, out=a)
-        msa.msa_sparse_decode_attend(plan, d.q, d.kv, d.block_table, d.seq_lens, d.topk, b,
-                                     sm_scale=case.sm_scale, k_scale=case.k_scale,
-                                     v_scale=case.v_scale)
-        msa.msa_sparse_decode_merge(plan, b, v_scale=case.v_scale)
-        torch.cuda.synchronize()
-        assert torch.equal(a.view(torch.int16), b.view(torch.int16)), splits
+    ref = oracle_attend(case)
+    plan = d.plan(splits, tile_rows=tile_rows)
+    assert (plan.num_splits, plan.tile_rows) == (splits, tile_rows)
+    a = d.new_out()
+    b = d.new_out()
+    d.run(plan, out=a)
+    msa.msa_sparse_decode_attend(plan, d.q, d.kv, d.block_table, d.seq_lens, d.topk, b,
+                                 sm_scale=case.sm_scale, k_scale=case.k_scale,
+                                 v_scale=case.v_scale)
+    msa.msa_sparse_decode_merge(plan, b, v_scale=case.v_scale)
+    torch.cuda.synchronize()
+    assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+    assert_parity(to_f64(b), ref, what=f"attend + merge, {splits} splits")
 
 
 def test_fused_merge_counters_return_to_zero():

@@ -986,3 +986,24 @@ def test_dense_decode_planted_mistake_is_caught(monkeypatch):
     monkeypatch.setattr(om, "visible_rows",
                         lambda pos, b: 0 if b < 0 or b * 128 > pos else min(128, pos - b * 128))
     assert not float(np.max(np.abs(run_dense_oracle(case) - dense_reference(case)))) < 1e-12
+
+
+def test_dense_decode_rows_without_live_keys_are_zeros():
+    """Rows that see no key -- a position before the first key (seq_len <
+    decode_query_len), or every visible block outside the pool -- are exact
+    zeros (the zero-row rule for padding and empty rows); every other row
+    still equals causal SDPA over its request's sequence."""
+    case = small_dense_case(8, 2, 4, pattern=(257, 513), pairs=2)
+    case.seq_lens = case.seq_lens.copy()
+    case.seq_lens[0] = 2                                   # positions -2, -1, 0, 1
+    ref = dense_reference(case)                            # before the pool change
+    case.block_table = case.block_table.copy()
+    case.block_table[1, :] = case.kv.shape[0]              # no page of the pool
+    got = run_dense_oracle(case)
+    dql = case.dql
+    empty = [0, 1] + list(range(dql, 2 * dql))             # request 0 rows 0-1, request 1
+    assert np.all(got[empty] == 0.0)
+    live = [t for t in range(case.batch * dql) if t not in empty]
+    assert len(live) >= 2 * dql
+    assert np.all(np.isfinite(ref[live]))
+    assert float(np.max(np.abs(got[live] - ref[live]))) < 1e-12

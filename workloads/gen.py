@@ -274,17 +274,18 @@ def pad_row(sel: np.ndarray, k: int) -> np.ndarray:
 
 
 def every_visible_topk(seq_lens, num_kv_heads: int, dql: int, k: int) -> np.ndarray:
-    """The ``_make_topk`` pattern: ascending 0..visible_pages-1, then -1."""
-    rows = len(seq_lens) * dql
-    topk = np.full((rows, num_kv_heads, k), -1, dtype=np.int32)
-    for r, s in enumerate(seq_lens):
-        for loc in range(dql):
-            t = r * dql + loc
-            visible_tokens = int(s) - dql + loc + 1
-            vp = math.ceil(visible_tokens / PAGE)
-            vp = max(0, min(vp, k))
-            topk[t, :, :vp] = np.arange(vp, dtype=np.int32)
-    return topk
+    """Every block a token can see, ascending, then -1 (the index pattern of
+    the vLLM test file's ``_make_topk`` fixture), built from the rule: token
+    row ``t = r*dql + l`` sits at ``pos = seq_len - dql + l`` and sees blocks
+    ``0 .. pos // 128`` (none when ``pos < 0``), capped at k slots."""
+    seq = np.asarray(seq_lens, dtype=np.int64)
+    rows = len(seq) * dql
+    t = np.arange(rows)
+    pos = seq[t // dql] - dql + (t % dql)
+    last = np.where(pos >= 0, pos // PAGE, -1)
+    slots = np.arange(k)
+    sel = np.where(slots[None, :] <= last[:, None], slots[None, :], -1).astype(np.int32)
+    return np.ascontiguousarray(np.broadcast_to(sel[:, None, :], (rows, num_kv_heads, k)))
 
 
 def poison_tail_slots(kv: np.ndarray, block_table, seq_lens, kv_dtype: str) -> None:
