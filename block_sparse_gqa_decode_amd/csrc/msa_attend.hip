@@ -103,11 +103,12 @@ __device__ __forceinline__ void merge_splits(const AttendParams& p, int64_t row,
   float acc[8];
 #pragma unroll
   for (int k = 0; k < 8; ++k) acc[k] = 0.f;
-  if (M != -INFINITY) {
+  // A split that saw no key weighs 0 (its sum and O are 0); the weight is
+  // multiplied in rather than the split skipped, so a NaN sum still reaches L.
+  {
     for (int s = 0; s < p.splits; ++s) {
       const float ms = ml[2 * s];
-      if (ms == -INFINITY) continue;
-      const float e = fast_exp2(ms - M);
+      const float e = ms == -INFINITY ? 0.f : fast_exp2(ms - M);
       L += e * ml[2 * s + 1];
       const float* po = p.part_o + (row * p.splits + s) * kHeadDim + d0;
       const f32x4_t a = *reinterpret_cast<const f32x4_t*>(po);
@@ -385,10 +386,11 @@ pages_done:
       mw[w] = s_m[w][qr];
       M = fmaxf(M, mw[w]);
     }
+    // A wavefront that saw no key weighs 0 (multiplied in, not skipped, so a
+    // NaN sum from NaN cache entries propagates as the definition gives).
 #pragma unroll
     for (int w = 0; w < kWaves; ++w) {
-      if (mw[w] == -INFINITY) continue;
-      const float e = fast_exp2(mw[w] - M);
+      const float e = mw[w] == -INFINITY ? 0.f : fast_exp2(mw[w] - M);
       L += e * s_l[w][qr];
 #pragma unroll
       for (int k = 0; k < 8; ++k) acc[k] += e * s_o[w][qr][d0 + k];

@@ -374,12 +374,13 @@ __device__ __forceinline__ void attend_page(const PageRegs<kv_kind(kKv)>& r,
 }
 
 // bf16 store of one output row chunk: acc / L * v_scale, or exact zeros when
-// the row saw no key (L == 0).
+// the row saw no key (L == 0).  A NaN sum (a NaN logit from NaN cache
+// entries) is stored as NaN, as the definition gives, not as an empty row.
 // Branch-free (selects, not a branch), so a caller's loads that feed acc are
 // not sunk behind the test of L and stay issued together.
 __device__ __forceinline__ void store_row(uint16_t* dst, const float (&acc)[8], float L,
                                           float v_scale) {
-  const bool live = L > 0.f;
+  const bool live = L != 0.f;
   const float inv = live ? v_scale / L : 0.f;
   u32x4_t ov;
   ov.x = pack_bf16x2(acc[0] * inv, acc[1] * inv);

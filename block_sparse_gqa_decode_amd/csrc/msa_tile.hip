@@ -412,10 +412,10 @@ __global__ __launch_bounds__(kThreads) void multi_kernel(AttendParams p) {
     float acc[8];
 #pragma unroll
     for (int kk = 0; kk < 8; ++kk) acc[kk] = 0.f;
+    // An empty wavefront weighs 0 (multiplied in, so a NaN sum propagates).
 #pragma unroll
     for (int w2 = 0; w2 < kWaves; ++w2) {
-      if (mw[w2] == -INFINITY) continue;
-      const float e = fast_exp2(mw[w2] - M);
+      const float e = mw[w2] == -INFINITY ? 0.f : fast_exp2(mw[w2] - M);
       L += e * s_l[w2][qr];
 #pragma unroll
       for (int kk = 0; kk < 8; ++kk) acc[kk] += e * s_o[w2][qr][d0 + kk];

@@ -209,6 +209,9 @@ def test_mxfp4_attend_extreme_scale_codes(qd, qs, tile_rows):
     torch.cuda.synchronize()
     got = to_f64(d.out)
     bad = ~np.isfinite(got).all(axis=2)
+    diff = np.argwhere(bad != nan_ref)
+    print(f"[parity] non-finite (row, q head): gpu {np.argwhere(bad).tolist()} "
+          f"oracle {np.argwhere(nan_ref).tolist()} differ at {diff.tolist()}", flush=True)
     assert np.array_equal(bad, nan_ref)
     rows = [t for t in range(case.num_token_rows) if not nan_ref[t].any()]
     assert_parity(got[rows], ref[rows], what="extreme scale codes")
