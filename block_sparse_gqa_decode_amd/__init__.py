@@ -44,7 +44,7 @@ import torch
 __all__ = [
     "MsaError", "MsaInvalidArgument", "MsaUnsupported", "DecodePlan", "PlanCache",
     "msa_sparse_decode_plan", "msa_sparse_decode_run", "msa_sparse_decode_attend",
-    "msa_sparse_decode_merge", "msa_block_score_topk", "msa_sparse_prefill_plan",
+    "msa_sparse_decode_merge", "msa_sparse_decode_run_noalloc", "msa_block_score_topk", "msa_sparse_prefill_plan",
     "msa_sparse_prefill_run",
     "msa_topk_select", "msa_fp8_e4m3_to_bf16", "msa_fp8_e5m2_to_bf16", "msa_mxfp4_to_bf16",
     "msa_probe_read_runs",
@@ -53,7 +53,7 @@ __all__ = [
     "PAGE_SIZE", "HEAD_DIM", "ABI_VERSION",
 ]
 
-ABI_VERSION = 5
+ABI_VERSION = 6
 PAGE_SIZE = 128
 HEAD_DIM = 128
 KV_BF16 = 0
@@ -135,6 +135,9 @@ def load_library():
         "msa_sparse_decode_attend": (i32, [vp, vp, vp, pi64, i64, f32, f32, f32, vp, vp,
                                            vp, pi64, vp, f32, vp]),
         "msa_sparse_decode_merge": (i32, [vp, vp, f32, vp]),
+        "msa_sparse_decode_run_noalloc": (i32, [ctypes.POINTER(_Shape), ctypes.c_int, vp, vp,
+                                                pi64, i64, f32, f32, f32, vp, vp, vp, pi64, vp,
+                                                f32, vp]),
         "msa_sparse_prefill_plan": (i32, [ctypes.POINTER(_PrefillShape), ctypes.c_int,
                                           ctypes.POINTER(vp)]),
         "msa_sparse_prefill_run": (i32, [vp, vp, vp, pi64, i64, f32, f32, f32, vp, vp, vp,
@@ -435,6 +438,50 @@ def msa_sparse_decode_run(plan: DecodePlan, q: torch.Tensor, kv_cache: torch.Ten
         *head, float(q_scale), float(k_scale), float(v_scale), block_table.data_ptr(), seq_lens.data_ptr(),
         _ptr(topk), _strides3(topk), out.data_ptr(), float(sm_scale),
         _stream_handle(stream, q.device)))
+
+
+class _ShapeArgs:
+    """The plan attributes the run-argument checks read, for the call that
+    takes a static shape instead of a plan."""
+
+    prefill = False
+
+    def __init__(self, shape: "_Shape"):
+        self.batch = shape.batch
+        self.num_token_rows = shape.num_token_rows or shape.batch * shape.decode_query_len
+        self.num_q_heads = shape.num_q_heads
+        self.num_kv_heads = shape.num_kv_heads
+        self.page_table_stride = shape.page_table_stride
+        self.topk_blocks = shape.topk_blocks
+        self.dense = shape.topk_blocks == 0
+        self.kv_dtype = shape.kv_dtype
+        self.q_dtype = shape.q_dtype
+        self.handle = None
+
+
+def msa_sparse_decode_run_noalloc(q: torch.Tensor, kv_cache: torch.Tensor,
+                                  block_table: torch.Tensor, seq_lens: torch.Tensor,
+                                  topk: Optional[torch.Tensor], out: torch.Tensor, *,
+                                  decode_query_len: int, num_q_heads: int, num_kv_heads: int,
+                                  topk_blocks: int, kv_dtype: int, sm_scale: float,
+                                  num_token_rows: int = 0, num_splits: int = 0,
+                                  q_dtype: int = Q_BF16, tile_rows: int = 0,
+                                  k_scale: float = 1.0, v_scale: float = 1.0,
+                                  q_scale: float = 1.0, stream=None) -> None:
+    """``msa_sparse_decode_run`` without a plan, for callers that cannot
+    allocate device memory: the split partials live in the library's static
+    per-device scratch (calls that overlap on one GPU race).  The batch is
+    ``seq_lens``' length and the device is ``q``'s."""
+    shape = _Shape(int(seq_lens.shape[0]), decode_query_len, num_token_rows,
+                   int(block_table.stride(0)), num_q_heads, num_kv_heads, PAGE_SIZE, HEAD_DIM,
+                   topk_blocks, kv_dtype, num_splits, q_dtype, tile_rows)
+    args = _ShapeArgs(shape)
+    head = _run_args(args, q, kv_cache, block_table, seq_lens, topk, out)
+    dev = q.device.index if q.device.index is not None else torch.cuda.current_device()
+    _check(load_library().msa_sparse_decode_run_noalloc(
+        ctypes.byref(shape), int(dev), *head[1:], float(q_scale), float(k_scale),
+        float(v_scale), block_table.data_ptr(), seq_lens.data_ptr(), _ptr(topk),
+        _strides3(topk), out.data_ptr(), float(sm_scale), _stream_handle(stream, q.device)))
 
 
 def msa_sparse_decode_attend(plan: DecodePlan, q: torch.Tensor, kv_cache: torch.Tensor,

@@ -15,6 +15,7 @@
 #include <string>
 
 #include "msa_internal.h"
+#include "msa_plan.h"
 #include "msa_sparse_decode.h"
 
 namespace msa {
@@ -24,27 +25,11 @@ hipError_t launch_read_runs(const uint8_t* base, int64_t buffer_bytes, const int
                             int32_t num_workgroups, uint32_t* out, hipStream_t stream);
 }  // namespace msa
 
-struct msa_plan_s {
-  msa_decode_shape shape;   // for a prefill plan: decode_query_len = 0
-  bool prefill;
-  bool dense;               // every visible block (topk_blocks == 0)
-  int32_t tile_rows;        // 1: one row per workgroup; 2 / 4: multi-row tiles
-  int32_t num_units;        // workgroups per split
-  int device;
-  int32_t splits;
-  int32_t real_rows;
-  int32_t num_rows;
-  bool fused;               // splits merged inside the attend (2..4 splits, 1 row)
-  int64_t arena_bytes;
-  void* arena;
-  float* part_o;
-  float* part_ml;
-  int32_t* arrivals;        // per-unit arrival counters of the fused merge
-};
-
 namespace {
-
 thread_local std::string g_last_error;
+}  // namespace
+
+namespace msa {
 
 msa_status fail(msa_status s, const char* fmt, ...) {
   char buf[512];
@@ -60,6 +45,13 @@ msa_status ok() {
   g_last_error.clear();
   return MSA_OK;
 }
+
+}  // namespace msa
+
+using msa::fail;
+using msa::ok;
+
+namespace {
 
 msa_status device_fail(hipError_t e, const char* what) {
   return fail(MSA_ERR_DEVICE, "%s failed: %s", what, hipGetErrorString(e));
@@ -80,51 +72,6 @@ msa_status check_scales(float q_scale, float k_scale) {
     return fail(MSA_ERR_INVALID_ARG, "scales must be finite");
   if (!(q_scale > 0.f) || !(k_scale > 0.f))
     return fail(MSA_ERR_INVALID_ARG, "q_scale and k_scale must be positive");
-  return MSA_OK;
-}
-
-// Checks shared by the plan and the indexer entry point.
-msa_status check_common_shape(const msa_decode_shape* s) {
-  if (s == nullptr) return fail(MSA_ERR_INVALID_ARG, "shape is NULL");
-  if (s->batch < 1) return fail(MSA_ERR_INVALID_ARG, "batch must be >= 1 (got %d)", s->batch);
-  if (s->decode_query_len < 1 || s->decode_query_len > 32)
-    return fail(MSA_ERR_INVALID_ARG, "decode_query_len must be in 1..32 (got %d)",
-                s->decode_query_len);
-  const int64_t real = (int64_t)s->batch * s->decode_query_len;
-  if (real > (1 << 24))
-    return fail(MSA_ERR_UNSUPPORTED, "batch*decode_query_len = %lld exceeds 2^24",
-                (long long)real);
-  if (s->num_token_rows != 0 && s->num_token_rows < real)
-    return fail(MSA_ERR_INVALID_ARG,
-                "num_token_rows (%d) must be 0 or >= batch*decode_query_len (%lld)",
-                s->num_token_rows, (long long)real);
-  if (s->num_token_rows > (1 << 24))
-    return fail(MSA_ERR_UNSUPPORTED, "num_token_rows exceeds 2^24");
-  if (s->page_table_stride < 1)
-    return fail(MSA_ERR_INVALID_ARG, "page_table_stride must be >= 1 (got %d)",
-                s->page_table_stride);
-  if (s->num_q_heads < 1 || s->num_kv_heads < 1)
-    return fail(MSA_ERR_INVALID_ARG, "head counts must be >= 1 (got %d q, %d kv)",
-                s->num_q_heads, s->num_kv_heads);
-  if (s->num_q_heads % s->num_kv_heads != 0)
-    return fail(MSA_ERR_INVALID_ARG, "num_q_heads (%d) must be a multiple of num_kv_heads (%d)",
-                s->num_q_heads, s->num_kv_heads);
-  if (s->num_q_heads / s->num_kv_heads > msa::kMaxGroup)
-    return fail(MSA_ERR_UNSUPPORTED, "GQA group %d exceeds %d q heads per kv head",
-                s->num_q_heads / s->num_kv_heads, msa::kMaxGroup);
-  if (s->num_q_heads > 1024)
-    return fail(MSA_ERR_UNSUPPORTED, "num_q_heads exceeds 1024");
-  if (s->page_size != msa::kPage)
-    return fail(MSA_ERR_UNSUPPORTED, "page_size must be 128 (got %d)", s->page_size);
-  if (s->head_dim != msa::kHeadDim)
-    return fail(MSA_ERR_UNSUPPORTED, "head_dim must be 128 (got %d)", s->head_dim);
-  if (s->kv_dtype != MSA_KV_BF16 && s->kv_dtype != MSA_KV_FP8_E4M3 &&
-      s->kv_dtype != MSA_KV_FP8_E5M2 && s->kv_dtype != MSA_KV_MXFP4)
-    return fail(MSA_ERR_INVALID_ARG, "unknown kv_dtype %d", s->kv_dtype);
-  if (s->q_dtype != MSA_Q_BF16 && s->q_dtype != MSA_Q_FP8_E4M3)
-    return fail(MSA_ERR_INVALID_ARG, "unknown q_dtype %d", s->q_dtype);
-  if (s->q_dtype == MSA_Q_FP8_E4M3 && s->kv_dtype == MSA_KV_BF16)
-    return fail(MSA_ERR_UNSUPPORTED, "an fp8 q needs an fp8 (e4m3 or e5m2) or MXFP4 KV cache");
   return MSA_OK;
 }
 
@@ -181,25 +128,59 @@ int32_t choose_splits(const msa_decode_shape* s, int64_t units, bool dense) {
   return splits;
 }
 
-struct DeviceGuard {
-  int prev = -1;
-  bool changed = false;
-  hipError_t enter(int dev) {
-    hipError_t e = hipGetDevice(&prev);
-    if (e != hipSuccess) return e;
-    if (prev != dev) {
-      e = hipSetDevice(dev);
-      if (e != hipSuccess) return e;
-      changed = true;
-    }
-    return hipSuccess;
-  }
-  ~DeviceGuard() {
-    if (changed) (void)hipSetDevice(prev);
-  }
-};
-
 }  // namespace
+
+namespace msa {
+
+// Checks shared by the plan and the indexer entry point.
+msa_status check_common_shape(const msa_decode_shape* s) {
+  if (s == nullptr) return fail(MSA_ERR_INVALID_ARG, "shape is NULL");
+  if (s->batch < 1) return fail(MSA_ERR_INVALID_ARG, "batch must be >= 1 (got %d)", s->batch);
+  if (s->decode_query_len < 1 || s->decode_query_len > 32)
+    return fail(MSA_ERR_INVALID_ARG, "decode_query_len must be in 1..32 (got %d)",
+                s->decode_query_len);
+  const int64_t real = (int64_t)s->batch * s->decode_query_len;
+  if (real > (1 << 24))
+    return fail(MSA_ERR_UNSUPPORTED, "batch*decode_query_len = %lld exceeds 2^24",
+                (long long)real);
+  if (s->num_token_rows != 0 && s->num_token_rows < real)
+    return fail(MSA_ERR_INVALID_ARG,
+                "num_token_rows (%d) must be 0 or >= batch*decode_query_len (%lld)",
+                s->num_token_rows, (long long)real);
+  if (s->num_token_rows > (1 << 24))
+    return fail(MSA_ERR_UNSUPPORTED, "num_token_rows exceeds 2^24");
+  if (s->page_table_stride < 1)
+    return fail(MSA_ERR_INVALID_ARG, "page_table_stride must be >= 1 (got %d)",
+                s->page_table_stride);
+  if (s->num_q_heads < 1 || s->num_kv_heads < 1)
+    return fail(MSA_ERR_INVALID_ARG, "head counts must be >= 1 (got %d q, %d kv)",
+                s->num_q_heads, s->num_kv_heads);
+  if (s->num_q_heads % s->num_kv_heads != 0)
+    return fail(MSA_ERR_INVALID_ARG, "num_q_heads (%d) must be a multiple of num_kv_heads (%d)",
+                s->num_q_heads, s->num_kv_heads);
+  if (s->num_q_heads / s->num_kv_heads > msa::kMaxGroup)
+    return fail(MSA_ERR_UNSUPPORTED, "GQA group %d exceeds %d q heads per kv head",
+                s->num_q_heads / s->num_kv_heads, msa::kMaxGroup);
+  if (s->num_q_heads > 1024)
+    return fail(MSA_ERR_UNSUPPORTED, "num_q_heads exceeds 1024");
+  if (s->page_size != msa::kPage)
+    return fail(MSA_ERR_UNSUPPORTED, "page_size must be 128 (got %d)", s->page_size);
+  if (s->head_dim != msa::kHeadDim)
+    return fail(MSA_ERR_UNSUPPORTED, "head_dim must be 128 (got %d)", s->head_dim);
+  if (s->kv_dtype != MSA_KV_BF16 && s->kv_dtype != MSA_KV_FP8_E4M3 &&
+      s->kv_dtype != MSA_KV_FP8_E5M2 && s->kv_dtype != MSA_KV_MXFP4)
+    return fail(MSA_ERR_INVALID_ARG, "unknown kv_dtype %d", s->kv_dtype);
+  if (s->q_dtype != MSA_Q_BF16 && s->q_dtype != MSA_Q_FP8_E4M3)
+    return fail(MSA_ERR_INVALID_ARG, "unknown q_dtype %d", s->q_dtype);
+  if (s->q_dtype == MSA_Q_FP8_E4M3 && s->kv_dtype == MSA_KV_BF16)
+    return fail(MSA_ERR_UNSUPPORTED, "an fp8 q needs an fp8 (e4m3 or e5m2) or MXFP4 KV cache");
+  return MSA_OK;
+}
+
+}  // namespace msa
+
+using msa::check_common_shape;
+using msa::DeviceGuard;
 
 extern "C" {
 
@@ -284,8 +265,12 @@ msa_status msa_sparse_prefill_plan(const msa_prefill_shape* pshape, int device,
   return make_plan(&s, true, keep_rows, device, plan_out);
 }
 
-static msa_status make_plan(const msa_decode_shape* shape, bool prefill, int32_t real_rows,
-                            int device, msa_plan* plan_out) {
+}  // extern "C"
+
+namespace msa {
+
+msa_status plan_config(const msa_decode_shape* shape, bool prefill, int32_t real_rows,
+                       int device, bool allow_fused, msa_plan_s* plan) {
   const bool dense = shape->topk_blocks == 0;
   if (dense && prefill)
     return fail(MSA_ERR_UNSUPPORTED, "a prefill plan needs top-k selections (topk_blocks >= 1)");
@@ -316,11 +301,11 @@ static msa_status make_plan(const msa_decode_shape* shape, bool prefill, int32_t
   const int64_t ml_bytes = splits > 1 ? (int64_t)num_rows * per_row * 2 * 4 : 0;
   // The single-row attend merges 2..4 splits itself (the last split of a unit
   // to finish combines them); other plans launch the merge kernel.
-  const bool fused = tile_rows == 1 && splits > 1 && splits <= msa::kMaxFusedSplits;
+  const bool fused =
+      allow_fused && tile_rows == 1 && splits > 1 && splits <= msa::kMaxFusedSplits;
   const int64_t arrival_bytes = fused ? (units * 4 + 255) / 256 * 256 : 0;
 
-  msa_plan plan = new (std::nothrow) msa_plan_s();
-  if (plan == nullptr) return fail(MSA_ERR_OUT_OF_MEMORY, "host allocation failed");
+  *plan = msa_plan_s{};
   plan->shape = *shape;
   plan->prefill = prefill;
   plan->dense = dense;
@@ -334,11 +319,23 @@ static msa_status make_plan(const msa_decode_shape* shape, bool prefill, int32_t
   plan->real_rows = real_rows;
   plan->num_rows = num_rows;
   plan->fused = fused;
+  plan->arrival_bytes = arrival_bytes;
+  plan->o_bytes = o_bytes;
   plan->arena_bytes = arrival_bytes + o_bytes + ml_bytes;
-  plan->arena = nullptr;
-  plan->part_o = nullptr;
-  plan->part_ml = nullptr;
-  plan->arrivals = nullptr;
+  return ok();
+}
+
+}  // namespace msa
+
+extern "C" {
+
+static msa_status make_plan(const msa_decode_shape* shape, bool prefill, int32_t real_rows,
+                            int device, msa_plan* plan_out) {
+  msa_plan_s cfg;
+  msa_status st = msa::plan_config(shape, prefill, real_rows, device, true, &cfg);
+  if (st != MSA_OK) return st;
+  msa_plan plan = new (std::nothrow) msa_plan_s(cfg);
+  if (plan == nullptr) return fail(MSA_ERR_OUT_OF_MEMORY, "host allocation failed");
   if (plan->arena_bytes > 0) {
     // The arena is the plan's only device state; a plan without one makes no
     // HIP call here.
@@ -350,27 +347,28 @@ static msa_status make_plan(const msa_decode_shape* shape, bool prefill, int32_t
     }
     e = hipMalloc(&plan->arena, (size_t)plan->arena_bytes);
     if (e != hipSuccess) {
+      const long long bytes = (long long)plan->arena_bytes;
       delete plan;
       if (e == hipErrorOutOfMemory || e == hipErrorMemoryAllocation)
-        return fail(MSA_ERR_OUT_OF_MEMORY, "partial arena of %lld bytes: %s",
-                    (long long)plan->arena_bytes, hipGetErrorString(e));
+        return fail(MSA_ERR_OUT_OF_MEMORY, "partial arena of %lld bytes: %s", bytes,
+                    hipGetErrorString(e));
       return device_fail(e, "hipMalloc");
     }
     char* base = static_cast<char*>(plan->arena);
-    if (fused) {
+    if (plan->fused) {
       // Counters start at zero; every fused run leaves them at zero.
       plan->arrivals = reinterpret_cast<int32_t*>(base);
-      e = hipMemset(plan->arrivals, 0, (size_t)arrival_bytes);
+      e = hipMemset(plan->arrivals, 0, (size_t)plan->arrival_bytes);
       if (e == hipSuccess) e = hipDeviceSynchronize();
       if (e != hipSuccess) {
         (void)hipFree(plan->arena);
         delete plan;
         return device_fail(e, "arrival counter initialisation");
       }
-      base += arrival_bytes;
+      base += plan->arrival_bytes;
     }
     plan->part_o = reinterpret_cast<float*>(base);
-    plan->part_ml = reinterpret_cast<float*>(base + o_bytes);
+    plan->part_ml = reinterpret_cast<float*>(base + plan->o_bytes);
   }
   *plan_out = plan;
   return ok();
@@ -400,12 +398,16 @@ msa_status msa_sparse_decode_plan_info(msa_plan plan, int32_t* num_splits, int64
 
 // seq_lens is the decode position source; cu_q / ctx the prefill one (a
 // prefill plan passes seq_lens = NULL).
-static msa_status run_phases(msa_plan plan, const void* q, const void* kv_cache,
-                             const int64_t kv_strides[4], int64_t num_kv_blocks, float q_scale,
-                             float k_scale, float v_scale, const int32_t* block_table,
-                             const int32_t* seq_lens, const int32_t* cu_q, const int32_t* ctx,
-                             const int32_t* topk, const int64_t topk_strides[3], void* out,
-                             float sm_scale, void* stream, bool merge) {
+}  // extern "C"
+
+namespace msa {
+
+msa_status run_plan(const msa_plan_s* plan, const void* q, const void* kv_cache,
+                    const int64_t kv_strides[4], int64_t num_kv_blocks, float q_scale,
+                    float k_scale, float v_scale, const int32_t* block_table,
+                    const int32_t* seq_lens, const int32_t* cu_q, const int32_t* ctx,
+                    const int32_t* topk, const int64_t topk_strides[3], void* out,
+                    float sm_scale, void* stream, bool merge) {
   if (plan == nullptr) return fail(MSA_ERR_INVALID_ARG, "plan is NULL");
   const msa_decode_shape& s = plan->shape;
   if (q == nullptr || out == nullptr) return fail(MSA_ERR_INVALID_ARG, "q and out must be non-NULL");
@@ -491,6 +493,10 @@ static msa_status run_phases(msa_plan plan, const void* q, const void* kv_cache,
   return ok();
 }
 
+}  // namespace msa
+
+extern "C" {
+
 msa_status msa_sparse_decode_run(msa_plan plan, const void* q, const void* kv_cache,
                                  const int64_t kv_strides[4], int64_t num_kv_blocks,
                                  float q_scale, float k_scale, float v_scale,
@@ -499,7 +505,7 @@ msa_status msa_sparse_decode_run(msa_plan plan, const void* q, const void* kv_ca
                                  float sm_scale, void* stream) {
   if (plan != nullptr && plan->prefill)
     return fail(MSA_ERR_INVALID_ARG, "a prefill plan runs through msa_sparse_prefill_run");
-  return run_phases(plan, q, kv_cache, kv_strides, num_kv_blocks, q_scale, k_scale, v_scale,
+  return msa::run_plan(plan, q, kv_cache, kv_strides, num_kv_blocks, q_scale, k_scale, v_scale,
                     block_table, seq_lens, nullptr, nullptr, topk, topk_strides, out, sm_scale,
                     stream, true);
 }
@@ -513,7 +519,7 @@ msa_status msa_sparse_prefill_run(msa_plan plan, const void* q, const void* kv_c
                                   void* stream) {
   if (plan != nullptr && !plan->prefill)
     return fail(MSA_ERR_INVALID_ARG, "a decode plan runs through msa_sparse_decode_run");
-  return run_phases(plan, q, kv_cache, kv_strides, num_kv_blocks, q_scale, k_scale, v_scale,
+  return msa::run_plan(plan, q, kv_cache, kv_strides, num_kv_blocks, q_scale, k_scale, v_scale,
                     block_table, nullptr, cu_seqlens_q, context_lens, topk, topk_strides, out,
                     sm_scale, stream, true);
 }
@@ -526,7 +532,7 @@ msa_status msa_sparse_decode_attend(msa_plan plan, const void* q, const void* kv
                                     void* out, float sm_scale, void* stream) {
   if (plan != nullptr && plan->prefill)
     return fail(MSA_ERR_INVALID_ARG, "a prefill plan runs through msa_sparse_prefill_run");
-  return run_phases(plan, q, kv_cache, kv_strides, num_kv_blocks, q_scale, k_scale, v_scale,
+  return msa::run_plan(plan, q, kv_cache, kv_strides, num_kv_blocks, q_scale, k_scale, v_scale,
                     block_table, seq_lens, nullptr, nullptr, topk, topk_strides, out, sm_scale,
                     stream, false);
 }

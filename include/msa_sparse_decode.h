@@ -53,7 +53,7 @@
 extern "C" {
 #endif
 
-#define MSA_ABI_VERSION 5
+#define MSA_ABI_VERSION 6
 
 typedef enum msa_status {
   MSA_OK = 0,
@@ -346,6 +346,34 @@ msa_status msa_fp8_e5m2_to_bf16(const void* in, void* out, int64_t n, void* stre
 msa_status msa_mxfp4_to_bf16(const void* kv_cache, const int64_t kv_strides[4],
                              int64_t num_kv_blocks, int32_t num_kv_heads, void* out,
                              void* stream);
+
+/* Bytes of the static device scratch msa_sparse_decode_run_noalloc uses. */
+#define MSA_NOALLOC_SCRATCH_BYTES (64LL << 20)
+
+/* For callers that cannot allocate device memory: code under HIP graph
+ * capture, tight serving loops, harnesses that forbid allocation.  The same
+ * decode step as msa_sparse_decode_run (same arguments, same result) without a
+ * plan: `shape` and `device` are what msa_sparse_decode_plan would take, and
+ * the launch is configured the same way on the host, except that several
+ * splits are always merged by a separate merge launch.  The fp32 split
+ * partials go to a static device array of MSA_NOALLOC_SCRATCH_BYTES (64 MiB)
+ * that the library holds on every device it runs on until the process ends;
+ * the call allocates nothing and frees nothing.  A shape whose partials need
+ * more (num_token_rows * num_q_heads * splits * 520 bytes when splits > 1)
+ * returns MSA_ERR_UNSUPPORTED with a message; pass fewer num_splits, or use a
+ * plan.  Every call on one device shares that device's array, so calls that
+ * overlap on one GPU (two streams or two host threads) race and give wrong
+ * results: serialize them.  The first call on each device looks up the
+ * array's address there (hipGetSymbolAddress, a runtime query, no
+ * allocation); make it outside graph capture.  Errors as for
+ * msa_sparse_decode_plan and msa_sparse_decode_run. */
+msa_status msa_sparse_decode_run_noalloc(const msa_decode_shape* shape, int device,
+                                         const void* q, const void* kv_cache,
+                                         const int64_t kv_strides[4], int64_t num_kv_blocks,
+                                         float q_scale, float k_scale, float v_scale,
+                                         const int32_t* block_table, const int32_t* seq_lens,
+                                         const int32_t* topk, const int64_t topk_strides[3],
+                                         void* out, float sm_scale, void* stream);
 
 /* Message for the last non-OK status returned on this thread ("" if none). */
 const char* msa_last_error(void);

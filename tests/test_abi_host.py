@@ -600,3 +600,21 @@ def test_read_runs_probe_rejects_bad_arguments(lib):
     assert call(wgs=1 << 25) == msa.MSA_ERR_UNSUPPORTED
     # No workgroups: nothing to launch, so no HIP call and no error.
     assert call(wgs=0, base=None) == msa.MSA_OK
+
+
+def test_noalloc_rejects_partials_beyond_its_scratch(lib):
+    """The no-allocation entry point checks the static scratch size on the
+    host, before any HIP call: 4096 rows x 64 q heads x 16 splits of partials
+    (about 2.2 GB) exceed its 64 MiB."""
+    s = shape(batch=128, decode_query_len=32, num_q_heads=64, num_kv_heads=4, num_splits=16)
+    strides = (ctypes.c_int64 * 4)(4 * 128 * 256, 128 * 256, 256, 1)
+    tk = (ctypes.c_int64 * 3)(64, 16, 1)
+    st = lib.msa_sparse_decode_run_noalloc(ctypes.byref(s), 0, None, None, strides, 1, 1.0,
+                                           1.0, 1.0, None, None, None, tk, None, 0.1, None)
+    assert st == -2
+    msg = lib.msa_last_error().decode()
+    assert "static scratch" in msg and "67108864" in msg
+    bad = shape(decode_query_len=33)
+    st = lib.msa_sparse_decode_run_noalloc(ctypes.byref(bad), 0, None, None, strides, 1, 1.0,
+                                           1.0, 1.0, None, None, None, tk, None, 0.1, None)
+    assert st == -1 and "decode_query_len" in lib.msa_last_error().decode()
