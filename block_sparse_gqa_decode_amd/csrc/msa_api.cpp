@@ -204,8 +204,11 @@ msa_status msa_sparse_decode_plan(const msa_decode_shape* shape, int device, msa
 static msa_status choose_tiles(const msa_decode_shape* s, bool prefill, bool dense,
                                int32_t num_rows, int32_t* tile_rows, int64_t* units) {
   int32_t tr = s->tile_rows;
-  if (tr != 0 && tr != 1 && tr != 2 && tr != 4)
-    return fail(MSA_ERR_INVALID_ARG, "tile_rows must be 0 (auto), 1, 2 or 4 (got %d)", tr);
+  if (tr != 0 && tr != 1 && tr != 2 && tr != 4 && tr != 8)
+    return fail(MSA_ERR_INVALID_ARG, "tile_rows must be 0 (auto), 1, 2, 4 or 8 (got %d)", tr);
+  const bool kv8 = s->kv_dtype == MSA_KV_FP8_E4M3 || s->kv_dtype == MSA_KV_FP8_E5M2;
+  if (tr == 8 && !kv8)
+    return fail(MSA_ERR_UNSUPPORTED, "8-row tiles need an 8-bit (fp8 e4m3 or e5m2) KV cache");
   if (tr == 0) {
     // Measured on one MI355X: rows that share many pages (long decode query
     // lengths, prefill chunks) gain from 2-row tiles; dense decode, where every
@@ -483,8 +486,14 @@ msa_status run_plan(const msa_plan_s* plan, const void* q, const void* kv_cache,
   hipError_t e = guard.enter(plan->device);
   if (e != hipSuccess) return device_fail(e, "hipSetDevice");
   hipStream_t st_ = static_cast<hipStream_t>(stream);
-  e = plan->tile_rows > 1 ? msa::launch_tile(p, s.kv_dtype, s.q_dtype, plan->tile_rows, st_)
-                          : msa::launch_attend(p, s.kv_dtype, s.q_dtype, st_);
+  // 8-row tiles (8-bit caches only) stage pages through LDS; 2- and 4-row
+  // tiles keep them in registers.
+  if (plan->tile_rows == 8)
+    e = msa::launch_union(p, s.kv_dtype, s.q_dtype, plan->tile_rows, st_);
+  else if (plan->tile_rows > 1)
+    e = msa::launch_tile(p, s.kv_dtype, s.q_dtype, plan->tile_rows, st_);
+  else
+    e = msa::launch_attend(p, s.kv_dtype, s.q_dtype, st_);
   if (e != hipSuccess) return device_fail(e, "attend launch");
   if (merge && plan->splits > 1 && !plan->fused) {
     e = msa::launch_merge(p, st_);

@@ -129,7 +129,6 @@ __device__ __forceinline__ void merge_splits(const AttendParams& p, int64_t row,
 // No workgroup waits for another and no cache is written back or invalidated
 // (a device-scope release fence writes back the whole L2 on this part).
 constexpr int kSysCoherent = 0x11;        // buffer cache policy: sc0 | sc1
-constexpr int kRsrcWord3 = 0x00020000;    // raw buffer descriptor, gfx9 family
 constexpr int kWaitVmem = 0x0F70;         // s_waitcnt vmcnt(0)
 
 template <int kS>
@@ -314,7 +313,8 @@ __global__ __launch_bounds__(kThreads) void attend_kernel(AttendParams p) {
   const int kbase = wave * kKeysPerWave;
   const uint8_t* head_base = p.kv + h * p.kv_s1;
   const uint32_t row_stride = (uint32_t)p.kv_s2;
-  const LaneRows lr = lane_rows<kKind>(kbase, n, g);
+  LaneRows lr = lane_rows<kKind>(kbase, n, g);
+  lane_offsets(lr, row_stride);
 
   float m_run = -INFINITY;
   float l_part = 0.f;
@@ -337,7 +337,7 @@ __global__ __launch_bounds__(kThreads) void attend_kernel(AttendParams p) {
       const int pi = min(lo + j, hi - 1);
       const int pg = __builtin_amdgcn_readfirstlane(s_page[pi]);
       bnv[j] = __builtin_amdgcn_readfirstlane(s_nvis[pi]);
-      load_page<kKind>(buf[j], head_base + (int64_t)pg * p.kv_s0, row_stride, bnv[j] - 1, lr);
+      load_page_rows<kKind>(buf[j], head_base + (int64_t)pg * p.kv_s0, row_stride, bnv[j], lr);
     }
     for (int i = lo;; i += kDepth) {
 #pragma unroll
@@ -348,8 +348,8 @@ __global__ __launch_bounds__(kThreads) void attend_kernel(AttendParams p) {
         const int nx = (j + kDepth - 1) % kDepth;
         const int pg = __builtin_amdgcn_readfirstlane(s_page[pn]);
         bnv[nx] = __builtin_amdgcn_readfirstlane(s_nvis[pn]);
-        load_page<kKind>(buf[nx], head_base + (int64_t)pg * p.kv_s0, row_stride, bnv[nx] - 1,
-                         lr);
+        load_page_rows<kKind>(buf[nx], head_base + (int64_t)pg * p.kv_s0, row_stride, bnv[nx],
+                              lr);
         const int nv = bnv[j];
         if (kbase < nv)
           attend_page<kKv, kQ>(buf[j], qf, lr, kbase, nv, g, p.scale_log2, m_run, l_part, o);

@@ -113,6 +113,10 @@ hipError_t launch_merge(const AttendParams& p, hipStream_t stream);
 // Multi-row tiles of tile_rows (2 or 4) token rows; p.num_units = tiles * hkv.
 hipError_t launch_tile(const AttendParams& p, int kv_fmt, int q_fmt, int tile_rows,
                        hipStream_t stream);
+// Row tiles of 8 token rows over 8-bit KV (e4m3 / e5m2), pages staged
+// through an LDS ring; p.num_units = tiles * hkv.
+hipError_t launch_union(const AttendParams& p, int kv_fmt, int q_fmt, int tile_rows,
+                        hipStream_t stream);
 hipError_t launch_score(const ScoreParams& p, int kv_fmt, int q_fmt, hipStream_t stream);
 hipError_t launch_select(const SelectParams& p, hipStream_t stream);
 // fmt: kKvE4m3 or kKvE5m2

@@ -72,6 +72,10 @@ struct LaneRows {
   uint32_t cv;  // first V byte of the lane's run
   uint32_t ksh; // 8 * (K block of head dims 32g..32g+31) = 8g
   uint32_t vsh; // 8 * (V block of head dims 8n..8n+7) = 8 * (n / 4)
+  // 16- and 8-bit pages: the byte offsets of the lane's K runs and V runs
+  // within a page-head, row * row_stride + column (set by lane_offsets).
+  uint32_t ok[2];
+  uint32_t ov[8];
 };
 
 template <int kKind>
@@ -86,6 +90,15 @@ __device__ __forceinline__ LaneRows lane_rows(int kbase, int n, int g) {
   lr.ksh = 8u * g;
   lr.vsh = 8u * (n >> 2);
   return lr;
+}
+
+// The per-lane byte offsets of the 16- and 8-bit page loads, fixed for a
+// launch (row strides < 2^24, so 24-bit multiplies).
+__device__ __forceinline__ void lane_offsets(LaneRows& lr, uint32_t row_stride) {
+#pragma unroll
+  for (int tau = 0; tau < 2; ++tau) lr.ok[tau] = __umul24((uint32_t)lr.rk[tau], row_stride) + lr.ck;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) lr.ov[j] = __umul24((uint32_t)lr.rv[j], row_stride) + lr.cv;
 }
 
 // 4-bit head slot: 128 rows x 64 data bytes, then 128 rows x 4 scale bytes.
@@ -138,6 +151,50 @@ __device__ __forceinline__ void load_page(PageRegs<kKind>& r, const uint8_t* pag
       } else {
         r.v[j] = *reinterpret_cast<const u32x4_t*>(page + off);
       }
+    }
+  }
+}
+
+constexpr int kRsrcWord3 = 0x00020000;    // raw buffer descriptor, gfx9 family
+
+// Loads of one page into registers through a buffer descriptor whose size is
+// the page-head's first `nvis` rows: the hardware returns zeros for every
+// lane whose row is past them, so stale rows are never read and no lane
+// offset is recomputed per page (16- and 8-bit pages; offsets from
+// lane_offsets).  4-bit pages, whose data and scales are separate runs, take
+// the clamped loads of load_page.
+template <int kKind>
+__device__ __forceinline__ void load_page_rows(PageRegs<kKind>& r, const uint8_t* page,
+                                               uint32_t row_stride, int nvis,
+                                               const LaneRows& lr) {
+  if constexpr (kKind == 2) {
+    load_page<2>(r, page, row_stride, max(nvis, 1) - 1, lr);
+  } else {
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint8_t*>(page), (short)0, (int)((uint32_t)nvis * row_stride), kRsrcWord3);
+#pragma unroll
+    for (int tau = 0; tau < 2; ++tau) {
+      if constexpr (kKind == 1) {
+        r.k[tau][0] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(
+                                                      rs, lr.ok[tau], 0, 0));
+        r.k[tau][1] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(
+                                                      rs, lr.ok[tau] + 64, 0, 0));
+      } else {
+#pragma unroll
+        for (int c = 0; c < 4; ++c)
+          r.k[tau][c] = __builtin_bit_cast(
+              u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(
+                           rs, lr.ok[tau] + 16 * (c & 1) + 128 * (c >> 1), 0, 0));
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      if constexpr (kKind == 1)
+        r.v[j] = __builtin_bit_cast(u32x2_t,
+                                    __builtin_amdgcn_raw_buffer_load_b64(rs, lr.ov[j], 0, 0));
+      else
+        r.v[j] = __builtin_bit_cast(u32x4_t,
+                                    __builtin_amdgcn_raw_buffer_load_b128(rs, lr.ov[j], 0, 0));
     }
   }
 }

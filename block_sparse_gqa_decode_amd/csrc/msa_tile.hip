@@ -135,58 +135,78 @@ __global__ __launch_bounds__(kThreads) void multi_kernel(AttendParams p) {
   const int h = unit - tile * p.hkv;
   const int head0 = h * p.group;
 
-  if (tid < kM) {
-    const int t = tile_row(p, tile, tid, kM);
-    int r = -1, pos = -1;
-    if (t >= 0 && t < p.num_rows) {
-      int rr = 0, pp = 0;
-      if (locate_token(p, t, rr, pp)) {
-        r = rr;
-        pos = pp;
-      }
-    }
-    s_row_r[tid] = r;
-    s_row_pos[tid] = pos;
+  // Prologue.  Everything the page list needs is requested before anything
+  // waits: each (row, slot) thread's top-k entry and its row's length, and
+  // the q staging loads (q of every row in range is staged; rows found dead
+  // below never read it).  Then the block-table entries of the visible
+  // slots; then the list is built in LDS.  Two dependent memory round trips
+  // before the first page's loads, where looking the rows up first, then
+  // staging q, then reading the top-k entries took four.
+  const int k = p.topk_k;
+  const int ew = tid / kMaxTopk;           // this thread's (row, slot) entry
+  const int ej = tid - ew * kMaxTopk;
+  const bool has_entry = !p.tile_dense && ew < kM;
+  const int et = has_entry ? tile_row(p, tile, ew, kM) : -1;
+  int b_raw = -1;
+  if (has_entry && ej < k && et >= 0 && et < p.num_rows)
+    b_raw = p.topk[et * p.tk_s0 + h * p.tk_s1 + ej * p.tk_s2];
+  constexpr int kQChunks = kQBytes / 16;
+  constexpr int kQLoads = (kM * 16 * kQChunks + kThreads - 1) / kThreads;
+  u32x4_t qv[kQInLds ? kQLoads : 1];
+#pragma unroll
+  for (int i = 0; i < (kQInLds ? kQLoads : 0); ++i) {
+    const int c = tid + i * kThreads;
+    const int w = c / (16 * kQChunks);
+    const int rem = c - w * (16 * kQChunks);
+    const int qh = rem / kQChunks;
+    const int off = (rem - qh * kQChunks) * 16;
+    const int t = w < kM ? tile_row(p, tile, w, kM) : -1;
+    qv[i] = u32x4_t{0u, 0u, 0u, 0u};
+    if (t >= 0 && t < p.num_rows && qh < p.group)
+      qv[i] = *reinterpret_cast<const u32x4_t*>(p.q + ((int64_t)t * p.hq + head0 + qh) *
+                                                          kQBytes + off);
   }
-  __syncthreads();
-  // Stage q (zeros for dead rows and q heads >= G); the barriers of the page
-  // list staging below order these writes before the first read.
-  for (int c = tid; kQInLds && c < kM * 16 * (kQBytes / 16); c += kThreads) {
-    const int w = c / (16 * (kQBytes / 16));
-    const int rem = c - w * (16 * (kQBytes / 16));
-    const int qh = rem / (kQBytes / 16);
-    const int off = (rem - qh * (kQBytes / 16)) * 16;
-    u32x4_t v = u32x4_t{0u, 0u, 0u, 0u};
-    if (s_row_r[w] >= 0 && qh < p.group) {
-      const int64_t q_row = (int64_t)tile_row(p, tile, w, kM) * p.hq + head0 + qh;
-      v = *reinterpret_cast<const u32x4_t*>(p.q + q_row * kQBytes + off);
+  // The row of this thread's entry (sparse), or of thread w < kM (dense).
+  const int lw = p.tile_dense ? tid : ew;
+  const int lt = p.tile_dense ? (tid < kM ? tile_row(p, tile, tid, kM) : -1) : et;
+  int row_r = -1, row_pos = -1;
+  if (lt >= 0 && lt < p.num_rows && lw < kM) {
+    int rr = 0, pp = 0;
+    if (locate_token(p, lt, rr, pp)) {
+      row_r = rr;
+      row_pos = pp;
     }
-    *reinterpret_cast<u32x4_t*>(&s_q[kQInLds ? w : 0][qh][off]) = v;
+  }
+  if (lw < kM && (p.tile_dense || ej == 0)) {
+    s_row_r[lw] = row_r;
+    s_row_pos[lw] = row_pos;
+  }
+#pragma unroll
+  for (int i = 0; i < (kQInLds ? kQLoads : 0); ++i) {
+    const int c = tid + i * kThreads;
+    if (c < kM * 16 * kQChunks) {
+      const int w = c / (16 * kQChunks);
+      const int rem = c - w * (16 * kQChunks);
+      const int qh = rem / kQChunks;
+      const int off = (rem - qh * kQChunks) * 16;
+      *reinterpret_cast<u32x4_t*>(&s_q[kQInLds ? w : 0][qh][off]) = qv[i];
+    }
   }
 
   int npages;
   int dense_r = -1, dense_pos_max = -1;
   if (!p.tile_dense) {
-    // Union of the rows' selections.  Thread (row w, slot j) = (tid / 64,
-    // tid % 64) stages its entry (page -1 for an empty, invalid or padding
-    // slot); row w's slots sit at w * kMaxTopk.
-    const int k = p.topk_k;
+    // Union of the rows' selections: thread (row w, slot j) stages its entry
+    // (page -1 for an empty, invalid or padding slot) at w * kMaxTopk + j.
     const int kq = (k + 3) & ~3;  // slots scanned per row (the pad is -1)
     int page = -1, nv = 0;
-    if (tid < kM * kMaxTopk) {
-      const int w = tid / kMaxTopk;
-      const int j = tid - w * kMaxTopk;
-      const int r = s_row_r[w];
-      const int pos = s_row_pos[w];
-      if (j < k && r >= 0) {
-        const int t = tile_row(p, tile, w, kM);
-        const int b = p.topk[t * p.tk_s0 + h * p.tk_s1 + j * p.tk_s2];
-        if (b >= 0 && b < p.bt_stride && (int64_t)b * kPage <= pos) {
-          const int pg = p.block_table[(int64_t)r * p.bt_stride + b];
-          if (pg >= 0 && pg < p.num_kv_blocks) {
-            page = pg;
-            nv = min(kPage, pos - b * kPage + 1);
-          }
+    if (has_entry) {
+      const int b = b_raw;
+      if (row_r >= 0 && (b >= 0) & (b < p.bt_stride) & ((int64_t)b * kPage <= row_pos)) {
+        const int pg = p.block_table[(int64_t)row_r * p.bt_stride + b];
+        if (pg >= 0 && pg < p.num_kv_blocks) {
+          page = pg;
+          nv = min(kPage, row_pos - b * kPage + 1);
         }
       }
       s_ent_page[tid] = page;
@@ -234,6 +254,7 @@ __global__ __launch_bounds__(kThreads) void multi_kernel(AttendParams p) {
     __syncthreads();
     npages = s_nlist;
   } else {
+    __syncthreads();  // the rows' lookups are in s_row_r / s_row_pos
     dense_r = s_row_r[0];
 #pragma unroll
     for (int w = 0; w < kM; ++w) dense_pos_max = max(dense_pos_max, s_row_pos[w]);

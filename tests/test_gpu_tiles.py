@@ -1,8 +1,10 @@
-"""GPU parity of the multi-row tile kernel and of dense decode.
+"""GPU parity of the multi-row tile kernels and of dense decode.
 
-The tile kernel (several token rows per workgroup, each page shared by its
-rows read once) must give what the oracle gives for any tile size: the
-randomized decode cases and the format cases are rerun on 2- and 4-row tiles,
+The tile kernels (several token rows per workgroup, each page shared by its
+rows read once: register-staged pages for 2-row tiles and 16-bit or 4-bit
+caches, LDS-staged pages for 4- and 8-row tiles over 8-bit caches) must give
+what the oracle gives for any tile size: the randomized decode cases and the
+format cases are rerun on 2-, 4- and 8-row tiles,
 the single-row kernel is checked on a long decode query length, and dense
 decode (every visible block, no top-k) is checked on the test page's shapes,
 randomized shapes (query lengths 1..8, padding rows, NHD, every split count,
@@ -15,6 +17,7 @@ import torch
 
 from workloads import gen
 
+import block_sparse_gqa_decode_amd as msa
 from gpu_helpers import DevCase, assert_parity, oracle_attend, oracle_dense, to_f64
 
 import test_gpu_parity as base
@@ -26,7 +29,7 @@ def _banner(msg):
     print(f"[case] {msg}", flush=True)
 
 
-@pytest.mark.parametrize("tile_rows", [2, 4])
+@pytest.mark.parametrize("tile_rows", [2, 4, 8])
 @pytest.mark.parametrize("seed,batch,dql,hq,hkv,k,lo,hi,kvd,pad,neg,splits,layout",
                          base.RANDOM_CASES)
 def test_random_cases_on_tiles(tile_rows, seed, batch, dql, hq, hkv, k, lo, hi, kvd, pad, neg,
@@ -36,6 +39,10 @@ def test_random_cases_on_tiles(tile_rows, seed, batch, dql, hq, hkv, k, lo, hi, 
     case = gen.make_random_case(seed, batch, dql, hq, hkv, k, lo, hi, kv_dtype=kvd,
                                 pad_rows=pad, neg_frac=neg)
     d = DevCase(case, layout=layout)
+    if tile_rows == 8 and kvd == gen.KV_BF16:
+        with pytest.raises(msa.MsaUnsupported, match="8-row tiles"):
+            d.plan(splits, tile_rows=tile_rows)
+        return
     plan = d.plan(splits, tile_rows=tile_rows)
     assert plan.tile_rows == tile_rows
     d.run(plan)
@@ -45,26 +52,27 @@ def test_random_cases_on_tiles(tile_rows, seed, batch, dql, hq, hkv, k, lo, hi, 
     assert np.all(got[case.real_rows:] == 0.0)
 
 
+@pytest.mark.parametrize("tile_rows", [4, 8])
 @pytest.mark.parametrize("seed,batch,dql,hq,hkv,k,lo,hi,kvd,qd,qs,pad,neg,splits,layout",
                          base.FORMAT_RANDOM_CASES)
-def test_format_cases_on_tiles(seed, batch, dql, hq, hkv, k, lo, hi, kvd, qd, qs, pad, neg,
-                               splits, layout):
-    _banner(f"tiles=4 random seed={seed} kv={kvd} q={qd}")
+def test_format_cases_on_tiles(tile_rows, seed, batch, dql, hq, hkv, k, lo, hi, kvd, qd, qs,
+                               pad, neg, splits, layout):
+    _banner(f"tiles={tile_rows} random seed={seed} kv={kvd} q={qd}")
     case = gen.make_random_case(seed, batch, dql, hq, hkv, k, lo, hi, kv_dtype=kvd,
                                 pad_rows=pad, neg_frac=neg, q_dtype=qd, q_scale=qs)
     case.k_scale, case.v_scale = 0.5, 1.5
     d = DevCase(case, layout=layout)
-    d.run(d.plan(splits, tile_rows=4))
+    d.run(d.plan(splits, tile_rows=tile_rows))
     torch.cuda.synchronize()
     assert_parity(to_f64(d.out), oracle_attend(case), what=f"tiles format {seed}")
 
 
 def test_long_query_length_single_row_and_tiles_agree_with_oracle():
-    _banner("dql=32, single-row kernel vs 2- and 4-row tiles")
+    _banner("dql=32, single-row kernel vs 2-, 4- and 8-row tiles")
     case = gen.make_random_case(171, 3, 32, 64, 4, 16, 300, 20000, pad_rows=3)
     d = DevCase(case)
     ref = oracle_attend(case)
-    for tr in (1, 2, 4):
+    for tr in (1, 2, 4, 8):
         d.out.fill_(float("nan"))
         plan = d.plan(tile_rows=tr)
         assert plan.tile_rows == tr
@@ -99,6 +107,8 @@ DENSE_CASES = [
     (184, 5, 3, 32, 4, 1, 3000, gen.KV_E5M2, gen.Q_BF16, 1.0, 0, 16, 4, "hnd"),
     (185, 2, 5, 16, 2, 5, 700, gen.KV_E5M2, gen.Q_FP8, 2.0, 3, 1, 2, "nhd"),
     (186, 2, 2, 12, 3, 40000, 60000, gen.KV_FP8, gen.Q_BF16, 1.0, 0, 0, 4, "hnd"),
+    (188, 3, 8, 64, 4, 1, 9000, gen.KV_FP8, gen.Q_BF16, 1.0, 2, 0, 8, "hnd"),
+    (189, 2, 11, 16, 1, 300, 4000, gen.KV_E5M2, gen.Q_FP8, 0.5, 1, 5, 8, "nhd"),
 ]
 
 
