@@ -107,7 +107,7 @@ def test_decode_query_len_bounds(lib, batch, dql, hq, hkv, ok):
     ("num_q_heads", 64, msa.MSA_ERR_UNSUPPORTED, "GQA group"),
     ("topk_blocks", -1, msa.MSA_ERR_INVALID_ARG, "topk_blocks"),
     ("tile_rows", 3, msa.MSA_ERR_INVALID_ARG, "tile_rows"),
-    ("tile_rows", 8, msa.MSA_ERR_INVALID_ARG, "tile_rows"),
+    ("tile_rows", 16, msa.MSA_ERR_INVALID_ARG, "tile_rows"),
     ("topk_blocks", 65, msa.MSA_ERR_UNSUPPORTED, "topk_blocks"),
     ("batch", 0, msa.MSA_ERR_INVALID_ARG, "batch"),
     ("page_table_stride", 0, msa.MSA_ERR_INVALID_ARG, "page_table_stride"),
@@ -618,3 +618,14 @@ def test_noalloc_rejects_partials_beyond_its_scratch(lib):
     st = lib.msa_sparse_decode_run_noalloc(ctypes.byref(bad), 0, None, None, strides, 1, 1.0,
                                            1.0, 1.0, None, None, None, tk, None, 0.1, None)
     assert st == -1 and "decode_query_len" in lib.msa_last_error().decode()
+
+
+def test_eight_row_tiles_need_an_8bit_cache(lib):
+    """8-row tiles stage fp8 pages through LDS: a bf16 or MXFP4 cache is refused
+    before any HIP call; e4m3 and e5m2 are accepted."""
+    for kvd in (msa.KV_BF16, msa.KV_MXFP4):
+        st, msg = plan_status(lib, shape(tile_rows=8, kv_dtype=kvd))
+        assert st == msa.MSA_ERR_UNSUPPORTED and "8-row tiles" in msg, (kvd, st, msg)
+    for kvd in (msa.KV_FP8_E4M3, msa.KV_FP8_E5M2):
+        st, msg = plan_status(lib, shape(tile_rows=8, kv_dtype=kvd, num_splits=1))
+        assert st == 0, (kvd, msg)
