@@ -295,9 +295,12 @@ msa_status plan_config(const msa_decode_shape* shape, bool prefill, int32_t real
   if (st != MSA_OK) return st;
   if (units > INT32_MAX) return fail(MSA_ERR_UNSUPPORTED, "launch grid too large");
   const int32_t splits = choose_splits(shape, units, dense);
-  const int64_t grid = (tile_rows == 1 ? msa::xcd_groups(units, shape->num_kv_heads)
-                                       : (units + msa::kXcdSlots - 1) / msa::kXcdSlots) *
-                       msa::kXcdSlots * splits;
+  const int64_t grid =
+      (tile_rows == 1 ? msa::xcd_groups(units, shape->num_kv_heads)
+       : (dense || tile_rows == 8)
+           ? (units + msa::kXcdSlots - 1) / msa::kXcdSlots
+           : msa::tile_block_groups(units / shape->num_kv_heads, shape->num_kv_heads)) *
+      msa::kXcdSlots * splits;
   if (grid > INT32_MAX) return fail(MSA_ERR_UNSUPPORTED, "launch grid too large");
   const int64_t per_row = (int64_t)shape->num_q_heads * splits;
   const int64_t o_bytes = splits > 1 ? (int64_t)num_rows * per_row * msa::kHeadDim * 4 : 0;

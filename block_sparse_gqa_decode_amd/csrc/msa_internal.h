@@ -43,6 +43,28 @@ inline int64_t xcd_groups(int64_t units, int hkv) {
   return (units + kXcdSlots * c - 1) / (kXcdSlots * c) * c;
 }
 
+// Sparse row tiles: units (tile, kv head) are dealt to the XCD slots in
+// chunks of kTileBlock consecutive tiles of one kv head, chunk c of the
+// launch going to slot c % 8.  A request's tiles draw on the same pages per
+// head, so a chunk's re-reads of a page meet in one L2 instead of two or more
+// (the plain round robin spread a head's tiles over two XCDs).  Per split,
+// the launch has tile_block_groups(tiles, hkv) workgroups per slot; the k-th
+// on slot x takes tile_block_unit(tiles, hkv, x, k), -1 past the last tile.
+constexpr int kTileBlock = 16;
+
+__host__ __device__ inline int64_t tile_block_groups(int64_t tiles, int hkv) {
+  const int64_t chunks = (tiles + kTileBlock - 1) / kTileBlock * hkv;
+  return (chunks + kXcdSlots - 1) / kXcdSlots * kTileBlock;
+}
+
+__host__ __device__ inline int tile_block_unit(int tiles, int hkv, int slot, int k) {
+  const int c = (k / kTileBlock) * kXcdSlots + slot;   // chunk of this workgroup
+  const int block = c / hkv;
+  const int h = c - block * hkv;
+  const int tile = block * kTileBlock + k % kTileBlock;
+  return tile < tiles ? tile * hkv + h : -1;
+}
+
 // Element formats (the values of msa_kv_dtype / msa_q_dtype).
 constexpr int kKvBf16 = 0;
 constexpr int kKvE4m3 = 1;     // OCP fp8 e4m3fn
