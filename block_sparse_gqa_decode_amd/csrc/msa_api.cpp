@@ -476,6 +476,12 @@ msa_status run_plan(const msa_plan_s* plan, const void* q, const void* kv_cache,
   p.splits = plan->splits;
   p.num_units = plan->num_units;
   p.tile_dense = plan->dense ? 1 : 0;
+  // Longest request first for sparse decode tiles (2 or 4 rows) of a small
+  // batch whose tiles never span two requests.
+  p.len_order = (!plan->prefill && !plan->dense && (plan->tile_rows == 2 || plan->tile_rows == 4) &&
+                 s.batch <= 64 && s.decode_query_len % plan->tile_rows == 0)
+                    ? 1
+                    : 0;
   p.arrivals = plan->fused ? plan->arrivals : nullptr;
   if (plan->prefill) {
     p.cu_q = cu_q;

@@ -100,6 +100,10 @@ struct AttendParams {
   // Multi-row tiles (tile kernel only): tile_dense selects every visible
   // block of request-aligned tiles instead of the rows' top-k union.
   int32_t tile_dense;
+  // Sparse decode row tiles of at most 64 requests whose tiles never span two
+  // requests: dispatch the requests' tiles longest request first (see
+  // msa_tile.hip).
+  int32_t len_order;
   // In-kernel split merge (single-row attend, 2..kMaxFusedSplits splits):
   // one arrival counter per unit, zero between launches; null = the merge
   // kernel combines the partials instead.
