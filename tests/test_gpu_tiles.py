@@ -109,6 +109,9 @@ DENSE_CASES = [
     (186, 2, 2, 12, 3, 40000, 60000, gen.KV_FP8, gen.Q_BF16, 1.0, 0, 0, 4, "hnd"),
     (188, 3, 8, 64, 4, 1, 9000, gen.KV_FP8, gen.Q_BF16, 1.0, 2, 0, 8, "hnd"),
     (189, 2, 11, 16, 1, 300, 4000, gen.KV_E5M2, gen.Q_FP8, 0.5, 1, 5, 8, "nhd"),
+    # seq_len below dql: the first rows of such a request see no key (exact zeros)
+    (190, 4, 4, 16, 1, 1, 6, gen.KV_FP8, gen.Q_BF16, 1.0, 1, 0, 2, "hnd"),
+    (191, 3, 8, 64, 4, 1, 10, gen.KV_FP8, gen.Q_FP8, 0.5, 0, 2, 4, "nhd"),
 ]
 
 
