@@ -121,9 +121,21 @@ __device__ __forceinline__ bf16x8_t row_scores(const PageRegs<kv_kind(kKv)>& r,
   return softmax_step(z, scale_log2, m_run, l_part, o);
 }
 
-template <int kKv, int kQ, int kM>
-__global__ __launch_bounds__(kThreads) void multi_kernel(AttendParams p) {
+// kOcc3 (2-row tiles over ragged prefill rows): three wavefronts per SIMD,
+// with no page prefetch inside a wavefront, so the register file holds a
+// third workgroup's wavefronts instead of a second page per wavefront.
+// Prefill tiles share few pages (about 1.2 rows per page on the
+// chunked-prefill workload), so each workgroup's page loop is bound by its
+// own dependent chain and a third workgroup per compute unit pays: 615
+// against 640 us there.  Decode tiles (the ragged dql-32 workload) keep two
+// wavefronts and the two-deep ring: its long requests' phase needs the
+// prefetch (86 against 83 us the other way).  bf16 caches keep it too
+// (their wider pages would spill at 168 VGPRs).
+template <int kKv, int kQ, int kM, bool kOcc3>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kOcc3 ? 3 : 1, kOcc3 ? 3 : 8)))
+void multi_kernel(AttendParams p) {
   constexpr int kKind = kv_kind(kKv);
+  constexpr int kRing = kOcc3 ? 1 : kDepth;   // pages per wavefront in the ring
   // Page list entry: (physical page, or 0 when no row sees the entry;
   // byte w = visible rows of the page for tile row w, 0 when it does not see
   // it).  One 8-byte LDS read per page gives its loads and every row's mask.
@@ -368,18 +380,18 @@ __global__ __launch_bounds__(kThreads) void multi_kernel(AttendParams p) {
       return nv4;
     };
 
-    PageRegs<kKind> buf[kDepth];
-    uint32_t bnv[kDepth];
+    PageRegs<kKind> buf[kRing];
+    uint32_t bnv[kRing];
 #pragma unroll
-    for (int j = 0; j < kDepth - 1; ++j) bnv[j] = fetch(min(c0 + j, c1 - 1), buf[j]);
-    for (int i = c0;; i += kDepth) {
+    for (int j = 0; j < kRing - 1; ++j) bnv[j] = fetch(min(c0 + j, c1 - 1), buf[j]);
+    for (int i = c0;; i += kRing) {
 #pragma unroll
-      for (int j = 0; j < kDepth; ++j) {
+      for (int j = 0; j < kRing; ++j) {
         const int cur = i + j;
         if (cur >= c1) goto chunk_done;
         {
-          const int nx = (j + kDepth - 1) % kDepth;
-          bnv[nx] = fetch(min(cur + kDepth - 1, c1 - 1), buf[nx]);
+          const int nx = (j + kRing - 1) % kRing;
+          bnv[nx] = fetch(min(cur + kRing - 1, c1 - 1), buf[nx]);
           const uint32_t nv4 = bnv[j];
           bool any = false;
 #pragma unroll
@@ -494,9 +506,12 @@ __global__ __launch_bounds__(kThreads) void multi_kernel(AttendParams p) {
 template <int kKv, int kQ>
 hipError_t launch_tile_fmt(const AttendParams& p, int tile_rows, dim3 gd, hipStream_t stream) {
   if (tile_rows == 4)
-    hipLaunchKernelGGL((multi_kernel<kKv, kQ, 4>), gd, dim3(kThreads), 0, stream, p);
+    hipLaunchKernelGGL((multi_kernel<kKv, kQ, 4, false>), gd, dim3(kThreads), 0, stream, p);
+  else if (kKv != kKvBf16 && p.cu_q != nullptr)  // bf16 pages would spill at 168 VGPRs
+    hipLaunchKernelGGL((multi_kernel<kKv, kQ, 2, kKv != kKvBf16>), gd, dim3(kThreads), 0,
+                       stream, p);
   else
-    hipLaunchKernelGGL((multi_kernel<kKv, kQ, 2>), gd, dim3(kThreads), 0, stream, p);
+    hipLaunchKernelGGL((multi_kernel<kKv, kQ, 2, false>), gd, dim3(kThreads), 0, stream, p);
   return hipGetLastError();
 }
 
