@@ -41,7 +41,8 @@ namespace {
 constexpr int kScoreWaves = 4;
 constexpr int kScoreThreads = 64 * kScoreWaves;
 constexpr int kScoreKeys = 32;     // keys of a block per wavefront
-constexpr int kScoreDepth = 4;     // blocks in flight per wavefront
+constexpr int kScoreDepth = 3;     // blocks in flight per wavefront (4: +1.3 us on the
+                                   // full indexer step, 5 / 6: +2 / +8 us)
 constexpr int kFlush = 32;         // items between LDS flushes of the maxima
 
 // The K halves of one block for one wavefront (its 32 keys), by KV kind; the
@@ -99,6 +100,29 @@ __device__ __forceinline__ void load_q(QRegs<kQ>& qf, const ScoreParams& p, int 
                             g);
 }
 
+// The max over a wavefront's 64 lanes, returned to every lane.  DPP row
+// shifts and row broadcasts (the GCN lane network CDNA keeps) take the max
+// into lane 63 in seven steps with no LDS round trip; the lane shuffles this
+// replaces went through LDS, six dependent round trips per block (full
+// indexer step 348 -> 344 us).  Every lane must be active.
+__device__ __forceinline__ float wave_max_dpp(float v) {
+  const int ninf = __float_as_int(-INFINITY);
+  // A lane whose source is outside its row, or in a row the step does not
+  // write, keeps -inf, which leaves its max unchanged.
+#define MSA_DPP_MAX(ctrl, row_mask, bank_mask)                                       \
+  v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(ninf, __float_as_int(v), ctrl, \
+                                                          row_mask, bank_mask, false)))
+  MSA_DPP_MAX(0x111, 0xf, 0xf);  // row_shr:1
+  MSA_DPP_MAX(0x112, 0xf, 0xf);  // row_shr:2
+  MSA_DPP_MAX(0x113, 0xf, 0xf);  // row_shr:3: lane i of a row holds lanes i-3..i
+  MSA_DPP_MAX(0x114, 0xf, 0xe);  // row_shr:4 into lanes 4..15
+  MSA_DPP_MAX(0x118, 0xf, 0xc);  // row_shr:8 into lanes 8..15: lane 15 holds its row
+  MSA_DPP_MAX(0x142, 0xa, 0xf);  // row_bcast:15 into rows 1 and 3
+  MSA_DPP_MAX(0x143, 0xc, 0xf);  // row_bcast:31 into rows 2 and 3: lane 63 holds all
+#undef MSA_DPP_MAX
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
+}
+
 // The wavefront's max over its 32 keys (those < nvis) and the group's rows of
 // qk_scale * q.k for one block and one token.
 template <int kKv, int kQ>
@@ -123,9 +147,7 @@ __device__ __forceinline__ float block_max(const KHalf<kv_kind(kKv)>& r,
       if (key < nvis && n < group) best = fmaxf(best, s[i] * qk_scale);
     }
   }
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) best = fmaxf(best, __shfl_xor(best, off));
-  return best;
+  return wave_max_dpp(best);
 }
 
 typedef __attribute__((address_space(4))) const int32_t const_i32;
