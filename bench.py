@@ -664,9 +664,30 @@ class FullStepSet:
         _, _, score, sel, _ = self.sets[i]
         self.msa.msa_topk_select(score, sel)
 
-    def run_step(self, i):
+    def run_score_only(self, i):
+        q, bt, score, _, _ = self.sets[i]
+        c = self.case
+        self.msa.msa_block_score_topk(q, self.kv, bt, self.seq_lens, decode_query_len=c.dql,
+                                      num_kv_heads=c.num_kv_heads, max_blocks=c.max_blocks,
+                                      score=score, topk_out=None, k_scale=c.k_scale,
+                                      q_scale=c.q_scale, kv_dtype=_kv_code(case=c))
+
+    def run_select_attend(self, i):
+        q, bt, score, _, out = self.sets[i]
+        c = self.case
+        self.msa.msa_sparse_decode_select_run(self.plan, q, self.kv, bt, self.seq_lens, score,
+                                              out, sm_scale=c.sm_scale, k_scale=c.k_scale,
+                                              v_scale=c.v_scale, q_scale=c.q_scale)
+
+    def run_step_separate(self, i):
+        """Three launches: scores, the selector, the attend over its top-k."""
         self.run_score(i)
         self.run_attend(i)
+
+    def run_step(self, i):
+        """Two launches: scores, then the attend that selects its own top-k."""
+        self.run_score_only(i)
+        self.run_select_attend(i)
 
 
 def _graph_time(fns, replicas, steps, warmup):
@@ -715,9 +736,12 @@ def time_full_step(name, steps, warmup, replicas, dev, verbose=True):
               f"(pool {case.kv.nbytes / 2**20:.0f} MiB x {replicas}, max_blocks "
               f"{case.max_blocks})", file=sys.stderr, flush=True)
     step_ms, n = _graph_time(fs.run_step, replicas, steps, warmup)
+    separate_ms, _ = _graph_time(fs.run_step_separate, replicas, steps, warmup)
     score_ms, _ = _graph_time(fs.run_score, replicas, steps, warmup)
+    scorer_ms, _ = _graph_time(fs.run_score_only, replicas, steps, warmup)
     select_ms, _ = _graph_time(fs.run_select, replicas, steps, warmup)
     attend_ms, _ = _graph_time(fs.run_attend, replicas, steps, warmup)
+    select_attend_ms, _ = _graph_time(fs.run_select_attend, replicas, steps, warmup)
     torch.cuda.synchronize()
     sb = scorer_bytes(case)
     ab = []
@@ -729,36 +753,40 @@ def time_full_step(name, steps, warmup, replicas, dev, verbose=True):
     eff = sum(b["effective_kv"] for b in ab) / len(ab)
     res = {
         "config": name, "steps": n, "steps_requested": steps, "ms_per_step": step_ms,
+        "step_note": "two launches: the scorer (msa_block_score_topk, topk_out NULL), then "
+                     "the attend that selects each row's top-16 itself "
+                     "(msa_sparse_decode_select_run)",
+        "ms_per_step_three_launches": separate_ms,
         "tokens_per_s": case.real_rows / (step_ms / 1e3),
-        "score_topk_ms": score_ms, "select_ms": select_ms, "attend_ms": attend_ms,
+        "scorer_ms": scorer_ms, "score_topk_ms": score_ms, "select_ms": select_ms,
+        "attend_ms": attend_ms, "select_attend_ms": select_attend_ms,
         "score_k_half_bytes": sb["k_half"], "score_algorithmic_bytes": sb["algorithmic"],
-        # scorer alone: the score+select launch pair minus the selector's own time
+        # the scorer alone (msa_block_score_topk with topk_out NULL)
         "scorer_bytes": sb["scorer"],
-        "scorer_gbs": sb["scorer"] / ((score_ms - select_ms) / 1e3) / 1e9,
-        "scorer_pct_hbm_peak": 100 * sb["scorer"] / ((score_ms - select_ms) / 1e3) / 1e9
-                               / HBM_PEAK_GBS,
+        "scorer_gbs": sb["scorer"] / (scorer_ms / 1e3) / 1e9,
+        "scorer_pct_hbm_peak": 100 * sb["scorer"] / (scorer_ms / 1e3) / 1e9 / HBM_PEAK_GBS,
         "score_traffic_bytes": (lambda t: None if t is None else t.get("hbm_bytes_per_launch"))(
             load_traffic(name, "score")),
         # MFMA use of the HBM-bound scorer: its matrix-core flops over its
         # time, against the dense peak of the MFMA it issues (bf16 q: bf16,
         # fp8 q: fp8).
-        "scorer_mfma_tflops": sb["mfma_flops"] / ((score_ms - select_ms) / 1e3) / 1e12,
+        "scorer_mfma_tflops": sb["mfma_flops"] / (scorer_ms / 1e3) / 1e12,
         "scorer_mfma_peak_tflops": MFMA_PEAK_TFLOPS[case.q_dtype == "fp8_e4m3"],
-        "scorer_mfma_pct_peak": 100 * sb["mfma_flops"] / ((score_ms - select_ms) / 1e3) / 1e12
+        "scorer_mfma_pct_peak": 100 * sb["mfma_flops"] / (scorer_ms / 1e3) / 1e12
                                 / MFMA_PEAK_TFLOPS[case.q_dtype == "fp8_e4m3"],
         "attend_algorithmic_bytes": att, "attend_effective_kv_bytes": eff,
         "attend_algorithmic_gbs": att / (attend_ms / 1e3) / 1e9,
         "step_algorithmic_gbs": (att + sb["algorithmic"]) / (step_ms / 1e3) / 1e9,
         "splits": fs.plan.num_splits, "real_rows": case.real_rows,
     }
-    ts = (score_ms - select_ms) / 1e3
+    ts = scorer_ms / 1e3
     res["roofline"] = _roofline(
         sb["scorer"], sb["mfma_flops"], ts, MFMA_PEAK_TFLOPS[case.q_dtype == "fp8_e4m3"],
         res["score_traffic_bytes"],
         {"kernel": f"score_kernel<kv {case.kv_dtype}, q {case.q_dtype}>",
          "basis": "K half of every visible row of every (request, kv head) + q + the score "
                   "write + block-table entries",
-         "timing": "HIP events: graph replays of score + select minus select alone"})
+         "timing": "HIP events: graph replays of the scorer alone"})
     uq = sum(b["unique_algorithmic"] for b in ab) / len(ab)
     fl = sum(b["flops"] for b in ab) / len(ab)
     at = load_traffic(name, "attend")

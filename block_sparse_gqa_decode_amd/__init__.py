@@ -44,7 +44,8 @@ import torch
 __all__ = [
     "MsaError", "MsaInvalidArgument", "MsaUnsupported", "DecodePlan", "PlanCache",
     "msa_sparse_decode_plan", "msa_sparse_decode_run", "msa_sparse_decode_attend",
-    "msa_sparse_decode_merge", "msa_sparse_decode_run_noalloc", "msa_block_score_topk", "msa_sparse_prefill_plan",
+    "msa_sparse_decode_merge", "msa_sparse_decode_run_noalloc", "msa_sparse_decode_select_run",
+    "msa_block_score_topk", "msa_sparse_prefill_plan",
     "msa_sparse_prefill_run",
     "msa_topk_select", "msa_fp8_e4m3_to_bf16", "msa_fp8_e5m2_to_bf16", "msa_mxfp4_to_bf16",
     "msa_probe_read_runs",
@@ -53,7 +54,7 @@ __all__ = [
     "PAGE_SIZE", "HEAD_DIM", "ABI_VERSION",
 ]
 
-ABI_VERSION = 6
+ABI_VERSION = 7
 PAGE_SIZE = 128
 HEAD_DIM = 128
 KV_BF16 = 0
@@ -135,6 +136,8 @@ def load_library():
         "msa_sparse_decode_attend": (i32, [vp, vp, vp, pi64, i64, f32, f32, f32, vp, vp,
                                            vp, pi64, vp, f32, vp]),
         "msa_sparse_decode_merge": (i32, [vp, vp, f32, vp]),
+        "msa_sparse_decode_select_run": (i32, [vp, vp, vp, pi64, i64, f32, f32, f32, vp, vp,
+                                               vp, pi64, i32, vp, vp, f32, vp]),
         "msa_sparse_decode_run_noalloc": (i32, [ctypes.POINTER(_Shape), ctypes.c_int, vp, vp,
                                                 pi64, i64, f32, f32, f32, vp, vp, vp, pi64, vp,
                                                 f32, vp]),
@@ -392,7 +395,8 @@ def _strides3(t: Optional[torch.Tensor]):
     return None if t is None else _I64x3(*t.stride())
 
 
-def _run_args(plan, q, kv_cache, block_table, seq_lens, topk, out, tables=True):
+def _run_args(plan, q, kv_cache, block_table, seq_lens, topk, out, tables=True,
+              selects=False):
     rows = plan.num_token_rows
     _check_q(q, "q", rows, plan.num_q_heads, plan.q_dtype)
     _check_q(out, "out", rows, plan.num_q_heads)
@@ -402,7 +406,10 @@ def _run_args(plan, q, kv_cache, block_table, seq_lens, topk, out, tables=True):
         _check_tables(block_table, seq_lens, plan.batch)
     if block_table.stride(0) != plan.page_table_stride:
         raise ValueError("block_table row stride does not match the plan")
-    if plan.dense:
+    if selects:
+        if plan.dense:
+            raise ValueError("a dense plan attends every visible block: nothing to select")
+    elif plan.dense:
         if topk is not None:
             raise ValueError("a dense plan attends every visible block: pass topk=None")
     elif (topk is None or topk.dtype != torch.int32 or topk.dim() != 3
@@ -438,6 +445,35 @@ def msa_sparse_decode_run(plan: DecodePlan, q: torch.Tensor, kv_cache: torch.Ten
         *head, float(q_scale), float(k_scale), float(v_scale), block_table.data_ptr(), seq_lens.data_ptr(),
         _ptr(topk), _strides3(topk), out.data_ptr(), float(sm_scale),
         _stream_handle(stream, q.device)))
+
+
+def msa_sparse_decode_select_run(plan: DecodePlan, q: torch.Tensor, kv_cache: torch.Tensor,
+                                 block_table: torch.Tensor, seq_lens: torch.Tensor,
+                                 score: torch.Tensor, out: torch.Tensor, *, sm_scale: float,
+                                 topk_out: Optional[torch.Tensor] = None, k_scale: float = 1.0,
+                                 v_scale: float = 1.0, q_scale: float = 1.0,
+                                 stream=None) -> None:
+    """The attend of msa_sparse_decode_run over the top-k rows that each
+    workgroup selects from ``score`` itself (float32 logical [Hkv, max_blocks,
+    rows], as msa_block_score_topk fills it); ``topk_out`` (optional, int32
+    [rows, Hkv, k]) receives the selection."""
+    _require_decode_plan(plan)
+    if score.dtype != torch.float32 or score.dim() != 3 or score.device != q.device:
+        raise ValueError("score must be a 3-D float32 tensor [Hkv, blocks, rows] on q's device")
+    hkv, nb, rows = score.shape
+    if hkv != plan.num_kv_heads or rows != plan.num_token_rows:
+        raise ValueError(f"score must be [{plan.num_kv_heads}, blocks, {plan.num_token_rows}]")
+    if topk_out is not None and (
+            topk_out.dtype != torch.int32 or not topk_out.is_contiguous()
+            or tuple(topk_out.shape) != (rows, hkv, plan.topk_blocks)
+            or topk_out.device != q.device):
+        raise ValueError(f"topk_out must be contiguous int32 [{rows}, {hkv}, "
+                         f"{plan.topk_blocks}] on q's device")
+    head = _run_args(plan, q, kv_cache, block_table, seq_lens, None, out, selects=True)
+    _check(load_library().msa_sparse_decode_select_run(
+        *head, float(q_scale), float(k_scale), float(v_scale), block_table.data_ptr(),
+        seq_lens.data_ptr(), score.data_ptr(), _I64x3(*score.stride()), nb, _ptr(topk_out),
+        out.data_ptr(), float(sm_scale), _stream_handle(stream, q.device)))
 
 
 class _ShapeArgs:
@@ -508,10 +544,12 @@ def msa_sparse_decode_merge(plan: DecodePlan, out: torch.Tensor, *, v_scale: flo
 
 def msa_block_score_topk(q: torch.Tensor, kv_cache: torch.Tensor, block_table: torch.Tensor,
                          seq_lens: torch.Tensor, *, decode_query_len: int, num_kv_heads: int,
-                         max_blocks: int, score: torch.Tensor, topk_out: torch.Tensor,
-                         k_scale: float = 1.0, q_scale: float = 1.0, num_token_rows: int = 0,
+                         max_blocks: int, score: torch.Tensor,
+                         topk_out: Optional[torch.Tensor], k_scale: float = 1.0,
+                         q_scale: float = 1.0, num_token_rows: int = 0,
                          kv_dtype: Optional[int] = None, stream=None) -> None:
-    """score[h, b, t] (logical; any strides) and topk_out[t, h, :] for every row.
+    """score[h, b, t] (logical; any strides) and topk_out[t, h, :] for every row
+    (topk_out=None: the scores alone, for msa_sparse_decode_select_run).
     The q format follows q's dtype; a uint8 cache is e4m3 unless ``kv_dtype``
     says otherwise."""
     batch = int(seq_lens.shape[0])
@@ -524,16 +562,19 @@ def msa_block_score_topk(q: torch.Tensor, kv_cache: torch.Tensor, block_table: t
     if score.dtype != torch.float32 or score.dim() != 3 or \
             tuple(score.shape) != (num_kv_heads, max_blocks, rows):
         raise ValueError(f"score must be float32 [{num_kv_heads}, {max_blocks}, {rows}]")
-    if topk_out.dtype != torch.int32 or not topk_out.is_contiguous() or topk_out.dim() != 3 \
-            or topk_out.shape[0] != rows or topk_out.shape[1] != num_kv_heads:
+    if topk_out is not None and (
+            topk_out.dtype != torch.int32 or not topk_out.is_contiguous()
+            or topk_out.dim() != 3 or topk_out.shape[0] != rows
+            or topk_out.shape[1] != num_kv_heads):
         raise ValueError(f"topk_out must be contiguous int32 [{rows}, {num_kv_heads}, k]")
+    k = int(topk_out.shape[2]) if topk_out is not None else 0
     shape = _Shape(batch, decode_query_len, rows, block_table.stride(0), q.shape[1],
-                   num_kv_heads, PAGE_SIZE, HEAD_DIM, topk_out.shape[2], kvd, 0, q_dtype)
+                   num_kv_heads, PAGE_SIZE, HEAD_DIM, k, kvd, 0, q_dtype)
     _check(load_library().msa_block_score_topk(
         ctypes.byref(shape), q.data_ptr(), kv_cache.data_ptr(), _kv_strides(kv_cache, kvd),
         kv_cache.shape[0], float(q_scale), float(k_scale), block_table.data_ptr(), seq_lens.data_ptr(),
-        int(max_blocks), score.data_ptr(), _I64x3(*score.stride()), topk_out.data_ptr(),
-        int(topk_out.shape[2]), _stream_handle(stream, q.device)))
+        int(max_blocks), score.data_ptr(), _I64x3(*score.stride()), _ptr(topk_out), k,
+        _stream_handle(stream, q.device)))
 
 
 def msa_topk_select(score: torch.Tensor, topk_out: torch.Tensor, stream=None) -> None:

@@ -413,7 +413,7 @@ msa_status run_plan(const msa_plan_s* plan, const void* q, const void* kv_cache,
                     float k_scale, float v_scale, const int32_t* block_table,
                     const int32_t* seq_lens, const int32_t* cu_q, const int32_t* ctx,
                     const int32_t* topk, const int64_t topk_strides[3], void* out,
-                    float sm_scale, void* stream, bool merge) {
+                    float sm_scale, void* stream, bool merge, const SelectSource* sel) {
   if (plan == nullptr) return fail(MSA_ERR_INVALID_ARG, "plan is NULL");
   const msa_decode_shape& s = plan->shape;
   if (q == nullptr || out == nullptr) return fail(MSA_ERR_INVALID_ARG, "q and out must be non-NULL");
@@ -425,12 +425,16 @@ msa_status run_plan(const msa_plan_s* plan, const void* q, const void* kv_cache,
                   "block_table, cu_seqlens_q, context_lens and topk must be non-NULL");
   } else if (block_table == nullptr || seq_lens == nullptr) {
     return fail(MSA_ERR_INVALID_ARG, "block_table and seq_lens must be non-NULL");
+  } else if (sel != nullptr) {
+    if (plan->dense || plan->tile_rows != 1)
+      return fail(MSA_ERR_UNSUPPORTED,
+                  "the selecting attend runs on single-row sparse decode plans (tile_rows 1)");
   } else if (plan->dense != (topk == nullptr)) {
     return fail(MSA_ERR_INVALID_ARG, plan->dense ? "a dense plan takes topk = NULL"
                                                  : "block_table, seq_lens and topk must be "
                                                    "non-NULL");
   }
-  if (!plan->dense) {
+  if (!plan->dense && sel == nullptr) {
     if (topk_strides == nullptr) return fail(MSA_ERR_INVALID_ARG, "topk_strides is NULL");
     for (int d = 0; d < 3; ++d)
       if (topk_strides[d] < 0) return fail(MSA_ERR_INVALID_ARG, "topk strides must be >= 0");
@@ -455,7 +459,14 @@ msa_status run_plan(const msa_plan_s* plan, const void* q, const void* kv_cache,
   p.bt_stride = s.page_table_stride;
   p.seq_lens = seq_lens;
   p.topk = topk;
-  if (!plan->dense) {
+  if (sel != nullptr) {
+    p.sel_score = sel->score;
+    p.sel_s0 = sel->s0;
+    p.sel_s1 = sel->s1;
+    p.sel_s2 = sel->s2;
+    p.sel_max_blocks = sel->max_blocks;
+    p.sel_topk_out = sel->topk_out;
+  } else if (!plan->dense) {
     p.tk_s0 = topk_strides[0];
     p.tk_s1 = topk_strides[1];
     p.tk_s2 = topk_strides[2];
@@ -555,6 +566,29 @@ msa_status msa_sparse_decode_attend(msa_plan plan, const void* q, const void* kv
                     stream, false);
 }
 
+msa_status msa_sparse_decode_select_run(msa_plan plan, const void* q, const void* kv_cache,
+                                        const int64_t kv_strides[4], int64_t num_kv_blocks,
+                                        float q_scale, float k_scale, float v_scale,
+                                        const int32_t* block_table, const int32_t* seq_lens,
+                                        const float* score, const int64_t score_strides[3],
+                                        int32_t max_blocks, int32_t* topk_out, void* out,
+                                        float sm_scale, void* stream) {
+  if (plan != nullptr && plan->prefill)
+    return fail(MSA_ERR_INVALID_ARG, "a prefill plan runs through msa_sparse_prefill_run");
+  if (score == nullptr) return fail(MSA_ERR_INVALID_ARG, "score must be non-NULL");
+  if (score_strides == nullptr) return fail(MSA_ERR_INVALID_ARG, "score_strides is NULL");
+  for (int d = 0; d < 3; ++d)
+    if (score_strides[d] < 0) return fail(MSA_ERR_INVALID_ARG, "score strides must be >= 0");
+  if (max_blocks < 1 || max_blocks > msa::kMaxScoreBlocks)
+    return fail(MSA_ERR_INVALID_ARG, "max_blocks must be in 1..%d (got %d)",
+                msa::kMaxScoreBlocks, max_blocks);
+  const msa::SelectSource sel{score, score_strides[0], score_strides[1], score_strides[2],
+                              max_blocks, topk_out};
+  return msa::run_plan(plan, q, kv_cache, kv_strides, num_kv_blocks, q_scale, k_scale, v_scale,
+                       block_table, seq_lens, nullptr, nullptr, nullptr, nullptr, out, sm_scale,
+                       stream, true, &sel);
+}
+
 msa_status msa_sparse_decode_merge(msa_plan plan, void* out, float v_scale, void* stream) {
   if (plan == nullptr) return fail(MSA_ERR_INVALID_ARG, "plan is NULL");
   if (plan->prefill)
@@ -630,8 +664,7 @@ msa_status msa_block_score_topk(const msa_decode_shape* shape, const void* q,
   if (q == nullptr || !aligned16(q)) return fail(MSA_ERR_INVALID_ARG, "q must be non-NULL and 16-byte aligned");
   if (block_table == nullptr || seq_lens == nullptr)
     return fail(MSA_ERR_INVALID_ARG, "block_table and seq_lens must be non-NULL");
-  if (score == nullptr || topk_out == nullptr)
-    return fail(MSA_ERR_INVALID_ARG, "score and topk_out must be non-NULL");
+  if (score == nullptr) return fail(MSA_ERR_INVALID_ARG, "score must be non-NULL");
   if (score_strides == nullptr) return fail(MSA_ERR_INVALID_ARG, "score_strides is NULL");
   for (int d = 0; d < 3; ++d)
     if (score_strides[d] < 0) return fail(MSA_ERR_INVALID_ARG, "score strides must be >= 0");
@@ -640,7 +673,7 @@ msa_status msa_block_score_topk(const msa_decode_shape* shape, const void* q,
   if (max_blocks < 1 || max_blocks > msa::kMaxScoreBlocks)
     return fail(MSA_ERR_INVALID_ARG, "max_blocks must be in 1..%d (got %d)",
                 msa::kMaxScoreBlocks, max_blocks);
-  if (topk_k < 1 || topk_k > msa::kMaxTopk)
+  if (topk_out != nullptr && (topk_k < 1 || topk_k > msa::kMaxTopk))
     return fail(MSA_ERR_INVALID_ARG, "topk_k must be in 1..%d (got %d)", msa::kMaxTopk, topk_k);
   st = check_scales(q_scale, k_scale);
   if (st != MSA_OK) return st;
@@ -677,6 +710,7 @@ msa_status msa_block_score_topk(const msa_decode_shape* shape, const void* q,
   hipStream_t hs = static_cast<hipStream_t>(stream);
   hipError_t e = msa::launch_score(p, shape->kv_dtype, shape->q_dtype, hs);
   if (e != hipSuccess) return device_fail(e, "score launch");
+  if (topk_out == nullptr) return ok();  // scores only (msa_sparse_decode_select_run selects)
   return msa_topk_select(score, score_strides, shape->num_kv_heads, max_blocks, num_rows,
                          topk_out, topk_k, stream);
 }

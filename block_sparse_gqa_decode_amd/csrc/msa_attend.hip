@@ -85,6 +85,7 @@
 #include "msa_internal.h"
 #include "msa_page.h"
 #include "msa_rows.h"
+#include "msa_select.h"
 
 namespace msa {
 namespace {
@@ -206,9 +207,16 @@ __device__ __forceinline__ void fused_merge(const AttendParams& p, int unit, int
   else combine_splits<4>(ro, rm, qr, d0, dst, p.v_scale);
 }
 
-template <int kKv, int kQ, bool kVarlen>
+// kSelPer > 0 (decode rows): the workgroup selects its row's top-k from the
+// block scores itself (select_row, kSelPer scores per thread) instead of
+// reading a top-k row, so an indexed step needs no separate selector launch
+// and no top-k round trip through memory.
+template <int kKv, int kQ, bool kVarlen, int kSelPer = 0>
 __global__ __launch_bounds__(kThreads) void attend_kernel(AttendParams p) {
   constexpr int kKind = kv_kind(kKv);
+  static_assert(kSelPer == 0 || (kThreads == kSelThreads && !kVarlen), "selecting attend");
+  __shared__ SelShared s_selsh;
+  __shared__ int32_t s_sel[kMaxTopk];
   __shared__ int32_t s_page[kMaxTopk];
   __shared__ int32_t s_nvis[kMaxTopk];
   __shared__ int32_t s_nlive;
@@ -264,6 +272,10 @@ __global__ __launch_bounds__(kThreads) void attend_kernel(AttendParams p) {
         uint16_t* dst = p.out + ((int64_t)t * p.hq + h * p.group + qr) * kHeadDim + d0;
         *reinterpret_cast<u32x4_t*>(dst) = u32x4_t{0u, 0u, 0u, 0u};
       }
+      // A padding row selects nothing (as the selector gives for its -inf
+      // scores).
+      if (kSelPer > 0 && p.sel_topk_out != nullptr && tid < p.topk_k)
+        p.sel_topk_out[((int64_t)t * p.hkv + h) * p.topk_k + tid] = -1;
     }
     return;
   }
@@ -274,11 +286,19 @@ __global__ __launch_bounds__(kThreads) void attend_kernel(AttendParams p) {
   // constant address space) are both in flight before either is used, and
   // the filter takes no short cuts, so neither read waits behind the other:
   // top-k and length, then the block table, then the pages.
+  if constexpr (kSelPer > 0) {
+    select_row<kSelPer>(p.sel_score + h * p.sel_s0 + (int64_t)t * p.sel_s2, p.sel_s1,
+                        p.sel_max_blocks, p.topk_k, s_selsh, s_sel);
+    __syncthreads();
+    if (p.sel_topk_out != nullptr && split == 0 && tid < p.topk_k)
+      p.sel_topk_out[((int64_t)t * p.hkv + h) * p.topk_k + tid] = s_sel[tid];
+  }
   if (wave == 0) {
     bool live = false;
     int page = 0, nvis = 0;
     const int li = lane < p.topk_k ? lane : 0;
-    const int b_raw = p.topk[t * p.tk_s0 + h * p.tk_s1 + li * p.tk_s2];
+    const int b_raw =
+        kSelPer > 0 ? s_sel[li] : p.topk[t * p.tk_s0 + h * p.tk_s1 + li * p.tk_s2];
     if constexpr (!kVarlen)
       pos = ((const const_i32*)p.seq_lens)[r] - p.dql + (t - r * p.dql);
     const int b = lane < p.topk_k ? b_raw : -1;
@@ -556,10 +576,46 @@ static hipError_t launch_attend_rows(const AttendParams& p, int kv_fmt, int q_fm
   return hipGetLastError();
 }
 
+template <int kSelPer>
+static hipError_t launch_attend_select(const AttendParams& p, int kv_fmt, int q_fmt, dim3 gd,
+                                       hipStream_t stream) {
+  const dim3 bd(kThreads);
+  if (q_fmt == kQE4m3) {
+    if (kv_fmt == kKvE4m3)
+      hipLaunchKernelGGL((attend_kernel<kKvE4m3, kQE4m3, false, kSelPer>), gd, bd, 0, stream, p);
+    else if (kv_fmt == kKvE5m2)
+      hipLaunchKernelGGL((attend_kernel<kKvE5m2, kQE4m3, false, kSelPer>), gd, bd, 0, stream, p);
+    else if (kv_fmt == kKvMxfp4)
+      hipLaunchKernelGGL((attend_kernel<kKvMxfp4, kQE4m3, false, kSelPer>), gd, bd, 0, stream,
+                         p);
+    else
+      return hipErrorInvalidValue;
+  } else {
+    if (kv_fmt == kKvE4m3)
+      hipLaunchKernelGGL((attend_kernel<kKvE4m3, kQBf16, false, kSelPer>), gd, bd, 0, stream, p);
+    else if (kv_fmt == kKvE5m2)
+      hipLaunchKernelGGL((attend_kernel<kKvE5m2, kQBf16, false, kSelPer>), gd, bd, 0, stream, p);
+    else if (kv_fmt == kKvMxfp4)
+      hipLaunchKernelGGL((attend_kernel<kKvMxfp4, kQBf16, false, kSelPer>), gd, bd, 0, stream,
+                         p);
+    else
+      hipLaunchKernelGGL((attend_kernel<kKvBf16, kQBf16, false, kSelPer>), gd, bd, 0, stream, p);
+  }
+  return hipGetLastError();
+}
+
 hipError_t launch_attend(const AttendParams& p, int kv_fmt, int q_fmt, hipStream_t stream) {
   const int64_t grid = xcd_groups(p.num_units, p.hkv) * kXcdSlots * p.splits;
   if (grid <= 0) return hipSuccess;
   const dim3 gd((uint32_t)grid);
+  if (p.sel_score != nullptr) {
+    // 8 scores per thread cover 2048 blocks (a 256k-token context); 64 the
+    // largest score row.
+    if (p.cu_q != nullptr) return hipErrorInvalidValue;
+    return p.sel_max_blocks <= 8 * kSelThreads
+               ? launch_attend_select<8>(p, kv_fmt, q_fmt, gd, stream)
+               : launch_attend_select<64>(p, kv_fmt, q_fmt, gd, stream);
+  }
   return p.cu_q != nullptr ? launch_attend_rows<true>(p, kv_fmt, q_fmt, gd, stream)
                            : launch_attend_rows<false>(p, kv_fmt, q_fmt, gd, stream);
 }

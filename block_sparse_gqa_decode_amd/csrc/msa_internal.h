@@ -108,6 +108,14 @@ struct AttendParams {
   // one arrival counter per unit, zero between launches; null = the merge
   // kernel combines the partials instead.
   int32_t* arrivals;
+  // Single-row decode attend that selects its own top-k (null = read topk):
+  // fp32 block scores [hkv, sel_max_blocks, rows] with element strides
+  // sel_s0..2; the selection is also written to sel_topk_out
+  // ([rows, hkv, topk_k], contiguous) when that is not null.
+  const float* sel_score;
+  int64_t sel_s0, sel_s1, sel_s2;
+  int32_t sel_max_blocks;
+  int32_t* sel_topk_out;
 };
 
 constexpr int kMaxFusedSplits = 4;

@@ -48,15 +48,27 @@ msa_status check_common_shape(const msa_decode_shape* s);
 msa_status plan_config(const msa_decode_shape* shape, bool prefill, int32_t real_rows,
                        int device, bool allow_fused, msa_plan_s* plan);
 
+// The block scores a single-row decode attend selects its own top-k from
+// (msa_sparse_decode_select_run); topk_out may be null.
+struct SelectSource {
+  const float* score;
+  int64_t s0, s1, s2;
+  int32_t max_blocks;
+  int32_t* topk_out;
+};
+
 // One decode or prefill run of a configured plan whose arena pointers are set
 // (seq_lens for decode, cu_q / ctx for prefill); `merge` false launches the
-// attend alone.  Validates every run argument before any HIP call.
+// attend alone.  With `sel`, topk is NULL and the attend selects each row's
+// top-k from the scores itself.  Validates every run argument before any HIP
+// call.
 msa_status run_plan(const msa_plan_s* plan, const void* q, const void* kv_cache,
                     const int64_t kv_strides[4], int64_t num_kv_blocks, float q_scale,
                     float k_scale, float v_scale, const int32_t* block_table,
                     const int32_t* seq_lens, const int32_t* cu_q, const int32_t* ctx,
                     const int32_t* topk, const int64_t topk_strides[3], void* out,
-                    float sm_scale, void* stream, bool merge);
+                    float sm_scale, void* stream, bool merge,
+                    const SelectSource* sel = nullptr);
 
 // Makes `dev` the current HIP device for the guard's lifetime.
 struct DeviceGuard {

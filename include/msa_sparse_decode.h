@@ -53,7 +53,7 @@
 extern "C" {
 #endif
 
-#define MSA_ABI_VERSION 6
+#define MSA_ABI_VERSION 7
 
 typedef enum msa_status {
   MSA_OK = 0,
@@ -307,6 +307,8 @@ msa_status msa_sparse_prefill_run(msa_plan plan, const void* q, const void* kv_c
  *                back on; the scores stay readable after the call.
  *   max_blocks   1..16384, at least ceil(max seq_len / 128).
  *   topk_out     int32 [num_token_rows, Hkv, topk_k], contiguous; topk_k 1..64.
+ *                NULL: the scores alone (one launch), for
+ *                msa_sparse_decode_select_run to select from.
  */
 msa_status msa_block_score_topk(const msa_decode_shape* shape, const void* q,
                                 const void* kv_cache, const int64_t kv_strides[4],
@@ -325,6 +327,37 @@ msa_status msa_block_score_topk(const msa_decode_shape* shape, const void* q,
 msa_status msa_topk_select(const float* score, const int64_t score_strides[3],
                            int32_t num_kv_heads, int32_t max_blocks, int32_t num_rows,
                            int32_t* topk_out, int32_t topk_k, void* stream);
+
+/* The selector and the attend of an indexed decode step in one launch: each
+ * (token row, kv head) workgroup of a single-row plan selects its row's
+ * top-k blocks from `score` (the msa_topk_select rule: the topk_blocks
+ * blocks with the largest score > -inf, ties to the lower block id, -1
+ * padding) and attends over them as msa_sparse_decode_run would over that
+ * top-k row.  No top-k row goes through memory between the two.
+ * Defined by: TensorRT-LLM PR #17171, indexer-scorer commit (block scores ->
+ * top-k selector -> the sparse attend over the selected blocks) and
+ * flash-decoding commit (the attend); vLLM sparse-attention page,
+ * MiniMaxM3SparseImpl (the attend over the selected blocks).
+ *   plan         a sparse decode plan with tile_rows 1 (single-row); a dense,
+ *                prefill or multi-row plan is MSA_ERR_UNSUPPORTED.  Splits as
+ *                for msa_sparse_decode_run (each split selects the same row).
+ *   q .. seq_lens, out, sm_scale, stream: as for msa_sparse_decode_run.
+ *   score        float32 logical [Hkv, max_blocks, num_token_rows] with
+ *                score_strides (elements), e.g. msa_block_score_topk's buffer;
+ *                read only.
+ *   max_blocks   1..16384.  Up to 2048 blocks the selecting workgroup keeps
+ *                two wavefronts per SIMD; larger rows run at one.
+ *   topk_out     NULL, or int32 [num_token_rows, Hkv, topk_blocks],
+ *                contiguous: receives the selection (padding rows all -1),
+ *                exactly what msa_topk_select gives for the same scores.
+ */
+msa_status msa_sparse_decode_select_run(msa_plan plan, const void* q, const void* kv_cache,
+                                        const int64_t kv_strides[4], int64_t num_kv_blocks,
+                                        float q_scale, float k_scale, float v_scale,
+                                        const int32_t* block_table, const int32_t* seq_lens,
+                                        const float* score, const int64_t score_strides[3],
+                                        int32_t max_blocks, int32_t* topk_out, void* out,
+                                        float sm_scale, void* stream);
 
 /* Decode n OCP fp8 e4m3fn codes to bf16 with the same in-register conversion
  * the attend uses (a self-check of the conversion path).  The format is the

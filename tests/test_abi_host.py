@@ -319,8 +319,7 @@ def _score(lib, s, **over):
 
 
 @pytest.mark.parametrize("over,fragment", [
-    (dict(sc=None), "score and topk_out"),
-    (dict(to=None), "score and topk_out"),
+    (dict(sc=None), "score must be"),
     (dict(mb=0), "max_blocks"),
     (dict(mb=16385), "max_blocks"),
     (dict(k=0), "topk_k"),
@@ -334,6 +333,15 @@ def _score(lib, s, **over):
 def test_score_topk_rejects_bad_arguments(lib, over, fragment):
     st, msg = _score(lib, shape(batch=2, decode_query_len=4), **over)
     assert st == msa.MSA_ERR_INVALID_ARG and fragment in msg, (st, msg)
+
+
+def test_score_without_topk_out_checks_everything_else(lib):
+    """topk_out = NULL asks for the scores alone (topk_k is then unused); the
+    other arguments are still checked before any HIP call."""
+    st, msg = _score(lib, shape(batch=2, decode_query_len=4), to=None, k=0, mb=0)
+    assert st == msa.MSA_ERR_INVALID_ARG and "max_blocks" in msg
+    st, msg = _score(lib, shape(batch=2, decode_query_len=4), to=None, k=0, qs=0.0)
+    assert st == msa.MSA_ERR_INVALID_ARG and "positive" in msg
 
 
 def test_score_topk_validates_shape(lib):
@@ -629,3 +637,57 @@ def test_eight_row_tiles_need_an_8bit_cache(lib):
     for kvd in (msa.KV_FP8_E4M3, msa.KV_FP8_E5M2):
         st, msg = plan_status(lib, shape(tile_rows=8, kv_dtype=kvd, num_splits=1))
         assert st == 0, (kvd, msg)
+
+
+def _select_run(lib, h, **over):
+    args = dict(q=FAKE, kv=FAKE, kvs=(256 * 128, 256 * 128, 256, 1), nb=10, bt=FAKE, sl=FAKE,
+                sc=FAKE, scs=(64 * 16, 16, 1), mb=64, tko=None, out=FAKE, sm=0.088)
+    args.update(over)
+    kvs = msa._I64x4(*args["kvs"])
+    scs = msa._I64x3(*args["scs"]) if args["scs"] is not None else None
+    st = lib.msa_sparse_decode_select_run(h, args["q"], args["kv"], kvs, args["nb"], 1.0, 1.0,
+                                          1.0, args["bt"], args["sl"], args["sc"], scs,
+                                          args["mb"], args["tko"], args["out"], args["sm"],
+                                          None)
+    return st, lib.msa_last_error().decode()
+
+
+@pytest.mark.parametrize("over,fragment", [
+    (dict(sc=None), "score"),
+    (dict(scs=None), "score_strides"),
+    (dict(scs=(64 * 16, -16, 1)), "score strides"),
+    (dict(mb=0), "max_blocks"),
+    (dict(mb=16385), "max_blocks"),
+    (dict(q=None), "q and out"),
+    (dict(bt=None), "block_table"),
+])
+def test_select_run_rejects_bad_arguments(lib, over, fragment):
+    h = _plan(lib)
+    try:
+        st, msg = _select_run(lib, h, **over)
+        assert st == msa.MSA_ERR_INVALID_ARG and fragment in msg, (st, msg)
+    finally:
+        lib.msa_sparse_decode_plan_destroy(h)
+
+
+@pytest.mark.parametrize("kw", [dict(topk_blocks=0), dict(decode_query_len=8, tile_rows=2)])
+def test_select_run_needs_a_single_row_sparse_plan(lib, kw):
+    """The selecting attend is the single-row kernel's; a dense plan or a
+    row-tile plan is refused before any HIP call."""
+    h = _plan(lib, **kw)
+    try:
+        st, msg = _select_run(lib, h)
+        assert st == msa.MSA_ERR_UNSUPPORTED and "single-row" in msg, (st, msg)
+    finally:
+        lib.msa_sparse_decode_plan_destroy(h)
+
+
+def test_select_run_refuses_a_prefill_plan(lib):
+    plan = msa.msa_sparse_prefill_plan(2, 40, num_q_heads=16, num_kv_heads=1,
+                                       page_table_stride=10, topk_blocks=8,
+                                       kv_dtype=msa.KV_FP8_E4M3, num_splits=1, device=0)
+    try:
+        st, msg = _select_run(lib, plan.handle)
+        assert st == msa.MSA_ERR_INVALID_ARG and "prefill" in msg
+    finally:
+        plan.close()

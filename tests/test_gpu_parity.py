@@ -754,3 +754,90 @@ def test_c5_full_step_full_size_sampled_rows():
     assert ok_rows
     ref_out = oracle_attend(case, rows=ok_rows, topk=full_sel)
     assert_parity(to_f64(out)[ok_rows], ref_out, what=f"c5 attend on {len(ok_rows)} rows")
+
+
+@pytest.mark.parametrize("kvd,qd,qs,splits,mb_extra", [
+    (gen.KV_FP8, gen.Q_BF16, 1.0, 1, 0),
+    (gen.KV_FP8, gen.Q_BF16, 1.0, 2, 0),        # the in-attend split merge
+    (gen.KV_FP8, gen.Q_FP8, 0.5, 8, 0),         # the merge kernel
+    (gen.KV_E5M2, gen.Q_BF16, 1.0, 3, 0),
+    (gen.KV_MXFP4, gen.Q_FP8, 0.5, 1, 0),
+    (gen.KV_FP8, gen.Q_BF16, 1.0, 1, 2100),     # more than 2048 score columns
+])
+def test_select_run_equals_select_then_run(kvd, qd, qs, splits, mb_extra):
+    """msa_sparse_decode_select_run selects each row's top-k from the scores
+    inside the attend: its output and selection equal, bit for bit, the
+    selector's top-k fed to msa_sparse_decode_run (padding rows: zeros and
+    all -1), and the rows match the oracle over that selection."""
+    _banner(f"select_run kv={kvd} q={qd} splits={splits} extra columns={mb_extra}")
+    case = gen.make_random_case(143, 5, 2, 64, 4, 16, 1500, 40000, kv_dtype=kvd, q_dtype=qd,
+                                q_scale=qs, pad_rows=3)
+    d = DevCase(case)
+    mb = case.max_blocks + mb_extra
+    rows = case.num_token_rows
+    score = torch.full((case.num_kv_heads, mb, rows), float("nan"), device="cuda")
+    sel = torch.full((rows, case.num_kv_heads, 16), -7, dtype=torch.int32, device="cuda")
+    d.score(score, sel, mb, num_token_rows=rows)
+    plan = d.plan(splits, tile_rows=1)
+    assert plan.num_splits == splits
+    ref = d.new_out()
+    d.run(plan, topk=sel, out=ref)
+    got = d.new_out()
+    sel2 = torch.full_like(sel, -7)
+    msa.msa_sparse_decode_select_run(plan, d.q, d.kv, d.block_table, d.seq_lens, score, got,
+                                     topk_out=sel2, sm_scale=case.sm_scale,
+                                     k_scale=case.k_scale, v_scale=case.v_scale,
+                                     q_scale=case.q_scale)
+    torch.cuda.synchronize()
+    assert torch.equal(sel2, sel)
+    assert torch.equal(got.view(torch.int16), ref.view(torch.int16))
+    assert np.all(to_f64(got)[case.real_rows:] == 0.0)
+    case.topk = sel.cpu().numpy()
+    rows_chk = list(range(0, case.real_rows, 3))
+    assert_parity(to_f64(got)[rows_chk], oracle_attend(case, rows=rows_chk),
+                  what="select_run rows")
+
+
+def test_select_run_in_a_graph_with_new_scores():
+    """Captured once, replayed with the score buffer rewritten in place: every
+    replay selects from the scores it finds (the selection equals the
+    selector's on the same scores)."""
+    _banner("select_run graph replay")
+    case = gen.make_random_case(144, 4, 1, 16, 1, 16, 3000, 20000)
+    d = DevCase(case)
+    mb = case.max_blocks
+    rows = case.num_token_rows
+    score = torch.full((1, mb, rows), float("nan"), device="cuda")
+    sel = torch.full((rows, 1, 16), -7, dtype=torch.int32, device="cuda")
+    d.score(score, sel, mb, num_token_rows=rows)
+    torch.cuda.synchronize()
+    plan = d.plan(2, tile_rows=1)
+    out = d.new_out()
+    got_sel = torch.full_like(sel, -7)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        msa.msa_sparse_decode_select_run(plan, d.q, d.kv, d.block_table, d.seq_lens, score,
+                                         out, topk_out=got_sel, sm_scale=case.sm_scale,
+                                         stream=s)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        msa.msa_sparse_decode_select_run(plan, d.q, d.kv, d.block_table, d.seq_lens, score,
+                                         out, topk_out=got_sel, sm_scale=case.sm_scale)
+    rng = np.random.default_rng(7)
+    finite = torch.isfinite(score)
+    for rep in range(3):
+        noise = torch.from_numpy(rng.standard_normal(tuple(score.shape)).astype(np.float32))
+        score.copy_(torch.where(finite, noise.cuda(), score))
+        ref_sel = torch.full_like(sel, -7)
+        msa.msa_topk_select(score, ref_sel)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(got_sel, ref_sel), rep
+        ref = d.new_out()
+        d.run(d.plan(2, tile_rows=1), topk=ref_sel, out=ref)
+        torch.cuda.synchronize()
+        assert torch.equal(out.view(torch.int16), ref.view(torch.int16)), rep
