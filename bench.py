@@ -37,6 +37,7 @@ import json
 import os
 import sys
 import time
+from typing import Optional
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
 if ROOT not in sys.path:
@@ -62,10 +63,12 @@ KERNEL_SOURCES = {
     "attend": ("block_sparse_gqa_decode_amd/csrc/msa_attend.hip",
                "block_sparse_gqa_decode_amd/csrc/msa_page.h",
                "block_sparse_gqa_decode_amd/csrc/msa_rows.h",
+               "block_sparse_gqa_decode_amd/csrc/msa_select.h",
                "block_sparse_gqa_decode_amd/csrc/msa_device.h",
                "block_sparse_gqa_decode_amd/csrc/msa_internal.h"),
     "score": ("block_sparse_gqa_decode_amd/csrc/msa_score.hip",
               "block_sparse_gqa_decode_amd/csrc/msa_page.h",
+              "block_sparse_gqa_decode_amd/csrc/msa_select.h",
               "block_sparse_gqa_decode_amd/csrc/msa_device.h",
               "block_sparse_gqa_decode_amd/csrc/msa_internal.h"),
     # the multi-row tile kernel (c4, pf1, d1 plans)
@@ -602,7 +605,8 @@ def scorer_bytes(case):
         case.num_kv_heads * case.dql
     mfma_flops = items * 2 * 16 * 128 * 128
     return {"k_half": k_bytes, "scorer": scorer, "selector": selector,
-            "algorithmic": scorer + selector, "mfma_flops": mfma_flops}
+            "score_read": score_bytes, "topk": topk_bytes, "algorithmic": scorer + selector,
+            "mfma_flops": mfma_flops}
 
 
 class FullStepSet:
@@ -795,6 +799,16 @@ def time_full_step(name, steps, warmup, replicas, dev, verbose=True):
         None if at is None else at.get("hbm_bytes_per_launch"),
         {"kernel": f"attend_kernel<kv {case.kv_dtype}, q {case.q_dtype}>",
          "basis": UNIQUE_BASIS, "timing": "HIP events around graph replays of the attend"})
+    # The attend of the two-launch step: the same pages plus one read of
+    # every (token row, kv head) score row it selects from, and no top-k read.
+    sa = load_traffic(name, "attend", record="select_attend")
+    res["select_attend_roofline"] = _roofline(
+        uq - sb["topk"] + sb["score_read"], fl, select_attend_ms / 1e3, MFMA_PEAK_TFLOPS[False],
+        None if sa is None else sa.get("hbm_bytes_per_launch"),
+        {"kernel": f"attend_kernel<kv {case.kv_dtype}, q {case.q_dtype}, selecting>",
+         "basis": UNIQUE_BASIS + ", with the score rows it selects from in place of the "
+                  "top-k entries",
+         "timing": "HIP events around graph replays of the selecting attend"})
     res["step_pct_hbm_peak"] = 100 * res["step_algorithmic_gbs"] / HBM_PEAK_GBS
     del fs
     torch.cuda.empty_cache()
@@ -977,12 +991,13 @@ def traffic_path(config: str, kernel: str) -> str:
     return os.path.join(TRAFFIC_DIR, f"{kernel}_{config}_traffic.json")
 
 
-def load_traffic(config: str, kernel: str):
+def load_traffic(config: str, kernel: str, record: Optional[str] = None):
     """HBM bytes per launch of `kernel` on `config` from the committed
-    rocprofv3 counter summary, if it was taken on the current sources of that
-    kernel; else None."""
+    rocprofv3 counter summary (file named for `record`, default the kernel's
+    own name), if it was taken on the current sources of that kernel; else
+    None."""
     try:
-        with open(traffic_path(config, kernel)) as f:
+        with open(traffic_path(config, record or kernel)) as f:
             rec = json.load(f)
     except (OSError, ValueError):
         return None
