@@ -341,7 +341,15 @@ void multi_kernel(AttendParams p) {
   const int kbase = wave * kKeysPerWave;
   const uint8_t* head_base = p.kv + h * p.kv_s1;
   const uint32_t row_stride = (uint32_t)p.kv_s2;
-  const LaneRows lr = lane_rows<kKind>(kbase, n, g);
+  // 2-row decode tiles read each page through a buffer descriptor bounded at
+  // the tile's largest visible count (zeros past it, the lane offsets fixed
+  // for the launch), as the single-row attend does: c4 82.7 -> 81.5 us.  The
+  // other tiles keep the clamped loads: the launch-long lane offsets add
+  // spills to the three-wave prefill tiles (pf1 613 -> 621 us), and the 4-row
+  // dense tiles ran 316 -> 368 us with them.
+  constexpr bool kBoundedLoads = kM == 2 && !kOcc3;
+  LaneRows lr = lane_rows<kKind>(kbase, n, g);
+  if constexpr (kBoundedLoads) lane_offsets(lr, row_stride);
   const int32_t* dense_row =
       p.block_table + (int64_t)(dense_r >= 0 ? dense_r : 0) * p.bt_stride;
 
@@ -375,8 +383,11 @@ void multi_kernel(AttendParams p) {
       uint32_t vmax = 0;
 #pragma unroll
       for (int w = 0; w < kM; ++w) vmax = max(vmax, (nv4 >> (8 * w)) & 0xffu);
-      load_page<kKind>(r, head_base + (int64_t)pg * p.kv_s0, row_stride,
-                       (int)max(vmax, 1u) - 1, lr);
+      if constexpr (kBoundedLoads)
+        load_page_rows<kKind>(r, head_base + (int64_t)pg * p.kv_s0, row_stride, (int)vmax, lr);
+      else
+        load_page<kKind>(r, head_base + (int64_t)pg * p.kv_s0, row_stride,
+                         (int)max(vmax, 1u) - 1, lr);
       return nv4;
     };
 
