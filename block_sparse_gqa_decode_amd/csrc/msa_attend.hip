@@ -224,6 +224,11 @@ __global__ __launch_bounds__(kThreads) void attend_kernel(AttendParams p) {
   __shared__ float s_m[kWaves][16];
   __shared__ float s_l[kWaves][16];
   __shared__ float s_o[kWaves][16][kHeadDim + kOPad];
+  // The selecting attend's staged block-table row (see below).
+  constexpr bool kStageTable = kSelPer > 0;
+  constexpr int kTableCap = kStageTable ? kTableLoads * kThreads : 1;
+  __shared__ int32_t s_table[kTableCap];
+  __shared__ int32_t s_len;
 
   // Every kernel argument the prologue reads, fetched as one batch of scalar
   // loads: left to itself the compiler loads them in three dependent
@@ -286,24 +291,64 @@ __global__ __launch_bounds__(kThreads) void attend_kernel(AttendParams p) {
   // constant address space) are both in flight before either is used, and
   // the filter takes no short cuts, so neither read waits behind the other:
   // top-k and length, then the block table, then the pages.
-  if constexpr (kSelPer > 0) {
+  //
+  // The selecting attend instead reads its row's block-table entries (the
+  // first kTableCap, coalesced across the workgroup) and length together
+  // with the score row it selects from, so the selected pages follow from
+  // LDS: 32.2 -> 31.9 us a launch on the indexed full step.  The top-k
+  // attend gained nothing from the same staging (its table read is not what
+  // bounds the launch), so it keeps the chain.
+  const int li = lane < p.topk_k ? lane : 0;
+  int b_raw = 0;
+  int table_n = 0;
+  if constexpr (kStageTable) {
+    table_n = min(p.bt_stride, kTableCap);
+    // Clamped, unconditional loads (entries past the row's end are never
+    // stored): a per-lane condition would branch around every load.
+    int32_t tv[kTableLoads];
+    const int32_t* trow = p.block_table + (int64_t)r * p.bt_stride;
+#pragma unroll
+    for (int i = 0; i < kTableLoads; ++i) tv[i] = trow[min(tid + i * kThreads, table_n - 1)];
+    // The length travels with the table entries (every thread stores the
+    // same value), so its read cannot be sunk behind them.
+    const int len = p.seq_lens[r];
     select_row<kSelPer>(p.sel_score + h * p.sel_s0 + (int64_t)t * p.sel_s2, p.sel_s1,
                         p.sel_max_blocks, p.topk_k, s_selsh, s_sel);
+#pragma unroll
+    for (int i = 0; i < kTableLoads; ++i) {
+      const int e = tid + i * kThreads;
+      if (e < table_n) s_table[e] = tv[i];
+    }
+    s_len = len;
     __syncthreads();
+    pos = s_len - p.dql + (t - r * p.dql);
     if (p.sel_topk_out != nullptr && split == 0 && tid < p.topk_k)
       p.sel_topk_out[((int64_t)t * p.hkv + h) * p.topk_k + tid] = s_sel[tid];
+    b_raw = s_sel[li];
   }
   if (wave == 0) {
     bool live = false;
     int page = 0, nvis = 0;
-    const int li = lane < p.topk_k ? lane : 0;
-    const int b_raw =
-        kSelPer > 0 ? s_sel[li] : p.topk[t * p.tk_s0 + h * p.tk_s1 + li * p.tk_s2];
-    if constexpr (!kVarlen)
-      pos = ((const const_i32*)p.seq_lens)[r] - p.dql + (t - r * p.dql);
+    if constexpr (!kStageTable) {
+      b_raw = p.topk[t * p.tk_s0 + h * p.tk_s1 + li * p.tk_s2];
+      if constexpr (!kVarlen)
+        pos = ((const const_i32*)p.seq_lens)[r] - p.dql + (t - r * p.dql);
+    }
     const int b = lane < p.topk_k ? b_raw : -1;
     if ((b >= 0) & (b < p.bt_stride) & ((int64_t)b * kPage <= pos)) {
-      const int pg = p.block_table[(int64_t)r * p.bt_stride + b];
+      int pg;
+      if constexpr (kStageTable) {
+        // An LDS read for every lane, a global read only for blocks past
+        // the staged entries (kept apart, so no flat load picks between
+        // them).
+        pg = s_table[min(b, table_n - 1)];
+        if (b >= table_n) {
+          pg = p.block_table[(int64_t)r * p.bt_stride + b];
+          asm volatile("" : "+v"(pg));
+        }
+      } else {
+        pg = p.block_table[(int64_t)r * p.bt_stride + b];
+      }
       if (pg >= 0 && pg < p.num_kv_blocks) {
         live = true;
         page = pg;

@@ -26,6 +26,7 @@ namespace msa {
 constexpr int kWaves = 4;      // wavefronts sharing one page (32 keys each)
 constexpr int kThreads = 64 * kWaves;
 constexpr int kDepth = 2;      // pages per wavefront in the register ring
+constexpr int kTableLoads = 8; // block-table entries per thread read ahead (2048 a workgroup)
 
 constexpr int kKeysPerWave = 32;
 constexpr int kOPad = 4;
