@@ -798,6 +798,39 @@ def test_select_run_equals_select_then_run(kvd, qd, qs, splits, mb_extra):
                   what="select_run rows")
 
 
+def test_select_run_rows_longer_than_the_staged_table():
+    """Rows of more than 2048 blocks: the selecting attend stages only the
+    first 2048 block-table entries of a request, and reads the entries of
+    later selected blocks from the table itself.  Equal, bit for bit, to the
+    selector's top-k fed to msa_sparse_decode_run, and to the oracle."""
+    _banner("select_run rows past the staged table (seq 270k..300k)")
+    case = gen.make_random_case(145, 2, 2, 16, 1, 16, 270000, 300000, pad_rows=1)
+    d = DevCase(case)
+    mb = case.max_blocks
+    assert mb > 2048
+    rows = case.num_token_rows
+    score = torch.full((1, mb, rows), float("nan"), device="cuda")
+    sel = torch.full((rows, 1, 16), -7, dtype=torch.int32, device="cuda")
+    d.score(score, sel, mb, num_token_rows=rows)
+    plan = d.plan(1, tile_rows=1)
+    ref = d.new_out()
+    d.run(plan, topk=sel, out=ref)
+    got = d.new_out()
+    sel2 = torch.full_like(sel, -7)
+    msa.msa_sparse_decode_select_run(plan, d.q, d.kv, d.block_table, d.seq_lens, score, got,
+                                     topk_out=sel2, sm_scale=case.sm_scale)
+    torch.cuda.synchronize()
+    picked = sel.cpu().numpy()
+    assert (picked[: case.real_rows] >= 2048).any(), "no selected block past the staged entries"
+    assert torch.equal(sel2, sel)
+    assert torch.equal(got.view(torch.int16), ref.view(torch.int16))
+    case.topk = picked
+    assert_parity(to_f64(got)[: case.real_rows],
+                  oracle_attend(case, rows=list(range(case.real_rows))),
+                  what="select_run long rows")
+    assert np.all(to_f64(got)[case.real_rows:] == 0.0)
+
+
 def test_select_run_in_a_graph_with_new_scores():
     """Captured once, replayed with the score buffer rewritten in place: every
     replay selects from the scores it finds (the selection equals the
