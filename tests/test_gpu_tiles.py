@@ -52,7 +52,7 @@ def test_random_cases_on_tiles(tile_rows, seed, batch, dql, hq, hkv, k, lo, hi, 
     assert np.all(got[case.real_rows:] == 0.0)
 
 
-@pytest.mark.parametrize("tile_rows", [4, 8])
+@pytest.mark.parametrize("tile_rows", [2, 4, 8])
 @pytest.mark.parametrize("seed,batch,dql,hq,hkv,k,lo,hi,kvd,qd,qs,pad,neg,splits,layout",
                          base.FORMAT_RANDOM_CASES)
 def test_format_cases_on_tiles(tile_rows, seed, batch, dql, hq, hkv, k, lo, hi, kvd, qd, qs,
