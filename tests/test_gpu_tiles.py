@@ -1,8 +1,8 @@
 """GPU parity of the multi-row tile kernels and of dense decode.
 
 The tile kernels (several token rows per workgroup, each page shared by its
-rows read once: register-staged pages for 2-row tiles and 16-bit or 4-bit
-caches, LDS-staged pages for 4- and 8-row tiles over 8-bit caches) must give
+rows read once: pages staged in registers for 2- and 4-row tiles, through an
+LDS ring for 8-row tiles over 8-bit caches) must give
 what the oracle gives for any tile size: the randomized decode cases and the
 format cases are rerun on 2-, 4- and 8-row tiles,
 the single-row kernel is checked on a long decode query length, and dense
