@@ -79,14 +79,20 @@ struct LaneRows {
   uint32_t ov[8];
 };
 
-template <int kKind>
+// kWholeK (8-bit K, the row-tile kernels): each K load reads 8 whole rows,
+// lane 16g + n taking row 2g + n / 8 of the 8 and bytes 16 (n % 8) .. +15,
+// the second load the next 8 rows; k8_whole_to_mfma then moves the bytes
+// into the MFMA's layout.
+template <int kKind, bool kWholeK = false>
 __device__ __forceinline__ LaneRows lane_rows(int kbase, int n, int g) {
   LaneRows lr;
+  constexpr bool kWhole = kWholeK && kKind == 1;
 #pragma unroll
-  for (int tau = 0; tau < 2; ++tau) lr.rk[tau] = kbase + 16 * tau + n;
+  for (int tau = 0; tau < 2; ++tau)
+    lr.rk[tau] = kbase + 16 * tau + (kWhole ? 2 * g + (n >> 3) : n);
 #pragma unroll
   for (int j = 0; j < 8; ++j) lr.rv[j] = kbase + key_of_slot(g, j);
-  lr.ck = kKind == 0 ? 32u * g : 16u * g;
+  lr.ck = kKind == 0 ? 32u * g : (kWhole ? 16u * (uint32_t)(n & 7) : 16u * g);
   lr.cv = kKind == 0 ? 2 * kHeadDim + 16u * n : (kKind == 1 ? kHeadDim + 8u * n : 4u * n);
   lr.ksh = 8u * g;
   lr.vsh = 8u * (n >> 2);
@@ -111,7 +117,7 @@ constexpr uint32_t kF4ScaleBase = kPage * kF4RowBytes;
 // per-lane part of every address is a 32-bit offset.  `row_stride` is the
 // byte stride of packed K|V rows, or for 4-bit pages the K slot -> V slot
 // offset.
-template <int kKind>
+template <int kKind, bool kWholeK = false>
 __device__ __forceinline__ void load_page(PageRegs<kKind>& r, const uint8_t* page,
                                           uint32_t row_stride, int lim, const LaneRows& lr) {
   if constexpr (kKind == 2) {
@@ -134,7 +140,11 @@ __device__ __forceinline__ void load_page(PageRegs<kKind>& r, const uint8_t* pag
 #pragma unroll
     for (int tau = 0; tau < 2; ++tau) {
       const uint32_t off = __umul24((uint32_t)min(lr.rk[tau], lim), row_stride) + lr.ck;
-      if constexpr (kKind == 1) {
+      if constexpr (kKind == 1 && kWholeK) {
+        const uint32_t off8 = __umul24((uint32_t)min(lr.rk[tau] + 8, lim), row_stride) + lr.ck;
+        r.k[tau][0] = *reinterpret_cast<const u32x4_t*>(page + off);
+        r.k[tau][1] = *reinterpret_cast<const u32x4_t*>(page + off8);
+      } else if constexpr (kKind == 1) {
         r.k[tau][0] = *reinterpret_cast<const u32x4_t*>(page + off);
         r.k[tau][1] = *reinterpret_cast<const u32x4_t*>(page + off + 64);
       } else {
@@ -164,7 +174,7 @@ constexpr int kRsrcWord3 = 0x00020000;    // raw buffer descriptor, gfx9 family
 // offset is recomputed per page (16- and 8-bit pages; offsets from
 // lane_offsets).  4-bit pages, whose data and scales are separate runs, take
 // the clamped loads of load_page.
-template <int kKind>
+template <int kKind, bool kWholeK = false>
 __device__ __forceinline__ void load_page_rows(PageRegs<kKind>& r, const uint8_t* page,
                                                uint32_t row_stride, int nvis,
                                                const LaneRows& lr) {
@@ -178,8 +188,9 @@ __device__ __forceinline__ void load_page_rows(PageRegs<kKind>& r, const uint8_t
       if constexpr (kKind == 1) {
         r.k[tau][0] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(
                                                       rs, lr.ok[tau], 0, 0));
-        r.k[tau][1] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(
-                                                      rs, lr.ok[tau] + 64, 0, 0));
+        r.k[tau][1] = __builtin_bit_cast(
+            u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(
+                         rs, kWholeK ? lr.ok[tau] + 8u * row_stride : lr.ok[tau] + 64u, 0, 0));
       } else {
 #pragma unroll
         for (int c = 0; c < 4; ++c)
@@ -197,6 +208,38 @@ __device__ __forceinline__ void load_page_rows(PageRegs<kKind>& r, const uint8_t
         r.v[j] = __builtin_bit_cast(u32x4_t,
                                     __builtin_amdgcn_raw_buffer_load_b128(rs, lr.ov[j], 0, 0));
     }
+  }
+}
+
+// A wavefront's whole-row 8-bit K registers (kWholeK loads) put into the
+// MFMA's layout, lane 16g + n holding row n's bytes 16g.. and 64+16g.. of
+// each key tile, through `scratch`, 4 KB of LDS the wavefront owns for the
+// page loop.  Row r of a key tile is stored with 16-byte chunk c at position
+// c ^ (r / 2 % 8): the writes (8 lanes a row) and the reads (16 rows, one
+// chunk each) are then free of bank conflicts.  A wavefront's LDS accesses
+// run in order, so the reads follow its own writes without a wait.
+//
+// Whole-row loads touch 8 full 128-byte lines each, where a load in the
+// MFMA's layout (16 rows, 64 bytes of each, four lanes a row 64 bytes apart)
+// touches 16 half lines and no two neighbouring lanes share a row.
+__device__ __forceinline__ void k8_whole_to_mfma(PageRegs<1>& r, uint8_t* scratch, int n,
+                                                 int g) {
+  const int ln = 16 * g + n;
+#pragma unroll
+  for (int tau = 0; tau < 2; ++tau) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const uint32_t row = 8u * h + (uint32_t)(ln >> 3);
+      const uint32_t pos = (uint32_t)(ln & 7) ^ ((row >> 1) & 7u);
+      *reinterpret_cast<u32x4_t*>(scratch + 2048u * tau + 128u * row + 16u * pos) = r.k[tau][h];
+    }
+  }
+  const uint32_t f = ((uint32_t)n >> 1) & 7u;
+#pragma unroll
+  for (int tau = 0; tau < 2; ++tau) {
+    const uint8_t* row = scratch + 2048u * tau + 128u * (uint32_t)n;
+    r.k[tau][0] = *reinterpret_cast<const u32x4_t*>(row + 16u * ((uint32_t)g ^ f));
+    r.k[tau][1] = *reinterpret_cast<const u32x4_t*>(row + 16u * ((4u + (uint32_t)g) ^ f));
   }
 }
 

@@ -348,7 +348,15 @@ void multi_kernel(AttendParams p) {
   // spills to the three-wave prefill tiles (pf1 613 -> 621 us), and the 4-row
   // dense tiles ran 316 -> 368 us with them.
   constexpr bool kBoundedLoads = kM == 2 && !kOcc3;
-  LaneRows lr = lane_rows<kKind>(kbase, n, g);
+  // 2-row tiles read 8-bit K whole-row and move it into the MFMA's layout
+  // through the wavefront's part of the merge buffer, which the page loop
+  // does not otherwise use (k8_whole_to_mfma): chunked prefill 617 -> 557 us,
+  // ragged dql-32 decode 81.9 -> 80.8 us.  The 4-row dense tiles, one
+  // wavefront per SIMD, lose more to the LDS round trip in their page chain
+  // than they gain (322 -> 336 us), and keep the MFMA-layout loads.
+  constexpr bool kWholeK = kKind == 1 && kM == 2;
+  uint8_t* k_scratch = reinterpret_cast<uint8_t*>(&s_o[wave][0][0]);
+  LaneRows lr = lane_rows<kKind, kWholeK>(kbase, n, g);
   if constexpr (kBoundedLoads) lane_offsets(lr, row_stride);
   const int32_t* dense_row =
       p.block_table + (int64_t)(dense_r >= 0 ? dense_r : 0) * p.bt_stride;
@@ -384,10 +392,11 @@ void multi_kernel(AttendParams p) {
 #pragma unroll
       for (int w = 0; w < kM; ++w) vmax = max(vmax, (nv4 >> (8 * w)) & 0xffu);
       if constexpr (kBoundedLoads)
-        load_page_rows<kKind>(r, head_base + (int64_t)pg * p.kv_s0, row_stride, (int)vmax, lr);
+        load_page_rows<kKind, kWholeK>(r, head_base + (int64_t)pg * p.kv_s0, row_stride,
+                                       (int)vmax, lr);
       else
-        load_page<kKind>(r, head_base + (int64_t)pg * p.kv_s0, row_stride,
-                         (int)max(vmax, 1u) - 1, lr);
+        load_page<kKind, kWholeK>(r, head_base + (int64_t)pg * p.kv_s0, row_stride,
+                                  (int)max(vmax, 1u) - 1, lr);
       return nv4;
     };
 
@@ -408,6 +417,7 @@ void multi_kernel(AttendParams p) {
 #pragma unroll
           for (int w = 0; w < kM; ++w) any |= (int)((nv4 >> (8 * w)) & 0xffu) > kbase;
           if (any) {
+            if constexpr (kWholeK) k8_whole_to_mfma(buf[j], k_scratch, n, g);
             // This wavefront's keys are widened once for all rows of the
             // tile: K first, for every row's S^T and softmax; then V, for
             // every row's P V.
