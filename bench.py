@@ -34,6 +34,7 @@ from __future__ import annotations
 import argparse
 import hashlib
 import json
+import math
 import os
 import sys
 import time
@@ -56,6 +57,35 @@ FULL_STEP_CONFIG = "c5_full_step"
 # Fewest steps ever timed, whatever --steps asks (the timed window then spans
 # at least this many step replays).
 MIN_TIMED_STEPS = 200
+# Shortest timed window.  After the host has left the GPU idle for a second
+# or two (generating a workload), the first ~30 ms of replays run up to 10%
+# slower than the steady state (c4: 90 us per step over the first 160 steps,
+# 80.7 us from about the 400th on), so a window of a few ms measures mostly
+# that ramp.  The window is therefore stretched, in whole replays, to at least
+# this long, judged from the warmup replays' own duration.
+MIN_TIMED_MS = 300.0
+
+
+def timed_window(g, steps: int, warmup: int, replicas: int) -> int:
+    """Run the warmup replays of graph g (each replays all `replicas` steps)
+    and return how many replays to time: --steps rounded up to at least
+    MIN_TIMED_STEPS steps and to MIN_TIMED_MS of replays at the warmup's
+    rate, in whole replays."""
+    import torch
+
+    warm = max(1, (warmup + replicas - 1) // replicas)
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    ev0.record()
+    for _ in range(warm):
+        g.replay()
+    ev1.record()
+    torch.cuda.synchronize()
+    per_replay = max(ev0.elapsed_time(ev1) / warm, 1e-3)
+    by_steps = (max(steps, MIN_TIMED_STEPS) + replicas - 1) // replicas
+    by_time = int(math.ceil(MIN_TIMED_MS / per_replay))
+    return max(1, by_steps, min(by_time, 200000))
 # rocprofv3 counter summaries (HBM bytes per launch), one file per workload,
 # each valid only for the kernel sources it was taken on.
 TRAFFIC_DIR = os.path.join(ROOT, "profiles")
@@ -375,19 +405,15 @@ def time_config(name, steps, warmup, replicas, splits, dev, verbose=True, tile_r
         torch.cuda.synchronize()
         return ev0.elapsed_time(ev1), time.perf_counter() - h0
 
-    warm_replays = max(1, (warmup + replicas - 1) // replicas)
-    replays = max(1, (max(steps, MIN_TIMED_STEPS) + replicas - 1) // replicas)
+    replays = timed_window(graph, steps, warmup, replicas)
     n_steps = replays * replicas
-    for _ in range(warm_replays):
-        graph.replay()
     gpu_ms, host_s = timed(graph, replays)
     ms_step = gpu_ms / n_steps
     # The attend kernel alone: same launches, without the merge pass (which
     # a single-row plan with 2..4 splits does inside the attend).
-    for _ in range(warm_replays):
-        attend_graph.replay()
-    attend_ms, _ = timed(attend_graph, replays)
-    attend_ms /= n_steps
+    a_replays = timed_window(attend_graph, steps, warmup, replicas)
+    attend_ms, _ = timed(attend_graph, a_replays)
+    attend_ms /= a_replays * replicas
     eff = ds.mean_bytes("effective_kv")
     uniq = ds.mean_bytes("unique_kv")
     alg = ds.mean_bytes("algorithmic")
@@ -555,9 +581,7 @@ def gather_ceiling(ds, replicas: int, steps: int, warmup: int, attend_ms: float)
         with torch.cuda.graph(g):
             for i in range(replicas):
                 launch(i)
-        reps = max(1, (steps + replicas - 1) // replicas)
-        for _ in range(max(1, (warmup + replicas - 1) // replicas)):
-            g.replay()
+        reps = timed_window(g, steps, warmup, replicas)
         e0 = torch.cuda.Event(enable_timing=True)
         e1 = torch.cuda.Event(enable_timing=True)
         torch.cuda.synchronize()
@@ -710,10 +734,7 @@ def _graph_time(fns, replicas, steps, warmup):
         for i in range(replicas):
             fns(i)
     torch.cuda.synchronize()
-    replays = max(1, (max(steps, MIN_TIMED_STEPS) + replicas - 1) // replicas)
-    for _ in range(max(1, (warmup + replicas - 1) // replicas)):
-        g.replay()
-    torch.cuda.synchronize()
+    replays = timed_window(g, steps, warmup, replicas)
     ev0 = torch.cuda.Event(enable_timing=True)
     ev1 = torch.cuda.Event(enable_timing=True)
     ev0.record()
@@ -1226,8 +1247,10 @@ def main():
         "n_gpus": 1,
         "steps": res["steps"],
         "steps_requested": args.steps,
-        "steps_note": f"timed steps = --steps rounded up to at least {MIN_TIMED_STEPS} and to "
-                      f"whole cycles of the {args.replicas} replicas captured in one graph",
+        "steps_note": f"timed steps = --steps rounded up to at least {MIN_TIMED_STEPS} steps and "
+                      f"at least {MIN_TIMED_MS:.0f} ms of replays (at the warmup replays' rate), "
+                      f"in whole cycles of the {args.replicas} replicas captured in one graph: "
+                      f"the GPU runs its first ~30 ms after an idle spell up to 10% slower",
         "warmup": args.warmup,
         "ms_per_step": round(res["ms_per_step"], 5),
         "higher_is_better": True,
