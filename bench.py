@@ -62,7 +62,7 @@ MIN_TIMED_STEPS = 200
 # slower than the steady state (c4: 90 us per step over the first 160 steps,
 # 80.7 us from about the 400th on), so a window of a few ms measures mostly
 # that ramp.  The window is therefore stretched, in whole replays, to at least
-# this long, judged from the warmup replays' own duration.
+# this long, estimated from the warmup replays' own duration.
 MIN_TIMED_MS = 300.0
 
 
