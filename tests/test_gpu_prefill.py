@@ -70,6 +70,32 @@ def test_prefill_many_requests(num_prefills, tile_rows):
     assert np.all(got[case.real_rows:] == 0.0)
 
 
+@pytest.mark.parametrize("tile_rows", [1, 2])
+def test_prefill_eight_thousand_requests(tile_rows):
+    """8192 requests of 0..3 new tokens over contexts of 0..120 tokens (a
+    13-level row -> request search): rows sampled across the whole range, the
+    first and last row of every 512th request, and the padding rows."""
+    _banner(f"prefill 8192 requests tile_rows={tile_rows}")
+    rng = np.random.default_rng(47)
+    n = 8192
+    q_lens = rng.integers(0, 4, size=n)
+    seq = np.maximum(q_lens + rng.integers(0, 121, size=n), 1)
+    case = gen.make_prefill_case(48, q_lens.tolist(), seq.tolist(), 16, 1, rule="zipf",
+                                 pad_rows=5)
+    d = PrefillDevCase(case)
+    d.run(d.plan(tile_rows=tile_rows))
+    torch.cuda.synchronize()
+    got = to_f64(d.out)
+    cu = case.cu_seqlens_q
+    rows = set(rng.choice(case.real_rows, 256, replace=False).tolist())
+    for r in range(0, n, 512):
+        if cu[r + 1] > cu[r]:
+            rows.update((int(cu[r]), int(cu[r + 1]) - 1))
+    rows = sorted(rows)
+    assert_parity(got[rows], oracle_prefill(case, rows=rows), what=f"8192 prefills, {len(rows)} rows")
+    assert np.all(got[case.real_rows:] == 0.0)
+
+
 def test_prefill_graph_replay_with_new_chunk_boundaries():
     """One captured run replayed after cu_seqlens_q / context_lens / top-k
     change in place (the rows they describe move; the shape does not)."""
