@@ -82,9 +82,14 @@ def timed_window(g, steps: int, warmup: int, replicas: int) -> int:
         g.replay()
     ev1.record()
     torch.cuda.synchronize()
-    per_replay = max(ev0.elapsed_time(ev1) / warm, 1e-3)
+    return window_replays(ev0.elapsed_time(ev1) / warm, steps, replicas)
+
+
+def window_replays(per_replay_ms: float, steps: int, replicas: int) -> int:
+    """Replays to time: enough for --steps (at least MIN_TIMED_STEPS) and for
+    MIN_TIMED_MS at per_replay_ms a replay, in whole replays."""
     by_steps = (max(steps, MIN_TIMED_STEPS) + replicas - 1) // replicas
-    by_time = int(math.ceil(MIN_TIMED_MS / per_replay))
+    by_time = int(math.ceil(MIN_TIMED_MS / max(per_replay_ms, 1e-3)))
     return max(1, by_steps, min(by_time, 200000))
 # rocprofv3 counter summaries (HBM bytes per launch), one file per workload,
 # each valid only for the kernel sources it was taken on.

@@ -40,3 +40,18 @@ def test_page_runs_cover_the_effective_bytes(name, splits):
         assert cl[cf[w]:cf[w + 1]].astype(np.int64).sum() == \
             lens[first[w]:first[w + 1]].astype(np.int64).sum()
     assert (co % 16 == 0).all() and (co + cl <= nbytes).all()
+
+
+def test_timed_window_rule():
+    """Timed windows: --steps rounded up to at least MIN_TIMED_STEPS steps and
+    to MIN_TIMED_MS of replays, in whole replays of the replicas."""
+    r = 8
+    # a slow step: the step count decides (200 steps = 25 replays of 8)
+    assert bench.window_replays(1000.0, 20, r) == (bench.MIN_TIMED_STEPS + r - 1) // r
+    # more steps asked than the floor: rounded up to whole replays
+    assert bench.window_replays(1000.0, 1001, r) == 126
+    # a fast step: the duration decides
+    n = bench.window_replays(0.65, 20, r)
+    assert n * 0.65 >= bench.MIN_TIMED_MS and (n - 1) * 0.65 < bench.MIN_TIMED_MS
+    # a degenerate timing never gives an unbounded window
+    assert bench.window_replays(0.0, 20, r) == 200000
