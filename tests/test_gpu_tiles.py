@@ -5,7 +5,8 @@ rows read once: pages staged in registers for 2- and 4-row tiles, through an
 LDS ring for 8-row tiles over 8-bit caches) must give
 what the oracle gives for any tile size: the randomized decode cases and the
 format cases are rerun on 2-, 4- and 8-row tiles,
-the single-row kernel is checked on a long decode query length, and dense
+the single-row kernel is checked on a long decode query length, a graph of
+sparse tiles is replayed with the requests' length order reversed, and dense
 decode (every visible block, no top-k) is checked on the test page's shapes,
 randomized shapes (query lengths 1..8, padding rows, NHD, every split count,
 all formats), a graph replayed with new lengths and the TP1-shaped dense
@@ -65,6 +66,53 @@ def test_format_cases_on_tiles(tile_rows, seed, batch, dql, hq, hkv, k, lo, hi, 
     d.run(d.plan(splits, tile_rows=tile_rows))
     torch.cuda.synchronize()
     assert_parity(to_f64(d.out), oracle_attend(case), what=f"tiles format {seed}")
+
+
+@pytest.mark.parametrize("tile_rows", [2, 4])
+def test_tiles_graph_replay_with_the_length_order_reversed(tile_rows):
+    """Sparse 2- and 4-row tiles deal the requests longest first, ranking them
+    by seq_lens on the device at every launch.  A graph captured with one
+    length order is replayed with the order reversed, then restored, with
+    fresh top-k rows for each; every replay is checked against the oracle."""
+    _banner(f"tiles={tile_rows} graph replay, request length order reversed")
+    B, dql = 8, 4
+    # tables and pages for 6000 tokens per request; shorter lengths use a prefix
+    case = gen.make_random_case(192, B, dql, 64, 4, 16, 6000, 6000, pad_rows=2)
+    rng = np.random.default_rng(193)
+    lens = np.array([6000, 5000, 4100, 3500, 600, 420, 250, 130], dtype=np.int32)
+    orders = [lens, lens[::-1].copy(), lens]
+
+    def topk_for(seq):
+        return gen._topk_rows(rng, seq, dql, case.num_kv_heads, 16,
+                              lambda r, last: gen.pick_uniform(rng, last, 16), True,
+                              pad_rows=2)
+
+    d = DevCase(case)
+    plan = d.plan(tile_rows=tile_rows)
+    assert plan.tile_rows == tile_rows
+    d.seq_lens.copy_(torch.from_numpy(orders[0]))
+    d.topk.copy_(torch.from_numpy(topk_for(orders[0])))
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        d.run(plan)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        d.run(plan)
+    for it, seq in enumerate(orders):
+        tk = topk_for(seq)
+        d.seq_lens.copy_(torch.from_numpy(seq))
+        d.topk.copy_(torch.from_numpy(tk))
+        d.out.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        case.seq_lens, case.topk = seq, tk
+        got = to_f64(d.out)
+        assert_parity(got, oracle_attend(case), what=f"replay {it}, lengths {seq.tolist()}")
+        assert np.all(got[case.real_rows:] == 0.0)
 
 
 def test_long_query_length_single_row_and_tiles_agree_with_oracle():
